@@ -1,0 +1,147 @@
+"""Float64 CPU oracle of the Mamba selective scan -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU product path
+(``selective_state_space_mssm_amd``) never imports it, and this package imports
+nothing from the product path: the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, float64, sequential in time,
+OpenMP over independent (batch, channel) rows).  This module only converts
+arrays to float64 -- exactly, since every stored float32/bfloat16 value is a
+float64 value -- and calls it.
+
+What the oracle computes is the sequential loop of the mamba-minimal page
+("PyTorch 한 파일에서의 Mamba 구현", Hacker News comments), with the
+discretisation, skip term, gate and step-size transform of the selective SSM
+(Mamba paper Section 3 / Algorithm 2, named on the page "Mamba SSM 架构");
+``oracle.c`` states the formulas.
+
+Pinning (what checks this oracle against something other than itself) is in
+``tests/test_oracle_fwd_pins.py`` and ``tests/test_oracle_bwd_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCE = os.path.join(_HERE, "oracle.c")
+
+_lib = None
+
+
+def build(verbose: bool = False, source: str = SOURCE, out: str = LIB_PATH) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (-O2, no fast-math)."""
+    import subprocess
+
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", out, source, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def open_library(path: str):
+    """Open a compiled oracle library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.oracle_scan_fwd.argtypes = [i64, i64, i64, i64, i32] + [p] * 11
+    lib.oracle_scan_fwd.restype = None
+    lib.oracle_step.argtypes = [i64, i64, i64, i32] + [p] * 10
+    lib.oracle_step.restype = None
+    lib.oracle_scan_bwd.argtypes = [i64, i64, i64, i64, i32] + [p] * 20
+    lib.oracle_scan_bwd.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = i32
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = open_library(LIB_PATH)
+    return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use on this host."""
+    return int(_load().oracle_num_threads())
+
+
+def _f64(x):
+    """Exact float64 copy of an input (numpy array or CPU/GPU torch tensor)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: bf16/fp32 -> fp64 is exact
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan_fwd(u, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
+             softplus=True):
+    """Return ``(y, h_final)`` in float64 for inputs of shapes
+    u, delta, z: (B, L, D); Bm, Cm: (B, L, N); A: (D, N); Dskip, dt_bias: (D);
+    h0: (B, D, N)."""
+    u, delta, A, Bm, Cm = map(_f64, (u, delta, A, Bm, Cm))
+    Dskip, z, dt_bias, h0 = map(_f64, (Dskip, z, dt_bias, h0))
+    Bsz, L, D = u.shape
+    N = A.shape[1]
+    assert delta.shape == u.shape and A.shape == (D, N)
+    assert Bm.shape == (Bsz, L, N) and Cm.shape == (Bsz, L, N)
+    assert z is None or z.shape == u.shape
+    assert h0 is None or h0.shape == (Bsz, D, N)
+    y = np.empty((Bsz, L, D), np.float64)
+    hf = np.empty((Bsz, D, N), np.float64)
+    _load().oracle_scan_fwd(Bsz, L, D, N, int(bool(softplus)), _ptr(u), _ptr(delta),
+                            _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+                            _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(hf))
+    return y, hf
+
+
+def step(u_t, delta_t, A, Bm_t, Cm_t, state, Dskip=None, z_t=None, dt_bias=None,
+         softplus=True):
+    """One recurrent step.  u_t, delta_t, z_t: (B, D); Bm_t, Cm_t: (B, N);
+    state: (B, D, N).  Returns ``(y_t, new_state)`` (the input is not modified)."""
+    u_t, delta_t, A, Bm_t, Cm_t = map(_f64, (u_t, delta_t, A, Bm_t, Cm_t))
+    Dskip, z_t, dt_bias = map(_f64, (Dskip, z_t, dt_bias))
+    st = _f64(state).copy()
+    Bsz, D = u_t.shape
+    N = A.shape[1]
+    y = np.empty((Bsz, D), np.float64)
+    _load().oracle_step(Bsz, D, N, int(bool(softplus)), _ptr(u_t), _ptr(delta_t),
+                        _ptr(A), _ptr(Bm_t), _ptr(Cm_t), _ptr(Dskip), _ptr(z_t),
+                        _ptr(dt_bias), _ptr(st), _ptr(y))
+    return y, st
+
+
+def scan_bwd(u, delta, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, h0=None,
+             dh_final=None, softplus=True):
+    """Analytic adjoint.  Returns a dict with du, ddelta, dA, dB, dC, dD, dz,
+    ddt_bias, dh0 (float64; dz is None without a gate)."""
+    u, delta, A, Bm, Cm, dy = map(_f64, (u, delta, A, Bm, Cm, dy))
+    Dskip, z, dt_bias, h0, dh_final = map(_f64, (Dskip, z, dt_bias, h0, dh_final))
+    Bsz, L, D = u.shape
+    N = A.shape[1]
+    out = {
+        "du": np.empty((Bsz, L, D)), "ddelta": np.empty((Bsz, L, D)),
+        "dA": np.empty((D, N)), "dB": np.empty((Bsz, L, N)), "dC": np.empty((Bsz, L, N)),
+        "dD": np.empty((D,)), "dz": np.empty((Bsz, L, D)) if z is not None else None,
+        "ddt_bias": np.empty((D,)), "dh0": np.empty((Bsz, D, N)),
+    }
+    _load().oracle_scan_bwd(
+        Bsz, L, D, N, int(bool(softplus)), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm),
+        _ptr(Cm), _ptr(Dskip), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(dy),
+        _ptr(dh_final), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+        _ptr(out["ddt_bias"]), _ptr(out["dh0"]))
+    return out
