@@ -1,0 +1,216 @@
+"""Benchmark of the selective scan on one MI355X.
+
+One step = one forward scan over the Mamba-2.8B layer workload (B=4, L=4096,
+D=5120, N=16; bfloat16 u/delta/z/Bm/Cm, float32 A/Dskip/dt_bias/state,
+float32 arithmetic), inputs resident in HBM.  Prints one JSON line:
+
+* value: algorithmic GB/s of the forward (bytes the method must move: u,
+  delta, z, y, Bm, Cm, A, Dskip, dt_bias and h_final; the (B,L,D,N) state
+  expansion is never moved) per wall time of a step;
+* roofline: the forward kernel's average launch duration from HIP events
+  recorded around every timed launch on the launch stream, against the VALU
+  issue-rate bound of the chip (the scan is VALU-bound: see the design doc);
+* cpu_baseline: the float64 oracle timed on this host on a bounded channel
+  sample of the same workload.
+
+``--gpus N`` with N > 1 exits: this benchmark and the library run on one GPU.
+``--extra`` adds the 130M-layer forward and the training-workload backward.
+``--copy-probe`` runs a plain device copy of 1 GiB first (counter calibration).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, published
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # lane-instructions/s: CUs x SIMDs x lanes x clock
+SLOTS_PER_ELEM_STATE = 6                  # 4 VALU + 1 v_exp_f32 at half rate (2 issue slots)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_bytes(w: workloads.Workload) -> int:
+    act = 2 if w.dtype == "bf16" else 4
+    return (w.B * w.L * w.D * 4 * act + w.B * w.L * w.N * 2 * act
+            + 4 * w.D * w.N + 8 * w.D + 4 * w.B * w.D * w.N)
+
+
+def bwd_bytes(w: workloads.Workload) -> int:
+    act = 2 if w.dtype == "bf16" else 4
+    # reads u, delta, z, dy, Bm, Cm, A, Dskip, dt_bias; writes du, ddelta, dz, dB, dC, dA, dD, ddt_bias
+    return (w.B * w.L * w.D * 7 * act + w.B * w.L * w.N * 4 * act
+            + 2 * 4 * w.D * w.N + 4 * 4 * w.D)
+
+
+def time_fwd(mssm, torch, w, steps, warmup):
+    inp = workloads.make_inputs(w)
+    t = workloads.to_torch(inp, "cuda")
+    del inp
+    y = torch.empty_like(t["u"])
+    hf = torch.empty((w.B, w.D, w.N), dtype=torch.float32, device="cuda")
+    ws_n = mssm.fwd_workspace_bytes(w.B, w.L, w.D, w.N, t["u"].dtype)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def run():
+        mssm.scan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"], t["dt_bias"],
+                      None, y=y, h_final=hf, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall, launch_ms
+
+
+def time_bwd(mssm, torch, w, steps, warmup):
+    inp = workloads.make_inputs(w, with_dy=True)
+    t = workloads.to_torch(inp, "cuda")
+    del inp
+    ws = torch.empty(mssm.bwd_workspace_bytes(w.B, w.L, w.D, w.N, t["u"].dtype), dtype=torch.uint8, device="cuda")
+
+    def run():
+        mssm.scan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["dy"], t["Dskip"], t["z"],
+                      t["dt_bias"], None, None, want_dh0=False, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def cpu_baseline(w: workloads.Workload, target_s: float = 12.0):
+    """Oracle (float64 C, OpenMP) on a channel sample of the workload."""
+    import oracle
+
+    inp = workloads.make_inputs(w)
+    rng = np.random.default_rng(0)
+
+    def run(ch):
+        sub = workloads.as_float32(workloads.select_channels(inp, ch))
+        t0 = time.perf_counter()
+        oracle.scan_fwd(sub["u"], sub["delta"], sub["A"], sub["Bm"], sub["Cm"], sub["Dskip"], sub["z"],
+                        sub["dt_bias"], None)
+        return time.perf_counter() - t0
+
+    probe = np.sort(rng.choice(w.D, 64, replace=False))
+    tp = run(probe)
+    nch = int(min(w.D, max(64, 64 * target_s / max(tp, 1e-3))))
+    nch = max(64, nch // 64 * 64)
+    ch = np.sort(rng.choice(w.D, nch, replace=False))
+    dt = run(ch)
+    frac = nch / w.D
+    gbs = fwd_bytes(w) * frac / dt / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{nch} of {w.D} channels of the {w.name} workload (B={w.B}, L={w.L}, full sequence), "
+                      f"{dt:.1f} s; elem_state_per_s={w.B * w.L * nch * w.N / dt:.3e}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="2.8b", choices=["2.8b", "130m", "long", "tiny", "train"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the selective-scan library has no multi-GPU path "
+              "(see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import selective_state_space_mssm_amd as mssm
+
+    if args.copy_probe:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy probe: 3 x 1 GiB device copies done")
+
+    w = workloads.WORKLOADS[args.workload]
+    log(f"workload {workloads.DESCRIPTIONS[w.name]}; steps {args.steps}, warmup {args.warmup}")
+    wall, launch_ms = time_fwd(mssm, torch, w, args.steps, args.warmup)
+    nbytes = fwd_bytes(w)
+    gbs = nbytes / wall / 1e9
+    kern_s = float(np.mean(launch_ms)) / 1e3
+    slots = SLOTS_PER_ELEM_STATE * w.elem_states
+    achieved = slots / kern_s / 1e12
+    out = {
+        "metric": "selective-scan fwd/bwd GB/s & % HBM peak (B·L·D·N elem/s) on 1 MI355X",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workloads.DESCRIPTIONS[w.name], "B": w.B, "L": w.L, "D": w.D, "N": w.N,
+                   "act_storage": w.dtype, "direction": "fwd"},
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "elem_state_per_s": float(f"{w.elem_states / wall:.4e}"),
+        "roofline": {
+            "bound": "alu",
+            "achieved": round(achieved, 3),
+            "peak": round(VALU_PEAK_TOPS, 3),
+            "unit": "T lane-instr/s",
+            "frac": round(achieved / VALU_PEAK_TOPS, 4),
+            "traffic": None,
+            "kernel": "scan_fwd_kernel",
+            "kernel_us": round(kern_s * 1e6, 2),
+            "work_per_launch": f"{SLOTS_PER_ELEM_STATE} VALU issue slots x {w.elem_states} (b,t,d,n)",
+            "hbm_achieved_GBs": round(nbytes / kern_s / 1e9, 1),
+            "hbm_peak_GBs": HBM_PEAK_GBS,
+        },
+    }
+    if args.extra:
+        for name in ("130m",):
+            ww = workloads.WORKLOADS[name]
+            wl, lm = time_fwd(mssm, torch, ww, 20, 3)
+            out.setdefault("extra", {})[f"{name}_fwd_GBs"] = round(fwd_bytes(ww) / wl / 1e9, 1)
+            out["extra"][f"{name}_fwd_us"] = round(wl * 1e6, 1)
+        tw = workloads.WORKLOADS["train"]
+        tb = time_bwd(mssm, torch, tw, 10, 2)
+        out.setdefault("extra", {})["train_bwd_us"] = round(tb * 1e6, 1)
+        out["extra"]["train_bwd_GBs"] = round(bwd_bytes(tw) / tb / 1e9, 1)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * mssm.h -- C ABI of the MI355X (gfx950) selective-scan library libmssm.so.
+ *
+ * The operation is the selective state-space scan of Mamba (selective SSM
+ * layer, Mamba paper Section 3 / Algorithm 2, named in the description section
+ * of the page "Mamba SSM 架构"): for every batch b and channel d, with state
+ * h[n], n < N,
+ *
+ *     x_t     = delta[b,t,d] + dt_bias[d]
+ *     Delta_t = softplus(x_t) if problem.delta_softplus else x_t
+ *     h_t[n]  = exp(Delta_t * A[d,n]) * h_{t-1}[n] + Delta_t * Bm[b,t,n] * u[b,t,d]
+ *     y[b,t,d]= (sum_n Cm[b,t,n] * h_t[n] + Dskip[d] * u[b,t,d]) * silu(z[b,t,d])
+ *
+ * with h_{-1} = h0 (zeros when h0 is NULL).  The state update and readout are
+ * the sequential loop printed in the Hacker News comments of the page
+ * "PyTorch 한 파일에서의 Mamba 구현" (deltaA = exp(Delta*A), deltaB_u =
+ * Delta*B*u, y = contraction of the state with C); the pages name deltaA and
+ * deltaB_u without a formula, and the zero-order-hold / Euler reading above is
+ * the one this library implements.  The state lives only in registers: the
+ * (B, L, D, N) expansion is never written to memory, which is the data
+ * movement the page "mamba.py: 一个简单高效的Mamba实现" (performance section,
+ * d_state paragraph, citing the paper's Appendix D) credits for the O(N)
+ * reduction in memory reads and writes.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layouts: row-major, contiguous, no strides.
+ *     u, delta, z, y, dy, du, ddelta, dz : (B, L, D)   D fastest
+ *     Bm, Cm, dB, dC                     : (B, L, N)   N fastest
+ *     A, dA                              : (D, N)      float32
+ *     Dskip, dt_bias, dD, ddt_bias       : (D)         float32
+ *     h0, h_final, dh_final, dh0, state  : (B, D, N)   float32
+ * Element type: problem.dtype (MSSM_F32 or MSSM_BF16) for u, delta, z, Bm, Cm,
+ *   y and their gradients; float32 for everything else.  Arithmetic is float32
+ *   throughout; bfloat16 outputs are rounded to nearest even.
+ * Memory: every pointer is a device pointer owned by the caller, 16-byte
+ *   aligned.  The library allocates and frees nothing and keeps no state
+ *   between calls; it is re-entrant.  Scratch memory is the caller's
+ *   `workspace`, of at least the size the matching *_workspace_bytes query
+ *   returns for the same problem (NULL is accepted when that size is 0).
+ * Streams: all work is enqueued on `hip_stream` (a hipStream_t; NULL = the
+ *   null stream); calls return once the work is enqueued.  Outputs are valid
+ *   when the stream reaches that point.
+ * Errors: argument errors are detected on the host before anything is
+ *   enqueued, and return without touching any buffer.  A launch failure
+ *   returns MSSM_ERR_HIP.  NaN and Inf in inputs are not trapped; they
+ *   propagate.  No exception crosses the ABI.
+ * Limits: 1 <= dstate <= MSSM_MAX_DSTATE and dstate a power of two;
+ *   batch, seqlen, dim >= 1; batch * dim and seqlen below 2^31; dim below
+ *   2^26; all indexing of (B, L, D) tensors is 64-bit.
+ */
+#ifndef MSSM_H
+#define MSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSSM_MAX_DSTATE 64
+
+typedef enum { MSSM_F32 = 0, MSSM_BF16 = 1 } mssm_dtype;
+
+typedef enum {
+    MSSM_OK = 0,
+    MSSM_ERR_NULL = -1,        /* a required pointer is NULL */
+    MSSM_ERR_SHAPE = -2,       /* a dimension is out of range */
+    MSSM_ERR_DTYPE = -3,       /* unknown problem.dtype */
+    MSSM_ERR_UNSUPPORTED = -4, /* valid but not built: dstate not a power of two or > MSSM_MAX_DSTATE */
+    MSSM_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+    MSSM_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the query returns */
+    MSSM_ERR_HIP = -7          /* a HIP launch failed */
+} mssm_status;
+
+typedef struct {
+    int64_t batch;          /* B */
+    int64_t seqlen;         /* L (ignored by mssm_step) */
+    int64_t dim;            /* D: channels */
+    int64_t dstate;         /* N: state size per channel */
+    int32_t dtype;          /* mssm_dtype of u, delta, z, Bm, Cm, y and their gradients */
+    int32_t delta_softplus; /* nonzero: Delta = softplus(delta + dt_bias) */
+} mssm_problem;
+
+/* Bytes of device scratch the forward needs (0 when the sequence is scanned
+ * in one pass; otherwise the cross-chunk carries, O(B * D * N * chunks)).
+ * Returns 0 for an invalid problem. */
+size_t mssm_scan_fwd_workspace_bytes(const mssm_problem* p);
+
+/* Bytes of device scratch the backward needs (chunk-boundary states and the
+ * per-tile partial sums of dA, dD, ddt_bias, dB, dC).  0 for an invalid problem. */
+size_t mssm_scan_bwd_workspace_bytes(const mssm_problem* p);
+
+/*
+ * Forward scan.  Required: p, u, delta, A, Bm, Cm, y.  Optional (NULL):
+ *   Dskip   -> 0             z       -> no gate (y = s)
+ *   dt_bias -> 0             h0      -> zero initial state
+ *   h_final -> not written
+ * Writes y (B, L, D) and, if given, h_final = h_{L-1} (B, D, N).
+ * y may not alias any input.
+ */
+mssm_status mssm_scan_fwd(const mssm_problem* p,
+                          const void* u, const void* delta, const float* A,
+                          const void* Bm, const void* Cm,
+                          const float* Dskip, const void* z, const float* dt_bias,
+                          const float* h0,
+                          void* y, float* h_final,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Backward scan: gradients of  sum(dy * y) + sum(dh_final * h_final)  with
+ * respect to every input, by the reverse-time adjoint scan with the forward
+ * states recomputed per chunk (nothing of the forward is stored between the
+ * calls).  Inputs are those of the forward plus dy (B, L, D) and the optional
+ * dh_final (B, D, N).
+ * Required outputs: du, ddelta (gradient w.r.t. the raw delta input, before
+ *   bias and softplus), dA, dB, dC.
+ * Optional outputs (NULL -> not written): dD (needs nothing), dz (only with
+ *   z; required when z is given), ddt_bias, dh0.
+ * Every gradient is overwritten, not accumulated.  Reductions over channels
+ * (dB, dC) and over batch and time (dA, dD, ddt_bias) use a fixed order:
+ * repeated calls give bitwise identical results.
+ */
+mssm_status mssm_scan_bwd(const mssm_problem* p,
+                          const void* u, const void* delta, const float* A,
+                          const void* Bm, const void* Cm,
+                          const float* Dskip, const void* z, const float* dt_bias,
+                          const float* h0,
+                          const void* dy, const float* dh_final,
+                          void* du, void* ddelta, float* dA, void* dB, void* dC,
+                          float* dD, void* dz, float* ddt_bias, float* dh0,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * One token of the recurrent (RNN) form, for streaming decode: the step
+ * function that the page "mamba.py: 一个简单高效的Mamba实现" lists in its
+ * updates section.  p->seqlen is ignored.  Shapes: u_t, delta_t, z_t, y_t
+ * (B, D) in p->dtype; Bm_t, Cm_t (B, N) in p->dtype; state (B, D, N) float32,
+ * read and overwritten in place with h_t.  Optional: Dskip, z_t, dt_bias.
+ * Calling it L times equals one mssm_scan_fwd over L steps with h0 = state.
+ */
+mssm_status mssm_step(const mssm_problem* p,
+                      const void* u_t, const void* delta_t, const float* A,
+                      const void* Bm_t, const void* Cm_t,
+                      const float* Dskip, const void* z_t, const float* dt_bias,
+                      float* state, void* y_t, void* hip_stream);
+
+/* Static, human-readable name of a status code. */
+const char* mssm_status_string(mssm_status s);
+
+/* Build description: target architecture and library version. */
+const char* mssm_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSSM_H */

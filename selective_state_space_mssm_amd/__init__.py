@@ -1,0 +1,13 @@
+"""Mamba selective scan, native on AMD Instinct MI355X (gfx950).
+
+The scan runs in hand-written HIP kernels behind the C ABI of
+``libmssm.so`` (declared in ``include/mssm.h``); this package is the thin
+Python binding over it.  PyTorch supplies device memory and streams only.
+"""
+from .binding import (  # noqa: F401
+    LIB_PATH, MSSM_BF16, MSSM_F32, EXPORTS, MssmError, Problem, bwd_workspace_bytes,
+    fwd_workspace_bytes, lib, problem, scan_bwd, scan_fwd, step,
+)
+
+__all__ = ["scan_fwd", "scan_bwd", "step", "fwd_workspace_bytes", "bwd_workspace_bytes",
+           "MssmError", "Problem", "problem", "lib", "LIB_PATH"]

@@ -1,0 +1,223 @@
+"""ctypes binding of libmssm.so (C ABI in include/mssm.h).
+
+Argument marshalling only: checks that tensors are on the GPU, contiguous and
+of the expected dtype and shape, allocates outputs and workspace with torch,
+and passes raw device pointers plus torch's current HIP stream to the C entry
+points.  Every step of the scan runs in the library's HIP kernels; there is no
+CPU or PyTorch fallback, and importing this module fails loudly when the
+library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmssm.so")
+
+MSSM_F32, MSSM_BF16 = 0, 1
+STATUS = {0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_SHAPE", -3: "MSSM_ERR_DTYPE",
+          -4: "MSSM_ERR_UNSUPPORTED", -5: "MSSM_ERR_ALIGN", -6: "MSSM_ERR_WORKSPACE",
+          -7: "MSSM_ERR_HIP"}
+EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd",
+           "mssm_scan_bwd", "mssm_step", "mssm_status_string", "mssm_build_info"]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("delta_softplus", ctypes.c_int32)]
+
+
+class MssmError(RuntimeError):
+    def __init__(self, status: int, lib):
+        self.status = status
+        super().__init__(lib.mssm_status_string(status).decode())
+
+
+def _open(path: str):
+    if not os.path.exists(path):
+        raise ImportError(
+            f"libmssm.so not found at {path}: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    P, sz, st, vp = ctypes.POINTER(Problem), ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p
+    lib.mssm_scan_fwd_workspace_bytes.argtypes = [P]
+    lib.mssm_scan_fwd_workspace_bytes.restype = sz
+    lib.mssm_scan_bwd_workspace_bytes.argtypes = [P]
+    lib.mssm_scan_bwd_workspace_bytes.restype = sz
+    lib.mssm_scan_fwd.argtypes = [P] + [vp] * 11 + [vp, sz, vp]
+    lib.mssm_scan_fwd.restype = st
+    lib.mssm_scan_bwd.argtypes = [P] + [vp] * 20 + [vp, sz, vp]
+    lib.mssm_scan_bwd.restype = st
+    lib.mssm_step.argtypes = [P] + [vp] * 10 + [vp]
+    lib.mssm_step.restype = st
+    lib.mssm_status_string.argtypes = [st]
+    lib.mssm_status_string.restype = ctypes.c_char_p
+    lib.mssm_build_info.argtypes = []
+    lib.mssm_build_info.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _open(LIB_PATH)
+
+
+def _check(status: int):
+    if status != 0:
+        raise MssmError(status, lib)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MSSM_F32
+    if t.dtype == torch.bfloat16:
+        return MSSM_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _req(t: torch.Tensor, name: str, shape, dtype) -> torch.Tensor:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _opt(t, name, shape, dtype):
+    return None if t is None else _req(t, name, shape, dtype)
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def problem(B: int, L: int, D: int, N: int, dtype=torch.float32, delta_softplus=True) -> Problem:
+    code = dtype if isinstance(dtype, int) else (MSSM_BF16 if dtype == torch.bfloat16 else MSSM_F32)
+    return Problem(B, L, D, N, code, 1 if delta_softplus else 0)
+
+
+def fwd_workspace_bytes(B, L, D, N, dtype=torch.float32) -> int:
+    return int(lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(problem(B, L, D, N, dtype))))
+
+
+def bwd_workspace_bytes(B, L, D, N, dtype=torch.float32) -> int:
+    return int(lib.mssm_scan_bwd_workspace_bytes(ctypes.byref(problem(B, L, D, N, dtype))))
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def scan_fwd(u, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
+             delta_softplus=True, return_final_state=True, y=None, h_final=None, workspace=None):
+    """Selective scan forward.  u, delta, z: (B, L, D); Bm, Cm: (B, L, N), all
+    float32 or all bfloat16; A (D, N), Dskip, dt_bias (D), h0 (B, D, N):
+    float32.  Returns (y, h_final) (h_final None unless requested)."""
+    act = u.dtype
+    B, L, D = u.shape
+    N = A.shape[1]
+    _req(u, "u", (B, L, D), act)
+    _req(delta, "delta", (B, L, D), act)
+    _req(A, "A", (D, N), torch.float32)
+    _req(Bm, "Bm", (B, L, N), act)
+    _req(Cm, "Cm", (B, L, N), act)
+    _opt(Dskip, "Dskip", (D,), torch.float32)
+    _opt(z, "z", (B, L, D), act)
+    _opt(dt_bias, "dt_bias", (D,), torch.float32)
+    _opt(h0, "h0", (B, D, N), torch.float32)
+    if y is None:
+        y = torch.empty((B, L, D), dtype=act, device=u.device)
+    _req(y, "y", (B, L, D), act)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((B, D, N), dtype=torch.float32, device=u.device)
+    _opt(h_final, "h_final", (B, D, N), torch.float32)
+    prob = problem(B, L, D, N, _dtype_code(u), delta_softplus)
+    nbytes = int(lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(prob)))
+    ws = _workspace(nbytes, u.device, workspace)
+    _check(lib.mssm_scan_fwd(ctypes.byref(prob), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                             _ptr(Dskip), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),
+                             _ptr(ws), nbytes, _stream(u.device)))
+    return y, h_final
+
+
+def scan_bwd(u, delta, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, h0=None, dh_final=None,
+             delta_softplus=True, want_dh0=True, workspace=None):
+    """Gradients of sum(dy*y) + sum(dh_final*h_final).  Returns a dict with
+    du, ddelta, dA, dB, dC, dD, dz (None without z), ddt_bias, dh0."""
+    act = u.dtype
+    B, L, D = u.shape
+    N = A.shape[1]
+    dev = u.device
+    _req(u, "u", (B, L, D), act)
+    _req(delta, "delta", (B, L, D), act)
+    _req(A, "A", (D, N), torch.float32)
+    _req(Bm, "Bm", (B, L, N), act)
+    _req(Cm, "Cm", (B, L, N), act)
+    _req(dy, "dy", (B, L, D), act)
+    _opt(Dskip, "Dskip", (D,), torch.float32)
+    _opt(z, "z", (B, L, D), act)
+    _opt(dt_bias, "dt_bias", (D,), torch.float32)
+    _opt(h0, "h0", (B, D, N), torch.float32)
+    _opt(dh_final, "dh_final", (B, D, N), torch.float32)
+    g = {
+        "du": torch.empty((B, L, D), dtype=act, device=dev),
+        "ddelta": torch.empty((B, L, D), dtype=act, device=dev),
+        "dA": torch.empty((D, N), dtype=torch.float32, device=dev),
+        "dB": torch.empty((B, L, N), dtype=act, device=dev),
+        "dC": torch.empty((B, L, N), dtype=act, device=dev),
+        "dD": torch.empty((D,), dtype=torch.float32, device=dev),
+        "dz": torch.empty((B, L, D), dtype=act, device=dev) if z is not None else None,
+        "ddt_bias": torch.empty((D,), dtype=torch.float32, device=dev),
+        "dh0": torch.empty((B, D, N), dtype=torch.float32, device=dev) if want_dh0 else None,
+    }
+    prob = problem(B, L, D, N, _dtype_code(u), delta_softplus)
+    nbytes = int(lib.mssm_scan_bwd_workspace_bytes(ctypes.byref(prob)))
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.mssm_scan_bwd(ctypes.byref(prob), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                             _ptr(Dskip), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(dy), _ptr(dh_final),
+                             _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                             _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddt_bias"]),
+                             _ptr(g["dh0"]), _ptr(ws), nbytes, _stream(dev)))
+    return g
+
+
+def step(u_t, delta_t, A, Bm_t, Cm_t, state, Dskip=None, z_t=None, dt_bias=None,
+         delta_softplus=True, y_t=None):
+    """One recurrent step.  u_t, delta_t, z_t: (B, D); Bm_t, Cm_t: (B, N);
+    state (B, D, N) float32 is updated in place.  Returns y_t (B, D)."""
+    act = u_t.dtype
+    B, D = u_t.shape
+    N = A.shape[1]
+    _req(u_t, "u_t", (B, D), act)
+    _req(delta_t, "delta_t", (B, D), act)
+    _req(A, "A", (D, N), torch.float32)
+    _req(Bm_t, "Bm_t", (B, N), act)
+    _req(Cm_t, "Cm_t", (B, N), act)
+    _req(state, "state", (B, D, N), torch.float32)
+    _opt(Dskip, "Dskip", (D,), torch.float32)
+    _opt(z_t, "z_t", (B, D), act)
+    _opt(dt_bias, "dt_bias", (D,), torch.float32)
+    if y_t is None:
+        y_t = torch.empty((B, D), dtype=act, device=u_t.device)
+    prob = problem(B, 1, D, N, _dtype_code(u_t), delta_softplus)
+    _check(lib.mssm_step(ctypes.byref(prob), _ptr(u_t), _ptr(delta_t), _ptr(A), _ptr(Bm_t), _ptr(Cm_t),
+                         _ptr(Dskip), _ptr(z_t), _ptr(dt_bias), _ptr(state), _ptr(y_t),
+                         _stream(u_t.device)))
+    return y_t

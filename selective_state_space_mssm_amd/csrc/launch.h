@@ -1,0 +1,69 @@
+// launch.h -- host-side interface between the C ABI (mssm_api.cpp) and the
+// kernel launchers (scan_fwd.hip, scan_bwd.hip, scan_step.hip).  Internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mssm {
+
+// Every pointer and size of one call, already validated by the C ABI layer.
+struct ScanArgs {
+    // problem
+    int64_t B, L, D, N;
+    int dtype;      // 0 = f32, 1 = bf16 (storage of u, delta, z, Bm, Cm, y, grads)
+    int softplus;   // Delta = softplus(delta + dt_bias) when nonzero
+    // forward inputs
+    const void* u;
+    const void* delta;
+    const void* z;       // nullable
+    const void* Bm;
+    const void* Cm;
+    const float* A;
+    const float* Dskip;    // nullable
+    const float* dt_bias;  // nullable
+    const float* h0;       // nullable
+    // forward outputs
+    void* y;
+    float* h_final;        // nullable
+    // backward inputs / outputs
+    const void* dy;
+    const float* dh_final; // nullable
+    void* du;
+    void* ddelta;
+    void* dz;              // nullable
+    void* dB;
+    void* dC;
+    float* dA;
+    float* dD;             // nullable
+    float* ddt_bias;       // nullable
+    float* dh0;            // nullable
+    // scratch
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+// Channels per workgroup: one wave64 lane per channel.
+constexpr int kChannelsPerBlock = 64;
+
+// Forward schedule: how the time axis is cut into chunks.
+struct FwdPlan {
+    int64_t chunks;      // K >= 1
+    int64_t chunk_len;   // steps per chunk (multiple of the time tile)
+    size_t ws_bytes;     // workspace bytes (0 when K == 1)
+};
+FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N);
+hipError_t launch_fwd(const ScanArgs& a, hipStream_t s);
+
+struct BwdPlan {
+    int64_t tile;        // time steps per recompute tile
+    int64_t tiles;       // ceil(L / tile)
+    size_t ws_bytes;
+};
+BwdPlan plan_bwd(int64_t B, int64_t L, int64_t D, int64_t N);
+hipError_t launch_bwd(const ScanArgs& a, hipStream_t s);
+
+hipError_t launch_step(const ScanArgs& a, float* state, hipStream_t s);
+
+}  // namespace mssm

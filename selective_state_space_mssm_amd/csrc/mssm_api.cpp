@@ -1,0 +1,146 @@
+// mssm_api.cpp -- the C ABI declared in include/mssm.h.
+//
+// Host-only layer: validates every argument before anything is enqueued
+// (so argument errors never touch a device buffer and need no GPU), sizes the
+// workspace, and hands a validated ScanArgs to the kernel launchers.
+#include "mssm.h"
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_version.h>
+
+#include <cstdint>
+#include <initializer_list>
+
+#include "launch.h"
+
+namespace {
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Problem checks shared by every entry point.  `need_seq`: seqlen matters.
+mssm_status check_problem(const mssm_problem* p, bool need_seq) {
+    if (!p) return MSSM_ERR_NULL;
+    if (p->dtype != MSSM_F32 && p->dtype != MSSM_BF16) return MSSM_ERR_DTYPE;
+    if (p->batch < 1 || p->dim < 1 || p->dstate < 1) return MSSM_ERR_SHAPE;
+    if (need_seq && p->seqlen < 1) return MSSM_ERR_SHAPE;
+    if (p->batch * p->dim >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
+    if (p->dim >= (int64_t{1} << 26)) return MSSM_ERR_SHAPE;  // per-tile offsets are 32-bit
+    if (need_seq && p->seqlen >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
+    if (!is_pow2(p->dstate) || p->dstate > MSSM_MAX_DSTATE) return MSSM_ERR_UNSUPPORTED;
+    return MSSM_OK;
+}
+
+// All non-null pointers must be 16-byte aligned.
+mssm_status check_align(std::initializer_list<const void*> ptrs) {
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return MSSM_ERR_ALIGN;
+    return MSSM_OK;
+}
+
+mssm::ScanArgs base_args(const mssm_problem* p) {
+    mssm::ScanArgs a{};
+    a.B = p->batch;
+    a.L = p->seqlen;
+    a.D = p->dim;
+    a.N = p->dstate;
+    a.dtype = p->dtype;
+    a.softplus = p->delta_softplus ? 1 : 0;
+    return a;
+}
+
+mssm_status from_hip(hipError_t e) { return e == hipSuccess ? MSSM_OK : MSSM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t mssm_scan_fwd_workspace_bytes(const mssm_problem* p) {
+    if (check_problem(p, true) != MSSM_OK) return 0;
+    return mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+}
+
+size_t mssm_scan_bwd_workspace_bytes(const mssm_problem* p) {
+    if (check_problem(p, true) != MSSM_OK) return 0;
+    return mssm::plan_bwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+}
+
+mssm_status mssm_scan_fwd(const mssm_problem* p, const void* u, const void* delta, const float* A,
+                          const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                          const float* dt_bias, const float* h0, void* y, float* h_final,
+                          void* workspace, size_t workspace_bytes, void* hip_stream) {
+    mssm_status st = check_problem(p, true);
+    if (st != MSSM_OK) return st;
+    if (!u || !delta || !A || !Bm || !Cm || !y) return MSSM_ERR_NULL;
+    st = check_align({u, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, y, h_final, workspace});
+    if (st != MSSM_OK) return st;
+    const size_t need = mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return MSSM_ERR_WORKSPACE;
+
+    mssm::ScanArgs a = base_args(p);
+    a.u = u; a.delta = delta; a.z = z; a.Bm = Bm; a.Cm = Cm;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0;
+    a.y = y; a.h_final = h_final;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return from_hip(mssm::launch_fwd(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+mssm_status mssm_scan_bwd(const mssm_problem* p, const void* u, const void* delta, const float* A,
+                          const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                          const float* dt_bias, const float* h0, const void* dy,
+                          const float* dh_final, void* du, void* ddelta, float* dA, void* dB,
+                          void* dC, float* dD, void* dz, float* ddt_bias, float* dh0,
+                          void* workspace, size_t workspace_bytes, void* hip_stream) {
+    mssm_status st = check_problem(p, true);
+    if (st != MSSM_OK) return st;
+    if (!u || !delta || !A || !Bm || !Cm || !dy) return MSSM_ERR_NULL;
+    if (!du || !ddelta || !dA || !dB || !dC) return MSSM_ERR_NULL;
+    if (z && !dz) return MSSM_ERR_NULL;
+    st = check_align({u, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, dy, dh_final, du, ddelta, dA, dB,
+                      dC, dD, dz, ddt_bias, dh0, workspace});
+    if (st != MSSM_OK) return st;
+    const size_t need = mssm::plan_bwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return MSSM_ERR_WORKSPACE;
+
+    mssm::ScanArgs a = base_args(p);
+    a.u = u; a.delta = delta; a.z = z; a.Bm = Bm; a.Cm = Cm;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0;
+    a.dy = dy; a.dh_final = dh_final;
+    a.du = du; a.ddelta = ddelta; a.dz = z ? dz : nullptr; a.dB = dB; a.dC = dC;
+    a.dA = dA; a.dD = dD; a.ddt_bias = ddt_bias; a.dh0 = dh0;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return from_hip(mssm::launch_bwd(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+mssm_status mssm_step(const mssm_problem* p, const void* u_t, const void* delta_t, const float* A,
+                      const void* Bm_t, const void* Cm_t, const float* Dskip, const void* z_t,
+                      const float* dt_bias, float* state, void* y_t, void* hip_stream) {
+    mssm_status st = check_problem(p, false);
+    if (st != MSSM_OK) return st;
+    if (!u_t || !delta_t || !A || !Bm_t || !Cm_t || !state || !y_t) return MSSM_ERR_NULL;
+    st = check_align({u_t, delta_t, A, Bm_t, Cm_t, Dskip, z_t, dt_bias, state, y_t});
+    if (st != MSSM_OK) return st;
+    mssm::ScanArgs a = base_args(p);
+    a.L = 1;
+    a.u = u_t; a.delta = delta_t; a.z = z_t; a.Bm = Bm_t; a.Cm = Cm_t;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.y = y_t;
+    return from_hip(mssm::launch_step(a, state, static_cast<hipStream_t>(hip_stream)));
+}
+
+const char* mssm_status_string(mssm_status s) {
+    switch (s) {
+        case MSSM_OK: return "MSSM_OK: success";
+        case MSSM_ERR_NULL: return "MSSM_ERR_NULL: a required pointer is NULL";
+        case MSSM_ERR_SHAPE: return "MSSM_ERR_SHAPE: a dimension is out of range";
+        case MSSM_ERR_DTYPE: return "MSSM_ERR_DTYPE: unknown element type";
+        case MSSM_ERR_UNSUPPORTED: return "MSSM_ERR_UNSUPPORTED: dstate must be a power of two <= 64";
+        case MSSM_ERR_ALIGN: return "MSSM_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case MSSM_ERR_WORKSPACE: return "MSSM_ERR_WORKSPACE: workspace missing or too small";
+        case MSSM_ERR_HIP: return "MSSM_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown mssm_status";
+}
+
+const char* mssm_build_info(void) { return "libmssm 0.1 (gfx950)"; }
+
+}  // extern "C"

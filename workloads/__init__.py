@@ -174,3 +174,20 @@ def as_float32(inp: dict) -> dict:
         if k in inp and inp[k] is not None:
             out[k] = to_f32(inp[k], inp["dtype"])
     return out
+
+
+def to_torch(inp: dict, device="cuda", keys=("u", "delta", "z", "Bm", "Cm", "dy", "dt_bias", "A", "Dskip")) -> dict:
+    """Storage form -> torch tensors on `device` (bfloat16 bits are
+    reinterpreted, not converted, so values are exact)."""
+    import torch
+
+    out = {}
+    for k in keys:
+        if k not in inp or inp[k] is None:
+            continue
+        x = inp[k]
+        if k in ("dt_bias", "A", "Dskip") or inp["dtype"] == "f32":
+            out[k] = torch.from_numpy(np.ascontiguousarray(x)).to(device)
+        else:
+            out[k] = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+    return out
