@@ -47,7 +47,7 @@
  *   propagate.  No exception crosses the ABI.
  * Limits: 1 <= dstate <= MSSM_MAX_DSTATE and dstate a power of two;
  *   batch, seqlen, dim >= 1; batch * dim and seqlen below 2^31; dim below
- *   2^26; all indexing of (B, L, D) tensors is 64-bit.
+ *   2^24; all indexing of (B, L, D) tensors is 64-bit.
  */
 #ifndef MSSM_H
 #define MSSM_H

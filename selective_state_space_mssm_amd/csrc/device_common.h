@@ -146,6 +146,26 @@ __device__ __forceinline__ void unpack_lane_row(const uint32_t (&q)[LaneRow<T, N
     }
 }
 
+// ---- buffer stores with hardware range checking ---------------------------------
+// A raw buffer resource over [base, base + bytes): a store whose byte offset
+// is outside the range is dropped by the hardware, so a lane that must not
+// write gets an out-of-range offset instead of a branch (branches split the
+// instruction stream the scheduler interleaves).  Word 3 is the gfx9
+// descriptor format for raw (untyped) buffer access.
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+constexpr uint32_t kNoStore = 0xFFFFFFF0u;  // an offset beyond any range
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufferWord3);
+}
+__device__ __forceinline__ void buffer_store_act(float v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off, float) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(byte_off), 0, 0);
+}
+__device__ __forceinline__ void buffer_store_act(float v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint16_t) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)), r,
+                                          static_cast<int>(byte_off), 0, 0);
+}
+
 // ---- DPP row broadcast -----------------------------------------------------------
 // row_newbcast:J -- every lane of a 16-lane row reads lane J of that row.  With
 // a value replicated over the four rows (lane l holding element l % 16), this

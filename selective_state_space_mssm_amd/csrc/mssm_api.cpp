@@ -25,7 +25,7 @@ mssm_status check_problem(const mssm_problem* p, bool need_seq) {
     if (p->batch < 1 || p->dim < 1 || p->dstate < 1) return MSSM_ERR_SHAPE;
     if (need_seq && p->seqlen < 1) return MSSM_ERR_SHAPE;
     if (p->batch * p->dim >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
-    if (p->dim >= (int64_t{1} << 26)) return MSSM_ERR_SHAPE;  // per-tile offsets are 32-bit
+    if (p->dim >= (int64_t{1} << 24)) return MSSM_ERR_SHAPE;  // per-tile byte offsets are 31-bit
     if (need_seq && p->seqlen >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
     if (!is_pow2(p->dstate) || p->dstate > MSSM_MAX_DSTATE) return MSSM_ERR_UNSUPPORTED;
     return MSSM_OK;

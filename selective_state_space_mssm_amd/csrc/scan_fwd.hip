@@ -114,11 +114,8 @@ __device__ __forceinline__ void fwd_step(int nval, int w, int lane, const float 
 template <int NG, int G, bool FULL, int... J>
 __device__ __forceinline__ void fwd_steps(std::integer_sequence<int, J...>, int nval, int w, int lane,
                                           const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
-                                          const float (&Ct)[NG], const float2 (&sDD)[kTB][64],
+                                          const float (&Ct)[NG], const float2 (&ddt)[kTB],
                                           float (&sP)[G][kTB][64]) {
-    // the whole tile's (Delta, Delta*u) first, so the LDS latency is paid once
-    float2 ddt[kTB];
-    ((ddt[J] = (FULL || J < nval) ? sDD[J][lane] : make_float2(0.0f, 0.0f)), ...);
     (fwd_step<NG, G, FULL, J>(nval, w, lane, A2, h, Bt, Ct, ddt, sP), ...);
 }
 
@@ -143,15 +140,146 @@ __device__ __forceinline__ void state_steps(std::integer_sequence<int, J...>, in
     (state_step<NG, FULL, J>(nval, A2, h, Bt, ddt, ssum), ...);
 }
 
-// Main forward kernel.  Grid: (B * dblocks, K).  Block: 64 * G threads.
+// Raw inputs of this wave's rows of tile `tile` of the chunk, branch-free:
+// the tile index is clamped to the chunk's last tile and the row to that
+// tile's last valid row, so every address is inside the chunk (rows that do
+// not exist are loaded from a valid row and never used).
+template <typename T, int SPW, bool HAS_Z>
+__device__ __forceinline__ void fetch_rows_clamped(const T* __restrict__ u_chunk, const T* __restrict__ d_chunk,
+                                                   const T* __restrict__ z_chunk, int tile, int ntiles, int t_len,
+                                                   int64_t D, int first_row, int lo, float (&ru)[SPW],
+                                                   float (&rd)[SPW], float (&rz)[SPW]) {
+    const int te = min(tile, ntiles - 1);
+    const int rows_left = t_len - te * kTB;  // >= 1
+    const int64_t base = static_cast<int64_t>(te) * kTB * D;
+    const int D32 = static_cast<int>(D);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int j = min(first_row + i, rows_left - 1);
+        const uint32_t off = static_cast<uint32_t>(j * D32 + lo);
+        ru[i] = load_act(u_chunk + base, off);
+        rd[i] = load_act(d_chunk + base, off);
+        if constexpr (HAS_Z) rz[i] = load_act(z_chunk + base, off);
+    }
+}
+
+// Per-element front end of one row: Delta = softplus(delta + dt_bias) (or
+// delta + dt_bias), Delta * u, the skip term Dskip * u and the gate silu(z).
+template <bool HAS_Z>
+__device__ __forceinline__ void prep_element(float uu, float dd, float zz, float bias, float Dk, int softplus_on,
+                                             float2& dDU, float& skip, float& gate) {
+    const float x = dd + bias;
+    const float sp = softplus(x);
+    const float dt = softplus_on ? sp : x;
+    dDU = make_float2(dt, dt * uu);
+    skip = Dk * uu;
+    gate = HAS_Z ? silu(zz) : 1.0f;
+}
+
+// Registers carried from one tile interval to the next.
 template <typename T, int NG, int G>
+struct FwdRegs {
+    static constexpr int SPW = kTB / G;
+    float ru[SPW], rd[SPW], rz[SPW];                       // raw inputs of the next tile to prepare
+    uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next recurrence tile
+    float skip_c[SPW], gate_c[SPW];                        // rows of the tile in recurrence
+    float skip_p[SPW], gate_p[SPW];                        // rows of the tile being finished
+};
+
+// Uniform facts about one tile interval.
+template <typename T, int NG, int G, bool HAS_Z>
+struct FwdInterval {
+    int k, ntiles, t_len, w, lane, lo;
+    bool dvalid;
+    int row_bytes, softplus_on;
+    float bias, Dk;
+    int64_t D;
+    int N, n0;
+    int64_t row0, last_row;
+    const T* u_chunk;
+    const T* d_chunk;
+    const T* z_chunk;
+    const T* Bm;
+    const T* Cm;
+    T* y_prev;  // first element (row0 - kTB, chan0) of the tile finished in this interval (k > 0)
+};
+
+// One interval: read this interval's LDS first (tile k's (Delta, Delta*u), the
+// partial readouts of tile k - 1), then -- in one straight-line block when
+// FULL -- prepare tile k + 1, issue the loads of tiles k + 1 / k + 2, run the
+// recurrence of tile k and store tile k - 1.  Work that does not exist
+// (tile k + 1 past the end, tile -1) runs on clamped inputs and stores to an
+// out-of-range offset, instead of branching.
+template <bool FULL, typename T, int NG, int G, bool HAS_Z>
+__device__ __forceinline__ void fwd_interval(const FwdInterval<T, NG, G, HAS_Z>& it, int nval,
+                                             const float (&A2)[NG], float (&h)[NG], FwdRegs<T, NG, G>& r,
+                                             float2 (&sDD)[2][kTB][64], float (&sP)[2][G][kTB][64]) {
+    constexpr int SPW = kTB / G;
+    const int cur = it.k & 1, prv = cur ^ 1;
+    const int lane = it.lane, w = it.w;
+    float2 ddt[kTB];
+#pragma unroll
+    for (int j = 0; j < kTB; ++j) ddt[j] = sDD[cur][j][lane];
+    float part[SPW][G];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+        for (int g = 0; g < G; ++g) part[i][g] = sP[prv][g][w * SPW + i][lane];
+    float Bt[NG], Ct[NG];
+    unpack_lane_row<T, NG>(r.qb, Bt);
+    unpack_lane_row<T, NG>(r.qc, Ct);
+    fetch_tile_rows<T, NG>(it.Bm, it.row0 + kTB, it.last_row, it.N, it.n0, lane, r.qb);
+    fetch_tile_rows<T, NG>(it.Cm, it.row0 + kTB, it.last_row, it.N, it.n0, lane, r.qc);
+    float skip_n[SPW], gate_n[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        float2 v;
+        prep_element<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], it.bias, it.Dk, it.softplus_on, v, skip_n[i], gate_n[i]);
+        sDD[prv][w * SPW + i][lane] = v;
+    }
+    fetch_rows_clamped<T, SPW, HAS_Z>(it.u_chunk, it.d_chunk, it.z_chunk, it.k + 2, it.ntiles, it.t_len, it.D,
+                                      w * SPW, it.lo, r.ru, r.rd, r.rz);
+    fwd_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, nval, w, lane, A2, h, Bt, Ct, ddt, sP[cur]);
+    {
+        // tile k - 1 (none when k == 0: every lane stores out of range)
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(it.y_prev, static_cast<uint32_t>(kTB * it.row_bytes));
+        const int D32 = static_cast<int>(it.D);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            float s = 0.0f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) s += part[i][g];
+            const int j = w * SPW + i;
+            const uint32_t off = (it.dvalid && it.k > 0)
+                                     ? static_cast<uint32_t>((j * D32 + lane) * static_cast<int>(sizeof(T)))
+                                     : kNoStore;
+            buffer_store_act((s + r.skip_p[i]) * r.gate_p[i], ry, off, T{});
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        r.skip_p[i] = r.skip_c[i];
+        r.gate_p[i] = r.gate_c[i];
+        r.skip_c[i] = skip_n[i];
+        r.gate_c[i] = gate_n[i];
+    }
+}
+
+// Main forward kernel.  Grid: (B * dblocks, K).  Block: 64 * G threads.
+//
+// Software-pipelined over tiles of kTB steps with one barrier per tile: in
+// the interval of tile k every wave prepares its rows of tile k + 1, runs the
+// recurrence of tile k and finishes its rows of tile k - 1 (LDS double
+// buffered), so the per-element work fills the latency gaps of the
+// recurrence's dependency chains.
+template <typename T, int NG, int G, bool HAS_Z>
 __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
     constexpr int N = NG * G;
     constexpr int SPW = kTB / G;  // rows prepared and finished per wave per tile
     constexpr int W = LaneRow<T, NG>::kWords;
     static_assert(kTB % G == 0, "tile must split evenly over the waves");
-    __shared__ float2 sDD[kTB][64];     // (Delta, Delta * u) per row and channel
-    __shared__ float sP[G][kTB][64];    // partial readout of each state group
+    __shared__ float2 sDD[2][kTB][64];   // (Delta, Delta * u) per row and channel
+    __shared__ float sP[2][G][kTB][64];  // partial readout of each state group
 
     const T* __restrict__ u = static_cast<const T*>(a.u);
     const T* __restrict__ dl = static_cast<const T*>(a.delta);
@@ -189,65 +317,63 @@ __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
     }
     const float bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
     const float Dk = a.Dskip ? a.Dskip[dc] : 0.0f;
+    const int softplus_on = a.softplus;
 
     const int64_t t_begin = c * a.chunk_len;
     const int t_len = static_cast<int>(imin64(L, t_begin + a.chunk_len) - t_begin);
     const int ntiles = (t_len + kTB - 1) / kTB;
     const int64_t row_begin = b * L + t_begin;  // row index of (b, t_begin)
     const int64_t last_row = row_begin + t_len - 1;
+    const int64_t chunk_off = row_begin * D + chan0;  // element (b, t_begin, chan0)
+    const T* u_chunk = u + chunk_off;
+    const T* d_chunk = dl + chunk_off;
+    const T* z_chunk = HAS_Z ? z + chunk_off : nullptr;
+    const int row_bytes = D32 * static_cast<int>(sizeof(T));
 
-    // everything a tile reads from memory is fetched one tile ahead
-    float ru[SPW], rd[SPW], rz[SPW];
-    uint32_t qb[W], qc[W];
-    fetch_rows<T, SPW>(u, dl, z, row_begin * D + chan0, w * SPW, t_len, D32, lo, ru, rd, rz);
-    fetch_tile_rows<T, NG>(Bm, row_begin, last_row, N, n0, lane, qb);
-    fetch_tile_rows<T, NG>(Cm, row_begin, last_row, N, n0, lane, qc);
-
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int nval = min(kTB, t_len - tile * kTB);
-        const int64_t row0 = row_begin + static_cast<int64_t>(tile) * kTB;
-        // ---- Delta, Delta*u, skip term and gate for this wave's rows
-        float skip[SPW], gate[SPW];
+    // ---- prologue: tile 0 prepared, tile 1 raw inputs and tile 0 Bm/Cm in flight
+    FwdRegs<T, NG, G> r;
+    fetch_rows_clamped<T, SPW, HAS_Z>(u_chunk, d_chunk, z_chunk, 0, ntiles, t_len, D, w * SPW, lo, r.ru, r.rd,
+                                      r.rz);
+    fetch_tile_rows<T, NG>(Bm, row_begin, last_row, N, n0, lane, r.qb);
+    fetch_tile_rows<T, NG>(Cm, row_begin, last_row, N, n0, lane, r.qc);
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int j = w * SPW + i;
-            skip[i] = 0.0f;
-            gate[i] = 1.0f;
-            if (j < nval) {
-                const float x = rd[i] + bias;
-                const float dt = a.softplus ? softplus(x) : x;
-                sDD[j][lane] = make_float2(dt, dt * ru[i]);
-                skip[i] = Dk * ru[i];
-                if (z) gate[i] = silu(rz[i]);
-            }
-        }
-        float Bt[NG], Ct[NG];
-        unpack_lane_row<T, NG>(qb, Bt);
-        unpack_lane_row<T, NG>(qc, Ct);
-        if (tile + 1 < ntiles) {  // in flight during the recurrence
-            fetch_rows<T, SPW>(u, dl, z, (row0 + kTB) * D + chan0, w * SPW, t_len - (tile + 1) * kTB, D32, lo,
-                               ru, rd, rz);
-            fetch_tile_rows<T, NG>(Bm, row0 + kTB, last_row, N, n0, lane, qb);
-            fetch_tile_rows<T, NG>(Cm, row0 + kTB, last_row, N, n0, lane, qc);
-        }
-        __syncthreads();
-        // ---- recurrence over the tile for this wave's NG states
+    for (int i = 0; i < SPW; ++i) {
+        float2 v;
+        prep_element<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], bias, Dk, softplus_on, v, r.skip_c[i], r.gate_c[i]);
+        sDD[0][w * SPW + i][lane] = v;  // rows past the chunk end hold finite junk, never used
+    }
+    fetch_rows_clamped<T, SPW, HAS_Z>(u_chunk, d_chunk, z_chunk, 1, ntiles, t_len, D, w * SPW, lo, r.ru, r.rd,
+                                      r.rz);
+    __syncthreads();
+
+    for (int k = 0; k < ntiles; ++k) {
+        const int nval = min(kTB, t_len - k * kTB);
+        const int64_t row0 = row_begin + static_cast<int64_t>(k) * kTB;
+        FwdInterval<T, NG, G, HAS_Z> it{k, ntiles, t_len, w, lane, lo, dvalid, row_bytes, softplus_on, bias, Dk,
+                                        D, N, n0, row0, last_row, u_chunk, d_chunk, z_chunk, Bm, Cm,
+                                        y + (k > 0 ? row0 - kTB : row0) * D + chan0};
         if (nval == kTB)
-            fwd_steps<NG, G, true>(std::make_integer_sequence<int, kTB>{}, kTB, w, lane, A2, h, Bt, Ct, sDD, sP);
+            fwd_interval<true>(it, kTB, A2, h, r, sDD, sP);
         else
-            fwd_steps<NG, G, false>(std::make_integer_sequence<int, kTB>{}, nval, w, lane, A2, h, Bt, Ct, sDD, sP);
+            fwd_interval<false>(it, nval, A2, h, r, sDD, sP);
         __syncthreads();
-        // ---- finish this wave's rows: combine the G partial readouts
-        T* __restrict__ yb = y + row0 * D + chan0;
+    }
+    // ---- epilogue: finish the last tile
+    {
+        const int klast = ntiles - 1;
+        const int nval = t_len - klast * kTB;
+        const int64_t row0 = row_begin + static_cast<int64_t>(klast) * kTB;
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + row0 * D + chan0, kTB * row_bytes);
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int j = w * SPW + i;
-            if (j < nval && dvalid) {
-                float s = 0.0f;
+            float s = 0.0f;
 #pragma unroll
-                for (int g = 0; g < G; ++g) s += sP[g][j][lane];
-                store_act(yb, static_cast<uint32_t>(j * D32 + lane), (s + skip[i]) * gate[i]);
-            }
+            for (int g = 0; g < G; ++g) s += sP[klast & 1][g][j][lane];
+            const uint32_t off = (dvalid && j < nval)
+                                     ? static_cast<uint32_t>((j * D32 + lane) * static_cast<int>(sizeof(T)))
+                                     : kNoStore;
+            buffer_store_act((s + r.skip_p[i]) * r.gate_p[i], ry, off, T{});
         }
     }
     if (a.h_final && dvalid && c == a.chunks - 1) {
@@ -392,16 +518,18 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, hipStream_t st) {
         hipLaunchKernelGGL(scan_carry_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st,
                            a, s.B, s.N);
     }
-    hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G>),
-                       dim3(static_cast<unsigned>(s.B * a.dblocks), static_cast<unsigned>(pl.chunks)),
-                       block, 0, st, a);
+    const dim3 grid(static_cast<unsigned>(s.B * a.dblocks), static_cast<unsigned>(pl.chunks));
+    if (s.z)
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
 // Waves per workgroup (state groups) for N = 16, the state size of every
 // pretrained Mamba model.
 #ifndef MSSM_FWD_WAVES_N16
-#define MSSM_FWD_WAVES_N16 4
+#define MSSM_FWD_WAVES_N16 8
 #endif
 
 template <typename T>
