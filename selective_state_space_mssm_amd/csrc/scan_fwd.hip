@@ -57,11 +57,15 @@ struct FwdKArgs {
     float* h_final;
     float* agg_h;          // (B, K, D, N) chunk end state from zero (chunk 0: from h0)
     float* agg_s;          // (B, K, D) chunk sum of Delta
+    uint32_t* flags;       // (nblk) balanced schedule: 1 once a block's split state is published
+    float* carry;          // (nblk, 64, N) balanced schedule: the published states
     int64_t L, D;
     int64_t chunk_len;
     int32_t dblocks;       // ceil(D / 64)
     int32_t chunks;        // K
     int32_t softplus;
+    int32_t workers;       // 0: one workgroup per (block, chunk); > 0: balanced persistent schedule
+    int32_t nblk;          // B * dblocks
 };
 
 // Raw inputs of this wave's rows of one tile (u, delta, z at (b, t, chan0 +
@@ -265,21 +269,19 @@ __device__ __forceinline__ void fwd_interval(const FwdInterval<T, NG, G, HAS_Z>&
     }
 }
 
-// Main forward kernel.  Grid: (B * dblocks, K).  Block: 64 * G threads.
-//
-// Software-pipelined over tiles of kTB steps with one barrier per tile: in
-// the interval of tile k every wave prepares its rows of tile k + 1, runs the
-// recurrence of tile k and finishes its rows of tile k - 1 (LDS double
-// buffered), so the per-element work fills the latency gaps of the
-// recurrence's dependency chains.
+// Runs steps [t_begin, t_end) of channel block `blk` (batch row b = blk /
+// dblocks, channels chan0 .. chan0 + 63) from the state in h, leaving the
+// final state in h.  Software-pipelined over tiles of kTB steps with one
+// barrier per tile: in the interval of tile k every wave prepares its rows of
+// tile k + 1, runs the recurrence of tile k and finishes its rows of tile
+// k - 1 (LDS double buffered), so the per-element work fills the latency gaps
+// of the recurrence's dependency chains.
 template <typename T, int NG, int G, bool HAS_Z>
-__global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
+__device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t t_begin, int64_t t_end,
+                                            float (&h)[NG], float2 (&sDD)[2][kTB][64],
+                                            float (&sP)[2][G][kTB][64]) {
     constexpr int N = NG * G;
     constexpr int SPW = kTB / G;  // rows prepared and finished per wave per tile
-    constexpr int W = LaneRow<T, NG>::kWords;
-    static_assert(kTB % G == 0, "tile must split evenly over the waves");
-    __shared__ float2 sDD[2][kTB][64];   // (Delta, Delta * u) per row and channel
-    __shared__ float sP[2][G][kTB][64];  // partial readout of each state group
 
     const T* __restrict__ u = static_cast<const T*>(a.u);
     const T* __restrict__ dl = static_cast<const T*>(a.delta);
@@ -290,9 +292,8 @@ __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int w = wave_id();
-    const int64_t b = blockIdx.x / a.dblocks;
-    const int64_t chan0 = static_cast<int64_t>(blockIdx.x % a.dblocks) * 64;
-    const int64_t c = blockIdx.y;
+    const int64_t b = blk / a.dblocks;
+    const int64_t chan0 = static_cast<int64_t>(blk % a.dblocks) * 64;
     const int64_t D = a.D, L = a.L;
     const int D32 = static_cast<int>(D);
     const bool dvalid = chan0 + lane < D;
@@ -300,27 +301,14 @@ __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
     const int64_t dc = chan0 + lo;
     const int n0 = w * NG;
 
-    float A2[NG], h[NG];
+    float A2[NG];
 #pragma unroll
     for (int k = 0; k < NG; ++k) A2[k] = a.A[dc * N + n0 + k] * kLog2e;
-    if (a.h_in) {
-        const float* hi = a.h_in + ((b * a.chunks + c) * D + dc) * N + n0;
-#pragma unroll
-        for (int k = 0; k < NG; ++k) h[k] = hi[k];
-    } else if (a.h0) {
-        const float* hi = a.h0 + (b * D + dc) * N + n0;
-#pragma unroll
-        for (int k = 0; k < NG; ++k) h[k] = hi[k];
-    } else {
-#pragma unroll
-        for (int k = 0; k < NG; ++k) h[k] = 0.0f;
-    }
     const float bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
     const float Dk = a.Dskip ? a.Dskip[dc] : 0.0f;
     const int softplus_on = a.softplus;
 
-    const int64_t t_begin = c * a.chunk_len;
-    const int t_len = static_cast<int>(imin64(L, t_begin + a.chunk_len) - t_begin);
+    const int t_len = static_cast<int>(t_end - t_begin);
     const int ntiles = (t_len + kTB - 1) / kTB;
     const int64_t row_begin = b * L + t_begin;  // row index of (b, t_begin)
     const int64_t last_row = row_begin + t_len - 1;
@@ -330,6 +318,7 @@ __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
     const T* z_chunk = HAS_Z ? z + chunk_off : nullptr;
     const int row_bytes = D32 * static_cast<int>(sizeof(T));
 
+    __syncthreads();  // LDS is reused from a previous segment
     // ---- prologue: tile 0 prepared, tile 1 raw inputs and tile 0 Bm/Cm in flight
     FwdRegs<T, NG, G> r;
     fetch_rows_clamped<T, SPW, HAS_Z>(u_chunk, d_chunk, z_chunk, 0, ntiles, t_len, D, w * SPW, lo, r.ru, r.rd,
@@ -340,7 +329,7 @@ __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
     for (int i = 0; i < SPW; ++i) {
         float2 v;
         prep_element<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], bias, Dk, softplus_on, v, r.skip_c[i], r.gate_c[i]);
-        sDD[0][w * SPW + i][lane] = v;  // rows past the chunk end hold finite junk, never used
+        sDD[0][w * SPW + i][lane] = v;  // rows past the segment end hold finite junk, never used
     }
     fetch_rows_clamped<T, SPW, HAS_Z>(u_chunk, d_chunk, z_chunk, 1, ntiles, t_len, D, w * SPW, lo, r.ru, r.rd,
                                       r.rz);
@@ -376,11 +365,109 @@ __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
             buffer_store_act((s + r.skip_p[i]) * r.gate_p[i], ry, off, T{});
         }
     }
-    if (a.h_final && dvalid && c == a.chunks - 1) {
-        float* hf = a.h_final + (b * D + chan0 + lane) * N + n0;
-#pragma unroll
-        for (int k = 0; k < NG; ++k) hf[k] = h[k];
+}
+
+// Main forward kernel.  Block: 64 * G threads.
+//  * workers == 0 -- grid (B * dblocks, K): one workgroup per channel block
+//    and time chunk (initial state from h_in when K > 1);
+//  * workers > 0 -- balanced persistent schedule, one workgroup per worker:
+//    the (block, tile) sequence is cut into `workers` equal contiguous ranges
+//    of at least one block each.  A block is split between at most two
+//    workers.  Each worker first runs its range's last piece if that piece
+//    ends inside a block (it starts at t = 0, so it depends on nobody) and
+//    publishes the end state; then its whole blocks; then its first piece if
+//    that starts inside a block, from the state the previous worker
+//    published.  Equal work per workgroup, no extra arithmetic.  A worker only
+//    waits on a lower-numbered worker, which never waits before publishing
+//    (workgroups are dispatched in increasing order), so every wait ends.
+template <typename T, int NG, int G, bool HAS_Z>
+__global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
+    constexpr int N = NG * G;
+    static_assert(kTB % G == 0, "tile must split evenly over the waves");
+    __shared__ float2 sDD[2][kTB][64];   // (Delta, Delta * u) per row and channel
+    __shared__ float sP[2][G][kTB][64];  // partial readout of each state group
+    float h[NG];
+    const int lane = threadIdx.x & 63;
+    const int n0 = wave_id() * NG;
+
+    // Segments of this workgroup, in processing order.  Each is (block,
+    // steps [t_begin, t_end), where its initial state comes from, what
+    // happens to its final state).
+    enum { kFromH0 = 0, kFromChunkCarry = 1, kFromPublished = 2 };
+    enum { kKeep = 0, kFinal = 1, kPublish = 2 };
+    int nseg = 1, tail_piece = 0, full_first = 0, b0 = 0, b1 = 0;
+    int64_t t0 = 0, t1 = 0, T_ = 0;
+    if (a.workers > 0) {
+        T_ = (a.L + kTB - 1) / kTB;  // tiles per sequence
+        const int64_t U = static_cast<int64_t>(a.nblk) * T_;
+        const int64_t u0 = U * blockIdx.x / a.workers;
+        const int64_t u1 = U * (blockIdx.x + 1) / a.workers;
+        b0 = static_cast<int>(u0 / T_);
+        t0 = u0 - b0 * T_;                               // first tile of the range, in block b0
+        b1 = static_cast<int>((u1 - 1) / T_);
+        t1 = u1 - static_cast<int64_t>(b1) * T_;        // end tile of the range, in block b1 (1..T)
+        tail_piece = (b1 > b0 && t1 < T_) ? 1 : 0;       // ends inside b1: run it first and publish
+        full_first = t0 == 0 ? b0 : b0 + 1;
+        const int full_last = t1 == T_ ? b1 : b1 - 1;
+        nseg = tail_piece + (full_last - full_first + 1) + (t0 > 0 ? 1 : 0);
     }
+    for (int sg = 0; sg < nseg; ++sg) {
+        int blk, from, to;
+        int64_t t_begin, t_end;
+        if (a.workers == 0) {  // grid: block blockIdx.x, chunk blockIdx.y
+            blk = blockIdx.x;
+            t_begin = static_cast<int64_t>(blockIdx.y) * a.chunk_len;
+            t_end = imin64(a.L, t_begin + a.chunk_len);
+            from = a.h_in ? kFromChunkCarry : kFromH0;
+            to = static_cast<int>(blockIdx.y) == a.chunks - 1 ? kFinal : kKeep;
+        } else if (sg < tail_piece) {  // last piece of the range, ends inside block b1
+            blk = b1; t_begin = 0; t_end = t1 * kTB; from = kFromH0; to = kPublish;
+        } else if (sg < nseg - (t0 > 0 ? 1 : 0)) {  // a whole block
+            blk = full_first + (sg - tail_piece); t_begin = 0; t_end = a.L; from = kFromH0; to = kFinal;
+        } else {  // first piece of the range, starts inside block b0
+            blk = b0; t_begin = t0 * kTB; t_end = a.L; from = kFromPublished; to = kFinal;
+        }
+        const int64_t b = blk / a.dblocks;
+        const int64_t chan0 = static_cast<int64_t>(blk % a.dblocks) * 64;
+        const int64_t dcl = imin64(chan0 + lane, a.D - 1);
+        float* carry_lane = a.carry ? a.carry + (static_cast<int64_t>(blk) * 64 + lane) * N + n0 : nullptr;
+        if (from == kFromH0) {
+#pragma unroll
+            for (int k = 0; k < NG; ++k) h[k] = a.h0 ? a.h0[(b * a.D + dcl) * N + n0 + k] : 0.0f;
+        } else if (from == kFromChunkCarry) {
+            const float* hi = a.h_in + ((b * a.chunks + blockIdx.y) * a.D + dcl) * N + n0;
+#pragma unroll
+            for (int k = 0; k < NG; ++k) h[k] = hi[k];
+        } else {
+            if (threadIdx.x == 0) {
+                while (__hip_atomic_load(a.flags + blk, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u)
+                    __builtin_amdgcn_s_sleep(2);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < NG; ++k)
+                h[k] = __hip_atomic_load(carry_lane + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        fwd_segment<T, NG, G, HAS_Z>(a, blk, t_begin, t_end, h, sDD, sP);
+        if (to == kFinal) {
+            if (a.h_final && chan0 + lane < a.D) {
+                float* hf = a.h_final + (b * a.D + chan0 + lane) * N + n0;
+#pragma unroll
+                for (int k = 0; k < NG; ++k) hf[k] = h[k];
+            }
+        } else if (to == kPublish) {
+#pragma unroll
+            for (int k = 0; k < NG; ++k) carry_lane[k] = h[k];
+            __threadfence();
+            __syncthreads();
+            if (threadIdx.x == 0) __hip_atomic_store(a.flags + blk, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void zero_flags_kernel(uint32_t* flags, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) flags[i] = 0u;
 }
 
 // Chunk aggregates: end state of chunk c started from zero (chunk 0 from h0)
@@ -491,6 +578,10 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(FwdKArgs a, int64_t B, 
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Smallest block count for which the balanced schedule may be chosen (a
+// device partition has at least this many CUs).
+constexpr int64_t kBalancedMinBlocks = 64;
+
 template <typename T, int NG, int G>
 hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, hipStream_t st) {
     FwdKArgs a{};
@@ -518,7 +609,24 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, hipStream_t st) {
         hipLaunchKernelGGL(scan_carry_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st,
                            a, s.B, s.N);
     }
-    const dim3 grid(static_cast<unsigned>(s.B * a.dblocks), static_cast<unsigned>(pl.chunks));
+    dim3 grid(static_cast<unsigned>(s.B * a.dblocks), static_cast<unsigned>(pl.chunks));
+    a.nblk = static_cast<int32_t>(s.B * a.dblocks);
+    if (pl.chunks == 1 && pl.ws_bytes > 0) {
+        // balanced persistent schedule when the blocks do not split evenly over the CUs
+        int dev = 0, ncu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (ncu > 0 && a.nblk >= ncu && a.nblk % ncu != 0) {
+            char* ws = static_cast<char*>(s.workspace);
+            a.workers = ncu;
+            a.flags = reinterpret_cast<uint32_t*>(ws);
+            a.carry = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(a.nblk) * sizeof(uint32_t)));
+            hipLaunchKernelGGL(zero_flags_kernel, dim3(static_cast<unsigned>((a.nblk + 255) / 256)), dim3(256), 0,
+                               st, a.flags, a.nblk);
+            grid = dim3(static_cast<unsigned>(ncu));
+        }
+    }
     if (s.z)
         hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true>), grid, block, 0, st, a);
     else
@@ -551,6 +659,12 @@ hipError_t dispatch_n(const ScanArgs& s, const FwdPlan& pl, hipStream_t st) {
 FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N) {
     FwdPlan p{1, L, 0};
     const int64_t blocks = B * ((D + 63) / 64);
+    if (blocks >= kBalancedMinBlocks) {
+        // room for the balanced schedule (used when the blocks do not split
+        // evenly over the CUs): a flag and a published 64 x N state per block
+        p.ws_bytes = align256(static_cast<size_t>(blocks) * sizeof(uint32_t)) +
+                     align256(static_cast<size_t>(blocks) * 64 * N * sizeof(float));
+    }
     // Cut time only when the channel blocks alone cannot occupy the chip.
     constexpr int64_t kTargetBlocks = 1024;
     constexpr int64_t kMinChunk = 1024;

@@ -91,6 +91,23 @@ def test_chunked_carry_schedule(mssm, dtype):
     check(mssm, workloads.custom(B, L, D, 16, dtype, seed=21), h0=True)
 
 
+@pytest.mark.parametrize("shape,dtype", [((5, 100, 3840), "f32"), ((3, 333, 5760), "bf16"), ((4, 37, 4160), "f32")])
+def test_balanced_schedule(mssm, shape, dtype):
+    # more channel blocks than CUs but not a multiple of them: the persistent
+    # balanced schedule splits blocks between workgroups mid-sequence and hands
+    # the state over through the workspace (on a 256-CU MI355X: 300, 270 and
+    # 260 blocks)
+    B, L, D = shape
+    assert mssm.fwd_workspace_bytes(B, L, D, 16) > 0
+    check(mssm, workloads.custom(B, L, D, 16, dtype, seed=B * L), h0=True)
+    # the published states are reset per call: a second call gives the same bits
+    w = workloads.custom(B, L, D, 16, dtype, seed=B * L)
+    t = gpu_inputs(workloads.make_inputs(w))
+    y1, h1 = run_gpu_fwd(mssm, t)
+    y2, h2 = run_gpu_fwd(mssm, t)
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
 def test_130m_layer_full(mssm):
     ey, eh = check(mssm, workloads.WORKLOADS["130m"])
     print(f"130M: y err {ey:.2e}, h_final err {eh:.2e}")
