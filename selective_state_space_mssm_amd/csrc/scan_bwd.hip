@@ -15,19 +15,28 @@
 // performance section), and the adjoint runs natively in reverse time, with
 // no flipped copies (the reverse scan listed in that page's to-do section).
 //
-// Three kernels:
-//  1. checkpoint: forward over the sequence, storing the state at the start
-//     of every TB-step tile (B, tiles, D, N);
-//  2. reverse: tiles in reverse order; per tile the states are recomputed
-//     from the checkpoint into VGPRs, then the adjoint runs backwards over the
-//     tile.  Same mapping as the forward (lane = channel, wave = state group,
-//     Delta shared through LDS).  dB/dC are summed over the wave's 64 channels
-//     with a cross-lane transpose-reduce and written as per-block partials;
-//  3. reduce: fixed-order sums of the partials (dB, dC over channel blocks;
-//     dA, dD, ddt_bias over the batch).  No atomics: results are bitwise
-//     reproducible.
+// Three launches:
+//  1. pre-pass (scan_fwd.hip, the forward kernel in pre-pass mode): the
+//     forward recurrence storing the state before every 16-step tile
+//     (B, tiles, D, N), sbar (B, L, D) float32 and dz;
+//  2. reverse (this file): one workgroup per 64-channel block walks the tiles
+//     from last to first.  Lane = channel, wave = state group, as in the
+//     forward.  Per tile it recomputes the tile's states and decays from the
+//     checkpoint into VGPRs, then runs the adjoint backwards over the tile.
+//     Bm/Cm reach the lanes by DPP row broadcast; (Delta, Delta*u, sbar) is
+//     shared by the waves through LDS.  Each wave leaves its partial sums over
+//     its states of lam*Bm and A*lam*a*h_prev in LDS, and in the next interval
+//     every wave finishes its share of the tile's rows (du, ddelta).  dB/dC
+//     are summed over the wave's 64 channels by a transpose-reduce across
+//     lanes (16 values in 35 instructions) and stored per channel block;
+//  3. reduce: fixed-order sums of the per-block dB/dC partials and of the
+//     per-batch-row dA/dD/ddt_bias partials.  No atomics: results are
+//     bitwise reproducible.
 #include "device_common.h"
 #include "launch.h"
+
+#include <algorithm>
+#include <utility>
 
 namespace mssm {
 namespace {
@@ -37,27 +46,23 @@ constexpr int kTB = 16;  // tile length (checkpoint spacing, VGPR history depth)
 struct BwdKArgs {
     const void* u;
     const void* delta;
-    const void* z;
     const void* Bm;
     const void* Cm;
-    const void* dy;
     const float* A;
     const float* Dskip;
     const float* dt_bias;
-    const float* h0;
     const float* dh_final;
+    const float* ckpt;   // (B, tiles, D, N) state before every tile (pre-pass)
+    const float* sbar;   // (B, L, D) (pre-pass)
     void* du;
     void* ddelta;
-    void* dz;
     void* dB;
     void* dC;
     float* dA;
     float* dD;
     float* ddt_bias;
     float* dh0;
-    float* ckpt;   // (B, tiles, D, N)
-    float* pB;     // (B, L, dblocks, N)
-    float* pC;     // (B, L, dblocks, N)
+    float* pBC;    // (B, L, dblocks, 2, N): per channel block, dB partial then dC partial
     float* pA;     // (B, D, N)
     float* pD;     // (B, D)
     float* pbias;  // (B, D)
@@ -67,47 +72,18 @@ struct BwdKArgs {
     int32_t softplus;
 };
 
-template <int NG>
-__device__ __forceinline__ void load_row(const float* __restrict__ p, float (&v)[NG]) {
-#pragma unroll
-    for (int k = 0; k < NG; ++k) v[k] = p[k];
-}
-template <int NG>
-__device__ __forceinline__ void load_row(const uint16_t* __restrict__ p, float (&v)[NG]) {
-    if constexpr (NG % 2 == 0) {
-        const uint32_t* __restrict__ q = reinterpret_cast<const uint32_t*>(p);
-#pragma unroll
-        for (int k = 0; k < NG / 2; ++k) {
-            const uint32_t w = q[k];
-            v[2 * k] = bf16_lo(w);
-            v[2 * k + 1] = bf16_hi(w);
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < NG; ++k) v[k] = load_act(p, k);
-    }
-}
-
-// ---- cross-lane sums -------------------------------------------------------
+// ---- cross-lane sums -------------------------------------------------------------
 // DPP controls (gfx9): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
-// row_half_mirror, row_mirror.
+// row_half_mirror (lane i <-> 7 - i within 8 lanes), row_ror:8 (i <-> i + 8
+// within a 16-lane row).  All four are involutions.
 constexpr int kDppQuadSwap1 = 0xB1;
 constexpr int kDppQuadSwap2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
-constexpr int kDppMirror = 0x140;
+constexpr int kDppRor8 = 0x128;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 16 lanes of every row; every lane of the row gets the sum.
-__device__ __forceinline__ float row_sum16(float v) {
-    v += dpp<kDppQuadSwap1>(v);
-    v += dpp<kDppQuadSwap2>(v);
-    v += dpp<kDppHalfMirror>(v);
-    v += dpp<kDppMirror>(v);
-    return v;
 }
 
 // v_permlane32_swap: lanes 32..63 of `a` <-> lanes 0..31 of `b`.
@@ -116,369 +92,500 @@ __device__ __forceinline__ void swap32(float& a, float& b) {
     a = __uint_as_float(r[0]);
     b = __uint_as_float(r[1]);
 }
-// v_permlane16_swap: odd rows of `a` <-> even rows of `b`.
+// v_permlane16_swap: odd 16-lane rows of `a` <-> even rows of `b`.
 __device__ __forceinline__ void swap16(float& a, float& b) {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
     a = __uint_as_float(r[0]);
     b = __uint_as_float(r[1]);
 }
 
-// Full 64-lane sum of one value (every lane gets it).
-__device__ __forceinline__ float wave_sum(float v) {
-    v = row_sum16(v);
-    float w = v;
-    swap16(v, w);
-    v += w;
-    w = v;
-    swap32(v, w);
-    return v + w;
+// Sums over the 64 lanes of 16 values at once, in 35 instructions.  Each
+// stage pairs the registers, exchanges half of the lanes of each pair with a
+// lane permutation and adds, so the register count halves while every
+// partial folds twice as many lanes: lanes 32 apart and 16 apart through the
+// permlane swaps, then 8 and 4 apart inside a row through DPP with a lane
+// select of which register is sent; two quad adds finish.  On return the
+// four lanes 4g .. 4g + 3 hold the full sum of v[bitrev4(g)].
+__device__ __forceinline__ float wave_sum16(float (&v)[16]) {
+    const int lane = threadIdx.x & 63;
+    float s[8], t[4], q[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float x = v[2 * i], y = v[2 * i + 1];
+        swap32(x, y);
+        s[i] = x + y;  // lanes 0-31: v[2i] folded over 32 lanes; 32-63: v[2i+1]
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float x = s[2 * i], y = s[2 * i + 1];
+        swap16(x, y);
+        t[i] = x + y;
+    }
+    const bool hi8 = (lane & 8) != 0, hi4 = (lane & 4) != 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float x = t[2 * i], y = t[2 * i + 1];
+        const float send = hi8 ? x : y, keep = hi8 ? y : x;
+        q[i] = keep + dpp<kDppRor8>(send);
+    }
+    const float send = hi4 ? q[0] : q[1], keep = hi4 ? q[1] : q[0];
+    float r = keep + dpp<kDppHalfMirror>(send);
+    r += dpp<kDppQuadSwap1>(r);
+    r += dpp<kDppQuadSwap2>(r);
+    return r;
 }
 
-// Sum over the 64 lanes of four values at once (transpose-reduce).  On
-// return, every lane of row r (= lane / 16) holds the sum of v[perm(r)] with
-// perm = {0, 2, 1, 3}.
-__device__ __forceinline__ float wave_sum4(float v0, float v1, float v2, float v3) {
-    swap32(v0, v1);  // v0 = [v0 lo, v1 lo], v1 = [v0 hi, v1 hi]
-    swap32(v2, v3);
-    float s01 = v0 + v1;  // lanes 0-31: v0 halves summed; lanes 32-63: v1
-    float s23 = v2 + v3;
-    swap16(s01, s23);     // rows: s01 = [v0 r0, v2 r0, v1 r2, v3 r2], s23 = [v0 r1, v2 r1, v1 r3, v3 r3]
-    return row_sum16(s01 + s23);
+__device__ __forceinline__ int bitrev4(int g) {
+    return ((g & 1) << 3) | ((g & 2) << 1) | ((g & 4) >> 1) | ((g & 8) >> 3);
 }
 
-// ---- kernel 1: checkpoints ---------------------------------------------------
+// This wave's Bm (or Cm) values of one tile: lane l loads step l % 16 (row
+// clamped to the sequence's last row).
+template <typename T, int NG>
+__device__ __forceinline__ void fetch_tile_rows(const T* __restrict__ M, int64_t row0, int64_t last_row, int N,
+                                                int n0, int lane, uint32_t (&q)[LaneRow<T, NG>::kWords]) {
+    const int64_t r = imin64(row0 + (lane & (kTB - 1)), last_row);
+    load_lane_row<T, NG>(M + r * N + n0, q);
+}
+
+// Raw u, delta, sbar of this wave's rows of tile `tile` (tile clamped to >= 0,
+// row to the sequence's last row: every address is inside the tensors).
+template <typename T, int SPW>
+__device__ __forceinline__ void fetch_rows(const T* __restrict__ u_b, const T* __restrict__ d_b,
+                                           const float* __restrict__ s_b, int tile, int L32, int D32,
+                                           int first_row, int lo, float (&ru)[SPW], float (&rd)[SPW],
+                                           float (&rs)[SPW]) {
+    const int t0 = max(tile, 0) * kTB;
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int t = min(t0 + first_row + i, L32 - 1);
+        const int64_t off = static_cast<int64_t>(t) * D32 + lo;
+        ru[i] = load_act(u_b, off);
+        rd[i] = load_act(d_b, off);
+        rs[i] = s_b[off];
+    }
+}
+
+// What a wave keeps of one of its rows from preparing it until finishing it.
+struct RowKeep {
+    float u, sig, dt, sb;  // u, dDelta/dx (sigmoid(x) with softplus, else 1), Delta, sbar
+};
+
+// Per-element front end of this wave's rows of one tile: (Delta, Delta*u,
+// sbar) to LDS for all waves.  Lanes past the last channel get u = sbar = 0,
+// so they add nothing to the dB/dC sums over the 64 lanes.
+template <int SPW>
+__device__ __forceinline__ void prep_rows(const float (&ru)[SPW], const float (&rd)[SPW], const float (&rs)[SPW],
+                                          float bias, int softplus_on, bool dvalid, int w, int lane,
+                                          float4 (&dst)[kTB][64], RowKeep (&keep)[SPW]) {
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const float x = rd[i] + bias;
+        const float dt = softplus_on ? softplus(x) : x;
+        const float sg = softplus_on ? sigmoid(x) : 1.0f;
+        const float uu = dvalid ? ru[i] : 0.0f;
+        const float sb = dvalid ? rs[i] : 0.0f;
+        dst[w * SPW + i][lane] = make_float4(dt, dt * uu, sb, 0.0f);
+        keep[i] = RowKeep{uu, sg, dt, sb};
+    }
+}
+
+// Finish this wave's rows of a tile from the G partial sums in LDS: du and
+// ddelta to memory (rows past `nvalid` dropped by the buffer range check),
+// the dD and ddt_bias sums in registers.
+template <typename T, int SPW, int G>
+__device__ __forceinline__ void finish_rows(const float2 (&sLQ)[G][kTB][64], const RowKeep (&kp)[SPW], int w,
+                                            int lane, bool dvalid, int nvalid, float Dk, T* du_tile,
+                                            T* dd_tile, int D32, float& accD, float& accBias) {
+    const uint32_t bytes = static_cast<uint32_t>(kTB) * static_cast<uint32_t>(D32) * sizeof(T);
+    const __amdgpu_buffer_rsrc_t rdu = make_rsrc(du_tile, bytes);
+    const __amdgpu_buffer_rsrc_t rdd = make_rsrc(dd_tile, bytes);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int j = w * SPW + i;
+        float lb = 0.0f, lq = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float2 p = sLQ[g][j][lane];
+            lb += p.x;
+            lq += p.y;
+        }
+        const float gu = __builtin_fmaf(kp[i].sb, Dk, kp[i].dt * lb);
+        const float gx = __builtin_fmaf(kp[i].u, lb, lq) * kp[i].sig;
+        const bool ok = dvalid && j < nvalid;
+        const uint32_t off =
+            ok ? (static_cast<uint32_t>(j) * static_cast<uint32_t>(D32) + static_cast<uint32_t>(lane)) * sizeof(T)
+               : kNoStore;
+        buffer_store_act(gu, rdu, off, T{});
+        buffer_store_act(gx, rdd, off, T{});
+        if (ok) {
+            accD = __builtin_fmaf(kp[i].sb, kp[i].u, accD);
+            accBias += gx;
+        }
+    }
+}
+
+// Recompute of step J: the state after step J and the step's decay.
+template <int NG, bool FULL, int J>
+__device__ __forceinline__ void rec_step(int nval, const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
+                                         const float4 (&xt)[kTB], float (&hist)[kTB][NG],
+                                         float (&ahist)[kTB][NG]) {
+    if (FULL || J < nval) {
+        const float4 x = xt[J];
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            const float a = fast_exp2(x.x * A2[k]);
+            h[k] = __builtin_fmaf(a, h[k], row_bcast<J>(Bt[k]) * x.y);
+            ahist[J][k] = a;
+            hist[J][k] = h[k];
+        }
+    } else {  // past the end (ragged last tile): no state, decay 1 as after the last step
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            ahist[J][k] = 1.0f;
+            hist[J][k] = 0.0f;
+        }
+    }
+}
+
+template <int NG, bool FULL, int... J>
+__device__ __forceinline__ void rec_steps(std::integer_sequence<int, J...>, int nval, const float (&A2)[NG],
+                                          float (&h)[NG], const float (&Bt)[NG], const float4 (&xt)[kTB],
+                                          float (&hist)[kTB][NG], float (&ahist)[kTB][NG]) {
+    (rec_step<NG, FULL, J>(nval, A2, h, Bt, xt, hist, ahist), ...);
+}
+
+// State that the reverse steps of one tile read and update.
+template <int NG, int G>
+struct RevCtx {
+    const float* Aval;       // [NG]
+    const float* Bt;         // [NG]
+    const float* Ct;         // [NG]
+    const float4* xt;        // [kTB]
+    const float (*hist)[NG];
+    const float (*ahist)[NG];
+    const float* hin;        // [NG] state before the tile
+    const float* anext;      // [NG] decay of the step after the tile (1 past the end)
+    float2 (*sLQ)[kTB][64];  // [G]
+    __amdgpu_buffer_rsrc_t rp;  // this block's dB/dC partial rows of the tile
+    int nval, w, lane, dblocks, N, n0;
+};
+
+// Reverse step J for this wave's NG states: the adjoint, its partial sums
+// for du/ddelta (to LDS), dA, and the step's dB/dC terms into the 16-value
+// batch `vals`; when the batch is complete (its lowest step), its sums over
+// the wave's channels are stored.
+template <int NG, int G, bool FULL, int J>
+__device__ __forceinline__ void rev_step(const RevCtx<NG, G>& c, float (&lam)[NG], float (&dA)[NG],
+                                         float (&vals)[16]) {
+    constexpr int S = 16 / (2 * NG);  // steps per batch
+    constexpr int slot = (J % S) * 2 * NG;
+    if (FULL || J < c.nval) {
+        const float4 x = c.xt[J];  // (Delta, Delta*u, sbar, -)
+        float lb = 0.0f, lq = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            // decay of the next step in time (1 past the end: the ragged tile's
+            // missing steps hold 1)
+            float an;
+            if constexpr (J + 1 < kTB) an = c.ahist[J + 1][k];
+            else an = c.anext[k];
+            lam[k] = __builtin_fmaf(an, lam[k], row_bcast<J>(c.Ct[k]) * x.z);
+            lb = k == 0 ? row_bcast<J>(c.Bt[0]) * lam[0] : fmac_row_bcast<J>(lb, c.Bt[k], lam[k]);
+            float hp;
+            if constexpr (J > 0) hp = c.hist[J - 1][k];
+            else hp = c.hin[k];
+            const float q = lam[k] * c.ahist[J][k] * hp;
+            lq = __builtin_fmaf(c.Aval[k], q, lq);
+            dA[k] = __builtin_fmaf(x.x, q, dA[k]);
+            vals[slot + k] = lam[k] * x.y;           // this channel's dB term
+            vals[slot + NG + k] = x.z * c.hist[J][k];  // this channel's dC term
+        }
+        c.sLQ[c.w][J][c.lane] = make_float2(lb, lq);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NG; ++k) vals[slot + k] = vals[slot + NG + k] = 0.0f;
+    }
+    if constexpr (J % S == 0) {
+        const float sum = wave_sum16(vals);
+        const int v = bitrev4(c.lane >> 2);
+        const int step = J + v / (2 * NG);
+        const int which = (v / NG) & 1;  // 0: dB, 1: dC
+        const int k = v % NG;
+        const bool store = (c.lane & 3) == 0 && step < c.nval;
+        const uint32_t off =
+            ((static_cast<uint32_t>(step) * c.dblocks * 2u + which) * c.N + c.n0 + k) * 4u;
+        buffer_store_act(sum, c.rp, store ? off : kNoStore, 0.0f);
+    }
+}
+
+template <int NG, int G, bool FULL, int... I>
+__device__ __forceinline__ void rev_steps(std::integer_sequence<int, I...>, const RevCtx<NG, G>& c,
+                                          float (&lam)[NG], float (&dA)[NG]) {
+    float vals[16];
+    (rev_step<NG, G, FULL, kTB - 1 - I>(c, lam, dA, vals), ...);  // J = 15 .. 0: backwards in time
+}
+
+// Registers carried from one reverse interval to the next.
 template <typename T, int NG, int G>
-__global__ __launch_bounds__(64 * G) void bwd_ckpt_kernel(BwdKArgs a) {
+struct RevRegs {
+    static constexpr int SPW = kTB / G;
+    float ru[SPW], rd[SPW], rs[SPW];  // raw u, delta, sbar of the next tile to prepare
+    uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next tile
+    float hin_next[NG];               // checkpoint of the next tile
+    RowKeep keep_c[SPW], keep_p[SPW];  // rows of the tile in flight / of the tile to finish
+    float lam[NG], dA[NG], anext[NG];
+    float accD, accBias;
+};
+
+// Uniform facts of one workgroup (and the lane's channel).
+template <typename T>
+struct RevBlock {
+    int w, lane, lo, n0, D32, L32, dblk, dblocks, ntiles, softplus_on;
+    bool dvalid;
+    float bias, Dk;
+    int64_t row_b, last_row, ck_stride;
+    const T* u_b;
+    const T* d_b;
+    const float* s_b;
+    const T* Bm;
+    const T* Cm;
+    T* du_b;
+    T* dd_b;
+    const float* ck_b;
+    float* pBC;
+};
+
+// Interval of tile k (tiles - 1 .. 0), between two barriers:
+//   A. read tile k's (Delta, Delta*u, sbar) from LDS; finish tile k + 1's
+//      rows from the partial sums its reverse steps left; recompute tile k's
+//      states from its checkpoint; prepare tile k - 1's rows into the other
+//      LDS buffer; issue the loads of tile k - 1's Bm/Cm/checkpoint and of
+//      tile k - 2's raw rows;
+//   B. (after a barrier: the partial sums of tile k + 1 are consumed) the
+//      reverse steps of tile k.
+// FULL: all 16 steps of the tile exist (every tile but a ragged last one).
+template <bool FULL, typename T, int NG, int G>
+__device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int nval, const float (&A2)[NG],
+                                             const float (&Aval)[NG], RevRegs<T, NG, G>& r,
+                                             float4 (&sX)[2][kTB][64], float2 (&sLQ)[G][kTB][64]) {
     constexpr int N = NG * G;
     constexpr int SPW = kTB / G;
-    __shared__ float sD[kTB][64];
-    __shared__ float sDU[kTB][64];
-    const T* __restrict__ u = static_cast<const T*>(a.u);
-    const T* __restrict__ dl = static_cast<const T*>(a.delta);
-    const T* __restrict__ Bm = static_cast<const T*>(a.Bm);
-    const int lane = threadIdx.x & 63;
-    const int w = wave_id();
-    const int64_t b = blockIdx.x / a.dblocks;
-    const int64_t dblk = blockIdx.x % a.dblocks;
-    const int64_t D = a.D, L = a.L;
-    const int64_t d = dblk * 64 + lane;
-    const bool dvalid = d < D;
-    const int64_t dc = dvalid ? d : D - 1;
-    const int n0 = w * NG;
-    float A2[NG], h[NG];
+    const int cur = k & 1, prv = cur ^ 1;
+    const int w = bk.w, lane = bk.lane;
+    // ---- A
+    float4 xt[kTB];
 #pragma unroll
-    for (int k = 0; k < NG; ++k) {
-        A2[k] = a.A[dc * N + n0 + k] * kLog2e;
-        h[k] = a.h0 ? a.h0[(b * D + dc) * N + n0 + k] : 0.0f;
+    for (int j = 0; j < kTB; ++j) xt[j] = sX[cur][j][lane];
+    if (k + 1 < bk.ntiles) {
+        const int64_t off = static_cast<int64_t>(k + 1) * kTB * bk.D32;
+        finish_rows<T, SPW, G>(sLQ, r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32 - (k + 1) * kTB), bk.Dk,
+                               bk.du_b + off, bk.dd_b + off, bk.D32, r.accD, r.accBias);
     }
-    const float bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
-    for (int64_t tile = 0; tile < a.tiles; ++tile) {
-        const int64_t tb = tile * kTB;
-        if (dvalid) {
-            float* cp = a.ckpt + ((b * a.tiles + tile) * D + d) * N + n0;
+    float Bt[NG], Ct[NG], hin[NG];
+    unpack_lane_row<T, NG>(r.qb, Bt);
+    unpack_lane_row<T, NG>(r.qc, Ct);
 #pragma unroll
-            for (int k = 0; k < NG; ++k) cp[k] = h[k];
-        }
-        if (tile == a.tiles - 1) break;  // the last tile's end state is not needed
-        const int nval = kTB;            // every tile but the last is full
+    for (int q = 0; q < NG; ++q) hin[q] = r.hin_next[q];
+    {
+        const int tp = max(k - 1, 0);
+        const int64_t rowp = bk.row_b + static_cast<int64_t>(tp) * kTB;
+        fetch_tile_rows<T, NG>(bk.Bm, rowp, bk.last_row, N, bk.n0, lane, r.qb);
+        fetch_tile_rows<T, NG>(bk.Cm, rowp, bk.last_row, N, bk.n0, lane, r.qc);
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int j = w * SPW + i;
-            const int64_t e = (b * L + tb + j) * D + dc;
-            const float x = load_act(dl, e) + bias;
-            const float dt = a.softplus ? softplus(x) : x;
-            sD[j][lane] = dt;
-            sDU[j][lane] = dt * load_act(u, e);
-        }
-        __syncthreads();
-        const T* __restrict__ brow = Bm + (b * L + tb) * N + n0;
+        for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tp * bk.ck_stride + q];
+    }
+    float hist[kTB][NG], ahist[kTB][NG];
+    {
+        float h[NG];
 #pragma unroll
-        for (int j = 0; j < nval; ++j) {
-            float bv[NG];
-            load_row<NG>(brow + j * N, bv);
-            const float dt = sD[j][lane];
-            const float du = sDU[j][lane];
+        for (int q = 0; q < NG; ++q) h[q] = hin[q];
+        rec_steps<NG, FULL>(std::make_integer_sequence<int, kTB>{}, nval, A2, h, Bt, xt, hist, ahist);
+    }
+    RowKeep keep_n[SPW];
+    prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, w, lane, sX[prv], keep_n);  // k == 0: unused
+    fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, k - 2, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
+    __syncthreads();
+    // ---- B
+    {
+        const int64_t row0 = bk.row_b + static_cast<int64_t>(k) * kTB;
+        RevCtx<NG, G> c{Aval, Bt, Ct, xt, hist, ahist, hin, r.anext, sLQ,
+                        make_rsrc(bk.pBC + (row0 * bk.dblocks + bk.dblk) * 2 * N,
+                                  static_cast<uint32_t>(kTB) * bk.dblocks * 2u * N * 4u),
+                        nval, w, lane, bk.dblocks, N, bk.n0};
+        rev_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, c, r.lam, r.dA);
+    }
 #pragma unroll
-            for (int k = 0; k < NG; ++k) h[k] = __builtin_fmaf(fast_exp2(dt * A2[k]), h[k], du * bv[k]);
-        }
-        __syncthreads();
+    for (int q = 0; q < NG; ++q) r.anext[q] = ahist[0][q];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        r.keep_p[i] = r.keep_c[i];
+        r.keep_c[i] = keep_n[i];
     }
 }
 
-// ---- kernel 2: reverse adjoint -------------------------------------------------
+// Reverse kernel.  Grid: B * dblocks workgroups of 64 * G threads.
 template <typename T, int NG, int G>
 __global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
     constexpr int N = NG * G;
     constexpr int SPW = kTB / G;
-    __shared__ float sD[kTB][64];
-    __shared__ float sDU[kTB][64];
-    __shared__ float sS[kTB][64];       // sbar
-    __shared__ float sP[G][kTB][64];    // partial readout, then partial sum lam*Bm
-    __shared__ float sQ[G][kTB][64];    // partial sum A * lam * a * h_prev
+    static_assert(kTB % G == 0 && 16 % (2 * NG) == 0, "tile and batch must split evenly");
+    __shared__ float4 sX[2][kTB][64];   // (Delta, Delta*u, sbar, -) per row and channel
+    __shared__ float2 sLQ[G][kTB][64];  // per state group: (sum lam*Bm, sum A*lam*a*h_prev)
     __shared__ float sRed[2][G][64];
 
-    const T* __restrict__ u = static_cast<const T*>(a.u);
-    const T* __restrict__ dl = static_cast<const T*>(a.delta);
-    const T* __restrict__ z = static_cast<const T*>(a.z);
-    const T* __restrict__ dy = static_cast<const T*>(a.dy);
-    const T* __restrict__ Bm = static_cast<const T*>(a.Bm);
-    const T* __restrict__ Cm = static_cast<const T*>(a.Cm);
-
-    const int lane = threadIdx.x & 63;
-    const int w = wave_id();
+    RevBlock<T> bk;
+    bk.lane = threadIdx.x & 63;
+    bk.w = wave_id();
     const int64_t b = blockIdx.x / a.dblocks;
-    const int64_t dblk = blockIdx.x % a.dblocks;
+    bk.dblk = static_cast<int>(blockIdx.x % a.dblocks);
+    bk.dblocks = a.dblocks;
+    const int64_t chan0 = static_cast<int64_t>(bk.dblk) * 64;
     const int64_t D = a.D, L = a.L;
-    const int64_t d = dblk * 64 + lane;
-    const bool dvalid = d < D;
-    const int64_t dc = dvalid ? d : D - 1;
-    const int n0 = w * NG;
+    bk.D32 = static_cast<int>(D);
+    bk.L32 = static_cast<int>(L);
+    bk.dvalid = chan0 + bk.lane < D;
+    bk.lo = bk.dvalid ? bk.lane : static_cast<int>(D - 1 - chan0);
+    const int64_t dc = chan0 + bk.lo;
+    bk.n0 = bk.w * NG;
+    bk.ntiles = static_cast<int>(a.tiles);
+    bk.softplus_on = a.softplus;
+    bk.bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
+    bk.Dk = a.Dskip ? a.Dskip[dc] : 0.0f;
+    bk.row_b = b * L;
+    bk.last_row = bk.row_b + L - 1;
+    bk.ck_stride = D * N;
+    bk.u_b = static_cast<const T*>(a.u) + bk.row_b * D + chan0;
+    bk.d_b = static_cast<const T*>(a.delta) + bk.row_b * D + chan0;
+    bk.s_b = a.sbar + bk.row_b * D + chan0;
+    bk.Bm = static_cast<const T*>(a.Bm);
+    bk.Cm = static_cast<const T*>(a.Cm);
+    bk.du_b = static_cast<T*>(a.du) + bk.row_b * D + chan0;
+    bk.dd_b = static_cast<T*>(a.ddelta) + bk.row_b * D + chan0;
+    bk.ck_b = a.ckpt + (b * a.tiles * D + dc) * N + bk.n0;
+    bk.pBC = a.pBC;
+    const int w = bk.w, lane = bk.lane, n0 = bk.n0;
 
-    float A2[NG], Aval[NG], lam[NG], dAacc[NG], anext[NG];
+    float A2[NG], Aval[NG];
+    RevRegs<T, NG, G> r;
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
         Aval[k] = a.A[dc * N + n0 + k];
         A2[k] = Aval[k] * kLog2e;
-        lam[k] = (a.dh_final && dvalid) ? a.dh_final[(b * D + d) * N + n0 + k] : 0.0f;
-        dAacc[k] = 0.0f;
-        anext[k] = 1.0f;  // no step after L-1
+        r.lam[k] = (a.dh_final && bk.dvalid) ? a.dh_final[(b * D + dc) * N + n0 + k] : 0.0f;
+        r.dA[k] = 0.0f;
+        r.anext[k] = 1.0f;  // no step after the last one
     }
-    const float bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
-    const float Dk = a.Dskip ? a.Dskip[dc] : 0.0f;
-    float accD = 0.0f, accBias = 0.0f;
+    r.accD = r.accBias = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) r.keep_p[i] = RowKeep{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int64_t tile = a.tiles - 1; tile >= 0; --tile) {
-        const int64_t tb = tile * kTB;
-        const int nval = static_cast<int>(imin64(kTB, L - tb));
-        // ---- rows of this wave: inputs and step sizes
-        float ru[SPW], rx[SPW], rdy[SPW], rz[SPW], rdt[SPW];
+    // ---- prologue: last tile prepared; its Bm/Cm/checkpoint and the next raw rows in flight
+    {
+        const int tl = bk.ntiles - 1;
+        const int64_t rowl = bk.row_b + static_cast<int64_t>(tl) * kTB;
+        fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
+        fetch_tile_rows<T, NG>(bk.Bm, rowl, bk.last_row, N, n0, lane, r.qb);
+        fetch_tile_rows<T, NG>(bk.Cm, rowl, bk.last_row, N, n0, lane, r.qc);
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int j = w * SPW + i;
-            ru[i] = rx[i] = rdy[i] = rz[i] = rdt[i] = 0.0f;
-            if (j < nval) {
-                const int64_t e = (b * L + tb + j) * D + dc;
-                ru[i] = load_act(u, e);
-                rx[i] = load_act(dl, e) + bias;
-                rdy[i] = dvalid ? load_act(dy, e) : 0.0f;
-                if (z) rz[i] = load_act(z, e);
-                rdt[i] = a.softplus ? softplus(rx[i]) : rx[i];
-                sD[j][lane] = rdt[i];
-                sDU[j][lane] = rdt[i] * ru[i];
-            }
-        }
-        __syncthreads();
-        // ---- recompute the tile's states from the checkpoint
-        float hin[NG], hist[kTB][NG], ahist[kTB][NG];
-        {
-            const float* cp = a.ckpt + ((b * a.tiles + tile) * D + dc) * N + n0;
-#pragma unroll
-            for (int k = 0; k < NG; ++k) hin[k] = cp[k];
-        }
-        const T* __restrict__ brow = Bm + (b * L + tb) * N + n0;
-        const T* __restrict__ crow = Cm + (b * L + tb) * N + n0;
-        {
-            float h[NG];
-#pragma unroll
-            for (int k = 0; k < NG; ++k) h[k] = hin[k];
-#pragma unroll
-            for (int j = 0; j < kTB; ++j) {
-                if (j < nval) {
-                    float bv[NG], cv[NG];
-                    load_row<NG>(brow + j * N, bv);
-                    load_row<NG>(crow + j * N, cv);
-                    const float dt = sD[j][lane];
-                    const float du = sDU[j][lane];
-                    float yp = 0.0f;
-#pragma unroll
-                    for (int k = 0; k < NG; ++k) {
-                        const float aa = fast_exp2(dt * A2[k]);
-                        h[k] = __builtin_fmaf(aa, h[k], du * bv[k]);
-                        ahist[j][k] = aa;
-                        hist[j][k] = h[k];
-                        yp = __builtin_fmaf(cv[k], h[k], yp);
-                    }
-                    sP[w][j][lane] = yp;
-                } else {
-#pragma unroll
-                    for (int k = 0; k < NG; ++k) ahist[j][k] = hist[j][k] = 0.0f;
-                }
-            }
-        }
-        __syncthreads();
-        // ---- gate: sbar and dz for this wave's rows
-        float rsbar[SPW];
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int j = w * SPW + i;
-            rsbar[i] = 0.0f;
-            if (j < nval) {
-                float s = Dk * ru[i];
-#pragma unroll
-                for (int g = 0; g < G; ++g) s += sP[g][j][lane];
-                float sbar = rdy[i];
-                if (z) {
-                    const float sg = sigmoid(rz[i]);
-                    sbar = rdy[i] * rz[i] * sg;
-                    if (dvalid) {
-                        const float gz = rdy[i] * s * sg * (1.0f + rz[i] * (1.0f - sg));
-                        store_act(static_cast<T*>(a.dz), (b * L + tb + j) * D + d, gz);
-                    }
-                }
-                rsbar[i] = sbar;
-                sS[j][lane] = sbar;
-            }
-        }
-        __syncthreads();
-        // ---- reverse over the tile
-#pragma unroll
-        for (int j = kTB - 1; j >= 0; --j) {
-            if (j < nval) {
-                float bv[NG], cv[NG];
-                load_row<NG>(brow + j * N, bv);
-                load_row<NG>(crow + j * N, cv);
-                const float sbar = sS[j][lane];
-                const float dt = sD[j][lane];
-                const float du = sDU[j][lane];
-                float lb = 0.0f, lq = 0.0f, gB[NG], gC[NG];
-#pragma unroll
-                for (int k = 0; k < NG; ++k) {
-                    const int jn = j + 1 < kTB ? j + 1 : j;  // next row inside the tile
-                    const float an = (j + 1 < kTB && j + 1 < nval) ? ahist[jn][k] : anext[k];
-                    lam[k] = __builtin_fmaf(an, lam[k], sbar * cv[k]);
-                    const int jp = j > 0 ? j - 1 : 0;
-                    const float hp = j > 0 ? hist[jp][k] : hin[k];
-                    const float q = lam[k] * ahist[j][k] * hp;
-                    lb = __builtin_fmaf(lam[k], bv[k], lb);
-                    lq = __builtin_fmaf(Aval[k], q, lq);
-                    dAacc[k] = __builtin_fmaf(dt, q, dAacc[k]);
-                    gB[k] = dvalid ? lam[k] * du : 0.0f;
-                    gC[k] = dvalid ? sbar * hist[j][k] : 0.0f;
-                }
-                sP[w][j][lane] = lb;
-                sQ[w][j][lane] = lq;
-                // sum dB, dC over this wave's 64 channels
-                const int64_t prow = ((b * L + tb + j) * a.dblocks + dblk) * N + n0;
-                if constexpr (NG == 4) {
-                    const float rb = wave_sum4(gB[0], gB[1], gB[2], gB[3]);
-                    const float rc = wave_sum4(gC[0], gC[1], gC[2], gC[3]);
-                    if ((lane & 15) == 0) {
-                        const int r = lane >> 4;
-                        const int k = ((r & 1) << 1) | (r >> 1);
-                        a.pB[prow + k] = rb;
-                        a.pC[prow + k] = rc;
-                    }
-                } else {
-#pragma unroll
-                    for (int k = 0; k < NG; ++k) {
-                        const float rb = wave_sum(gB[k]);
-                        const float rc = wave_sum(gC[k]);
-                        if (lane == 0) {
-                            a.pB[prow + k] = rb;
-                            a.pC[prow + k] = rc;
-                        }
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < NG; ++k) anext[k] = ahist[0][k];
-        __syncthreads();
-        // ---- per-element gradients for this wave's rows
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int j = w * SPW + i;
-            if (j < nval && dvalid) {
-                float lb = 0.0f, lq = 0.0f;
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    lb += sP[g][j][lane];
-                    lq += sQ[g][j][lane];
-                }
-                const int64_t e = (b * L + tb + j) * D + d;
-                store_act(static_cast<T*>(a.du), e, __builtin_fmaf(rsbar[i], Dk, rdt[i] * lb));
-                const float dDelta = __builtin_fmaf(ru[i], lb, lq);
-                const float gx = a.softplus ? dDelta * sigmoid(rx[i]) : dDelta;
-                store_act(static_cast<T*>(a.ddelta), e, gx);
-                accD = __builtin_fmaf(rsbar[i], ru[i], accD);
-                accBias += gx;
-            }
-        }
-        __syncthreads();
+        for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tl * bk.ck_stride + q];
+        prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, w, lane, sX[tl & 1], r.keep_c);
+        fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl - 1, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
     }
-    // ---- per-(b, d) results
-    if (dvalid) {
-#pragma unroll
-        for (int k = 0; k < NG; ++k) {
-            a.pA[(b * D + d) * N + n0 + k] = dAacc[k];
-            if (a.dh0) a.dh0[(b * D + d) * N + n0 + k] = anext[k] * lam[k];
-        }
-    }
-    sRed[0][w][lane] = accD;
-    sRed[1][w][lane] = accBias;
     __syncthreads();
-    if (w == 0 && dvalid) {
+
+    for (int k = bk.ntiles - 1; k >= 0; --k) {
+        const int nval = min(kTB, bk.L32 - k * kTB);
+        if (nval == kTB)
+            rev_interval<true>(bk, k, kTB, A2, Aval, r, sX, sLQ);
+        else
+            rev_interval<false>(bk, k, nval, A2, Aval, r, sX, sLQ);
+        __syncthreads();
+    }
+    // ---- epilogue: finish tile 0, then the per-(b, d) results
+    finish_rows<T, SPW, G>(sLQ, r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32), bk.Dk, bk.du_b, bk.dd_b, bk.D32,
+                           r.accD, r.accBias);
+    if (bk.dvalid) {
+        float* pa = a.pA + (b * D + dc) * N + n0;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) pa[k] = r.dA[k];
+        if (a.dh0) {
+            float* g0 = a.dh0 + (b * D + dc) * N + n0;
+#pragma unroll
+            for (int k = 0; k < NG; ++k) g0[k] = r.anext[k] * r.lam[k];  // a_0 lam_0
+        }
+    }
+    sRed[0][w][lane] = r.accD;
+    sRed[1][w][lane] = r.accBias;
+    __syncthreads();
+    if (w == 0 && bk.dvalid) {
         float sd = 0.0f, sb = 0.0f;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             sd += sRed[0][g][lane];
             sb += sRed[1][g][lane];
         }
-        a.pD[b * D + d] = sd;
-        a.pbias[b * D + d] = sb;
+        a.pD[b * D + dc] = sd;
+        a.pbias[b * D + dc] = sb;
     }
 }
 
-// ---- kernel 3: fixed-order reductions ---------------------------------------------
+// ---- fixed-order reductions ----------------------------------------------------------
+// Items [0, B*L*N): dB, dC of (b, t, n), summed over the channel blocks;
+// items [B*L*N, B*L*N + D*N): dA of (d, n) summed over the batch (and dD,
+// ddt_bias of d with n == 0).  Grid-stride.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdKArgs a) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t nBC = a.B * a.L * a.N;
-    if (i < nBC) {  // dB, dC: sum over channel blocks
-        const int64_t n = i % a.N, bt = i / a.N;
-        const float* pb = a.pB + bt * a.dblocks * a.N + n;
-        const float* pc = a.pC + bt * a.dblocks * a.N + n;
-        float sb = 0.0f, sc = 0.0f;
-        for (int32_t k = 0; k < a.dblocks; ++k) {
-            sb += pb[k * a.N];
-            sc += pc[k * a.N];
-        }
-        store_act(static_cast<T*>(a.dB), i, sb);
-        store_act(static_cast<T*>(a.dC), i, sc);
-        return;
-    }
-    const int64_t j = i - nBC;
-    if (j < a.D * a.N) {  // dA: sum over the batch
-        float s = 0.0f;
-        for (int64_t b = 0; b < a.B; ++b) s += a.pA[b * a.D * a.N + j];
-        a.dA[j] = s;
-        if (j % a.N == 0) {
-            const int64_t d = j / a.N;
-            float sd = 0.0f, sb = 0.0f;
-            for (int64_t b = 0; b < a.B; ++b) {
-                sd += a.pD[b * a.D + d];
-                sb += a.pbias[b * a.D + d];
+    const int64_t total = nBC + a.D * a.N;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        if (i < nBC) {
+            const int64_t n = i % a.N, bt = i / a.N;
+            const float* p = a.pBC + bt * a.dblocks * 2 * a.N + n;
+            float sb = 0.0f, sc = 0.0f;
+            for (int32_t k = 0; k < a.dblocks; ++k) {
+                sb += p[(2 * k) * a.N];
+                sc += p[(2 * k + 1) * a.N];
             }
-            if (a.dD) a.dD[d] = sd;
-            if (a.ddt_bias) a.ddt_bias[d] = sb;
+            store_act(static_cast<T*>(a.dB), i, sb);
+            store_act(static_cast<T*>(a.dC), i, sc);
+        } else {
+            const int64_t j = i - nBC;
+            float s = 0.0f;
+            for (int64_t b = 0; b < a.B; ++b) s += a.pA[b * a.D * a.N + j];
+            a.dA[j] = s;
+            if (j % a.N == 0) {
+                const int64_t d = j / a.N;
+                float sd = 0.0f, sb = 0.0f;
+                for (int64_t b = 0; b < a.B; ++b) {
+                    sd += a.pD[b * a.D + d];
+                    sb += a.pbias[b * a.D + d];
+                }
+                if (a.dD) a.dD[d] = sd;
+                if (a.ddt_bias) a.ddt_bias[d] = sb;
+            }
         }
     }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Workspace: the forward schedule's own scratch, then the pre-pass outputs,
+// then the partial sums.
 struct WsLayout {
-    size_t ckpt, pB, pC, pA, pD, pbias, total;
+    size_t fwd, ckpt, sbar, pBC, pA, pD, pbias, total;
 };
 WsLayout ws_layout(int64_t B, int64_t L, int64_t D, int64_t N, int64_t tiles) {
     const int64_t dblocks = (D + 63) / 64;
     WsLayout w{};
     size_t off = 0;
-    w.ckpt = off; off += align256(static_cast<size_t>(B) * tiles * D * N * 4);
-    w.pB = off;   off += align256(static_cast<size_t>(B) * L * dblocks * N * 4);
-    w.pC = off;   off += align256(static_cast<size_t>(B) * L * dblocks * N * 4);
-    w.pA = off;   off += align256(static_cast<size_t>(B) * D * N * 4);
-    w.pD = off;   off += align256(static_cast<size_t>(B) * D * 4);
+    w.fwd = off;   off += align256(plan_fwd(B, L, D, N).ws_bytes);
+    w.ckpt = off;  off += align256(static_cast<size_t>(B) * tiles * D * N * 4);
+    w.sbar = off;  off += align256(static_cast<size_t>(B) * L * D * 4);
+    w.pBC = off;   off += align256(static_cast<size_t>(B) * L * dblocks * 2 * N * 4);
+    w.pA = off;    off += align256(static_cast<size_t>(B) * D * N * 4);
+    w.pD = off;    off += align256(static_cast<size_t>(B) * D * 4);
     w.pbias = off; off += align256(static_cast<size_t>(B) * D * 4);
     w.total = off;
     return w;
@@ -489,14 +596,17 @@ hipError_t launch_bwd_t(const ScanArgs& s, hipStream_t st) {
     const BwdPlan pl = plan_bwd(s.B, s.L, s.D, s.N);
     const WsLayout wl = ws_layout(s.B, s.L, s.D, s.N, pl.tiles);
     char* ws = static_cast<char*>(s.workspace);
+    float* ckpt = reinterpret_cast<float*>(ws + wl.ckpt);
+    float* sbar = reinterpret_cast<float*>(ws + wl.sbar);
+    hipError_t e = launch_fwd_prepass(s, ws + wl.fwd, ckpt, sbar, st);
+    if (e != hipSuccess) return e;
     BwdKArgs a{};
-    a.u = s.u; a.delta = s.delta; a.z = s.z; a.Bm = s.Bm; a.Cm = s.Cm; a.dy = s.dy;
-    a.A = s.A; a.Dskip = s.Dskip; a.dt_bias = s.dt_bias; a.h0 = s.h0; a.dh_final = s.dh_final;
-    a.du = s.du; a.ddelta = s.ddelta; a.dz = s.dz; a.dB = s.dB; a.dC = s.dC;
+    a.u = s.u; a.delta = s.delta; a.Bm = s.Bm; a.Cm = s.Cm;
+    a.A = s.A; a.Dskip = s.Dskip; a.dt_bias = s.dt_bias; a.dh_final = s.dh_final;
+    a.ckpt = ckpt; a.sbar = sbar;
+    a.du = s.du; a.ddelta = s.ddelta; a.dB = s.dB; a.dC = s.dC;
     a.dA = s.dA; a.dD = s.dD; a.ddt_bias = s.ddt_bias; a.dh0 = s.dh0;
-    a.ckpt = reinterpret_cast<float*>(ws + wl.ckpt);
-    a.pB = reinterpret_cast<float*>(ws + wl.pB);
-    a.pC = reinterpret_cast<float*>(ws + wl.pC);
+    a.pBC = reinterpret_cast<float*>(ws + wl.pBC);
     a.pA = reinterpret_cast<float*>(ws + wl.pA);
     a.pD = reinterpret_cast<float*>(ws + wl.pD);
     a.pbias = reinterpret_cast<float*>(ws + wl.pbias);
@@ -504,24 +614,24 @@ hipError_t launch_bwd_t(const ScanArgs& s, hipStream_t st) {
     a.tiles = pl.tiles;
     a.dblocks = static_cast<int32_t>((s.D + 63) / 64);
     a.softplus = s.softplus;
-    const dim3 grid(static_cast<unsigned>(s.B * a.dblocks));
-    hipLaunchKernelGGL((bwd_ckpt_kernel<T, NG, G>), grid, dim3(64 * G), 0, st, a);
-    hipLaunchKernelGGL((bwd_reverse_kernel<T, NG, G>), grid, dim3(64 * G), 0, st, a);
-    const int64_t nred = s.B * s.L * s.N + s.D * s.N;
-    hipLaunchKernelGGL((bwd_reduce_kernel<T>), dim3(static_cast<unsigned>((nred + 255) / 256)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bwd_reverse_kernel<T, NG, G>), dim3(static_cast<unsigned>(s.B * a.dblocks)),
+                       dim3(64 * G), 0, st, a);
+    const int64_t items = s.B * s.L * s.N + s.D * s.N;
+    const int64_t blocks = std::min<int64_t>((items + 255) / 256, 16384);
+    hipLaunchKernelGGL((bwd_reduce_kernel<T>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t dispatch_n(const ScanArgs& s, hipStream_t st) {
-    switch (s.N) {
+    switch (s.N) {  // NG states per wave x G waves; NG divides 8 (16-value batches)
         case 1: return launch_bwd_t<T, 1, 1>(s, st);
         case 2: return launch_bwd_t<T, 1, 2>(s, st);
         case 4: return launch_bwd_t<T, 1, 4>(s, st);
         case 8: return launch_bwd_t<T, 2, 4>(s, st);
-        case 16: return launch_bwd_t<T, 4, 4>(s, st);
-        case 32: return launch_bwd_t<T, 8, 4>(s, st);
-        case 64: return launch_bwd_t<T, 16, 4>(s, st);
+        case 16: return launch_bwd_t<T, 2, 8>(s, st);
+        case 32: return launch_bwd_t<T, 4, 8>(s, st);
+        case 64: return launch_bwd_t<T, 8, 8>(s, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -66,6 +66,12 @@ struct FwdKArgs {
     int32_t softplus;
     int32_t workers;       // 0: one workgroup per (block, chunk); > 0: balanced persistent schedule
     int32_t nblk;          // B * dblocks
+    // backward pre-pass only
+    const void* dy;
+    void* dz;              // nullable (no gate)
+    float* sbar;           // (B, L, D) dy * silu(z), or dy without a gate
+    float* ckpt;           // (B, tiles, D, N) state before every kTB-step tile
+    int64_t tiles;         // ceil(L / kTB)
 };
 
 // Raw inputs of this wave's rows of one tile (u, delta, z at (b, t, chan0 +
@@ -148,11 +154,12 @@ __device__ __forceinline__ void state_steps(std::integer_sequence<int, J...>, in
 // the tile index is clamped to the chunk's last tile and the row to that
 // tile's last valid row, so every address is inside the chunk (rows that do
 // not exist are loaded from a valid row and never used).
-template <typename T, int SPW, bool HAS_Z>
+template <typename T, int SPW, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fetch_rows_clamped(const T* __restrict__ u_chunk, const T* __restrict__ d_chunk,
-                                                   const T* __restrict__ z_chunk, int tile, int ntiles, int t_len,
-                                                   int64_t D, int first_row, int lo, float (&ru)[SPW],
-                                                   float (&rd)[SPW], float (&rz)[SPW]) {
+                                                   const T* __restrict__ z_chunk, const T* __restrict__ dy_chunk,
+                                                   int tile, int ntiles, int t_len, int64_t D, int first_row,
+                                                   int lo, float (&ru)[SPW], float (&rd)[SPW], float (&rz)[SPW],
+                                                   float (&rdy)[SPW]) {
     const int te = min(tile, ntiles - 1);
     const int rows_left = t_len - te * kTB;  // >= 1
     const int64_t base = static_cast<int64_t>(te) * kTB * D;
@@ -164,6 +171,7 @@ __device__ __forceinline__ void fetch_rows_clamped(const T* __restrict__ u_chunk
         ru[i] = load_act(u_chunk + base, off);
         rd[i] = load_act(d_chunk + base, off);
         if constexpr (HAS_Z) rz[i] = load_act(z_chunk + base, off);
+        if constexpr (PRE) rdy[i] = load_act(dy_chunk + base, off);
     }
 }
 
@@ -180,18 +188,41 @@ __device__ __forceinline__ void prep_element(float uu, float dd, float zz, float
     gate = HAS_Z ? silu(zz) : 1.0f;
 }
 
+// Backward pre-pass front end of one row: the forward's (Delta, Delta*u) and
+// skip term, plus sbar = dy * silu(z) (dy without a gate) and the factor
+// dzf = dy * silu'(z) that turns the row's readout s into dz = s * dzf.
+template <bool HAS_Z>
+__device__ __forceinline__ void prep_element_pre(float uu, float dd, float zz, float gy, float bias, float Dk,
+                                                 int softplus_on, float2& dDU, float& skip, float& dzf,
+                                                 float& sb) {
+    const float x = dd + bias;
+    const float sp = softplus(x);
+    const float dt = softplus_on ? sp : x;
+    dDU = make_float2(dt, dt * uu);
+    skip = Dk * uu;
+    if constexpr (HAS_Z) {
+        const float sg = sigmoid(zz);
+        sb = gy * zz * sg;
+        dzf = gy * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
+    } else {
+        sb = gy;
+        dzf = 0.0f;
+    }
+}
+
 // Registers carried from one tile interval to the next.
 template <typename T, int NG, int G>
 struct FwdRegs {
     static constexpr int SPW = kTB / G;
-    float ru[SPW], rd[SPW], rz[SPW];                       // raw inputs of the next tile to prepare
+    float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];             // raw inputs of the next tile to prepare
     uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next recurrence tile
     float skip_c[SPW], gate_c[SPW];                        // rows of the tile in recurrence
     float skip_p[SPW], gate_p[SPW];                        // rows of the tile being finished
+    // (backward pre-pass: "gate" holds dzf, the factor with s * dzf = dz)
 };
 
 // Uniform facts about one tile interval.
-template <typename T, int NG, int G, bool HAS_Z>
+template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 struct FwdInterval {
     int k, ntiles, t_len, w, lane, lo;
     bool dvalid;
@@ -206,6 +237,10 @@ struct FwdInterval {
     const T* Bm;
     const T* Cm;
     T* y_prev;  // first element (row0 - kTB, chan0) of the tile finished in this interval (k > 0)
+    // backward pre-pass
+    const T* dy_chunk;
+    float* sbar_next;  // first element (row0 + kTB, chan0) of sbar for the tile prepared here
+    float* ckpt_tile;  // ckpt row of this tile for channel chan0: ((b * tiles + tile) * D + chan0) * N
 };
 
 // One interval: read this interval's LDS first (tile k's (Delta, Delta*u), the
@@ -214,8 +249,8 @@ struct FwdInterval {
 // recurrence of tile k and store tile k - 1.  Work that does not exist
 // (tile k + 1 past the end, tile -1) runs on clamped inputs and stores to an
 // out-of-range offset, instead of branching.
-template <bool FULL, typename T, int NG, int G, bool HAS_Z>
-__device__ __forceinline__ void fwd_interval(const FwdInterval<T, NG, G, HAS_Z>& it, int nval,
+template <bool FULL, typename T, int NG, int G, bool HAS_Z, bool PRE>
+__device__ __forceinline__ void fwd_interval(const FwdInterval<T, NG, G, HAS_Z, PRE>& it, int nval,
                                              const float (&A2)[NG], float (&h)[NG], FwdRegs<T, NG, G>& r,
                                              float2 (&sDD)[2][kTB][64], float (&sP)[2][G][kTB][64]) {
     constexpr int SPW = kTB / G;
@@ -235,28 +270,53 @@ __device__ __forceinline__ void fwd_interval(const FwdInterval<T, NG, G, HAS_Z>&
     fetch_tile_rows<T, NG>(it.Bm, it.row0 + kTB, it.last_row, it.N, it.n0, lane, r.qb);
     fetch_tile_rows<T, NG>(it.Cm, it.row0 + kTB, it.last_row, it.N, it.n0, lane, r.qc);
     float skip_n[SPW], gate_n[SPW];
+    const int D32 = static_cast<int>(it.D);
+    if constexpr (PRE) {
+        // rows of tile k + 1; sbar goes straight to memory (rows past the end: out of range)
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(it.sbar_next, static_cast<uint32_t>(kTB * D32 * 4));
+        const int rows_next = it.t_len - (it.k + 1) * kTB;
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        float2 v;
-        prep_element<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], it.bias, it.Dk, it.softplus_on, v, skip_n[i], gate_n[i]);
-        sDD[prv][w * SPW + i][lane] = v;
+        for (int i = 0; i < SPW; ++i) {
+            float2 v;
+            float sb;
+            prep_element_pre<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], r.rdy[i], it.bias, it.Dk, it.softplus_on, v,
+                                    skip_n[i], gate_n[i], sb);
+            sDD[prv][w * SPW + i][lane] = v;
+            const int j = w * SPW + i;
+            const uint32_t off = (it.dvalid && j < rows_next) ? static_cast<uint32_t>((j * D32 + lane) * 4) : kNoStore;
+            buffer_store_act(sb, rs, off, 0.0f);
+        }
+        // the state before tile k
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(it.ckpt_tile, static_cast<uint32_t>(64 * it.N * 4));
+#pragma unroll
+        for (int q = 0; q < NG; ++q)
+            buffer_store_act(h[q], rc, it.dvalid ? static_cast<uint32_t>((lane * it.N + it.n0 + q) * 4) : kNoStore,
+                             0.0f);
+    } else {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            float2 v;
+            prep_element<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], it.bias, it.Dk, it.softplus_on, v, skip_n[i],
+                                gate_n[i]);
+            sDD[prv][w * SPW + i][lane] = v;
+        }
     }
-    fetch_rows_clamped<T, SPW, HAS_Z>(it.u_chunk, it.d_chunk, it.z_chunk, it.k + 2, it.ntiles, it.t_len, it.D,
-                                      w * SPW, it.lo, r.ru, r.rd, r.rz);
+    fetch_rows_clamped<T, SPW, HAS_Z, PRE>(it.u_chunk, it.d_chunk, it.z_chunk, it.dy_chunk, it.k + 2, it.ntiles,
+                                           it.t_len, it.D, w * SPW, it.lo, r.ru, r.rd, r.rz, r.rdy);
     fwd_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, nval, w, lane, A2, h, Bt, Ct, ddt, sP[cur]);
     {
         // tile k - 1 (none when k == 0: every lane stores out of range)
+        // (pre-pass: y_prev points into dz, and s * dzf is the gate gradient)
         const __amdgpu_buffer_rsrc_t ry = make_rsrc(it.y_prev, static_cast<uint32_t>(kTB * it.row_bytes));
-        const int D32 = static_cast<int>(it.D);
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             float s = 0.0f;
 #pragma unroll
             for (int g = 0; g < G; ++g) s += part[i][g];
             const int j = w * SPW + i;
-            const uint32_t off = (it.dvalid && it.k > 0)
-                                     ? static_cast<uint32_t>((j * D32 + lane) * static_cast<int>(sizeof(T)))
-                                     : kNoStore;
+            const bool store = it.dvalid && it.k > 0 && (!PRE || HAS_Z);
+            const uint32_t off = store ? static_cast<uint32_t>((j * D32 + lane) * static_cast<int>(sizeof(T)))
+                                       : kNoStore;
             buffer_store_act((s + r.skip_p[i]) * r.gate_p[i], ry, off, T{});
         }
     }
@@ -276,7 +336,7 @@ __device__ __forceinline__ void fwd_interval(const FwdInterval<T, NG, G, HAS_Z>&
 // tile k + 1, runs the recurrence of tile k and finishes its rows of tile
 // k - 1 (LDS double buffered), so the per-element work fills the latency gaps
 // of the recurrence's dependency chains.
-template <typename T, int NG, int G, bool HAS_Z>
+template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t t_begin, int64_t t_end,
                                             float (&h)[NG], float2 (&sDD)[2][kTB][64],
                                             float (&sP)[2][G][kTB][64]) {
@@ -316,31 +376,50 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     const T* u_chunk = u + chunk_off;
     const T* d_chunk = dl + chunk_off;
     const T* z_chunk = HAS_Z ? z + chunk_off : nullptr;
+    const T* dy_chunk = PRE ? static_cast<const T*>(a.dy) + chunk_off : nullptr;
     const int row_bytes = D32 * static_cast<int>(sizeof(T));
+    const int64_t gtile0 = t_begin / kTB;  // segments start on tile boundaries
 
     __syncthreads();  // LDS is reused from a previous segment
     // ---- prologue: tile 0 prepared, tile 1 raw inputs and tile 0 Bm/Cm in flight
     FwdRegs<T, NG, G> r;
-    fetch_rows_clamped<T, SPW, HAS_Z>(u_chunk, d_chunk, z_chunk, 0, ntiles, t_len, D, w * SPW, lo, r.ru, r.rd,
-                                      r.rz);
+    fetch_rows_clamped<T, SPW, HAS_Z, PRE>(u_chunk, d_chunk, z_chunk, dy_chunk, 0, ntiles, t_len, D, w * SPW, lo,
+                                           r.ru, r.rd, r.rz, r.rdy);
     fetch_tile_rows<T, NG>(Bm, row_begin, last_row, N, n0, lane, r.qb);
     fetch_tile_rows<T, NG>(Cm, row_begin, last_row, N, n0, lane, r.qc);
+    if constexpr (PRE) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.sbar + chunk_off, static_cast<uint32_t>(kTB * D32 * 4));
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        float2 v;
-        prep_element<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], bias, Dk, softplus_on, v, r.skip_c[i], r.gate_c[i]);
-        sDD[0][w * SPW + i][lane] = v;  // rows past the segment end hold finite junk, never used
+        for (int i = 0; i < SPW; ++i) {
+            float2 v;
+            float sb;
+            prep_element_pre<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], r.rdy[i], bias, Dk, softplus_on, v, r.skip_c[i],
+                                    r.gate_c[i], sb);
+            sDD[0][w * SPW + i][lane] = v;
+            const int j = w * SPW + i;
+            buffer_store_act(sb, rs, (dvalid && j < t_len) ? static_cast<uint32_t>((j * D32 + lane) * 4) : kNoStore,
+                             0.0f);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            float2 v;
+            prep_element<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], bias, Dk, softplus_on, v, r.skip_c[i], r.gate_c[i]);
+            sDD[0][w * SPW + i][lane] = v;  // rows past the segment end hold finite junk, never used
+        }
     }
-    fetch_rows_clamped<T, SPW, HAS_Z>(u_chunk, d_chunk, z_chunk, 1, ntiles, t_len, D, w * SPW, lo, r.ru, r.rd,
-                                      r.rz);
+    fetch_rows_clamped<T, SPW, HAS_Z, PRE>(u_chunk, d_chunk, z_chunk, dy_chunk, 1, ntiles, t_len, D, w * SPW, lo,
+                                           r.ru, r.rd, r.rz, r.rdy);
     __syncthreads();
 
     for (int k = 0; k < ntiles; ++k) {
         const int nval = min(kTB, t_len - k * kTB);
         const int64_t row0 = row_begin + static_cast<int64_t>(k) * kTB;
-        FwdInterval<T, NG, G, HAS_Z> it{k, ntiles, t_len, w, lane, lo, dvalid, row_bytes, softplus_on, bias, Dk,
-                                        D, N, n0, row0, last_row, u_chunk, d_chunk, z_chunk, Bm, Cm,
-                                        y + (k > 0 ? row0 - kTB : row0) * D + chan0};
+        FwdInterval<T, NG, G, HAS_Z, PRE> it{
+            k, ntiles, t_len, w, lane, lo, dvalid, row_bytes, softplus_on, bias, Dk, D, N, n0, row0, last_row,
+            u_chunk, d_chunk, z_chunk, Bm, Cm, y + (k > 0 ? row0 - kTB : row0) * D + chan0, dy_chunk,
+            PRE ? a.sbar + (k + 1 < ntiles ? row0 + kTB : row0) * D + chan0 : nullptr,
+            PRE ? a.ckpt + ((b * a.tiles + gtile0 + k) * D + chan0) * N : nullptr};
         if (nval == kTB)
             fwd_interval<true>(it, kTB, A2, h, r, sDD, sP);
         else
@@ -359,7 +438,7 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
             float s = 0.0f;
 #pragma unroll
             for (int g = 0; g < G; ++g) s += sP[klast & 1][g][j][lane];
-            const uint32_t off = (dvalid && j < nval)
+            const uint32_t off = (dvalid && j < nval && (!PRE || HAS_Z))
                                      ? static_cast<uint32_t>((j * D32 + lane) * static_cast<int>(sizeof(T)))
                                      : kNoStore;
             buffer_store_act((s + r.skip_p[i]) * r.gate_p[i], ry, off, T{});
@@ -380,7 +459,7 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
 //    published.  Equal work per workgroup, no extra arithmetic.  A worker only
 //    waits on a lower-numbered worker, which never waits before publishing
 //    (workgroups are dispatched in increasing order), so every wait ends.
-template <typename T, int NG, int G, bool HAS_Z>
+template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
     constexpr int N = NG * G;
     static_assert(kTB % G == 0, "tile must split evenly over the waves");
@@ -448,7 +527,7 @@ __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
             for (int k = 0; k < NG; ++k)
                 h[k] = __hip_atomic_load(carry_lane + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        fwd_segment<T, NG, G, HAS_Z>(a, blk, t_begin, t_end, h, sDD, sP);
+        fwd_segment<T, NG, G, HAS_Z, PRE>(a, blk, t_begin, t_end, h, sDD, sP);
         if (to == kFinal) {
             if (a.h_final && chan0 + lane < a.D) {
                 float* hf = a.h_final + (b * a.D + chan0 + lane) * N + n0;
@@ -582,8 +661,16 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // device partition has at least this many CUs).
 constexpr int64_t kBalancedMinBlocks = 64;
 
-template <typename T, int NG, int G>
-hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, hipStream_t st) {
+// Extra outputs of the backward pre-pass (all null for the forward).
+struct PreOut {
+    const void* dy;
+    void* dz;
+    float* sbar;
+    float* ckpt;
+};
+
+template <typename T, int NG, int G, bool PRE>
+hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, void* scratch, const PreOut& pre, hipStream_t st) {
     FwdKArgs a{};
     a.u = s.u; a.delta = s.delta; a.z = s.z; a.Bm = s.Bm; a.Cm = s.Cm;
     a.A = s.A; a.Dskip = s.Dskip; a.dt_bias = s.dt_bias; a.h0 = s.h0;
@@ -593,11 +680,20 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, hipStream_t st) {
     a.chunks = static_cast<int32_t>(pl.chunks);
     a.dblocks = static_cast<int32_t>((s.D + 63) / 64);
     a.softplus = s.softplus;
+    a.tiles = (s.L + kTB - 1) / kTB;
+    if constexpr (PRE) {
+        a.dy = pre.dy;
+        a.dz = pre.dz;
+        a.sbar = pre.sbar;
+        a.ckpt = pre.ckpt;
+        a.y = pre.dz ? pre.dz : static_cast<void*>(pre.sbar);  // dz goes where y would; never stored without z
+        a.h_final = nullptr;
+    }
     const dim3 block(64 * G);
+    char* ws = static_cast<char*>(scratch);
     if (pl.chunks > 1) {
         const size_t nh = static_cast<size_t>(s.B) * pl.chunks * s.D * s.N * sizeof(float);
         const size_t ns = static_cast<size_t>(s.B) * pl.chunks * s.D * sizeof(float);
-        char* ws = static_cast<char*>(s.workspace);
         a.agg_h = reinterpret_cast<float*>(ws);
         a.agg_s = reinterpret_cast<float*>(ws + align256(nh));
         a.h_in = nullptr;
@@ -618,7 +714,6 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, hipStream_t st) {
         if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
         if (ncu > 0 && a.nblk >= ncu && a.nblk % ncu != 0) {
-            char* ws = static_cast<char*>(s.workspace);
             a.workers = ncu;
             a.flags = reinterpret_cast<uint32_t*>(ws);
             a.carry = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(a.nblk) * sizeof(uint32_t)));
@@ -628,9 +723,9 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, hipStream_t st) {
         }
     }
     if (s.z)
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false, PRE>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 
@@ -640,16 +735,16 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, hipStream_t st) {
 #define MSSM_FWD_WAVES_N16 8
 #endif
 
-template <typename T>
-hipError_t dispatch_n(const ScanArgs& s, const FwdPlan& pl, hipStream_t st) {
+template <typename T, bool PRE>
+hipError_t dispatch_n(const ScanArgs& s, const FwdPlan& pl, void* scratch, const PreOut& pre, hipStream_t st) {
     switch (s.N) {
-        case 1: return launch_fwd_t<T, 1, 1>(s, pl, st);
-        case 2: return launch_fwd_t<T, 1, 2>(s, pl, st);
-        case 4: return launch_fwd_t<T, 1, 4>(s, pl, st);
-        case 8: return launch_fwd_t<T, 2, 4>(s, pl, st);
-        case 16: return launch_fwd_t<T, 16 / MSSM_FWD_WAVES_N16, MSSM_FWD_WAVES_N16>(s, pl, st);
-        case 32: return launch_fwd_t<T, 8, 4>(s, pl, st);
-        case 64: return launch_fwd_t<T, 16, 4>(s, pl, st);
+        case 1: return launch_fwd_t<T, 1, 1, PRE>(s, pl, scratch, pre, st);
+        case 2: return launch_fwd_t<T, 1, 2, PRE>(s, pl, scratch, pre, st);
+        case 4: return launch_fwd_t<T, 1, 4, PRE>(s, pl, scratch, pre, st);
+        case 8: return launch_fwd_t<T, 2, 4, PRE>(s, pl, scratch, pre, st);
+        case 16: return launch_fwd_t<T, 16 / MSSM_FWD_WAVES_N16, MSSM_FWD_WAVES_N16, PRE>(s, pl, scratch, pre, st);
+        case 32: return launch_fwd_t<T, 8, 4, PRE>(s, pl, scratch, pre, st);
+        case 64: return launch_fwd_t<T, 16, 4, PRE>(s, pl, scratch, pre, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -685,7 +780,16 @@ FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N) {
 
 hipError_t launch_fwd(const ScanArgs& s, hipStream_t st) {
     const FwdPlan pl = plan_fwd(s.B, s.L, s.D, s.N);
-    return s.dtype == 1 ? dispatch_n<uint16_t>(s, pl, st) : dispatch_n<float>(s, pl, st);
+    const PreOut none{};
+    return s.dtype == 1 ? dispatch_n<uint16_t, false>(s, pl, s.workspace, none, st)
+                        : dispatch_n<float, false>(s, pl, s.workspace, none, st);
+}
+
+hipError_t launch_fwd_prepass(const ScanArgs& s, void* fwd_scratch, float* ckpt, float* sbar, hipStream_t st) {
+    const FwdPlan pl = plan_fwd(s.B, s.L, s.D, s.N);
+    const PreOut pre{s.dy, s.dz, sbar, ckpt};
+    return s.dtype == 1 ? dispatch_n<uint16_t, true>(s, pl, fwd_scratch, pre, st)
+                        : dispatch_n<float, true>(s, pl, fwd_scratch, pre, st);
 }
 
 }  // namespace mssm
