@@ -178,12 +178,14 @@ __device__ __forceinline__ float row_bcast(float v) {
 
 // acc + row_bcast<J>(c) * h as one v_fmac_f32 with a DPP source (the
 // compiler does not fold DPP into the tied-accumulator form by itself).
-// Arithmetic only; `c` must not have been written by the previous two VALU
-// instructions (DPP read-after-write), which holds for the per-tile Bm/Cm
-// registers it is used with.
+// Arithmetic only.  A DPP source must not have been written by either of the
+// two preceding VALU instructions; the compiler does not check that for
+// inline assembly, so the statement starts with two wait states of its own
+// (s_nop 1) -- the register holding `c` may have just been written, e.g. by
+// the bf16 unpacking of a Bm/Cm tile.
 template <int J>
 __device__ __forceinline__ float fmac_row_bcast(float acc, float c, float h) {
-    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+    asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
         : "+v"(acc)
         : "v"(c), "v"(h), "i"(J));
     return acc;

@@ -77,7 +77,7 @@ struct FwdKArgs {
 // Raw inputs of this wave's rows of one tile (u, delta, z at (b, t, chan0 +
 // lane)), loaded with 32-bit offsets from a uniform row base.
 template <typename T, int SPW>
-__device__ __forceinline__ void fetch_rows(const T* __restrict__ u, const T* __restrict__ dl,
+__device__ __forceinline__ void fetch_rows_ptr(const T* __restrict__ u, const T* __restrict__ dl,
                                            const T* __restrict__ z, int64_t base, int first_row, int rows_left,
                                            int D32, int lo, float (&ru)[SPW], float (&rd)[SPW], float (&rz)[SPW]) {
 #pragma unroll
@@ -150,28 +150,42 @@ __device__ __forceinline__ void state_steps(std::integer_sequence<int, J...>, in
     (state_step<NG, FULL, J>(nval, A2, h, Bt, ddt, ssum), ...);
 }
 
-// Raw inputs of this wave's rows of tile `tile` of the chunk, branch-free:
-// the tile index is clamped to the chunk's last tile and the row to that
-// tile's last valid row, so every address is inside the chunk (rows that do
-// not exist are loaded from a valid row and never used).
-template <typename T, int SPW, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void fetch_rows_clamped(const T* __restrict__ u_chunk, const T* __restrict__ d_chunk,
-                                                   const T* __restrict__ z_chunk, const T* __restrict__ dy_chunk,
-                                                   int tile, int ntiles, int t_len, int64_t D, int first_row,
-                                                   int lo, float (&ru)[SPW], float (&rd)[SPW], float (&rz)[SPW],
-                                                   float (&rdy)[SPW]) {
-    const int te = min(tile, ntiles - 1);
-    const int rows_left = t_len - te * kTB;  // >= 1
-    const int64_t base = static_cast<int64_t>(te) * kTB * D;
-    const int D32 = static_cast<int>(D);
+// ---- buffer loads ---------------------------------------------------------------
+// The activations and Bm/Cm of one tile are read through a buffer resource
+// rebased at the tile (uniform 64-bit address arithmetic on the scalar unit)
+// with a per-lane byte offset that is the same for every tile, so a load costs
+// no vector address arithmetic.  The resource's range ends at the segment's
+// last element: loads past it (rows after the end, channels past the last one
+// in the last row) return 0 -- finite values whose results are never stored.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
+    const int64_t b = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
+    return make_rsrc(base, static_cast<uint32_t>(b));
+}
+__device__ __forceinline__ float buffer_load_act(__amdgpu_buffer_rsrc_t r, uint32_t off, float) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+}
+__device__ __forceinline__ float buffer_load_act(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t) {
+    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0))
+                           << 16);
+}
+// NG consecutive values of one Bm/Cm row (LaneRow layout) through a buffer.
+template <typename T, int NG>
+__device__ __forceinline__ void buffer_load_lane_row(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                     uint32_t (&q)[LaneRow<T, NG>::kWords]) {
+    constexpr int bytes = LaneRow<T, NG>::kBytes;
+    if constexpr (bytes >= 16) {
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int j = min(first_row + i, rows_left - 1);
-        const uint32_t off = static_cast<uint32_t>(j * D32 + lo);
-        ru[i] = load_act(u_chunk + base, off);
-        rd[i] = load_act(d_chunk + base, off);
-        if constexpr (HAS_Z) rz[i] = load_act(z_chunk + base, off);
-        if constexpr (PRE) rdy[i] = load_act(dy_chunk + base, off);
+        for (int i = 0; i < bytes / 16; ++i) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off + 16 * i), 0, 0);
+            q[4 * i] = v[0]; q[4 * i + 1] = v[1]; q[4 * i + 2] = v[2]; q[4 * i + 3] = v[3];
+        }
+    } else if constexpr (bytes == 8) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0);
+        q[0] = v[0]; q[1] = v[1];
+    } else if constexpr (bytes == 4) {
+        q[0] = __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
+    } else {
+        q[0] = __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0);
     }
 }
 
@@ -210,132 +224,203 @@ __device__ __forceinline__ void prep_element_pre(float uu, float dd, float zz, f
     }
 }
 
+// Uniform facts of one segment (a block's steps [t_begin, t_end)) and the
+// lane's constant offsets.
+template <typename T, int NG, int G, bool HAS_Z, bool PRE>
+struct FwdSeg {
+    static constexpr int SPW = kTB / G;
+    int ntiles, t_len, w, lane;
+    bool dvalid;
+    int softplus_on;
+    float bias, Dk;
+    int64_t D;
+    int64_t seg_elems;  // elements from (b, t_begin, chan0) to the segment's last, (b, t_end - 1, D - 1)
+    int N, n0;
+    const T* u_seg;   // element (b, t_begin, chan0) of u; the same for delta, z, dy, y
+    const T* d_seg;
+    const T* z_seg;
+    const T* dy_seg;
+    T* y_seg;
+    const T* Bm_seg;  // row (b, t_begin) of Bm / Cm
+    const T* Cm_seg;
+    float* sbar_seg;  // pre-pass: element (b, t_begin, chan0) of sbar
+    float* ckpt_seg;  // pre-pass: ((b * tiles + t_begin / kTB) * D + chan0) * N
+    uint32_t row_off[SPW];  // byte offset of this wave's row i of a tile, this lane's channel
+    uint32_t bc_off;        // byte offset of this lane's Bm/Cm values in a tile (step lane % 16)
+};
+
 // Registers carried from one tile interval to the next.
 template <typename T, int NG, int G>
 struct FwdRegs {
     static constexpr int SPW = kTB / G;
-    float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];             // raw inputs of the next tile to prepare
+    float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];   // raw inputs of the tile prepared next (k + 2)
     uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next recurrence tile
-    float skip_c[SPW], gate_c[SPW];                        // rows of the tile in recurrence
-    float skip_p[SPW], gate_p[SPW];                        // rows of the tile being finished
-    // (backward pre-pass: "gate" holds dzf, the factor with s * dzf = dz)
+    // skip term and gate (pre-pass: dz factor) of the rows of tiles k + 1 (n),
+    // k (c) and k - 1 (p), and of tile k + 2 while it is prepared
+    float skip_n[SPW], gate_n[SPW], skip_c[SPW], gate_c[SPW], skip_p[SPW], gate_p[SPW];
 };
 
-// Uniform facts about one tile interval.
+// Raw inputs of this wave's rows of segment tile `tile` (zeros past the end).
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-struct FwdInterval {
-    int k, ntiles, t_len, w, lane, lo;
-    bool dvalid;
-    int row_bytes, softplus_on;
-    float bias, Dk;
-    int64_t D;
-    int N, n0;
-    int64_t row0, last_row;
-    const T* u_chunk;
-    const T* d_chunk;
-    const T* z_chunk;
-    const T* Bm;
-    const T* Cm;
-    T* y_prev;  // first element (row0 - kTB, chan0) of the tile finished in this interval (k > 0)
-    // backward pre-pass
-    const T* dy_chunk;
-    float* sbar_next;  // first element (row0 + kTB, chan0) of sbar for the tile prepared here
-    float* ckpt_tile;  // ckpt row of this tile for channel chan0: ((b * tiles + tile) * D + chan0) * N
-};
+__device__ __forceinline__ void fetch_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
+                                           float (&ru)[kTB / G], float (&rd)[kTB / G], float (&rz)[kTB / G],
+                                           float (&rdy)[kTB / G]) {
+    constexpr int SPW = kTB / G;
+    const int64_t first = static_cast<int64_t>(tile) * kTB * sg.D;       // first element of the tile
+    const int64_t bytes = (sg.seg_elems - first) * static_cast<int64_t>(sizeof(T));
+    const __amdgpu_buffer_rsrc_t ru_r = range_rsrc(sg.u_seg + first, bytes);
+    const __amdgpu_buffer_rsrc_t rd_r = range_rsrc(sg.d_seg + first, bytes);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        ru[i] = buffer_load_act(ru_r, sg.row_off[i], T{});
+        rd[i] = buffer_load_act(rd_r, sg.row_off[i], T{});
+    }
+    if constexpr (HAS_Z) {
+        const __amdgpu_buffer_rsrc_t rz_r = range_rsrc(sg.z_seg + first, bytes);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) rz[i] = buffer_load_act(rz_r, sg.row_off[i], T{});
+    }
+    if constexpr (PRE) {
+        const __amdgpu_buffer_rsrc_t ry_r = range_rsrc(sg.dy_seg + first, bytes);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) rdy[i] = buffer_load_act(ry_r, sg.row_off[i], T{});
+    }
+}
 
-// One interval: read this interval's LDS first (tile k's (Delta, Delta*u), the
-// partial readouts of tile k - 1), then -- in one straight-line block when
-// FULL -- prepare tile k + 1, issue the loads of tiles k + 1 / k + 2, run the
-// recurrence of tile k and store tile k - 1.  Work that does not exist
-// (tile k + 1 past the end, tile -1) runs on clamped inputs and stores to an
-// out-of-range offset, instead of branching.
+// This wave's Bm and Cm values of segment tile `tile`: lane l holds step
+// l % 16 (zeros past the end).
+template <typename T, int NG, int G, bool HAS_Z, bool PRE>
+__device__ __forceinline__ void fetch_bc(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
+                                         uint32_t (&qb)[LaneRow<T, NG>::kWords],
+                                         uint32_t (&qc)[LaneRow<T, NG>::kWords]) {
+    const int64_t first = static_cast<int64_t>(tile) * kTB * sg.N;
+    const int64_t bytes = (static_cast<int64_t>(sg.t_len) * sg.N - first) * static_cast<int64_t>(sizeof(T));
+    buffer_load_lane_row<T, NG>(range_rsrc(sg.Bm_seg + first, bytes), sg.bc_off, qb);
+    buffer_load_lane_row<T, NG>(range_rsrc(sg.Cm_seg + first, bytes), sg.bc_off, qc);
+}
+
+// Front end of this wave's rows of segment tile `tile` into sDD (and, in the
+// pre-pass, sbar to memory).  Rows past the end hold finite values that are
+// never used.
+template <typename T, int NG, int G, bool HAS_Z, bool PRE>
+__device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile, const float (&ru)[kTB / G],
+                                          const float (&rd)[kTB / G], const float (&rz)[kTB / G],
+                                          const float (&rdy)[kTB / G], float2 (&dst)[kTB][64],
+                                          float (&skip)[kTB / G], float (&gate)[kTB / G]) {
+    constexpr int SPW = kTB / G;
+    if constexpr (PRE) {
+        const int rows = sg.t_len - tile * kTB;
+        const int D32 = static_cast<int>(sg.D);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(sg.sbar_seg + (rows > 0 ? static_cast<int64_t>(tile) * kTB * sg.D : 0),
+                      static_cast<uint32_t>(kTB) * static_cast<uint32_t>(D32) * 4u);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            float2 v;
+            float sb;
+            prep_element_pre<HAS_Z>(ru[i], rd[i], rz[i], rdy[i], sg.bias, sg.Dk, sg.softplus_on, v, skip[i], gate[i],
+                                    sb);
+            const int j = sg.w * SPW + i;
+            dst[j][sg.lane] = v;
+            const uint32_t off = (sg.dvalid && j < rows)
+                                     ? (static_cast<uint32_t>(j) * static_cast<uint32_t>(D32) +
+                                        static_cast<uint32_t>(sg.lane)) * 4u
+                                     : kNoStore;
+            buffer_store_act(sb, rs, off, 0.0f);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            float2 v;
+            prep_element<HAS_Z>(ru[i], rd[i], rz[i], sg.bias, sg.Dk, sg.softplus_on, v, skip[i], gate[i]);
+            dst[sg.w * SPW + i][sg.lane] = v;
+        }
+    }
+}
+
+// Sum of the G partial readouts plus the skip term, times the gate, of this
+// wave's rows of segment tile `tile` -> y (pre-pass: dz).
+template <typename T, int NG, int G, bool HAS_Z, bool PRE>
+__device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
+                                            const float (&part)[kTB / G][G], const float (&skip)[kTB / G],
+                                            const float (&gate)[kTB / G]) {
+    constexpr int SPW = kTB / G;
+    const int rows = tile >= 0 ? sg.t_len - tile * kTB : 0;  // tile -1: nothing
+    const int D32 = static_cast<int>(sg.D);
+    const __amdgpu_buffer_rsrc_t ry =
+        make_rsrc(sg.y_seg + (rows > 0 ? static_cast<int64_t>(tile) * kTB * sg.D : 0),
+                  static_cast<uint32_t>(kTB) * static_cast<uint32_t>(D32) * sizeof(T));
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        float s = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) s += part[i][g];
+        const int j = sg.w * SPW + i;
+        const bool store = sg.dvalid && j < rows && (!PRE || HAS_Z);
+        const uint32_t off = store ? (static_cast<uint32_t>(j) * static_cast<uint32_t>(D32) +
+                                      static_cast<uint32_t>(sg.lane)) * static_cast<uint32_t>(sizeof(T))
+                                   : kNoStore;
+        buffer_store_act((s + skip[i]) * gate[i], ry, off, T{});
+    }
+}
+
+// Interval of segment tile k (software pipeline, one barrier per tile):
+//  * LDS reads first: the partial readouts of tile k - 1 and (Delta, Delta*u)
+//    of tile k + 1 (prepared in the previous interval), so the LDS latency of
+//    the next tile overlaps this tile's recurrence;
+//  * the front end of tile k + 2 into the other LDS buffer;
+//  * loads of tile k + 1's Bm/Cm and tile k + 3's raw inputs;
+//  * the recurrence of tile k from registers; tile k - 1's rows finished.
+// Work that does not exist (tiles past the end, tile -1) runs on zeros and
+// stores to out-of-range offsets instead of branching.
+// ddt holds tile k's (Delta, Delta*u); ddt_next receives tile k + 1's (two
+// register sets used alternately by consecutive intervals, so nothing is copied).
 template <bool FULL, typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void fwd_interval(const FwdInterval<T, NG, G, HAS_Z, PRE>& it, int nval,
+__device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int k, int nval,
                                              const float (&A2)[NG], float (&h)[NG], FwdRegs<T, NG, G>& r,
+                                             const float2 (&ddt)[kTB], float2 (&ddt_next)[kTB],
                                              float2 (&sDD)[2][kTB][64], float (&sP)[2][G][kTB][64]) {
     constexpr int SPW = kTB / G;
-    const int cur = it.k & 1, prv = cur ^ 1;
-    const int lane = it.lane, w = it.w;
-    float2 ddt[kTB];
-#pragma unroll
-    for (int j = 0; j < kTB; ++j) ddt[j] = sDD[cur][j][lane];
+    const int cur = k & 1, prv = cur ^ 1;
+    const int lane = sg.lane, w = sg.w;
     float part[SPW][G];
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
 #pragma unroll
         for (int g = 0; g < G; ++g) part[i][g] = sP[prv][g][w * SPW + i][lane];
+#pragma unroll
+    for (int j = 0; j < kTB; ++j) ddt_next[j] = sDD[prv][j][lane];  // tile k + 1 sits in buffer (k + 1) & 1
     float Bt[NG], Ct[NG];
     unpack_lane_row<T, NG>(r.qb, Bt);
     unpack_lane_row<T, NG>(r.qc, Ct);
-    fetch_tile_rows<T, NG>(it.Bm, it.row0 + kTB, it.last_row, it.N, it.n0, lane, r.qb);
-    fetch_tile_rows<T, NG>(it.Cm, it.row0 + kTB, it.last_row, it.N, it.n0, lane, r.qc);
-    float skip_n[SPW], gate_n[SPW];
-    const int D32 = static_cast<int>(it.D);
-    if constexpr (PRE) {
-        // rows of tile k + 1; sbar goes straight to memory (rows past the end: out of range)
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(it.sbar_next, static_cast<uint32_t>(kTB * D32 * 4));
-        const int rows_next = it.t_len - (it.k + 1) * kTB;
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            float2 v;
-            float sb;
-            prep_element_pre<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], r.rdy[i], it.bias, it.Dk, it.softplus_on, v,
-                                    skip_n[i], gate_n[i], sb);
-            sDD[prv][w * SPW + i][lane] = v;
-            const int j = w * SPW + i;
-            const uint32_t off = (it.dvalid && j < rows_next) ? static_cast<uint32_t>((j * D32 + lane) * 4) : kNoStore;
-            buffer_store_act(sb, rs, off, 0.0f);
-        }
-        // the state before tile k
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(it.ckpt_tile, static_cast<uint32_t>(64 * it.N * 4));
+    fetch_bc(sg, k + 1, r.qb, r.qc);
+    float skip_nn[SPW], gate_nn[SPW];
+    prep_rows(sg, k + 2, r.ru, r.rd, r.rz, r.rdy, sDD[cur], skip_nn, gate_nn);  // buffer (k + 2) & 1 == k & 1
+    fetch_rows(sg, k + 3, r.ru, r.rd, r.rz, r.rdy);
+    if constexpr (PRE) {  // the state before tile k
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(sg.ckpt_seg + static_cast<int64_t>(k) * sg.D * sg.N, static_cast<uint32_t>(64 * sg.N * 4));
 #pragma unroll
         for (int q = 0; q < NG; ++q)
-            buffer_store_act(h[q], rc, it.dvalid ? static_cast<uint32_t>((lane * it.N + it.n0 + q) * 4) : kNoStore,
-                             0.0f);
-    } else {
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            float2 v;
-            prep_element<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], it.bias, it.Dk, it.softplus_on, v, skip_n[i],
-                                gate_n[i]);
-            sDD[prv][w * SPW + i][lane] = v;
-        }
+            buffer_store_act(h[q], rc,
+                             sg.dvalid ? static_cast<uint32_t>((lane * sg.N + sg.n0 + q) * 4) : kNoStore, 0.0f);
     }
-    fetch_rows_clamped<T, SPW, HAS_Z, PRE>(it.u_chunk, it.d_chunk, it.z_chunk, it.dy_chunk, it.k + 2, it.ntiles,
-                                           it.t_len, it.D, w * SPW, it.lo, r.ru, r.rd, r.rz, r.rdy);
     fwd_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, nval, w, lane, A2, h, Bt, Ct, ddt, sP[cur]);
-    {
-        // tile k - 1 (none when k == 0: every lane stores out of range)
-        // (pre-pass: y_prev points into dz, and s * dzf is the gate gradient)
-        const __amdgpu_buffer_rsrc_t ry = make_rsrc(it.y_prev, static_cast<uint32_t>(kTB * it.row_bytes));
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            float s = 0.0f;
-#pragma unroll
-            for (int g = 0; g < G; ++g) s += part[i][g];
-            const int j = w * SPW + i;
-            const bool store = it.dvalid && it.k > 0 && (!PRE || HAS_Z);
-            const uint32_t off = store ? static_cast<uint32_t>((j * D32 + lane) * static_cast<int>(sizeof(T)))
-                                       : kNoStore;
-            buffer_store_act((s + r.skip_p[i]) * r.gate_p[i], ry, off, T{});
-        }
-    }
+    finish_rows(sg, k - 1, part, r.skip_p, r.gate_p);  // k == 0: nothing stored
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
         r.skip_p[i] = r.skip_c[i];
         r.gate_p[i] = r.gate_c[i];
-        r.skip_c[i] = skip_n[i];
-        r.gate_c[i] = gate_n[i];
+        r.skip_c[i] = r.skip_n[i];
+        r.gate_c[i] = r.gate_n[i];
+        r.skip_n[i] = skip_nn[i];
+        r.gate_n[i] = gate_nn[i];
     }
 }
 
 // Runs steps [t_begin, t_end) of channel block `blk` (batch row b = blk /
 // dblocks, channels chan0 .. chan0 + 63) from the state in h, leaving the
-// final state in h.  Software-pipelined over tiles of kTB steps with one
-// barrier per tile: in the interval of tile k every wave prepares its rows of
-// tile k + 1, runs the recurrence of tile k and finishes its rows of tile
-// k - 1 (LDS double buffered), so the per-element work fills the latency gaps
-// of the recurrence's dependency chains.
+// final state in h.
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t t_begin, int64_t t_end,
                                             float (&h)[NG], float2 (&sDD)[2][kTB][64],
@@ -343,106 +428,98 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     constexpr int N = NG * G;
     constexpr int SPW = kTB / G;  // rows prepared and finished per wave per tile
 
-    const T* __restrict__ u = static_cast<const T*>(a.u);
-    const T* __restrict__ dl = static_cast<const T*>(a.delta);
-    const T* __restrict__ z = static_cast<const T*>(a.z);
-    const T* __restrict__ Bm = static_cast<const T*>(a.Bm);
-    const T* __restrict__ Cm = static_cast<const T*>(a.Cm);
-    T* __restrict__ y = static_cast<T*>(a.y);
-
-    const int lane = threadIdx.x & 63;
-    const int w = wave_id();
+    FwdSeg<T, NG, G, HAS_Z, PRE> sg;
+    sg.lane = threadIdx.x & 63;
+    sg.w = wave_id();
     const int64_t b = blk / a.dblocks;
     const int64_t chan0 = static_cast<int64_t>(blk % a.dblocks) * 64;
     const int64_t D = a.D, L = a.L;
-    const int D32 = static_cast<int>(D);
-    const bool dvalid = chan0 + lane < D;
-    const int lo = dvalid ? lane : static_cast<int>(D - 1 - chan0);  // clamped lane offset for loads
-    const int64_t dc = chan0 + lo;
-    const int n0 = w * NG;
+    sg.D = D;
+    sg.N = N;
+    sg.dvalid = chan0 + sg.lane < D;
+    const int64_t dc = imin64(chan0 + sg.lane, D - 1);
+    sg.n0 = sg.w * NG;
+    const int lane = sg.lane, w = sg.w, n0 = sg.n0;
 
     float A2[NG];
 #pragma unroll
     for (int k = 0; k < NG; ++k) A2[k] = a.A[dc * N + n0 + k] * kLog2e;
-    const float bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
-    const float Dk = a.Dskip ? a.Dskip[dc] : 0.0f;
-    const int softplus_on = a.softplus;
+    sg.bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
+    sg.Dk = a.Dskip ? a.Dskip[dc] : 0.0f;
+    sg.softplus_on = a.softplus;
 
-    const int t_len = static_cast<int>(t_end - t_begin);
-    const int ntiles = (t_len + kTB - 1) / kTB;
+    sg.t_len = static_cast<int>(t_end - t_begin);
+    sg.ntiles = (sg.t_len + kTB - 1) / kTB;
+    sg.seg_elems = static_cast<int64_t>(sg.t_len) * D - chan0;
     const int64_t row_begin = b * L + t_begin;  // row index of (b, t_begin)
-    const int64_t last_row = row_begin + t_len - 1;
-    const int64_t chunk_off = row_begin * D + chan0;  // element (b, t_begin, chan0)
-    const T* u_chunk = u + chunk_off;
-    const T* d_chunk = dl + chunk_off;
-    const T* z_chunk = HAS_Z ? z + chunk_off : nullptr;
-    const T* dy_chunk = PRE ? static_cast<const T*>(a.dy) + chunk_off : nullptr;
-    const int row_bytes = D32 * static_cast<int>(sizeof(T));
-    const int64_t gtile0 = t_begin / kTB;  // segments start on tile boundaries
+    const int64_t seg_off = row_begin * D + chan0;  // element (b, t_begin, chan0)
+    sg.u_seg = static_cast<const T*>(a.u) + seg_off;
+    sg.d_seg = static_cast<const T*>(a.delta) + seg_off;
+    sg.z_seg = HAS_Z ? static_cast<const T*>(a.z) + seg_off : nullptr;
+    sg.dy_seg = PRE ? static_cast<const T*>(a.dy) + seg_off : nullptr;
+    sg.y_seg = static_cast<T*>(a.y) + seg_off;
+    sg.Bm_seg = static_cast<const T*>(a.Bm) + row_begin * N;
+    sg.Cm_seg = static_cast<const T*>(a.Cm) + row_begin * N;
+    sg.sbar_seg = PRE ? a.sbar + seg_off : nullptr;
+    sg.ckpt_seg = PRE ? a.ckpt + ((b * a.tiles + t_begin / kTB) * D + chan0) * N : nullptr;
+    const int D32 = static_cast<int>(D);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+        sg.row_off[i] = (static_cast<uint32_t>(w * SPW + i) * static_cast<uint32_t>(D32) + static_cast<uint32_t>(lane)) *
+                        static_cast<uint32_t>(sizeof(T));
+    sg.bc_off = static_cast<uint32_t>(((lane & (kTB - 1)) * N + n0) * static_cast<int>(sizeof(T)));
 
     __syncthreads();  // LDS is reused from a previous segment
-    // ---- prologue: tile 0 prepared, tile 1 raw inputs and tile 0 Bm/Cm in flight
+    // ---- prologue: tiles 0 and 1 prepared, tile 0's (Delta, Delta*u) in
+    // registers, tile 0's Bm/Cm and tile 2's raw inputs in flight
     FwdRegs<T, NG, G> r;
-    fetch_rows_clamped<T, SPW, HAS_Z, PRE>(u_chunk, d_chunk, z_chunk, dy_chunk, 0, ntiles, t_len, D, w * SPW, lo,
-                                           r.ru, r.rd, r.rz, r.rdy);
-    fetch_tile_rows<T, NG>(Bm, row_begin, last_row, N, n0, lane, r.qb);
-    fetch_tile_rows<T, NG>(Cm, row_begin, last_row, N, n0, lane, r.qc);
-    if constexpr (PRE) {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.sbar + chunk_off, static_cast<uint32_t>(kTB * D32 * 4));
+    {
+        float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];
+        fetch_bc(sg, 0, r.qb, r.qc);
+        fetch_rows(sg, 0, ru, rd, rz, rdy);
+        fetch_rows(sg, 1, r.ru, r.rd, r.rz, r.rdy);
+        prep_rows(sg, 0, ru, rd, rz, rdy, sDD[0], r.skip_c, r.gate_c);
+        prep_rows(sg, 1, r.ru, r.rd, r.rz, r.rdy, sDD[1], r.skip_n, r.gate_n);
+        fetch_rows(sg, 2, r.ru, r.rd, r.rz, r.rdy);
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            float2 v;
-            float sb;
-            prep_element_pre<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], r.rdy[i], bias, Dk, softplus_on, v, r.skip_c[i],
-                                    r.gate_c[i], sb);
-            sDD[0][w * SPW + i][lane] = v;
-            const int j = w * SPW + i;
-            buffer_store_act(sb, rs, (dvalid && j < t_len) ? static_cast<uint32_t>((j * D32 + lane) * 4) : kNoStore,
-                             0.0f);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            float2 v;
-            prep_element<HAS_Z>(r.ru[i], r.rd[i], r.rz[i], bias, Dk, softplus_on, v, r.skip_c[i], r.gate_c[i]);
-            sDD[0][w * SPW + i][lane] = v;  // rows past the segment end hold finite junk, never used
-        }
+        for (int i = 0; i < SPW; ++i) r.skip_p[i] = r.gate_p[i] = 0.0f;
     }
-    fetch_rows_clamped<T, SPW, HAS_Z, PRE>(u_chunk, d_chunk, z_chunk, dy_chunk, 1, ntiles, t_len, D, w * SPW, lo,
-                                           r.ru, r.rd, r.rz, r.rdy);
     __syncthreads();
+    float2 ddtA[kTB], ddtB[kTB];
+#pragma unroll
+    for (int j = 0; j < kTB; ++j) ddtA[j] = sDD[0][j][lane];
+    __syncthreads();  // every wave has read buffer 0 before interval 0 refills it
 
-    for (int k = 0; k < ntiles; ++k) {
-        const int nval = min(kTB, t_len - k * kTB);
-        const int64_t row0 = row_begin + static_cast<int64_t>(k) * kTB;
-        FwdInterval<T, NG, G, HAS_Z, PRE> it{
-            k, ntiles, t_len, w, lane, lo, dvalid, row_bytes, softplus_on, bias, Dk, D, N, n0, row0, last_row,
-            u_chunk, d_chunk, z_chunk, Bm, Cm, y + (k > 0 ? row0 - kTB : row0) * D + chan0, dy_chunk,
-            PRE ? a.sbar + (k + 1 < ntiles ? row0 + kTB : row0) * D + chan0 : nullptr,
-            PRE ? a.ckpt + ((b * a.tiles + gtile0 + k) * D + chan0) * N : nullptr};
-        if (nval == kTB)
-            fwd_interval<true>(it, kTB, A2, h, r, sDD, sP);
-        else
-            fwd_interval<false>(it, nval, A2, h, r, sDD, sP);
+    // full tiles in pairs (even tiles compute from ddtA, odd ones from ddtB),
+    // then what is left: at most one full tile and a ragged last tile
+    const int nfull = sg.t_len / kTB;
+    int k = 0;
+    for (; k + 2 <= nfull; k += 2) {
+        fwd_interval<true>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
         __syncthreads();
+        fwd_interval<true>(sg, k + 1, kTB, A2, h, r, ddtB, ddtA, sDD, sP);
+        __syncthreads();
+    }
+    if (k < sg.ntiles) {
+        if (k < nfull)
+            fwd_interval<true>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+        else
+            fwd_interval<false>(sg, k, sg.t_len - k * kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+        __syncthreads();
+        if (k + 1 < sg.ntiles) {  // ragged last tile after a full one
+            fwd_interval<false>(sg, k + 1, sg.t_len - (k + 1) * kTB, A2, h, r, ddtB, ddtA, sDD, sP);
+            __syncthreads();
+        }
     }
     // ---- epilogue: finish the last tile
     {
-        const int klast = ntiles - 1;
-        const int nval = t_len - klast * kTB;
-        const int64_t row0 = row_begin + static_cast<int64_t>(klast) * kTB;
-        const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + row0 * D + chan0, kTB * row_bytes);
+        const int klast = sg.ntiles - 1;
+        float part[SPW][G];
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int j = w * SPW + i;
-            float s = 0.0f;
+        for (int i = 0; i < SPW; ++i)
 #pragma unroll
-            for (int g = 0; g < G; ++g) s += sP[klast & 1][g][j][lane];
-            const uint32_t off = (dvalid && j < nval && (!PRE || HAS_Z))
-                                     ? static_cast<uint32_t>((j * D32 + lane) * static_cast<int>(sizeof(T)))
-                                     : kNoStore;
-            buffer_store_act((s + r.skip_p[i]) * r.gate_p[i], ry, off, T{});
-        }
+            for (int g = 0; g < G; ++g) part[i][g] = sP[klast & 1][g][w * SPW + i][lane];
+        finish_rows(sg, klast, part, r.skip_p, r.gate_p);
     }
 }
 
@@ -595,7 +672,7 @@ __global__ __launch_bounds__(64 * G) void scan_chunk_state_kernel(FwdKArgs a) {
     const int64_t last_row = row_begin + t_len - 1;
     float ru[SPW], rd[SPW], rz[SPW];
     uint32_t qb[W];
-    fetch_rows<T, SPW>(u, dl, static_cast<const T*>(nullptr), row_begin * D + chan0, w * SPW, t_len, D32, lo,
+    fetch_rows_ptr<T, SPW>(u, dl, static_cast<const T*>(nullptr), row_begin * D + chan0, w * SPW, t_len, D32, lo,
                        ru, rd, rz);
     fetch_tile_rows<T, NG>(Bm, row_begin, last_row, N, n0, lane, qb);
     for (int tile = 0; tile < ntiles; ++tile) {
@@ -613,7 +690,7 @@ __global__ __launch_bounds__(64 * G) void scan_chunk_state_kernel(FwdKArgs a) {
         float Bt[NG];
         unpack_lane_row<T, NG>(qb, Bt);
         if (tile + 1 < ntiles) {
-            fetch_rows<T, SPW>(u, dl, static_cast<const T*>(nullptr), (row0 + kTB) * D + chan0, w * SPW,
+            fetch_rows_ptr<T, SPW>(u, dl, static_cast<const T*>(nullptr), (row0 + kTB) * D + chan0, w * SPW,
                                t_len - (tile + 1) * kTB, D32, lo, ru, rd, rz);
             fetch_tile_rows<T, NG>(Bm, row0 + kTB, last_row, N, n0, lane, qb);
         }
