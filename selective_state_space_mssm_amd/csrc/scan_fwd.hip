@@ -42,6 +42,14 @@ namespace {
 
 constexpr int kTB = 16;  // time steps per tile (= lanes per DPP row)
 
+// Waves of a workgroup that also run the per-element front end (softplus,
+// gate, loads of u/delta/z) and the finishing of rows (sum of partial
+// readouts, store); the others run only the recurrence of their states.
+#ifndef MSSM_FWD_FRONT_DIV
+#define MSSM_FWD_FRONT_DIV 2
+#endif
+constexpr int front_waves(int G) { return G >= MSSM_FWD_FRONT_DIV ? G / MSSM_FWD_FRONT_DIV : 1; }
+
 struct FwdKArgs {
     const void* u;
     const void* delta;
@@ -228,7 +236,7 @@ __device__ __forceinline__ void prep_element_pre(float uu, float dd, float zz, f
 // lane's constant offsets.
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 struct FwdSeg {
-    static constexpr int SPW = kTB / G;
+    static constexpr int SPW = kTB / front_waves(G);
     int ntiles, t_len, w, lane;
     bool dvalid;
     int softplus_on;
@@ -252,7 +260,7 @@ struct FwdSeg {
 // Registers carried from one tile interval to the next.
 template <typename T, int NG, int G>
 struct FwdRegs {
-    static constexpr int SPW = kTB / G;
+    static constexpr int SPW = kTB / front_waves(G);
     float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];   // raw inputs of the tile prepared next (k + 2)
     uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next recurrence tile
     // skip term and gate (pre-pass: dz factor) of the rows of tiles k + 1 (n),
@@ -263,9 +271,9 @@ struct FwdRegs {
 // Raw inputs of this wave's rows of segment tile `tile` (zeros past the end).
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fetch_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                           float (&ru)[kTB / G], float (&rd)[kTB / G], float (&rz)[kTB / G],
-                                           float (&rdy)[kTB / G]) {
-    constexpr int SPW = kTB / G;
+                                           float (&ru)[kTB / front_waves(G)], float (&rd)[kTB / front_waves(G)],
+                                           float (&rz)[kTB / front_waves(G)], float (&rdy)[kTB / front_waves(G)]) {
+    constexpr int SPW = kTB / front_waves(G);
     const int64_t first = static_cast<int64_t>(tile) * kTB * sg.D;       // first element of the tile
     const int64_t bytes = (sg.seg_elems - first) * static_cast<int64_t>(sizeof(T));
     const __amdgpu_buffer_rsrc_t ru_r = range_rsrc(sg.u_seg + first, bytes);
@@ -303,11 +311,11 @@ __device__ __forceinline__ void fetch_bc(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg,
 // pre-pass, sbar to memory).  Rows past the end hold finite values that are
 // never used.
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile, const float (&ru)[kTB / G],
-                                          const float (&rd)[kTB / G], const float (&rz)[kTB / G],
-                                          const float (&rdy)[kTB / G], float2 (&dst)[kTB][64],
-                                          float (&skip)[kTB / G], float (&gate)[kTB / G]) {
-    constexpr int SPW = kTB / G;
+__device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile, const float (&ru)[kTB / front_waves(G)],
+                                          const float (&rd)[kTB / front_waves(G)], const float (&rz)[kTB / front_waves(G)],
+                                          const float (&rdy)[kTB / front_waves(G)], float2 (&dst)[kTB][64],
+                                          float (&skip)[kTB / front_waves(G)], float (&gate)[kTB / front_waves(G)]) {
+    constexpr int SPW = kTB / front_waves(G);
     if constexpr (PRE) {
         const int rows = sg.t_len - tile * kTB;
         const int D32 = static_cast<int>(sg.D);
@@ -342,9 +350,9 @@ __device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg
 // wave's rows of segment tile `tile` -> y (pre-pass: dz).
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                            const float (&part)[kTB / G][G], const float (&skip)[kTB / G],
-                                            const float (&gate)[kTB / G]) {
-    constexpr int SPW = kTB / G;
+                                            const float (&part)[kTB / front_waves(G)][G], const float (&skip)[kTB / front_waves(G)],
+                                            const float (&gate)[kTB / front_waves(G)]) {
+    constexpr int SPW = kTB / front_waves(G);
     const int rows = tile >= 0 ? sg.t_len - tile * kTB : 0;  // tile -1: nothing
     const int D32 = static_cast<int>(sg.D);
     const __amdgpu_buffer_rsrc_t ry =
@@ -375,19 +383,22 @@ __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& 
 // stores to out-of-range offsets instead of branching.
 // ddt holds tile k's (Delta, Delta*u); ddt_next receives tile k + 1's (two
 // register sets used alternately by consecutive intervals, so nothing is copied).
-template <bool FULL, typename T, int NG, int G, bool HAS_Z, bool PRE>
+// FRONT: this wave also runs the front end and the finishing of its rows.
+template <bool FULL, bool FRONT, typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int k, int nval,
                                              const float (&A2)[NG], float (&h)[NG], FwdRegs<T, NG, G>& r,
                                              const float2 (&ddt)[kTB], float2 (&ddt_next)[kTB],
                                              float2 (&sDD)[2][kTB][64], float (&sP)[2][G][kTB][64]) {
-    constexpr int SPW = kTB / G;
+    constexpr int SPW = kTB / front_waves(G);
     const int cur = k & 1, prv = cur ^ 1;
     const int lane = sg.lane, w = sg.w;
     float part[SPW][G];
+    if constexpr (FRONT) {
 #pragma unroll
-    for (int i = 0; i < SPW; ++i)
+        for (int i = 0; i < SPW; ++i)
 #pragma unroll
-        for (int g = 0; g < G; ++g) part[i][g] = sP[prv][g][w * SPW + i][lane];
+            for (int g = 0; g < G; ++g) part[i][g] = sP[prv][g][w * SPW + i][lane];
+    }
 #pragma unroll
     for (int j = 0; j < kTB; ++j) ddt_next[j] = sDD[prv][j][lane];  // tile k + 1 sits in buffer (k + 1) & 1
     float Bt[NG], Ct[NG];
@@ -395,8 +406,10 @@ __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>&
     unpack_lane_row<T, NG>(r.qc, Ct);
     fetch_bc(sg, k + 1, r.qb, r.qc);
     float skip_nn[SPW], gate_nn[SPW];
-    prep_rows(sg, k + 2, r.ru, r.rd, r.rz, r.rdy, sDD[cur], skip_nn, gate_nn);  // buffer (k + 2) & 1 == k & 1
-    fetch_rows(sg, k + 3, r.ru, r.rd, r.rz, r.rdy);
+    if constexpr (FRONT) {
+        prep_rows(sg, k + 2, r.ru, r.rd, r.rz, r.rdy, sDD[cur], skip_nn, gate_nn);  // buffer (k + 2) & 1 == k & 1
+        fetch_rows(sg, k + 3, r.ru, r.rd, r.rz, r.rdy);
+    }
     if constexpr (PRE) {  // the state before tile k
         const __amdgpu_buffer_rsrc_t rc =
             make_rsrc(sg.ckpt_seg + static_cast<int64_t>(k) * sg.D * sg.N, static_cast<uint32_t>(64 * sg.N * 4));
@@ -406,27 +419,29 @@ __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>&
                              sg.dvalid ? static_cast<uint32_t>((lane * sg.N + sg.n0 + q) * 4) : kNoStore, 0.0f);
     }
     fwd_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, nval, w, lane, A2, h, Bt, Ct, ddt, sP[cur]);
-    finish_rows(sg, k - 1, part, r.skip_p, r.gate_p);  // k == 0: nothing stored
+    if constexpr (FRONT) {
+        finish_rows(sg, k - 1, part, r.skip_p, r.gate_p);  // k == 0: nothing stored
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        r.skip_p[i] = r.skip_c[i];
-        r.gate_p[i] = r.gate_c[i];
-        r.skip_c[i] = r.skip_n[i];
-        r.gate_c[i] = r.gate_n[i];
-        r.skip_n[i] = skip_nn[i];
-        r.gate_n[i] = gate_nn[i];
+        for (int i = 0; i < SPW; ++i) {
+            r.skip_p[i] = r.skip_c[i];
+            r.gate_p[i] = r.gate_c[i];
+            r.skip_c[i] = r.skip_n[i];
+            r.gate_c[i] = r.gate_n[i];
+            r.skip_n[i] = skip_nn[i];
+            r.gate_n[i] = gate_nn[i];
+        }
     }
 }
 
 // Runs steps [t_begin, t_end) of channel block `blk` (batch row b = blk /
 // dblocks, channels chan0 .. chan0 + 63) from the state in h, leaving the
 // final state in h.
-template <typename T, int NG, int G, bool HAS_Z, bool PRE>
+template <bool FRONT, typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t t_begin, int64_t t_end,
                                             float (&h)[NG], float2 (&sDD)[2][kTB][64],
                                             float (&sP)[2][G][kTB][64]) {
     constexpr int N = NG * G;
-    constexpr int SPW = kTB / G;  // rows prepared and finished per wave per tile
+    constexpr int SPW = kTB / front_waves(G);  // rows prepared and finished per front wave per tile
 
     FwdSeg<T, NG, G, HAS_Z, PRE> sg;
     sg.lane = threadIdx.x & 63;
@@ -473,9 +488,9 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     // ---- prologue: tiles 0 and 1 prepared, tile 0's (Delta, Delta*u) in
     // registers, tile 0's Bm/Cm and tile 2's raw inputs in flight
     FwdRegs<T, NG, G> r;
-    {
+    fetch_bc(sg, 0, r.qb, r.qc);
+    if constexpr (FRONT) {
         float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];
-        fetch_bc(sg, 0, r.qb, r.qc);
         fetch_rows(sg, 0, ru, rd, rz, rdy);
         fetch_rows(sg, 1, r.ru, r.rd, r.rz, r.rdy);
         prep_rows(sg, 0, ru, rd, rz, rdy, sDD[0], r.skip_c, r.gate_c);
@@ -495,24 +510,24 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     const int nfull = sg.t_len / kTB;
     int k = 0;
     for (; k + 2 <= nfull; k += 2) {
-        fwd_interval<true>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+        fwd_interval<true, FRONT>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
         __syncthreads();
-        fwd_interval<true>(sg, k + 1, kTB, A2, h, r, ddtB, ddtA, sDD, sP);
+        fwd_interval<true, FRONT>(sg, k + 1, kTB, A2, h, r, ddtB, ddtA, sDD, sP);
         __syncthreads();
     }
     if (k < sg.ntiles) {
         if (k < nfull)
-            fwd_interval<true>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+            fwd_interval<true, FRONT>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
         else
-            fwd_interval<false>(sg, k, sg.t_len - k * kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+            fwd_interval<false, FRONT>(sg, k, sg.t_len - k * kTB, A2, h, r, ddtA, ddtB, sDD, sP);
         __syncthreads();
         if (k + 1 < sg.ntiles) {  // ragged last tile after a full one
-            fwd_interval<false>(sg, k + 1, sg.t_len - (k + 1) * kTB, A2, h, r, ddtB, ddtA, sDD, sP);
+            fwd_interval<false, FRONT>(sg, k + 1, sg.t_len - (k + 1) * kTB, A2, h, r, ddtB, ddtA, sDD, sP);
             __syncthreads();
         }
     }
     // ---- epilogue: finish the last tile
-    {
+    if constexpr (FRONT) {
         const int klast = sg.ntiles - 1;
         float part[SPW][G];
 #pragma unroll
@@ -604,7 +619,11 @@ __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
             for (int k = 0; k < NG; ++k)
                 h[k] = __hip_atomic_load(carry_lane + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        fwd_segment<T, NG, G, HAS_Z, PRE>(a, blk, t_begin, t_end, h, sDD, sP);
+        // the same barriers on both paths: the roles differ only in work between them
+        if (wave_id() < front_waves(G))
+            fwd_segment<true, T, NG, G, HAS_Z, PRE>(a, blk, t_begin, t_end, h, sDD, sP);
+        else
+            fwd_segment<false, T, NG, G, HAS_Z, PRE>(a, blk, t_begin, t_end, h, sDD, sP);
         if (to == kFinal) {
             if (a.h_final && chan0 + lane < a.D) {
                 float* hf = a.h_final + (b * a.D + chan0 + lane) * N + n0;
