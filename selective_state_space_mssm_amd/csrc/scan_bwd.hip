@@ -43,6 +43,15 @@ namespace {
 
 constexpr int kTB = 16;  // tile length (checkpoint spacing, VGPR history depth)
 
+// Waves of a workgroup that also run the per-element front end and the
+// finishing of rows (du, ddelta); the others run only the recompute and the
+// adjoint of their states.  (Issue arbitration favours the waves dispatched
+// first, so those get the extra work.)
+#ifndef MSSM_BWD_FRONT_DIV
+#define MSSM_BWD_FRONT_DIV 2
+#endif
+constexpr int front_waves(int G) { return G >= MSSM_BWD_FRONT_DIV ? G / MSSM_BWD_FRONT_DIV : 1; }
+
 struct BwdKArgs {
     const void* u;
     const void* delta;
@@ -329,7 +338,7 @@ __device__ __forceinline__ void rev_steps(std::integer_sequence<int, I...>, cons
 // Registers carried from one reverse interval to the next.
 template <typename T, int NG, int G>
 struct RevRegs {
-    static constexpr int SPW = kTB / G;
+    static constexpr int SPW = kTB / front_waves(G);
     float ru[SPW], rd[SPW], rs[SPW];  // raw u, delta, sbar of the next tile to prepare
     uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next tile
     float hin_next[NG];               // checkpoint of the next tile
@@ -365,19 +374,20 @@ struct RevBlock {
 //   B. (after a barrier: the partial sums of tile k + 1 are consumed) the
 //      reverse steps of tile k.
 // FULL: all 16 steps of the tile exist (every tile but a ragged last one).
-template <bool FULL, typename T, int NG, int G>
+// FRONT: this wave also prepares and finishes rows.
+template <bool FULL, bool FRONT, typename T, int NG, int G>
 __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int nval, const float (&A2)[NG],
                                              const float (&Aval)[NG], RevRegs<T, NG, G>& r,
                                              float4 (&sX)[2][kTB][64], float2 (&sLQ)[G][kTB][64]) {
     constexpr int N = NG * G;
-    constexpr int SPW = kTB / G;
+    constexpr int SPW = kTB / front_waves(G);
     const int cur = k & 1, prv = cur ^ 1;
     const int w = bk.w, lane = bk.lane;
     // ---- A
     float4 xt[kTB];
 #pragma unroll
     for (int j = 0; j < kTB; ++j) xt[j] = sX[cur][j][lane];
-    if (k + 1 < bk.ntiles) {
+    if (FRONT && k + 1 < bk.ntiles) {
         const int64_t off = static_cast<int64_t>(k + 1) * kTB * bk.D32;
         finish_rows<T, SPW, G>(sLQ, r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32 - (k + 1) * kTB), bk.Dk,
                                bk.du_b + off, bk.dd_b + off, bk.D32, r.accD, r.accBias);
@@ -403,8 +413,10 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
         rec_steps<NG, FULL>(std::make_integer_sequence<int, kTB>{}, nval, A2, h, Bt, xt, hist, ahist);
     }
     RowKeep keep_n[SPW];
-    prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, w, lane, sX[prv], keep_n);  // k == 0: unused
-    fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, k - 2, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
+    if constexpr (FRONT) {
+        prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, w, lane, sX[prv], keep_n);  // k == 0: unused
+        fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, k - 2, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
+    }
     __syncthreads();
     // ---- B
     {
@@ -417,22 +429,64 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
     }
 #pragma unroll
     for (int q = 0; q < NG; ++q) r.anext[q] = ahist[0][q];
+    if constexpr (FRONT) {
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        r.keep_p[i] = r.keep_c[i];
-        r.keep_c[i] = keep_n[i];
+        for (int i = 0; i < SPW; ++i) {
+            r.keep_p[i] = r.keep_c[i];
+            r.keep_c[i] = keep_n[i];
+        }
     }
+}
+
+// The reverse walk over all tiles (FRONT: with the front end and finishing).
+// Both roles execute the same barriers.
+template <bool FRONT, typename T, int NG, int G>
+__device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)[NG], const float (&Aval)[NG],
+                                        RevRegs<T, NG, G>& r, float4 (&sX)[2][kTB][64],
+                                        float2 (&sLQ)[G][kTB][64]) {
+    constexpr int N = NG * G;
+    constexpr int SPW = kTB / front_waves(G);
+    const int w = bk.w, lane = bk.lane, n0 = bk.n0;
+    // ---- prologue: last tile prepared; its Bm/Cm/checkpoint and the next raw rows in flight
+    {
+        const int tl = bk.ntiles - 1;
+        const int64_t rowl = bk.row_b + static_cast<int64_t>(tl) * kTB;
+        if constexpr (FRONT)
+            fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
+        fetch_tile_rows<T, NG>(bk.Bm, rowl, bk.last_row, N, n0, lane, r.qb);
+        fetch_tile_rows<T, NG>(bk.Cm, rowl, bk.last_row, N, n0, lane, r.qc);
+#pragma unroll
+        for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tl * bk.ck_stride + q];
+        if constexpr (FRONT) {
+            prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, w, lane, sX[tl & 1], r.keep_c);
+            fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl - 1, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
+        }
+    }
+    __syncthreads();
+
+    for (int k = bk.ntiles - 1; k >= 0; --k) {
+        const int nval = min(kTB, bk.L32 - k * kTB);
+        if (nval == kTB)
+            rev_interval<true, FRONT>(bk, k, kTB, A2, Aval, r, sX, sLQ);
+        else
+            rev_interval<false, FRONT>(bk, k, nval, A2, Aval, r, sX, sLQ);
+        __syncthreads();
+    }
+    // ---- epilogue: finish tile 0
+    if constexpr (FRONT)
+        finish_rows<T, SPW, G>(sLQ, r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32), bk.Dk, bk.du_b, bk.dd_b,
+                               bk.D32, r.accD, r.accBias);
 }
 
 // Reverse kernel.  Grid: B * dblocks workgroups of 64 * G threads.
 template <typename T, int NG, int G>
 __global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
     constexpr int N = NG * G;
-    constexpr int SPW = kTB / G;
     static_assert(kTB % G == 0 && 16 % (2 * NG) == 0, "tile and batch must split evenly");
     __shared__ float4 sX[2][kTB][64];   // (Delta, Delta*u, sbar, -) per row and channel
     __shared__ float2 sLQ[G][kTB][64];  // per state group: (sum lam*Bm, sum A*lam*a*h_prev)
     __shared__ float sRed[2][G][64];
+    constexpr int SPW = kTB / front_waves(G);
 
     RevBlock<T> bk;
     bk.lane = threadIdx.x & 63;
@@ -480,31 +534,11 @@ __global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i) r.keep_p[i] = RowKeep{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // ---- prologue: last tile prepared; its Bm/Cm/checkpoint and the next raw rows in flight
-    {
-        const int tl = bk.ntiles - 1;
-        const int64_t rowl = bk.row_b + static_cast<int64_t>(tl) * kTB;
-        fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
-        fetch_tile_rows<T, NG>(bk.Bm, rowl, bk.last_row, N, n0, lane, r.qb);
-        fetch_tile_rows<T, NG>(bk.Cm, rowl, bk.last_row, N, n0, lane, r.qc);
-#pragma unroll
-        for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tl * bk.ck_stride + q];
-        prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, w, lane, sX[tl & 1], r.keep_c);
-        fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl - 1, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
-    }
-    __syncthreads();
-
-    for (int k = bk.ntiles - 1; k >= 0; --k) {
-        const int nval = min(kTB, bk.L32 - k * kTB);
-        if (nval == kTB)
-            rev_interval<true>(bk, k, kTB, A2, Aval, r, sX, sLQ);
-        else
-            rev_interval<false>(bk, k, nval, A2, Aval, r, sX, sLQ);
-        __syncthreads();
-    }
-    // ---- epilogue: finish tile 0, then the per-(b, d) results
-    finish_rows<T, SPW, G>(sLQ, r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32), bk.Dk, bk.du_b, bk.dd_b, bk.D32,
-                           r.accD, r.accBias);
+    if (w < front_waves(G))
+        rev_run<true>(bk, A2, Aval, r, sX, sLQ);
+    else
+        rev_run<false>(bk, A2, Aval, r, sX, sLQ);
+    // ---- per-(b, d) results
     if (bk.dvalid) {
         float* pa = a.pA + (b * D + dc) * N + n0;
 #pragma unroll
