@@ -365,20 +365,20 @@ struct RevBlock {
     float* pBC;
 };
 
-// Interval of tile k (tiles - 1 .. 0), between two barriers:
+// Interval of tile k (tiles - 1 .. 0), one barrier after it:
 //   A. read tile k's (Delta, Delta*u, sbar) from LDS; finish tile k + 1's
 //      rows from the partial sums its reverse steps left; recompute tile k's
 //      states from its checkpoint; prepare tile k - 1's rows into the other
 //      LDS buffer; issue the loads of tile k - 1's Bm/Cm/checkpoint and of
 //      tile k - 2's raw rows;
-//   B. (after a barrier: the partial sums of tile k + 1 are consumed) the
-//      reverse steps of tile k.
+//   B. the reverse steps of tile k, whose partial sums go to the other of
+//      the two partial-sum buffers (tile k + 1's are still being read).
 // FULL: all 16 steps of the tile exist (every tile but a ragged last one).
 // FRONT: this wave also prepares and finishes rows.
 template <bool FULL, bool FRONT, typename T, int NG, int G>
 __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int nval, const float (&A2)[NG],
                                              const float (&Aval)[NG], RevRegs<T, NG, G>& r,
-                                             float4 (&sX)[2][kTB][64], float2 (&sLQ)[G][kTB][64]) {
+                                             float4 (&sX)[2][kTB][64], float2 (&sLQ)[2][G][kTB][64]) {
     constexpr int N = NG * G;
     constexpr int SPW = kTB / front_waves(G);
     const int cur = k & 1, prv = cur ^ 1;
@@ -389,7 +389,7 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
     for (int j = 0; j < kTB; ++j) xt[j] = sX[cur][j][lane];
     if (FRONT && k + 1 < bk.ntiles) {
         const int64_t off = static_cast<int64_t>(k + 1) * kTB * bk.D32;
-        finish_rows<T, SPW, G>(sLQ, r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32 - (k + 1) * kTB), bk.Dk,
+        finish_rows<T, SPW, G>(sLQ[prv], r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32 - (k + 1) * kTB), bk.Dk,
                                bk.du_b + off, bk.dd_b + off, bk.D32, r.accD, r.accBias);
     }
     float Bt[NG], Ct[NG], hin[NG];
@@ -417,11 +417,10 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
         prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, w, lane, sX[prv], keep_n);  // k == 0: unused
         fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, k - 2, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
     }
-    __syncthreads();
-    // ---- B
+    // ---- B (partials of tile k go to the other buffer than those of tile k + 1 just read)
     {
         const int64_t row0 = bk.row_b + static_cast<int64_t>(k) * kTB;
-        RevCtx<NG, G> c{Aval, Bt, Ct, xt, hist, ahist, hin, r.anext, sLQ,
+        RevCtx<NG, G> c{Aval, Bt, Ct, xt, hist, ahist, hin, r.anext, sLQ[cur],
                         make_rsrc(bk.pBC + (row0 * bk.dblocks + bk.dblk) * 2 * N,
                                   static_cast<uint32_t>(kTB) * bk.dblocks * 2u * N * 4u),
                         nval, w, lane, bk.dblocks, N, bk.n0};
@@ -443,7 +442,7 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
 template <bool FRONT, typename T, int NG, int G>
 __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)[NG], const float (&Aval)[NG],
                                         RevRegs<T, NG, G>& r, float4 (&sX)[2][kTB][64],
-                                        float2 (&sLQ)[G][kTB][64]) {
+                                        float2 (&sLQ)[2][G][kTB][64]) {
     constexpr int N = NG * G;
     constexpr int SPW = kTB / front_waves(G);
     const int w = bk.w, lane = bk.lane, n0 = bk.n0;
@@ -474,7 +473,7 @@ __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)
     }
     // ---- epilogue: finish tile 0
     if constexpr (FRONT)
-        finish_rows<T, SPW, G>(sLQ, r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32), bk.Dk, bk.du_b, bk.dd_b,
+        finish_rows<T, SPW, G>(sLQ[0], r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32), bk.Dk, bk.du_b, bk.dd_b,
                                bk.D32, r.accD, r.accBias);
 }
 
@@ -483,9 +482,12 @@ template <typename T, int NG, int G>
 __global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
     constexpr int N = NG * G;
     static_assert(kTB % G == 0 && 16 % (2 * NG) == 0, "tile and batch must split evenly");
-    __shared__ float4 sX[2][kTB][64];   // (Delta, Delta*u, sbar, -) per row and channel
-    __shared__ float2 sLQ[G][kTB][64];  // per state group: (sum lam*Bm, sum A*lam*a*h_prev)
-    __shared__ float sRed[2][G][64];
+    // (Delta, Delta*u, sbar, -) per row and channel; after the walk, the
+    // per-wave dD / ddt_bias sums
+    __shared__ float4 sX[2][kTB][64];
+    __shared__ float2 sLQ[2][G][kTB][64];  // per state group: (sum lam*Bm, sum A*lam*a*h_prev)
+    float (&sRed)[2][G][64] = *reinterpret_cast<float (*)[2][G][64]>(&sX[0][0][0]);
+    static_assert(sizeof(float) * 2 * G * 64 <= sizeof(sX), "reduction scratch must fit in sX");
     constexpr int SPW = kTB / front_waves(G);
 
     RevBlock<T> bk;
