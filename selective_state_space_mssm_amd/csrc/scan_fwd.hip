@@ -310,11 +310,39 @@ __device__ __forceinline__ void fetch_bc(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg,
 // Front end of this wave's rows of segment tile `tile` into sDD (and, in the
 // pre-pass, sbar to memory).  Rows past the end hold finite values that are
 // never used.
+// (Pre-pass: sbar of the rows goes to `sbv`, stored by store_sbar after the
+// next loads are issued, so that waiting for those loads never waits for
+// these stores.)
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile, const float (&ru)[kTB / front_waves(G)],
+__device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, const float (&ru)[kTB / front_waves(G)],
                                           const float (&rd)[kTB / front_waves(G)], const float (&rz)[kTB / front_waves(G)],
                                           const float (&rdy)[kTB / front_waves(G)], float2 (&dst)[kTB][64],
-                                          float (&skip)[kTB / front_waves(G)], float (&gate)[kTB / front_waves(G)]) {
+                                          float (&skip)[kTB / front_waves(G)], float (&gate)[kTB / front_waves(G)],
+                                          float (&sbv)[kTB / front_waves(G)]) {
+    constexpr int SPW = kTB / front_waves(G);
+    if constexpr (PRE) {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            float2 v;
+            prep_element_pre<HAS_Z>(ru[i], rd[i], rz[i], rdy[i], sg.bias, sg.Dk, sg.softplus_on, v, skip[i], gate[i],
+                                    sbv[i]);
+            dst[sg.w * SPW + i][sg.lane] = v;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            float2 v;
+            prep_element<HAS_Z>(ru[i], rd[i], rz[i], sg.bias, sg.Dk, sg.softplus_on, v, skip[i], gate[i]);
+            dst[sg.w * SPW + i][sg.lane] = v;
+            sbv[i] = 0.0f;
+        }
+    }
+}
+
+// Pre-pass: sbar of this wave's rows of segment tile `tile` (rows past the end dropped).
+template <typename T, int NG, int G, bool HAS_Z, bool PRE>
+__device__ __forceinline__ void store_sbar(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
+                                           const float (&sbv)[kTB / front_waves(G)]) {
     constexpr int SPW = kTB / front_waves(G);
     if constexpr (PRE) {
         const int rows = sg.t_len - tile * kTB;
@@ -324,24 +352,12 @@ __device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg
                       static_cast<uint32_t>(kTB) * static_cast<uint32_t>(D32) * 4u);
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            float2 v;
-            float sb;
-            prep_element_pre<HAS_Z>(ru[i], rd[i], rz[i], rdy[i], sg.bias, sg.Dk, sg.softplus_on, v, skip[i], gate[i],
-                                    sb);
             const int j = sg.w * SPW + i;
-            dst[j][sg.lane] = v;
             const uint32_t off = (sg.dvalid && j < rows)
                                      ? (static_cast<uint32_t>(j) * static_cast<uint32_t>(D32) +
                                         static_cast<uint32_t>(sg.lane)) * 4u
                                      : kNoStore;
-            buffer_store_act(sb, rs, off, 0.0f);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            float2 v;
-            prep_element<HAS_Z>(ru[i], rd[i], rz[i], sg.bias, sg.Dk, sg.softplus_on, v, skip[i], gate[i]);
-            dst[sg.w * SPW + i][sg.lane] = v;
+            buffer_store_act(sbv[i], rs, off, 0.0f);
         }
     }
 }
@@ -407,8 +423,10 @@ __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>&
     fetch_bc(sg, k + 1, r.qb, r.qc);
     float skip_nn[SPW], gate_nn[SPW];
     if constexpr (FRONT) {
-        prep_rows(sg, k + 2, r.ru, r.rd, r.rz, r.rdy, sDD[cur], skip_nn, gate_nn);  // buffer (k + 2) & 1 == k & 1
+        float sbv[SPW];
+        prep_rows(sg, r.ru, r.rd, r.rz, r.rdy, sDD[cur], skip_nn, gate_nn, sbv);  // buffer (k + 2) & 1 == k & 1
         fetch_rows(sg, k + 3, r.ru, r.rd, r.rz, r.rdy);
+        store_sbar(sg, k + 2, sbv);
     }
     if constexpr (PRE) {  // the state before tile k
         const __amdgpu_buffer_rsrc_t rc =
@@ -493,9 +511,12 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
         float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];
         fetch_rows(sg, 0, ru, rd, rz, rdy);
         fetch_rows(sg, 1, r.ru, r.rd, r.rz, r.rdy);
-        prep_rows(sg, 0, ru, rd, rz, rdy, sDD[0], r.skip_c, r.gate_c);
-        prep_rows(sg, 1, r.ru, r.rd, r.rz, r.rdy, sDD[1], r.skip_n, r.gate_n);
+        float sb0[SPW], sb1[SPW];
+        prep_rows(sg, ru, rd, rz, rdy, sDD[0], r.skip_c, r.gate_c, sb0);
+        prep_rows(sg, r.ru, r.rd, r.rz, r.rdy, sDD[1], r.skip_n, r.gate_n, sb1);
         fetch_rows(sg, 2, r.ru, r.rd, r.rz, r.rdy);
+        store_sbar(sg, 0, sb0);
+        store_sbar(sg, 1, sb1);
 #pragma unroll
         for (int i = 0; i < SPW; ++i) r.skip_p[i] = r.gate_p[i] = 0.0f;
     }
