@@ -190,6 +190,15 @@ __device__ __forceinline__ float fmac_row_bcast(float acc, float c, float h) {
         : "v"(c), "v"(h), "i"(J));
     return acc;
 }
+// Two independent fmac_row_bcast behind one pair of wait states.
+template <int J>
+__device__ __forceinline__ void fmac_row_bcast2(float& acc0, float c0, float h0, float& acc1, float c1, float h1) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %2, %3 row_newbcast:%6 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %4, %5 row_newbcast:%6 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "+v"(acc0), "+v"(acc1)
+        : "v"(c0), "v"(h0), "v"(c1), "v"(h1), "i"(J));
+}
 
 // ---- transcendental building blocks (hardware v_exp/v_log/v_rcp) --------
 

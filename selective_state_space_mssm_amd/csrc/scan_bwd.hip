@@ -24,11 +24,13 @@
 //     forward.  Per tile it recomputes the tile's states and decays from the
 //     checkpoint into VGPRs, then runs the adjoint backwards over the tile.
 //     Bm/Cm reach the lanes by DPP row broadcast; (Delta, Delta*u, sbar) is
-//     shared by the waves through LDS.  Each wave leaves its partial sums over
-//     its states of lam*Bm and A*lam*a*h_prev in LDS, and in the next interval
-//     every wave finishes its share of the tile's rows (du, ddelta).  dB/dC
-//     are summed over the wave's 64 channels by a transpose-reduce across
-//     lanes (16 values in 35 instructions) and stored per channel block;
+//     shared by the waves through LDS (prepared by the first half of the
+//     waves).  Each wave leaves its partial sums over its states of lam*Bm
+//     and A*lam*a*h_prev in LDS (two buffers, one barrier per tile), and in
+//     the next interval the same front waves finish the tile's rows (du,
+//     ddelta).  dB/dC are summed over the wave's 64 channels by a
+//     transpose-reduce across lanes (16 values in 35 instructions) and
+//     stored per channel block;
 //  3. reduce: fixed-order sums of the per-block dB/dC partials and of the
 //     per-batch-row dA/dD/ddt_bias partials.  No atomics: results are
 //     bitwise reproducible.
@@ -274,7 +276,6 @@ struct RevCtx {
     const float (*hist)[NG];
     const float (*ahist)[NG];
     const float* hin;        // [NG] state before the tile
-    const float* anext;      // [NG] decay of the step after the tile (1 past the end)
     float2 (*sLQ)[kTB][64];  // [G]
     __amdgpu_buffer_rsrc_t rp;  // this block's dB/dC partial rows of the tile
     int nval, w, lane, dblocks, N, n0;
@@ -283,28 +284,37 @@ struct RevCtx {
 // Reverse step J for this wave's NG states: the adjoint, its partial sums
 // for du/ddelta (to LDS), dA, and the step's dB/dC terms into the 16-value
 // batch `vals`; when the batch is complete (its lowest step), its sums over
-// the wave's channels are stored.
+// the wave's channels are stored.  `pc` carries a_{t+1} lam_{t+1} from the
+// step after (dh_final before the last step), so that
+// lam_t = pc + sbar_t Cm_t is one DPP fmac and a_t lam_t serves both the
+// dA / ddelta term and the next step.
 template <int NG, int G, bool FULL, int J>
-__device__ __forceinline__ void rev_step(const RevCtx<NG, G>& c, float (&lam)[NG], float (&dA)[NG],
+__device__ __forceinline__ void rev_step(const RevCtx<NG, G>& c, float (&pc)[NG], float (&dA)[NG],
                                          float (&vals)[16]) {
     constexpr int S = 16 / (2 * NG);  // steps per batch
     constexpr int slot = (J % S) * 2 * NG;
     if (FULL || J < c.nval) {
         const float4 x = c.xt[J];  // (Delta, Delta*u, sbar, -)
+        float lam[NG];
+#pragma unroll
+        for (int k = 0; k < NG; ++k) lam[k] = pc[k];
+        if constexpr (NG % 2 == 0) {
+#pragma unroll
+            for (int k = 0; k < NG; k += 2)
+                fmac_row_bcast2<J>(lam[k], c.Ct[k], x.z, lam[k + 1], c.Ct[k + 1], x.z);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NG; ++k) lam[k] = fmac_row_bcast<J>(lam[k], c.Ct[k], x.z);
+        }
         float lb = 0.0f, lq = 0.0f;
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
-            // decay of the next step in time (1 past the end: the ragged tile's
-            // missing steps hold 1)
-            float an;
-            if constexpr (J + 1 < kTB) an = c.ahist[J + 1][k];
-            else an = c.anext[k];
-            lam[k] = __builtin_fmaf(an, lam[k], row_bcast<J>(c.Ct[k]) * x.z);
             lb = k == 0 ? row_bcast<J>(c.Bt[0]) * lam[0] : fmac_row_bcast<J>(lb, c.Bt[k], lam[k]);
             float hp;
             if constexpr (J > 0) hp = c.hist[J - 1][k];
             else hp = c.hin[k];
-            const float q = lam[k] * c.ahist[J][k] * hp;
+            pc[k] = lam[k] * c.ahist[J][k];
+            const float q = pc[k] * hp;
             lq = __builtin_fmaf(c.Aval[k], q, lq);
             dA[k] = __builtin_fmaf(x.x, q, dA[k]);
             vals[slot + k] = lam[k] * x.y;           // this channel's dB term
@@ -330,9 +340,9 @@ __device__ __forceinline__ void rev_step(const RevCtx<NG, G>& c, float (&lam)[NG
 
 template <int NG, int G, bool FULL, int... I>
 __device__ __forceinline__ void rev_steps(std::integer_sequence<int, I...>, const RevCtx<NG, G>& c,
-                                          float (&lam)[NG], float (&dA)[NG]) {
+                                          float (&pc)[NG], float (&dA)[NG]) {
     float vals[16];
-    (rev_step<NG, G, FULL, kTB - 1 - I>(c, lam, dA, vals), ...);  // J = 15 .. 0: backwards in time
+    (rev_step<NG, G, FULL, kTB - 1 - I>(c, pc, dA, vals), ...);  // J = 15 .. 0: backwards in time
 }
 
 // Registers carried from one reverse interval to the next.
@@ -343,7 +353,7 @@ struct RevRegs {
     uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next tile
     float hin_next[NG];               // checkpoint of the next tile
     RowKeep keep_c[SPW], keep_p[SPW];  // rows of the tile in flight / of the tile to finish
-    float lam[NG], dA[NG], anext[NG];
+    float pc[NG], dA[NG];  // a_{t+1} lam_{t+1} into the next step back; the dA sums
     float accD, accBias;
 };
 
@@ -420,14 +430,12 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
     // ---- B (partials of tile k go to the other buffer than those of tile k + 1 just read)
     {
         const int64_t row0 = bk.row_b + static_cast<int64_t>(k) * kTB;
-        RevCtx<NG, G> c{Aval, Bt, Ct, xt, hist, ahist, hin, r.anext, sLQ[cur],
+        RevCtx<NG, G> c{Aval, Bt, Ct, xt, hist, ahist, hin, sLQ[cur],
                         make_rsrc(bk.pBC + (row0 * bk.dblocks + bk.dblk) * 2 * N,
                                   static_cast<uint32_t>(kTB) * bk.dblocks * 2u * N * 4u),
                         nval, w, lane, bk.dblocks, N, bk.n0};
-        rev_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, c, r.lam, r.dA);
+        rev_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, c, r.pc, r.dA);
     }
-#pragma unroll
-    for (int q = 0; q < NG; ++q) r.anext[q] = ahist[0][q];
     if constexpr (FRONT) {
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
@@ -528,9 +536,8 @@ __global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
     for (int k = 0; k < NG; ++k) {
         Aval[k] = a.A[dc * N + n0 + k];
         A2[k] = Aval[k] * kLog2e;
-        r.lam[k] = (a.dh_final && bk.dvalid) ? a.dh_final[(b * D + dc) * N + n0 + k] : 0.0f;
+        r.pc[k] = (a.dh_final && bk.dvalid) ? a.dh_final[(b * D + dc) * N + n0 + k] : 0.0f;
         r.dA[k] = 0.0f;
-        r.anext[k] = 1.0f;  // no step after the last one
     }
     r.accD = r.accBias = 0.0f;
 #pragma unroll
@@ -548,7 +555,7 @@ __global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
         if (a.dh0) {
             float* g0 = a.dh0 + (b * D + dc) * N + n0;
 #pragma unroll
-            for (int k = 0; k < NG; ++k) g0[k] = r.anext[k] * r.lam[k];  // a_0 lam_0
+            for (int k = 0; k < NG; ++k) g0[k] = r.pc[k];  // a_0 lam_0
         }
     }
     sRed[0][w][lane] = r.accD;

@@ -18,11 +18,21 @@
 //    16-lane rows), and step j reads it through a DPP row_newbcast:j source
 //    modifier on the v_mul / v_fmac that consumes it -- a broadcast with no
 //    extra instruction, no LDS traffic and no scalar-load waits;
-//  * per time tile of TB steps: every wave turns TB/G rows of (u, delta)
-//    into (Delta, Delta*u) in LDS (softplus once per element, shared by the
-//    G waves); every wave runs the recurrence for its states over the tile
-//    and leaves its partial readout in LDS; every wave then finishes TB/G
-//    rows: sum of the G partials + Dskip*u, times silu(z), store.
+//  * per time tile of 16 steps: the first half of the waves (the "front"
+//    waves) turn the tile's rows of (u, delta, z) into (Delta, Delta*u) in
+//    LDS, the skip term and the gate (softplus and silu once per element,
+//    shared by all G waves); every wave runs the recurrence for its states
+//    over the tile and leaves its partial readout in LDS; the front waves
+//    then finish the rows: sum of the G partials + Dskip*u, times silu(z),
+//    store.  (The hardware favours the waves dispatched first when two waves
+//    of a SIMD are ready; giving them the per-element work balances the two.)
+//  * software pipeline, one barrier per tile: front end two tiles ahead,
+//    finishing one tile behind, the next tile's (Delta, Delta*u) read from
+//    LDS while the current one runs; global loads through buffer resources;
+//  * when the channel blocks outnumber the CUs but do not divide evenly over
+//    them, a persistent balanced schedule gives every CU an equal share of
+//    (block, tile) work, handing the state of a split block over through
+//    memory;
 //  * long sequences: the time axis is cut into K chunks.  A first kernel
 //    computes per chunk the end state from zero and the step-size sum
 //    (the chunk aggregate of the associative operator
