@@ -236,26 +236,38 @@ __device__ __forceinline__ void finish_rows(const float2 (&sLQ)[G][kTB][64], con
     }
 }
 
-// Recompute of step J: the state after step J and the step's decay.
+// Recompute of one tile from its checkpoint, in two passes over the steps:
+// every step's decay and input first (independent of the state), then the
+// dependent state updates.  Steps past the end of a ragged last tile hold
+// state 0 and decay 1.
 template <int NG, bool FULL, int J>
-__device__ __forceinline__ void rec_step(int nval, const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
-                                         const float4 (&xt)[kTB], float (&hist)[kTB][NG],
-                                         float (&ahist)[kTB][NG]) {
+__device__ __forceinline__ void rec_pre(int nval, const float (&A2)[NG], const float (&Bt)[NG],
+                                        const float4 (&xt)[kTB], float (&g)[kTB][NG], float (&ahist)[kTB][NG]) {
     if (FULL || J < nval) {
         const float4 x = xt[J];
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
-            const float a = fast_exp2(x.x * A2[k]);
-            h[k] = __builtin_fmaf(a, h[k], row_bcast<J>(Bt[k]) * x.y);
-            ahist[J][k] = a;
-            hist[J][k] = h[k];
+            ahist[J][k] = fast_exp2(x.x * A2[k]);
+            g[J][k] = row_bcast<J>(Bt[k]) * x.y;
         }
-    } else {  // past the end (ragged last tile): no state, decay 1 as after the last step
+    } else {
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
             ahist[J][k] = 1.0f;
-            hist[J][k] = 0.0f;
+            g[J][k] = 0.0f;
         }
+    }
+}
+
+template <int NG, bool FULL, int J>
+__device__ __forceinline__ void rec_step(int nval, float (&h)[NG], const float (&g)[kTB][NG],
+                                         const float (&ahist)[kTB][NG], float (&hist)[kTB][NG]) {
+    if (FULL || J < nval) {
+#pragma unroll
+        for (int k = 0; k < NG; ++k) hist[J][k] = h[k] = __builtin_fmaf(ahist[J][k], h[k], g[J][k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NG; ++k) hist[J][k] = 0.0f;
     }
 }
 
@@ -263,7 +275,9 @@ template <int NG, bool FULL, int... J>
 __device__ __forceinline__ void rec_steps(std::integer_sequence<int, J...>, int nval, const float (&A2)[NG],
                                           float (&h)[NG], const float (&Bt)[NG], const float4 (&xt)[kTB],
                                           float (&hist)[kTB][NG], float (&ahist)[kTB][NG]) {
-    (rec_step<NG, FULL, J>(nval, A2, h, Bt, xt, hist, ahist), ...);
+    float g[kTB][NG];
+    (rec_pre<NG, FULL, J>(nval, A2, Bt, xt, g, ahist), ...);
+    (rec_step<NG, FULL, J>(nval, h, g, ahist, hist), ...);
 }
 
 // State that the reverse steps of one tile read and update.

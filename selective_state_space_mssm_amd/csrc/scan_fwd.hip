@@ -119,19 +119,30 @@ __device__ __forceinline__ void fetch_tile_rows(const T* __restrict__ M, int64_t
     load_lane_row<T, NG>(M + r * N + n0, q);
 }
 
-// One step J of the recurrence for this wave's NG states; leaves the partial
-// readout in sP[w][J].
-template <int NG, int G, bool FULL, int J>
-__device__ __forceinline__ void fwd_step(int nval, int w, int lane, const float (&A2)[NG], float (&h)[NG],
-                                         const float (&Bt)[NG], const float (&Ct)[NG], const float2 (&ddt)[kTB],
-                                         float (&sP)[G][kTB][64]) {
+// The recurrence of one tile in two passes over its 16 steps: first every
+// step's decay exp(Delta A) and input Bm Delta u (independent of the state,
+// so these instructions can overlap the dependent chain), then the state
+// updates and readouts.  Decay and input of step J:
+template <int NG, bool FULL, int J>
+__device__ __forceinline__ void fwd_pre(int nval, const float (&A2)[NG], const float (&Bt)[NG],
+                                        const float2 (&ddt)[kTB], float (&ea)[kTB][NG], float (&eg)[kTB][NG]) {
     if (FULL || J < nval) {
         const float2 dd = ddt[J];
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
-            const float dA = fast_exp2(dd.x * A2[k]);
-            h[k] = __builtin_fmaf(dA, h[k], row_bcast<J>(Bt[k]) * dd.y);
+            ea[J][k] = fast_exp2(dd.x * A2[k]);
+            eg[J][k] = row_bcast<J>(Bt[k]) * dd.y;
         }
+    }
+}
+// State update and partial readout (to sP[w][J]) of step J:
+template <int NG, int G, bool FULL, int J>
+__device__ __forceinline__ void fwd_step(int nval, int w, int lane, float (&h)[NG], const float (&Ct)[NG],
+                                         const float (&ea)[kTB][NG], const float (&eg)[kTB][NG],
+                                         float (&sP)[G][kTB][64]) {
+    if (FULL || J < nval) {
+#pragma unroll
+        for (int k = 0; k < NG; ++k) h[k] = __builtin_fmaf(ea[J][k], h[k], eg[J][k]);
         float yp = row_bcast<J>(Ct[0]) * h[0];
 #pragma unroll
         for (int k = 1; k < NG; ++k) yp = fmac_row_bcast<J>(yp, Ct[k], h[k]);
@@ -144,7 +155,9 @@ __device__ __forceinline__ void fwd_steps(std::integer_sequence<int, J...>, int 
                                           const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
                                           const float (&Ct)[NG], const float2 (&ddt)[kTB],
                                           float (&sP)[G][kTB][64]) {
-    (fwd_step<NG, G, FULL, J>(nval, w, lane, A2, h, Bt, Ct, ddt, sP), ...);
+    float ea[kTB][NG], eg[kTB][NG];
+    (fwd_pre<NG, FULL, J>(nval, A2, Bt, ddt, ea, eg), ...);
+    (fwd_step<NG, G, FULL, J>(nval, w, lane, h, Ct, ea, eg, sP), ...);
 }
 
 template <int NG, bool FULL, int J>
