@@ -4,7 +4,8 @@ element with the relative criterion of helpers.grad_err.
 
 Covers the training workload (B=8, L=2048, D=1536, N=16, fp32) in full, ragged
 small shapes with every optional input (h0, dh_final, z, Dskip, dt_bias), the
-ungated path, every supported state size, bfloat16 activations, and bitwise
+ungated path, every supported state size, bfloat16 activations, the forward
+pre-pass under its chunked and its balanced schedules, and bitwise
 reproducibility (the reductions have a fixed order, no atomics)."""
 import numpy as np
 import pytest
@@ -76,6 +77,26 @@ def test_state_sizes(mssm, N):
 def test_bf16(mssm):
     g, r = run_both(mssm, workloads.custom(2, 64, 96, 16, "bf16", seed=60))
     assert_grads(g, r, GRAD_TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunked_prepass(mssm, dtype):
+    # one channel block and L >= 2048: the forward pre-pass runs the chunked
+    # schedule (chunk end states, carry, rescan), the last chunk ragged
+    B, L, D = 1, 4500, 40
+    assert mssm.fwd_workspace_bytes(B, L, D, 16) > 0
+    g, r = run_both(mssm, workloads.custom(B, L, D, 16, dtype, seed=41))
+    assert_grads(g, r, GRAD_TOL[dtype])
+
+
+@pytest.mark.parametrize("shape,dtype", [((3, 48, 5760), "f32"), ((5, 37, 3840), "bf16")])
+def test_balanced_prepass(mssm, shape, dtype):
+    # more channel blocks than CUs but not a multiple of them (270 and 300 on
+    # a 256-CU MI355X): the forward pre-pass runs the balanced persistent
+    # schedule, handing split blocks' states over through the workspace
+    B, L, D = shape
+    g, r = run_both(mssm, workloads.custom(B, L, D, 16, dtype, seed=B * L + 1), dhf=False)
+    assert_grads(g, r, GRAD_TOL[dtype])
 
 
 def test_training_workload_full(mssm):
