@@ -108,6 +108,14 @@ def test_balanced_schedule(mssm, shape, dtype):
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
 
 
+@pytest.mark.parametrize("N", [1, 8, 64])
+def test_schedules_other_state_sizes(mssm, N):
+    # the chunked (1 block, L >= 2048) and the balanced (270 blocks) schedules
+    # with one state per wave (N = 1, a single wave), 2 and 16 states per wave
+    check(mssm, workloads.custom(1, 2100, 40, N, "f32", seed=N + 90), h0=True)
+    check(mssm, workloads.custom(3, 40, 5760, N, "bf16", seed=N + 91), h0=True)
+
+
 def test_130m_layer_full(mssm):
     ey, eh = check(mssm, workloads.WORKLOADS["130m"])
     print(f"130M: y err {ey:.2e}, h_final err {eh:.2e}")
