@@ -52,13 +52,11 @@ namespace {
 
 constexpr int kTB = 16;  // time steps per tile (= lanes per DPP row)
 
-// Waves of a workgroup that also run the per-element front end (softplus,
-// gate, loads of u/delta/z) and the finishing of rows (sum of partial
-// readouts, store); the others run only the recurrence of their states.
-#ifndef MSSM_FWD_FRONT_DIV
-#define MSSM_FWD_FRONT_DIV 2
-#endif
-constexpr int front_waves(int G) { return G >= MSSM_FWD_FRONT_DIV ? G / MSSM_FWD_FRONT_DIV : 1; }
+// Helper waves of a workgroup: besides the G state waves, which run only the
+// recurrence of their states, the workgroup has G/2 (at least one) helper
+// waves that run the per-element front end (loads of u/delta/z, softplus,
+// gate) and the finishing of rows (sum of the partial readouts, store).
+constexpr int helper_waves(int G) { return G >= 2 ? G / 2 : 1; }
 
 struct FwdKArgs {
     const void* u;
@@ -135,6 +133,22 @@ __device__ __forceinline__ void fwd_pre(int nval, const float (&A2)[NG], const f
         }
     }
 }
+// Decay, input, state update and partial readout of step J at once.
+template <int NG, int G, bool FULL, int J>
+__device__ __forceinline__ void fwd_pre_step(int nval, int w, int lane, const float (&A2)[NG], float (&h)[NG],
+                                             const float (&Bt)[NG], const float (&Ct)[NG], const float2 (&ddt)[kTB],
+                                             float (&sP)[G][kTB][64]) {
+    if (FULL || J < nval) {
+        const float2 dd = ddt[J];
+#pragma unroll
+        for (int k = 0; k < NG; ++k)
+            h[k] = __builtin_fmaf(fast_exp2(dd.x * A2[k]), h[k], row_bcast<J>(Bt[k]) * dd.y);
+        float yp = row_bcast<J>(Ct[0]) * h[0];
+#pragma unroll
+        for (int k = 1; k < NG; ++k) yp = fmac_row_bcast<J>(yp, Ct[k], h[k]);
+        sP[w][J][lane] = yp;
+    }
+}
 // State update and partial readout (to sP[w][J]) of step J:
 template <int NG, int G, bool FULL, int J>
 __device__ __forceinline__ void fwd_step(int nval, int w, int lane, float (&h)[NG], const float (&Ct)[NG],
@@ -155,9 +169,13 @@ __device__ __forceinline__ void fwd_steps(std::integer_sequence<int, J...>, int 
                                           const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
                                           const float (&Ct)[NG], const float2 (&ddt)[kTB],
                                           float (&sP)[G][kTB][64]) {
-    float ea[kTB][NG], eg[kTB][NG];
-    (fwd_pre<NG, FULL, J>(nval, A2, Bt, ddt, ea, eg), ...);
-    (fwd_step<NG, G, FULL, J>(nval, w, lane, h, Ct, ea, eg, sP), ...);
+    if constexpr (NG <= 2) {
+        float ea[kTB][NG], eg[kTB][NG];
+        (fwd_pre<NG, FULL, J>(nval, A2, Bt, ddt, ea, eg), ...);
+        (fwd_step<NG, G, FULL, J>(nval, w, lane, h, Ct, ea, eg, sP), ...);
+    } else {  // many states per wave: enough independent work per step, and too many registers to stage
+        ((fwd_pre_step<NG, G, FULL, J>(nval, w, lane, A2, h, Bt, Ct, ddt, sP)), ...);
+    }
 }
 
 template <int NG, bool FULL, int J>
@@ -259,8 +277,9 @@ __device__ __forceinline__ void prep_element_pre(float uu, float dd, float zz, f
 // lane's constant offsets.
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 struct FwdSeg {
-    static constexpr int SPW = kTB / front_waves(G);
+    static constexpr int SPW = kTB / helper_waves(G);
     int ntiles, t_len, w, lane;
+    int hw;  // helper waves: index among the helpers (rows hw * SPW ..)
     bool dvalid;
     int softplus_on;
     float bias, Dk;
@@ -283,7 +302,7 @@ struct FwdSeg {
 // Registers carried from one tile interval to the next.
 template <typename T, int NG, int G>
 struct FwdRegs {
-    static constexpr int SPW = kTB / front_waves(G);
+    static constexpr int SPW = kTB / helper_waves(G);
     float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];   // raw inputs of the tile prepared next (k + 2)
     uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next recurrence tile
     // skip term and gate (pre-pass: dz factor) of the rows of tiles k + 1 (n),
@@ -294,9 +313,9 @@ struct FwdRegs {
 // Raw inputs of this wave's rows of segment tile `tile` (zeros past the end).
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fetch_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                           float (&ru)[kTB / front_waves(G)], float (&rd)[kTB / front_waves(G)],
-                                           float (&rz)[kTB / front_waves(G)], float (&rdy)[kTB / front_waves(G)]) {
-    constexpr int SPW = kTB / front_waves(G);
+                                           float (&ru)[kTB / helper_waves(G)], float (&rd)[kTB / helper_waves(G)],
+                                           float (&rz)[kTB / helper_waves(G)], float (&rdy)[kTB / helper_waves(G)]) {
+    constexpr int SPW = kTB / helper_waves(G);
     const int64_t first = static_cast<int64_t>(tile) * kTB * sg.D;       // first element of the tile
     const int64_t bytes = (sg.seg_elems - first) * static_cast<int64_t>(sizeof(T));
     const __amdgpu_buffer_rsrc_t ru_r = range_rsrc(sg.u_seg + first, bytes);
@@ -337,26 +356,26 @@ __device__ __forceinline__ void fetch_bc(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg,
 // next loads are issued, so that waiting for those loads never waits for
 // these stores.)
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, const float (&ru)[kTB / front_waves(G)],
-                                          const float (&rd)[kTB / front_waves(G)], const float (&rz)[kTB / front_waves(G)],
-                                          const float (&rdy)[kTB / front_waves(G)], float2 (&dst)[kTB][64],
-                                          float (&skip)[kTB / front_waves(G)], float (&gate)[kTB / front_waves(G)],
-                                          float (&sbv)[kTB / front_waves(G)]) {
-    constexpr int SPW = kTB / front_waves(G);
+__device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, const float (&ru)[kTB / helper_waves(G)],
+                                          const float (&rd)[kTB / helper_waves(G)], const float (&rz)[kTB / helper_waves(G)],
+                                          const float (&rdy)[kTB / helper_waves(G)], float2 (&dst)[kTB][64],
+                                          float (&skip)[kTB / helper_waves(G)], float (&gate)[kTB / helper_waves(G)],
+                                          float (&sbv)[kTB / helper_waves(G)]) {
+    constexpr int SPW = kTB / helper_waves(G);
     if constexpr (PRE) {
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             float2 v;
             prep_element_pre<HAS_Z>(ru[i], rd[i], rz[i], rdy[i], sg.bias, sg.Dk, sg.softplus_on, v, skip[i], gate[i],
                                     sbv[i]);
-            dst[sg.w * SPW + i][sg.lane] = v;
+            dst[sg.hw * SPW + i][sg.lane] = v;
         }
     } else {
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             float2 v;
             prep_element<HAS_Z>(ru[i], rd[i], rz[i], sg.bias, sg.Dk, sg.softplus_on, v, skip[i], gate[i]);
-            dst[sg.w * SPW + i][sg.lane] = v;
+            dst[sg.hw * SPW + i][sg.lane] = v;
             sbv[i] = 0.0f;
         }
     }
@@ -365,8 +384,8 @@ __device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg
 // Pre-pass: sbar of this wave's rows of segment tile `tile` (rows past the end dropped).
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void store_sbar(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                           const float (&sbv)[kTB / front_waves(G)]) {
-    constexpr int SPW = kTB / front_waves(G);
+                                           const float (&sbv)[kTB / helper_waves(G)]) {
+    constexpr int SPW = kTB / helper_waves(G);
     if constexpr (PRE) {
         const int rows = sg.t_len - tile * kTB;
         const int D32 = static_cast<int>(sg.D);
@@ -375,7 +394,7 @@ __device__ __forceinline__ void store_sbar(const FwdSeg<T, NG, G, HAS_Z, PRE>& s
                       static_cast<uint32_t>(kTB) * static_cast<uint32_t>(D32) * 4u);
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int j = sg.w * SPW + i;
+            const int j = sg.hw * SPW + i;
             const uint32_t off = (sg.dvalid && j < rows)
                                      ? (static_cast<uint32_t>(j) * static_cast<uint32_t>(D32) +
                                         static_cast<uint32_t>(sg.lane)) * 4u
@@ -389,9 +408,9 @@ __device__ __forceinline__ void store_sbar(const FwdSeg<T, NG, G, HAS_Z, PRE>& s
 // wave's rows of segment tile `tile` -> y (pre-pass: dz).
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                            const float (&part)[kTB / front_waves(G)][G], const float (&skip)[kTB / front_waves(G)],
-                                            const float (&gate)[kTB / front_waves(G)]) {
-    constexpr int SPW = kTB / front_waves(G);
+                                            const float (&part)[kTB / helper_waves(G)][G], const float (&skip)[kTB / helper_waves(G)],
+                                            const float (&gate)[kTB / helper_waves(G)]) {
+    constexpr int SPW = kTB / helper_waves(G);
     const int rows = tile >= 0 ? sg.t_len - tile * kTB : 0;  // tile -1: nothing
     const int D32 = static_cast<int>(sg.D);
     const __amdgpu_buffer_rsrc_t ry =
@@ -402,7 +421,7 @@ __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& 
         float s = 0.0f;
 #pragma unroll
         for (int g = 0; g < G; ++g) s += part[i][g];
-        const int j = sg.w * SPW + i;
+        const int j = sg.hw * SPW + i;
         const bool store = sg.dvalid && j < rows && (!PRE || HAS_Z);
         const uint32_t off = store ? (static_cast<uint32_t>(j) * static_cast<uint32_t>(D32) +
                                       static_cast<uint32_t>(sg.lane)) * static_cast<uint32_t>(sizeof(T))
@@ -422,45 +441,26 @@ __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& 
 // stores to out-of-range offsets instead of branching.
 // ddt holds tile k's (Delta, Delta*u); ddt_next receives tile k + 1's (two
 // register sets used alternately by consecutive intervals, so nothing is copied).
-// FRONT: this wave also runs the front end and the finishing of its rows.
-template <bool FULL, bool FRONT, typename T, int NG, int G, bool HAS_Z, bool PRE>
+// HELPER: a helper wave (front end and finishing of rows); else a state wave
+// (recurrence of its states).
+template <bool FULL, bool HELPER, typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int k, int nval,
                                              const float (&A2)[NG], float (&h)[NG], FwdRegs<T, NG, G>& r,
                                              const float2 (&ddt)[kTB], float2 (&ddt_next)[kTB],
                                              float2 (&sDD)[2][kTB][64], float (&sP)[2][G][kTB][64]) {
-    constexpr int SPW = kTB / front_waves(G);
+    constexpr int SPW = kTB / helper_waves(G);
     const int cur = k & 1, prv = cur ^ 1;
     const int lane = sg.lane, w = sg.w;
-    float part[SPW][G];
-    if constexpr (FRONT) {
+    if constexpr (HELPER) {
+        float part[SPW][G];
 #pragma unroll
         for (int i = 0; i < SPW; ++i)
 #pragma unroll
-            for (int g = 0; g < G; ++g) part[i][g] = sP[prv][g][w * SPW + i][lane];
-    }
-#pragma unroll
-    for (int j = 0; j < kTB; ++j) ddt_next[j] = sDD[prv][j][lane];  // tile k + 1 sits in buffer (k + 1) & 1
-    float Bt[NG], Ct[NG];
-    unpack_lane_row<T, NG>(r.qb, Bt);
-    unpack_lane_row<T, NG>(r.qc, Ct);
-    fetch_bc(sg, k + 1, r.qb, r.qc);
-    float skip_nn[SPW], gate_nn[SPW];
-    if constexpr (FRONT) {
-        float sbv[SPW];
+            for (int g = 0; g < G; ++g) part[i][g] = sP[prv][g][sg.hw * SPW + i][lane];
+        float skip_nn[SPW], gate_nn[SPW], sbv[SPW];
         prep_rows(sg, r.ru, r.rd, r.rz, r.rdy, sDD[cur], skip_nn, gate_nn, sbv);  // buffer (k + 2) & 1 == k & 1
         fetch_rows(sg, k + 3, r.ru, r.rd, r.rz, r.rdy);
         store_sbar(sg, k + 2, sbv);
-    }
-    if constexpr (PRE) {  // the state before tile k
-        const __amdgpu_buffer_rsrc_t rc =
-            make_rsrc(sg.ckpt_seg + static_cast<int64_t>(k) * sg.D * sg.N, static_cast<uint32_t>(64 * sg.N * 4));
-#pragma unroll
-        for (int q = 0; q < NG; ++q)
-            buffer_store_act(h[q], rc,
-                             sg.dvalid ? static_cast<uint32_t>((lane * sg.N + sg.n0 + q) * 4) : kNoStore, 0.0f);
-    }
-    fwd_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, nval, w, lane, A2, h, Bt, Ct, ddt, sP[cur]);
-    if constexpr (FRONT) {
         finish_rows(sg, k - 1, part, r.skip_p, r.gate_p);  // k == 0: nothing stored
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
@@ -471,18 +471,34 @@ __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>&
             r.skip_n[i] = skip_nn[i];
             r.gate_n[i] = gate_nn[i];
         }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kTB; ++j) ddt_next[j] = sDD[prv][j][lane];  // tile k + 1 sits in buffer (k + 1) & 1
+        float Bt[NG], Ct[NG];
+        unpack_lane_row<T, NG>(r.qb, Bt);
+        unpack_lane_row<T, NG>(r.qc, Ct);
+        fetch_bc(sg, k + 1, r.qb, r.qc);
+        if constexpr (PRE) {  // the state before tile k
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(sg.ckpt_seg + static_cast<int64_t>(k) * sg.D * sg.N,
+                                                        static_cast<uint32_t>(64 * sg.N * 4));
+#pragma unroll
+            for (int q = 0; q < NG; ++q)
+                buffer_store_act(h[q], rc,
+                                 sg.dvalid ? static_cast<uint32_t>((lane * sg.N + sg.n0 + q) * 4) : kNoStore, 0.0f);
+        }
+        fwd_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, nval, w, lane, A2, h, Bt, Ct, ddt, sP[cur]);
     }
 }
 
 // Runs steps [t_begin, t_end) of channel block `blk` (batch row b = blk /
 // dblocks, channels chan0 .. chan0 + 63) from the state in h, leaving the
 // final state in h.
-template <bool FRONT, typename T, int NG, int G, bool HAS_Z, bool PRE>
+template <bool HELPER, typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t t_begin, int64_t t_end,
                                             float (&h)[NG], float2 (&sDD)[2][kTB][64],
                                             float (&sP)[2][G][kTB][64]) {
     constexpr int N = NG * G;
-    constexpr int SPW = kTB / front_waves(G);  // rows prepared and finished per front wave per tile
+    constexpr int SPW = kTB / helper_waves(G);  // rows prepared and finished per helper wave per tile
 
     FwdSeg<T, NG, G, HAS_Z, PRE> sg;
     sg.lane = threadIdx.x & 63;
@@ -494,12 +510,13 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     sg.N = N;
     sg.dvalid = chan0 + sg.lane < D;
     const int64_t dc = imin64(chan0 + sg.lane, D - 1);
-    sg.n0 = sg.w * NG;
-    const int lane = sg.lane, w = sg.w, n0 = sg.n0;
+    sg.n0 = HELPER ? 0 : sg.w * NG;
+    sg.hw = HELPER ? sg.w - G : 0;
+    const int lane = sg.lane, n0 = sg.n0;
 
     float A2[NG];
 #pragma unroll
-    for (int k = 0; k < NG; ++k) A2[k] = a.A[dc * N + n0 + k] * kLog2e;
+    for (int k = 0; k < NG; ++k) A2[k] = HELPER ? 0.0f : a.A[dc * N + n0 + k] * kLog2e;
     sg.bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
     sg.Dk = a.Dskip ? a.Dskip[dc] : 0.0f;
     sg.softplus_on = a.softplus;
@@ -521,7 +538,7 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     const int D32 = static_cast<int>(D);
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
-        sg.row_off[i] = (static_cast<uint32_t>(w * SPW + i) * static_cast<uint32_t>(D32) + static_cast<uint32_t>(lane)) *
+        sg.row_off[i] = (static_cast<uint32_t>(sg.hw * SPW + i) * static_cast<uint32_t>(D32) + static_cast<uint32_t>(lane)) *
                         static_cast<uint32_t>(sizeof(T));
     sg.bc_off = static_cast<uint32_t>(((lane & (kTB - 1)) * N + n0) * static_cast<int>(sizeof(T)));
 
@@ -529,8 +546,8 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     // ---- prologue: tiles 0 and 1 prepared, tile 0's (Delta, Delta*u) in
     // registers, tile 0's Bm/Cm and tile 2's raw inputs in flight
     FwdRegs<T, NG, G> r;
-    fetch_bc(sg, 0, r.qb, r.qc);
-    if constexpr (FRONT) {
+    if constexpr (!HELPER) fetch_bc(sg, 0, r.qb, r.qc);
+    if constexpr (HELPER) {
         float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];
         fetch_rows(sg, 0, ru, rd, rz, rdy);
         fetch_rows(sg, 1, r.ru, r.rd, r.rz, r.rdy);
@@ -545,8 +562,10 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     }
     __syncthreads();
     float2 ddtA[kTB], ddtB[kTB];
+    if constexpr (!HELPER) {
 #pragma unroll
-    for (int j = 0; j < kTB; ++j) ddtA[j] = sDD[0][j][lane];
+        for (int j = 0; j < kTB; ++j) ddtA[j] = sDD[0][j][lane];
+    }
     __syncthreads();  // every wave has read buffer 0 before interval 0 refills it
 
     // full tiles in pairs (even tiles compute from ddtA, odd ones from ddtB),
@@ -554,30 +573,30 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     const int nfull = sg.t_len / kTB;
     int k = 0;
     for (; k + 2 <= nfull; k += 2) {
-        fwd_interval<true, FRONT>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+        fwd_interval<true, HELPER>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
         __syncthreads();
-        fwd_interval<true, FRONT>(sg, k + 1, kTB, A2, h, r, ddtB, ddtA, sDD, sP);
+        fwd_interval<true, HELPER>(sg, k + 1, kTB, A2, h, r, ddtB, ddtA, sDD, sP);
         __syncthreads();
     }
     if (k < sg.ntiles) {
         if (k < nfull)
-            fwd_interval<true, FRONT>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+            fwd_interval<true, HELPER>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
         else
-            fwd_interval<false, FRONT>(sg, k, sg.t_len - k * kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+            fwd_interval<false, HELPER>(sg, k, sg.t_len - k * kTB, A2, h, r, ddtA, ddtB, sDD, sP);
         __syncthreads();
         if (k + 1 < sg.ntiles) {  // ragged last tile after a full one
-            fwd_interval<false, FRONT>(sg, k + 1, sg.t_len - (k + 1) * kTB, A2, h, r, ddtB, ddtA, sDD, sP);
+            fwd_interval<false, HELPER>(sg, k + 1, sg.t_len - (k + 1) * kTB, A2, h, r, ddtB, ddtA, sDD, sP);
             __syncthreads();
         }
     }
     // ---- epilogue: finish the last tile
-    if constexpr (FRONT) {
+    if constexpr (HELPER) {
         const int klast = sg.ntiles - 1;
         float part[SPW][G];
 #pragma unroll
         for (int i = 0; i < SPW; ++i)
 #pragma unroll
-            for (int g = 0; g < G; ++g) part[i][g] = sP[klast & 1][g][w * SPW + i][lane];
+            for (int g = 0; g < G; ++g) part[i][g] = sP[klast & 1][g][sg.hw * SPW + i][lane];
         finish_rows(sg, klast, part, r.skip_p, r.gate_p);
     }
 }
@@ -596,14 +615,15 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
 //    waits on a lower-numbered worker, which never waits before publishing
 //    (workgroups are dispatched in increasing order), so every wait ends.
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
+__global__ __launch_bounds__(64 * (G + helper_waves(G))) void scan_fwd_kernel(FwdKArgs a) {
     constexpr int N = NG * G;
-    static_assert(kTB % G == 0, "tile must split evenly over the waves");
+    static_assert(kTB % helper_waves(G) == 0, "tile must split evenly over the helper waves");
     __shared__ float2 sDD[2][kTB][64];   // (Delta, Delta * u) per row and channel
     __shared__ float sP[2][G][kTB][64];  // partial readout of each state group
     float h[NG];
     const int lane = threadIdx.x & 63;
-    const int n0 = wave_id() * NG;
+    const bool state_wave = wave_id() < G;
+    const int n0 = state_wave ? wave_id() * NG : 0;
 
     // Segments of this workgroup, in processing order.  Each is (block,
     // steps [t_begin, t_end), where its initial state comes from, what
@@ -646,29 +666,42 @@ __global__ __launch_bounds__(64 * G) void scan_fwd_kernel(FwdKArgs a) {
         const int64_t chan0 = static_cast<int64_t>(blk % a.dblocks) * 64;
         const int64_t dcl = imin64(chan0 + lane, a.D - 1);
         float* carry_lane = a.carry ? a.carry + (static_cast<int64_t>(blk) * 64 + lane) * N + n0 : nullptr;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) h[k] = 0.0f;
         if (from == kFromH0) {
+            if (state_wave && a.h0) {
 #pragma unroll
-            for (int k = 0; k < NG; ++k) h[k] = a.h0 ? a.h0[(b * a.D + dcl) * N + n0 + k] : 0.0f;
+                for (int k = 0; k < NG; ++k) h[k] = a.h0[(b * a.D + dcl) * N + n0 + k];
+            }
         } else if (from == kFromChunkCarry) {
-            const float* hi = a.h_in + ((b * a.chunks + blockIdx.y) * a.D + dcl) * N + n0;
+            if (state_wave) {
+                const float* hi = a.h_in + ((b * a.chunks + blockIdx.y) * a.D + dcl) * N + n0;
 #pragma unroll
-            for (int k = 0; k < NG; ++k) h[k] = hi[k];
+                for (int k = 0; k < NG; ++k) h[k] = hi[k];
+            }
         } else {
             if (threadIdx.x == 0) {
                 while (__hip_atomic_load(a.flags + blk, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u)
                     __builtin_amdgcn_s_sleep(2);
             }
             __syncthreads();
+            if (state_wave) {
 #pragma unroll
-            for (int k = 0; k < NG; ++k)
-                h[k] = __hip_atomic_load(carry_lane + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int k = 0; k < NG; ++k)
+                    h[k] = __hip_atomic_load(carry_lane + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
         // the same barriers on both paths: the roles differ only in work between them
-        if (wave_id() < front_waves(G))
-            fwd_segment<true, T, NG, G, HAS_Z, PRE>(a, blk, t_begin, t_end, h, sDD, sP);
-        else
+        if (state_wave)
             fwd_segment<false, T, NG, G, HAS_Z, PRE>(a, blk, t_begin, t_end, h, sDD, sP);
-        if (to == kFinal) {
+        else
+            fwd_segment<true, T, NG, G, HAS_Z, PRE>(a, blk, t_begin, t_end, h, sDD, sP);
+        if (!state_wave) {
+            if (to == kPublish) {  // the barriers of the state waves' hand-over
+                __threadfence();
+                __syncthreads();
+            }
+        } else if (to == kFinal) {
             if (a.h_final && chan0 + lane < a.D) {
                 float* hf = a.h_final + (b * a.D + chan0 + lane) * N + n0;
 #pragma unroll
@@ -862,10 +895,11 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, void* scratch, con
             grid = dim3(static_cast<unsigned>(ncu));
         }
     }
+    const dim3 main_block(64 * (G + helper_waves(G)));  // state waves + helper waves
     if (s.z)
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE>), grid, main_block, 0, st, a);
     else
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false, PRE>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false, PRE>), grid, main_block, 0, st, a);
     return hipGetLastError();
 }
 
@@ -883,8 +917,8 @@ hipError_t dispatch_n(const ScanArgs& s, const FwdPlan& pl, void* scratch, const
         case 4: return launch_fwd_t<T, 1, 4, PRE>(s, pl, scratch, pre, st);
         case 8: return launch_fwd_t<T, 2, 4, PRE>(s, pl, scratch, pre, st);
         case 16: return launch_fwd_t<T, 16 / MSSM_FWD_WAVES_N16, MSSM_FWD_WAVES_N16, PRE>(s, pl, scratch, pre, st);
-        case 32: return launch_fwd_t<T, 8, 4, PRE>(s, pl, scratch, pre, st);
-        case 64: return launch_fwd_t<T, 16, 4, PRE>(s, pl, scratch, pre, st);
+        case 32: return launch_fwd_t<T, 4, 8, PRE>(s, pl, scratch, pre, st);
+        case 64: return launch_fwd_t<T, 8, 8, PRE>(s, pl, scratch, pre, st);
         default: return hipErrorInvalidValue;
     }
 }
