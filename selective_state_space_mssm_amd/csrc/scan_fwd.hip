@@ -164,12 +164,14 @@ __device__ __forceinline__ void fwd_step(int nval, int w, int lane, float (&h)[N
     }
 }
 
-template <int NG, int G, bool FULL, int... J>
+// STAGE: decays and inputs of the tile staged ahead of the state chain (costs
+// 2 * 16 * NG registers).
+template <int NG, int G, bool FULL, bool STAGE, int... J>
 __device__ __forceinline__ void fwd_steps(std::integer_sequence<int, J...>, int nval, int w, int lane,
                                           const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
                                           const float (&Ct)[NG], const float2 (&ddt)[kTB],
                                           float (&sP)[G][kTB][64]) {
-    if constexpr (NG <= 2) {
+    if constexpr (STAGE) {
         float ea[kTB][NG], eg[kTB][NG];
         (fwd_pre<NG, FULL, J>(nval, A2, Bt, ddt, ea, eg), ...);
         (fwd_step<NG, G, FULL, J>(nval, w, lane, h, Ct, ea, eg, sP), ...);
@@ -486,7 +488,10 @@ __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>&
                 buffer_store_act(h[q], rc,
                                  sg.dvalid ? static_cast<uint32_t>((lane * sg.N + sg.n0 + q) * 4) : kNoStore, 0.0f);
         }
-        fwd_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, nval, w, lane, A2, h, Bt, Ct, ddt, sP[cur]);
+        // staging only where registers allow: two states per wave, and not in
+        // the backward pre-pass (whose extra outputs need the registers)
+        fwd_steps<NG, G, FULL, NG <= 2 && !PRE>(std::make_integer_sequence<int, kTB>{}, nval, w, lane, A2, h, Bt,
+                                                 Ct, ddt, sP[cur]);
     }
 }
 
