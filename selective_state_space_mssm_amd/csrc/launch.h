@@ -56,7 +56,7 @@ struct FwdPlan {
 FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N);
 hipError_t launch_fwd(const ScanArgs& a, hipStream_t s);
 // Backward pre-pass: the forward recurrence with, instead of y, the state
-// before every 16-step tile (ckpt, (B, tiles, D, N)), sbar = dy * silu(z)
+// before every 16-step tile (ckpt, (B, tiles, N, D)), sbar = dy * silu(z)
 // ((B, L, D) float32) and dz; fwd_scratch is plan_fwd(...).ws_bytes of scratch.
 hipError_t launch_fwd_prepass(const ScanArgs& a, void* fwd_scratch, float* ckpt, float* sbar, hipStream_t s);
 

@@ -18,7 +18,7 @@
 // Three launches:
 //  1. pre-pass (scan_fwd.hip, the forward kernel in pre-pass mode): the
 //     forward recurrence storing the state before every 16-step tile
-//     (B, tiles, D, N), sbar (B, L, D) float32 and dz;
+//     (B, tiles, N, D), sbar (B, L, D) float32 and dz;
 //  2. reverse (this file): one workgroup per 64-channel block walks the tiles
 //     from last to first.  Lane = channel, wave = state group, as in the
 //     forward.  Per tile it recomputes the tile's states and decays from the
@@ -63,7 +63,7 @@ struct BwdKArgs {
     const float* Dskip;
     const float* dt_bias;
     const float* dh_final;
-    const float* ckpt;   // (B, tiles, D, N) state before every tile (pre-pass)
+    const float* ckpt;   // (B, tiles, N, D) state before every tile (pre-pass)
     const float* sbar;   // (B, L, D) (pre-pass)
     void* du;
     void* ddelta;
@@ -427,7 +427,7 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
         fetch_tile_rows<T, NG>(bk.Bm, rowp, bk.last_row, N, bk.n0, lane, r.qb);
         fetch_tile_rows<T, NG>(bk.Cm, rowp, bk.last_row, N, bk.n0, lane, r.qc);
 #pragma unroll
-        for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tp * bk.ck_stride + q];
+        for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tp * bk.ck_stride + q * bk.D32];
     }
     float hist[kTB][NG], ahist[kTB][NG];
     {
@@ -477,7 +477,7 @@ __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)
         fetch_tile_rows<T, NG>(bk.Bm, rowl, bk.last_row, N, n0, lane, r.qb);
         fetch_tile_rows<T, NG>(bk.Cm, rowl, bk.last_row, N, n0, lane, r.qc);
 #pragma unroll
-        for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tl * bk.ck_stride + q];
+        for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tl * bk.ck_stride + q * bk.D32];
         if constexpr (FRONT) {
             prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, w, lane, sX[tl & 1], r.keep_c);
             fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl - 1, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
     bk.Cm = static_cast<const T*>(a.Cm);
     bk.du_b = static_cast<T*>(a.du) + bk.row_b * D + chan0;
     bk.dd_b = static_cast<T*>(a.ddelta) + bk.row_b * D + chan0;
-    bk.ck_b = a.ckpt + (b * a.tiles * D + dc) * N + bk.n0;
+    bk.ck_b = a.ckpt + (b * a.tiles * N + bk.n0) * D + dc;  // + tile * N * D + state * D
     bk.pBC = a.pBC;
     const int w = bk.w, lane = bk.lane, n0 = bk.n0;
 

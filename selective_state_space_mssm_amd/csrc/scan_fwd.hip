@@ -86,7 +86,7 @@ struct FwdKArgs {
     const void* dy;
     void* dz;              // nullable (no gate)
     float* sbar;           // (B, L, D) dy * silu(z), or dy without a gate
-    float* ckpt;           // (B, tiles, D, N) state before every kTB-step tile
+    float* ckpt;           // (B, tiles, N, D) state before every kTB-step tile
     int64_t tiles;         // ceil(L / kTB)
 };
 
@@ -296,7 +296,7 @@ struct FwdSeg {
     const T* Bm_seg;  // row (b, t_begin) of Bm / Cm
     const T* Cm_seg;
     float* sbar_seg;  // pre-pass: element (b, t_begin, chan0) of sbar
-    float* ckpt_seg;  // pre-pass: ((b * tiles + t_begin / kTB) * D + chan0) * N
+    float* ckpt_seg;  // pre-pass: element (b, t_begin / kTB, 0, chan0) of the (B, tiles, N, D) states
     uint32_t row_off[SPW];  // byte offset of this wave's row i of a tile, this lane's channel
     uint32_t bc_off;        // byte offset of this lane's Bm/Cm values in a tile (step lane % 16)
 };
@@ -480,13 +480,13 @@ __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>&
         unpack_lane_row<T, NG>(r.qb, Bt);
         unpack_lane_row<T, NG>(r.qc, Ct);
         fetch_bc(sg, k + 1, r.qb, r.qc);
-        if constexpr (PRE) {  // the state before tile k
-            const __amdgpu_buffer_rsrc_t rc = make_rsrc(sg.ckpt_seg + static_cast<int64_t>(k) * sg.D * sg.N,
-                                                        static_cast<uint32_t>(64 * sg.N * 4));
+        if constexpr (PRE) {  // the state before tile k: per state one 64-channel row, coalesced
 #pragma unroll
-            for (int q = 0; q < NG; ++q)
-                buffer_store_act(h[q], rc,
-                                 sg.dvalid ? static_cast<uint32_t>((lane * sg.N + sg.n0 + q) * 4) : kNoStore, 0.0f);
+            for (int q = 0; q < NG; ++q) {
+                const __amdgpu_buffer_rsrc_t rc =
+                    make_rsrc(sg.ckpt_seg + (static_cast<int64_t>(k) * sg.N + sg.n0 + q) * sg.D, 64u * 4u);
+                buffer_store_act(h[q], rc, sg.dvalid ? static_cast<uint32_t>(lane) * 4u : kNoStore, 0.0f);
+            }
         }
         // staging only where registers allow: two states per wave, and not in
         // the backward pre-pass (whose extra outputs need the registers)
@@ -539,7 +539,7 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     sg.Bm_seg = static_cast<const T*>(a.Bm) + row_begin * N;
     sg.Cm_seg = static_cast<const T*>(a.Cm) + row_begin * N;
     sg.sbar_seg = PRE ? a.sbar + seg_off : nullptr;
-    sg.ckpt_seg = PRE ? a.ckpt + ((b * a.tiles + t_begin / kTB) * D + chan0) * N : nullptr;
+    sg.ckpt_seg = PRE ? a.ckpt + (b * a.tiles + t_begin / kTB) * N * D + chan0 : nullptr;
     const int D32 = static_cast<int>(D);
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
