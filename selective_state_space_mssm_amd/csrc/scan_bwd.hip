@@ -45,14 +45,10 @@ namespace {
 
 constexpr int kTB = 16;  // tile length (checkpoint spacing, VGPR history depth)
 
-// Waves of a workgroup that also run the per-element front end and the
-// finishing of rows (du, ddelta); the others run only the recompute and the
-// adjoint of their states.  (Issue arbitration favours the waves dispatched
-// first, so those get the extra work.)
-#ifndef MSSM_BWD_FRONT_DIV
-#define MSSM_BWD_FRONT_DIV 2
-#endif
-constexpr int front_waves(int G) { return G >= MSSM_BWD_FRONT_DIV ? G / MSSM_BWD_FRONT_DIV : 1; }
+// Helper waves: besides the G state waves (recompute and adjoint of their
+// states), a workgroup has G/2 (at least one) helper waves that run the
+// per-element front end and the finishing of rows (du, ddelta).
+constexpr int helper_waves(int G) { return G >= 2 ? G / 2 : 1; }
 
 struct BwdKArgs {
     const void* u;
@@ -362,7 +358,7 @@ __device__ __forceinline__ void rev_steps(std::integer_sequence<int, I...>, cons
 // Registers carried from one reverse interval to the next.
 template <typename T, int NG, int G>
 struct RevRegs {
-    static constexpr int SPW = kTB / front_waves(G);
+    static constexpr int SPW = kTB / helper_waves(G);
     float ru[SPW], rd[SPW], rs[SPW];  // raw u, delta, sbar of the next tile to prepare
     uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next tile
     float hin_next[NG];               // checkpoint of the next tile
@@ -375,6 +371,7 @@ struct RevRegs {
 template <typename T>
 struct RevBlock {
     int w, lane, lo, n0, D32, L32, dblk, dblocks, ntiles, softplus_on;
+    int hw;  // helper waves: index among the helpers
     bool dvalid;
     float bias, Dk;
     int64_t row_b, last_row, ck_stride;
@@ -398,51 +395,57 @@ struct RevBlock {
 //   B. the reverse steps of tile k, whose partial sums go to the other of
 //      the two partial-sum buffers (tile k + 1's are still being read).
 // FULL: all 16 steps of the tile exist (every tile but a ragged last one).
-// FRONT: this wave also prepares and finishes rows.
-template <bool FULL, bool FRONT, typename T, int NG, int G>
+// HELPER: a helper wave (rows' front end and finishing), else a state wave.
+template <bool FULL, bool HELPER, typename T, int NG, int G>
 __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int nval, const float (&A2)[NG],
                                              const float (&Aval)[NG], RevRegs<T, NG, G>& r,
                                              float4 (&sX)[2][kTB][64], float2 (&sLQ)[2][G][kTB][64]) {
     constexpr int N = NG * G;
-    constexpr int SPW = kTB / front_waves(G);
+    constexpr int SPW = kTB / helper_waves(G);
     const int cur = k & 1, prv = cur ^ 1;
     const int w = bk.w, lane = bk.lane;
-    // ---- A
-    float4 xt[kTB];
+    if constexpr (HELPER) {
+        if (k + 1 < bk.ntiles) {
+            const int64_t off = static_cast<int64_t>(k + 1) * kTB * bk.D32;
+            finish_rows<T, SPW, G>(sLQ[prv], r.keep_p, bk.hw, lane, bk.dvalid, min(kTB, bk.L32 - (k + 1) * kTB),
+                                   bk.Dk, bk.du_b + off, bk.dd_b + off, bk.D32, r.accD, r.accBias);
+        }
+        RowKeep keep_n[SPW];
+        prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, bk.hw, lane, sX[prv],
+                       keep_n);  // k == 0: unused
+        fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, k - 2, bk.L32, bk.D32, bk.hw * SPW, bk.lo, r.ru, r.rd, r.rs);
 #pragma unroll
-    for (int j = 0; j < kTB; ++j) xt[j] = sX[cur][j][lane];
-    if (FRONT && k + 1 < bk.ntiles) {
-        const int64_t off = static_cast<int64_t>(k + 1) * kTB * bk.D32;
-        finish_rows<T, SPW, G>(sLQ[prv], r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32 - (k + 1) * kTB), bk.Dk,
-                               bk.du_b + off, bk.dd_b + off, bk.D32, r.accD, r.accBias);
-    }
-    float Bt[NG], Ct[NG], hin[NG];
-    unpack_lane_row<T, NG>(r.qb, Bt);
-    unpack_lane_row<T, NG>(r.qc, Ct);
+        for (int i = 0; i < SPW; ++i) {
+            r.keep_p[i] = r.keep_c[i];
+            r.keep_c[i] = keep_n[i];
+        }
+    } else {
+        // ---- tile k's (Delta, Delta*u, sbar); its states recomputed from the checkpoint
+        float4 xt[kTB];
 #pragma unroll
-    for (int q = 0; q < NG; ++q) hin[q] = r.hin_next[q];
-    {
-        const int tp = max(k - 1, 0);
-        const int64_t rowp = bk.row_b + static_cast<int64_t>(tp) * kTB;
-        fetch_tile_rows<T, NG>(bk.Bm, rowp, bk.last_row, N, bk.n0, lane, r.qb);
-        fetch_tile_rows<T, NG>(bk.Cm, rowp, bk.last_row, N, bk.n0, lane, r.qc);
+        for (int j = 0; j < kTB; ++j) xt[j] = sX[cur][j][lane];
+        float Bt[NG], Ct[NG], hin[NG];
+        unpack_lane_row<T, NG>(r.qb, Bt);
+        unpack_lane_row<T, NG>(r.qc, Ct);
 #pragma unroll
-        for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tp * bk.ck_stride + q * bk.D32];
-    }
-    float hist[kTB][NG], ahist[kTB][NG];
-    {
-        float h[NG];
+        for (int q = 0; q < NG; ++q) hin[q] = r.hin_next[q];
+        {
+            const int tp = max(k - 1, 0);
+            const int64_t rowp = bk.row_b + static_cast<int64_t>(tp) * kTB;
+            fetch_tile_rows<T, NG>(bk.Bm, rowp, bk.last_row, N, bk.n0, lane, r.qb);
+            fetch_tile_rows<T, NG>(bk.Cm, rowp, bk.last_row, N, bk.n0, lane, r.qc);
 #pragma unroll
-        for (int q = 0; q < NG; ++q) h[q] = hin[q];
-        rec_steps<NG, FULL>(std::make_integer_sequence<int, kTB>{}, nval, A2, h, Bt, xt, hist, ahist);
-    }
-    RowKeep keep_n[SPW];
-    if constexpr (FRONT) {
-        prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, w, lane, sX[prv], keep_n);  // k == 0: unused
-        fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, k - 2, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
-    }
-    // ---- B (partials of tile k go to the other buffer than those of tile k + 1 just read)
-    {
+            for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tp * bk.ck_stride + q * bk.D32];
+        }
+        float hist[kTB][NG], ahist[kTB][NG];
+        {
+            float h[NG];
+#pragma unroll
+            for (int q = 0; q < NG; ++q) h[q] = hin[q];
+            rec_steps<NG, FULL>(std::make_integer_sequence<int, kTB>{}, nval, A2, h, Bt, xt, hist, ahist);
+        }
+        // ---- the reverse steps of tile k; partials to the other buffer than
+        // those of tile k + 1 that the helpers are reading
         const int64_t row0 = bk.row_b + static_cast<int64_t>(k) * kTB;
         RevCtx<NG, G> c{Aval, Bt, Ct, xt, hist, ahist, hin, sLQ[cur],
                         make_rsrc(bk.pBC + (row0 * bk.dblocks + bk.dblk) * 2 * N,
@@ -450,37 +453,31 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
                         nval, w, lane, bk.dblocks, N, bk.n0};
         rev_steps<NG, G, FULL>(std::make_integer_sequence<int, kTB>{}, c, r.pc, r.dA);
     }
-    if constexpr (FRONT) {
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            r.keep_p[i] = r.keep_c[i];
-            r.keep_c[i] = keep_n[i];
-        }
-    }
 }
 
-// The reverse walk over all tiles (FRONT: with the front end and finishing).
-// Both roles execute the same barriers.
-template <bool FRONT, typename T, int NG, int G>
+// The reverse walk over all tiles.  Both roles execute the same barriers.
+template <bool HELPER, typename T, int NG, int G>
 __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)[NG], const float (&Aval)[NG],
                                         RevRegs<T, NG, G>& r, float4 (&sX)[2][kTB][64],
                                         float2 (&sLQ)[2][G][kTB][64]) {
     constexpr int N = NG * G;
-    constexpr int SPW = kTB / front_waves(G);
-    const int w = bk.w, lane = bk.lane, n0 = bk.n0;
+    constexpr int SPW = kTB / helper_waves(G);
+    const int lane = bk.lane, n0 = bk.n0;
     // ---- prologue: last tile prepared; its Bm/Cm/checkpoint and the next raw rows in flight
     {
         const int tl = bk.ntiles - 1;
         const int64_t rowl = bk.row_b + static_cast<int64_t>(tl) * kTB;
-        if constexpr (FRONT)
-            fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
-        fetch_tile_rows<T, NG>(bk.Bm, rowl, bk.last_row, N, n0, lane, r.qb);
-        fetch_tile_rows<T, NG>(bk.Cm, rowl, bk.last_row, N, n0, lane, r.qc);
+        if constexpr (HELPER) {
+            fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl, bk.L32, bk.D32, bk.hw * SPW, bk.lo, r.ru, r.rd, r.rs);
+            prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, bk.hw, lane, sX[tl & 1],
+                           r.keep_c);
+            fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl - 1, bk.L32, bk.D32, bk.hw * SPW, bk.lo, r.ru, r.rd,
+                               r.rs);
+        } else {
+            fetch_tile_rows<T, NG>(bk.Bm, rowl, bk.last_row, N, n0, lane, r.qb);
+            fetch_tile_rows<T, NG>(bk.Cm, rowl, bk.last_row, N, n0, lane, r.qc);
 #pragma unroll
-        for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tl * bk.ck_stride + q * bk.D32];
-        if constexpr (FRONT) {
-            prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, w, lane, sX[tl & 1], r.keep_c);
-            fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl - 1, bk.L32, bk.D32, w * SPW, bk.lo, r.ru, r.rd, r.rs);
+            for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tl * bk.ck_stride + q * bk.D32];
         }
     }
     __syncthreads();
@@ -488,29 +485,30 @@ __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)
     for (int k = bk.ntiles - 1; k >= 0; --k) {
         const int nval = min(kTB, bk.L32 - k * kTB);
         if (nval == kTB)
-            rev_interval<true, FRONT>(bk, k, kTB, A2, Aval, r, sX, sLQ);
+            rev_interval<true, HELPER>(bk, k, kTB, A2, Aval, r, sX, sLQ);
         else
-            rev_interval<false, FRONT>(bk, k, nval, A2, Aval, r, sX, sLQ);
+            rev_interval<false, HELPER>(bk, k, nval, A2, Aval, r, sX, sLQ);
         __syncthreads();
     }
     // ---- epilogue: finish tile 0
-    if constexpr (FRONT)
-        finish_rows<T, SPW, G>(sLQ[0], r.keep_p, w, lane, bk.dvalid, min(kTB, bk.L32), bk.Dk, bk.du_b, bk.dd_b,
-                               bk.D32, r.accD, r.accBias);
+    if constexpr (HELPER)
+        finish_rows<T, SPW, G>(sLQ[0], r.keep_p, bk.hw, lane, bk.dvalid, min(kTB, bk.L32), bk.Dk, bk.du_b,
+                               bk.dd_b, bk.D32, r.accD, r.accBias);
 }
 
-// Reverse kernel.  Grid: B * dblocks workgroups of 64 * G threads.
+// Reverse kernel.  Grid: B * dblocks workgroups of G state waves + the helper waves.
 template <typename T, int NG, int G>
-__global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
+__global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel(BwdKArgs a) {
     constexpr int N = NG * G;
-    static_assert(kTB % G == 0 && 16 % (2 * NG) == 0, "tile and batch must split evenly");
+    constexpr int H = helper_waves(G);
+    static_assert(kTB % H == 0 && 16 % (2 * NG) == 0, "tile and batch must split evenly");
     // (Delta, Delta*u, sbar, -) per row and channel; after the walk, the
-    // per-wave dD / ddt_bias sums
+    // helper waves' dD / ddt_bias sums
     __shared__ float4 sX[2][kTB][64];
     __shared__ float2 sLQ[2][G][kTB][64];  // per state group: (sum lam*Bm, sum A*lam*a*h_prev)
-    float (&sRed)[2][G][64] = *reinterpret_cast<float (*)[2][G][64]>(&sX[0][0][0]);
-    static_assert(sizeof(float) * 2 * G * 64 <= sizeof(sX), "reduction scratch must fit in sX");
-    constexpr int SPW = kTB / front_waves(G);
+    float (&sRed)[2][H][64] = *reinterpret_cast<float (*)[2][H][64]>(&sX[0][0][0]);
+    static_assert(sizeof(float) * 2 * H * 64 <= sizeof(sX), "reduction scratch must fit in sX");
+    constexpr int SPW = kTB / H;
 
     RevBlock<T> bk;
     bk.lane = threadIdx.x & 63;
@@ -525,7 +523,9 @@ __global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
     bk.dvalid = chan0 + bk.lane < D;
     bk.lo = bk.dvalid ? bk.lane : static_cast<int>(D - 1 - chan0);
     const int64_t dc = chan0 + bk.lo;
-    bk.n0 = bk.w * NG;
+    const bool state_wave = bk.w < G;
+    bk.n0 = state_wave ? bk.w * NG : 0;
+    bk.hw = state_wave ? 0 : bk.w - G;
     bk.ntiles = static_cast<int>(a.tiles);
     bk.softplus_on = a.softplus;
     bk.bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
@@ -548,21 +548,21 @@ __global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
     RevRegs<T, NG, G> r;
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
-        Aval[k] = a.A[dc * N + n0 + k];
+        Aval[k] = state_wave ? a.A[dc * N + n0 + k] : 0.0f;
         A2[k] = Aval[k] * kLog2e;
-        r.pc[k] = (a.dh_final && bk.dvalid) ? a.dh_final[(b * D + dc) * N + n0 + k] : 0.0f;
+        r.pc[k] = (state_wave && a.dh_final && bk.dvalid) ? a.dh_final[(b * D + dc) * N + n0 + k] : 0.0f;
         r.dA[k] = 0.0f;
     }
     r.accD = r.accBias = 0.0f;
 #pragma unroll
     for (int i = 0; i < SPW; ++i) r.keep_p[i] = RowKeep{0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (w < front_waves(G))
-        rev_run<true>(bk, A2, Aval, r, sX, sLQ);
-    else
+    if (state_wave)
         rev_run<false>(bk, A2, Aval, r, sX, sLQ);
+    else
+        rev_run<true>(bk, A2, Aval, r, sX, sLQ);
     // ---- per-(b, d) results
-    if (bk.dvalid) {
+    if (state_wave && bk.dvalid) {
         float* pa = a.pA + (b * D + dc) * N + n0;
 #pragma unroll
         for (int k = 0; k < NG; ++k) pa[k] = r.dA[k];
@@ -572,13 +572,15 @@ __global__ __launch_bounds__(64 * G) void bwd_reverse_kernel(BwdKArgs a) {
             for (int k = 0; k < NG; ++k) g0[k] = r.pc[k];  // a_0 lam_0
         }
     }
-    sRed[0][w][lane] = r.accD;
-    sRed[1][w][lane] = r.accBias;
+    if (!state_wave) {
+        sRed[0][bk.hw][lane] = r.accD;
+        sRed[1][bk.hw][lane] = r.accBias;
+    }
     __syncthreads();
-    if (w == 0 && bk.dvalid) {
+    if (w == G && bk.dvalid) {
         float sd = 0.0f, sb = 0.0f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < H; ++g) {
             sd += sRed[0][g][lane];
             sb += sRed[1][g][lane];
         }
@@ -672,7 +674,7 @@ hipError_t launch_bwd_t(const ScanArgs& s, hipStream_t st) {
     a.dblocks = static_cast<int32_t>((s.D + 63) / 64);
     a.softplus = s.softplus;
     hipLaunchKernelGGL((bwd_reverse_kernel<T, NG, G>), dim3(static_cast<unsigned>(s.B * a.dblocks)),
-                       dim3(64 * G), 0, st, a);
+                       dim3(64 * (G + helper_waves(G))), 0, st, a);
     const int64_t items = s.B * s.L * s.N + s.D * s.N;
     const int64_t blocks = std::min<int64_t>((items + 255) / 256, 16384);
     hipLaunchKernelGGL((bwd_reduce_kernel<T>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
