@@ -53,10 +53,15 @@ namespace {
 constexpr int kTB = 16;  // time steps per tile (= lanes per DPP row)
 
 // Helper waves of a workgroup: besides the G state waves, which run only the
-// recurrence of their states, the workgroup has G/2 (at least one) helper
-// waves that run the per-element front end (loads of u/delta/z, softplus,
-// gate) and the finishing of rows (sum of the partial readouts, store).
-constexpr int helper_waves(int G) { return G >= 2 ? G / 2 : 1; }
+// recurrence of their states, the workgroup has helper waves that run the
+// per-element front end (loads of u/delta/z, softplus, gate) and the
+// finishing of rows (sum of the partial readouts, store): G/2 (at least one)
+// in the forward; G in the backward pre-pass, whose per-element work is
+// heavier (dy, sbar, the dz factor), unless the state waves hold 8 states
+// each (then 2G waves would leave too few registers per wave and spill).
+constexpr int helper_waves(int NG, int G, bool pre) {
+    return (pre && NG <= 4) ? G : (G >= 2 ? G / 2 : 1);
+}
 
 struct FwdKArgs {
     const void* u;
@@ -279,7 +284,7 @@ __device__ __forceinline__ void prep_element_pre(float uu, float dd, float zz, f
 // lane's constant offsets.
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 struct FwdSeg {
-    static constexpr int SPW = kTB / helper_waves(G);
+    static constexpr int SPW = kTB / helper_waves(NG, G, PRE);
     int ntiles, t_len, w, lane;
     int hw;  // helper waves: index among the helpers (rows hw * SPW ..)
     bool dvalid;
@@ -302,9 +307,9 @@ struct FwdSeg {
 };
 
 // Registers carried from one tile interval to the next.
-template <typename T, int NG, int G>
+template <typename T, int NG, int G, bool PRE>
 struct FwdRegs {
-    static constexpr int SPW = kTB / helper_waves(G);
+    static constexpr int SPW = kTB / helper_waves(NG, G, PRE);
     float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];   // raw inputs of the tile prepared next (k + 2)
     uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next recurrence tile
     // skip term and gate (pre-pass: dz factor) of the rows of tiles k + 1 (n),
@@ -315,9 +320,9 @@ struct FwdRegs {
 // Raw inputs of this wave's rows of segment tile `tile` (zeros past the end).
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fetch_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                           float (&ru)[kTB / helper_waves(G)], float (&rd)[kTB / helper_waves(G)],
-                                           float (&rz)[kTB / helper_waves(G)], float (&rdy)[kTB / helper_waves(G)]) {
-    constexpr int SPW = kTB / helper_waves(G);
+                                           float (&ru)[kTB / helper_waves(NG, G, PRE)], float (&rd)[kTB / helper_waves(NG, G, PRE)],
+                                           float (&rz)[kTB / helper_waves(NG, G, PRE)], float (&rdy)[kTB / helper_waves(NG, G, PRE)]) {
+    constexpr int SPW = kTB / helper_waves(NG, G, PRE);
     const int64_t first = static_cast<int64_t>(tile) * kTB * sg.D;       // first element of the tile
     const int64_t bytes = (sg.seg_elems - first) * static_cast<int64_t>(sizeof(T));
     const __amdgpu_buffer_rsrc_t ru_r = range_rsrc(sg.u_seg + first, bytes);
@@ -358,12 +363,12 @@ __device__ __forceinline__ void fetch_bc(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg,
 // next loads are issued, so that waiting for those loads never waits for
 // these stores.)
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, const float (&ru)[kTB / helper_waves(G)],
-                                          const float (&rd)[kTB / helper_waves(G)], const float (&rz)[kTB / helper_waves(G)],
-                                          const float (&rdy)[kTB / helper_waves(G)], float2 (&dst)[kTB][64],
-                                          float (&skip)[kTB / helper_waves(G)], float (&gate)[kTB / helper_waves(G)],
-                                          float (&sbv)[kTB / helper_waves(G)]) {
-    constexpr int SPW = kTB / helper_waves(G);
+__device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, const float (&ru)[kTB / helper_waves(NG, G, PRE)],
+                                          const float (&rd)[kTB / helper_waves(NG, G, PRE)], const float (&rz)[kTB / helper_waves(NG, G, PRE)],
+                                          const float (&rdy)[kTB / helper_waves(NG, G, PRE)], float2 (&dst)[kTB][64],
+                                          float (&skip)[kTB / helper_waves(NG, G, PRE)], float (&gate)[kTB / helper_waves(NG, G, PRE)],
+                                          float (&sbv)[kTB / helper_waves(NG, G, PRE)]) {
+    constexpr int SPW = kTB / helper_waves(NG, G, PRE);
     if constexpr (PRE) {
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
@@ -386,8 +391,8 @@ __device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg
 // Pre-pass: sbar of this wave's rows of segment tile `tile` (rows past the end dropped).
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void store_sbar(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                           const float (&sbv)[kTB / helper_waves(G)]) {
-    constexpr int SPW = kTB / helper_waves(G);
+                                           const float (&sbv)[kTB / helper_waves(NG, G, PRE)]) {
+    constexpr int SPW = kTB / helper_waves(NG, G, PRE);
     if constexpr (PRE) {
         const int rows = sg.t_len - tile * kTB;
         const int D32 = static_cast<int>(sg.D);
@@ -410,9 +415,9 @@ __device__ __forceinline__ void store_sbar(const FwdSeg<T, NG, G, HAS_Z, PRE>& s
 // wave's rows of segment tile `tile` -> y (pre-pass: dz).
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                            const float (&part)[kTB / helper_waves(G)][G], const float (&skip)[kTB / helper_waves(G)],
-                                            const float (&gate)[kTB / helper_waves(G)]) {
-    constexpr int SPW = kTB / helper_waves(G);
+                                            const float (&part)[kTB / helper_waves(NG, G, PRE)][G], const float (&skip)[kTB / helper_waves(NG, G, PRE)],
+                                            const float (&gate)[kTB / helper_waves(NG, G, PRE)]) {
+    constexpr int SPW = kTB / helper_waves(NG, G, PRE);
     const int rows = tile >= 0 ? sg.t_len - tile * kTB : 0;  // tile -1: nothing
     const int D32 = static_cast<int>(sg.D);
     const __amdgpu_buffer_rsrc_t ry =
@@ -447,10 +452,10 @@ __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& 
 // (recurrence of its states).
 template <bool FULL, bool HELPER, typename T, int NG, int G, bool HAS_Z, bool PRE>
 __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int k, int nval,
-                                             const float (&A2)[NG], float (&h)[NG], FwdRegs<T, NG, G>& r,
+                                             const float (&A2)[NG], float (&h)[NG], FwdRegs<T, NG, G, PRE>& r,
                                              const float2 (&ddt)[kTB], float2 (&ddt_next)[kTB],
                                              float2 (&sDD)[2][kTB][64], float (&sP)[2][G][kTB][64]) {
-    constexpr int SPW = kTB / helper_waves(G);
+    constexpr int SPW = kTB / helper_waves(NG, G, PRE);
     const int cur = k & 1, prv = cur ^ 1;
     const int lane = sg.lane, w = sg.w;
     if constexpr (HELPER) {
@@ -503,7 +508,7 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
                                             float (&h)[NG], float2 (&sDD)[2][kTB][64],
                                             float (&sP)[2][G][kTB][64]) {
     constexpr int N = NG * G;
-    constexpr int SPW = kTB / helper_waves(G);  // rows prepared and finished per helper wave per tile
+    constexpr int SPW = kTB / helper_waves(NG, G, PRE);  // rows prepared and finished per helper wave per tile
 
     FwdSeg<T, NG, G, HAS_Z, PRE> sg;
     sg.lane = threadIdx.x & 63;
@@ -550,7 +555,7 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     __syncthreads();  // LDS is reused from a previous segment
     // ---- prologue: tiles 0 and 1 prepared, tile 0's (Delta, Delta*u) in
     // registers, tile 0's Bm/Cm and tile 2's raw inputs in flight
-    FwdRegs<T, NG, G> r;
+    FwdRegs<T, NG, G, PRE> r;
     if constexpr (!HELPER) fetch_bc(sg, 0, r.qb, r.qc);
     if constexpr (HELPER) {
         float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];
@@ -620,9 +625,9 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
 //    waits on a lower-numbered worker, which never waits before publishing
 //    (workgroups are dispatched in increasing order), so every wait ends.
 template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__global__ __launch_bounds__(64 * (G + helper_waves(G))) void scan_fwd_kernel(FwdKArgs a) {
+__global__ __launch_bounds__(64 * (G + helper_waves(NG, G, PRE))) void scan_fwd_kernel(FwdKArgs a) {
     constexpr int N = NG * G;
-    static_assert(kTB % helper_waves(G) == 0, "tile must split evenly over the helper waves");
+    static_assert(kTB % helper_waves(NG, G, PRE) == 0, "tile must split evenly over the helper waves");
     __shared__ float2 sDD[2][kTB][64];   // (Delta, Delta * u) per row and channel
     __shared__ float sP[2][G][kTB][64];  // partial readout of each state group
     float h[NG];
@@ -900,7 +905,7 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, void* scratch, con
             grid = dim3(static_cast<unsigned>(ncu));
         }
     }
-    const dim3 main_block(64 * (G + helper_waves(G)));  // state waves + helper waves
+    const dim3 main_block(64 * (G + helper_waves(NG, G, PRE)));  // state waves + helper waves
     if (s.z)
         hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE>), grid, main_block, 0, st, a);
     else
