@@ -196,8 +196,32 @@ __device__ __forceinline__ void fmac_row_bcast2(float& acc0, float c0, float h0,
     asm("s_nop 1\n\t"
         "v_fmac_f32_dpp %0, %2, %3 row_newbcast:%6 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
         "v_fmac_f32_dpp %1, %4, %5 row_newbcast:%6 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-        : "+v"(acc0), "+v"(acc1)
+        : "+&v"(acc0), "+&v"(acc1)
         : "v"(c0), "v"(h0), "v"(c1), "v"(h1), "i"(J));
+}
+// Two steps J0, J0 + 1 of one state at once (as fmac_row_bcast_x4 below).
+template <int J0>
+__device__ __forceinline__ void fmac_row_bcast_x2(float (&acc)[2], float c, const float (&h)[2]) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %2, %3 row_newbcast:%5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %4 row_newbcast:%6 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "+&v"(acc[0]), "+&v"(acc[1])
+        : "v"(c), "v"(h[0]), "v"(h[1]), "i"(J0), "i"(J0 + 1));
+}
+// Four steps J0 .. J0 + 3 of one state at once: acc[j] += row_bcast<J0 + j>(c)
+// * h[j], behind one pair of wait states.  Inside the statement the four
+// accumulators are independent, so the next statement's update of acc[j]
+// (the next state) comes at least three wait states after this one's.  The
+// accumulators are early-clobber: no input shares a register with them.
+template <int J0>
+__device__ __forceinline__ void fmac_row_bcast_x4(float (&acc)[4], float c, const float (&h)[4]) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %4, %5 row_newbcast:%9 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %4, %6 row_newbcast:%10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %2, %4, %7 row_newbcast:%11 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %3, %4, %8 row_newbcast:%12 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+        : "+&v"(acc[0]), "+&v"(acc[1]), "+&v"(acc[2]), "+&v"(acc[3])
+        : "v"(c), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "i"(J0), "i"(J0 + 1), "i"(J0 + 2), "i"(J0 + 3));
 }
 
 // ---- transcendental building blocks (hardware v_exp/v_log/v_rcp) --------

@@ -55,12 +55,13 @@ constexpr int kTB = 16;  // time steps per tile (= lanes per DPP row)
 // Helper waves of a workgroup: besides the G state waves, which run only the
 // recurrence of their states, the workgroup has helper waves that run the
 // per-element front end (loads of u/delta/z, softplus, gate) and the
-// finishing of rows (sum of the partial readouts, store): G/2 (at least one)
-// in the forward; G in the backward pre-pass, whose per-element work is
-// heavier (dy, sbar, the dz factor), unless the state waves hold 8 states
-// each (then 2G waves would leave too few registers per wave and spill).
+// finishing of rows (sum of the partial readouts, store): one per state wave
+// up to four state waves (one of each per SIMD), else G/2.  The backward
+// pre-pass, whose per-element work is heavier (dy, sbar, the dz factor), has
+// one per state wave also with eight state waves of up to two states (more
+// states per wave would leave too few registers at 16 waves and spill).
 constexpr int helper_waves(int NG, int G, bool pre) {
-    return (pre && NG <= 4) ? G : (G >= 2 ? G / 2 : 1);
+    return (G <= 4 || (pre && NG <= 2)) ? G : G / 2;
 }
 
 struct FwdKArgs {
@@ -138,50 +139,92 @@ __device__ __forceinline__ void fwd_pre(int nval, const float (&A2)[NG], const f
         }
     }
 }
-// Decay, input, state update and partial readout of step J at once.
-template <int NG, int G, bool FULL, int J>
-__device__ __forceinline__ void fwd_pre_step(int nval, int w, int lane, const float (&A2)[NG], float (&h)[NG],
-                                             const float (&Bt)[NG], const float (&Ct)[NG], const float2 (&ddt)[kTB],
-                                             float (&sP)[G][kTB][64]) {
+// Steps per readout group: the states after each step of a group stay in
+// registers (NG * S of them) until the group's readouts.  Measured on the
+// 2.8B and 130M layer shapes: four steps for bf16 activations, two for fp32
+// ones (16 % and 10 % faster than the other choice); two with eight states
+// per wave, where four would spill.
+template <typename T, int NG>
+constexpr int group_steps() { return (sizeof(T) == 4 || NG >= 8) ? 2 : 4; }
+
+// State update of step J, from the staged decay and input (ea, eg non-null)
+// or computing them here; the state after the step goes to hs[.][J % S]
+// for the readout of its group.
+template <int NG, int S, bool FULL, int J>
+__device__ __forceinline__ void fwd_update(int nval, const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
+                                           const float2 (&ddt)[kTB], const float (*ea)[NG], const float (*eg)[NG],
+                                           float (&hs)[NG][S]) {
     if (FULL || J < nval) {
-        const float2 dd = ddt[J];
+        if (ea) {
 #pragma unroll
-        for (int k = 0; k < NG; ++k)
-            h[k] = __builtin_fmaf(fast_exp2(dd.x * A2[k]), h[k], row_bcast<J>(Bt[k]) * dd.y);
-        float yp = row_bcast<J>(Ct[0]) * h[0];
+            for (int k = 0; k < NG; ++k) h[k] = __builtin_fmaf(ea[J][k], h[k], eg[J][k]);
+        } else {
+            const float2 dd = ddt[J];
 #pragma unroll
-        for (int k = 1; k < NG; ++k) yp = fmac_row_bcast<J>(yp, Ct[k], h[k]);
-        sP[w][J][lane] = yp;
+            for (int k = 0; k < NG; ++k)
+                h[k] = __builtin_fmaf(fast_exp2(dd.x * A2[k]), h[k], row_bcast<J>(Bt[k]) * dd.y);
+        }
     }
+#pragma unroll
+    for (int k = 0; k < NG; ++k) hs[k][J % S] = h[k];
 }
-// State update and partial readout (to sP[w][J]) of step J:
-template <int NG, int G, bool FULL, int J>
-__device__ __forceinline__ void fwd_step(int nval, int w, int lane, float (&h)[NG], const float (&Ct)[NG],
-                                         const float (&ea)[kTB][NG], const float (&eg)[kTB][NG],
-                                         float (&sP)[G][kTB][64]) {
-    if (FULL || J < nval) {
-#pragma unroll
-        for (int k = 0; k < NG; ++k) h[k] = __builtin_fmaf(ea[J][k], h[k], eg[J][k]);
-        float yp = row_bcast<J>(Ct[0]) * h[0];
-#pragma unroll
-        for (int k = 1; k < NG; ++k) yp = fmac_row_bcast<J>(yp, Ct[k], h[k]);
-        sP[w][J][lane] = yp;
+// Partial readouts sum_k Cm[t, k] h_t[k] over this wave's states of the
+// steps J0 .. J0 + S - 1, to sP[w][J].  Per state one DPP statement covers
+// the group (one pair of wait states per S multiply-adds).
+template <int NG, int G, int S, bool FULL, int J0>
+__device__ __forceinline__ void fwd_readout(int nval, int w, int lane, const float (&Ct)[NG],
+                                            const float (&hs)[NG][S], float (&sP)[G][kTB][64]) {
+    static_assert(S == 2 || S == 4, "groups of two or four steps");
+    float y[S];
+    y[0] = row_bcast<J0>(Ct[0]) * hs[0][0];
+    y[1] = row_bcast<J0 + 1>(Ct[0]) * hs[0][1];
+    if constexpr (S == 4) {
+        y[2] = row_bcast<J0 + 2>(Ct[0]) * hs[0][2];
+        y[3] = row_bcast<J0 + 3>(Ct[0]) * hs[0][3];
     }
+#pragma unroll
+    for (int k = 1; k < NG; ++k) {
+        if constexpr (S == 4) fmac_row_bcast_x4<J0>(y, Ct[k], hs[k]);
+        else fmac_row_bcast_x2<J0>(y, Ct[k], hs[k]);
+    }
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+        if (FULL || J0 + j < nval) sP[w][J0 + j][lane] = y[j];
+}
+// Steps J0 .. J0 + S - 1: state updates, then their readouts.
+template <int NG, int G, int S, bool FULL, int J0, int... J>
+__device__ __forceinline__ void fwd_group(std::integer_sequence<int, J...>, int nval, int w, int lane,
+                                          const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
+                                          const float (&Ct)[NG], const float2 (&ddt)[kTB], const float (*ea)[NG],
+                                          const float (*eg)[NG], float (&sP)[G][kTB][64]) {
+    float hs[NG][S];
+    (fwd_update<NG, S, FULL, J0 + J>(nval, A2, h, Bt, ddt, ea, eg, hs), ...);
+    fwd_readout<NG, G, S, FULL, J0>(nval, w, lane, Ct, hs, sP);
 }
 
-// STAGE: decays and inputs of the tile staged ahead of the state chain (costs
-// 2 * 16 * NG registers).
-template <int NG, int G, bool FULL, bool STAGE, int... J>
-__device__ __forceinline__ void fwd_steps(std::integer_sequence<int, J...>, int nval, int w, int lane,
+template <int NG, bool FULL, int... J>
+__device__ __forceinline__ void fwd_pre_all(std::integer_sequence<int, J...>, int nval, const float (&A2)[NG],
+                                            const float (&Bt)[NG], const float2 (&ddt)[kTB], float (&ea)[kTB][NG],
+                                            float (&eg)[kTB][NG]) {
+    (fwd_pre<NG, FULL, J>(nval, A2, Bt, ddt, ea, eg), ...);
+}
+
+// The tile's 16 steps in groups of S.  STAGE: decays and inputs of the
+// whole tile staged ahead of the state chain (costs 2 * 16 * NG registers).
+template <int NG, int G, int S, bool FULL, bool STAGE, int... Q>
+__device__ __forceinline__ void fwd_steps(std::integer_sequence<int, Q...>, int nval, int w, int lane,
                                           const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
                                           const float (&Ct)[NG], const float2 (&ddt)[kTB],
                                           float (&sP)[G][kTB][64]) {
+    static_assert(sizeof...(Q) * S == kTB, "the groups cover the tile");
     if constexpr (STAGE) {
         float ea[kTB][NG], eg[kTB][NG];
-        (fwd_pre<NG, FULL, J>(nval, A2, Bt, ddt, ea, eg), ...);
-        (fwd_step<NG, G, FULL, J>(nval, w, lane, h, Ct, ea, eg, sP), ...);
+        fwd_pre_all<NG, FULL>(std::make_integer_sequence<int, kTB>{}, nval, A2, Bt, ddt, ea, eg);
+        (fwd_group<NG, G, S, FULL, S * Q>(std::make_integer_sequence<int, S>{}, nval, w, lane, A2, h, Bt, Ct,
+                                           ddt, ea, eg, sP), ...);
     } else {  // many states per wave: enough independent work per step, and too many registers to stage
-        ((fwd_pre_step<NG, G, FULL, J>(nval, w, lane, A2, h, Bt, Ct, ddt, sP)), ...);
+        (fwd_group<NG, G, S, FULL, S * Q>(std::make_integer_sequence<int, S>{}, nval, w, lane, A2, h, Bt, Ct,
+                                           ddt, nullptr, nullptr, sP), ...);
     }
 }
 
@@ -493,10 +536,11 @@ __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>&
                 buffer_store_act(h[q], rc, sg.dvalid ? static_cast<uint32_t>(lane) * 4u : kNoStore, 0.0f);
             }
         }
+        constexpr int S = group_steps<T, NG>();
         // staging only where registers allow: two states per wave, and not in
         // the backward pre-pass (whose extra outputs need the registers)
-        fwd_steps<NG, G, FULL, NG <= 2 && !PRE>(std::make_integer_sequence<int, kTB>{}, nval, w, lane, A2, h, Bt,
-                                                 Ct, ddt, sP[cur]);
+        fwd_steps<NG, G, S, FULL, NG <= 2 && !PRE>(std::make_integer_sequence<int, kTB / S>{}, nval, w, lane, A2,
+                                                    h, Bt, Ct, ddt, sP[cur]);
     }
 }
 
@@ -913,12 +957,6 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, void* scratch, con
     return hipGetLastError();
 }
 
-// Waves per workgroup (state groups) for N = 16, the state size of every
-// pretrained Mamba model.
-#ifndef MSSM_FWD_WAVES_N16
-#define MSSM_FWD_WAVES_N16 8
-#endif
-
 template <typename T, bool PRE>
 hipError_t dispatch_n(const ScanArgs& s, const FwdPlan& pl, void* scratch, const PreOut& pre, hipStream_t st) {
     switch (s.N) {
@@ -926,7 +964,9 @@ hipError_t dispatch_n(const ScanArgs& s, const FwdPlan& pl, void* scratch, const
         case 2: return launch_fwd_t<T, 1, 2, PRE>(s, pl, scratch, pre, st);
         case 4: return launch_fwd_t<T, 1, 4, PRE>(s, pl, scratch, pre, st);
         case 8: return launch_fwd_t<T, 2, 4, PRE>(s, pl, scratch, pre, st);
-        case 16: return launch_fwd_t<T, 16 / MSSM_FWD_WAVES_N16, MSSM_FWD_WAVES_N16, PRE>(s, pl, scratch, pre, st);
+        case 16:  // the state size of every pretrained Mamba model
+            if constexpr (PRE) return launch_fwd_t<T, 2, 8, PRE>(s, pl, scratch, pre, st);
+            else return launch_fwd_t<T, 4, 4, PRE>(s, pl, scratch, pre, st);
         case 32: return launch_fwd_t<T, 4, 8, PRE>(s, pl, scratch, pre, st);
         case 64: return launch_fwd_t<T, 8, 8, PRE>(s, pl, scratch, pre, st);
         default: return hipErrorInvalidValue;
