@@ -11,7 +11,10 @@ float32 arithmetic), inputs resident in HBM.  Prints one JSON line:
   recorded around every timed launch on the launch stream, against the VALU
   issue-rate bound of the chip: the scan does 4 VALU instructions and one
   half-rate v_exp_f32 per (b, t, d, n) and moves only O(B L D) bytes, so at
-  these shapes the VALU, not HBM, bounds it;
+  these shapes the VALU, not HBM, bounds it.  Also the median and minimum
+  launch, a cold launch (after overwriting the 256 MB last-level cache with a
+  512 MB scratch write, untimed) and the bandwidth of a plain 1 GiB device
+  copy measured in the same run;
 * cpu_baseline: the float64 oracle timed on this host on a bounded channel
   sample of the same workload.
 
@@ -95,7 +98,7 @@ def measured_traffic():
         return None
 
 
-def time_fwd(mssm, torch, w, steps, warmup):
+def time_fwd(mssm, torch, w, steps, warmup, cold_reps=0):
     inp = workloads.make_inputs(w)
     t = workloads.to_torch(inp, "cuda")
     del inp
@@ -121,7 +124,38 @@ def time_fwd(mssm, torch, w, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     launch_ms = [a.elapsed_time(b) for a, b in ev]
-    return wall, launch_ms
+    cold_ms = []
+    if cold_reps:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        for _ in range(cold_reps):
+            scratch.fill_(1)  # untimed: evicts the inputs from the last-level cache
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold_ms.append(a.elapsed_time(b))
+        del scratch
+    return wall, launch_ms, cold_ms
+
+
+def copy_bandwidth(torch, reps=5):
+    """Read + write bytes per second of a plain 1 GiB device-to-device copy."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    return 2 * n / (float(np.median(ms)) / 1e3) / 1e9
 
 
 def time_bwd(mssm, torch, w, steps, warmup):
@@ -208,7 +242,8 @@ def main():
 
     w = workloads.WORKLOADS[args.workload]
     log(f"workload {workloads.DESCRIPTIONS[w.name]}; steps {args.steps}, warmup {args.warmup}")
-    wall, launch_ms = time_fwd(mssm, torch, w, args.steps, args.warmup)
+    wall, launch_ms, cold_ms = time_fwd(mssm, torch, w, args.steps, args.warmup, cold_reps=5)
+    copy_gbs = copy_bandwidth(torch)
     nbytes = fwd_bytes(w)
     gbs = nbytes / wall / 1e9
     kern_s = float(np.mean(launch_ms)) / 1e3
@@ -241,14 +276,19 @@ def main():
             "kernel": "scan_fwd_kernel",
             "kernel_us": round(kern_s * 1e6, 2),
             "work_per_launch": f"{SLOTS_PER_ELEM_STATE} VALU issue slots x {w.elem_states} (b,t,d,n)",
+            "kernel_us_median": round(float(np.median(launch_ms)) * 1e3, 2),
+            "kernel_us_min": round(float(np.min(launch_ms)) * 1e3, 2),
+            "kernel_us_cold": round(float(np.median(cold_ms)) * 1e3, 2),
             "hbm_achieved_GBs": round(nbytes / kern_s / 1e9, 1),
             "hbm_peak_GBs": HBM_PEAK_GBS,
+            "copy_GBs": round(copy_gbs, 1),
+            "frac_of_copy": round(nbytes / kern_s / 1e9 / copy_gbs, 4),
         },
     }
     if args.extra:
         for name in ("130m",):
             ww = workloads.WORKLOADS[name]
-            wl, lm = time_fwd(mssm, torch, ww, 20, 3)
+            wl, _, _ = time_fwd(mssm, torch, ww, 20, 3)
             out.setdefault("extra", {})[f"{name}_fwd_GBs"] = round(fwd_bytes(ww) / wl / 1e9, 1)
             out["extra"][f"{name}_fwd_us"] = round(wl * 1e6, 1)
         tw = workloads.WORKLOADS["train"]
@@ -258,7 +298,7 @@ def main():
         if args.long:
             lw = workloads.WORKLOADS["long"]
             log("generating the 1M-step workload")
-            wl, _ = time_fwd(mssm, torch, lw, 5, 1)
+            wl, _, _ = time_fwd(mssm, torch, lw, 5, 1)
             out["extra"]["long_fwd_us"] = round(wl * 1e6, 1)
             out["extra"]["long_fwd_GBs"] = round(fwd_bytes(lw) / wl / 1e9, 1)
             out["extra"]["long_elem_state_per_s"] = float(f"{lw.elem_states / wl:.4e}")
