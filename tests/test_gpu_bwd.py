@@ -79,6 +79,19 @@ def test_bf16(mssm):
     assert_grads(g, r, GRAD_TOL["bf16"])
 
 
+@pytest.mark.parametrize("L", [23, 46])
+def test_bf16_ragged(mssm, L):
+    # the pre-pass's readout groups end inside a group in the last tile
+    g, r = run_both(mssm, workloads.custom(2, L, 96, 16, "bf16", seed=L + 61))
+    assert_grads(g, r, GRAD_TOL["bf16"])
+
+
+@pytest.mark.parametrize("N", [4, 8, 64])
+def test_state_sizes_bf16(mssm, N):
+    g, r = run_both(mssm, workloads.custom(2, 43, 70, N, "bf16", seed=N + 70))
+    assert_grads(g, r, GRAD_TOL["bf16"])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_chunked_prepass(mssm, dtype):
     # one channel block and L >= 2048: the forward pre-pass runs the chunked

@@ -3,8 +3,8 @@ float64 oracle, element by element, on seeded synthetic inputs.
 
 Covers: the Tiny workload in full; ragged small shapes (channels not a
 multiple of 64, sequence not a multiple of the 16-step tile) with every
-optional input present and absent, softplus on and off; every supported
-state size; bfloat16 activations; the chunked (cross-chunk carry) schedule
+optional input present and absent, softplus on and off; last tiles that end
+inside a readout group; every supported state size in fp32 and bf16; the chunked (cross-chunk carry) schedule
 with a ragged last chunk; the 130M and 2.8B layer workloads (130M in full,
 2.8B on sampled channels over the whole sequence -- channels are independent,
 so the oracle computes them one by one); the 1M-step workload on sampled
@@ -58,6 +58,14 @@ def test_ragged_shapes_all_options(mssm, shape, dtype):
     check(mssm, workloads.custom(B, L, D, 16, dtype, seed=L + D), h0=True)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("L", [18, 23, 30, 47])
+def test_ragged_readout_groups(mssm, L, dtype):
+    # the partial readouts of a tile are formed in groups of 2 (fp32) or 4
+    # (bf16) steps: a last tile of 2, 7, 14 or 15 steps ends inside a group
+    check(mssm, workloads.custom(2, L, 96, 16, dtype, seed=L + 500), h0=True)
+
+
 @pytest.mark.parametrize("use", [(), ("z",), ("Dskip",), ("dt_bias",), ("Dskip", "dt_bias")])
 def test_optional_inputs(mssm, use):
     check(mssm, workloads.custom(2, 45, 80, 16, "f32", seed=11), h0=False, use=use)
@@ -80,6 +88,13 @@ def test_softplus_off(mssm):
 @pytest.mark.parametrize("N", [1, 2, 4, 8, 32, 64])
 def test_state_sizes(mssm, N):
     check(mssm, workloads.custom(2, 50, 90, N, "f32", seed=N), h0=True)
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 32, 64])
+def test_state_sizes_bf16(mssm, N):
+    # bf16 rows of Bm/Cm per lane (one value for N = 1), readout groups of
+    # 4 steps (2 with 8 states per wave), a last tile of 3 steps
+    check(mssm, workloads.custom(2, 51, 90, N, "bf16", seed=N + 7), h0=True)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
