@@ -246,10 +246,9 @@ __device__ __forceinline__ void fwd_steps(std::integer_sequence<int, Q...>, int 
 
 template <int NG, bool FULL, int J>
 __device__ __forceinline__ void state_step(int nval, const float (&A2)[NG], float (&h)[NG],
-                                           const float (&Bt)[NG], const float2 (&ddt)[kTB], float& ssum) {
+                                           const float (&Bt)[NG], const float2 (&ddt)[kTB]) {
     if (FULL || J < nval) {
         const float2 dd = ddt[J];
-        ssum += dd.x;
 #pragma unroll
         for (int k = 0; k < NG; ++k)
             h[k] = __builtin_fmaf(fast_exp2(dd.x * A2[k]), h[k], row_bcast<J>(Bt[k]) * dd.y);
@@ -259,10 +258,10 @@ __device__ __forceinline__ void state_step(int nval, const float (&A2)[NG], floa
 template <int NG, bool FULL, int... J>
 __device__ __forceinline__ void state_steps(std::integer_sequence<int, J...>, int nval, int lane,
                                             const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
-                                            const float2 (&sDD)[kTB][64], float& ssum) {
+                                            const float2 (&sDD)[kTB][64]) {
     float2 ddt[kTB];
     ((ddt[J] = (FULL || J < nval) ? sDD[J][lane] : make_float2(0.0f, 0.0f)), ...);
-    (state_step<NG, FULL, J>(nval, A2, h, Bt, ddt, ssum), ...);
+    (state_step<NG, FULL, J>(nval, A2, h, Bt, ddt), ...);
 }
 
 // ---- buffer loads ---------------------------------------------------------------
@@ -793,13 +792,18 @@ __global__ __launch_bounds__(256) void zero_flags_kernel(uint32_t* flags, int n)
 }
 
 // Chunk aggregates: end state of chunk c started from zero (chunk 0 from h0)
-// and the chunk's sum of Delta.  Grid: (B * dblocks, K - 1).
+// and the chunk's sum of Delta.  Grid: (B * dblocks, K - 1).  Per tile, each
+// wave prepares (Delta, Delta*u) of its rows of the next tile into the other
+// LDS buffer while every wave runs the recurrence of its states over this
+// tile: one barrier per tile.  Each wave sums Delta over its own rows; the
+// waves' sums are added in a fixed order at the end.
 template <typename T, int NG, int G>
 __global__ __launch_bounds__(64 * G) void scan_chunk_state_kernel(FwdKArgs a) {
     constexpr int N = NG * G;
     constexpr int SPW = kTB / G;
     constexpr int W = LaneRow<T, NG>::kWords;
-    __shared__ float2 sDD[kTB][64];
+    __shared__ float2 sDD[2][kTB][64];
+    __shared__ float sSum[G][64];
 
     const T* __restrict__ u = static_cast<const T*>(a.u);
     const T* __restrict__ dl = static_cast<const T*>(a.delta);
@@ -829,7 +833,7 @@ __global__ __launch_bounds__(64 * G) void scan_chunk_state_kernel(FwdKArgs a) {
         for (int k = 0; k < NG; ++k) h[k] = 0.0f;
     }
     const float bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
-    float ssum = 0.0f;
+    float psum = 0.0f;  // sum of Delta over this wave's rows
 
     const int64_t t_begin = c * a.chunk_len;
     const int t_len = static_cast<int>(imin64(L, t_begin + a.chunk_len) - t_begin);
@@ -837,41 +841,62 @@ __global__ __launch_bounds__(64 * G) void scan_chunk_state_kernel(FwdKArgs a) {
     const int64_t row_begin = b * L + t_begin;
     const int64_t last_row = row_begin + t_len - 1;
     float ru[SPW], rd[SPW], rz[SPW];
-    uint32_t qb[W];
-    fetch_rows_ptr<T, SPW>(u, dl, static_cast<const T*>(nullptr), row_begin * D + chan0, w * SPW, t_len, D32, lo,
-                       ru, rd, rz);
-    fetch_tile_rows<T, NG>(Bm, row_begin, last_row, N, n0, lane, qb);
-    for (int tile = 0; tile < ntiles; ++tile) {
+    uint32_t qb[W], qn[W];
+
+    // (Delta, Delta * u) of this wave's rows of segment tile `tile` (raw rows in ru, rd) into buffer `buf`
+    auto prep = [&](int tile, int buf) {
         const int nval = min(kTB, t_len - tile * kTB);
-        const int64_t row0 = row_begin + static_cast<int64_t>(tile) * kTB;
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int j = w * SPW + i;
             if (j < nval) {
                 const float x = rd[i] + bias;
                 const float dt = a.softplus ? softplus(x) : x;
-                sDD[j][lane] = make_float2(dt, dt * ru[i]);
+                sDD[buf][j][lane] = make_float2(dt, dt * ru[i]);
+                psum += dt;
             }
         }
+    };
+    auto fetch = [&](int tile, uint32_t (&q)[W]) {
+        const int64_t row0 = row_begin + static_cast<int64_t>(tile) * kTB;
+        fetch_rows_ptr<T, SPW>(u, dl, static_cast<const T*>(nullptr), row0 * D + chan0, w * SPW,
+                               t_len - tile * kTB, D32, lo, ru, rd, rz);
+        fetch_tile_rows<T, NG>(Bm, row0, last_row, N, n0, lane, q);
+    };
+
+    fetch(0, qb);
+    prep(0, 0);
+    if (ntiles > 1) fetch(1, qn);
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int cur = tile & 1;
         float Bt[NG];
         unpack_lane_row<T, NG>(qb, Bt);
         if (tile + 1 < ntiles) {
-            fetch_rows_ptr<T, SPW>(u, dl, static_cast<const T*>(nullptr), (row0 + kTB) * D + chan0, w * SPW,
-                               t_len - (tile + 1) * kTB, D32, lo, ru, rd, rz);
-            fetch_tile_rows<T, NG>(Bm, row0 + kTB, last_row, N, n0, lane, qb);
+            prep(tile + 1, cur ^ 1);
+#pragma unroll
+            for (int i = 0; i < W; ++i) qb[i] = qn[i];
+            if (tile + 2 < ntiles) fetch(tile + 2, qn);
         }
-        __syncthreads();
+        const int nval = min(kTB, t_len - tile * kTB);
         if (nval == kTB)
-            state_steps<NG, true>(std::make_integer_sequence<int, kTB>{}, kTB, lane, A2, h, Bt, sDD, ssum);
+            state_steps<NG, true>(std::make_integer_sequence<int, kTB>{}, kTB, lane, A2, h, Bt, sDD[cur]);
         else
-            state_steps<NG, false>(std::make_integer_sequence<int, kTB>{}, nval, lane, A2, h, Bt, sDD, ssum);
+            state_steps<NG, false>(std::make_integer_sequence<int, kTB>{}, nval, lane, A2, h, Bt, sDD[cur]);
         __syncthreads();
     }
+    sSum[w][lane] = psum;
+    __syncthreads();
     if (dvalid) {
         float* ho = a.agg_h + ((b * a.chunks + c) * D + chan0 + lane) * N + n0;
 #pragma unroll
         for (int k = 0; k < NG; ++k) ho[k] = h[k];
-        if (w == 0) a.agg_s[(b * a.chunks + c) * D + chan0 + lane] = ssum;
+        if (w == 0) {
+            float ssum = 0.0f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) ssum += sSum[g][lane];
+            a.agg_s[(b * a.chunks + c) * D + chan0 + lane] = ssum;
+        }
     }
 }
 
