@@ -20,15 +20,15 @@
 //     forward recurrence storing the state before every 16-step tile
 //     (B, tiles, N, D), sbar (B, L, D) float32 and dz;
 //  2. reverse (this file): one workgroup per 64-channel block walks the tiles
-//     from last to first.  Lane = channel, wave = state group, as in the
-//     forward.  Per tile it recomputes the tile's states and decays from the
-//     checkpoint into VGPRs, then runs the adjoint backwards over the tile.
-//     Bm/Cm reach the lanes by DPP row broadcast; (Delta, Delta*u, sbar) is
-//     shared by the waves through LDS (prepared by the first half of the
-//     waves).  Each wave leaves its partial sums over its states of lam*Bm
-//     and A*lam*a*h_prev in LDS (two buffers, one barrier per tile), and in
-//     the next interval the same front waves finish the tile's rows (du,
-//     ddelta).  dB/dC are summed over the wave's 64 channels by a
+//     from last to first.  Lane = channel; each state wave owns a group of
+//     states, as in the forward (N = 16: 8 state waves of 2 states), plus
+//     helper waves.  Per tile each state wave recomputes the tile's states and
+//     decays from the checkpoint into VGPRs, then runs the adjoint backwards
+//     over the tile.  Bm/Cm reach the lanes by DPP row broadcast; (Delta,
+//     Delta*u, sbar) is prepared by the helper waves and shared through LDS.
+//     Each state wave leaves its partial sums over its states of lam*Bm and
+//     A*lam*a*h_prev in LDS (two buffers, one barrier per tile), and in the
+//     next interval the helpers finish the tile's rows (du, ddelta).  dB/dC are summed over the wave's 64 channels by a
 //     transpose-reduce across lanes (16 values in 35 instructions) and
 //     stored per channel block;
 //  3. reduce: fixed-order sums of the per-block dB/dC partials and of the

@@ -10,22 +10,25 @@
 // Mapping (one workgroup = one batch row b x 64 channels x one time chunk):
 //  * lane = channel d: u, delta, z, y are read/written one row (b, t, 64 d)
 //    at a time, consecutive lanes on consecutive addresses;
-//  * wave w of the G waves = state group n in [w*NG, (w+1)*NG); the NG
-//    states of each channel live in VGPRs and are never written to memory
-//    (the (B,L,D,N) expansion does not exist);
+//  * state wave w of the G state waves = state group n in [w*NG, (w+1)*NG);
+//    the NG states of each channel live in VGPRs and are never written to
+//    memory (the (B,L,D,N) expansion does not exist).  N = 16: 4 state waves
+//    of 4 states;
 //  * Bm[b,t,n], Cm[b,t,n] are the same for all 64 channels: a tile of them
 //    sits in VGPRs with lane l holding step l % 16 (replicated over the four
 //    16-lane rows), and step j reads it through a DPP row_newbcast:j source
 //    modifier on the v_mul / v_fmac that consumes it -- a broadcast with no
 //    extra instruction, no LDS traffic and no scalar-load waits;
-//  * per time tile of 16 steps: the first half of the waves (the "front"
-//    waves) turn the tile's rows of (u, delta, z) into (Delta, Delta*u) in
-//    LDS, the skip term and the gate (softplus and silu once per element,
-//    shared by all G waves); every wave runs the recurrence for its states
-//    over the tile and leaves its partial readout in LDS; the front waves
-//    then finish the rows: sum of the G partials + Dskip*u, times silu(z),
-//    store.  (The hardware favours the waves dispatched first when two waves
-//    of a SIMD are ready; giving them the per-element work balances the two.)
+//  * per time tile of 16 steps: helper waves (one per state wave for N = 16)
+//    turn the tile's rows of (u, delta, z) into (Delta, Delta*u) in LDS, the
+//    skip term and the gate (softplus and silu once per element, shared by
+//    all state waves); every state wave runs the recurrence of its states
+//    over the tile and leaves its partial readout per step in LDS; the
+//    helpers then finish the rows: sum of the G partials + Dskip*u, times
+//    silu(z), store;
+//  * the partial readouts of a group of 2 or 4 steps are issued together, one
+//    DPP multiply-add statement per state, so that a pair of wait states
+//    (the DPP read-after-write rule) covers the whole group;
 //  * software pipeline, one barrier per tile: front end two tiles ahead,
 //    finishing one tile behind, the next tile's (Delta, Delta*u) read from
 //    LDS while the current one runs; global loads through buffer resources;
