@@ -19,8 +19,11 @@ float32 arithmetic), inputs resident in HBM.  Prints one JSON line:
   sample of the same workload.
 
 ``--gpus N`` with N > 1 exits: this benchmark and the library run on one GPU.
-``--extra`` adds the 130M-layer forward and the training-workload backward
-(``--long`` also the 1M-step forward).
+``--extra`` adds the 130M-layer forward, the recurrent step at the 2.8B layer's
+width (B=4, D=5120, N=16: one decode step per call from Python, so the host's
+launch overhead, not the kernel, sets this rate; the kernel's own duration is
+in the kernel trace) and the training-workload backward (``--long`` also the
+1M-step forward).
 ``--copy-probe`` runs a plain device copy of 1 GiB first (counter calibration).
 """
 from __future__ import annotations
@@ -178,6 +181,32 @@ def time_bwd(mssm, torch, w, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def time_step(mssm, torch, w, reps=200):
+    """One recurrent step (decode) at the workload's width: (B, D) inputs, the
+    (B, D, N) float32 state updated in place.  Returns (us per call, GB/s of
+    algorithmic bytes: state read + write, inputs, y, A, Dskip, dt_bias)."""
+    inp = workloads.make_inputs(workloads.custom(w.B, 1, w.D, w.N, w.dtype, seed=w.seed))
+    t = workloads.to_torch(inp, "cuda")
+    args = [t["u"][:, 0].contiguous(), t["delta"][:, 0].contiguous(), t["A"], t["Bm"][:, 0].contiguous(),
+            t["Cm"][:, 0].contiguous()]
+    z_t = t["z"][:, 0].contiguous()
+    state = torch.zeros((w.B, w.D, w.N), dtype=torch.float32, device="cuda")
+    y_t = torch.empty_like(z_t)
+    for _ in range(10):
+        mssm.step(*args, state, t["Dskip"], z_t, t["dt_bias"], y_t=y_t)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        mssm.step(*args, state, t["Dskip"], z_t, t["dt_bias"], y_t=y_t)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    act = 2 if w.dtype == "bf16" else 4
+    nbytes = 8 * w.B * w.D * w.N + 4 * w.B * w.D * act + 2 * w.B * w.N * act + 4 * w.D * w.N + 8 * w.D
+    return us, nbytes / (us * 1e-6) / 1e9
+
+
 def cpu_baseline(w: workloads.Workload, target_s: float = 12.0):
     """Oracle (float64 C, OpenMP) on a channel sample of the workload."""
     import oracle
@@ -291,6 +320,9 @@ def main():
             wl, _, _ = time_fwd(mssm, torch, ww, 20, 3)
             out.setdefault("extra", {})[f"{name}_fwd_GBs"] = round(fwd_bytes(ww) / wl / 1e9, 1)
             out["extra"][f"{name}_fwd_us"] = round(wl * 1e6, 1)
+        st_us, st_gbs = time_step(mssm, torch, w)
+        out.setdefault("extra", {})["step_us_per_call"] = round(st_us, 2)
+        out["extra"]["step_GBs_per_call"] = round(st_gbs, 1)
         tw = workloads.WORKLOADS["train"]
         tb = time_bwd(mssm, torch, tw, 10, 2)
         out.setdefault("extra", {})["train_bwd_us"] = round(tb * 1e6, 1)
