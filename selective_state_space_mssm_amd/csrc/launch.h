@@ -63,6 +63,8 @@ hipError_t launch_fwd_prepass(const ScanArgs& a, void* fwd_scratch, float* ckpt,
 struct BwdPlan {
     int64_t tile;        // time steps per recompute tile
     int64_t tiles;       // ceil(L / tile)
+    int64_t chunks;      // K >= 1: the reverse walk cut into K time chunks (carry of the adjoint between them)
+    int64_t chunk_tiles; // tiles per chunk (the last may have fewer)
     size_t ws_bytes;
 };
 BwdPlan plan_bwd(int64_t B, int64_t L, int64_t D, int64_t N);

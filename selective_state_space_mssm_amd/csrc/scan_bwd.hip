@@ -70,13 +70,18 @@ struct BwdKArgs {
     float* ddt_bias;
     float* dh0;
     float* pBC;    // (B, L, dblocks, 2, N): per channel block, dB partial then dC partial
-    float* pA;     // (B, D, N)
-    float* pD;     // (B, D)
-    float* pbias;  // (B, D)
+    float* pA;     // (B, K, D, N): per time chunk
+    float* pD;     // (B, K, D)
+    float* pbias;  // (B, K, D)
+    float* qlam;   // (B, K - 1, D, N): chunks 1 .. K-1, a_{t0} lam_{t0} from a zero adjoint at the chunk's end
+    float* slam;   // (B, K - 1, D): chunks 1 .. K-1, sum of Delta over the chunk
+    float* pin;    // (B, K, D, N): a_{t1} lam_{t1} entering each chunk at its end (t1 = its end step)
     int64_t B, L, D, N;
     int64_t tiles;
     int32_t dblocks;
     int32_t softplus;
+    int32_t chunks;       // K
+    int32_t chunk_tiles;  // tiles per chunk
 };
 
 // ---- cross-lane sums -------------------------------------------------------------
@@ -370,7 +375,8 @@ struct RevRegs {
 // Uniform facts of one workgroup (and the lane's channel).
 template <typename T>
 struct RevBlock {
-    int w, lane, lo, n0, D32, L32, dblk, dblocks, ntiles, softplus_on;
+    int w, lane, lo, n0, D32, L32, dblk, dblocks, softplus_on;
+    int tile_begin, tile_end;  // this workgroup's time chunk: tiles [tile_begin, tile_end)
     int hw;  // helper waves: index among the helpers
     bool dvalid;
     float bias, Dk;
@@ -405,7 +411,7 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
     const int cur = k & 1, prv = cur ^ 1;
     const int w = bk.w, lane = bk.lane;
     if constexpr (HELPER) {
-        if (k + 1 < bk.ntiles) {
+        if (k + 1 < bk.tile_end) {
             const int64_t off = static_cast<int64_t>(k + 1) * kTB * bk.D32;
             finish_rows<T, SPW, G>(sLQ[prv], r.keep_p, bk.hw, lane, bk.dvalid, min(kTB, bk.L32 - (k + 1) * kTB),
                                    bk.Dk, bk.du_b + off, bk.dd_b + off, bk.D32, r.accD, r.accBias);
@@ -455,7 +461,7 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
     }
 }
 
-// The reverse walk over all tiles.  Both roles execute the same barriers.
+// The reverse walk over the chunk's tiles.  Both roles execute the same barriers.
 template <bool HELPER, typename T, int NG, int G>
 __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)[NG], const float (&Aval)[NG],
                                         RevRegs<T, NG, G>& r, float4 (&sX)[2][kTB][64],
@@ -465,7 +471,7 @@ __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)
     const int lane = bk.lane, n0 = bk.n0;
     // ---- prologue: last tile prepared; its Bm/Cm/checkpoint and the next raw rows in flight
     {
-        const int tl = bk.ntiles - 1;
+        const int tl = bk.tile_end - 1;
         const int64_t rowl = bk.row_b + static_cast<int64_t>(tl) * kTB;
         if constexpr (HELPER) {
             fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl, bk.L32, bk.D32, bk.hw * SPW, bk.lo, r.ru, r.rd, r.rs);
@@ -482,7 +488,7 @@ __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)
     }
     __syncthreads();
 
-    for (int k = bk.ntiles - 1; k >= 0; --k) {
+    for (int k = bk.tile_end - 1; k >= bk.tile_begin; --k) {
         const int nval = min(kTB, bk.L32 - k * kTB);
         if (nval == kTB)
             rev_interval<true, HELPER>(bk, k, kTB, A2, Aval, r, sX, sLQ);
@@ -490,13 +496,18 @@ __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)
             rev_interval<false, HELPER>(bk, k, nval, A2, Aval, r, sX, sLQ);
         __syncthreads();
     }
-    // ---- epilogue: finish tile 0
-    if constexpr (HELPER)
-        finish_rows<T, SPW, G>(sLQ[0], r.keep_p, bk.hw, lane, bk.dvalid, min(kTB, bk.L32), bk.Dk, bk.du_b,
-                               bk.dd_b, bk.D32, r.accD, r.accBias);
+    // ---- epilogue: finish the chunk's first tile
+    if constexpr (HELPER) {
+        const int kb = bk.tile_begin;
+        const int64_t off = static_cast<int64_t>(kb) * kTB * bk.D32;
+        finish_rows<T, SPW, G>(sLQ[kb & 1], r.keep_p, bk.hw, lane, bk.dvalid, min(kTB, bk.L32 - kb * kTB), bk.Dk,
+                               bk.du_b + off, bk.dd_b + off, bk.D32, r.accD, r.accBias);
+    }
 }
 
-// Reverse kernel.  Grid: B * dblocks workgroups of G state waves + the helper waves.
+// Reverse kernel.  Grid: (B * dblocks, K) workgroups of G state waves + the
+// helper waves; workgroup (blk, c) walks time chunk c of channel block blk,
+// starting from the adjoint that enters the chunk at its end.
 template <typename T, int NG, int G>
 __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel(BwdKArgs a) {
     constexpr int N = NG * G;
@@ -526,7 +537,9 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
     const bool state_wave = bk.w < G;
     bk.n0 = state_wave ? bk.w * NG : 0;
     bk.hw = state_wave ? 0 : bk.w - G;
-    bk.ntiles = static_cast<int>(a.tiles);
+    const int64_t chunk = blockIdx.y;
+    bk.tile_begin = static_cast<int>(chunk) * a.chunk_tiles;
+    bk.tile_end = min(bk.tile_begin + a.chunk_tiles, static_cast<int>(a.tiles));
     bk.softplus_on = a.softplus;
     bk.bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
     bk.Dk = a.Dskip ? a.Dskip[dc] : 0.0f;
@@ -550,7 +563,10 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
     for (int k = 0; k < NG; ++k) {
         Aval[k] = state_wave ? a.A[dc * N + n0 + k] : 0.0f;
         A2[k] = Aval[k] * kLog2e;
-        r.pc[k] = (state_wave && a.dh_final && bk.dvalid) ? a.dh_final[(b * D + dc) * N + n0 + k] : 0.0f;
+        if (a.chunks > 1)
+            r.pc[k] = (state_wave && bk.dvalid) ? a.pin[((b * a.chunks + chunk) * D + dc) * N + n0 + k] : 0.0f;
+        else
+            r.pc[k] = (state_wave && a.dh_final && bk.dvalid) ? a.dh_final[(b * D + dc) * N + n0 + k] : 0.0f;
         r.dA[k] = 0.0f;
     }
     r.accD = r.accBias = 0.0f;
@@ -563,10 +579,10 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
         rev_run<true>(bk, A2, Aval, r, sX, sLQ);
     // ---- per-(b, d) results
     if (state_wave && bk.dvalid) {
-        float* pa = a.pA + (b * D + dc) * N + n0;
+        float* pa = a.pA + ((b * a.chunks + chunk) * D + dc) * N + n0;
 #pragma unroll
         for (int k = 0; k < NG; ++k) pa[k] = r.dA[k];
-        if (a.dh0) {
+        if (a.dh0 && chunk == 0) {
             float* g0 = a.dh0 + (b * D + dc) * N + n0;
 #pragma unroll
             for (int k = 0; k < NG; ++k) g0[k] = r.pc[k];  // a_0 lam_0
@@ -584,46 +600,209 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
             sd += sRed[0][g][lane];
             sb += sRed[1][g][lane];
         }
-        a.pD[b * D + dc] = sd;
-        a.pbias[b * D + dc] = sb;
+        a.pD[(b * a.chunks + chunk) * D + dc] = sd;
+        a.pbias[(b * a.chunks + chunk) * D + dc] = sb;
+    }
+}
+
+// ---- reverse chunk carry -----------------------------------------------------------
+// The adjoint is linear in what enters a time chunk at its end.  With
+// p = a_{t1} lam_{t1} entering chunk c = steps [t0, t1) and p_out =
+// a_{t0} lam_{t0} leaving it, p_out = Q_c + R_c p, where R_c = prod_{t in c}
+// a_t = exp(A sum_{t in c} Delta_t) (the forward's chunk decay) and Q_c is
+// p_out for p = 0.  bwd_chunk_lambda_kernel computes Q_c and the chunk's sum
+// of Delta for every chunk but the first; bwd_lambda_carry_kernel chains
+// them from the last chunk (p = dh_final) back to the first; then every
+// chunk's reverse walk runs from its own entering p, all chunks at once.
+
+// Reverse step J of the zero-started adjoint: lam = p + sbar Cm, p = a lam.
+template <int NG, bool FULL, int J>
+__device__ __forceinline__ void lam_step(int nval, const float (&A2)[NG], const float (&Ct)[NG],
+                                         const float2 (&xs)[kTB], float (&p)[NG]) {
+    if (FULL || J < nval) {
+        const float2 x = xs[J];  // (Delta, sbar)
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            const float lam = __builtin_fmaf(row_bcast<J>(Ct[k]), x.y, p[k]);
+            p[k] = lam * fast_exp2(x.x * A2[k]);
+        }
+    }
+}
+template <int NG, bool FULL, int... I>
+__device__ __forceinline__ void lam_steps(std::integer_sequence<int, I...>, int nval, const float (&A2)[NG],
+                                          const float (&Ct)[NG], const float2 (&xs)[kTB], float (&p)[NG]) {
+    (lam_step<NG, FULL, kTB - 1 - I>(nval, A2, Ct, xs, p), ...);  // J = 15 .. 0
+}
+
+// Grid: (B * dblocks, K - 1), G waves; workgroup (blk, c - 1) walks chunk c
+// backwards.  Per tile each wave prepares (Delta, sbar) of its rows of the
+// tile before into the other LDS buffer while every wave runs the adjoint of
+// its states over this tile: one barrier per tile.
+template <typename T, int NG, int G>
+__global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
+    constexpr int N = NG * G;
+    constexpr int SPW = kTB / G;
+    constexpr int W = LaneRow<T, NG>::kWords;
+    static_assert(kTB % G == 0, "tile must split evenly over the waves");
+    __shared__ float2 sDS[2][kTB][64];  // (Delta, sbar) per row and channel
+    __shared__ float sSum[G][64];
+
+    const int lane = threadIdx.x & 63;
+    const int w = wave_id();
+    const int64_t b = blockIdx.x / a.dblocks;
+    const int64_t chan0 = static_cast<int64_t>(blockIdx.x % a.dblocks) * 64;
+    const int64_t c = static_cast<int64_t>(blockIdx.y) + 1;
+    const int64_t D = a.D, L = a.L;
+    const int L32 = static_cast<int>(L);
+    const bool dvalid = chan0 + lane < D;
+    const int lo = dvalid ? lane : static_cast<int>(D - 1 - chan0);
+    const int64_t dc = chan0 + lo;
+    const int n0 = w * NG;
+
+    float A2[NG], p[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+        A2[k] = a.A[dc * N + n0 + k] * kLog2e;
+        p[k] = 0.0f;
+    }
+    const float bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
+    float psum = 0.0f;  // sum of Delta over this wave's rows
+
+    const int tb = static_cast<int>(c) * a.chunk_tiles;
+    const int te = min(tb + a.chunk_tiles, static_cast<int>(a.tiles));
+    const int64_t row_b = b * L;
+    const int64_t last_row = row_b + L - 1;
+    const T* d_b = static_cast<const T*>(a.delta) + row_b * D + chan0;
+    const float* s_b = a.sbar + row_b * D + chan0;
+    const T* Cm = static_cast<const T*>(a.Cm);
+    float rd[SPW], rs[SPW];
+    uint32_t qc[W], qn[W];
+
+    // raw delta and sbar of this wave's rows of `tile` (clamped to the last row), and the tile's Cm
+    auto fetch = [&](int tile, uint32_t (&q)[W]) {
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int t = min(tile * kTB + w * SPW + i, L32 - 1);
+            const int64_t off = static_cast<int64_t>(t) * D + lo;
+            rd[i] = load_act(d_b, off);
+            rs[i] = s_b[off];
+        }
+        fetch_tile_rows<T, NG>(Cm, row_b + static_cast<int64_t>(tile) * kTB, last_row, N, n0, lane, q);
+    };
+    // (Delta, sbar) of this wave's rows of `tile` into buffer `buf`
+    auto prep = [&](int tile, int buf) {
+        const int nval = min(kTB, L32 - tile * kTB);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int j = w * SPW + i;
+            if (j < nval) {
+                const float x = rd[i] + bias;
+                const float dt = a.softplus ? softplus(x) : x;
+                sDS[buf][j][lane] = make_float2(dt, rs[i]);
+                psum += dt;
+            }
+        }
+    };
+
+    fetch(te - 1, qc);
+    prep(te - 1, (te - 1) & 1);
+    if (te - 2 >= tb) fetch(te - 2, qn);
+    __syncthreads();
+    for (int tile = te - 1; tile >= tb; --tile) {
+        const int cur = tile & 1;
+        float Ct[NG];
+        unpack_lane_row<T, NG>(qc, Ct);
+        if (tile - 1 >= tb) {
+            prep(tile - 1, cur ^ 1);
+#pragma unroll
+            for (int i = 0; i < W; ++i) qc[i] = qn[i];
+            if (tile - 2 >= tb) fetch(tile - 2, qn);
+        }
+        const int nval = min(kTB, L32 - tile * kTB);
+        float2 xs[kTB];
+#pragma unroll
+        for (int j = 0; j < kTB; ++j) xs[j] = sDS[cur][j][lane];
+        if (nval == kTB)
+            lam_steps<NG, true>(std::make_integer_sequence<int, kTB>{}, kTB, A2, Ct, xs, p);
+        else
+            lam_steps<NG, false>(std::make_integer_sequence<int, kTB>{}, nval, A2, Ct, xs, p);
+        __syncthreads();
+    }
+    sSum[w][lane] = psum;
+    __syncthreads();
+    if (dvalid) {
+        const int64_t q = (b * (a.chunks - 1) + (c - 1)) * D + dc;
+        float* qo = a.qlam + q * N + n0;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) qo[k] = p[k];
+        if (w == 0) {
+            float ssum = 0.0f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) ssum += sSum[g][lane];
+            a.slam[q] = ssum;
+        }
+    }
+}
+
+// pin of every chunk, from the last (dh_final, or 0) back to the first:
+// p_in(c - 1) = Q_c + exp(A sum Delta_c) p_in(c).  One thread per (b, d, n).
+__global__ __launch_bounds__(256) void bwd_lambda_carry_kernel(BwdKArgs a) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= a.B * a.D * a.N) return;
+    const int64_t n = i % a.N, bd = i / a.N;
+    const int64_t d = bd % a.D, b = bd / a.D;
+    const int64_t K = a.chunks;
+    const float A = a.A[d * a.N + n];
+    float p = a.dh_final ? a.dh_final[i] : 0.0f;
+    a.pin[((b * K + (K - 1)) * a.D + d) * a.N + n] = p;
+    for (int64_t c = K - 1; c >= 1; --c) {
+        const int64_t q = (b * (K - 1) + (c - 1)) * a.D + d;
+        p = __builtin_fmaf(expf(A * a.slam[q]), p, a.qlam[q * a.N + n]);
+        a.pin[((b * K + (c - 1)) * a.D + d) * a.N + n] = p;
     }
 }
 
 // ---- fixed-order reductions ----------------------------------------------------------
 // Items [0, B*L*N): dB, dC of (b, t, n), summed over the channel blocks;
-// items [B*L*N, B*L*N + D*N): dA of (d, n) summed over the batch (and dD,
-// ddt_bias of d with n == 0).  Grid-stride.
+// items [B*L*N, + D*N): dA of (d, n), summed over the (batch row, time
+// chunk) partials in order; items [B*L*N + D*N, + D): dD and ddt_bias of d,
+// likewise.  Grid-stride.  The loops over partials are unrolled so their
+// loads are issued together; the additions stay in order.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdKArgs a) {
     const int64_t nBC = a.B * a.L * a.N;
-    const int64_t total = nBC + a.D * a.N;
+    const int64_t nA = a.D * a.N;
+    const int64_t total = nBC + nA + a.D;
+    const int64_t parts = a.B * a.chunks;  // (b, c) in order
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
          i += static_cast<int64_t>(gridDim.x) * 256) {
         if (i < nBC) {
             const int64_t n = i % a.N, bt = i / a.N;
             const float* p = a.pBC + bt * a.dblocks * 2 * a.N + n;
             float sb = 0.0f, sc = 0.0f;
+#pragma unroll 8
             for (int32_t k = 0; k < a.dblocks; ++k) {
                 sb += p[(2 * k) * a.N];
                 sc += p[(2 * k + 1) * a.N];
             }
             store_act(static_cast<T*>(a.dB), i, sb);
             store_act(static_cast<T*>(a.dC), i, sc);
-        } else {
+        } else if (i < nBC + nA) {
             const int64_t j = i - nBC;
             float s = 0.0f;
-            for (int64_t b = 0; b < a.B; ++b) s += a.pA[b * a.D * a.N + j];
+#pragma unroll 8
+            for (int64_t q = 0; q < parts; ++q) s += a.pA[q * nA + j];
             a.dA[j] = s;
-            if (j % a.N == 0) {
-                const int64_t d = j / a.N;
-                float sd = 0.0f, sb = 0.0f;
-                for (int64_t b = 0; b < a.B; ++b) {
-                    sd += a.pD[b * a.D + d];
-                    sb += a.pbias[b * a.D + d];
-                }
-                if (a.dD) a.dD[d] = sd;
-                if (a.ddt_bias) a.ddt_bias[d] = sb;
+        } else {
+            const int64_t d = i - nBC - nA;
+            float sd = 0.0f, sb = 0.0f;
+#pragma unroll 8
+            for (int64_t q = 0; q < parts; ++q) {
+                sd += a.pD[q * a.D + d];
+                sb += a.pbias[q * a.D + d];
             }
+            if (a.dD) a.dD[d] = sd;
+            if (a.ddt_bias) a.ddt_bias[d] = sb;
         }
     }
 }
@@ -633,9 +812,9 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // Workspace: the forward schedule's own scratch, then the pre-pass outputs,
 // then the partial sums.
 struct WsLayout {
-    size_t fwd, ckpt, sbar, pBC, pA, pD, pbias, total;
+    size_t fwd, ckpt, sbar, pBC, pA, pD, pbias, qlam, slam, pin, total;
 };
-WsLayout ws_layout(int64_t B, int64_t L, int64_t D, int64_t N, int64_t tiles) {
+WsLayout ws_layout(int64_t B, int64_t L, int64_t D, int64_t N, int64_t tiles, int64_t K) {
     const int64_t dblocks = (D + 63) / 64;
     WsLayout w{};
     size_t off = 0;
@@ -643,9 +822,12 @@ WsLayout ws_layout(int64_t B, int64_t L, int64_t D, int64_t N, int64_t tiles) {
     w.ckpt = off;  off += align256(static_cast<size_t>(B) * tiles * D * N * 4);
     w.sbar = off;  off += align256(static_cast<size_t>(B) * L * D * 4);
     w.pBC = off;   off += align256(static_cast<size_t>(B) * L * dblocks * 2 * N * 4);
-    w.pA = off;    off += align256(static_cast<size_t>(B) * D * N * 4);
-    w.pD = off;    off += align256(static_cast<size_t>(B) * D * 4);
-    w.pbias = off; off += align256(static_cast<size_t>(B) * D * 4);
+    w.pA = off;    off += align256(static_cast<size_t>(B) * K * D * N * 4);
+    w.pD = off;    off += align256(static_cast<size_t>(B) * K * D * 4);
+    w.pbias = off; off += align256(static_cast<size_t>(B) * K * D * 4);
+    w.qlam = off;  off += align256(static_cast<size_t>(B) * (K - 1) * D * N * 4);
+    w.slam = off;  off += align256(static_cast<size_t>(B) * (K - 1) * D * 4);
+    w.pin = off;   off += align256(K > 1 ? static_cast<size_t>(B) * K * D * N * 4 : 0);
     w.total = off;
     return w;
 }
@@ -653,7 +835,7 @@ WsLayout ws_layout(int64_t B, int64_t L, int64_t D, int64_t N, int64_t tiles) {
 template <typename T, int NG, int G>
 hipError_t launch_bwd_t(const ScanArgs& s, hipStream_t st) {
     const BwdPlan pl = plan_bwd(s.B, s.L, s.D, s.N);
-    const WsLayout wl = ws_layout(s.B, s.L, s.D, s.N, pl.tiles);
+    const WsLayout wl = ws_layout(s.B, s.L, s.D, s.N, pl.tiles, pl.chunks);
     char* ws = static_cast<char*>(s.workspace);
     float* ckpt = reinterpret_cast<float*>(ws + wl.ckpt);
     float* sbar = reinterpret_cast<float*>(ws + wl.sbar);
@@ -669,13 +851,29 @@ hipError_t launch_bwd_t(const ScanArgs& s, hipStream_t st) {
     a.pA = reinterpret_cast<float*>(ws + wl.pA);
     a.pD = reinterpret_cast<float*>(ws + wl.pD);
     a.pbias = reinterpret_cast<float*>(ws + wl.pbias);
+    a.qlam = reinterpret_cast<float*>(ws + wl.qlam);
+    a.slam = reinterpret_cast<float*>(ws + wl.slam);
+    a.pin = reinterpret_cast<float*>(ws + wl.pin);
     a.B = s.B; a.L = s.L; a.D = s.D; a.N = s.N;
     a.tiles = pl.tiles;
     a.dblocks = static_cast<int32_t>((s.D + 63) / 64);
     a.softplus = s.softplus;
-    hipLaunchKernelGGL((bwd_reverse_kernel<T, NG, G>), dim3(static_cast<unsigned>(s.B * a.dblocks)),
+    a.chunks = static_cast<int32_t>(pl.chunks);
+    a.chunk_tiles = static_cast<int32_t>(pl.chunk_tiles);
+    const unsigned nblk = static_cast<unsigned>(s.B * a.dblocks);
+    if (pl.chunks > 1) {
+        // its own layout: four states per wave where N allows (no LDS partial sums to keep small)
+        constexpr int NGc = NG * G >= 16 ? (NG > 4 ? NG : 4) : NG;
+        constexpr int Gc = NG * G / NGc;
+        hipLaunchKernelGGL((bwd_chunk_lambda_kernel<T, NGc, Gc>), dim3(nblk, static_cast<unsigned>(pl.chunks - 1)),
+                           dim3(64 * Gc), 0, st, a);
+        const int64_t threads = s.B * s.D * s.N;
+        hipLaunchKernelGGL(bwd_lambda_carry_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
+                           st, a);
+    }
+    hipLaunchKernelGGL((bwd_reverse_kernel<T, NG, G>), dim3(nblk, static_cast<unsigned>(pl.chunks)),
                        dim3(64 * (G + helper_waves(G))), 0, st, a);
-    const int64_t items = s.B * s.L * s.N + s.D * s.N;
+    const int64_t items = s.B * s.L * s.N + s.D * s.N + s.D;
     const int64_t blocks = std::min<int64_t>((items + 255) / 256, 16384);
     hipLaunchKernelGGL((bwd_reduce_kernel<T>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
     return hipGetLastError();
@@ -697,11 +895,23 @@ hipError_t dispatch_n(const ScanArgs& s, hipStream_t st) {
 
 }  // namespace
 
+// Time chunks of the reverse walk: when the channel blocks fill at most half
+// of a 256-CU MI355X, enough chunks for about three workgroups per CU, each
+// at least 4 tiles long.  (The chunk carry's extra pass costs about a quarter
+// of the reverse walk over the chunks it covers; with more blocks it costs
+// what it gains: 192 blocks, 4 chunks: reverse 408 -> 306 us, carry 115 us.)
+// Depends only on the problem (the workspace size query has no device).
 BwdPlan plan_bwd(int64_t B, int64_t L, int64_t D, int64_t N) {
     BwdPlan p{};
     p.tile = kTB;
     p.tiles = (L + kTB - 1) / kTB;
-    p.ws_bytes = ws_layout(B, L, D, N, p.tiles).total;
+    const int64_t nblk = B * ((D + 63) / 64);
+    int64_t K = 1;
+    if (nblk <= 128) K = std::min<int64_t>((768 + nblk - 1) / nblk, p.tiles / 4);
+    K = std::max<int64_t>(K, 1);
+    p.chunk_tiles = (p.tiles + K - 1) / K;
+    p.chunks = (p.tiles + p.chunk_tiles - 1) / p.chunk_tiles;  // no empty chunk
+    p.ws_bytes = ws_layout(B, L, D, N, p.tiles, p.chunks).total;
     return p;
 }
 

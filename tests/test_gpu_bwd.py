@@ -4,9 +4,10 @@ element with the relative criterion of helpers.grad_err.
 
 Covers the training workload (B=8, L=2048, D=1536, N=16, fp32) in full, ragged
 small shapes with every optional input (h0, dh_final, z, Dskip, dt_bias), the
-ungated path, every supported state size, bfloat16 activations, the forward
-pre-pass under its chunked and its balanced schedules, and bitwise
-reproducibility (the reductions have a fixed order, no atomics)."""
+ungated path, every supported state size, bfloat16 activations, the reverse
+walk cut into time chunks joined by the adjoint carry, the forward pre-pass
+under its chunked and its balanced schedules, and bitwise reproducibility
+(the reductions have a fixed order, no atomics)."""
 import numpy as np
 import pytest
 
@@ -90,6 +91,45 @@ def test_bf16_ragged(mssm, L):
 def test_state_sizes_bf16(mssm, N):
     g, r = run_both(mssm, workloads.custom(2, 43, 70, N, "bf16", seed=N + 70))
     assert_grads(g, r, GRAD_TOL["bf16"])
+
+
+@pytest.mark.parametrize("shape,dtype", [((1, 300, 70), "f32"), ((1, 300, 70), "bf16"), ((2, 1000, 40), "f32")])
+def test_chunked_reverse(mssm, shape, dtype):
+    # few channel blocks: the reverse walk is cut into time chunks (L = 300:
+    # 4 chunks of 5, 5, 5, 4 tiles, the last tile ragged; L = 1000: 13 chunks)
+    # joined by the adjoint carry; dh_final enters the last chunk, dh0 leaves the first
+    B, L, D = shape
+    g, r = run_both(mssm, workloads.custom(B, L, D, 16, dtype, seed=L + D + 7))
+    assert_grads(g, r, GRAD_TOL[dtype])
+
+
+def test_chunked_reverse_plain(mssm):
+    # no dh_final (the last chunk starts from zero), no gate, no h0, softplus off
+    w = workloads.custom(1, 300, 70, 16, "f32", seed=17)
+    g, r = run_both(mssm, w, h0=False, dhf=False, gate=False)
+    assert_grads(g, r, GRAD_TOL["f32"])
+    inp = workloads.make_inputs(w, with_dy=True)
+    inp["delta"] = (0.05 * np.abs(inp["delta"])).astype(np.float32)
+    inp["dt_bias"] = np.full(w.D, 0.01, np.float32)
+    t = gpu_inputs(inp)
+    g = mssm.scan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["dy"], t["Dskip"], t["z"], t["dt_bias"],
+                      None, None, delta_softplus=False)
+    f = workloads.as_float32(inp)
+    r = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["Bm"], f["Cm"], f["dy"], Dskip=f["Dskip"], z=f["z"],
+                        dt_bias=f["dt_bias"], softplus=False)
+    assert_grads(g, r, GRAD_TOL["f32"])
+
+
+def test_chunked_reverse_many_chunks(mssm):
+    # 24 channel blocks: 32 chunks of 8 tiles
+    g, r = run_both(mssm, workloads.custom(1, 4096, 1536, 16, "f32", seed=77))
+    assert_grads(g, r, GRAD_TOL["f32"])
+
+
+@pytest.mark.parametrize("N", [1, 4, 64])
+def test_chunked_reverse_state_sizes(mssm, N):
+    g, r = run_both(mssm, workloads.custom(1, 200, 50, N, "f32", seed=N + 300))
+    assert_grads(g, r, GRAD_TOL["f32"])
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
