@@ -58,13 +58,15 @@ constexpr int kTB = 16;  // time steps per tile (= lanes per DPP row)
 // Helper waves of a workgroup: besides the G state waves, which run only the
 // recurrence of their states, the workgroup has helper waves that run the
 // per-element front end (loads of u/delta/z, softplus, gate) and the
-// finishing of rows (sum of the partial readouts, store): one per state wave
-// up to four state waves (one of each per SIMD), else G/2.  The backward
-// pre-pass, whose per-element work is heavier (dy, sbar, the dz factor), has
-// one per state wave also with eight state waves of up to two states (more
-// states per wave would leave too few registers at 16 waves and spill).
+// finishing of rows (sum of the partial readouts, store).  Forward: one per
+// state wave up to four state waves (one of each per SIMD), else G/2.  The
+// backward pre-pass, whose per-element work is heavier (dy, sbar, the dz
+// factor), has two per state wave with four waves of 4 states (N = 16) and
+// one per state wave with eight waves of up to two states (more states per
+// wave at 16 waves would leave too few registers and spill).
 constexpr int helper_waves(int NG, int G, bool pre) {
-    return (G <= 4 || (pre && NG <= 2)) ? G : G / 2;
+    if (pre) return (G <= 4 && NG >= 4) ? 2 * G : ((G <= 4 || NG <= 2) ? G : G / 2);
+    return G <= 4 ? G : G / 2;
 }
 
 struct FwdKArgs {
@@ -1008,9 +1010,7 @@ hipError_t dispatch_n(const ScanArgs& s, const FwdPlan& pl, void* scratch, const
         case 2: return launch_fwd_t<T, 1, 2, PRE>(s, pl, scratch, pre, st);
         case 4: return launch_fwd_t<T, 1, 4, PRE>(s, pl, scratch, pre, st);
         case 8: return launch_fwd_t<T, 2, 4, PRE>(s, pl, scratch, pre, st);
-        case 16:  // the state size of every pretrained Mamba model
-            if constexpr (PRE) return launch_fwd_t<T, 2, 8, PRE>(s, pl, scratch, pre, st);
-            else return launch_fwd_t<T, 4, 4, PRE>(s, pl, scratch, pre, st);
+        case 16: return launch_fwd_t<T, 4, 4, PRE>(s, pl, scratch, pre, st);  // every pretrained Mamba model
         case 32: return launch_fwd_t<T, 4, 8, PRE>(s, pl, scratch, pre, st);
         case 64: return launch_fwd_t<T, 8, 8, PRE>(s, pl, scratch, pre, st);
         default: return hipErrorInvalidValue;
