@@ -4,8 +4,10 @@
 // section: RNN form for inference): read the carried state h (B, D, N), apply
 // one iteration of the selective-scan recurrence, write h back in place and
 // emit y_t.  The cost is the state read + write (8 B per state element) plus
-// the launch, so one thread per (b, d) streams its N contiguous states with
-// 16-byte accesses; consecutive threads touch consecutive 4*N-byte rows.
+// the launch.  A (b, d) row of N states is handled by N/4 lanes (one lane for
+// N < 4), each owning 4 consecutive states as one 16-byte access, so a wave
+// reads and writes one contiguous stretch of the state; the row's lanes add
+// their partial readouts with lane shuffles and the first one stores y.
 #include "device_common.h"
 #include "launch.h"
 
@@ -29,50 +31,57 @@ struct StepKArgs {
 
 template <typename T, int N>
 __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // (b, d)
+    constexpr int V = N >= 4 ? 4 : N;  // states per lane
+    constexpr int R = N / V;           // lanes per (b, d) row: a power of two dividing 64
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t i = g / R;  // (b, d); the R lanes of a row are all in range or all out
+    const int q = static_cast<int>(g % R);
     if (i >= a.B * a.D) return;
     const int64_t b = i / a.D, d = i % a.D;
-    const T* __restrict__ Bm = static_cast<const T*>(a.Bm) + b * N;
-    const T* __restrict__ Cm = static_cast<const T*>(a.Cm) + b * N;
+    const int n0 = q * V;
+    const T* __restrict__ Bm = static_cast<const T*>(a.Bm) + b * N + n0;
+    const T* __restrict__ Cm = static_cast<const T*>(a.Cm) + b * N + n0;
     const float uu = load_act(static_cast<const T*>(a.u), i);
     const float x = load_act(static_cast<const T*>(a.delta), i) + (a.dt_bias ? a.dt_bias[d] : 0.0f);
     const float dt = a.softplus ? softplus(x) : x;
     const float du = dt * uu;
     const float dtl = dt * kLog2e;
-    float* __restrict__ st = a.state + i * N;
-    const float* __restrict__ Ad = a.A + d * N;
+    float* __restrict__ st = a.state + i * N + n0;
+    const float* __restrict__ Ad = a.A + d * N + n0;
     float s = 0.0f;
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int n = 0; n < N; n += 4) {
-            float4 h = *reinterpret_cast<const float4*>(st + n);
-            const float4 av = *reinterpret_cast<const float4*>(Ad + n);
-            h.x = __builtin_fmaf(fast_exp2(dtl * av.x), h.x, du * load_act(Bm, n + 0));
-            h.y = __builtin_fmaf(fast_exp2(dtl * av.y), h.y, du * load_act(Bm, n + 1));
-            h.z = __builtin_fmaf(fast_exp2(dtl * av.z), h.z, du * load_act(Bm, n + 2));
-            h.w = __builtin_fmaf(fast_exp2(dtl * av.w), h.w, du * load_act(Bm, n + 3));
-            s = __builtin_fmaf(load_act(Cm, n + 0), h.x, s);
-            s = __builtin_fmaf(load_act(Cm, n + 1), h.y, s);
-            s = __builtin_fmaf(load_act(Cm, n + 2), h.z, s);
-            s = __builtin_fmaf(load_act(Cm, n + 3), h.w, s);
-            *reinterpret_cast<float4*>(st + n) = h;
-        }
+    if constexpr (V == 4) {
+        float4 h = *reinterpret_cast<const float4*>(st);
+        const float4 av = *reinterpret_cast<const float4*>(Ad);
+        h.x = __builtin_fmaf(fast_exp2(dtl * av.x), h.x, du * load_act(Bm, 0));
+        h.y = __builtin_fmaf(fast_exp2(dtl * av.y), h.y, du * load_act(Bm, 1));
+        h.z = __builtin_fmaf(fast_exp2(dtl * av.z), h.z, du * load_act(Bm, 2));
+        h.w = __builtin_fmaf(fast_exp2(dtl * av.w), h.w, du * load_act(Bm, 3));
+        s = load_act(Cm, 0) * h.x;
+        s = __builtin_fmaf(load_act(Cm, 1), h.y, s);
+        s = __builtin_fmaf(load_act(Cm, 2), h.z, s);
+        s = __builtin_fmaf(load_act(Cm, 3), h.w, s);
+        *reinterpret_cast<float4*>(st) = h;
     } else {
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
+        for (int n = 0; n < V; ++n) {
             const float h = __builtin_fmaf(fast_exp2(dtl * Ad[n]), st[n], du * load_act(Bm, n));
             s = __builtin_fmaf(load_act(Cm, n), h, s);
             st[n] = h;
         }
     }
-    s = __builtin_fmaf(a.Dskip ? a.Dskip[d] : 0.0f, uu, s);
-    if (a.z) s *= silu(load_act(static_cast<const T*>(a.z), i));
-    store_act(static_cast<T*>(a.y), i, s);
+#pragma unroll
+    for (int m = 1; m < R; m <<= 1) s += __shfl_xor(s, m);
+    if (q == 0) {
+        s = __builtin_fmaf(a.Dskip ? a.Dskip[d] : 0.0f, uu, s);
+        if (a.z) s *= silu(load_act(static_cast<const T*>(a.z), i));
+        store_act(static_cast<T*>(a.y), i, s);
+    }
 }
 
 template <typename T>
 hipError_t dispatch(const StepKArgs& k, int64_t N, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>((k.B * k.D + 255) / 256));
+    const int64_t lanes = k.B * k.D * (N >= 4 ? N / 4 : 1);  // N/4 lanes per (b, d) row
+    const dim3 grid(static_cast<unsigned>((lanes + 255) / 256));
     switch (N) {
         case 1: hipLaunchKernelGGL((scan_step_kernel<T, 1>), grid, dim3(256), 0, st, k); break;
         case 2: hipLaunchKernelGGL((scan_step_kernel<T, 2>), grid, dim3(256), 0, st, k); break;
