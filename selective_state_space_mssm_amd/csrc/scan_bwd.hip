@@ -281,15 +281,47 @@ __device__ __forceinline__ void rec_steps(std::integer_sequence<int, J...>, int 
     (rec_step<NG, FULL, J>(nval, h, g, ahist, hist), ...);
 }
 
-// State that the reverse steps of one tile read and update.
+// Four or more states per wave keep fewer registers per tile (the 168 of a
+// 12-wave workgroup would not hold 2 * 16 * NG of states and decays beside
+// the tile's (Delta, Delta*u, sbar)): the rows are read from LDS at each use,
+// the recompute computes each step's decay and input in place and keeps only
+// the states, and the reverse step recomputes the decay (one exp more per
+// state-step).
+template <int NG>
+constexpr bool kLowReg = NG >= 4;
+
+template <int NG, bool FULL, int XS, int J>
+__device__ __forceinline__ void rec_step_fused(int nval, const float (&A2)[NG], float (&h)[NG],
+                                               const float (&Bt)[NG], const float4* xt, float (&hist)[kTB][NG]) {
+    if (FULL || J < nval) {
+        const float4 x = xt[J * XS];
+#pragma unroll
+        for (int k = 0; k < NG; ++k)
+            hist[J][k] = h[k] = __builtin_fmaf(fast_exp2(x.x * A2[k]), h[k], row_bcast<J>(Bt[k]) * x.y);
+    } else {
+#pragma unroll
+        for (int k = 0; k < NG; ++k) hist[J][k] = 0.0f;
+    }
+}
+template <int NG, bool FULL, int XS, int... J>
+__device__ __forceinline__ void rec_steps_fused(std::integer_sequence<int, J...>, int nval, const float (&A2)[NG],
+                                                float (&h)[NG], const float (&Bt)[NG], const float4* xt,
+                                                float (&hist)[kTB][NG]) {
+    (rec_step_fused<NG, FULL, XS, J>(nval, A2, h, Bt, xt, hist), ...);
+}
+
+// State that the reverse steps of one tile read and update.  xt[J * XS] is
+// step J's (Delta, Delta*u, sbar): registers (XS = 1) or the LDS rows (XS = 64).
 template <int NG, int G>
 struct RevCtx {
+    static constexpr int XS = kLowReg<NG> ? 64 : 1;
     const float* Aval;       // [NG]
+    const float* A2;         // [NG] A * log2(e)
     const float* Bt;         // [NG]
     const float* Ct;         // [NG]
-    const float4* xt;        // [kTB]
+    const float4* xt;        // [kTB * XS]
     const float (*hist)[NG];
-    const float (*ahist)[NG];
+    const float (*ahist)[NG];  // unused with kLowReg (the decay is recomputed)
     const float* hin;        // [NG] state before the tile
     float2 (*sLQ)[kTB][64];  // [G]
     __amdgpu_buffer_rsrc_t rp;  // this block's dB/dC partial rows of the tile
@@ -309,7 +341,7 @@ __device__ __forceinline__ void rev_step(const RevCtx<NG, G>& c, float (&pc)[NG]
     constexpr int S = 16 / (2 * NG);  // steps per batch
     constexpr int slot = (J % S) * 2 * NG;
     if (FULL || J < c.nval) {
-        const float4 x = c.xt[J];  // (Delta, Delta*u, sbar, -)
+        const float4 x = c.xt[J * RevCtx<NG, G>::XS];  // (Delta, Delta*u, sbar, -)
         float lam[NG];
 #pragma unroll
         for (int k = 0; k < NG; ++k) lam[k] = pc[k];
@@ -328,7 +360,10 @@ __device__ __forceinline__ void rev_step(const RevCtx<NG, G>& c, float (&pc)[NG]
             float hp;
             if constexpr (J > 0) hp = c.hist[J - 1][k];
             else hp = c.hin[k];
-            pc[k] = lam[k] * c.ahist[J][k];
+            if constexpr (kLowReg<NG>)
+                pc[k] = lam[k] * fast_exp2(x.x * c.A2[k]);
+            else
+                pc[k] = lam[k] * c.ahist[J][k];
             const float q = pc[k] * hp;
             lq = __builtin_fmaf(c.Aval[k], q, lq);
             dA[k] = __builtin_fmaf(x.x, q, dA[k]);
@@ -427,9 +462,13 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
         }
     } else {
         // ---- tile k's (Delta, Delta*u, sbar); its states recomputed from the checkpoint
-        float4 xt[kTB];
+        constexpr bool LOWREG = kLowReg<NG>;
+        float4 xt[LOWREG ? 1 : kTB];
+        if constexpr (!LOWREG) {
 #pragma unroll
-        for (int j = 0; j < kTB; ++j) xt[j] = sX[cur][j][lane];
+            for (int j = 0; j < kTB; ++j) xt[j] = sX[cur][j][lane];
+        }
+        const float4* xp = LOWREG ? &sX[cur][0][lane] : xt;
         float Bt[NG], Ct[NG], hin[NG];
         unpack_lane_row<T, NG>(r.qb, Bt);
         unpack_lane_row<T, NG>(r.qc, Ct);
@@ -443,17 +482,20 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
 #pragma unroll
             for (int q = 0; q < NG; ++q) r.hin_next[q] = bk.ck_b[tp * bk.ck_stride + q * bk.D32];
         }
-        float hist[kTB][NG], ahist[kTB][NG];
+        float hist[kTB][NG], ahist[LOWREG ? 1 : kTB][NG];
         {
             float h[NG];
 #pragma unroll
             for (int q = 0; q < NG; ++q) h[q] = hin[q];
-            rec_steps<NG, FULL>(std::make_integer_sequence<int, kTB>{}, nval, A2, h, Bt, xt, hist, ahist);
+            if constexpr (LOWREG)
+                rec_steps_fused<NG, FULL, 64>(std::make_integer_sequence<int, kTB>{}, nval, A2, h, Bt, xp, hist);
+            else
+                rec_steps<NG, FULL>(std::make_integer_sequence<int, kTB>{}, nval, A2, h, Bt, xt, hist, ahist);
         }
         // ---- the reverse steps of tile k; partials to the other buffer than
         // those of tile k + 1 that the helpers are reading
         const int64_t row0 = bk.row_b + static_cast<int64_t>(k) * kTB;
-        RevCtx<NG, G> c{Aval, Bt, Ct, xt, hist, ahist, hin, sLQ[cur],
+        RevCtx<NG, G> c{Aval, A2, Bt, Ct, xp, hist, ahist, hin, sLQ[cur],
                         make_rsrc(bk.pBC + (row0 * bk.dblocks + bk.dblk) * 2 * N,
                                   static_cast<uint32_t>(kTB) * bk.dblocks * 2u * N * 4u),
                         nval, w, lane, bk.dblocks, N, bk.n0};
