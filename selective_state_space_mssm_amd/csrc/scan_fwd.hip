@@ -1028,11 +1028,13 @@ FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N) {
         p.ws_bytes = align256(static_cast<size_t>(blocks) * sizeof(uint32_t)) +
                      align256(static_cast<size_t>(blocks) * 64 * N * sizeof(float));
     }
-    // Cut time only when the channel blocks alone cannot occupy the chip.
+    // Cut time only when the channel blocks alone cannot occupy the chip:
+    // at most 1024 (block, chunk) workgroups, a whole number of rounds on 256
+    // CUs with one or two workgroups per CU (1032 would add a round of 8).
     constexpr int64_t kTargetBlocks = 1024;
     constexpr int64_t kMinChunk = 1024;
     if (blocks >= 128 || L < 2 * kMinChunk) return p;
-    int64_t K = std::min<int64_t>((kTargetBlocks + blocks - 1) / blocks, L / kMinChunk);
+    int64_t K = std::min<int64_t>(kTargetBlocks / blocks, L / kMinChunk);
     K = std::max<int64_t>(K, 1);
     int64_t len = (L + K - 1) / K;
     len = (len + kTB - 1) / kTB * kTB;
