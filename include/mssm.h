@@ -88,8 +88,12 @@ typedef struct {
  * Returns 0 for an invalid problem. */
 size_t mssm_scan_fwd_workspace_bytes(const mssm_problem* p);
 
-/* Bytes of device scratch the backward needs (chunk-boundary states and the
- * per-tile partial sums of dA, dD, ddt_bias, dB, dC).  0 for an invalid problem. */
+/* Bytes of device scratch the backward needs: the forward's own scratch, the
+ * state before every 16-step tile, sbar = dy * silu(z) in float32, the partial
+ * sums of dB, dC (per 64-channel block) and of dA, dD, ddt_bias (per batch row
+ * and time chunk), and, when the reverse walk is cut into time chunks (few
+ * channel blocks, long sequences), each chunk's adjoint carry.  0 for an
+ * invalid problem. */
 size_t mssm_scan_bwd_workspace_bytes(const mssm_problem* p);
 
 /*
