@@ -22,8 +22,9 @@ float32 arithmetic), inputs resident in HBM.  Prints one JSON line:
 ``--extra`` adds the 130M-layer forward, the recurrent step at the 2.8B layer's
 width (B=4, D=5120, N=16: one decode step per call from Python, so the host's
 launch overhead, not the kernel, sets this rate; the kernel's own duration is
-in the kernel trace) and the training-workload backward (``--long`` also the
-1M-step forward).
+in the kernel trace), the same step at B = 64 and 256 (batched decode, where the
+state's read and write set the rate) and the training-workload backward
+(``--long`` also the 1M-step forward).
 ``--copy-probe`` runs a plain device copy of 1 GiB first (counter calibration).
 """
 from __future__ import annotations
@@ -181,10 +182,13 @@ def time_bwd(mssm, torch, w, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def time_step(mssm, torch, w, reps=200):
+def time_step(mssm, torch, w, reps=200, batch=None):
     """One recurrent step (decode) at the workload's width: (B, D) inputs, the
-    (B, D, N) float32 state updated in place.  Returns (us per call, GB/s of
-    algorithmic bytes: state read + write, inputs, y, A, Dskip, dt_bias)."""
+    (B, D, N) float32 state updated in place; `batch` overrides B (batched
+    decode).  Returns (us per call, GB/s of algorithmic bytes: state read +
+    write, inputs, y, A, Dskip, dt_bias)."""
+    if batch is not None:
+        w = workloads.custom(batch, 1, w.D, w.N, w.dtype, seed=w.seed)
     inp = workloads.make_inputs(workloads.custom(w.B, 1, w.D, w.N, w.dtype, seed=w.seed))
     t = workloads.to_torch(inp, "cuda")
     args = [t["u"][:, 0].contiguous(), t["delta"][:, 0].contiguous(), t["A"], t["Bm"][:, 0].contiguous(),
@@ -323,6 +327,10 @@ def main():
         st_us, st_gbs = time_step(mssm, torch, w)
         out.setdefault("extra", {})["step_us_per_call"] = round(st_us, 2)
         out["extra"]["step_GBs_per_call"] = round(st_gbs, 1)
+        for bb in (64, 256):  # batched decode: the state read and write dominate
+            st_us, st_gbs = time_step(mssm, torch, w, reps=100, batch=bb)
+            out["extra"][f"step_B{bb}_us_per_call"] = round(st_us, 2)
+            out["extra"][f"step_B{bb}_GBs"] = round(st_gbs, 1)
         tw = workloads.WORKLOADS["train"]
         tb = time_bwd(mssm, torch, tw, 10, 2)
         out.setdefault("extra", {})["train_bwd_us"] = round(tb * 1e6, 1)

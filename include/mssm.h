@@ -102,7 +102,11 @@ size_t mssm_scan_bwd_workspace_bytes(const mssm_problem* p);
  *   dt_bias -> 0             h0      -> zero initial state
  *   h_final -> not written
  * Writes y (B, L, D) and, if given, h_final = h_{L-1} (B, D, N).
- * y may not alias any input.
+ * y may not alias any input.  h_final may be the same buffer as h0: the state
+ * is then advanced in place by L steps, a multi-token form of mssm_step (each
+ * lane reads a channel's initial state before that channel's final state is
+ * written, in every schedule the library uses).  No other partial overlap of
+ * h0 and h_final is allowed.
  */
 mssm_status mssm_scan_fwd(const mssm_problem* p,
                           const void* u, const void* delta, const float* A,

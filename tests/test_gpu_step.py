@@ -72,3 +72,35 @@ def test_batched_decode_shape(mssm):
     yr, hr = run_oracle_fwd(oracle, inp, h0)
     assert fwd_err(to_np(y), yr[:, 0]) <= FWD_TOL["bf16"]
     assert fwd_err(to_np(state), hr) <= 1e-5   # state stays float32
+
+
+@pytest.mark.parametrize("B,D,segments,dtype", [
+    (2, 100, [1, 3, 16, 17, 40], "f32"),          # one workgroup per channel block
+    (5, 4096, [1, 16, 31], "bf16"),               # 320 blocks: the balanced persistent schedule
+    (1, 128, [2100, 5, 2048], "f32"),             # few blocks, long segments: time chunks + carry
+])
+def test_multi_token_steps_in_place(mssm, B, D, segments, dtype):
+    """The forward scan with h0 and h_final the same buffer advances the state
+    in place: a chain of calls over consecutive segments equals one scan over
+    the whole sequence (the oracle's)."""
+    L = sum(segments)
+    w = workloads.custom(B, L, D, 16, dtype, seed=60 + len(segments))
+    print(f"[multi-token] {w} segments {segments}", flush=True)
+    inp = workloads.make_inputs(w)
+    t = gpu_inputs(inp)
+    h0 = np.random.default_rng(3).standard_normal((B, D, 16)).astype(np.float32)
+    state = torch.from_numpy(h0).cuda()
+    ys, t0 = [], 0
+    for n in segments:
+        sl = slice(t0, t0 + n)
+        y, hf = mssm.scan_fwd(t["u"][:, sl].contiguous(), t["delta"][:, sl].contiguous(), t["A"],
+                              t["Bm"][:, sl].contiguous(), t["Cm"][:, sl].contiguous(), t["Dskip"],
+                              t["z"][:, sl].contiguous(), t["dt_bias"], state, h_final=state)
+        assert hf is state
+        ys.append(y)
+        t0 += n
+    torch.cuda.synchronize()
+    yr, hr = run_oracle_fwd(oracle, inp, h0)
+    tol = FWD_TOL[dtype]
+    assert fwd_err(to_np(torch.cat(ys, 1)), yr) <= tol
+    assert fwd_err(to_np(state), hr) <= tol
