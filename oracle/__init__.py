@@ -16,8 +16,17 @@ discretisation, skip term, gate and step-size transform of the selective SSM
 (Mamba paper Section 3 / Algorithm 2, named on the page "Mamba SSM 架构");
 ``oracle.c`` states the formulas.
 
+The Mamba block's causal conv1d + SiLU, which produces the scan's u (the
+fused front end of ``mssm_conv_scan_fwd``), is ``causal_conv_silu`` below,
+written out in numpy: a depthwise convolution of kernel size d_conv over
+time, causal (output t sees inputs t - d_conv + 1 .. t), with bias, as
+torch.nn.Conv1d(groups=D, padding=d_conv - 1) truncated to the first L
+outputs -- the layer the mamba-minimal page runs in place of the CUDA conv,
+with d_conv = 4 in the configurations of the page "Mamba SSM 架构".
+
 Pinning (what checks this oracle against something other than itself) is in
-``tests/test_oracle_fwd_pins.py`` and ``tests/test_oracle_bwd_pins.py``.
+``tests/test_oracle_fwd_pins.py``, ``tests/test_oracle_bwd_pins.py`` and
+``tests/test_oracle_conv_pins.py``.
 """
 from __future__ import annotations
 
@@ -106,6 +115,37 @@ def scan_fwd(u, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
                             _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
                             _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(hf))
     return y, hf
+
+
+def causal_conv_silu(x, weight, bias=None, x_prev=None, silu=True):
+    """u[b,t,d] = silu(bias[d] + sum_k weight[d,k] * x[b, t - K + 1 + k, d]) in
+    float64, K = d_conv.  x: (B, L, D); weight: (D, K) (or (D, 1, K), the
+    torch.nn.Conv1d layout); bias: (D); x_prev: (B, K - 1, D), the inputs at
+    t = -(K - 1) .. -1, zeros when None (the left padding).  silu=False returns
+    the convolution alone."""
+    x, weight, bias, x_prev = map(_f64, (x, weight, bias, x_prev))
+    Bsz, L, D = x.shape
+    weight = weight.reshape(D, -1)
+    K = weight.shape[1]
+    if x_prev is None:
+        x_prev = np.zeros((Bsz, K - 1, D))
+    assert x_prev.shape == (Bsz, K - 1, D)
+    xx = np.concatenate([x_prev, x], axis=1)          # time -(K-1) .. L-1
+    c = np.zeros((Bsz, L, D)) if bias is None else np.broadcast_to(bias, (Bsz, L, D)).copy()
+    for k in range(K):                                 # tap k sees input t - (K - 1) + k
+        c += weight[:, k] * xx[:, k:k + L, :]
+    if not silu:
+        return c
+    return c / (1.0 + np.exp(-c))
+
+
+def conv_scan_fwd(x, weight, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
+                  bias=None, x_prev=None, softplus=True):
+    """The scan behind the conv front end: ``(y, h_final, u)`` in float64 with
+    u = causal_conv_silu(x, weight, bias, x_prev) fed to ``scan_fwd``."""
+    u = causal_conv_silu(x, weight, bias, x_prev)
+    y, hf = scan_fwd(u, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, softplus=softplus)
+    return y, hf, u
 
 
 def step(u_t, delta_t, A, Bm_t, Cm_t, state, Dskip=None, z_t=None, dt_bias=None,
