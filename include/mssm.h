@@ -60,6 +60,8 @@ extern "C" {
 #endif
 
 #define MSSM_MAX_DSTATE 64
+/* Widest causal conv1d the fused front end (mssm_conv_scan_fwd) takes. */
+#define MSSM_MAX_DCONV 4
 
 typedef enum { MSSM_F32 = 0, MSSM_BF16 = 1 } mssm_dtype;
 
@@ -115,6 +117,40 @@ mssm_status mssm_scan_fwd(const mssm_problem* p,
                           const float* h0,
                           void* y, float* h_final,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Forward scan behind the Mamba block's causal conv1d + SiLU, fused: the scan
+ * input is formed inside the kernels as
+ *
+ *   u[b,t,d] = silu(conv_b[d] + sum_{k<d_conv} conv_w[d,k] * x[b, t-d_conv+1+k, d])
+ *
+ * (a depthwise causal convolution of kernel size d_conv; the configurations on
+ * the page "Mamba SSM 架构" use d_conv = 4, and the mamba-minimal page "PyTorch
+ * 한 파일에서의 Mamba 구현" runs it as torch.nn.Conv1d, whose weight layout
+ * (D, 1, d_conv) this matches) and never stored unless u_out is given.  Then
+ * exactly mssm_scan_fwd with that u.
+ *   x       (B, L, D) in p->dtype, the conv input (replaces u)
+ *   conv_w  (D, d_conv) float32, row-major; 1 <= d_conv <= MSSM_MAX_DCONV
+ *   conv_b  (D) float32, NULL -> 0
+ *   x_prev  (B, d_conv - 1, D) in p->dtype, the d_conv - 1 inputs just before
+ *           t = 0 in time order (streaming: the last d_conv - 1 rows of the
+ *           previous call's x); NULL -> zeros (the convolution's left padding)
+ *   u_out   (B, L, D) in p->dtype, NULL -> not written; else receives u (what
+ *           mssm_scan_bwd needs as its u)
+ * The other arguments, the workspace (mssm_scan_fwd_workspace_bytes) and the
+ * errors are those of mssm_scan_fwd; d_conv out of range -> MSSM_ERR_SHAPE,
+ * conv_w NULL -> MSSM_ERR_NULL.  y and u_out may not alias any input; h_final
+ * may be h0 (the state advanced in place).
+ */
+mssm_status mssm_conv_scan_fwd(const mssm_problem* p, int32_t d_conv,
+                               const void* x, const float* conv_w, const float* conv_b,
+                               const void* x_prev,
+                               const void* delta, const float* A,
+                               const void* Bm, const void* Cm,
+                               const float* Dskip, const void* z, const float* dt_bias,
+                               const float* h0,
+                               void* y, float* h_final, void* u_out,
+                               void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * Backward scan: gradients of  sum(dy * y) + sum(dh_final * h_final)  with

@@ -22,7 +22,8 @@ STATUS = {0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_SHAPE", -3: "MSSM_ERR
           -4: "MSSM_ERR_UNSUPPORTED", -5: "MSSM_ERR_ALIGN", -6: "MSSM_ERR_WORKSPACE",
           -7: "MSSM_ERR_HIP"}
 EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd",
-           "mssm_scan_bwd", "mssm_step", "mssm_status_string", "mssm_build_info"]
+           "mssm_conv_scan_fwd", "mssm_scan_bwd", "mssm_step", "mssm_status_string", "mssm_build_info"]
+MAX_DCONV = 4
 
 
 class Problem(ctypes.Structure):
@@ -49,6 +50,8 @@ def _open(path: str):
     lib.mssm_scan_bwd_workspace_bytes.restype = sz
     lib.mssm_scan_fwd.argtypes = [P] + [vp] * 11 + [vp, sz, vp]
     lib.mssm_scan_fwd.restype = st
+    lib.mssm_conv_scan_fwd.argtypes = [P, ctypes.c_int32] + [vp] * 15 + [vp, sz, vp]
+    lib.mssm_conv_scan_fwd.restype = st
     lib.mssm_scan_bwd.argtypes = [P] + [vp] * 20 + [vp, sz, vp]
     lib.mssm_scan_bwd.restype = st
     lib.mssm_step.argtypes = [P] + [vp] * 10 + [vp]
@@ -155,6 +158,63 @@ def scan_fwd(u, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
                              _ptr(Dskip), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),
                              _ptr(ws), nbytes, _stream(u.device)))
     return y, h_final
+
+
+def conv_scan_fwd(x, conv_w, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None, conv_b=None,
+                  x_prev=None, delta_softplus=True, return_final_state=True, return_u=False, y=None,
+                  h_final=None, u_out=None, workspace=None):
+    """Selective scan forward behind the fused causal conv1d + SiLU front end:
+    the scan's u = silu(conv_b + depthwise causal conv of x with conv_w) is
+    formed inside the kernels.  x, delta, z: (B, L, D); conv_w (D, d_conv) or
+    (D, 1, d_conv) float32 (the torch.nn.Conv1d layout), conv_b (D) float32;
+    x_prev (B, d_conv - 1, D): the inputs before t = 0 (zeros when None).
+    Returns (y, h_final, u): h_final None unless requested, u (B, L, D) only
+    with return_u (or u_out)."""
+    act = x.dtype
+    B, L, D = x.shape
+    N = A.shape[1]
+    if conv_w is None or conv_w.dim() not in (2, 3) or conv_w.shape[0] != D:
+        raise ValueError("conv_w must be (D, d_conv) or (D, 1, d_conv)")
+    K = conv_w.shape[-1]
+    if conv_w.dim() == 3:
+        if conv_w.shape[1] != 1:
+            raise ValueError("conv_w must be depthwise: (D, 1, d_conv)")
+        _req(conv_w, "conv_w", (D, 1, K), torch.float32)
+        conv_w = conv_w.view(D, K)
+    if not 1 <= K <= MAX_DCONV:
+        raise ValueError(f"d_conv = {K} not in 1..{MAX_DCONV}")
+    _req(x, "x", (B, L, D), act)
+    _req(conv_w, "conv_w", (D, K), torch.float32)
+    _opt(conv_b, "conv_b", (D,), torch.float32)
+    if K > 1:
+        _opt(x_prev, "x_prev", (B, K - 1, D), act)
+    else:
+        x_prev = None
+    _req(delta, "delta", (B, L, D), act)
+    _req(A, "A", (D, N), torch.float32)
+    _req(Bm, "Bm", (B, L, N), act)
+    _req(Cm, "Cm", (B, L, N), act)
+    _opt(Dskip, "Dskip", (D,), torch.float32)
+    _opt(z, "z", (B, L, D), act)
+    _opt(dt_bias, "dt_bias", (D,), torch.float32)
+    _opt(h0, "h0", (B, D, N), torch.float32)
+    if y is None:
+        y = torch.empty((B, L, D), dtype=act, device=x.device)
+    _req(y, "y", (B, L, D), act)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((B, D, N), dtype=torch.float32, device=x.device)
+    _opt(h_final, "h_final", (B, D, N), torch.float32)
+    if return_u and u_out is None:
+        u_out = torch.empty((B, L, D), dtype=act, device=x.device)
+    _opt(u_out, "u_out", (B, L, D), act)
+    prob = problem(B, L, D, N, _dtype_code(x), delta_softplus)
+    nbytes = int(lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(prob)))
+    ws = _workspace(nbytes, x.device, workspace)
+    _check(lib.mssm_conv_scan_fwd(ctypes.byref(prob), K, _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(x_prev),
+                                  _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+                                  _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(u_out),
+                                  _ptr(ws), nbytes, _stream(x.device)))
+    return y, h_final, u_out
 
 
 def scan_bwd(u, delta, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, h0=None, dh_final=None,

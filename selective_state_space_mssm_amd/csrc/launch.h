@@ -27,6 +27,12 @@ struct ScanArgs {
     // forward outputs
     void* y;
     float* h_final;        // nullable
+    // fused causal conv1d + SiLU front end (forward only; u is then its input x)
+    const float* conv_w;   // (D, d_conv); null: no front end, u is the scan input
+    const float* conv_b;   // nullable
+    const void* x_prev;    // (B, d_conv - 1, D), nullable
+    void* u_out;           // (B, L, D), nullable
+    int d_conv;
     // backward inputs / outputs
     const void* dy;
     const float* dh_final; // nullable
@@ -55,6 +61,11 @@ struct FwdPlan {
 };
 FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N);
 hipError_t launch_fwd(const ScanArgs& a, hipStream_t s);
+// The forward behind the fused front end: a.u is x, a.conv_w (a.conv_b,
+// a.x_prev) its causal conv; u = silu(conv(x) + bias) is formed inside the
+// kernels (and written to a.u_out if set).  Same schedule and workspace as
+// launch_fwd.
+hipError_t launch_conv_fwd(const ScanArgs& a, hipStream_t s);
 // Backward pre-pass: the forward recurrence with, instead of y, the state
 // before every 16-step tile (ckpt, (B, tiles, N, D)), sbar = dy * silu(z)
 // ((B, L, D) float32) and dz; fwd_scratch is plan_fwd(...).ws_bytes of scratch.

@@ -85,6 +85,31 @@ mssm_status mssm_scan_fwd(const mssm_problem* p, const void* u, const void* delt
     return from_hip(mssm::launch_fwd(a, static_cast<hipStream_t>(hip_stream)));
 }
 
+mssm_status mssm_conv_scan_fwd(const mssm_problem* p, int32_t d_conv, const void* x, const float* conv_w,
+                               const float* conv_b, const void* x_prev, const void* delta, const float* A,
+                               const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                               const float* dt_bias, const float* h0, void* y, float* h_final, void* u_out,
+                               void* workspace, size_t workspace_bytes, void* hip_stream) {
+    mssm_status st = check_problem(p, true);
+    if (st != MSSM_OK) return st;
+    if (d_conv < 1 || d_conv > MSSM_MAX_DCONV) return MSSM_ERR_SHAPE;
+    if (!x || !conv_w || !delta || !A || !Bm || !Cm || !y) return MSSM_ERR_NULL;
+    st = check_align({x, conv_w, conv_b, x_prev, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, y, h_final, u_out,
+                      workspace});
+    if (st != MSSM_OK) return st;
+    const size_t need = mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return MSSM_ERR_WORKSPACE;
+
+    mssm::ScanArgs a = base_args(p);
+    a.u = x; a.delta = delta; a.z = z; a.Bm = Bm; a.Cm = Cm;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0;
+    a.y = y; a.h_final = h_final;
+    a.conv_w = conv_w; a.conv_b = conv_b; a.x_prev = d_conv > 1 ? x_prev : nullptr; a.u_out = u_out;
+    a.d_conv = d_conv;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return from_hip(mssm::launch_conv_fwd(a, static_cast<hipStream_t>(hip_stream)));
+}
+
 mssm_status mssm_scan_bwd(const mssm_problem* p, const void* u, const void* delta, const float* A,
                           const void* Bm, const void* Cm, const float* Dskip, const void* z,
                           const float* dt_bias, const float* h0, const void* dy,

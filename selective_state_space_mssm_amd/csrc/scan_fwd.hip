@@ -1,1026 +1,9 @@
-// scan_fwd.hip -- forward selective scan for gfx950 (MI355X).
-//
-// Operation: for each (b, d), h_t[n] = exp(Delta_t A[d,n]) h_{t-1}[n] +
-// Delta_t Bm[b,t,n] u[b,t,d] and y[b,t,d] = (sum_n Cm[b,t,n] h_t[n] +
-// Dskip[d] u[b,t,d]) silu(z[b,t,d]), Delta_t = softplus(delta + dt_bias) --
-// the sequential loop of the mamba-minimal page ("PyTorch 한 파일에서의 Mamba
-// 구현", Hacker News comments) with the selective-SSM discretisation (Mamba
-// paper Section 3 / Algorithm 2, named on the page "Mamba SSM 架构").
-//
-// Mapping (one workgroup = one batch row b x 64 channels x one time chunk):
-//  * lane = channel d: u, delta, z, y are read/written one row (b, t, 64 d)
-//    at a time, consecutive lanes on consecutive addresses;
-//  * state wave w of the G state waves = state group n in [w*NG, (w+1)*NG);
-//    the NG states of each channel live in VGPRs and are never written to
-//    memory (the (B,L,D,N) expansion does not exist).  N = 16: 4 state waves
-//    of 4 states;
-//  * Bm[b,t,n], Cm[b,t,n] are the same for all 64 channels: a tile of them
-//    sits in VGPRs with lane l holding step l % 16 (replicated over the four
-//    16-lane rows), and step j reads it through a DPP row_newbcast:j source
-//    modifier on the v_mul / v_fmac that consumes it -- a broadcast with no
-//    extra instruction, no LDS traffic and no scalar-load waits;
-//  * per time tile of 16 steps: helper waves (one per state wave for N = 16)
-//    turn the tile's rows of (u, delta, z) into (Delta, Delta*u) in LDS, the
-//    skip term and the gate (softplus and silu once per element, shared by
-//    all state waves); every state wave runs the recurrence of its states
-//    over the tile and leaves its partial readout per step in LDS; the
-//    helpers then finish the rows: sum of the G partials + Dskip*u, times
-//    silu(z), store;
-//  * the partial readouts of a group of 2 or 4 steps are issued together, one
-//    DPP multiply-add statement per state, so that a pair of wait states
-//    (the DPP read-after-write rule) covers the whole group;
-//  * software pipeline, one barrier per tile: front end two tiles ahead,
-//    finishing one tile behind, the next tile's (Delta, Delta*u) read from
-//    LDS while the current one runs; global loads through buffer resources;
-//  * when the channel blocks outnumber the CUs but do not divide evenly over
-//    them, a persistent balanced schedule gives every CU an equal share of
-//    (block, tile) work, handing the state of a split block over through
-//    memory;
-//  * long sequences: the time axis is cut into K chunks.  A first kernel
-//    computes per chunk the end state from zero and the step-size sum
-//    (the chunk aggregate of the associative operator
-//    (a1, g1) o (a2, g2) = (a1 a2, a2 g1 + g2)); a small kernel chains the
-//    aggregates over chunks (the parallel-scan combination the page
-//    "mamba.py: 一个简单高效的Mamba实现" credits for parallelising the time
-//    dimension); the main kernel then scans every chunk from its true
-//    initial state.
-#include "device_common.h"
-#include "launch.h"
-
-#include <algorithm>
-#include <utility>
+// scan_fwd.hip -- the forward selective scan and the backward pre-pass: the
+// schedule (plan_fwd) and the launchers over the kernels of scan_fwd_kernels.h,
+// whose header describes the mapping onto gfx950.
+#include "scan_fwd_kernels.h"
 
 namespace mssm {
-namespace {
-
-constexpr int kTB = 16;  // time steps per tile (= lanes per DPP row)
-
-// Helper waves of a workgroup: besides the G state waves, which run only the
-// recurrence of their states, the workgroup has helper waves that run the
-// per-element front end (loads of u/delta/z, softplus, gate) and the
-// finishing of rows (sum of the partial readouts, store).  Forward: one per
-// state wave up to four state waves (one of each per SIMD), else G/2.  The
-// backward pre-pass, whose per-element work is heavier (dy, sbar, the dz
-// factor), has two per state wave with four waves of 4 states (N = 16) and
-// one per state wave with eight waves of up to two states (more states per
-// wave at 16 waves would leave too few registers and spill).
-constexpr int helper_waves(int NG, int G, bool pre) {
-    if (pre) return (G <= 4 && NG >= 4) ? 2 * G : ((G <= 4 || NG <= 2) ? G : G / 2);
-    return G <= 4 ? G : G / 2;
-}
-
-struct FwdKArgs {
-    const void* u;
-    const void* delta;
-    const void* z;
-    const void* Bm;
-    const void* Cm;
-    const float* A;
-    const float* Dskip;
-    const float* dt_bias;
-    const float* h0;       // used by chunk 0 when h_in is null
-    const float* h_in;     // (B, K, D, N) initial state of every chunk, or null
-    void* y;
-    float* h_final;
-    float* agg_h;          // (B, K, D, N) chunk end state from zero (chunk 0: from h0)
-    float* agg_s;          // (B, K, D) chunk sum of Delta
-    uint32_t* flags;       // (nblk) balanced schedule: 1 once a block's split state is published
-    float* carry;          // (nblk, 64, N) balanced schedule: the published states
-    int64_t L, D;
-    int64_t chunk_len;
-    int32_t dblocks;       // ceil(D / 64)
-    int32_t chunks;        // K
-    int32_t softplus;
-    int32_t workers;       // 0: one workgroup per (block, chunk); > 0: balanced persistent schedule
-    int32_t nblk;          // B * dblocks
-    // backward pre-pass only
-    const void* dy;
-    void* dz;              // nullable (no gate)
-    float* sbar;           // (B, L, D) dy * silu(z), or dy without a gate
-    float* ckpt;           // (B, tiles, N, D) state before every kTB-step tile
-    int64_t tiles;         // ceil(L / kTB)
-};
-
-// Raw inputs of this wave's rows of one tile (u, delta, z at (b, t, chan0 +
-// lane)), loaded with 32-bit offsets from a uniform row base.
-template <typename T, int SPW>
-__device__ __forceinline__ void fetch_rows_ptr(const T* __restrict__ u, const T* __restrict__ dl,
-                                           const T* __restrict__ z, int64_t base, int first_row, int rows_left,
-                                           int D32, int lo, float (&ru)[SPW], float (&rd)[SPW], float (&rz)[SPW]) {
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int j = first_row + i;
-        if (j < rows_left) {
-            const uint32_t off = static_cast<uint32_t>(j * D32 + lo);
-            ru[i] = load_act(u + base, off);
-            rd[i] = load_act(dl + base, off);
-            if (z) rz[i] = load_act(z + base, off);
-        }
-    }
-}
-
-// This wave's Bm (and Cm) values of one tile: lane l loads step l % 16 (row
-// clamped to the chunk's last row, so nothing outside the tensor is read).
-template <typename T, int NG>
-__device__ __forceinline__ void fetch_tile_rows(const T* __restrict__ M, int64_t row0, int64_t last_row, int N,
-                                                int n0, int lane, uint32_t (&q)[LaneRow<T, NG>::kWords]) {
-    const int64_t r = imin64(row0 + (lane & (kTB - 1)), last_row);
-    load_lane_row<T, NG>(M + r * N + n0, q);
-}
-
-// The recurrence of one tile: decays exp(Delta A) and inputs Bm Delta u do
-// not depend on the state, so they are computed ahead of the dependent state
-// chain -- for the whole tile (staging) or for each group of steps -- and
-// their instructions overlap it.  Decay and input of step J into slot j
-// (steps past the end: decay 1, input 0, which leaves the state as it is):
-template <int NG, bool FULL, int J, int j, int M>
-__device__ __forceinline__ void fwd_pre(int nval, const float (&A2)[NG], const float (&Bt)[NG],
-                                        const float2 (&ddt)[kTB], float (&ea)[M][NG], float (&eg)[M][NG]) {
-    if (FULL || J < nval) {
-        const float2 dd = ddt[J];
-#pragma unroll
-        for (int k = 0; k < NG; ++k) {
-            ea[j][k] = fast_exp2(dd.x * A2[k]);
-            eg[j][k] = row_bcast<J>(Bt[k]) * dd.y;
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < NG; ++k) {
-            ea[j][k] = 1.0f;
-            eg[j][k] = 0.0f;
-        }
-    }
-}
-
-// Steps per readout group: the states after each step of a group stay in
-// registers (NG * S of them) until the group's readouts.  Measured on the
-// 2.8B and 130M layer shapes: four steps for bf16 activations, two for fp32
-// ones (16 % and 10 % faster than the other choice); two with eight states
-// per wave, where four would spill.
-template <typename T, int NG>
-constexpr int group_steps() { return (sizeof(T) == 4 || NG >= 8) ? 2 : 4; }
-
-// State update of step J; the state after the step goes to hs[.][J % S] for
-// the readout of its group.
-template <int NG, int S, int J>
-__device__ __forceinline__ void fwd_update(float (&h)[NG], const float (&e)[NG], const float (&g)[NG],
-                                           float (&hs)[NG][S]) {
-#pragma unroll
-    for (int k = 0; k < NG; ++k) hs[k][J % S] = h[k] = __builtin_fmaf(e[k], h[k], g[k]);
-}
-// The same with the decays and inputs computed in place.
-template <int NG, int S, bool FULL, int J>
-__device__ __forceinline__ void fwd_update_fused(int nval, const float (&A2)[NG], float (&h)[NG],
-                                                 const float (&Bt)[NG], const float2 (&ddt)[kTB], float (&hs)[NG][S]) {
-    if (FULL || J < nval) {
-        const float2 dd = ddt[J];
-#pragma unroll
-        for (int k = 0; k < NG; ++k)
-            h[k] = __builtin_fmaf(fast_exp2(dd.x * A2[k]), h[k], row_bcast<J>(Bt[k]) * dd.y);
-    }
-#pragma unroll
-    for (int k = 0; k < NG; ++k) hs[k][J % S] = h[k];
-}
-// Partial readouts sum_k Cm[t, k] h_t[k] over this wave's states of the
-// steps J0 .. J0 + S - 1, to sP[w][J].  Per state one DPP statement covers
-// the group (one pair of wait states per S multiply-adds).
-template <int NG, int G, int S, bool FULL, int J0>
-__device__ __forceinline__ void fwd_readout(int nval, int w, int lane, const float (&Ct)[NG],
-                                            const float (&hs)[NG][S], float (&sP)[G][kTB][64]) {
-    static_assert(S == 2 || S == 4, "groups of two or four steps");
-    float y[S];
-    y[0] = row_bcast<J0>(Ct[0]) * hs[0][0];
-    y[1] = row_bcast<J0 + 1>(Ct[0]) * hs[0][1];
-    if constexpr (S == 4) {
-        y[2] = row_bcast<J0 + 2>(Ct[0]) * hs[0][2];
-        y[3] = row_bcast<J0 + 3>(Ct[0]) * hs[0][3];
-    }
-#pragma unroll
-    for (int k = 1; k < NG; ++k) {
-        if constexpr (S == 4) fmac_row_bcast_x4<J0>(y, Ct[k], hs[k]);
-        else fmac_row_bcast_x2<J0>(y, Ct[k], hs[k]);
-    }
-#pragma unroll
-    for (int j = 0; j < S; ++j)
-        if (FULL || J0 + j < nval) sP[w][J0 + j][lane] = y[j];
-}
-// Steps J0 .. J0 + S - 1: decays and inputs (unless staged for the tile),
-// state updates, readouts.  With up to four states per wave and groups of
-// two steps (fp32 activations) the group's decays and inputs come first;
-// otherwise each step's are computed in place (measured: 4 % faster on the
-// 130M layer shape in fp32, 4 % slower on the 2.8B layer shape in bf16).
-template <int NG, int G, int S, bool FULL, bool STAGE, int J0, int... J>
-__device__ __forceinline__ void fwd_group(std::integer_sequence<int, J...>, int nval, int w, int lane,
-                                          const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
-                                          const float (&Ct)[NG], const float2 (&ddt)[kTB],
-                                          const float (&ea)[STAGE ? kTB : 1][NG],
-                                          const float (&eg)[STAGE ? kTB : 1][NG], float (&sP)[G][kTB][64]) {
-    float hs[NG][S];
-    if constexpr (STAGE) {
-        (fwd_update<NG, S, J0 + J>(h, ea[J0 + J], eg[J0 + J], hs), ...);
-    } else if constexpr (NG <= 4 && S == 2) {
-        float e[S][NG], g[S][NG];
-        (fwd_pre<NG, FULL, J0 + J, J>(nval, A2, Bt, ddt, e, g), ...);
-        (fwd_update<NG, S, J0 + J>(h, e[J], g[J], hs), ...);
-    } else {
-        (fwd_update_fused<NG, S, FULL, J0 + J>(nval, A2, h, Bt, ddt, hs), ...);
-    }
-    fwd_readout<NG, G, S, FULL, J0>(nval, w, lane, Ct, hs, sP);
-}
-
-template <int NG, bool FULL, int... J>
-__device__ __forceinline__ void fwd_pre_all(std::integer_sequence<int, J...>, int nval, const float (&A2)[NG],
-                                            const float (&Bt)[NG], const float2 (&ddt)[kTB], float (&ea)[kTB][NG],
-                                            float (&eg)[kTB][NG]) {
-    (fwd_pre<NG, FULL, J, J>(nval, A2, Bt, ddt, ea, eg), ...);
-}
-
-// The tile's 16 steps in groups of S.  STAGE: decays and inputs of the
-// whole tile staged ahead of the state chain (costs 2 * 16 * NG registers).
-template <int NG, int G, int S, bool FULL, bool STAGE, int... Q>
-__device__ __forceinline__ void fwd_steps(std::integer_sequence<int, Q...>, int nval, int w, int lane,
-                                          const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
-                                          const float (&Ct)[NG], const float2 (&ddt)[kTB],
-                                          float (&sP)[G][kTB][64]) {
-    static_assert(sizeof...(Q) * S == kTB, "the groups cover the tile");
-    float ea[STAGE ? kTB : 1][NG], eg[STAGE ? kTB : 1][NG];
-    if constexpr (STAGE) fwd_pre_all<NG, FULL>(std::make_integer_sequence<int, kTB>{}, nval, A2, Bt, ddt, ea, eg);
-    (fwd_group<NG, G, S, FULL, STAGE, S * Q>(std::make_integer_sequence<int, S>{}, nval, w, lane, A2, h, Bt, Ct,
-                                              ddt, ea, eg, sP), ...);
-}
-
-template <int NG, bool FULL, int J>
-__device__ __forceinline__ void state_step(int nval, const float (&A2)[NG], float (&h)[NG],
-                                           const float (&Bt)[NG], const float2 (&ddt)[kTB]) {
-    if (FULL || J < nval) {
-        const float2 dd = ddt[J];
-#pragma unroll
-        for (int k = 0; k < NG; ++k)
-            h[k] = __builtin_fmaf(fast_exp2(dd.x * A2[k]), h[k], row_bcast<J>(Bt[k]) * dd.y);
-    }
-}
-
-template <int NG, bool FULL, int... J>
-__device__ __forceinline__ void state_steps(std::integer_sequence<int, J...>, int nval, int lane,
-                                            const float (&A2)[NG], float (&h)[NG], const float (&Bt)[NG],
-                                            const float2 (&sDD)[kTB][64]) {
-    float2 ddt[kTB];
-    ((ddt[J] = (FULL || J < nval) ? sDD[J][lane] : make_float2(0.0f, 0.0f)), ...);
-    (state_step<NG, FULL, J>(nval, A2, h, Bt, ddt), ...);
-}
-
-// ---- buffer loads ---------------------------------------------------------------
-// The activations and Bm/Cm of one tile are read through a buffer resource
-// rebased at the tile (uniform 64-bit address arithmetic on the scalar unit)
-// with a per-lane byte offset that is the same for every tile, so a load costs
-// no vector address arithmetic.  The resource's range ends at the segment's
-// last element: loads past it (rows after the end, channels past the last one
-// in the last row) return 0 -- finite values whose results are never stored.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, int64_t bytes) {
-    const int64_t b = bytes < 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : bytes);
-    return make_rsrc(base, static_cast<uint32_t>(b));
-}
-__device__ __forceinline__ float buffer_load_act(__amdgpu_buffer_rsrc_t r, uint32_t off, float) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
-}
-__device__ __forceinline__ float buffer_load_act(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t) {
-    return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0))
-                           << 16);
-}
-// NG consecutive values of one Bm/Cm row (LaneRow layout) through a buffer.
-template <typename T, int NG>
-__device__ __forceinline__ void buffer_load_lane_row(__amdgpu_buffer_rsrc_t r, uint32_t off,
-                                                     uint32_t (&q)[LaneRow<T, NG>::kWords]) {
-    constexpr int bytes = LaneRow<T, NG>::kBytes;
-    if constexpr (bytes >= 16) {
-#pragma unroll
-        for (int i = 0; i < bytes / 16; ++i) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off + 16 * i), 0, 0);
-            q[4 * i] = v[0]; q[4 * i + 1] = v[1]; q[4 * i + 2] = v[2]; q[4 * i + 3] = v[3];
-        }
-    } else if constexpr (bytes == 8) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0);
-        q[0] = v[0]; q[1] = v[1];
-    } else if constexpr (bytes == 4) {
-        q[0] = __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
-    } else {
-        q[0] = __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0);
-    }
-}
-
-// Per-element front end of one row: Delta = softplus(delta + dt_bias) (or
-// delta + dt_bias), Delta * u, the skip term Dskip * u and the gate silu(z).
-template <bool HAS_Z>
-__device__ __forceinline__ void prep_element(float uu, float dd, float zz, float bias, float Dk, int softplus_on,
-                                             float2& dDU, float& skip, float& gate) {
-    const float x = dd + bias;
-    const float sp = softplus(x);
-    const float dt = softplus_on ? sp : x;
-    dDU = make_float2(dt, dt * uu);
-    skip = Dk * uu;
-    gate = HAS_Z ? silu(zz) : 1.0f;
-}
-
-// Backward pre-pass front end of one row: the forward's (Delta, Delta*u) and
-// skip term, plus sbar = dy * silu(z) (dy without a gate) and the factor
-// dzf = dy * silu'(z) that turns the row's readout s into dz = s * dzf.
-template <bool HAS_Z>
-__device__ __forceinline__ void prep_element_pre(float uu, float dd, float zz, float gy, float bias, float Dk,
-                                                 int softplus_on, float2& dDU, float& skip, float& dzf,
-                                                 float& sb) {
-    const float x = dd + bias;
-    const float sp = softplus(x);
-    const float dt = softplus_on ? sp : x;
-    dDU = make_float2(dt, dt * uu);
-    skip = Dk * uu;
-    if constexpr (HAS_Z) {
-        const float sg = sigmoid(zz);
-        sb = gy * zz * sg;
-        dzf = gy * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
-    } else {
-        sb = gy;
-        dzf = 0.0f;
-    }
-}
-
-// Uniform facts of one segment (a block's steps [t_begin, t_end)) and the
-// lane's constant offsets.
-template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-struct FwdSeg {
-    static constexpr int SPW = kTB / helper_waves(NG, G, PRE);
-    int ntiles, t_len, w, lane;
-    int hw;  // helper waves: index among the helpers (rows hw * SPW ..)
-    bool dvalid;
-    int softplus_on;
-    float bias, Dk;
-    int64_t D;
-    int64_t seg_elems;  // elements from (b, t_begin, chan0) to the segment's last, (b, t_end - 1, D - 1)
-    int N, n0;
-    const T* u_seg;   // element (b, t_begin, chan0) of u; the same for delta, z, dy, y
-    const T* d_seg;
-    const T* z_seg;
-    const T* dy_seg;
-    T* y_seg;
-    const T* Bm_seg;  // row (b, t_begin) of Bm / Cm
-    const T* Cm_seg;
-    float* sbar_seg;  // pre-pass: element (b, t_begin, chan0) of sbar
-    float* ckpt_seg;  // pre-pass: element (b, t_begin / kTB, 0, chan0) of the (B, tiles, N, D) states
-    uint32_t row_off[SPW];  // byte offset of this wave's row i of a tile, this lane's channel
-    uint32_t bc_off;        // byte offset of this lane's Bm/Cm values in a tile (step lane % 16)
-};
-
-// Registers carried from one tile interval to the next.
-template <typename T, int NG, int G, bool PRE>
-struct FwdRegs {
-    static constexpr int SPW = kTB / helper_waves(NG, G, PRE);
-    float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];   // raw inputs of the tile prepared next (k + 2)
-    uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next recurrence tile
-    // skip term and gate (pre-pass: dz factor) of the rows of tiles k + 1 (n),
-    // k (c) and k - 1 (p), and of tile k + 2 while it is prepared
-    float skip_n[SPW], gate_n[SPW], skip_c[SPW], gate_c[SPW], skip_p[SPW], gate_p[SPW];
-};
-
-// Raw inputs of this wave's rows of segment tile `tile` (zeros past the end).
-template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void fetch_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                           float (&ru)[kTB / helper_waves(NG, G, PRE)], float (&rd)[kTB / helper_waves(NG, G, PRE)],
-                                           float (&rz)[kTB / helper_waves(NG, G, PRE)], float (&rdy)[kTB / helper_waves(NG, G, PRE)]) {
-    constexpr int SPW = kTB / helper_waves(NG, G, PRE);
-    const int64_t first = static_cast<int64_t>(tile) * kTB * sg.D;       // first element of the tile
-    const int64_t bytes = (sg.seg_elems - first) * static_cast<int64_t>(sizeof(T));
-    const __amdgpu_buffer_rsrc_t ru_r = range_rsrc(sg.u_seg + first, bytes);
-    const __amdgpu_buffer_rsrc_t rd_r = range_rsrc(sg.d_seg + first, bytes);
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        ru[i] = buffer_load_act(ru_r, sg.row_off[i], T{});
-        rd[i] = buffer_load_act(rd_r, sg.row_off[i], T{});
-    }
-    if constexpr (HAS_Z) {
-        const __amdgpu_buffer_rsrc_t rz_r = range_rsrc(sg.z_seg + first, bytes);
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) rz[i] = buffer_load_act(rz_r, sg.row_off[i], T{});
-    }
-    if constexpr (PRE) {
-        const __amdgpu_buffer_rsrc_t ry_r = range_rsrc(sg.dy_seg + first, bytes);
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) rdy[i] = buffer_load_act(ry_r, sg.row_off[i], T{});
-    }
-}
-
-// This wave's Bm and Cm values of segment tile `tile`: lane l holds step
-// l % 16 (zeros past the end).
-template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void fetch_bc(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                         uint32_t (&qb)[LaneRow<T, NG>::kWords],
-                                         uint32_t (&qc)[LaneRow<T, NG>::kWords]) {
-    const int64_t first = static_cast<int64_t>(tile) * kTB * sg.N;
-    const int64_t bytes = (static_cast<int64_t>(sg.t_len) * sg.N - first) * static_cast<int64_t>(sizeof(T));
-    buffer_load_lane_row<T, NG>(range_rsrc(sg.Bm_seg + first, bytes), sg.bc_off, qb);
-    buffer_load_lane_row<T, NG>(range_rsrc(sg.Cm_seg + first, bytes), sg.bc_off, qc);
-}
-
-// Front end of this wave's rows of segment tile `tile` into sDD (and, in the
-// pre-pass, sbar to memory).  Rows past the end hold finite values that are
-// never used.
-// (Pre-pass: sbar of the rows goes to `sbv`, stored by store_sbar after the
-// next loads are issued, so that waiting for those loads never waits for
-// these stores.)
-template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void prep_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, const float (&ru)[kTB / helper_waves(NG, G, PRE)],
-                                          const float (&rd)[kTB / helper_waves(NG, G, PRE)], const float (&rz)[kTB / helper_waves(NG, G, PRE)],
-                                          const float (&rdy)[kTB / helper_waves(NG, G, PRE)], float2 (&dst)[kTB][64],
-                                          float (&skip)[kTB / helper_waves(NG, G, PRE)], float (&gate)[kTB / helper_waves(NG, G, PRE)],
-                                          float (&sbv)[kTB / helper_waves(NG, G, PRE)]) {
-    constexpr int SPW = kTB / helper_waves(NG, G, PRE);
-    if constexpr (PRE) {
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            float2 v;
-            prep_element_pre<HAS_Z>(ru[i], rd[i], rz[i], rdy[i], sg.bias, sg.Dk, sg.softplus_on, v, skip[i], gate[i],
-                                    sbv[i]);
-            dst[sg.hw * SPW + i][sg.lane] = v;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            float2 v;
-            prep_element<HAS_Z>(ru[i], rd[i], rz[i], sg.bias, sg.Dk, sg.softplus_on, v, skip[i], gate[i]);
-            dst[sg.hw * SPW + i][sg.lane] = v;
-            sbv[i] = 0.0f;
-        }
-    }
-}
-
-// Pre-pass: sbar of this wave's rows of segment tile `tile` (rows past the end dropped).
-template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void store_sbar(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                           const float (&sbv)[kTB / helper_waves(NG, G, PRE)]) {
-    constexpr int SPW = kTB / helper_waves(NG, G, PRE);
-    if constexpr (PRE) {
-        const int rows = sg.t_len - tile * kTB;
-        const int D32 = static_cast<int>(sg.D);
-        const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc(sg.sbar_seg + (rows > 0 ? static_cast<int64_t>(tile) * kTB * sg.D : 0),
-                      static_cast<uint32_t>(kTB) * static_cast<uint32_t>(D32) * 4u);
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int j = sg.hw * SPW + i;
-            const uint32_t off = (sg.dvalid && j < rows)
-                                     ? (static_cast<uint32_t>(j) * static_cast<uint32_t>(D32) +
-                                        static_cast<uint32_t>(sg.lane)) * 4u
-                                     : kNoStore;
-            buffer_store_act(sbv[i], rs, off, 0.0f);
-        }
-    }
-}
-
-// Sum of the G partial readouts plus the skip term, times the gate, of this
-// wave's rows of segment tile `tile` -> y (pre-pass: dz).
-template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int tile,
-                                            const float (&part)[kTB / helper_waves(NG, G, PRE)][G], const float (&skip)[kTB / helper_waves(NG, G, PRE)],
-                                            const float (&gate)[kTB / helper_waves(NG, G, PRE)]) {
-    constexpr int SPW = kTB / helper_waves(NG, G, PRE);
-    const int rows = tile >= 0 ? sg.t_len - tile * kTB : 0;  // tile -1: nothing
-    const int D32 = static_cast<int>(sg.D);
-    const __amdgpu_buffer_rsrc_t ry =
-        make_rsrc(sg.y_seg + (rows > 0 ? static_cast<int64_t>(tile) * kTB * sg.D : 0),
-                  static_cast<uint32_t>(kTB) * static_cast<uint32_t>(D32) * sizeof(T));
-#pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        float s = 0.0f;
-#pragma unroll
-        for (int g = 0; g < G; ++g) s += part[i][g];
-        const int j = sg.hw * SPW + i;
-        const bool store = sg.dvalid && j < rows && (!PRE || HAS_Z);
-        const uint32_t off = store ? (static_cast<uint32_t>(j) * static_cast<uint32_t>(D32) +
-                                      static_cast<uint32_t>(sg.lane)) * static_cast<uint32_t>(sizeof(T))
-                                   : kNoStore;
-        buffer_store_act((s + skip[i]) * gate[i], ry, off, T{});
-    }
-}
-
-// Interval of segment tile k (software pipeline, one barrier per tile):
-//  * LDS reads first: the partial readouts of tile k - 1 and (Delta, Delta*u)
-//    of tile k + 1 (prepared in the previous interval), so the LDS latency of
-//    the next tile overlaps this tile's recurrence;
-//  * the front end of tile k + 2 into the other LDS buffer;
-//  * loads of tile k + 1's Bm/Cm and tile k + 3's raw inputs;
-//  * the recurrence of tile k from registers; tile k - 1's rows finished.
-// Work that does not exist (tiles past the end, tile -1) runs on zeros and
-// stores to out-of-range offsets instead of branching.
-// ddt holds tile k's (Delta, Delta*u); ddt_next receives tile k + 1's (two
-// register sets used alternately by consecutive intervals, so nothing is copied).
-// HELPER: a helper wave (front end and finishing of rows); else a state wave
-// (recurrence of its states).
-template <bool FULL, bool HELPER, typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE>& sg, int k, int nval,
-                                             const float (&A2)[NG], float (&h)[NG], FwdRegs<T, NG, G, PRE>& r,
-                                             const float2 (&ddt)[kTB], float2 (&ddt_next)[kTB],
-                                             float2 (&sDD)[2][kTB][64], float (&sP)[2][G][kTB][64]) {
-    constexpr int SPW = kTB / helper_waves(NG, G, PRE);
-    const int cur = k & 1, prv = cur ^ 1;
-    const int lane = sg.lane, w = sg.w;
-    if constexpr (HELPER) {
-        float part[SPW][G];
-#pragma unroll
-        for (int i = 0; i < SPW; ++i)
-#pragma unroll
-            for (int g = 0; g < G; ++g) part[i][g] = sP[prv][g][sg.hw * SPW + i][lane];
-        float skip_nn[SPW], gate_nn[SPW], sbv[SPW];
-        prep_rows(sg, r.ru, r.rd, r.rz, r.rdy, sDD[cur], skip_nn, gate_nn, sbv);  // buffer (k + 2) & 1 == k & 1
-        fetch_rows(sg, k + 3, r.ru, r.rd, r.rz, r.rdy);
-        store_sbar(sg, k + 2, sbv);
-        finish_rows(sg, k - 1, part, r.skip_p, r.gate_p);  // k == 0: nothing stored
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            r.skip_p[i] = r.skip_c[i];
-            r.gate_p[i] = r.gate_c[i];
-            r.skip_c[i] = r.skip_n[i];
-            r.gate_c[i] = r.gate_n[i];
-            r.skip_n[i] = skip_nn[i];
-            r.gate_n[i] = gate_nn[i];
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < kTB; ++j) ddt_next[j] = sDD[prv][j][lane];  // tile k + 1 sits in buffer (k + 1) & 1
-        float Bt[NG], Ct[NG];
-        unpack_lane_row<T, NG>(r.qb, Bt);
-        unpack_lane_row<T, NG>(r.qc, Ct);
-        fetch_bc(sg, k + 1, r.qb, r.qc);
-        if constexpr (PRE) {  // the state before tile k: per state one 64-channel row, coalesced
-#pragma unroll
-            for (int q = 0; q < NG; ++q) {
-                const __amdgpu_buffer_rsrc_t rc =
-                    make_rsrc(sg.ckpt_seg + (static_cast<int64_t>(k) * sg.N + sg.n0 + q) * sg.D, 64u * 4u);
-                buffer_store_act(h[q], rc, sg.dvalid ? static_cast<uint32_t>(lane) * 4u : kNoStore, 0.0f);
-            }
-        }
-        constexpr int S = group_steps<T, NG>();
-        // staging only where registers allow: two states per wave, and not in
-        // the backward pre-pass (whose extra outputs need the registers)
-        fwd_steps<NG, G, S, FULL, NG <= 2 && !PRE>(std::make_integer_sequence<int, kTB / S>{}, nval, w, lane, A2,
-                                                    h, Bt, Ct, ddt, sP[cur]);
-    }
-}
-
-// Runs steps [t_begin, t_end) of channel block `blk` (batch row b = blk /
-// dblocks, channels chan0 .. chan0 + 63) from the state in h, leaving the
-// final state in h.
-template <bool HELPER, typename T, int NG, int G, bool HAS_Z, bool PRE>
-__device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t t_begin, int64_t t_end,
-                                            float (&h)[NG], float2 (&sDD)[2][kTB][64],
-                                            float (&sP)[2][G][kTB][64]) {
-    constexpr int N = NG * G;
-    constexpr int SPW = kTB / helper_waves(NG, G, PRE);  // rows prepared and finished per helper wave per tile
-
-    FwdSeg<T, NG, G, HAS_Z, PRE> sg;
-    sg.lane = threadIdx.x & 63;
-    sg.w = wave_id();
-    const int64_t b = blk / a.dblocks;
-    const int64_t chan0 = static_cast<int64_t>(blk % a.dblocks) * 64;
-    const int64_t D = a.D, L = a.L;
-    sg.D = D;
-    sg.N = N;
-    sg.dvalid = chan0 + sg.lane < D;
-    const int64_t dc = imin64(chan0 + sg.lane, D - 1);
-    sg.n0 = HELPER ? 0 : sg.w * NG;
-    sg.hw = HELPER ? sg.w - G : 0;
-    const int lane = sg.lane, n0 = sg.n0;
-
-    float A2[NG];
-#pragma unroll
-    for (int k = 0; k < NG; ++k) A2[k] = HELPER ? 0.0f : a.A[dc * N + n0 + k] * kLog2e;
-    sg.bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
-    sg.Dk = a.Dskip ? a.Dskip[dc] : 0.0f;
-    sg.softplus_on = a.softplus;
-
-    sg.t_len = static_cast<int>(t_end - t_begin);
-    sg.ntiles = (sg.t_len + kTB - 1) / kTB;
-    sg.seg_elems = static_cast<int64_t>(sg.t_len) * D - chan0;
-    const int64_t row_begin = b * L + t_begin;  // row index of (b, t_begin)
-    const int64_t seg_off = row_begin * D + chan0;  // element (b, t_begin, chan0)
-    sg.u_seg = static_cast<const T*>(a.u) + seg_off;
-    sg.d_seg = static_cast<const T*>(a.delta) + seg_off;
-    sg.z_seg = HAS_Z ? static_cast<const T*>(a.z) + seg_off : nullptr;
-    sg.dy_seg = PRE ? static_cast<const T*>(a.dy) + seg_off : nullptr;
-    sg.y_seg = static_cast<T*>(a.y) + seg_off;
-    sg.Bm_seg = static_cast<const T*>(a.Bm) + row_begin * N;
-    sg.Cm_seg = static_cast<const T*>(a.Cm) + row_begin * N;
-    sg.sbar_seg = PRE ? a.sbar + seg_off : nullptr;
-    sg.ckpt_seg = PRE ? a.ckpt + (b * a.tiles + t_begin / kTB) * N * D + chan0 : nullptr;
-    const int D32 = static_cast<int>(D);
-#pragma unroll
-    for (int i = 0; i < SPW; ++i)
-        sg.row_off[i] = (static_cast<uint32_t>(sg.hw * SPW + i) * static_cast<uint32_t>(D32) + static_cast<uint32_t>(lane)) *
-                        static_cast<uint32_t>(sizeof(T));
-    sg.bc_off = static_cast<uint32_t>(((lane & (kTB - 1)) * N + n0) * static_cast<int>(sizeof(T)));
-
-    __syncthreads();  // LDS is reused from a previous segment
-    // ---- prologue: tiles 0 and 1 prepared, tile 0's (Delta, Delta*u) in
-    // registers, tile 0's Bm/Cm and tile 2's raw inputs in flight
-    FwdRegs<T, NG, G, PRE> r;
-    if constexpr (!HELPER) fetch_bc(sg, 0, r.qb, r.qc);
-    if constexpr (HELPER) {
-        float ru[SPW], rd[SPW], rz[SPW], rdy[SPW];
-        fetch_rows(sg, 0, ru, rd, rz, rdy);
-        fetch_rows(sg, 1, r.ru, r.rd, r.rz, r.rdy);
-        float sb0[SPW], sb1[SPW];
-        prep_rows(sg, ru, rd, rz, rdy, sDD[0], r.skip_c, r.gate_c, sb0);
-        prep_rows(sg, r.ru, r.rd, r.rz, r.rdy, sDD[1], r.skip_n, r.gate_n, sb1);
-        fetch_rows(sg, 2, r.ru, r.rd, r.rz, r.rdy);
-        store_sbar(sg, 0, sb0);
-        store_sbar(sg, 1, sb1);
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) r.skip_p[i] = r.gate_p[i] = 0.0f;
-    }
-    __syncthreads();
-    float2 ddtA[kTB], ddtB[kTB];
-    if constexpr (!HELPER) {
-#pragma unroll
-        for (int j = 0; j < kTB; ++j) ddtA[j] = sDD[0][j][lane];
-    }
-    __syncthreads();  // every wave has read buffer 0 before interval 0 refills it
-
-    // full tiles in pairs (even tiles compute from ddtA, odd ones from ddtB),
-    // then what is left: at most one full tile and a ragged last tile
-    const int nfull = sg.t_len / kTB;
-    int k = 0;
-    for (; k + 2 <= nfull; k += 2) {
-        fwd_interval<true, HELPER>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
-        __syncthreads();
-        fwd_interval<true, HELPER>(sg, k + 1, kTB, A2, h, r, ddtB, ddtA, sDD, sP);
-        __syncthreads();
-    }
-    if (k < sg.ntiles) {
-        if (k < nfull)
-            fwd_interval<true, HELPER>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
-        else
-            fwd_interval<false, HELPER>(sg, k, sg.t_len - k * kTB, A2, h, r, ddtA, ddtB, sDD, sP);
-        __syncthreads();
-        if (k + 1 < sg.ntiles) {  // ragged last tile after a full one
-            fwd_interval<false, HELPER>(sg, k + 1, sg.t_len - (k + 1) * kTB, A2, h, r, ddtB, ddtA, sDD, sP);
-            __syncthreads();
-        }
-    }
-    // ---- epilogue: finish the last tile
-    if constexpr (HELPER) {
-        const int klast = sg.ntiles - 1;
-        float part[SPW][G];
-#pragma unroll
-        for (int i = 0; i < SPW; ++i)
-#pragma unroll
-            for (int g = 0; g < G; ++g) part[i][g] = sP[klast & 1][g][sg.hw * SPW + i][lane];
-        finish_rows(sg, klast, part, r.skip_p, r.gate_p);
-    }
-}
-
-// Main forward kernel.  Block: 64 * G threads.
-//  * workers == 0 -- grid (B * dblocks, K): one workgroup per channel block
-//    and time chunk (initial state from h_in when K > 1);
-//  * workers > 0 -- balanced persistent schedule, one workgroup per worker:
-//    the (block, tile) sequence is cut into `workers` equal contiguous ranges
-//    of at least one block each.  A block is split between at most two
-//    workers.  Each worker first runs its range's last piece if that piece
-//    ends inside a block (it starts at t = 0, so it depends on nobody) and
-//    publishes the end state; then its whole blocks; then its first piece if
-//    that starts inside a block, from the state the previous worker
-//    published.  Equal work per workgroup, no extra arithmetic.  A worker only
-//    waits on a lower-numbered worker, which never waits before publishing
-//    (workgroups are dispatched in increasing order), so every wait ends.
-template <typename T, int NG, int G, bool HAS_Z, bool PRE>
-__global__ __launch_bounds__(64 * (G + helper_waves(NG, G, PRE))) void scan_fwd_kernel(FwdKArgs a) {
-    constexpr int N = NG * G;
-    static_assert(kTB % helper_waves(NG, G, PRE) == 0, "tile must split evenly over the helper waves");
-    __shared__ float2 sDD[2][kTB][64];   // (Delta, Delta * u) per row and channel
-    __shared__ float sP[2][G][kTB][64];  // partial readout of each state group
-    float h[NG];
-    const int lane = threadIdx.x & 63;
-    const bool state_wave = wave_id() < G;
-    const int n0 = state_wave ? wave_id() * NG : 0;
-
-    // Segments of this workgroup, in processing order.  Each is (block,
-    // steps [t_begin, t_end), where its initial state comes from, what
-    // happens to its final state).
-    enum { kFromH0 = 0, kFromChunkCarry = 1, kFromPublished = 2 };
-    enum { kKeep = 0, kFinal = 1, kPublish = 2 };
-    int nseg = 1, tail_piece = 0, full_first = 0, b0 = 0, b1 = 0;
-    int64_t t0 = 0, t1 = 0, T_ = 0;
-    if (a.workers > 0) {
-        T_ = (a.L + kTB - 1) / kTB;  // tiles per sequence
-        const int64_t U = static_cast<int64_t>(a.nblk) * T_;
-        const int64_t u0 = U * blockIdx.x / a.workers;
-        const int64_t u1 = U * (blockIdx.x + 1) / a.workers;
-        b0 = static_cast<int>(u0 / T_);
-        t0 = u0 - b0 * T_;                               // first tile of the range, in block b0
-        b1 = static_cast<int>((u1 - 1) / T_);
-        t1 = u1 - static_cast<int64_t>(b1) * T_;        // end tile of the range, in block b1 (1..T)
-        tail_piece = (b1 > b0 && t1 < T_) ? 1 : 0;       // ends inside b1: run it first and publish
-        full_first = t0 == 0 ? b0 : b0 + 1;
-        const int full_last = t1 == T_ ? b1 : b1 - 1;
-        nseg = tail_piece + (full_last - full_first + 1) + (t0 > 0 ? 1 : 0);
-    }
-    for (int sg = 0; sg < nseg; ++sg) {
-        int blk, from, to;
-        int64_t t_begin, t_end;
-        if (a.workers == 0) {  // grid: block blockIdx.x, chunk blockIdx.y
-            blk = blockIdx.x;
-            t_begin = static_cast<int64_t>(blockIdx.y) * a.chunk_len;
-            t_end = imin64(a.L, t_begin + a.chunk_len);
-            from = a.h_in ? kFromChunkCarry : kFromH0;
-            to = static_cast<int>(blockIdx.y) == a.chunks - 1 ? kFinal : kKeep;
-        } else if (sg < tail_piece) {  // last piece of the range, ends inside block b1
-            blk = b1; t_begin = 0; t_end = t1 * kTB; from = kFromH0; to = kPublish;
-        } else if (sg < nseg - (t0 > 0 ? 1 : 0)) {  // a whole block
-            blk = full_first + (sg - tail_piece); t_begin = 0; t_end = a.L; from = kFromH0; to = kFinal;
-        } else {  // first piece of the range, starts inside block b0
-            blk = b0; t_begin = t0 * kTB; t_end = a.L; from = kFromPublished; to = kFinal;
-        }
-        const int64_t b = blk / a.dblocks;
-        const int64_t chan0 = static_cast<int64_t>(blk % a.dblocks) * 64;
-        const int64_t dcl = imin64(chan0 + lane, a.D - 1);
-        float* carry_lane = a.carry ? a.carry + (static_cast<int64_t>(blk) * 64 + lane) * N + n0 : nullptr;
-#pragma unroll
-        for (int k = 0; k < NG; ++k) h[k] = 0.0f;
-        if (from == kFromH0) {
-            if (state_wave && a.h0) {
-#pragma unroll
-                for (int k = 0; k < NG; ++k) h[k] = a.h0[(b * a.D + dcl) * N + n0 + k];
-            }
-        } else if (from == kFromChunkCarry) {
-            if (state_wave) {
-                const float* hi = a.h_in + ((b * a.chunks + blockIdx.y) * a.D + dcl) * N + n0;
-#pragma unroll
-                for (int k = 0; k < NG; ++k) h[k] = hi[k];
-            }
-        } else {
-            if (threadIdx.x == 0) {
-                while (__hip_atomic_load(a.flags + blk, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u)
-                    __builtin_amdgcn_s_sleep(2);
-            }
-            __syncthreads();
-            if (state_wave) {
-#pragma unroll
-                for (int k = 0; k < NG; ++k)
-                    h[k] = __hip_atomic_load(carry_lane + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        // the same barriers on both paths: the roles differ only in work between them
-        if (state_wave)
-            fwd_segment<false, T, NG, G, HAS_Z, PRE>(a, blk, t_begin, t_end, h, sDD, sP);
-        else
-            fwd_segment<true, T, NG, G, HAS_Z, PRE>(a, blk, t_begin, t_end, h, sDD, sP);
-        if (!state_wave) {
-            if (to == kPublish) {  // the barriers of the state waves' hand-over
-                __threadfence();
-                __syncthreads();
-            }
-        } else if (to == kFinal) {
-            if (a.h_final && chan0 + lane < a.D) {
-                float* hf = a.h_final + (b * a.D + chan0 + lane) * N + n0;
-#pragma unroll
-                for (int k = 0; k < NG; ++k) hf[k] = h[k];
-            }
-        } else if (to == kPublish) {
-#pragma unroll
-            for (int k = 0; k < NG; ++k) carry_lane[k] = h[k];
-            __threadfence();
-            __syncthreads();
-            if (threadIdx.x == 0) __hip_atomic_store(a.flags + blk, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-}
-
-__global__ __launch_bounds__(256) void zero_flags_kernel(uint32_t* flags, int n) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) flags[i] = 0u;
-}
-
-// Chunk aggregates: end state of chunk c started from zero (chunk 0 from h0)
-// and the chunk's sum of Delta.  Grid: (B * dblocks, K - 1).  Per tile, each
-// wave prepares (Delta, Delta*u) of its rows of the next tile into the other
-// LDS buffer while every wave runs the recurrence of its states over this
-// tile: one barrier per tile.  Each wave sums Delta over its own rows; the
-// waves' sums are added in a fixed order at the end.
-template <typename T, int NG, int G>
-__global__ __launch_bounds__(64 * G) void scan_chunk_state_kernel(FwdKArgs a) {
-    constexpr int N = NG * G;
-    constexpr int SPW = kTB / G;
-    constexpr int W = LaneRow<T, NG>::kWords;
-    __shared__ float2 sDD[2][kTB][64];
-    __shared__ float sSum[G][64];
-
-    const T* __restrict__ u = static_cast<const T*>(a.u);
-    const T* __restrict__ dl = static_cast<const T*>(a.delta);
-    const T* __restrict__ Bm = static_cast<const T*>(a.Bm);
-
-    const int lane = threadIdx.x & 63;
-    const int w = wave_id();
-    const int64_t b = blockIdx.x / a.dblocks;
-    const int64_t chan0 = static_cast<int64_t>(blockIdx.x % a.dblocks) * 64;
-    const int64_t c = blockIdx.y;
-    const int64_t D = a.D, L = a.L;
-    const int D32 = static_cast<int>(D);
-    const bool dvalid = chan0 + lane < D;
-    const int lo = dvalid ? lane : static_cast<int>(D - 1 - chan0);
-    const int64_t dc = chan0 + lo;
-    const int n0 = w * NG;
-
-    float A2[NG], h[NG];
-#pragma unroll
-    for (int k = 0; k < NG; ++k) A2[k] = a.A[dc * N + n0 + k] * kLog2e;
-    if (c == 0 && a.h0) {
-        const float* hi = a.h0 + (b * D + dc) * N + n0;
-#pragma unroll
-        for (int k = 0; k < NG; ++k) h[k] = hi[k];
-    } else {
-#pragma unroll
-        for (int k = 0; k < NG; ++k) h[k] = 0.0f;
-    }
-    const float bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
-    float psum = 0.0f;  // sum of Delta over this wave's rows
-
-    const int64_t t_begin = c * a.chunk_len;
-    const int t_len = static_cast<int>(imin64(L, t_begin + a.chunk_len) - t_begin);
-    const int ntiles = (t_len + kTB - 1) / kTB;
-    const int64_t row_begin = b * L + t_begin;
-    const int64_t last_row = row_begin + t_len - 1;
-    float ru[SPW], rd[SPW], rz[SPW];
-    uint32_t qb[W], qn[W];
-
-    // (Delta, Delta * u) of this wave's rows of segment tile `tile` (raw rows in ru, rd) into buffer `buf`
-    auto prep = [&](int tile, int buf) {
-        const int nval = min(kTB, t_len - tile * kTB);
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int j = w * SPW + i;
-            if (j < nval) {
-                const float x = rd[i] + bias;
-                const float dt = a.softplus ? softplus(x) : x;
-                sDD[buf][j][lane] = make_float2(dt, dt * ru[i]);
-                psum += dt;
-            }
-        }
-    };
-    auto fetch = [&](int tile, uint32_t (&q)[W]) {
-        const int64_t row0 = row_begin + static_cast<int64_t>(tile) * kTB;
-        fetch_rows_ptr<T, SPW>(u, dl, static_cast<const T*>(nullptr), row0 * D + chan0, w * SPW,
-                               t_len - tile * kTB, D32, lo, ru, rd, rz);
-        fetch_tile_rows<T, NG>(Bm, row0, last_row, N, n0, lane, q);
-    };
-
-    fetch(0, qb);
-    prep(0, 0);
-    if (ntiles > 1) fetch(1, qn);
-    __syncthreads();
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int cur = tile & 1;
-        float Bt[NG];
-        unpack_lane_row<T, NG>(qb, Bt);
-        if (tile + 1 < ntiles) {
-            prep(tile + 1, cur ^ 1);
-#pragma unroll
-            for (int i = 0; i < W; ++i) qb[i] = qn[i];
-            if (tile + 2 < ntiles) fetch(tile + 2, qn);
-        }
-        const int nval = min(kTB, t_len - tile * kTB);
-        if (nval == kTB)
-            state_steps<NG, true>(std::make_integer_sequence<int, kTB>{}, kTB, lane, A2, h, Bt, sDD[cur]);
-        else
-            state_steps<NG, false>(std::make_integer_sequence<int, kTB>{}, nval, lane, A2, h, Bt, sDD[cur]);
-        __syncthreads();
-    }
-    sSum[w][lane] = psum;
-    __syncthreads();
-    if (dvalid) {
-        float* ho = a.agg_h + ((b * a.chunks + c) * D + chan0 + lane) * N + n0;
-#pragma unroll
-        for (int k = 0; k < NG; ++k) ho[k] = h[k];
-        if (w == 0) {
-            float ssum = 0.0f;
-#pragma unroll
-            for (int g = 0; g < G; ++g) ssum += sSum[g][lane];
-            a.agg_s[(b * a.chunks + c) * D + chan0 + lane] = ssum;
-        }
-    }
-}
-
-// Chain the chunk aggregates: h_in[c] = P_{c-1} h_in[c-1] + H_{c-1}, with
-// P = exp(A * sum Delta).  One thread per (b, d, n); sequential over chunks.
-__global__ __launch_bounds__(256) void scan_carry_kernel(FwdKArgs a, int64_t B, int64_t N) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t D = a.D;
-    if (i >= B * D * N) return;
-    const int64_t n = i % N;
-    const int64_t d = (i / N) % D;
-    const int64_t b = i / (N * D);
-    const float A2 = a.A[d * N + n] * kLog2e;
-    float* hin = const_cast<float*>(a.h_in);
-    const int64_t K = a.chunks;
-    hin[((b * K + 0) * D + d) * N + n] = a.h0 ? a.h0[(b * D + d) * N + n] : 0.0f;
-    float h = a.agg_h[((b * K + 0) * D + d) * N + n];   // chunk 0 aggregate includes h0
-    for (int64_t c = 1; c < K; ++c) {
-        hin[((b * K + c) * D + d) * N + n] = h;
-        if (c + 1 < K) {
-            const float P = fast_exp2(A2 * a.agg_s[(b * K + c) * D + d]);
-            h = __builtin_fmaf(P, h, a.agg_h[((b * K + c) * D + d) * N + n]);
-        }
-    }
-}
-
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-// Smallest block count for which the balanced schedule may be chosen (a
-// device partition has at least this many CUs).
-constexpr int64_t kBalancedMinBlocks = 64;
-
-// Extra outputs of the backward pre-pass (all null for the forward).
-struct PreOut {
-    const void* dy;
-    void* dz;
-    float* sbar;
-    float* ckpt;
-};
-
-template <typename T, int NG, int G, bool PRE>
-hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, void* scratch, const PreOut& pre, hipStream_t st) {
-    FwdKArgs a{};
-    a.u = s.u; a.delta = s.delta; a.z = s.z; a.Bm = s.Bm; a.Cm = s.Cm;
-    a.A = s.A; a.Dskip = s.Dskip; a.dt_bias = s.dt_bias; a.h0 = s.h0;
-    a.y = s.y; a.h_final = s.h_final;
-    a.L = s.L; a.D = s.D;
-    a.chunk_len = pl.chunk_len;
-    a.chunks = static_cast<int32_t>(pl.chunks);
-    a.dblocks = static_cast<int32_t>((s.D + 63) / 64);
-    a.softplus = s.softplus;
-    a.tiles = (s.L + kTB - 1) / kTB;
-    if constexpr (PRE) {
-        a.dy = pre.dy;
-        a.dz = pre.dz;
-        a.sbar = pre.sbar;
-        a.ckpt = pre.ckpt;
-        a.y = pre.dz ? pre.dz : static_cast<void*>(pre.sbar);  // dz goes where y would; never stored without z
-        a.h_final = nullptr;
-    }
-    char* ws = static_cast<char*>(scratch);
-    if (pl.chunks > 1) {
-        const size_t nh = static_cast<size_t>(s.B) * pl.chunks * s.D * s.N * sizeof(float);
-        const size_t ns = static_cast<size_t>(s.B) * pl.chunks * s.D * sizeof(float);
-        a.agg_h = reinterpret_cast<float*>(ws);
-        a.agg_s = reinterpret_cast<float*>(ws + align256(nh));
-        a.h_in = nullptr;
-        // its own layout: for N = 16, 8 waves of 2 states (measured 5-8 % faster
-        // on the 1M-step forward than the main kernel's 4 waves of 4)
-        constexpr int NGc = NG * G == 16 ? 2 : NG;
-        constexpr int Gc = NG * G / NGc;
-        hipLaunchKernelGGL((scan_chunk_state_kernel<T, NGc, Gc>),
-                           dim3(static_cast<unsigned>(s.B * a.dblocks), static_cast<unsigned>(pl.chunks - 1)),
-                           dim3(64 * Gc), 0, st, a);
-        a.h_in = reinterpret_cast<const float*>(ws + align256(nh) + align256(ns));
-        const int64_t threads = s.B * s.D * s.N;
-        hipLaunchKernelGGL(scan_carry_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, st,
-                           a, s.B, s.N);
-    }
-    dim3 grid(static_cast<unsigned>(s.B * a.dblocks), static_cast<unsigned>(pl.chunks));
-    a.nblk = static_cast<int32_t>(s.B * a.dblocks);
-    if (pl.chunks == 1 && pl.ws_bytes > 0) {
-        // balanced persistent schedule when the blocks do not split evenly over the CUs
-        int dev = 0, ncu = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        if (ncu > 0 && a.nblk >= ncu && a.nblk % ncu != 0) {
-            a.workers = ncu;
-            a.flags = reinterpret_cast<uint32_t*>(ws);
-            a.carry = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(a.nblk) * sizeof(uint32_t)));
-            hipLaunchKernelGGL(zero_flags_kernel, dim3(static_cast<unsigned>((a.nblk + 255) / 256)), dim3(256), 0,
-                               st, a.flags, a.nblk);
-            grid = dim3(static_cast<unsigned>(ncu));
-        }
-    }
-    const dim3 main_block(64 * (G + helper_waves(NG, G, PRE)));  // state waves + helper waves
-    if (s.z)
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE>), grid, main_block, 0, st, a);
-    else
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false, PRE>), grid, main_block, 0, st, a);
-    return hipGetLastError();
-}
-
-template <typename T, bool PRE>
-hipError_t dispatch_n(const ScanArgs& s, const FwdPlan& pl, void* scratch, const PreOut& pre, hipStream_t st) {
-    switch (s.N) {
-        case 1: return launch_fwd_t<T, 1, 1, PRE>(s, pl, scratch, pre, st);
-        case 2: return launch_fwd_t<T, 1, 2, PRE>(s, pl, scratch, pre, st);
-        case 4: return launch_fwd_t<T, 1, 4, PRE>(s, pl, scratch, pre, st);
-        case 8: return launch_fwd_t<T, 2, 4, PRE>(s, pl, scratch, pre, st);
-        case 16: return launch_fwd_t<T, 4, 4, PRE>(s, pl, scratch, pre, st);  // every pretrained Mamba model
-        case 32: return launch_fwd_t<T, 4, 8, PRE>(s, pl, scratch, pre, st);
-        case 64: return launch_fwd_t<T, 8, 8, PRE>(s, pl, scratch, pre, st);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-}  // namespace
 
 FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N) {
     FwdPlan p{1, L, 0};
@@ -1054,15 +37,16 @@ FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N) {
 hipError_t launch_fwd(const ScanArgs& s, hipStream_t st) {
     const FwdPlan pl = plan_fwd(s.B, s.L, s.D, s.N);
     const PreOut none{};
-    return s.dtype == 1 ? dispatch_n<uint16_t, false>(s, pl, s.workspace, none, st)
-                        : dispatch_n<float, false>(s, pl, s.workspace, none, st);
+    return s.dtype == 1 ? dispatch_n<uint16_t, false, false>(s, pl, s.workspace, none, st)
+                        : dispatch_n<float, false, false>(s, pl, s.workspace, none, st);
 }
 
 hipError_t launch_fwd_prepass(const ScanArgs& s, void* fwd_scratch, float* ckpt, float* sbar, hipStream_t st) {
     const FwdPlan pl = plan_fwd(s.B, s.L, s.D, s.N);
     const PreOut pre{s.dy, s.dz, sbar, ckpt};
-    return s.dtype == 1 ? dispatch_n<uint16_t, true>(s, pl, fwd_scratch, pre, st)
-                        : dispatch_n<float, true>(s, pl, fwd_scratch, pre, st);
+    return s.dtype == 1 ? dispatch_n<uint16_t, true, false>(s, pl, fwd_scratch, pre, st)
+                        : dispatch_n<float, true, false>(s, pl, fwd_scratch, pre, st);
 }
 
 }  // namespace mssm
+

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     for n in names:
         assert hasattr(lib, n), f"libmssm.so does not export {n}"
     assert sorted(mssm.EXPORTS) == names
@@ -46,6 +46,19 @@ def fwd(p, u=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dskip=None, z=None, dt_
     v = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
     return lib.mssm_scan_fwd(pp, v(u), v(delta), v(A), v(Bm), v(Cm), v(Dskip), v(z), v(dt_bias),
                              v(h0), v(y), v(hf), v(ws), wsb, None)
+
+
+def conv_fwd(p, d_conv=4, **kw):
+    names = ["x", "conv_w", "conv_b", "x_prev", "delta", "A", "Bm", "Cm", "Dskip", "z", "dt_bias", "h0", "y",
+             "h_final", "u_out"]
+    required = {"x", "conv_w", "delta", "A", "Bm", "Cm", "y"}
+    args = []
+    for n in names:
+        x = kw.get(n, FAKE if n in required else None)
+        args.append(None if x is None else ctypes.c_void_p(x))
+    ws = kw.get("ws", None)
+    return lib.mssm_conv_scan_fwd(ctypes.byref(p) if p is not None else None, d_conv, *args,
+                                  None if ws is None else ctypes.c_void_p(ws), kw.get("wsb", 0), None)
 
 
 def bwd(p, **kw):
@@ -113,6 +126,23 @@ def test_alignment():
     assert step(good(), state=MIS) == -5
 
 
+def test_conv_front_end_validation():
+    # the problem checks of the forward, then the conv's own: width, required taps, alignment
+    assert conv_fwd(None) == -1
+    assert conv_fwd(good(N=12)) == -4
+    assert conv_fwd(good(L=0)) == -2
+    for k in (0, 5, -1):
+        assert conv_fwd(good(), d_conv=k) == -2, k
+    for k in ("x", "conv_w", "delta", "A", "Bm", "Cm", "y"):
+        assert conv_fwd(good(), **{k: None}) == -1, k
+    for k in ("x", "conv_w", "conv_b", "x_prev", "u_out", "h_final"):
+        assert conv_fwd(good(), **{k: MIS}) == -5, k
+    long_ = P(1, 1 << 20, 1536, 16, 1, 1)
+    nws = lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(long_))
+    assert conv_fwd(long_, ws=None) == -6
+    assert conv_fwd(long_, ws=FAKE, wsb=nws - 1) == -6
+
+
 def test_workspace_sizes_and_checks():
     tiny = good(1, 64, 32, 16)
     assert lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(tiny)) == 0
@@ -138,6 +168,10 @@ def test_binding_rejects_cpu_tensors_and_bad_shapes():
     Bm = torch.zeros(1, 8, 16)
     with pytest.raises(ValueError):
         mssm.scan_fwd(u, u, A, Bm, Bm)          # CPU tensors: no fallback path exists
+    with pytest.raises(ValueError):
+        mssm.conv_scan_fwd(u, torch.zeros(4, 4), u, A, Bm, Bm)
+    with pytest.raises(ValueError):
+        mssm.conv_scan_fwd(u, torch.zeros(4, 5), u, A, Bm, Bm)   # d_conv 5 > the widest built
     with pytest.raises(TypeError):
         mssm.binding._dtype_code(torch.zeros(1, dtype=torch.float16))
 

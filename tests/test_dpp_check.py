@@ -90,7 +90,7 @@ def test_library_device_code_has_no_dpp_hazards():
 
     with tempfile.TemporaryDirectory(prefix="mssm_dpp_") as d:
         procs = []
-        for src in ("scan_fwd.hip", "scan_bwd.hip", "scan_step.hip"):
+        for src in ("scan_fwd.hip", "scan_conv_fwd.hip", "scan_bwd.hip", "scan_step.hip"):
             cmd = (["hipcc"] + entry.HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
                                                    "--cuda-device-only", "-S", os.path.join(CSRC, src),
                                                    "-o", os.path.join(d, src + ".s")])
@@ -100,7 +100,7 @@ def test_library_device_code_has_no_dpp_hazards():
             if p.returncode != 0:
                 pytest.fail(err[-2000:])
         total = 0
-        for src in ("scan_fwd.hip", "scan_bwd.hip"):
+        for src in ("scan_fwd.hip", "scan_conv_fwd.hip", "scan_bwd.hip"):
             text = open(os.path.join(d, src + ".s")).read()
             assert dpp_check.check_asm(text) == []
             total += dpp_check.count_dpp(text)

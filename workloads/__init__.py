@@ -20,6 +20,12 @@ Recipe (fixed draw order, numpy ``Generator(PCG64)``):
 4. ``u ~ N(0,1)``;  5. ``delta = 0.5 * N(0,1)``;  6. ``z ~ N(0,1)``;
 7. ``Bm ~ N(0,1)``; 8. ``Cm ~ N(0,1)``;  9. ``dy ~ N(0,1)`` (training only).
 
+Causal conv1d front end (``conv_front_end``): the conv input x is the u
+drawn above; taps (D, d_conv) and bias (D) uniform on [-1/sqrt(d_conv),
+1/sqrt(d_conv)] (torch.nn.Conv1d's default initialisation for a depthwise
+layer, whose fan-in is d_conv), and the history x_prev (B, d_conv - 1, D) ~
+N(0,1), from ``SeedSequence(seed, spawn_key=(2**20, d_conv))``.
+
 Normals are drawn in float32.  For bfloat16 workloads u, delta, z, Bm, Cm are
 rounded to nearest-even bfloat16 and kept as uint16 bit patterns ("storage
 form"); float32 workloads keep float32 arrays.  Steps 4-9 are drawn per block
@@ -144,6 +150,19 @@ def make_inputs(w: Workload, with_dy: bool | None = None, threads: int = 8) -> d
     return out
 
 
+def conv_front_end(w: Workload, d_conv: int = 4) -> dict:
+    """Seeded parameters of the causal conv1d front end of workload `w`:
+    conv_w (D, d_conv) and conv_b (D) float32, x_prev (B, d_conv - 1, D) in
+    the workload's storage form.  Merge into the dict of ``make_inputs``; its
+    u then serves as the conv input x."""
+    rng = np.random.default_rng(np.random.SeedSequence(w.seed, spawn_key=(1 << 20, d_conv)))
+    bound = 1.0 / np.sqrt(d_conv)
+    conv_w = rng.uniform(-bound, bound, (w.D, d_conv)).astype(np.float32)
+    conv_b = rng.uniform(-bound, bound, w.D).astype(np.float32)
+    xp = rng.standard_normal((w.B, d_conv - 1, w.D), dtype=np.float32)
+    return {"conv_w": conv_w, "conv_b": conv_b, "x_prev": bf16_bits(xp) if w.dtype == "bf16" else xp}
+
+
 def select_channels(inp: dict, channels) -> dict:
     """Inputs restricted to a subset of channels (channels are independent in
     the scan; Bm and Cm are shared by all channels and kept whole)."""
@@ -152,9 +171,14 @@ def select_channels(inp: dict, channels) -> dict:
     for k in ("u", "delta", "z", "dy"):
         if k in inp and inp[k] is not None:
             out[k] = np.ascontiguousarray(inp[k][:, :, ch])
-    for k in ("dt_bias", "Dskip"):
-        out[k] = np.ascontiguousarray(inp[k][ch])
-    out["A"] = np.ascontiguousarray(inp["A"][ch])
+    for k in ("dt_bias", "Dskip", "conv_b"):
+        if k in inp and inp[k] is not None:
+            out[k] = np.ascontiguousarray(inp[k][ch])
+    for k in ("A", "conv_w"):
+        if k in inp and inp[k] is not None:
+            out[k] = np.ascontiguousarray(inp[k][ch])
+    if inp.get("x_prev") is not None:
+        out["x_prev"] = np.ascontiguousarray(inp["x_prev"][:, :, ch])
     return out
 
 
@@ -170,13 +194,14 @@ def select_time(inp: dict, t0: int, t1: int) -> dict:
 def as_float32(inp: dict) -> dict:
     """Storage form -> float32 arrays (exact)."""
     out = dict(inp)
-    for k in ("u", "delta", "z", "dy", "Bm", "Cm"):
+    for k in ("u", "delta", "z", "dy", "Bm", "Cm", "x_prev"):
         if k in inp and inp[k] is not None:
             out[k] = to_f32(inp[k], inp["dtype"])
     return out
 
 
-def to_torch(inp: dict, device="cuda", keys=("u", "delta", "z", "Bm", "Cm", "dy", "dt_bias", "A", "Dskip")) -> dict:
+def to_torch(inp: dict, device="cuda", keys=("u", "delta", "z", "Bm", "Cm", "dy", "dt_bias", "A", "Dskip", "conv_w",
+                                             "conv_b", "x_prev")) -> dict:
     """Storage form -> torch tensors on `device` (bfloat16 bits are
     reinterpreted, not converted, so values are exact)."""
     import torch
@@ -186,7 +211,7 @@ def to_torch(inp: dict, device="cuda", keys=("u", "delta", "z", "Bm", "Cm", "dy"
         if k not in inp or inp[k] is None:
             continue
         x = inp[k]
-        if k in ("dt_bias", "A", "Dskip") or inp["dtype"] == "f32":
+        if k in ("dt_bias", "A", "Dskip", "conv_w", "conv_b") or inp["dtype"] == "f32":
             out[k] = torch.from_numpy(np.ascontiguousarray(x)).to(device)
         else:
             out[k] = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
