@@ -19,7 +19,8 @@ float32 arithmetic), inputs resident in HBM.  Prints one JSON line:
   sample of the same workload.
 
 ``--gpus N`` with N > 1 exits: this benchmark and the library run on one GPU.
-``--extra`` adds the 130M-layer forward, the recurrent step at the 2.8B layer's
+``--extra`` adds the 130M-layer forward, the 2.8B-layer forward behind the fused
+causal conv1d + SiLU front end (x in place of u, d_conv = 4), the recurrent step at the 2.8B layer's
 width (B=4, D=5120, N=16: one decode step per call from Python, so the host's
 launch overhead, not the kernel, sets this rate; the kernel's own duration is
 in the kernel trace), the same step at B = 64 and 256 (batched decode, where the
@@ -63,6 +64,12 @@ def fwd_bytes(w: workloads.Workload) -> int:
             + 4 * w.D * w.N + 8 * w.D + 4 * w.B * w.D * w.N)
 
 
+def conv_fwd_bytes(w: workloads.Workload, d_conv: int = 4) -> int:
+    """The forward behind the fused conv front end: x in place of u, plus the
+    taps and bias (u itself never moves)."""
+    return fwd_bytes(w) + 4 * w.D * d_conv + 4 * w.D
+
+
 def bwd_bytes(w: workloads.Workload) -> int:
     act = 2 if w.dtype == "bf16" else 4
     # reads u, delta, z, dy, Bm, Cm, A, Dskip, dt_bias; writes du, ddelta, dz, dB, dC, dA, dD, ddt_bias
@@ -102,8 +109,13 @@ def measured_traffic():
         return None
 
 
-def time_fwd(mssm, torch, w, steps, warmup, cold_reps=0):
+def time_fwd(mssm, torch, w, steps, warmup, cold_reps=0, conv=False):
+    """Forward kernel time per call (HIP events on the launch stream); with
+    `conv`, the forward behind the fused causal conv1d + SiLU front end
+    (d_conv = 4), the workload's u serving as the conv input x."""
     inp = workloads.make_inputs(w)
+    if conv:
+        inp.update(workloads.conv_front_end(w, 4))
     t = workloads.to_torch(inp, "cuda")
     del inp
     y = torch.empty_like(t["u"])
@@ -112,8 +124,12 @@ def time_fwd(mssm, torch, w, steps, warmup, cold_reps=0):
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
 
     def run():
-        mssm.scan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"], t["dt_bias"],
-                      None, y=y, h_final=hf, workspace=ws)
+        if conv:
+            mssm.conv_scan_fwd(t["u"], t["conv_w"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"],
+                               t["dt_bias"], None, conv_b=t["conv_b"], y=y, h_final=hf, workspace=ws)
+        else:
+            mssm.scan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"], t["dt_bias"],
+                          None, y=y, h_final=hf, workspace=ws)
 
     for _ in range(warmup):
         run()
@@ -324,6 +340,11 @@ def main():
             wl, _, _ = time_fwd(mssm, torch, ww, 20, 3)
             out.setdefault("extra", {})[f"{name}_fwd_GBs"] = round(fwd_bytes(ww) / wl / 1e9, 1)
             out["extra"][f"{name}_fwd_us"] = round(wl * 1e6, 1)
+        _, cl, _ = time_fwd(mssm, torch, w, 20, 3, conv=True)
+        conv_us = float(np.median(cl)) * 1e3
+        out["extra"]["conv_fwd_us"] = round(conv_us, 1)   # median kernel time, fused conv1d + SiLU front end
+        out["extra"]["conv_fwd_GBs"] = round(conv_fwd_bytes(w) / conv_us / 1e3, 1)
+        out["extra"]["conv_fwd_vs_plain_median"] = round(conv_us / (float(np.median(launch_ms)) * 1e3), 3)
         st_us, st_gbs = time_step(mssm, torch, w)
         out.setdefault("extra", {})["step_us_per_call"] = round(st_us, 2)
         out["extra"]["step_GBs_per_call"] = round(st_gbs, 1)
