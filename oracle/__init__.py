@@ -139,6 +139,31 @@ def causal_conv_silu(x, weight, bias=None, x_prev=None, silu=True):
     return c / (1.0 + np.exp(-c))
 
 
+def causal_conv_silu_bwd(x, weight, du, bias=None, x_prev=None):
+    """Adjoint of ``causal_conv_silu`` in float64: given du = dL/du, returns a
+    dict with dx (B, L, D), dweight (D, K), dbias (D) and dx_prev (B, K - 1, D).
+    With c the convolution and g = du * silu'(c), silu'(c) = s (1 + c (1 - s)),
+    s = sigmoid(c): dbias = sum_{b,t} g, dweight[d,k] = sum_{b,t} g[t] xx[t+k]
+    and dxx[tau] = sum_k weight[d,k] g[tau - k] over the history and the
+    sequence together (xx, time -(K - 1) .. L - 1), split into dx_prev and dx."""
+    x, weight, du, bias, x_prev = map(_f64, (x, weight, du, bias, x_prev))
+    Bsz, L, D = x.shape
+    weight = weight.reshape(D, -1)
+    K = weight.shape[1]
+    if x_prev is None:
+        x_prev = np.zeros((Bsz, K - 1, D))
+    xx = np.concatenate([x_prev, x], axis=1)
+    c = causal_conv_silu(x, weight, bias, x_prev, silu=False)
+    s = 1.0 / (1.0 + np.exp(-c))
+    g = du * s * (1.0 + c * (1.0 - s))
+    dxx = np.zeros_like(xx)
+    dw = np.zeros((D, K))
+    for k in range(K):                                 # c[t] took weight[:, k] * xx[t + k]
+        dxx[:, k:k + L, :] += weight[:, k] * g
+        dw[:, k] = np.sum(g * xx[:, k:k + L, :], axis=(0, 1))
+    return {"dx": dxx[:, K - 1:], "dweight": dw, "dbias": g.sum(axis=(0, 1)), "dx_prev": dxx[:, :K - 1]}
+
+
 def conv_scan_fwd(x, weight, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
                   bias=None, x_prev=None, softplus=True):
     """The scan behind the conv front end: ``(y, h_final, u)`` in float64 with

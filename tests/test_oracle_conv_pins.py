@@ -137,3 +137,93 @@ def test_pins_catch_conv_mutation(name, monkeypatch):
         except (AssertionError, ValueError):
             failed += 1
     assert failed >= 1, f"no pin caught the mutation '{name}'"
+
+
+# ---- the adjoint (oracle.causal_conv_silu_bwd) -------------------------------------------------
+
+@pytest.mark.parametrize("K,prev", [(4, True), (4, False), (3, True), (1, False)])
+def test_backward_against_torch_autograd(K, prev):
+    """torch.autograd in float64 through the layer the pages name
+    (torch.nn.functional.conv1d, groups = D, over history + sequence) and
+    SiLU: a library route to every gradient."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    x, w, b, xp = case(B=2, L=11, D=3, K=K, prev=prev)
+    B, L, D = x.shape
+    du = RNG.standard_normal((B, L, D))
+    xt = torch.tensor(x, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    bt = torch.tensor(b, requires_grad=True)
+    xpt = torch.tensor(xp if prev else np.zeros((B, K - 1, D)), requires_grad=True)
+    xx = torch.cat([xpt, xt], 1).transpose(1, 2)
+    u = F.silu(F.conv1d(xx, wt.reshape(D, 1, K), bt, groups=D)).transpose(1, 2)
+    (u * torch.tensor(du)).sum().backward()
+    g = oracle.causal_conv_silu_bwd(x, w, du, b, xp if prev else None)
+    np.testing.assert_allclose(g["dx"], xt.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(g["dweight"], wt.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(g["dbias"], bt.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(g["dx_prev"], xpt.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_backward_finite_differences():
+    x, w, b, xp = case(B=1, L=6, D=2, K=4)
+    du = RNG.standard_normal(x.shape)
+    g = oracle.causal_conv_silu_bwd(x, w, du, b, xp)
+    loss = lambda x_, w_, b_, p_: float(np.sum(du * oracle.causal_conv_silu(x_, w_, b_, p_)))  # noqa: E731
+    eps = 1e-6
+    for name, arr, grad, pos in (("dx", x, g["dx"], lambda a: (a, w, b, xp)),
+                                 ("dweight", w, g["dweight"], lambda a: (x, a, b, xp)),
+                                 ("dbias", b, g["dbias"], lambda a: (x, w, a, xp)),
+                                 ("dx_prev", xp, g["dx_prev"], lambda a: (x, w, b, a))):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            p, m = arr.copy(), arr.copy()
+            p[idx] += eps
+            m[idx] -= eps
+            num[idx] = (loss(*pos(p)) - loss(*pos(m))) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_backward_invariants():
+    """dbias is the sum of dx over the sequence and history for an identity
+    kernel scaled by one; with a pure delay, dx is g shifted back."""
+    x, _, b, xp = case(K=4)
+    du = RNG.standard_normal(x.shape)
+    delay = np.zeros((x.shape[2], 4))
+    delay[:, 0] = 1.0
+    g = oracle.causal_conv_silu_bwd(x, delay, du, b, xp)
+    c = oracle.causal_conv_silu(x, delay, b, xp, silu=False)
+    from scipy.special import expit
+    gg = du * (expit(c) * (1 + c * (1 - expit(c))))
+    np.testing.assert_allclose(g["dx"][:, :-3], gg[:, 3:], rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(g["dx"][:, -3:], 0.0)
+    np.testing.assert_allclose(g["dx_prev"], gg[:, :3], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(g["dbias"], gg.sum(axis=(0, 1)), rtol=1e-13)
+
+
+BWD_CONV_PINS = [lambda: test_backward_against_torch_autograd(4, True), test_backward_invariants]
+
+BWD_MUTATIONS = {
+    "silu derivative without the c term": ("g = du * s * (1.0 + c * (1.0 - s))", "g = du * s"),
+    "dx stencil not transposed": ("dxx[:, k:k + L, :] += weight[:, k] * g", "dxx[:, k:k + L, :] += weight[:, K - 1 - k] * g"),
+    "dweight against the wrong tap": ("dw[:, k] = np.sum(g * xx[:, k:k + L, :], axis=(0, 1))",
+                                      "dw[:, k] = np.sum(g * xx[:, K - 1:K - 1 + L, :], axis=(0, 1))"),
+    "history gradient dropped": ('"dx_prev": dxx[:, :K - 1]', '"dx_prev": 0.0 * dxx[:, :K - 1]'),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_pins_catch_conv_backward_mutation(name, monkeypatch):
+    old, new = BWD_MUTATIONS[name]
+    src = textwrap.dedent(inspect.getsource(oracle.causal_conv_silu_bwd))
+    assert src.count(old) == 1, "mutation anchor not found: " + old
+    ns = {"np": np, "_f64": oracle._f64, "causal_conv_silu": oracle.causal_conv_silu}
+    exec(src.replace(old, new), ns)
+    monkeypatch.setattr(oracle, "causal_conv_silu_bwd", ns["causal_conv_silu_bwd"])
+    failed = 0
+    for pin in BWD_CONV_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            failed += 1
+    assert failed >= 1, f"no pin caught the mutation '{name}'"
