@@ -152,6 +152,31 @@ mssm_status mssm_conv_scan_fwd(const mssm_problem* p, int32_t d_conv,
                                void* y, float* h_final, void* u_out,
                                void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Bytes of device scratch mssm_conv_bwd needs (per (batch row, time chunk)
+ * partial sums of dconv_w and dconv_b); p->dstate is ignored.  0 for an
+ * invalid problem or d_conv. */
+size_t mssm_conv_bwd_workspace_bytes(const mssm_problem* p, int32_t d_conv);
+
+/*
+ * Backward of the conv1d + SiLU front end of mssm_conv_scan_fwd: given du =
+ * dL/du for u = silu(conv_b + causal depthwise conv of x with conv_w) (the du
+ * that mssm_scan_bwd returns for the u that mssm_conv_scan_fwd formed),
+ * writes, with g = du * silu'(c) and c the convolution:
+ *   dx       (B, L, D) p->dtype   dx[t] = sum_k conv_w[d,k] g[t + d_conv - 1 - k]
+ *   dconv_w  (D, d_conv) float32  sum over (b, t) of g[t] x[t - d_conv + 1 + k]
+ *   dconv_b  (D) float32, NULL -> not written; sum over (b, t) of g
+ *   dx_prev  (B, d_conv - 1, D) p->dtype, NULL -> not written; the gradient of
+ *            the history rows x_prev (zero history: the gradient of the padding)
+ * x, conv_w, conv_b, x_prev and d_conv as in mssm_conv_scan_fwd; p->dstate
+ * and p->delta_softplus are ignored.  Gradients are overwritten; dconv_w and
+ * dconv_b are summed in a fixed order (bitwise reproducible).  Errors as for
+ * mssm_conv_scan_fwd (required: x, conv_w, du, dx, dconv_w, workspace).
+ */
+mssm_status mssm_conv_bwd(const mssm_problem* p, int32_t d_conv,
+                          const void* x, const float* conv_w, const float* conv_b, const void* x_prev,
+                          const void* du, void* dx, float* dconv_w, float* dconv_b, void* dx_prev,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /*
  * Backward scan: gradients of  sum(dy * y) + sum(dh_final * h_final)  with
  * respect to every input, by the reverse-time adjoint scan with the forward

@@ -22,7 +22,8 @@ STATUS = {0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_SHAPE", -3: "MSSM_ERR
           -4: "MSSM_ERR_UNSUPPORTED", -5: "MSSM_ERR_ALIGN", -6: "MSSM_ERR_WORKSPACE",
           -7: "MSSM_ERR_HIP"}
 EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd",
-           "mssm_conv_scan_fwd", "mssm_scan_bwd", "mssm_step", "mssm_status_string", "mssm_build_info"]
+           "mssm_conv_scan_fwd", "mssm_conv_bwd_workspace_bytes", "mssm_conv_bwd", "mssm_scan_bwd", "mssm_step",
+           "mssm_status_string", "mssm_build_info"]
 MAX_DCONV = 4
 
 
@@ -52,6 +53,10 @@ def _open(path: str):
     lib.mssm_scan_fwd.restype = st
     lib.mssm_conv_scan_fwd.argtypes = [P, ctypes.c_int32] + [vp] * 15 + [vp, sz, vp]
     lib.mssm_conv_scan_fwd.restype = st
+    lib.mssm_conv_bwd_workspace_bytes.argtypes = [P, ctypes.c_int32]
+    lib.mssm_conv_bwd_workspace_bytes.restype = sz
+    lib.mssm_conv_bwd.argtypes = [P, ctypes.c_int32] + [vp] * 9 + [vp, sz, vp]
+    lib.mssm_conv_bwd.restype = st
     lib.mssm_scan_bwd.argtypes = [P] + [vp] * 20 + [vp, sz, vp]
     lib.mssm_scan_bwd.restype = st
     lib.mssm_step.argtypes = [P] + [vp] * 10 + [vp]
@@ -215,6 +220,43 @@ def conv_scan_fwd(x, conv_w, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None,
                                   _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(u_out),
                                   _ptr(ws), nbytes, _stream(x.device)))
     return y, h_final, u_out
+
+
+def conv_bwd(x, conv_w, du, conv_b=None, x_prev=None, want_dconv_b=True, want_dx_prev=False, workspace=None):
+    """Backward of the conv1d + SiLU front end of conv_scan_fwd: given du
+    (B, L, D), returns a dict with dx (B, L, D), dconv_w (D, d_conv) float32,
+    dconv_b (D) float32 (None unless wanted) and dx_prev (B, d_conv - 1, D)
+    (None unless wanted)."""
+    act = x.dtype
+    B, L, D = x.shape
+    if conv_w is None or conv_w.dim() not in (2, 3) or conv_w.shape[0] != D:
+        raise ValueError("conv_w must be (D, d_conv) or (D, 1, d_conv)")
+    K = conv_w.shape[-1]
+    if conv_w.dim() == 3:
+        _req(conv_w, "conv_w", (D, 1, K), torch.float32)
+        conv_w = conv_w.view(D, K)
+    if not 1 <= K <= MAX_DCONV:
+        raise ValueError(f"d_conv = {K} not in 1..{MAX_DCONV}")
+    _req(x, "x", (B, L, D), act)
+    _req(conv_w, "conv_w", (D, K), torch.float32)
+    _opt(conv_b, "conv_b", (D,), torch.float32)
+    if K > 1:
+        _opt(x_prev, "x_prev", (B, K - 1, D), act)
+    else:
+        x_prev, want_dx_prev = None, False
+    _req(du, "du", (B, L, D), act)
+    dev = x.device
+    g = {"dx": torch.empty((B, L, D), dtype=act, device=dev),
+         "dconv_w": torch.empty((D, K), dtype=torch.float32, device=dev),
+         "dconv_b": torch.empty((D,), dtype=torch.float32, device=dev) if want_dconv_b else None,
+         "dx_prev": torch.empty((B, K - 1, D), dtype=act, device=dev) if want_dx_prev else None}
+    prob = problem(B, L, D, 1, _dtype_code(x))
+    nbytes = int(lib.mssm_conv_bwd_workspace_bytes(ctypes.byref(prob), K))
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.mssm_conv_bwd(ctypes.byref(prob), K, _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(x_prev), _ptr(du),
+                             _ptr(g["dx"]), _ptr(g["dconv_w"]), _ptr(g["dconv_b"]), _ptr(g["dx_prev"]),
+                             _ptr(ws), nbytes, _stream(dev)))
+    return g
 
 
 def scan_bwd(u, delta, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, h0=None, dh_final=None,

@@ -83,4 +83,23 @@ hipError_t launch_bwd(const ScanArgs& a, hipStream_t s);
 
 hipError_t launch_step(const ScanArgs& a, float* state, hipStream_t s);
 
+// Backward of the conv1d + SiLU front end (a.u = x, a.conv_w, a.conv_b,
+// a.x_prev, a.d_conv as in launch_conv_fwd): time chunks of T steps, partial
+// sums of dw and dbias per (batch row, chunk) in the workspace.
+struct ConvBwdPlan {
+    int64_t T;           // steps per chunk
+    int64_t chunks;
+    int64_t workgroups;  // of the main kernel (must fit a 1-D grid)
+    size_t ws_bytes;
+};
+ConvBwdPlan plan_conv_bwd(int64_t B, int64_t L, int64_t D);
+struct ConvBwdIO {
+    const void* du;
+    void* dx;
+    void* dx_prev;       // nullable
+    float* dconv_w;
+    float* dconv_b;      // nullable
+};
+hipError_t launch_conv_bwd(const ScanArgs& a, const ConvBwdIO& io, hipStream_t s);
+
 }  // namespace mssm

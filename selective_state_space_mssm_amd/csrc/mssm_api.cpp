@@ -51,6 +51,17 @@ mssm::ScanArgs base_args(const mssm_problem* p) {
 
 mssm_status from_hip(hipError_t e) { return e == hipSuccess ? MSSM_OK : MSSM_ERR_HIP; }
 
+// The conv front end's backward: the problem without its state size.
+mssm_status check_conv_problem(const mssm_problem* p, int32_t d_conv) {
+    if (!p) return MSSM_ERR_NULL;
+    if (p->dtype != MSSM_F32 && p->dtype != MSSM_BF16) return MSSM_ERR_DTYPE;
+    if (p->batch < 1 || p->dim < 1 || p->seqlen < 1) return MSSM_ERR_SHAPE;
+    if (p->batch * p->dim >= (int64_t{1} << 31) || p->seqlen >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
+    if (d_conv < 1 || d_conv > MSSM_MAX_DCONV) return MSSM_ERR_SHAPE;
+    if (mssm::plan_conv_bwd(p->batch, p->seqlen, p->dim).workgroups >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
+    return MSSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +119,30 @@ mssm_status mssm_conv_scan_fwd(const mssm_problem* p, int32_t d_conv, const void
     a.d_conv = d_conv;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     return from_hip(mssm::launch_conv_fwd(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+size_t mssm_conv_bwd_workspace_bytes(const mssm_problem* p, int32_t d_conv) {
+    if (check_conv_problem(p, d_conv) != MSSM_OK) return 0;
+    return mssm::plan_conv_bwd(p->batch, p->seqlen, p->dim).ws_bytes;
+}
+
+mssm_status mssm_conv_bwd(const mssm_problem* p, int32_t d_conv, const void* x, const float* conv_w,
+                          const float* conv_b, const void* x_prev, const void* du, void* dx, float* dconv_w,
+                          float* dconv_b, void* dx_prev, void* workspace, size_t workspace_bytes,
+                          void* hip_stream) {
+    mssm_status st = check_conv_problem(p, d_conv);
+    if (st != MSSM_OK) return st;
+    if (!x || !conv_w || !du || !dx || !dconv_w) return MSSM_ERR_NULL;
+    st = check_align({x, conv_w, conv_b, x_prev, du, dx, dconv_w, dconv_b, dx_prev, workspace});
+    if (st != MSSM_OK) return st;
+    const size_t need = mssm::plan_conv_bwd(p->batch, p->seqlen, p->dim).ws_bytes;
+    if (!workspace || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
+
+    mssm::ScanArgs a = base_args(p);
+    a.u = x; a.conv_w = conv_w; a.conv_b = conv_b; a.x_prev = d_conv > 1 ? x_prev : nullptr; a.d_conv = d_conv;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    const mssm::ConvBwdIO io{du, dx, d_conv > 1 ? dx_prev : nullptr, dconv_w, dconv_b};
+    return from_hip(mssm::launch_conv_bwd(a, io, static_cast<hipStream_t>(hip_stream)));
 }
 
 mssm_status mssm_scan_bwd(const mssm_problem* p, const void* u, const void* delta, const float* A,

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 8, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), f"libmssm.so does not export {n}"
     assert sorted(mssm.EXPORTS) == names
@@ -141,6 +141,30 @@ def test_conv_front_end_validation():
     nws = lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(long_))
     assert conv_fwd(long_, ws=None) == -6
     assert conv_fwd(long_, ws=FAKE, wsb=nws - 1) == -6
+
+
+def test_conv_backward_validation():
+    v = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+
+    def cb(p, d_conv=4, x=FAKE, w=FAKE, b=None, xp=None, du=FAKE, dx=FAKE, dw=FAKE, db=None, dxp=None, ws=FAKE,
+           wsb=1 << 40):
+        return lib.mssm_conv_bwd(ctypes.byref(p) if p is not None else None, d_conv, v(x), v(w), v(b), v(xp), v(du),
+                                 v(dx), v(dw), v(db), v(dxp), v(ws), wsb, None)
+    assert cb(None) == -1
+    assert cb(good(dtype=3)) == -3
+    assert cb(good(L=0)) == -2
+    assert cb(good(N=12), x=None) == -1   # the state size plays no part: validation goes on to the pointers
+    for k in (0, 5):
+        assert cb(good(), d_conv=k) == -2
+    for k in ("x", "w", "du", "dx", "dw"):
+        assert cb(good(), **{k: None}) == -1, k
+    for k in ("x", "w", "b", "xp", "du", "dx", "dw", "db", "dxp"):
+        assert cb(good(), **{k: MIS}) == -5, k
+    nws = lib.mssm_conv_bwd_workspace_bytes(ctypes.byref(good()), 4)
+    assert nws > 0
+    assert cb(good(), ws=None) == -6
+    assert cb(good(), wsb=nws - 1) == -6
+    assert lib.mssm_conv_bwd_workspace_bytes(ctypes.byref(good()), 9) == 0
 
 
 def test_workspace_sizes_and_checks():

@@ -148,3 +148,98 @@ def test_full_size_2p8b_sampled(mssm):
     yr, hr, ur = oracle_run(sub)
     cht = torch.from_numpy(ch).cuda()
     check((y[:, :, cht], hf[:, cht], u[:, :, cht]), (yr, hr, ur), "bf16")
+
+
+# ---- backward of the front end (mssm_conv_bwd) --------------------------------------------------
+
+from helpers import GRAD_TOL, grad_err  # noqa: E402
+
+
+def conv_bwd_case(mssm, B, L, D, dtype, K, use=("x_prev", "conv_b"), seed=0):
+    w = workloads.custom(B, L, D, 16, dtype, seed=seed)
+    inp, t = make(w, K)
+    du_np = np.random.default_rng(seed + 1).standard_normal((B, L, D)).astype(np.float32)
+    du_st = workloads.bf16_bits(du_np) if dtype == "bf16" else du_np
+    du = workloads.to_torch({"u": du_st, "dtype": dtype}, "cuda", keys=("u",))["u"]
+    xp = t["x_prev"] if "x_prev" in use else None
+    g = mssm.conv_bwd(t["u"], t["conv_w"], du, conv_b=t["conv_b"] if "conv_b" in use else None, x_prev=xp,
+                      want_dx_prev=K > 1)
+    torch.cuda.synchronize()
+    f = workloads.as_float32(inp)
+    r = oracle.causal_conv_silu_bwd(f["u"], f["conv_w"], workloads.to_f32(du_st, dtype),
+                                    f["conv_b"] if "conv_b" in use else None, f["x_prev"] if "x_prev" in use else None)
+    return g, r
+
+
+def check_conv_grads(g, r, dtype, K):
+    tol = GRAD_TOL[dtype]
+    assert grad_err(to_np(g["dx"]), r["dx"]) <= tol
+    assert grad_err(to_np(g["dconv_w"]), r["dweight"]) <= tol
+    if g["dconv_b"] is not None:
+        assert grad_err(to_np(g["dconv_b"]), r["dbias"]) <= tol
+    if K > 1:
+        assert grad_err(to_np(g["dx_prev"]), r["dx_prev"]) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("K", [4, 3, 2, 1])
+def test_conv_backward_parity(mssm, dtype, K):
+    # 300 channels: a ragged second block of 256; 200 steps: four 64-step chunks, the last one short
+    print(f"[conv bwd] dtype={dtype} d_conv={K}", flush=True)
+    g, r = conv_bwd_case(mssm, 2, 200, 300, dtype, K, seed=130 + K)
+    check_conv_grads(g, r, dtype, K)
+
+
+@pytest.mark.parametrize("use", [(), ("x_prev",), ("conv_b",)])
+def test_conv_backward_optional_inputs(mssm, use):
+    print(f"[conv bwd] with {use}", flush=True)
+    g, r = conv_bwd_case(mssm, 1, 70, 64, "f32", 4, use=use, seed=140)
+    check_conv_grads(g, r, "f32", 4)
+
+
+@pytest.mark.parametrize("B,L,D", [(1, 3, 40), (3, 1, 64), (1, 70000, 64)])
+def test_conv_backward_edge_shapes(mssm, B, L, D):
+    # shorter than the window; a single step; long chunks (70,000 steps: 69 per chunk, 1,015 chunks)
+    print(f"[conv bwd] B={B} L={L} D={D}", flush=True)
+    g, r = conv_bwd_case(mssm, B, L, D, "f32", 4, seed=150)
+    check_conv_grads(g, r, "f32", 4)
+
+
+def test_conv_backward_full_size_2p8b_sampled(mssm):
+    """The 2.8B layer shape (B=4, L=4096, D=5120, bf16): dx, dconv_w and dconv_b
+    of sampled channels against the oracle on those channels."""
+    w = workloads.WORKLOADS["2.8b"]
+    inp, t = make(w, 4)
+    print(f"[conv bwd] {w} full size", flush=True)
+    du_st = workloads.bf16_bits(np.random.default_rng(7).standard_normal((w.B, w.L, w.D)).astype(np.float32))
+    du = workloads.to_torch({"u": du_st, "dtype": "bf16"}, "cuda", keys=("u",))["u"]
+    g = mssm.conv_bwd(t["u"], t["conv_w"], du, conv_b=t["conv_b"], x_prev=t["x_prev"], want_dx_prev=True)
+    torch.cuda.synchronize()
+    ch = np.unique(np.concatenate([[0, 255, 256, 5119], np.random.default_rng(8).choice(w.D, 40, replace=False)]))
+    sub = workloads.as_float32(workloads.select_channels(inp, ch))
+    r = oracle.causal_conv_silu_bwd(sub["u"], sub["conv_w"], workloads.to_f32(du_st, "bf16")[:, :, ch],
+                                    sub["conv_b"], sub["x_prev"])
+    cht = torch.from_numpy(ch).cuda()
+    sel = {"dx": g["dx"][:, :, cht], "dconv_w": g["dconv_w"][cht], "dconv_b": g["dconv_b"][cht],
+           "dx_prev": g["dx_prev"][:, :, cht]}
+    check_conv_grads(sel, r, "bf16", 4)
+
+
+def test_training_chain_through_the_front_end(mssm):
+    """Forward with the fused front end (u_out), the scan's backward on that
+    u, then the front end's backward: every gradient against the oracle's
+    chain (conv + SiLU, scan adjoint, conv adjoint)."""
+    w = workloads.custom(2, 150, 130, 16, "f32", seed=160, backward=True)
+    inp, t = make(w, 4)
+    print(f"[conv chain] {w}", flush=True)
+    y, hf, u = gpu_run(mssm, t)
+    gs = mssm.scan_bwd(u, t["delta"], t["A"], t["Bm"], t["Cm"], t["dy"], t["Dskip"], t["z"], t["dt_bias"])
+    gc = mssm.conv_bwd(t["u"], t["conv_w"], gs["du"], conv_b=t["conv_b"], x_prev=t["x_prev"], want_dx_prev=True)
+    torch.cuda.synchronize()
+    f = workloads.as_float32(inp)
+    ur = oracle.causal_conv_silu(f["u"], f["conv_w"], f["conv_b"], f["x_prev"])
+    rs = oracle.scan_bwd(ur, f["delta"], f["A"], f["Bm"], f["Cm"], f["dy"], f["Dskip"], f["z"], f["dt_bias"])
+    rc = oracle.causal_conv_silu_bwd(f["u"], f["conv_w"], rs["du"], f["conv_b"], f["x_prev"])
+    for k in ("ddelta", "dA", "dB", "dC", "dD", "dz", "ddt_bias"):
+        assert grad_err(to_np(gs[k]), rs[k]) <= GRAD_TOL["f32"], k
+    check_conv_grads(gc, rc, "f32", 4)
