@@ -197,9 +197,10 @@ def test_conv_backward_optional_inputs(mssm, use):
     check_conv_grads(g, r, "f32", 4)
 
 
-@pytest.mark.parametrize("B,L,D", [(1, 3, 40), (3, 1, 64), (1, 70000, 64)])
+@pytest.mark.parametrize("B,L,D", [(1, 3, 40), (3, 1, 64), (1, 70000, 64), (2, 100, 77)])
 def test_conv_backward_edge_shapes(mssm, B, L, D):
-    # shorter than the window; a single step; long chunks (70,000 steps: 69 per chunk, 1,015 chunks)
+    # shorter than the window; a single step; long chunks (70,000 steps: 69 per chunk, 1,015 chunks);
+    # an odd channel count (one channel per thread instead of pairs)
     print(f"[conv bwd] B={B} L={L} D={D}", flush=True)
     g, r = conv_bwd_case(mssm, B, L, D, "f32", 4, seed=150)
     check_conv_grads(g, r, "f32", 4)
