@@ -20,7 +20,7 @@ float32 arithmetic), inputs resident in HBM.  Prints one JSON line:
 
 ``--gpus N`` with N > 1 exits: this benchmark and the library run on one GPU.
 ``--extra`` adds the 130M-layer forward, the 2.8B-layer forward behind the fused
-causal conv1d + SiLU front end (x in place of u, d_conv = 4), the recurrent step at the 2.8B layer's
+causal conv1d + SiLU front end (x in place of u, d_conv = 4) and that front end's backward, the recurrent step at the 2.8B layer's
 width (B=4, D=5120, N=16: one decode step per call from Python, so the host's
 launch overhead, not the kernel, sets this rate; the kernel's own duration is
 in the kernel trace), the same step at B = 64 and 256 (batched decode, where the
@@ -68,6 +68,37 @@ def conv_fwd_bytes(w: workloads.Workload, d_conv: int = 4) -> int:
     """The forward behind the fused conv front end: x in place of u, plus the
     taps and bias (u itself never moves)."""
     return fwd_bytes(w) + 4 * w.D * d_conv + 4 * w.D
+
+
+def conv_bwd_bytes(w: workloads.Workload, d_conv: int = 4) -> int:
+    """Backward of the conv front end: reads x and du, writes dx; the taps,
+    bias and their gradients."""
+    act = 2 if w.dtype == "bf16" else 4
+    return 3 * w.B * w.L * w.D * act + 2 * 4 * w.D * (d_conv + 1)
+
+
+def time_conv_bwd(mssm, torch, w, reps=20, warmup=3):
+    """Median time of one mssm_conv_bwd call (both of its kernels), HIP events."""
+    inp = workloads.make_inputs(w)
+    inp.update(workloads.conv_front_end(w, 4))
+    t = workloads.to_torch(inp, "cuda", keys=("u", "conv_w", "conv_b", "x_prev"))
+    du = workloads.to_torch(dict(inp, u=inp["z"]), "cuda", keys=("u",))["u"]  # any (B, L, D) activations
+    del inp
+
+    def run():
+        mssm.conv_bwd(t["u"], t["conv_w"], du, conv_b=t["conv_b"], x_prev=t["x_prev"])
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
 
 
 def bwd_bytes(w: workloads.Workload) -> int:
@@ -345,6 +376,9 @@ def main():
         out["extra"]["conv_fwd_us"] = round(conv_us, 1)   # median kernel time, fused conv1d + SiLU front end
         out["extra"]["conv_fwd_GBs"] = round(conv_fwd_bytes(w) / conv_us / 1e3, 1)
         out["extra"]["conv_fwd_vs_plain_median"] = round(conv_us / (float(np.median(launch_ms)) * 1e3), 3)
+        cb_us = time_conv_bwd(mssm, torch, w)
+        out["extra"]["conv_bwd_us"] = round(cb_us, 1)   # median, backward of the conv front end
+        out["extra"]["conv_bwd_GBs"] = round(conv_bwd_bytes(w) / cb_us / 1e3, 1)
         st_us, st_gbs = time_step(mssm, torch, w)
         out.setdefault("extra", {})["step_us_per_call"] = round(st_us, 2)
         out["extra"]["step_GBs_per_call"] = round(st_gbs, 1)
