@@ -64,6 +64,15 @@ def test_parity(mssm, dtype, N, K):
     check(out, oracle_run(inp, h0=h0), dtype)
 
 
+@pytest.mark.parametrize("N", [1, 2, 8, 32])
+def test_other_state_sizes(mssm, N):
+    # every other layout the forward dispatches (1, 2, 8, 32 states), bf16, d_conv = 4
+    w = workloads.custom(2, 50, 130, N, "bf16", seed=170 + N)
+    print(f"[conv] {w}", flush=True)
+    inp, t = make(w, 4)
+    check(gpu_run(mssm, t), oracle_run(inp), "bf16")
+
+
 @pytest.mark.parametrize("use", [(), ("z",), ("x_prev",), ("conv_b", "Dskip"), ("dt_bias", "z", "conv_b")])
 def test_optional_inputs(mssm, use):
     w = workloads.custom(1, 40, 70, 16, "f32", seed=80)
