@@ -215,6 +215,26 @@ mssm_status mssm_step(const mssm_problem* p,
                       const float* Dskip, const void* z_t, const float* dt_bias,
                       float* state, void* y_t, void* hip_stream);
 
+/*
+ * One token through the conv1d + SiLU front end and the recurrent step, for
+ * streaming decode of a Mamba block: u_t = silu(conv_b + sum_k conv_w[d,k] *
+ * x_{t-d_conv+1+k}) with x_{t-d_conv+1} .. x_{t-1} read from conv_state, then
+ * exactly mssm_step with that u_t.  conv_state (B, d_conv - 1, D) in
+ * p->dtype, the previous inputs in time order (the x_prev of
+ * mssm_conv_scan_fwd; after a prefill call, the last d_conv - 1 rows of its
+ * history and x), is read and overwritten in place with x_{t-d_conv+2} .. x_t.
+ * Shapes otherwise as mssm_step (x_t replaces u_t); conv_w, conv_b, d_conv as
+ * in mssm_conv_scan_fwd (conv_state may be NULL only when d_conv = 1).
+ * Calling it L times equals one mssm_conv_scan_fwd over L steps with
+ * x_prev = conv_state and h0 = state.
+ */
+mssm_status mssm_conv_step(const mssm_problem* p, int32_t d_conv,
+                           const void* x_t, const float* conv_w, const float* conv_b, void* conv_state,
+                           const void* delta_t, const float* A,
+                           const void* Bm_t, const void* Cm_t,
+                           const float* Dskip, const void* z_t, const float* dt_bias,
+                           float* state, void* y_t, void* hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char* mssm_status_string(mssm_status s);
 

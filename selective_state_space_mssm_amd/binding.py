@@ -23,7 +23,7 @@ STATUS = {0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_SHAPE", -3: "MSSM_ERR
           -7: "MSSM_ERR_HIP"}
 EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd",
            "mssm_conv_scan_fwd", "mssm_conv_bwd_workspace_bytes", "mssm_conv_bwd", "mssm_scan_bwd", "mssm_step",
-           "mssm_status_string", "mssm_build_info"]
+           "mssm_conv_step", "mssm_status_string", "mssm_build_info"]
 MAX_DCONV = 4
 
 
@@ -61,6 +61,8 @@ def _open(path: str):
     lib.mssm_scan_bwd.restype = st
     lib.mssm_step.argtypes = [P] + [vp] * 10 + [vp]
     lib.mssm_step.restype = st
+    lib.mssm_conv_step.argtypes = [P, ctypes.c_int32] + [vp] * 13 + [vp]
+    lib.mssm_conv_step.restype = st
     lib.mssm_status_string.argtypes = [st]
     lib.mssm_status_string.restype = ctypes.c_char_p
     lib.mssm_build_info.argtypes = []
@@ -322,4 +324,45 @@ def step(u_t, delta_t, A, Bm_t, Cm_t, state, Dskip=None, z_t=None, dt_bias=None,
     _check(lib.mssm_step(ctypes.byref(prob), _ptr(u_t), _ptr(delta_t), _ptr(A), _ptr(Bm_t), _ptr(Cm_t),
                          _ptr(Dskip), _ptr(z_t), _ptr(dt_bias), _ptr(state), _ptr(y_t),
                          _stream(u_t.device)))
+    return y_t
+
+
+def conv_step(x_t, conv_w, conv_state, delta_t, A, Bm_t, Cm_t, state, Dskip=None, z_t=None, dt_bias=None,
+              conv_b=None, delta_softplus=True, y_t=None):
+    """One token through the conv1d + SiLU front end and the recurrent step.
+    x_t, delta_t, z_t: (B, D); Bm_t, Cm_t: (B, N); conv_w (D, d_conv) or
+    (D, 1, d_conv) float32; conv_state (B, d_conv - 1, D) (the previous inputs,
+    shifted in place), state (B, D, N) float32 updated in place.  Returns y_t."""
+    act = x_t.dtype
+    B, D = x_t.shape
+    N = A.shape[1]
+    if conv_w is None or conv_w.dim() not in (2, 3) or conv_w.shape[0] != D:
+        raise ValueError("conv_w must be (D, d_conv) or (D, 1, d_conv)")
+    K = conv_w.shape[-1]
+    if conv_w.dim() == 3:
+        _req(conv_w, "conv_w", (D, 1, K), torch.float32)
+        conv_w = conv_w.view(D, K)
+    if not 1 <= K <= MAX_DCONV:
+        raise ValueError(f"d_conv = {K} not in 1..{MAX_DCONV}")
+    _req(x_t, "x_t", (B, D), act)
+    _req(conv_w, "conv_w", (D, K), torch.float32)
+    _opt(conv_b, "conv_b", (D,), torch.float32)
+    if K > 1:
+        _req(conv_state, "conv_state", (B, K - 1, D), act)
+    else:
+        conv_state = None
+    _req(delta_t, "delta_t", (B, D), act)
+    _req(A, "A", (D, N), torch.float32)
+    _req(Bm_t, "Bm_t", (B, N), act)
+    _req(Cm_t, "Cm_t", (B, N), act)
+    _req(state, "state", (B, D, N), torch.float32)
+    _opt(Dskip, "Dskip", (D,), torch.float32)
+    _opt(z_t, "z_t", (B, D), act)
+    _opt(dt_bias, "dt_bias", (D,), torch.float32)
+    if y_t is None:
+        y_t = torch.empty((B, D), dtype=act, device=x_t.device)
+    prob = problem(B, 1, D, N, _dtype_code(x_t), delta_softplus)
+    _check(lib.mssm_conv_step(ctypes.byref(prob), K, _ptr(x_t), _ptr(conv_w), _ptr(conv_b), _ptr(conv_state),
+                              _ptr(delta_t), _ptr(A), _ptr(Bm_t), _ptr(Cm_t), _ptr(Dskip), _ptr(z_t),
+                              _ptr(dt_bias), _ptr(state), _ptr(y_t), _stream(x_t.device)))
     return y_t

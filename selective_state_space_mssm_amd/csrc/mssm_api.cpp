@@ -187,6 +187,25 @@ mssm_status mssm_step(const mssm_problem* p, const void* u_t, const void* delta_
     return from_hip(mssm::launch_step(a, state, static_cast<hipStream_t>(hip_stream)));
 }
 
+mssm_status mssm_conv_step(const mssm_problem* p, int32_t d_conv, const void* x_t, const float* conv_w,
+                           const float* conv_b, void* conv_state, const void* delta_t, const float* A,
+                           const void* Bm_t, const void* Cm_t, const float* Dskip, const void* z_t,
+                           const float* dt_bias, float* state, void* y_t, void* hip_stream) {
+    mssm_status st = check_problem(p, false);
+    if (st != MSSM_OK) return st;
+    if (d_conv < 1 || d_conv > MSSM_MAX_DCONV) return MSSM_ERR_SHAPE;
+    if (!x_t || !conv_w || (d_conv > 1 && !conv_state) || !delta_t || !A || !Bm_t || !Cm_t || !state || !y_t)
+        return MSSM_ERR_NULL;
+    st = check_align({x_t, conv_w, conv_b, conv_state, delta_t, A, Bm_t, Cm_t, Dskip, z_t, dt_bias, state, y_t});
+    if (st != MSSM_OK) return st;
+    mssm::ScanArgs a = base_args(p);
+    a.L = 1;
+    a.u = x_t; a.delta = delta_t; a.z = z_t; a.Bm = Bm_t; a.Cm = Cm_t;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.y = y_t;
+    a.conv_w = conv_w; a.conv_b = conv_b; a.x_prev = d_conv > 1 ? conv_state : nullptr; a.d_conv = d_conv;
+    return from_hip(mssm::launch_step(a, state, static_cast<hipStream_t>(hip_stream)));
+}
+
 const char* mssm_status_string(mssm_status s) {
     switch (s) {
         case MSSM_OK: return "MSSM_OK: success";

@@ -8,6 +8,13 @@
 // N < 4), each owning 4 consecutive states as one 16-byte access, so a wave
 // reads and writes one contiguous stretch of the state; the row's lanes add
 // their partial readouts with lane shuffles and the first one stores y.
+//
+// With the fused conv front end (mssm_conv_step), the step's u is formed from
+// x_t and the conv state, the d_conv - 1 previous inputs (B, d_conv - 1, D):
+// u = silu(bias + sum_k w_k x_{t-3+k}), taps zero-padded to 4 as in the
+// forward; the row's first lane then shifts x_t into the conv state.  The
+// lanes of a row sit in one wave, so all of them have read the old state
+// before it is overwritten.
 #include "device_common.h"
 #include "launch.h"
 
@@ -27,9 +34,14 @@ struct StepKArgs {
     void* y;
     int64_t B, D;
     int32_t softplus;
+    // fused conv front end (u is then x_t)
+    const float* conv_w;   // (D, K)
+    const float* conv_b;   // (D) nullable
+    void* conv_state;      // (B, K - 1, D), in/out
+    int32_t K;
 };
 
-template <typename T, int N>
+template <typename T, int N, bool CONV>
 __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
     constexpr int V = N >= 4 ? 4 : N;  // states per lane
     constexpr int R = N / V;           // lanes per (b, d) row: a power of two dividing 64
@@ -41,7 +53,34 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
     const int n0 = q * V;
     const T* __restrict__ Bm = static_cast<const T*>(a.Bm) + b * N + n0;
     const T* __restrict__ Cm = static_cast<const T*>(a.Cm) + b * N + n0;
-    const float uu = load_act(static_cast<const T*>(a.u), i);
+    float uu = load_act(static_cast<const T*>(a.u), i);
+    if constexpr (CONV) {
+        // the row's first lane alone reads and shifts the conv state (its loads
+        // and stores of one address then come from one thread, in program
+        // order); the row's other lanes take c from it
+        constexpr int kTaps = 4;
+        float c = 0.0f;
+        if (q == 0) {
+            const int K = a.K;
+            T* cs = static_cast<T*>(a.conv_state) + b * (K - 1) * a.D + d;  // (b, 0, d)
+            float xs[kTaps - 1];  // x_{t-3} .. x_{t-1}; the state holds x_{t-K+1} .. x_{t-1} in its K - 1 rows
+#pragma unroll
+            for (int k = 0; k < kTaps - 1; ++k)
+                xs[k] = k >= kTaps - K ? load_act(cs, (k - (kTaps - K)) * a.D) : 0.0f;
+            c = a.conv_b ? a.conv_b[d] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < kTaps - 1; ++k)
+                if (k >= kTaps - K) c = __builtin_fmaf(a.conv_w[d * K + k - (kTaps - K)], xs[k], c);
+            c = __builtin_fmaf(a.conv_w[d * K + K - 1], uu, c);
+            // shift x_t in: row j <- row j + 1, the last row <- x_t
+#pragma unroll
+            for (int k = kTaps - 1 - (kTaps - 2); k < kTaps - 1; ++k)
+                if (k - 1 >= kTaps - K) store_act(cs, (k - 1 - (kTaps - K)) * a.D, xs[k]);
+            if (K > 1) store_act(cs, (K - 2) * a.D, uu);
+        }
+        if constexpr (R > 1) c = __shfl(c, static_cast<int>(threadIdx.x & 63) - q);
+        uu = silu(c);
+    }
     const float x = load_act(static_cast<const T*>(a.delta), i) + (a.dt_bias ? a.dt_bias[d] : 0.0f);
     const float dt = a.softplus ? softplus(x) : x;
     const float du = dt * uu;
@@ -78,18 +117,18 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
     }
 }
 
-template <typename T>
+template <typename T, bool CONV>
 hipError_t dispatch(const StepKArgs& k, int64_t N, hipStream_t st) {
     const int64_t lanes = k.B * k.D * (N >= 4 ? N / 4 : 1);  // N/4 lanes per (b, d) row
     const dim3 grid(static_cast<unsigned>((lanes + 255) / 256));
     switch (N) {
-        case 1: hipLaunchKernelGGL((scan_step_kernel<T, 1>), grid, dim3(256), 0, st, k); break;
-        case 2: hipLaunchKernelGGL((scan_step_kernel<T, 2>), grid, dim3(256), 0, st, k); break;
-        case 4: hipLaunchKernelGGL((scan_step_kernel<T, 4>), grid, dim3(256), 0, st, k); break;
-        case 8: hipLaunchKernelGGL((scan_step_kernel<T, 8>), grid, dim3(256), 0, st, k); break;
-        case 16: hipLaunchKernelGGL((scan_step_kernel<T, 16>), grid, dim3(256), 0, st, k); break;
-        case 32: hipLaunchKernelGGL((scan_step_kernel<T, 32>), grid, dim3(256), 0, st, k); break;
-        case 64: hipLaunchKernelGGL((scan_step_kernel<T, 64>), grid, dim3(256), 0, st, k); break;
+        case 1: hipLaunchKernelGGL((scan_step_kernel<T, 1, CONV>), grid, dim3(256), 0, st, k); break;
+        case 2: hipLaunchKernelGGL((scan_step_kernel<T, 2, CONV>), grid, dim3(256), 0, st, k); break;
+        case 4: hipLaunchKernelGGL((scan_step_kernel<T, 4, CONV>), grid, dim3(256), 0, st, k); break;
+        case 8: hipLaunchKernelGGL((scan_step_kernel<T, 8, CONV>), grid, dim3(256), 0, st, k); break;
+        case 16: hipLaunchKernelGGL((scan_step_kernel<T, 16, CONV>), grid, dim3(256), 0, st, k); break;
+        case 32: hipLaunchKernelGGL((scan_step_kernel<T, 32, CONV>), grid, dim3(256), 0, st, k); break;
+        case 64: hipLaunchKernelGGL((scan_step_kernel<T, 64, CONV>), grid, dim3(256), 0, st, k); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -102,7 +141,10 @@ hipError_t launch_step(const ScanArgs& s, float* state, hipStream_t st) {
     k.u = s.u; k.delta = s.delta; k.z = s.z; k.Bm = s.Bm; k.Cm = s.Cm;
     k.A = s.A; k.Dskip = s.Dskip; k.dt_bias = s.dt_bias;
     k.state = state; k.y = s.y; k.B = s.B; k.D = s.D; k.softplus = s.softplus;
-    return s.dtype == 1 ? dispatch<uint16_t>(k, s.N, st) : dispatch<float>(k, s.N, st);
+    k.conv_w = s.conv_w; k.conv_b = s.conv_b; k.conv_state = const_cast<void*>(s.x_prev); k.K = s.d_conv;
+    if (s.conv_w)
+        return s.dtype == 1 ? dispatch<uint16_t, true>(k, s.N, st) : dispatch<float, true>(k, s.N, st);
+    return s.dtype == 1 ? dispatch<uint16_t, false>(k, s.N, st) : dispatch<float, false>(k, s.N, st);
 }
 
 }  // namespace mssm

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), f"libmssm.so does not export {n}"
     assert sorted(mssm.EXPORTS) == names
@@ -165,6 +165,25 @@ def test_conv_backward_validation():
     assert cb(good(), ws=None) == -6
     assert cb(good(), wsb=nws - 1) == -6
     assert lib.mssm_conv_bwd_workspace_bytes(ctypes.byref(good()), 9) == 0
+
+
+def test_conv_step_validation():
+    v = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+
+    def cs(p, d_conv=4, **kw):
+        names = ["x_t", "conv_w", "conv_b", "conv_state", "delta_t", "A", "Bm_t", "Cm_t", "Dskip", "z_t", "dt_bias",
+                 "state", "y_t"]
+        req = {"x_t", "conv_w", "conv_state", "delta_t", "A", "Bm_t", "Cm_t", "state", "y_t"}
+        args = [v(kw.get(n, FAKE if n in req else None)) for n in names]
+        return lib.mssm_conv_step(ctypes.byref(p) if p is not None else None, d_conv, *args, None)
+    assert cs(None) == -1
+    assert cs(good(N=12)) == -4
+    for k in (0, 5):
+        assert cs(good(), d_conv=k) == -2
+    for k in ("x_t", "conv_w", "conv_state", "delta_t", "A", "Bm_t", "Cm_t", "state", "y_t"):
+        assert cs(good(), **{k: None}) == -1, k
+    for k in ("x_t", "conv_w", "conv_b", "conv_state", "state", "y_t"):
+        assert cs(good(), **{k: MIS}) == -5, k
 
 
 def test_workspace_sizes_and_checks():

@@ -253,3 +253,55 @@ def test_training_chain_through_the_front_end(mssm):
     for k in ("ddelta", "dA", "dB", "dC", "dD", "dz", "ddt_bias"):
         assert grad_err(to_np(gs[k]), rs[k]) <= GRAD_TOL["f32"], k
     check_conv_grads(gc, rc, "f32", 4)
+
+
+# ---- decode through the front end (mssm_conv_step) ----------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,K", [(16, 4), (4, 3), (64, 2), (2, 4), (16, 1)])
+def test_conv_step_decode(mssm, dtype, N, K):
+    """Token by token through mssm_conv_step equals the oracle's one scan
+    behind the conv over the whole sequence; the conv state ends as the last
+    d_conv - 1 inputs (exactly: it only moves stored values)."""
+    w = workloads.custom(3, 24, 100, N, dtype, seed=180 + N + K)
+    inp, t = make(w, K)
+    print(f"[conv step] {w} d_conv={K}", flush=True)
+    h0 = np.random.default_rng(9).standard_normal((w.B, w.D, N)).astype(np.float32)
+    state = torch.from_numpy(h0).cuda()
+    cst = t["x_prev"].clone() if K > 1 else None
+    ys = []
+    for i in range(w.L):
+        ys.append(mssm.conv_step(t["u"][:, i].contiguous(), t["conv_w"], cst, t["delta"][:, i].contiguous(), t["A"],
+                                 t["Bm"][:, i].contiguous(), t["Cm"][:, i].contiguous(), state, t["Dskip"],
+                                 t["z"][:, i].contiguous(), t["dt_bias"], conv_b=t["conv_b"]))
+    torch.cuda.synchronize()
+    yr, hr, _ = oracle_run(inp, h0=h0)
+    tol = FWD_TOL[dtype]
+    assert fwd_err(to_np(torch.stack(ys, 1)), yr) <= tol
+    assert fwd_err(to_np(state), hr) <= tol
+    if K > 1:
+        assert torch.equal(cst, torch.cat([t["x_prev"], t["u"]], 1)[:, -(K - 1):])
+
+
+def test_prefill_then_decode(mssm):
+    """A prefill with mssm_conv_scan_fwd (state in place), the conv state taken
+    from its inputs, then decode steps: equal to one scan over all tokens."""
+    w = workloads.custom(2, 40, 192, 16, "bf16", seed=190)
+    inp, t = make(w, 4)
+    print(f"[conv prefill+decode] {w}", flush=True)
+    state = torch.zeros((w.B, w.D, 16), device="cuda")
+    P = 30
+    y0, _, _ = mssm.conv_scan_fwd(t["u"][:, :P].contiguous(), t["conv_w"], t["delta"][:, :P].contiguous(), t["A"],
+                                  t["Bm"][:, :P].contiguous(), t["Cm"][:, :P].contiguous(), t["Dskip"],
+                                  t["z"][:, :P].contiguous(), t["dt_bias"], state, conv_b=t["conv_b"],
+                                  x_prev=t["x_prev"], h_final=state)
+    cst = torch.cat([t["x_prev"], t["u"][:, :P]], 1)[:, -3:].contiguous()
+    ys = [y0]
+    for i in range(P, w.L):
+        ys.append(mssm.conv_step(t["u"][:, i].contiguous(), t["conv_w"], cst, t["delta"][:, i].contiguous(), t["A"],
+                                 t["Bm"][:, i].contiguous(), t["Cm"][:, i].contiguous(), state, t["Dskip"],
+                                 t["z"][:, i].contiguous(), t["dt_bias"], conv_b=t["conv_b"])[:, None])
+    torch.cuda.synchronize()
+    yr, hr, _ = oracle_run(inp)
+    assert fwd_err(to_np(torch.cat(ys, 1)), yr) <= FWD_TOL["bf16"]
+    assert fwd_err(to_np(state), hr) <= FWD_TOL["bf16"]
