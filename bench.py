@@ -24,7 +24,7 @@ causal conv1d + SiLU front end (x in place of u, d_conv = 4) and that front end'
 width (B=4, D=5120, N=16: one decode step per call from Python, so the host's
 launch overhead, not the kernel, sets this rate; the kernel's own duration is
 in the kernel trace), the same step at B = 64 and 256 (batched decode, where the
-state's read and write set the rate) and the training-workload backward
+state's read and write set the rate), the step behind the conv front end at B = 256 and the training-workload backward
 (``--long`` also the 1M-step forward).
 ``--copy-probe`` runs a plain device copy of 1 GiB first (counter calibration).
 """
@@ -229,6 +229,31 @@ def time_bwd(mssm, torch, w, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def time_conv_step(mssm, torch, w, batch, reps=100):
+    """mssm_conv_step (conv front end + recurrent step, d_conv = 4) at batch
+    `batch`, the workload's width: median us per call (HIP events)."""
+    ww = workloads.custom(batch, 1, w.D, w.N, w.dtype, seed=w.seed)
+    inp = workloads.make_inputs(ww)
+    inp.update(workloads.conv_front_end(ww, 4))
+    t = workloads.to_torch(inp, "cuda")
+    state = torch.zeros((ww.B, ww.D, ww.N), dtype=torch.float32, device="cuda")
+    cst = t["x_prev"].clone()
+    args = [t["u"][:, 0].contiguous(), t["conv_w"], cst, t["delta"][:, 0].contiguous(), t["A"],
+            t["Bm"][:, 0].contiguous(), t["Cm"][:, 0].contiguous(), state, t["Dskip"], t["z"][:, 0].contiguous(),
+            t["dt_bias"]]
+    y_t = torch.empty_like(args[0])
+    for _ in range(10):
+        mssm.conv_step(*args, conv_b=t["conv_b"], y_t=y_t)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        mssm.conv_step(*args, conv_b=t["conv_b"], y_t=y_t)
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+
 def time_step(mssm, torch, w, reps=200, batch=None):
     """One recurrent step (decode) at the workload's width: (B, D) inputs, the
     (B, D, N) float32 state updated in place; `batch` overrides B (batched
@@ -386,6 +411,7 @@ def main():
             st_us, st_gbs = time_step(mssm, torch, w, reps=100, batch=bb)
             out["extra"][f"step_B{bb}_us_per_call"] = round(st_us, 2)
             out["extra"][f"step_B{bb}_GBs"] = round(st_gbs, 1)
+        out["extra"]["conv_step_B256_us"] = round(time_conv_step(mssm, torch, w, 256), 2)  # conv front end + step
         tw = workloads.WORKLOADS["train"]
         tb = time_bwd(mssm, torch, tw, 10, 2)
         out.setdefault("extra", {})["train_bwd_us"] = round(tb * 1e6, 1)
