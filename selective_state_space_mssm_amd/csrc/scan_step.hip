@@ -11,10 +11,11 @@
 //
 // With the fused conv front end (mssm_conv_step), the step's u is formed from
 // x_t and the conv state, the d_conv - 1 previous inputs (B, d_conv - 1, D):
-// u = silu(bias + sum_k w_k x_{t-3+k}), taps zero-padded to 4 as in the
-// forward; the row's first lane then shifts x_t into the conv state.  The
-// lanes of a row sit in one wave, so all of them have read the old state
-// before it is overwritten.
+// u = silu(bias + sum_k w_k x_{t-d_conv+1+k}), and x_t is shifted into the
+// conv state in place.  Every address of the conv state is read and written
+// by one lane (lane q owns row q when a row has four lanes or more, else the
+// row's first lane owns all rows), so its read precedes its write in program
+// order.
 #include "device_common.h"
 #include "launch.h"
 
@@ -60,7 +61,21 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
         // order); the row's other lanes take c from it
         constexpr int kTaps = 4;
         float c = 0.0f;
-        if (q == 0) {
+        if constexpr (R >= kTaps) {
+            // four or more lanes per row: lane q < K takes tap q, whose input is
+            // conv-state row q (x_t for q = K - 1); lane q < K - 1 then writes
+            // row q from lane q + 1's input (each state address is read and
+            // written by one lane); the products are summed over the row
+            const int K = a.K;
+            T* cs = static_cast<T*>(a.conv_state) + b * (K - 1) * a.D + d;  // (b, 0, d)
+            const float in = q < K - 1 ? load_act(cs, q * a.D) : uu;
+            float prod = q < K ? a.conv_w[d * K + q] * in : 0.0f;
+            const float next = __shfl(in, static_cast<int>(threadIdx.x & 63) + 1);
+            if (q < K - 1) store_act(cs, q * a.D, next);
+#pragma unroll
+            for (int m = 1; m < R; m <<= 1) prod += __shfl_xor(prod, m);
+            c = (a.conv_b ? a.conv_b[d] : 0.0f) + prod;
+        } else if (q == 0) {
             const int K = a.K;
             T* cs = static_cast<T*>(a.conv_state) + b * (K - 1) * a.D + d;  // (b, 0, d)
             float xs[kTaps - 1];  // x_{t-3} .. x_{t-1}; the state holds x_{t-K+1} .. x_{t-1} in its K - 1 rows
@@ -78,7 +93,7 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
                 if (k - 1 >= kTaps - K) store_act(cs, (k - 1 - (kTaps - K)) * a.D, xs[k]);
             if (K > 1) store_act(cs, (K - 2) * a.D, uu);
         }
-        if constexpr (R > 1) c = __shfl(c, static_cast<int>(threadIdx.x & 63) - q);
+        if constexpr (R > 1 && R < kTaps) c = __shfl(c, static_cast<int>(threadIdx.x & 63) - q);
         uu = silu(c);
     }
     const float x = load_act(static_cast<const T*>(a.delta), i) + (a.dt_bias ? a.dt_bias[d] : 0.0f);
