@@ -35,6 +35,7 @@ FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N) {
 }
 
 hipError_t launch_fwd(const ScanArgs& s, hipStream_t st) {
+    if (use_tokens(s.B, s.L, s.D)) return launch_tokens(s, st);  // a few tokens: the state moves once (scan_step.hip)
     const FwdPlan pl = plan_fwd(s.B, s.L, s.D, s.N);
     const PreOut none{};
     return s.dtype == 1 ? dispatch_n<uint16_t, false, false>(s, pl, s.workspace, none, st)

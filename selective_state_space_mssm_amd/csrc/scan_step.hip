@@ -132,6 +132,79 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
     }
 }
 
+// Short sequences: the forward over L steps with the step's mapping (N/4
+// lanes per (b, d) row, 4 states per lane, rows of the state contiguous),
+// the state in registers from h0 to h_final, so it moves once per call
+// rather than once per token; inputs at (b, t, d) and (b, t, n) as the
+// forward takes them.  The forward kernel's tile pipeline needs whole 16-step
+// tiles to pay for itself; for a few tokens over many (b, d) rows this is
+// the faster form.
+struct TokKArgs {
+    const void* u;
+    const void* delta;
+    const void* z;
+    const void* Bm;
+    const void* Cm;
+    const float* A;
+    const float* Dskip;
+    const float* dt_bias;
+    const float* h0;      // nullable: zeros
+    float* h_final;       // nullable; may be h0
+    void* y;
+    int64_t B, L, D;
+    int32_t softplus;
+};
+
+template <typename T, int N>
+__global__ __launch_bounds__(256) void scan_tokens_kernel(TokKArgs a) {
+    constexpr int V = N >= 4 ? 4 : N;
+    constexpr int R = N / V;
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t i = g / R;  // (b, d); a row's lanes are all in range or all out
+    const int q = static_cast<int>(g % R);
+    if (i >= a.B * a.D) return;
+    const int64_t b = i / a.D, d = i % a.D;
+    const int n0 = q * V;
+    const int64_t D = a.D, L = a.L;
+    float A2[V], h[V];
+#pragma unroll
+    for (int n = 0; n < V; ++n) {
+        A2[n] = a.A[d * N + n0 + n] * kLog2e;
+        h[n] = a.h0 ? a.h0[i * N + n0 + n] : 0.0f;
+    }
+    const float bias = a.dt_bias ? a.dt_bias[d] : 0.0f;
+    const float Dk = a.Dskip ? a.Dskip[d] : 0.0f;
+    const T* __restrict__ u = static_cast<const T*>(a.u) + b * L * D + d;
+    const T* __restrict__ dl = static_cast<const T*>(a.delta) + b * L * D + d;
+    const T* __restrict__ z = a.z ? static_cast<const T*>(a.z) + b * L * D + d : nullptr;
+    T* __restrict__ y = static_cast<T*>(a.y) + b * L * D + d;
+    const T* __restrict__ Bm = static_cast<const T*>(a.Bm) + b * L * N + n0;
+    const T* __restrict__ Cm = static_cast<const T*>(a.Cm) + b * L * N + n0;
+    for (int64_t t = 0; t < L; ++t) {
+        const float uu = load_act(u, t * D);
+        const float x = load_act(dl, t * D) + bias;
+        const float dt = a.softplus ? softplus(x) : x;
+        const float du = dt * uu;
+        float s = 0.0f;
+#pragma unroll
+        for (int n = 0; n < V; ++n) {
+            h[n] = __builtin_fmaf(fast_exp2(dt * A2[n]), h[n], du * load_act(Bm, t * N + n));  // A2 = A log2(e)
+            s = __builtin_fmaf(load_act(Cm, t * N + n), h[n], s);
+        }
+#pragma unroll
+        for (int m = 1; m < R; m <<= 1) s += __shfl_xor(s, m);
+        if (q == 0) {
+            s = __builtin_fmaf(Dk, uu, s);
+            if (z) s *= silu(load_act(z, t * D));
+            store_act(y, t * D, s);
+        }
+    }
+    if (a.h_final) {
+#pragma unroll
+        for (int n = 0; n < V; ++n) a.h_final[i * N + n0 + n] = h[n];
+    }
+}
+
 template <typename T, bool CONV>
 hipError_t dispatch(const StepKArgs& k, int64_t N, hipStream_t st) {
     const int64_t lanes = k.B * k.D * (N >= 4 ? N / 4 : 1);  // N/4 lanes per (b, d) row
@@ -150,6 +223,31 @@ hipError_t dispatch(const StepKArgs& k, int64_t N, hipStream_t st) {
 }
 
 }  // namespace
+
+template <typename T>
+hipError_t dispatch_tokens(const TokKArgs& k, int64_t N, hipStream_t st) {
+    const int64_t lanes = k.B * k.D * (N >= 4 ? N / 4 : 1);
+    const dim3 grid(static_cast<unsigned>((lanes + 255) / 256));
+    switch (N) {
+        case 1: hipLaunchKernelGGL((scan_tokens_kernel<T, 1>), grid, dim3(256), 0, st, k); break;
+        case 2: hipLaunchKernelGGL((scan_tokens_kernel<T, 2>), grid, dim3(256), 0, st, k); break;
+        case 4: hipLaunchKernelGGL((scan_tokens_kernel<T, 4>), grid, dim3(256), 0, st, k); break;
+        case 8: hipLaunchKernelGGL((scan_tokens_kernel<T, 8>), grid, dim3(256), 0, st, k); break;
+        case 16: hipLaunchKernelGGL((scan_tokens_kernel<T, 16>), grid, dim3(256), 0, st, k); break;
+        case 32: hipLaunchKernelGGL((scan_tokens_kernel<T, 32>), grid, dim3(256), 0, st, k); break;
+        case 64: hipLaunchKernelGGL((scan_tokens_kernel<T, 64>), grid, dim3(256), 0, st, k); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_tokens(const ScanArgs& s, hipStream_t st) {
+    TokKArgs k{};
+    k.u = s.u; k.delta = s.delta; k.z = s.z; k.Bm = s.Bm; k.Cm = s.Cm;
+    k.A = s.A; k.Dskip = s.Dskip; k.dt_bias = s.dt_bias; k.h0 = s.h0; k.h_final = s.h_final; k.y = s.y;
+    k.B = s.B; k.L = s.L; k.D = s.D; k.softplus = s.softplus;
+    return s.dtype == 1 ? dispatch_tokens<uint16_t>(k, s.N, st) : dispatch_tokens<float>(k, s.N, st);
+}
 
 hipError_t launch_step(const ScanArgs& s, float* state, hipStream_t st) {
     StepKArgs k{};

@@ -52,14 +52,16 @@ def test_tiny_workload(mssm):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [(2, 37, 70), (3, 16, 64), (1, 1, 1), (1, 200, 130), (2, 5, 200)])
+@pytest.mark.parametrize("shape", [(2, 37, 70), (3, 16, 64), (1, 1, 1), (1, 200, 130), (2, 5, 200),
+                                   (2, 101, 70), (3, 80, 64), (1, 65, 1), (2, 69, 200)])
 def test_ragged_shapes_all_options(mssm, shape, dtype):
+    # up to 64 steps the short-sequence path runs, above it the tiled kernel (the same remainders mod 16)
     B, L, D = shape
     check(mssm, workloads.custom(B, L, D, 16, dtype, seed=L + D), h0=True)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("L", [18, 23, 30, 47])
+@pytest.mark.parametrize("L", [82, 87, 94, 111])
 def test_ragged_readout_groups(mssm, L, dtype):
     # the partial readouts of a tile are formed in groups of 2 (fp32) or 4
     # (bf16) steps: a last tile of 2, 7, 14 or 15 steps ends inside a group
@@ -68,13 +70,13 @@ def test_ragged_readout_groups(mssm, L, dtype):
 
 @pytest.mark.parametrize("use", [(), ("z",), ("Dskip",), ("dt_bias",), ("Dskip", "dt_bias")])
 def test_optional_inputs(mssm, use):
-    check(mssm, workloads.custom(2, 45, 80, 16, "f32", seed=11), h0=False, use=use)
+    check(mssm, workloads.custom(2, 109, 80, 16, "f32", seed=11), h0=False, use=use)
 
 
 def test_softplus_off(mssm):
     # flag off: Delta = delta + dt_bias is used as is.  Keep it positive (as a
     # step size is) so the recurrence stays contractive and float32 finite.
-    w = workloads.custom(2, 40, 70, 16, "f32", seed=12)
+    w = workloads.custom(2, 104, 70, 16, "f32", seed=12)
     inp = workloads.make_inputs(w)
     inp["delta"] = (0.05 * np.abs(inp["delta"])).astype(np.float32)
     inp["dt_bias"] = np.full(w.D, 0.01, np.float32)
@@ -87,14 +89,14 @@ def test_softplus_off(mssm):
 
 @pytest.mark.parametrize("N", [1, 2, 4, 8, 32, 64])
 def test_state_sizes(mssm, N):
-    check(mssm, workloads.custom(2, 50, 90, N, "f32", seed=N), h0=True)
+    check(mssm, workloads.custom(2, 114, 90, N, "f32", seed=N), h0=True)
 
 
 @pytest.mark.parametrize("N", [1, 2, 4, 8, 32, 64])
 def test_state_sizes_bf16(mssm, N):
     # bf16 rows of Bm/Cm per lane (one value for N = 1), readout groups of
     # 4 steps (2 with 8 states per wave), a last tile of 3 steps
-    check(mssm, workloads.custom(2, 51, 90, N, "bf16", seed=N + 7), h0=True)
+    check(mssm, workloads.custom(2, 115, 90, N, "bf16", seed=N + 7), h0=True)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -106,7 +108,7 @@ def test_chunked_carry_schedule(mssm, dtype):
     check(mssm, workloads.custom(B, L, D, 16, dtype, seed=21), h0=True)
 
 
-@pytest.mark.parametrize("shape,dtype", [((5, 100, 3840), "f32"), ((3, 333, 5760), "bf16"), ((4, 37, 4160), "f32")])
+@pytest.mark.parametrize("shape,dtype", [((5, 100, 3840), "f32"), ((3, 333, 5760), "bf16"), ((4, 101, 4160), "f32")])
 def test_balanced_schedule(mssm, shape, dtype):
     # more channel blocks than CUs but not a multiple of them: the persistent
     # balanced schedule splits blocks between workgroups mid-sequence and hands
@@ -128,7 +130,7 @@ def test_schedules_other_state_sizes(mssm, N):
     # the chunked (1 block, L >= 2048) and the balanced (270 blocks) schedules
     # with one state per wave (N = 1, a single wave), 2 and 16 states per wave
     check(mssm, workloads.custom(1, 2100, 40, N, "f32", seed=N + 90), h0=True)
-    check(mssm, workloads.custom(3, 40, 5760, N, "bf16", seed=N + 91), h0=True)
+    check(mssm, workloads.custom(3, 104, 5760, N, "bf16", seed=N + 91), h0=True)
 
 
 def test_130m_layer_full(mssm):
@@ -175,10 +177,11 @@ def test_bitwise_deterministic(mssm):
 
 
 def test_split_scan_equals_one_scan(mssm):
-    w = workloads.custom(2, 160, 96, 16, "f32", seed=6)
+    # both parts longer than the short-sequence path (64 steps), so all three calls run the tiled kernel
+    w = workloads.custom(2, 320, 96, 16, "f32", seed=6)
     t = gpu_inputs(workloads.make_inputs(w))
     y, hf = run_gpu_fwd(mssm, t)
-    L1 = 64  # a tile boundary: the two halves see exactly the same arithmetic
+    L1 = 128  # a tile boundary: the two halves see exactly the same arithmetic
     t1 = {k: (v[:, :L1].contiguous() if k in ("u", "delta", "z", "Bm", "Cm") else v) for k, v in t.items()}
     t2 = {k: (v[:, L1:].contiguous() if k in ("u", "delta", "z", "Bm", "Cm") else v) for k, v in t.items()}
     y1, h1 = run_gpu_fwd(mssm, t1)

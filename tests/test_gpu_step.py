@@ -104,3 +104,56 @@ def test_multi_token_steps_in_place(mssm, B, D, segments, dtype):
     tol = FWD_TOL[dtype]
     assert fwd_err(to_np(torch.cat(ys, 1)), yr) <= tol
     assert fwd_err(to_np(state), hr) <= tol
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_short_sequence_path(mssm, N, dtype):
+    """Short sequences take the short path (the state in registers across the
+    steps; here, over 260 (b, d) rows, up to 64 steps): against the oracle at
+    lengths around the switch (1, 7, 64) and the tiled path just above it (65)."""
+    for L in (1, 7, 64, 65):
+        w = workloads.custom(2, L, 130, N, dtype, seed=200 + N + L)
+        print(f"[short] {w}", flush=True)
+        inp = workloads.make_inputs(w)
+        t = gpu_inputs(inp)
+        h0 = np.random.default_rng(L).standard_normal((w.B, w.D, N)).astype(np.float32)
+        y, hf = mssm.scan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"], t["dt_bias"],
+                              torch.from_numpy(h0).cuda())
+        torch.cuda.synchronize()
+        yr, hr = run_oracle_fwd(oracle, inp, h0)
+        tol = FWD_TOL[dtype]
+        assert fwd_err(to_np(y), yr) <= tol
+        assert fwd_err(to_np(hf), hr) <= tol
+
+
+@pytest.mark.parametrize("use,softplus", [((), True), (("z",), False), (("Dskip", "dt_bias"), True)])
+def test_short_sequence_optional_inputs(mssm, use, softplus):
+    # 20 steps over 600 (b, d) rows: the short path
+    w = workloads.custom(3, 20, 200, 16, "f32", seed=210)
+    inp = workloads.make_inputs(w)
+    if not softplus:  # flag off: Delta used as is; keep it a positive step so the recurrence stays contractive
+        inp["delta"] = (0.05 * np.abs(inp["delta"])).astype(np.float32)
+    t = gpu_inputs(inp)
+    y, hf = mssm.scan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"] if "Dskip" in use else None,
+                          t["z"] if "z" in use else None, t["dt_bias"] if "dt_bias" in use else None, None,
+                          delta_softplus=softplus)
+    torch.cuda.synchronize()
+    yr, hr = run_oracle_fwd(oracle, inp, None, use=use, softplus=softplus)
+    assert fwd_err(to_np(y), yr) <= FWD_TOL["f32"]
+    assert fwd_err(to_np(hf), hr) <= FWD_TOL["f32"]
+
+
+def test_short_path_many_rows(mssm):
+    """Up to 8 steps the short path runs at any row count: 64 x 1,536 rows, 1
+    and 8 steps, against the oracle; 9 steps take the tiled kernel."""
+    for L in (1, 8, 9):
+        w = workloads.custom(64, L, 1536, 16, "bf16", seed=220 + L)
+        print(f"[short] {w}", flush=True)
+        inp = workloads.make_inputs(w)
+        t = gpu_inputs(inp)
+        y, hf = mssm.scan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"], t["dt_bias"])
+        torch.cuda.synchronize()
+        yr, hr = run_oracle_fwd(oracle, inp)
+        assert fwd_err(to_np(y), yr) <= FWD_TOL["bf16"]
+        assert fwd_err(to_np(hf), hr) <= FWD_TOL["bf16"]
