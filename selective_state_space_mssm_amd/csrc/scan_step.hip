@@ -139,6 +139,35 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
 // forward takes them.  The forward kernel's tile pipeline needs whole 16-step
 // tiles to pay for itself; for a few tokens over many (b, d) rows this is
 // the faster form.
+// V consecutive values (V = 4: one 8-byte bf16 / 16-byte fp32 load; the
+// lane's first state index is a multiple of 4, so the address is aligned).
+template <int V>
+__device__ __forceinline__ void load_states(const uint16_t* p, float (&v)[V]) {
+    if constexpr (V == 4) {
+        const uint2 q = *reinterpret_cast<const uint2*>(p);
+        v[0] = bf16_lo(q.x);
+        v[1] = bf16_hi(q.x);
+        v[2] = bf16_lo(q.y);
+        v[3] = bf16_hi(q.y);
+    } else {
+#pragma unroll
+        for (int n = 0; n < V; ++n) v[n] = load_act(p, n);
+    }
+}
+template <int V>
+__device__ __forceinline__ void load_states(const float* p, float (&v)[V]) {
+    if constexpr (V == 4) {
+        const float4 q = *reinterpret_cast<const float4*>(p);
+        v[0] = q.x;
+        v[1] = q.y;
+        v[2] = q.z;
+        v[3] = q.w;
+    } else {
+#pragma unroll
+        for (int n = 0; n < V; ++n) v[n] = p[n];
+    }
+}
+
 struct TokKArgs {
     const void* u;
     const void* delta;
@@ -185,11 +214,14 @@ __global__ __launch_bounds__(256) void scan_tokens_kernel(TokKArgs a) {
         const float x = load_act(dl, t * D) + bias;
         const float dt = a.softplus ? softplus(x) : x;
         const float du = dt * uu;
+        float bv[V], cv[V];  // this lane's V values of Bm_t, Cm_t: one vector load each
+        load_states<V>(Bm + t * N, bv);
+        load_states<V>(Cm + t * N, cv);
         float s = 0.0f;
 #pragma unroll
         for (int n = 0; n < V; ++n) {
-            h[n] = __builtin_fmaf(fast_exp2(dt * A2[n]), h[n], du * load_act(Bm, t * N + n));  // A2 = A log2(e)
-            s = __builtin_fmaf(load_act(Cm, t * N + n), h[n], s);
+            h[n] = __builtin_fmaf(fast_exp2(dt * A2[n]), h[n], du * bv[n]);  // A2 = A log2(e)
+            s = __builtin_fmaf(cv[n], h[n], s);
         }
 #pragma unroll
         for (int m = 1; m < R; m <<= 1) s += __shfl_xor(s, m);
