@@ -209,14 +209,29 @@ __global__ __launch_bounds__(256) void scan_tokens_kernel(TokKArgs a) {
     T* __restrict__ y = static_cast<T*>(a.y) + b * L * D + d;
     const T* __restrict__ Bm = static_cast<const T*>(a.Bm) + b * L * N + n0;
     const T* __restrict__ Cm = static_cast<const T*>(a.Cm) + b * L * N + n0;
+    // token t's inputs are loaded during token t - 1 (one token of prefetch)
+    float nu = load_act(u, 0), nx = load_act(dl, 0), nz = z ? load_act(z, 0) : 0.0f;
+    float nb[V], nc[V];
+    load_states<V>(Bm, nb);
+    load_states<V>(Cm, nc);
     for (int64_t t = 0; t < L; ++t) {
-        const float uu = load_act(u, t * D);
-        const float x = load_act(dl, t * D) + bias;
+        const float uu = nu, zz = nz;
+        const float x = nx + bias;
+        float bv[V], cv[V];  // this lane's V values of Bm_t, Cm_t: one vector load each
+#pragma unroll
+        for (int n = 0; n < V; ++n) {
+            bv[n] = nb[n];
+            cv[n] = nc[n];
+        }
+        if (t + 1 < L) {
+            nu = load_act(u, (t + 1) * D);
+            nx = load_act(dl, (t + 1) * D);
+            if (z) nz = load_act(z, (t + 1) * D);
+            load_states<V>(Bm + (t + 1) * N, nb);
+            load_states<V>(Cm + (t + 1) * N, nc);
+        }
         const float dt = a.softplus ? softplus(x) : x;
         const float du = dt * uu;
-        float bv[V], cv[V];  // this lane's V values of Bm_t, Cm_t: one vector load each
-        load_states<V>(Bm + t * N, bv);
-        load_states<V>(Cm + t * N, cv);
         float s = 0.0f;
 #pragma unroll
         for (int n = 0; n < V; ++n) {
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(256) void scan_tokens_kernel(TokKArgs a) {
         for (int m = 1; m < R; m <<= 1) s += __shfl_xor(s, m);
         if (q == 0) {
             s = __builtin_fmaf(Dk, uu, s);
-            if (z) s *= silu(load_act(z, t * D));
+            if (z) s *= silu(zz);
             store_act(y, t * D, s);
         }
     }
