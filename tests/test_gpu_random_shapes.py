@@ -1,0 +1,97 @@
+"""GPU parity on seeded random problems: shapes, state sizes, activation types
+and optional inputs drawn at random, so that combinations the targeted tests
+do not name (ragged channel blocks, short and long sequences, every layout and
+schedule) are compared with the float64 oracle too.  Every case prints its
+draw before it runs."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import FWD_TOL, GRAD_TOL, fwd_err, gpu_inputs, grad_err, run_oracle_fwd, to_np
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+STATES = [1, 2, 4, 8, 16, 32, 64]
+OPTIONAL = ("Dskip", "z", "dt_bias")
+
+
+def draw(i):
+    rng = np.random.default_rng(1000 + i)
+    B = int(rng.integers(1, 7))
+    L = int(rng.choice([rng.integers(1, 65), rng.integers(65, 400), rng.integers(2048, 2600)], p=[0.4, 0.5, 0.1]))
+    D = int(rng.integers(1, 700)) if rng.random() < 0.8 else int(rng.integers(3000, 4400))
+    if L >= 2048:
+        B, D = 1, int(rng.integers(1, 200))  # long sequences: few channel blocks (the chunked schedule)
+    N = int(rng.choice(STATES))
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    use = tuple(k for k in OPTIONAL if rng.random() < 0.7)
+    h0 = bool(rng.random() < 0.5)
+    K = int(rng.integers(1, 5))
+    return B, L, D, N, dtype, use, h0, K
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_forward(mssm_lib, i):
+    B, L, D, N, dtype, use, h0, K = draw(i)
+    print(f"[random fwd {i}] B={B} L={L} D={D} N={N} {dtype} use={use} h0={h0}", flush=True)
+    w = workloads.custom(B, L, D, N, dtype, seed=3000 + i)
+    inp = workloads.make_inputs(w)
+    t = gpu_inputs(inp)
+    h0n = np.random.default_rng(i).standard_normal((B, D, N)).astype(np.float32) if h0 else None
+    g = lambda k: t[k] if k in use else None  # noqa: E731
+    y, hf = mssm_lib.scan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], g("Dskip"), g("z"), g("dt_bias"),
+                              torch.from_numpy(h0n).cuda() if h0 else None)
+    torch.cuda.synchronize()
+    yr, hr = run_oracle_fwd(oracle, inp, h0n, use=use)
+    assert fwd_err(to_np(y), yr) <= FWD_TOL[dtype]
+    assert fwd_err(to_np(hf), hr) <= FWD_TOL[dtype]
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_conv_forward(mssm_lib, i):
+    B, L, D, N, dtype, use, h0, K = draw(100 + i)
+    print(f"[random conv fwd {i}] B={B} L={L} D={D} N={N} {dtype} use={use} d_conv={K}", flush=True)
+    w = workloads.custom(B, L, D, N, dtype, seed=3100 + i)
+    inp = workloads.make_inputs(w)
+    inp.update(workloads.conv_front_end(w, K))
+    t = gpu_inputs(inp)
+    g = lambda k: t[k] if k in use else None  # noqa: E731
+    y, hf, _ = mssm_lib.conv_scan_fwd(t["u"], t["conv_w"], t["delta"], t["A"], t["Bm"], t["Cm"], g("Dskip"), g("z"),
+                                      g("dt_bias"), None, conv_b=t["conv_b"], x_prev=t["x_prev"] if K > 1 else None)
+    torch.cuda.synchronize()
+    f = workloads.as_float32(inp)
+    h = lambda k: f[k] if k in use else None  # noqa: E731
+    yr, hr, _ = oracle.conv_scan_fwd(f["u"], f["conv_w"], f["delta"], f["A"], f["Bm"], f["Cm"], h("Dskip"), h("z"),
+                                     h("dt_bias"), None, bias=f["conv_b"], x_prev=f["x_prev"] if K > 1 else None)
+    assert fwd_err(to_np(y), yr) <= FWD_TOL[dtype]
+    assert fwd_err(to_np(hf), hr) <= FWD_TOL[dtype]
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_backward(mssm_lib, i):
+    B, L, D, N, dtype, use, h0, K = draw(200 + i)
+    L = min(L, 300)  # the float64 adjoint keeps the whole state history
+    print(f"[random bwd {i}] B={B} L={L} D={D} N={N} {dtype} use={use} h0={h0}", flush=True)
+    w = workloads.custom(B, L, D, N, dtype, seed=3200 + i, backward=True)
+    inp = workloads.make_inputs(w)
+    t = gpu_inputs(inp)
+    h0n = np.random.default_rng(i).standard_normal((B, D, N)).astype(np.float32) if h0 else None
+    g = lambda k: t[k] if k in use else None  # noqa: E731
+    gg = mssm_lib.scan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["dy"], g("Dskip"), g("z"), g("dt_bias"),
+                           torch.from_numpy(h0n).cuda() if h0 else None)
+    torch.cuda.synchronize()
+    f = workloads.as_float32(inp)
+    h = lambda k: f[k] if k in use else None  # noqa: E731
+    r = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["Bm"], f["Cm"], f["dy"], h("Dskip"), h("z"), h("dt_bias"), h0n)
+    tol = GRAD_TOL[dtype]
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddt_bias") + (("dz",) if "z" in use else ()) + \
+            (("dh0",) if h0 else ()):
+        assert grad_err(to_np(gg[k]), r[k]) <= tol, k
+
+
+@pytest.fixture(scope="module")
+def mssm_lib():
+    import selective_state_space_mssm_amd as m
+    return m
