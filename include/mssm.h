@@ -30,6 +30,11 @@
  *     A, dA                              : (D, N)      float32
  *     Dskip, dt_bias, dD, ddt_bias       : (D)         float32
  *     h0, h_final, dh_final, dh0, state  : (B, D, N)   float32
+ *   and for the conv1d + SiLU front end (mssm_conv_*):
+ *     x, dx                              : (B, L, D)   as u
+ *     x_prev, dx_prev, conv_state        : (B, d_conv - 1, D), in time order
+ *     conv_w, dconv_w                    : (D, d_conv) float32 (torch.nn.Conv1d's (D, 1, d_conv))
+ *     conv_b, dconv_b                    : (D)         float32
  * Element type: problem.dtype (MSSM_F32 or MSSM_BF16) for u, delta, z, Bm, Cm,
  *   y and their gradients; float32 for everything else.  Arithmetic is float32
  *   throughout; bfloat16 outputs are rounded to nearest even.

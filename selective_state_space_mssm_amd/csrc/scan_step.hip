@@ -16,6 +16,10 @@
 // by one lane (lane q owns row q when a row has four lanes or more, else the
 // row's first lane owns all rows), so its read precedes its write in program
 // order.
+//
+// scan_tokens_kernel: mssm_scan_fwd's path for short sequences (a few tokens
+// over many rows), the same mapping with the state held in registers across
+// the L tokens.
 #include "device_common.h"
 #include "launch.h"
 
@@ -132,13 +136,6 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
     }
 }
 
-// Short sequences: the forward over L steps with the step's mapping (N/4
-// lanes per (b, d) row, 4 states per lane, rows of the state contiguous),
-// the state in registers from h0 to h_final, so it moves once per call
-// rather than once per token; inputs at (b, t, d) and (b, t, n) as the
-// forward takes them.  The forward kernel's tile pipeline needs whole 16-step
-// tiles to pay for itself; for a few tokens over many (b, d) rows this is
-// the faster form.
 // V consecutive values (V = 4: one 8-byte bf16 / 16-byte fp32 load; the
 // lane's first state index is a multiple of 4, so the address is aligned).
 template <int V>
@@ -168,6 +165,13 @@ __device__ __forceinline__ void load_states(const float* p, float (&v)[V]) {
     }
 }
 
+// Short sequences: the forward over L steps with the step's mapping (N/4
+// lanes per (b, d) row, 4 states per lane, rows of the state contiguous),
+// the state in registers from h0 to h_final, so it moves once per call
+// rather than once per token; inputs at (b, t, d) and (b, t, n) as the
+// forward takes them.  The forward kernel's tile pipeline needs whole 16-step
+// tiles to pay for itself; for a few tokens over many (b, d) rows this is
+// the faster form.
 struct TokKArgs {
     const void* u;
     const void* delta;
