@@ -36,7 +36,10 @@ class Problem(ctypes.Structure):
 class MssmError(RuntimeError):
     def __init__(self, status: int, lib):
         self.status = status
-        super().__init__(lib.mssm_status_string(status).decode())
+        msg = lib.mssm_status_string(status).decode()
+        if status == -5:  # a slice such as x[:, t] of a batch-1 tensor is "contiguous" but starts mid-allocation
+            msg += " (pass a fresh tensor, e.g. .clone(), instead of a view at an offset)"
+        super().__init__(msg)
 
 
 def _open(path: str):

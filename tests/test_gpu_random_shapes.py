@@ -95,3 +95,52 @@ def test_random_backward(mssm_lib, i):
 def mssm_lib():
     import selective_state_space_mssm_amd as m
     return m
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_conv_backward(mssm_lib, i):
+    B, L, D, N, dtype, use, h0, K = draw(300 + i)
+    L = min(L, 3000)
+    print(f"[random conv bwd {i}] B={B} L={L} D={D} {dtype} d_conv={K}", flush=True)
+    w = workloads.custom(B, L, D, 16, dtype, seed=3300 + i)
+    inp = workloads.make_inputs(w)
+    inp.update(workloads.conv_front_end(w, K))
+    t = gpu_inputs(inp)
+    du = t["z"]  # any (B, L, D) activations of the same type serve as du
+    with_prev = K > 1 and i % 2 == 0
+    g = mssm_lib.conv_bwd(t["u"], t["conv_w"], du, conv_b=t["conv_b"], x_prev=t["x_prev"] if with_prev else None,
+                          want_dx_prev=K > 1)
+    torch.cuda.synchronize()
+    f = workloads.as_float32(inp)
+    r = oracle.causal_conv_silu_bwd(f["u"], f["conv_w"], f["z"], f["conv_b"], f["x_prev"] if with_prev else None)
+    tol = GRAD_TOL[dtype]
+    assert grad_err(to_np(g["dx"]), r["dx"]) <= tol
+    assert grad_err(to_np(g["dconv_w"]), r["dweight"]) <= tol
+    assert grad_err(to_np(g["dconv_b"]), r["dbias"]) <= tol
+    if K > 1:
+        assert grad_err(to_np(g["dx_prev"]), r["dx_prev"]) <= tol
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_conv_decode(mssm_lib, i):
+    B, L, D, N, dtype, use, h0, K = draw(400 + i)
+    L = min(L, 12)
+    print(f"[random conv decode {i}] B={B} L={L} D={D} N={N} {dtype} d_conv={K}", flush=True)
+    w = workloads.custom(B, L, D, N, dtype, seed=3400 + i)
+    inp = workloads.make_inputs(w)
+    inp.update(workloads.conv_front_end(w, K))
+    t = gpu_inputs(inp)
+    state = torch.zeros((B, D, N), device="cuda")
+    cst = t["x_prev"].clone() if K > 1 else None
+    # per-token slices as fresh (16-byte aligned) tensors: with B = 1 a slice is already "contiguous" and
+    # would be passed at its offset inside the sequence, which the C ABI rejects as misaligned
+    col = lambda a, s: a[:, s].clone()  # noqa: E731
+    ys = [mssm_lib.conv_step(col(t["u"], s), t["conv_w"], cst, col(t["delta"], s), t["A"], col(t["Bm"], s),
+                             col(t["Cm"], s), state, t["Dskip"], col(t["z"], s), t["dt_bias"], conv_b=t["conv_b"])
+          for s in range(L)]
+    torch.cuda.synchronize()
+    f = workloads.as_float32(inp)
+    yr, hr, _ = oracle.conv_scan_fwd(f["u"], f["conv_w"], f["delta"], f["A"], f["Bm"], f["Cm"], f["Dskip"], f["z"],
+                                     f["dt_bias"], None, bias=f["conv_b"], x_prev=f["x_prev"] if K > 1 else None)
+    assert fwd_err(to_np(torch.stack(ys, 1)), yr) <= FWD_TOL[dtype]
+    assert fwd_err(to_np(state), hr) <= FWD_TOL[dtype]
