@@ -24,7 +24,7 @@ causal conv1d + SiLU front end (x in place of u, d_conv = 4) and that front end'
 width (B=4, D=5120, N=16: one decode step per call from Python, so the host's
 launch overhead, not the kernel, sets this rate; the kernel's own duration is
 in the kernel trace), the same step at B = 64 and 256 (batched decode, where the
-state's read and write set the rate), the step behind the conv front end at B = 256 and the training-workload backward
+state's read and write set the rate), the step behind the conv front end at B = 256, a 4-token forward at B = 256 (the short-sequence path) and the training-workload backward
 (``--long`` also the 1M-step forward).
 ``--copy-probe`` runs a plain device copy of 1 GiB first (counter calibration).
 """
@@ -412,6 +412,10 @@ def main():
             out["extra"][f"step_B{bb}_us_per_call"] = round(st_us, 2)
             out["extra"][f"step_B{bb}_GBs"] = round(st_gbs, 1)
         out["extra"]["conv_step_B256_us"] = round(time_conv_step(mssm, torch, w, 256), 2)  # conv front end + step
+        # a few tokens over many rows (the forward's short-sequence path): B = 256, 4 tokens
+        sw = workloads.custom(256, 4, w.D, w.N, w.dtype, seed=w.seed)
+        _, sl, _ = time_fwd(mssm, torch, sw, 30, 3)
+        out["extra"]["short_fwd_B256_L4_us"] = round(float(np.median(sl)) * 1e3, 1)
         tw = workloads.WORKLOADS["train"]
         tb = time_bwd(mssm, torch, tw, 10, 2)
         out.setdefault("extra", {})["train_bwd_us"] = round(tb * 1e6, 1)
