@@ -24,9 +24,14 @@ torch.nn.Conv1d(groups=D, padding=d_conv - 1) truncated to the first L
 outputs -- the layer the mamba-minimal page runs in place of the CUDA conv,
 with d_conv = 4 in the configurations of the page "Mamba SSM 架构".
 
+Mamba-2's layer (``ssd_fwd``), which the pages name without equations, is
+read as the same scan with one scalar decay and one step size per head,
+shared by the head's channels and states, and Bm, Cm shared by all heads; the
+oracle runs it through ``scan_fwd`` on the flattened channels.
+
 Pinning (what checks this oracle against something other than itself) is in
-``tests/test_oracle_fwd_pins.py``, ``tests/test_oracle_bwd_pins.py`` and
-``tests/test_oracle_conv_pins.py``.
+``tests/test_oracle_fwd_pins.py``, ``tests/test_oracle_bwd_pins.py``,
+``tests/test_oracle_conv_pins.py`` and ``tests/test_ssd_dual_form.py``.
 """
 from __future__ import annotations
 
@@ -171,6 +176,24 @@ def conv_scan_fwd(x, weight, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None,
     u = causal_conv_silu(x, weight, bias, x_prev)
     y, hf = scan_fwd(u, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, softplus=softplus)
     return y, hf, u
+
+
+def ssd_fwd(x, dt, A, Bm, Cm, Dskip=None, dt_bias=None, h0=None, softplus=True):
+    """Mamba-2 (state-space dual) forward in float64, as the selective scan
+    over channels d = (h, p) with A[d, n] = A[h], delta[b,t,d] = dt[b,t,h],
+    Dskip[d] = Dskip[h], dt_bias[d] = dt_bias[h] (the pages name Mamba-2 in the
+    model list of "mamba.py: 一个简单高效的Mamba实现" and the versions paragraph
+    of "Mamba SSM 架构"; this per-head scalar-decay reading is the library's).
+    x (B, L, H, P); dt (B, L, H); A, Dskip, dt_bias (H); Bm, Cm (B, L, N);
+    h0 (B, H, P, N).  Returns ``(y (B, L, H, P), h_final (B, H, P, N))``."""
+    x, dt, A, Bm, Cm = _f64(x), _f64(dt), _f64(A), _f64(Bm), _f64(Cm)
+    B, L, H, P = x.shape
+    N = Bm.shape[2]
+    rep = lambda v: None if v is None else np.repeat(_f64(v), P, axis=-1)  # noqa: E731
+    y, hf = scan_fwd(x.reshape(B, L, H * P), rep(dt), np.repeat(A, P)[:, None] * np.ones((1, N)), Bm, Cm,
+                     rep(Dskip), None, rep(dt_bias), None if h0 is None else _f64(h0).reshape(B, H * P, N),
+                     softplus=softplus)
+    return y.reshape(B, L, H, P), hf.reshape(B, H, P, N)
 
 
 def step(u_t, delta_t, A, Bm_t, Cm_t, state, Dskip=None, z_t=None, dt_bias=None,

@@ -216,3 +216,22 @@ def to_torch(inp: dict, device="cuda", keys=("u", "delta", "z", "Bm", "Cm", "dy"
         else:
             out[k] = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
     return out
+
+
+def ssd_inputs(B: int, L: int, H: int, P: int, N: int, seed: int = 0) -> dict:
+    """Seeded float32 inputs of a Mamba-2 (SSD) layer: x (B, L, H, P) ~ N(0,1);
+    dt (B, L, H) = 0.5 * N(0,1); Bm, Cm (B, L, N) ~ N(0,1); per head, dt_bias =
+    softplus^-1 of a step log-uniform on [1e-3, 1e-1] (as ``channel_params``),
+    A = -U(1, 16) and Dskip = 1.  One ``Generator(PCG64(SeedSequence(seed,
+    spawn_key=(2**21,))))`` in that order."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(1 << 21,))))
+    dt_step = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=H))
+    return {
+        "dt_bias": (dt_step + np.log(-np.expm1(-dt_step))).astype(np.float32),
+        "A": (-rng.uniform(1.0, 16.0, size=H)).astype(np.float32),
+        "Dskip": np.ones(H, np.float32),
+        "x": rng.standard_normal((B, L, H, P), dtype=np.float32),
+        "dt": np.float32(0.5) * rng.standard_normal((B, L, H), dtype=np.float32),
+        "Bm": rng.standard_normal((B, L, N), dtype=np.float32),
+        "Cm": rng.standard_normal((B, L, N), dtype=np.float32),
+    }
