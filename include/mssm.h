@@ -240,6 +240,44 @@ mssm_status mssm_conv_step(const mssm_problem* p, int32_t d_conv,
                            const float* Dskip, const void* z_t, const float* dt_bias,
                            float* state, void* y_t, void* hip_stream);
 
+/*
+ * Forward of the Mamba-2 layer, the state-space dual (SSD).  The pages name
+ * Mamba-2 (the model list of "mamba.py: 一个简单高效的Mamba实现", the versions
+ * paragraph of "Mamba SSM 架构") without its equations; the library reads it as
+ * the selective scan above with, per head h, one scalar decay A[h] and one
+ * step dt[b,t,h] shared by the head's headdim channels and all dstate states,
+ * and Bm, Cm shared by all heads (one group):
+ *
+ *     Delta   = softplus(dt[b,t,h] + dt_bias[h])   (or without softplus)
+ *     h_t[p,n] = exp(Delta A[h]) h_{t-1}[p,n] + Delta Bm[b,t,n] x[b,t,h,p]
+ *     y[b,t,h,p] = sum_n Cm[b,t,n] h_t[p,n] + Dskip[h] x[b,t,h,p]
+ *
+ * i.e. mssm_scan_fwd over the H * P channels d = h * P + p with
+ * A[d, n] = A[h], delta[b,t,d] = dt[b,t,h], Dskip[d] = Dskip[h].  Computed in
+ * chunks of 64 steps as dense products on the matrix cores.
+ *   x, y       (B, L, H, P) float32        dt        (B, L, H) float32
+ *   Bm, Cm     (B, L, N) float32           A, Dskip, dt_bias  (H) float32
+ *   h0, h_final (B, H, P, N) float32
+ * Required: p, x, dt, A, Bm, Cm, y.  Optional (NULL): Dskip, dt_bias (-> 0),
+ * h0 (-> zeros), h_final (not written; may be the same buffer as h0).
+ * Built for headdim P = 64 and dstate N in {64, 128}, float32 only: other
+ * sizes or dtype MSSM_BF16 -> MSSM_ERR_UNSUPPORTED.  Other errors as
+ * mssm_scan_fwd; batch * nheads must be below 2^31.  No workspace.
+ */
+typedef struct {
+    int64_t batch;          /* B */
+    int64_t seqlen;         /* L */
+    int64_t nheads;         /* H */
+    int64_t headdim;        /* P */
+    int64_t dstate;         /* N */
+    int32_t dtype;          /* mssm_dtype; only MSSM_F32 is built */
+    int32_t delta_softplus; /* nonzero: Delta = softplus(dt + dt_bias) */
+} mssm_ssd_problem;
+
+mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const float* x, const float* dt, const float* A,
+                         const float* Bm, const float* Cm, const float* Dskip, const float* dt_bias,
+                         const float* h0, float* y, float* h_final, void* hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char* mssm_status_string(mssm_status s);
 

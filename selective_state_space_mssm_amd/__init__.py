@@ -6,8 +6,9 @@ Python binding over it.  PyTorch supplies device memory and streams only.
 """
 from .binding import (  # noqa: F401
     LIB_PATH, MAX_DCONV, MSSM_BF16, MSSM_F32, EXPORTS, MssmError, Problem, bwd_workspace_bytes,
-    conv_bwd, conv_scan_fwd, conv_step, fwd_workspace_bytes, lib, problem, scan_bwd, scan_fwd, step,
+    conv_bwd, conv_scan_fwd, conv_step, fwd_workspace_bytes, lib, problem, scan_bwd, scan_fwd, ssd_fwd,
+    step,
 )
 
-__all__ = ["scan_fwd", "conv_scan_fwd", "conv_bwd", "scan_bwd", "step", "conv_step", "fwd_workspace_bytes", "bwd_workspace_bytes",
+__all__ = ["scan_fwd", "conv_scan_fwd", "conv_bwd", "scan_bwd", "step", "conv_step", "ssd_fwd", "fwd_workspace_bytes", "bwd_workspace_bytes",
            "MssmError", "Problem", "problem", "lib", "LIB_PATH"]

@@ -23,13 +23,19 @@ STATUS = {0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_SHAPE", -3: "MSSM_ERR
           -7: "MSSM_ERR_HIP"}
 EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd",
            "mssm_conv_scan_fwd", "mssm_conv_bwd_workspace_bytes", "mssm_conv_bwd", "mssm_scan_bwd", "mssm_step",
-           "mssm_conv_step", "mssm_status_string", "mssm_build_info"]
+           "mssm_conv_step", "mssm_ssd_fwd", "mssm_status_string", "mssm_build_info"]
 MAX_DCONV = 4
 
 
 class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("delta_softplus", ctypes.c_int32)]
+
+
+class SsdProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("dtype", ctypes.c_int32),
                 ("delta_softplus", ctypes.c_int32)]
 
 
@@ -66,6 +72,8 @@ def _open(path: str):
     lib.mssm_step.restype = st
     lib.mssm_conv_step.argtypes = [P, ctypes.c_int32] + [vp] * 13 + [vp]
     lib.mssm_conv_step.restype = st
+    lib.mssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdProblem)] + [vp] * 10 + [vp]
+    lib.mssm_ssd_fwd.restype = st
     lib.mssm_status_string.argtypes = [st]
     lib.mssm_status_string.restype = ctypes.c_char_p
     lib.mssm_build_info.argtypes = []
@@ -369,3 +377,31 @@ def conv_step(x_t, conv_w, conv_state, delta_t, A, Bm_t, Cm_t, state, Dskip=None
                               _ptr(delta_t), _ptr(A), _ptr(Bm_t), _ptr(Cm_t), _ptr(Dskip), _ptr(z_t),
                               _ptr(dt_bias), _ptr(state), _ptr(y_t), _stream(x_t.device)))
     return y_t
+
+
+def ssd_fwd(x, dt, A, Bm, Cm, Dskip=None, dt_bias=None, h0=None, delta_softplus=True,
+            return_final_state=True, y=None, h_final=None):
+    """Mamba-2 (SSD) forward.  x: (B, L, H, P); dt: (B, L, H); Bm, Cm: (B, L, N);
+    A, Dskip, dt_bias: (H); h0: (B, H, P, N); all float32.  Returns (y, h_final)
+    (h_final None unless requested)."""
+    B, L, H, P = x.shape
+    N = Bm.shape[2]
+    f = torch.float32
+    _req(x, "x", (B, L, H, P), f)
+    _req(dt, "dt", (B, L, H), f)
+    _req(A, "A", (H,), f)
+    _req(Bm, "Bm", (B, L, N), f)
+    _req(Cm, "Cm", (B, L, N), f)
+    _opt(Dskip, "Dskip", (H,), f)
+    _opt(dt_bias, "dt_bias", (H,), f)
+    _opt(h0, "h0", (B, H, P, N), f)
+    if y is None:
+        y = torch.empty((B, L, H, P), dtype=f, device=x.device)
+    _req(y, "y", (B, L, H, P), f)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((B, H, P, N), dtype=f, device=x.device)
+    _opt(h_final, "h_final", (B, H, P, N), f)
+    prob = SsdProblem(B, L, H, P, N, MSSM_F32, 1 if delta_softplus else 0)
+    _check(lib.mssm_ssd_fwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
+                            _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _stream(x.device)))
+    return y, h_final

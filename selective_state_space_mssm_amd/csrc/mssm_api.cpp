@@ -12,6 +12,7 @@
 #include <initializer_list>
 
 #include "launch.h"
+#include "ssd.h"
 
 namespace {
 
@@ -204,6 +205,26 @@ mssm_status mssm_conv_step(const mssm_problem* p, int32_t d_conv, const void* x_
     a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.y = y_t;
     a.conv_w = conv_w; a.conv_b = conv_b; a.x_prev = d_conv > 1 ? conv_state : nullptr; a.d_conv = d_conv;
     return from_hip(mssm::launch_step(a, state, static_cast<hipStream_t>(hip_stream)));
+}
+
+mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const float* x, const float* dt, const float* A,
+                         const float* Bm, const float* Cm, const float* Dskip, const float* dt_bias,
+                         const float* h0, float* y, float* h_final, void* hip_stream) {
+    if (!p) return MSSM_ERR_NULL;
+    if (p->dtype != MSSM_F32 && p->dtype != MSSM_BF16) return MSSM_ERR_DTYPE;
+    if (p->batch < 1 || p->seqlen < 1 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1) return MSSM_ERR_SHAPE;
+    if (p->batch * p->nheads >= (int64_t{1} << 31) || p->seqlen >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
+    if (p->dtype != MSSM_F32 || !mssm::ssd_supported(p->headdim, p->dstate)) return MSSM_ERR_UNSUPPORTED;
+    if (!x || !dt || !A || !Bm || !Cm || !y) return MSSM_ERR_NULL;
+    const mssm_status st = check_align({x, dt, A, Bm, Cm, Dskip, dt_bias, h0, y, h_final});
+    if (st != MSSM_OK) return st;
+
+    mssm::SsdArgs a{};
+    a.B = p->batch; a.L = p->seqlen; a.H = p->nheads; a.P = p->headdim; a.N = p->dstate;
+    a.softplus = p->delta_softplus ? 1 : 0;
+    a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm;
+    a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0; a.y = y; a.h_final = h_final;
+    return from_hip(mssm::launch_ssd_fwd(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 const char* mssm_status_string(mssm_status s) {

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), f"libmssm.so does not export {n}"
     assert sorted(mssm.EXPORTS) == names
@@ -184,6 +184,33 @@ def test_conv_step_validation():
         assert cs(good(), **{k: None}) == -1, k
     for k in ("x_t", "conv_w", "conv_b", "conv_state", "state", "y_t"):
         assert cs(good(), **{k: MIS}) == -5, k
+
+
+def ssd(p, **kw):
+    names = ["x", "dt", "A", "Bm", "Cm", "Dskip", "dt_bias", "h0", "y", "h_final"]
+    required = {"x", "dt", "A", "Bm", "Cm", "y"}
+    args = [None if kw.get(n, FAKE if n in required else None) is None else
+            ctypes.c_void_p(kw.get(n, FAKE)) for n in names]
+    return lib.mssm_ssd_fwd(ctypes.byref(p) if p is not None else None, *args, None)
+
+
+def test_ssd_validation():
+    S = mssm.binding.SsdProblem
+    good = lambda **k: S(**{**dict(batch=2, seqlen=100, nheads=3, headdim=64, dstate=64, dtype=0,  # noqa: E731
+                                   delta_softplus=1), **k})
+    assert ssd(None) == -1
+    assert ssd(good(dtype=7)) == -3
+    for k in ("batch", "seqlen", "nheads", "headdim", "dstate"):
+        assert ssd(good(**{k: 0})) == -2, k
+    assert ssd(good(batch=1 << 20, nheads=1 << 11)) == -2   # B*H >= 2^31
+    assert ssd(good(seqlen=1 << 31)) == -2
+    assert ssd(good(headdim=32)) == -4                      # built for P = 64
+    assert ssd(good(dstate=16)) == -4                       # built for N in {64, 128}
+    assert ssd(good(dtype=1)) == -4                         # float32 only
+    for n in ("x", "dt", "A", "Bm", "Cm", "y"):
+        assert ssd(good(), **{n: None}) == -1, n
+    for n in ("x", "dt", "A", "Bm", "Cm", "Dskip", "dt_bias", "h0", "y", "h_final"):
+        assert ssd(good(), **{n: MIS}) == -5, n
 
 
 def test_workspace_sizes_and_checks():
