@@ -262,7 +262,8 @@ mssm_status mssm_conv_step(const mssm_problem* p, int32_t d_conv,
  * h0 (-> zeros), h_final (not written; may be the same buffer as h0).
  * Built for headdim P = 64 and dstate N in {64, 128}, float32 only: other
  * sizes or dtype MSSM_BF16 -> MSSM_ERR_UNSUPPORTED.  Other errors as
- * mssm_scan_fwd; batch * nheads must be below 2^31.  No workspace.
+ * mssm_scan_fwd; batch * nheads must be below 2^31 and nheads * headdim below
+ * 2^23 (else MSSM_ERR_SHAPE).  No workspace.
  */
 typedef struct {
     int64_t batch;          /* B */

@@ -214,6 +214,7 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const float* x, const float*
     if (p->dtype != MSSM_F32 && p->dtype != MSSM_BF16) return MSSM_ERR_DTYPE;
     if (p->batch < 1 || p->seqlen < 1 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1) return MSSM_ERR_SHAPE;
     if (p->batch * p->nheads >= (int64_t{1} << 31) || p->seqlen >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
+    if (p->nheads * p->headdim >= (int64_t{1} << 23)) return MSSM_ERR_SHAPE;  // a 64-step chunk stays below 2^31 bytes
     if (p->dtype != MSSM_F32 || !mssm::ssd_supported(p->headdim, p->dstate)) return MSSM_ERR_UNSUPPORTED;
     if (!x || !dt || !A || !Bm || !Cm || !y) return MSSM_ERR_NULL;
     const mssm_status st = check_align({x, dt, A, Bm, Cm, Dskip, dt_bias, h0, y, h_final});

@@ -46,6 +46,16 @@ __device__ __forceinline__ int acc_row(int r, int hl) { return (r >> 2) * 8 + hl
 
 __device__ __forceinline__ float fexp(float x) { return fast_exp2(x * kLog2e); }
 
+// An integer the compiler must treat as unknown at this point (an empty asm
+// statement, no instruction).  Recomputing a lane's LDS base offsets through
+// it once per chunk keeps them out of loop-invariant hoisting: each step's
+// address stays base + constant, with the constant folded into the ds_read
+// offset field, instead of one precomputed address register per step.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // One chunk's operands.  Rows padded by one float so that reading a column
 // (32 rows at one k, the A-operand pattern) hits 32 different banks.
 template <int N>
@@ -59,6 +69,85 @@ struct SsdSmem {
     float dlt[kQ];         // Delta (0 past the sequence end)
     float w[kQ];           // exp(cum_last - cum_j) Delta_j
 };
+
+// acc += sum over STEPS k-steps of A_s B_s, the operands of step s read by
+// ld(s, a, b).  The reads run DIST steps ahead of the MFMAs, so the LDS
+// latency hides behind the matrix core (one wave per SIMD has no other wave
+// to cover it).  DIST times the reads per step stays within the 15 LDS
+// operations the wave's lgkm counter can track.
+template <int STEPS, int DIST = 6, class F>
+__device__ __forceinline__ f32x16 mfma_chain(f32x16 acc, F&& ld) {
+    float av[STEPS], bv[STEPS];
+#pragma unroll
+    for (int s = 0; s < DIST && s < STEPS; ++s) ld(s, av[s], bv[s]);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        if (s + DIST < STEPS) ld(s + DIST, av[s + DIST], bv[s + DIST]);
+        // keep the reads issued ahead: the scheduler would otherwise sink each
+        // one next to its MFMA and wait out its latency there
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma32(av[s], bv[s], acc);
+    }
+    return acc;
+}
+
+// As mfma_chain, with the A operand of step s the product of two values
+// ld(s, a, a2, b) reads: the product is formed when the step issues, so its
+// reads stay DIST steps ahead too.
+template <int STEPS, int DIST = 4, class F>
+__device__ __forceinline__ f32x16 mfma_chain_scaled(f32x16 acc, F&& ld) {
+    float av[STEPS], a2[STEPS], bv[STEPS];
+#pragma unroll
+    for (int s = 0; s < DIST && s < STEPS; ++s) ld(s, av[s], a2[s], bv[s]);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        if (s + DIST < STEPS) ld(s + DIST, av[s + DIST], a2[s + DIST], bv[s + DIST]);
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma32(av[s] * a2[s], bv[s], acc);
+    }
+    return acc;
+}
+
+// One chunk's global inputs, held in registers from the previous chunk's
+// compute until they are staged into LDS.
+template <int N>
+struct ChunkRegs {
+    static constexpr int kX = kQ * kP / 4 / kThreads;  // float4 per thread of X
+    static constexpr int kB = kQ * N / 4 / kThreads;   // float4 per thread of Bm, of Cm
+    float4 x[kX], b[kB], c[kB];
+    float dt;
+};
+
+// Loads chunk [t0, t0 + 64) into registers through buffer resources that
+// cover only the chunk's valid rows: a row past the sequence end lies outside
+// its resource and reads as zeros, with no branch and no address select (a
+// chunk wholly past the end has an empty resource and touches no memory).
+template <int N>
+__device__ __forceinline__ void load_chunk(const SsdArgs& a, int64_t bi, int64_t h, int64_t t0, int tid,
+                                           ChunkRegs<N>& g) {
+    const int64_t H = a.H, L = a.L;
+    const int64_t nv = L - t0 < 0 ? 0 : imin64(kQ, L - t0);
+    const int64_t row0 = bi * L + t0;
+    const auto rx = make_rsrc(a.x + row0 * H * kP, (uint32_t)(nv * H * kP * 4));
+    const auto rb = make_rsrc(a.Bm + row0 * N, (uint32_t)(nv * N * 4));
+    const auto rc = make_rsrc(a.Cm + row0 * N, (uint32_t)(nv * N * 4));
+    const auto rd = make_rsrc(a.dt + row0 * H, (uint32_t)(nv * H * 4));
+#pragma unroll
+    for (int e = 0; e < ChunkRegs<N>::kX; ++e) {
+        const int q = e * kThreads + tid, i = q / (kP / 4), p = (q % (kP / 4)) * 4;
+        const int off = (int)((i * H + h) * kP + p) * 4;
+        g.x[e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+    }
+#pragma unroll
+    for (int e = 0; e < ChunkRegs<N>::kB; ++e) {
+        const int q = e * kThreads + tid, i = q / (N / 4), n = (q % (N / 4)) * 4;
+        const int off = (i * N + n) * 4;
+        g.b[e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+        g.c[e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
+    }
+    // step sizes, used by wave 0 only
+    g.dt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)((tid & 63) * H + h) * 4, 0, 0));
+}
 
 template <int N>
 __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
@@ -75,52 +164,53 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const float Dh = a.Dskip ? a.Dskip[h] : 0.0f;
 
-    // this wave's state tiles: rows p in [sp * 32, +32), columns n in [(wv & 1) * NT + k) * 32, +32)
+    // this wave's state tiles: rows p in [sp * 32, +32), columns n in [((wv & 1) * NT + k) * 32, +32)
     const int sp = wv >> 1;
     const int64_t state_base = (bi * H + h) * kP * N;
     f32x16 S[NT];
+    if (a.h0) {
 #pragma unroll
-    for (int k = 0; k < NT; ++k) {
-        const int n = ((wv & 1) * NT + k) * 32 + l32;
+        for (int k = 0; k < NT; ++k) {
+            const int n = ((wv & 1) * NT + k) * 32 + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            S[k][r] = a.h0 ? a.h0[state_base + (int64_t)(sp * 32 + acc_row(r, hl)) * N + n] : 0.0f;
+            for (int r = 0; r < 16; ++r) S[k][r] = a.h0[state_base + (int64_t)(sp * 32 + acc_row(r, hl)) * N + n];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < NT; ++k) S[k] = f32x16{};
     }
 
     // this wave's tile (ti, tj) of M (Q x Q) and of Y (Q x P)
     const int ti = wv >> 1, tj = wv & 1;
 
+    ChunkRegs<N> g;
+    load_chunk<N>(a, bi, h, 0, tid, g);
+
     for (int64_t t0 = 0; t0 < L; t0 += kQ) {
         const int nv = (int)imin64(kQ, L - t0);
 
-        // ---- stage: S^T and the chunk's operands into LDS; cum, Delta, w ----
+        // ---- stage: the chunk's operands and S^T into LDS; cum, Delta, w ----
+#pragma unroll
+        for (int e = 0; e < ChunkRegs<N>::kX; ++e) {
+            const int q = e * kThreads + tid, i = q / (kP / 4), p = (q % (kP / 4)) * 4;
+            s.x[i][p] = g.x[e].x; s.x[i][p + 1] = g.x[e].y; s.x[i][p + 2] = g.x[e].z; s.x[i][p + 3] = g.x[e].w;
+        }
+#pragma unroll
+        for (int e = 0; e < ChunkRegs<N>::kB; ++e) {
+            const int q = e * kThreads + tid, i = q / (N / 4), n = (q % (N / 4)) * 4;
+            s.b[i][n] = g.b[e].x; s.b[i][n + 1] = g.b[e].y; s.b[i][n + 2] = g.b[e].z; s.b[i][n + 3] = g.b[e].w;
+            s.c[i][n] = g.c[e].x; s.c[i][n + 1] = g.c[e].y; s.c[i][n + 2] = g.c[e].z; s.c[i][n + 3] = g.c[e].w;
+        }
 #pragma unroll
         for (int k = 0; k < NT; ++k) {
             const int n = ((wv & 1) * NT + k) * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s.st[n][sp * 32 + acc_row(r, hl)] = S[k][r];
         }
-        for (int e = tid; e < kQ * kP / 4; e += kThreads) {
-            const int i = e / (kP / 4), p = (e % (kP / 4)) * 4;
-            float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (i < nv) v = *reinterpret_cast<const float4*>(a.x + ((bi * L + t0 + i) * H + h) * kP + p);
-            s.x[i][p] = v.x; s.x[i][p + 1] = v.y; s.x[i][p + 2] = v.z; s.x[i][p + 3] = v.w;
-        }
-        for (int e = tid; e < kQ * N / 4; e += kThreads) {
-            const int i = e / (N / 4), n = (e % (N / 4)) * 4;
-            float4 vb = make_float4(0.0f, 0.0f, 0.0f, 0.0f), vc = vb;
-            if (i < nv) {
-                const int64_t o = (bi * L + t0 + i) * N + n;
-                vb = *reinterpret_cast<const float4*>(a.Bm + o);
-                vc = *reinterpret_cast<const float4*>(a.Cm + o);
-            }
-            s.b[i][n] = vb.x; s.b[i][n + 1] = vb.y; s.b[i][n + 2] = vb.z; s.b[i][n + 3] = vb.w;
-            s.c[i][n] = vc.x; s.c[i][n + 1] = vc.y; s.c[i][n + 2] = vc.z; s.c[i][n + 3] = vc.w;
-        }
         if (wv == 0) {
             float d = 0.0f;
             if (lane < nv) {
-                const float v = a.dt[(bi * L + t0 + lane) * H + h] + bias;
+                const float v = g.dt + bias;
                 d = a.softplus ? softplus(v) : v;
             }
             float c = d * Ah;  // inclusive prefix sum over the wave
@@ -136,41 +226,66 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
         }
         __syncthreads();
 
+        // the next chunk's inputs travel while this chunk computes (past the end: no access)
+        load_chunk<N>(a, bi, h, t0 + kQ, tid, g);
+
+        // per-lane LDS base offsets (floats) of the MFMA operands; step k adds a constant
+        const float* cf = &s.c[0][0];
+        const float* bf = &s.b[0][0];
+        const float* xf = &s.x[0][0];
+        const float* mf = &s.m[0][0];
+        const float* stf = &s.st[0][0];
+        const int oc = opaque((ti * 32 + l32) * (N + 1) + hl);                // C[i][k + hl]
+        const int ob = opaque((tj * 32 + l32) * (N + 1) + hl);                // B^T[k + hl][j]
+        const int ost = opaque(hl * (kP + 1) + tj * 32 + l32);                // S^T[k + hl][p]
+        const int om = opaque((ti * 32 + l32) * (kQ + 1) + hl);               // M[i][k + hl]
+        const int ox = opaque(hl * (kP + 1) + tj * 32 + l32);                 // X[k + hl][p]
+        const int oxs = opaque(hl * (kP + 1) + sp * 32 + l32);                // X[j + hl][p] of the state rows
+        const int ob_s = opaque(hl * (N + 1) + (wv & 1) * NT * 32 + l32);     // B[j + hl][n]
+
         // ---- M = (C B^T) o Lmask, tile (ti, tj); the tile above the diagonal is zero ----
         {
-            f32x16 g = {};
-            if (ti >= tj) {
-#pragma unroll 8
-                for (int k = 0; k < N; k += 2)
-                    g = mfma32(s.c[ti * 32 + l32][k + hl], s.b[tj * 32 + l32][k + hl], g);
-            }
+            f32x16 gm = {};
+            if (ti >= tj)
+                gm = mfma_chain<N / 2>(gm, [&](int k, float& av, float& bv) {
+                    av = cf[oc + 2 * k];
+                    bv = bf[ob + 2 * k];
+                });
             const int j = tj * 32 + l32;
             const float cj = s.cum[j], dj = s.dlt[j];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = ti * 32 + acc_row(r, hl);
-                s.m[i][j] = j <= i ? g[r] * fexp(s.cum[i] - cj) * dj : 0.0f;
+                s.m[i][j] = j <= i ? gm[r] * fexp(s.cum[i] - cj) * dj : 0.0f;
             }
         }
         __syncthreads();
 
         // ---- Y tile (ti, tj): exp(cum_i) (C S^T) + M X + D X ----
         {
-            f32x16 y = {};
-#pragma unroll 8
-            for (int k = 0; k < N; k += 2) y = mfma32(s.c[ti * 32 + l32][k + hl], s.st[k + hl][tj * 32 + l32], y);
+            f32x16 y = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
+                av = cf[oc + 2 * k];
+                bv = stf[ost + 2 * k * (kP + 1)];
+            });
 #pragma unroll
             for (int r = 0; r < 16; ++r) y[r] *= fexp(s.cum[ti * 32 + acc_row(r, hl)]);
-            for (int kb = 0; kb <= ti; ++kb) {  // M is zero right of the diagonal tile
-#pragma unroll
-                for (int k = kb * 32; k < kb * 32 + 32; k += 2)
-                    y = mfma32(s.m[ti * 32 + l32][k + hl], s.x[k + hl][tj * 32 + l32], y);
-            }
+            auto ld_mx = [&](int k, float& av, float& bv) {
+                av = mf[om + 2 * k];
+                bv = xf[ox + 2 * k * (kP + 1)];
+            };
+            // M is zero right of the diagonal tile: row block ti contracts over k < (ti + 1) * 32
+            if (ti == 0)
+                y = mfma_chain<16>(y, ld_mx);
+            else
+                y = mfma_chain<32>(y, ld_mx);
+            // rows past the sequence end fall outside the resource and are dropped
+            const auto ry = make_rsrc(a.y + (bi * L + t0) * H * kP, (uint32_t)(nv * H * kP * 4));
             const int p = tj * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = ti * 32 + acc_row(r, hl);
-                if (i < nv) a.y[((bi * L + t0 + i) * H + h) * kP + p] = y[r] + Dh * s.x[i][p];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[r] + Dh * s.x[i][p]), ry,
+                                                      (int)((i * H + h) * kP + p) * 4, 0, 0);
             }
         }
 
@@ -179,12 +294,12 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             const float decay = fexp(s.cum[kQ - 1]);
 #pragma unroll
             for (int k = 0; k < NT; ++k) {
-                const int n0 = ((wv & 1) * NT + k) * 32;
-                f32x16 acc = S[k] * decay;
-#pragma unroll 8
-                for (int j = 0; j < kQ; j += 2)
-                    acc = mfma32(s.w[j + hl] * s.x[j + hl][sp * 32 + l32], s.b[j + hl][n0 + l32], acc);
-                S[k] = acc;
+                const int obs = ob_s + k * 32;
+                S[k] = mfma_chain_scaled<kQ / 2>(S[k] * decay, [&](int j, float& av, float& a2, float& bv) {
+                    av = s.w[2 * j + hl];
+                    a2 = xf[oxs + 2 * j * (kP + 1)];
+                    bv = bf[obs + 2 * j * (N + 1)];
+                });
             }
         }
         __syncthreads();

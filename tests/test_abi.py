@@ -204,6 +204,7 @@ def test_ssd_validation():
         assert ssd(good(**{k: 0})) == -2, k
     assert ssd(good(batch=1 << 20, nheads=1 << 11)) == -2   # B*H >= 2^31
     assert ssd(good(seqlen=1 << 31)) == -2
+    assert ssd(good(batch=1, nheads=1 << 17)) == -2         # H * P >= 2^23
     assert ssd(good(headdim=32)) == -4                      # built for P = 64
     assert ssd(good(dstate=16)) == -4                       # built for N in {64, 128}
     assert ssd(good(dtype=1)) == -4                         # float32 only
