@@ -254,6 +254,34 @@ def time_conv_step(mssm, torch, w, batch, reps=100):
     return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
 
 
+def time_ssd(mssm, torch, B, L, H, N, reps=20):
+    """Mamba-2 (SSD) forward, head dim 64, float32: median us per call (HIP
+    events), and the dense flops of its chunked dual form at 64-step chunks
+    (C B^T, C S^T, M X, and the state update, as full 64 x 64 products)."""
+    inp = workloads.ssd_inputs(B, L, H, 64, N, seed=11)
+    t = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    del inp
+    y = torch.empty_like(t["x"])
+    hf = torch.empty((B, H, 64, N), dtype=torch.float32, device="cuda")
+
+    def run():
+        mssm.ssd_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["dt_bias"], y=y, h_final=hf)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    Q, P = 64, 64
+    flops = B * H * (-(-L // Q)) * 2 * (Q * Q * N + Q * P * N + Q * Q * P + Q * P * N)
+    return us, flops
+
+
 def time_step(mssm, torch, w, reps=200, batch=None):
     """One recurrent step (decode) at the workload's width: (B, D) inputs, the
     (B, D, N) float32 state updated in place; `batch` overrides B (batched
@@ -416,6 +444,10 @@ def main():
         sw = workloads.custom(256, 4, w.D, w.N, w.dtype, seed=w.seed)
         _, sl, _ = time_fwd(mssm, torch, sw, 30, 3)
         out["extra"]["short_fwd_B256_L4_us"] = round(float(np.median(sl)) * 1e3, 1)
+        # Mamba-2 (SSD) layer of the 2.7B shape: 80 heads of 64, d_state 128, B = 8, L = 2048, float32 on MFMA
+        ssd_us, ssd_flops = time_ssd(mssm, torch, 8, 2048, 80, 128)
+        out["extra"]["ssd_fwd_H80_N128_B8_L2048_us"] = round(ssd_us, 1)
+        out["extra"]["ssd_fwd_dense_TFLOPs"] = round(ssd_flops / ssd_us / 1e6, 1)
         tw = workloads.WORKLOADS["train"]
         tb = time_bwd(mssm, torch, tw, 10, 2)
         out.setdefault("extra", {})["train_bwd_us"] = round(tb * 1e6, 1)

@@ -253,10 +253,14 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                 });
             const int j = tj * 32 + l32;
             const float cj = s.cum[j], dj = s.dlt[j];
+            // above the diagonal: exponent -inf and a selected 0 (a non-finite future Bm row must not
+            // reach an earlier output), both as selects rather than a branch around the exponential
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = ti * 32 + acc_row(r, hl);
-                s.m[i][j] = j <= i ? gm[r] * fexp(s.cum[i] - cj) * dj : 0.0f;
+                const bool keep = j <= i;
+                const float v = gm[r] * fexp(keep ? s.cum[i] - cj : -__builtin_inff()) * dj;
+                s.m[i][j] = keep ? v : 0.0f;
             }
         }
         __syncthreads();
