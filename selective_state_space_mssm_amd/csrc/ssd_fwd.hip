@@ -56,15 +56,23 @@ __device__ __forceinline__ int opaque(int v) {
     return v;
 }
 
-// One chunk's operands.  Rows padded by one float so that reading a column
-// (32 rows at one k, the A-operand pattern) hits 32 different banks.
+// Row padding (floats) of the LDS operands: kPadCol for arrays read down a
+// column (32 rows at one k, the A-operand pattern), kPadRow for arrays read
+// along rows by both lane halves (two rows, 32 consecutive columns each).
+constexpr int kPadCol = 1;
+constexpr int kPadRow = 1;
+
+// One chunk's operands.
 template <int N>
 struct SsdSmem {
-    float x[kQ][kP + 1];   // X: the chunk's inputs of this head
-    float b[kQ][N + 1];    // Bm rows
-    float c[kQ][N + 1];    // Cm rows
-    float m[kQ][kQ + 1];   // M = G o Lmask
-    float st[N][kP + 1];   // S^T, the state entering the chunk
+    static constexpr int kSB = N + kPadCol;    // row stride of b, c
+    static constexpr int kSX = kP + kPadRow;   // row stride of x, st
+    static constexpr int kSM = kQ + kPadCol;   // row stride of m
+    float x[kQ][kSX];      // X: the chunk's inputs of this head
+    float b[kQ][kSB];      // Bm rows
+    float c[kQ][kSB];      // Cm rows
+    float m[kQ][kSM];      // M = G o Lmask
+    float st[N][kSX];      // S^T, the state entering the chunk
     float cum[kQ];         // chunk-local cumulative Delta * A_h
     float dlt[kQ];         // Delta (0 past the sequence end)
     float w[kQ];           // exp(cum_last - cum_j) Delta_j
@@ -230,18 +238,19 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
         load_chunk<N>(a, bi, h, t0 + kQ, tid, g);
 
         // per-lane LDS base offsets (floats) of the MFMA operands; step k adds a constant
+        constexpr int SB = SsdSmem<N>::kSB, SX = SsdSmem<N>::kSX, SM = SsdSmem<N>::kSM;
         const float* cf = &s.c[0][0];
         const float* bf = &s.b[0][0];
         const float* xf = &s.x[0][0];
         const float* mf = &s.m[0][0];
         const float* stf = &s.st[0][0];
-        const int oc = opaque((ti * 32 + l32) * (N + 1) + hl);                // C[i][k + hl]
-        const int ob = opaque((tj * 32 + l32) * (N + 1) + hl);                // B^T[k + hl][j]
-        const int ost = opaque(hl * (kP + 1) + tj * 32 + l32);                // S^T[k + hl][p]
-        const int om = opaque((ti * 32 + l32) * (kQ + 1) + hl);               // M[i][k + hl]
-        const int ox = opaque(hl * (kP + 1) + tj * 32 + l32);                 // X[k + hl][p]
-        const int oxs = opaque(hl * (kP + 1) + sp * 32 + l32);                // X[j + hl][p] of the state rows
-        const int ob_s = opaque(hl * (N + 1) + (wv & 1) * NT * 32 + l32);     // B[j + hl][n]
+        const int oc = opaque((ti * 32 + l32) * SB + hl);   // C[i][k + hl]
+        const int ob = opaque((tj * 32 + l32) * SB + hl);   // B^T[k + hl][j]
+        const int ost = opaque(hl * SX + tj * 32 + l32);     // S^T[k + hl][p]
+        const int om = opaque((ti * 32 + l32) * SM + hl);   // M[i][k + hl]
+        const int ox = opaque(hl * SX + tj * 32 + l32);     // X[k + hl][p]
+        const int oxs = opaque(hl * SX + sp * 32 + l32);     // X[j + hl][p] of the state rows
+        const int ob_s = opaque(hl * SB + (wv & 1) * NT * 32 + l32);   // B[j + hl][n]
 
         // ---- M = (C B^T) o Lmask, tile (ti, tj); the tile above the diagonal is zero ----
         {
@@ -269,13 +278,13 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
         {
             f32x16 y = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
                 av = cf[oc + 2 * k];
-                bv = stf[ost + 2 * k * (kP + 1)];
+                bv = stf[ost + 2 * k * SX];
             });
 #pragma unroll
             for (int r = 0; r < 16; ++r) y[r] *= fexp(s.cum[ti * 32 + acc_row(r, hl)]);
             auto ld_mx = [&](int k, float& av, float& bv) {
                 av = mf[om + 2 * k];
-                bv = xf[ox + 2 * k * (kP + 1)];
+                bv = xf[ox + 2 * k * SX];
             };
             // M is zero right of the diagonal tile: row block ti contracts over k < (ti + 1) * 32
             if (ti == 0)
@@ -301,8 +310,8 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                 const int obs = ob_s + k * 32;
                 S[k] = mfma_chain_scaled<kQ / 2>(S[k] * decay, [&](int j, float& av, float& a2, float& bv) {
                     av = s.w[2 * j + hl];
-                    a2 = xf[oxs + 2 * j * (kP + 1)];
-                    bv = bf[obs + 2 * j * (N + 1)];
+                    a2 = xf[oxs + 2 * j * SX];
+                    bv = bf[obs + 2 * j * SB];
                 });
             }
         }
