@@ -116,6 +116,18 @@ __device__ __forceinline__ f32x16 mfma_chain_scaled(f32x16 acc, F&& ld) {
     return acc;
 }
 
+// The (batch, head) a workgroup takes.  Workgroups are dealt to the eight
+// XCDs round robin (workgroup i to XCD i % 8), each XCD with its own L2; this
+// order gives XCD x a contiguous run of (batch, head) pairs, so the heads of a
+// batch, which all read the same Bm and Cm rows, share one L2 instead of each
+// XCD fetching those rows again.  A bijection of [0, n) for any n.
+__device__ __forceinline__ int64_t xcd_order(int64_t i, int64_t n) {
+    constexpr int64_t kXcds = 8;
+    const int64_t per = n / kXcds, rem = n % kXcds;
+    const int64_t x = i % kXcds, slot = i / kXcds;
+    return x * per + (x < rem ? x : rem) + slot;
+}
+
 // One chunk's global inputs, held in registers from the previous chunk's
 // compute until they are staged into LDS.
 template <int N>
@@ -166,7 +178,8 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     const int lane = tid & 63;
     const int l32 = lane & 31, hl = lane >> 5;
     const int64_t H = a.H, L = a.L;
-    const int64_t bi = blockIdx.x / H, h = blockIdx.x % H;
+    const int64_t job = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t bi = job / H, h = job % H;
 
     const float Ah = a.A[h];
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
