@@ -263,7 +263,8 @@ mssm_status mssm_conv_step(const mssm_problem* p, int32_t d_conv,
  * Built for headdim P = 64 and dstate N in {64, 128}, float32 only: other
  * sizes or dtype MSSM_BF16 -> MSSM_ERR_UNSUPPORTED.  Other errors as
  * mssm_scan_fwd; batch * nheads must be below 2^31 and nheads * headdim below
- * 2^23 (else MSSM_ERR_SHAPE).  No workspace.
+ * 2^23 (else MSSM_ERR_SHAPE).  workspace as mssm_scan_fwd's, sized by
+ * mssm_ssd_fwd_workspace_bytes.
  */
 typedef struct {
     int64_t batch;          /* B */
@@ -275,9 +276,17 @@ typedef struct {
     int32_t delta_softplus; /* nonzero: Delta = softplus(dt + dt_bias) */
 } mssm_ssd_problem;
 
+/* Bytes of device scratch mssm_ssd_fwd needs: 0 when there are at least 128
+ * (batch, head) pairs or the sequence is shorter than 4 chunks; otherwise the
+ * sequence is cut into time segments scanned in parallel, and the scratch
+ * holds each segment's state and log-decay, (B * H * segments * (P * N + 1))
+ * floats.  0 for an invalid problem. */
+size_t mssm_ssd_fwd_workspace_bytes(const mssm_ssd_problem* p);
+
 mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const float* x, const float* dt, const float* A,
                          const float* Bm, const float* Cm, const float* Dskip, const float* dt_bias,
-                         const float* h0, float* y, float* h_final, void* hip_stream);
+                         const float* h0, float* y, float* h_final,
+                         void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Static, human-readable name of a status code. */
 const char* mssm_status_string(mssm_status s);

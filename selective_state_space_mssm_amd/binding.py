@@ -23,7 +23,7 @@ STATUS = {0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_SHAPE", -3: "MSSM_ERR
           -7: "MSSM_ERR_HIP"}
 EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd",
            "mssm_conv_scan_fwd", "mssm_conv_bwd_workspace_bytes", "mssm_conv_bwd", "mssm_scan_bwd", "mssm_step",
-           "mssm_conv_step", "mssm_ssd_fwd", "mssm_status_string", "mssm_build_info"]
+           "mssm_conv_step", "mssm_ssd_fwd_workspace_bytes", "mssm_ssd_fwd", "mssm_status_string", "mssm_build_info"]
 MAX_DCONV = 4
 
 
@@ -72,7 +72,9 @@ def _open(path: str):
     lib.mssm_step.restype = st
     lib.mssm_conv_step.argtypes = [P, ctypes.c_int32] + [vp] * 13 + [vp]
     lib.mssm_conv_step.restype = st
-    lib.mssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdProblem)] + [vp] * 10 + [vp]
+    lib.mssm_ssd_fwd_workspace_bytes.argtypes = [ctypes.POINTER(SsdProblem)]
+    lib.mssm_ssd_fwd_workspace_bytes.restype = sz
+    lib.mssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdProblem)] + [vp] * 10 + [vp, sz, vp]
     lib.mssm_ssd_fwd.restype = st
     lib.mssm_status_string.argtypes = [st]
     lib.mssm_status_string.restype = ctypes.c_char_p
@@ -380,7 +382,7 @@ def conv_step(x_t, conv_w, conv_state, delta_t, A, Bm_t, Cm_t, state, Dskip=None
 
 
 def ssd_fwd(x, dt, A, Bm, Cm, Dskip=None, dt_bias=None, h0=None, delta_softplus=True,
-            return_final_state=True, y=None, h_final=None):
+            return_final_state=True, y=None, h_final=None, workspace=None):
     """Mamba-2 (SSD) forward.  x: (B, L, H, P); dt: (B, L, H); Bm, Cm: (B, L, N);
     A, Dskip, dt_bias: (H); h0: (B, H, P, N); all float32.  Returns (y, h_final)
     (h_final None unless requested)."""
@@ -402,6 +404,8 @@ def ssd_fwd(x, dt, A, Bm, Cm, Dskip=None, dt_bias=None, h0=None, delta_softplus=
         h_final = torch.empty((B, H, P, N), dtype=f, device=x.device)
     _opt(h_final, "h_final", (B, H, P, N), f)
     prob = SsdProblem(B, L, H, P, N, MSSM_F32, 1 if delta_softplus else 0)
+    nbytes = int(lib.mssm_ssd_fwd_workspace_bytes(ctypes.byref(prob)))
+    ws = _workspace(nbytes, x.device, workspace)
     _check(lib.mssm_ssd_fwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
-                            _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _stream(x.device)))
+                            _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(ws), nbytes, _stream(x.device)))
     return y, h_final

@@ -21,6 +21,10 @@ struct SsdArgs {
     const float* h0;       // may be null
     float* y;
     float* h_final;        // may be null
+    // time segments scanned in parallel (1: the whole sequence in one pass)
+    int64_t nseg;
+    int64_t seg_len;       // steps per segment, a multiple of the chunk length (L when nseg == 1)
+    float* ws;             // nseg > 1: segment states (B, H, nseg, P, N), then log-decays (B, H, nseg)
 };
 
 constexpr int kSsdHeadDim = 64;   // P the kernel is built for
@@ -28,6 +32,34 @@ constexpr int kSsdChunk = 64;     // chunk length of the dual form
 
 // True when the kernel is built for this head dimension and state size.
 inline bool ssd_supported(int64_t P, int64_t N) { return P == kSsdHeadDim && (N == 64 || N == 128); }
+
+// How the sequence is cut: with fewer (batch, head) pairs than half the 256
+// CUs, the sequence splits into segments of at least two chunks, enough to
+// give about 256 workgroups; each segment is scanned from a zero state, a
+// carry pass forms the state entering every segment, and a correction pass
+// adds that state's contribution to the segment's outputs.
+struct SsdPlan {
+    int64_t nseg;
+    int64_t seg_len;
+    size_t ws_bytes;
+};
+
+inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N) {
+    SsdPlan pl{1, L, 0};
+    const int64_t jobs = B * H, chunks = (L + kSsdChunk - 1) / kSsdChunk;
+    if (jobs >= 128 || chunks < 4) return pl;
+    const int64_t want = (256 + jobs - 1) / jobs, most = chunks / 2;
+    const int64_t segs = want < most ? want : most;
+    const int64_t per = (chunks + segs - 1) / segs;  // chunks per segment
+    pl.seg_len = per * kSsdChunk;
+    pl.nseg = (L + pl.seg_len - 1) / pl.seg_len;
+    if (pl.nseg == 1) {
+        pl.seg_len = L;
+        return pl;
+    }
+    pl.ws_bytes = static_cast<size_t>(jobs * pl.nseg * (P * N + 1)) * sizeof(float);
+    return pl;
+}
 
 hipError_t launch_ssd_fwd(const SsdArgs& a, hipStream_t st);
 

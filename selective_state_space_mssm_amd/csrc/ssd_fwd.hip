@@ -139,14 +139,14 @@ struct ChunkRegs {
 };
 
 // Loads chunk [t0, t0 + 64) into registers through buffer resources that
-// cover only the chunk's valid rows: a row past the sequence end lies outside
+// cover only the chunk's valid rows (those before t_end): a row past the sequence end lies outside
 // its resource and reads as zeros, with no branch and no address select (a
 // chunk wholly past the end has an empty resource and touches no memory).
 template <int N>
-__device__ __forceinline__ void load_chunk(const SsdArgs& a, int64_t bi, int64_t h, int64_t t0, int tid,
-                                           ChunkRegs<N>& g) {
+__device__ __forceinline__ void load_chunk(const SsdArgs& a, int64_t bi, int64_t h, int64_t t0, int64_t t_end,
+                                           int tid, ChunkRegs<N>& g) {
     const int64_t H = a.H, L = a.L;
-    const int64_t nv = L - t0 < 0 ? 0 : imin64(kQ, L - t0);
+    const int64_t nv = t_end - t0 < 0 ? 0 : imin64(kQ, t_end - t0);
     const int64_t row0 = bi * L + t0;
     const auto rx = make_rsrc(a.x + row0 * H * kP, (uint32_t)(nv * H * kP * 4));
     const auto rb = make_rsrc(a.Bm + row0 * N, (uint32_t)(nv * N * 4));
@@ -178,8 +178,10 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     const int lane = tid & 63;
     const int l32 = lane & 31, hl = lane >> 5;
     const int64_t H = a.H, L = a.L;
+    // job = (batch, head, time segment); the segment's steps are [t_begin, t_end)
     const int64_t job = xcd_order(blockIdx.x, gridDim.x);
-    const int64_t bi = job / H, h = job % H;
+    const int64_t seg = job % a.nseg, bi = job / a.nseg / H, h = job / a.nseg % H;
+    const int64_t t_begin = seg * a.seg_len, t_end = imin64(L, t_begin + a.seg_len);
 
     const float Ah = a.A[h];
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     const int sp = wv >> 1;
     const int64_t state_base = (bi * H + h) * kP * N;
     f32x16 S[NT];
-    if (a.h0) {
+    if (a.h0 && seg == 0) {  // later segments start from zero; the carry pass supplies their state
 #pragma unroll
         for (int k = 0; k < NT; ++k) {
             const int n = ((wv & 1) * NT + k) * 32 + l32;
@@ -205,10 +207,11 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     const int ti = wv >> 1, tj = wv & 1;
 
     ChunkRegs<N> g;
-    load_chunk<N>(a, bi, h, 0, tid, g);
+    load_chunk<N>(a, bi, h, t_begin, t_end, tid, g);
+    float lam = 0.0f;  // the segment's total log-decay, sum of Delta A_h
 
-    for (int64_t t0 = 0; t0 < L; t0 += kQ) {
-        const int nv = (int)imin64(kQ, L - t0);
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kQ) {
+        const int nv = (int)imin64(kQ, t_end - t0);
 
         // ---- stage: the chunk's operands and S^T into LDS; cum, Delta, w ----
 #pragma unroll
@@ -248,7 +251,8 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
         __syncthreads();
 
         // the next chunk's inputs travel while this chunk computes (past the end: no access)
-        load_chunk<N>(a, bi, h, t0 + kQ, tid, g);
+        load_chunk<N>(a, bi, h, t0 + kQ, t_end, tid, g);
+        lam += s.cum[kQ - 1];
 
         // per-lane LDS base offsets (floats) of the MFMA operands; step k adds a constant
         constexpr int SB = SsdSmem<N>::kSB, SX = SsdSmem<N>::kSX, SM = SsdSmem<N>::kSM;
@@ -331,25 +335,132 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
         __syncthreads();
     }
 
-    if (a.h_final) {
+    // one segment: the final state; several: this segment's state from zero and its log-decay, for the carry pass
+    float* out = a.nseg > 1 ? a.ws + ((bi * H + h) * a.nseg + seg) * kP * N : a.h_final ? a.h_final + state_base : nullptr;
+    if (out) {
 #pragma unroll
         for (int k = 0; k < NT; ++k) {
             const int n = ((wv & 1) * NT + k) * 32 + l32;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                a.h_final[state_base + (int64_t)(sp * 32 + acc_row(r, hl)) * N + n] = S[k][r];
+            for (int r = 0; r < 16; ++r) out[(int64_t)(sp * 32 + acc_row(r, hl)) * N + n] = S[k][r];
         }
+    }
+    if (a.nseg > 1 && tid == 0) a.ws[a.B * H * a.nseg * kP * N + (bi * H + h) * a.nseg + seg] = lam;
+}
+
+// Carry pass over the segments, one thread per (batch, head, p, n): the state
+// entering segment k is exp(lam_{k-1}) times the state entering k - 1 plus
+// segment k - 1's own final state.  Segment 0 was scanned from h0, so its
+// final state is already exact and the carry starts from zero.  Each entering
+// state replaces the segment's slot in the workspace; the last carry is h_final.
+__global__ __launch_bounds__(256) void ssd_carry_kernel(SsdArgs a) {
+    const int64_t PN = a.P * a.N, e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= a.B * a.H * PN) return;
+    const int64_t bh = e / PN, pn = e % PN;
+    const float* lam = a.ws + a.B * a.H * a.nseg * PN + bh * a.nseg;
+    float cur = 0.0f;
+    for (int64_t k = 0; k < a.nseg; ++k) {
+        float* slot = a.ws + (bh * a.nseg + k) * PN + pn;
+        const float loc = *slot;
+        *slot = cur;
+        cur = fexp(lam[k]) * cur + loc;
+    }
+    if (a.h_final) a.h_final[e] = cur;
+}
+
+// Correction pass, one workgroup per (batch, head, segment k >= 1): adds the
+// entering state's contribution exp(cum_t) C_t S_in^T to every output row of
+// the segment, cum_t being the log-decay from the segment's start through t.
+template <int N>
+struct SsdCorrSmem {
+    float c[kQ][N + kPadCol];
+    float st[N][kP + kPadRow];
+    float cum[kQ];
+};
+
+template <int N>
+__global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
+    __shared__ SsdCorrSmem<N> s;
+    constexpr int SB = N + kPadCol, SX = kP + kPadRow;
+    const int tid = threadIdx.x;
+    const int wv = wave_id();
+    const int lane = tid & 63;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int64_t H = a.H, L = a.L, S1 = a.nseg - 1;
+    const int64_t job = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t seg = job % S1 + 1, bi = job / S1 / H, h = job / S1 % H;
+    const int64_t t_begin = seg * a.seg_len, t_end = imin64(L, t_begin + a.seg_len);
+    const float Ah = a.A[h];
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const int ti = wv >> 1, tj = wv & 1;
+
+    // S_in^T into LDS, once: the state is the same for the whole segment
+    const float* sin = a.ws + ((bi * H + h) * a.nseg + seg) * kP * N;
+    for (int e = tid; e < kP * N; e += kThreads) s.st[e % N][e / N] = sin[e];
+
+    float carry = 0.0f;  // log-decay from the segment's start to the current chunk's start
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += kQ) {
+        const int nv = (int)imin64(kQ, t_end - t0);
+        const int64_t row0 = bi * L + t0;
+        const auto rc = make_rsrc(a.Cm + row0 * N, (uint32_t)(nv * N * 4));
+        for (int e = tid; e < kQ * N / 4; e += kThreads) {
+            const int i = e / (N / 4), n = (e % (N / 4)) * 4;
+            const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, (i * N + n) * 4, 0, 0));
+            s.c[i][n] = v.x; s.c[i][n + 1] = v.y; s.c[i][n + 2] = v.z; s.c[i][n + 3] = v.w;
+        }
+        if (wv == 0) {
+            const auto rd = make_rsrc(a.dt + row0 * H, (uint32_t)(nv * H * 4));
+            const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)(lane * H + h) * 4, 0, 0)) + bias;
+            float c = lane < nv ? (a.softplus ? softplus(v) : v) * Ah : 0.0f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float o = __shfl_up(c, off);
+                if (lane >= off) c += o;
+            }
+            s.cum[lane] = carry + c;
+        }
+        __syncthreads();
+
+        const int oc = opaque((ti * 32 + l32) * SB + hl);
+        const int ost = opaque(hl * SX + tj * 32 + l32);
+        const float* cf = &s.c[0][0];
+        const float* stf = &s.st[0][0];
+        f32x16 y = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
+            av = cf[oc + 2 * k];
+            bv = stf[ost + 2 * k * SX];
+        });
+        // add into the segment's outputs; rows past the end fall outside the resource
+        const auto ry = make_rsrc(a.y + row0 * H * kP, (uint32_t)(nv * H * kP * 4));
+        const int p = tj * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = ti * 32 + acc_row(r, hl);
+            const int off = (int)((i * H + h) * kP + p) * 4;
+            const float old = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ry, off, 0, 0));
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(old + y[r] * fexp(s.cum[i])), ry, off, 0, 0);
+        }
+        carry = s.cum[kQ - 1];
+        __syncthreads();
     }
 }
 
 }  // namespace
 
 hipError_t launch_ssd_fwd(const SsdArgs& a, hipStream_t st) {
-    const dim3 grid((unsigned)(a.B * a.H)), block(kThreads);
+    const dim3 grid((unsigned)(a.B * a.H * a.nseg)), block(kThreads);
     if (a.N == 64)
         hipLaunchKernelGGL(ssd_fwd_kernel<64>, grid, block, 0, st, a);
     else
         hipLaunchKernelGGL(ssd_fwd_kernel<128>, grid, block, 0, st, a);
+    if (a.nseg > 1) {
+        const int64_t n = a.B * a.H * a.P * a.N;
+        hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+        const dim3 cgrid((unsigned)(a.B * a.H * (a.nseg - 1)));
+        if (a.N == 64)
+            hipLaunchKernelGGL(ssd_correct_kernel<64>, cgrid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL(ssd_correct_kernel<128>, cgrid, block, 0, st, a);
+    }
     return hipGetLastError();
 }
 

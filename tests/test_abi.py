@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), f"libmssm.so does not export {n}"
     assert sorted(mssm.EXPORTS) == names
@@ -191,7 +191,9 @@ def ssd(p, **kw):
     required = {"x", "dt", "A", "Bm", "Cm", "y"}
     args = [None if kw.get(n, FAKE if n in required else None) is None else
             ctypes.c_void_p(kw.get(n, FAKE)) for n in names]
-    return lib.mssm_ssd_fwd(ctypes.byref(p) if p is not None else None, *args, None)
+    ws = kw.get("ws", None)
+    return lib.mssm_ssd_fwd(ctypes.byref(p) if p is not None else None, *args,
+                            None if ws is None else ctypes.c_void_p(ws), kw.get("wsb", 0), None)
 
 
 def test_ssd_validation():
@@ -212,6 +214,14 @@ def test_ssd_validation():
         assert ssd(good(), **{n: None}) == -1, n
     for n in ("x", "dt", "A", "Bm", "Cm", "Dskip", "dt_bias", "h0", "y", "h_final"):
         assert ssd(good(), **{n: MIS}) == -5, n
+    # few (batch, head) pairs: the sequence is cut into segments and scratch is required
+    q = lambda **k: lib.mssm_ssd_fwd_workspace_bytes(ctypes.byref(good(**k)))  # noqa: E731
+    need = q(seqlen=1000)  # 6 pairs, 16 chunks: 8 segments of 128 steps
+    assert need == 6 * 8 * (64 * 64 + 1) * 4
+    assert q() == 0 and q(seqlen=1000, batch=64, nheads=2) == 0 and q(seqlen=1000, dstate=16) == 0
+    assert ssd(good(seqlen=1000)) == -6
+    assert ssd(good(seqlen=1000), ws=FAKE, wsb=need - 1) == -6
+    assert ssd(good(seqlen=1000), ws=MIS, wsb=need) == -5
 
 
 def test_workspace_sizes_and_checks():

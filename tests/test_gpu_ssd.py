@@ -100,3 +100,22 @@ def test_ssd_mamba2_layer_sampled(lib):
                             inp["dt_bias"][heads])
     assert fwd_err(to_np(y[:, :, heads]), yr) <= TOL
     assert fwd_err(to_np(hf[:, heads]), hr) <= TOL
+
+
+@pytest.mark.parametrize("B,L,H,N", [(1, 2048, 24, 128), (1, 700, 3, 64), (2, 1100, 1, 64)])
+def test_ssd_time_segments(lib, B, L, H, N):
+    # few (batch, head) pairs: the sequence is cut into segments scanned in parallel, then a carry pass and a
+    # correction pass (mssm_ssd_fwd_workspace_bytes > 0); with h0, the state advanced in place, every optional input
+    import ctypes
+    prob = lib.binding.SsdProblem(B, L, H, 64, N, 0, 1)
+    assert lib.lib.mssm_ssd_fwd_workspace_bytes(ctypes.byref(prob)) > 0
+    print(f"[ssd segments] B={B} L={L} H={H} N={N}", flush=True)
+    inp = workloads.ssd_inputs(B, L, H, 64, N, seed=L + H)
+    t = gpu(inp)
+    h0n = np.random.default_rng(H).standard_normal((B, H, 64, N)).astype(np.float32)
+    state = torch.from_numpy(h0n).cuda()
+    y, _ = lib.ssd_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["dt_bias"], state, h_final=state)
+    torch.cuda.synchronize()
+    yr, hr = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["Bm"], inp["Cm"], inp["Dskip"], inp["dt_bias"], h0n)
+    assert fwd_err(to_np(y), yr) <= TOL
+    assert fwd_err(to_np(state), hr) <= TOL
