@@ -448,6 +448,9 @@ def main():
         ssd_us, ssd_flops = time_ssd(mssm, torch, 8, 2048, 80, 128)
         out["extra"]["ssd_fwd_H80_N128_B8_L2048_us"] = round(ssd_us, 1)
         out["extra"]["ssd_fwd_dense_TFLOPs"] = round(ssd_flops / ssd_us / 1e6, 1)
+        # batch-1 prefill of a 24-head layer (Mamba-2 130M shape): time segments scanned in parallel
+        ssd_us, _ = time_ssd(mssm, torch, 1, 2048, 24, 128)
+        out["extra"]["ssd_fwd_H24_N128_B1_L2048_us"] = round(ssd_us, 1)
         tw = workloads.WORKLOADS["train"]
         tb = time_bwd(mssm, torch, tw, 10, 2)
         out.setdefault("extra", {})["train_bwd_us"] = round(tb * 1e6, 1)
