@@ -398,19 +398,34 @@ __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
     const float* sin = a.ws + ((bi * H + h) * a.nseg + seg) * kP * N;
     for (int e = tid; e < kP * N; e += kThreads) s.st[e % N][e / N] = sin[e];
 
+    // one chunk's Cm rows and step sizes, loaded a chunk ahead; rows past the segment's end read zeros
+    constexpr int kC = kQ * N / 4 / kThreads;
+    float4 cr[kC];
+    float dtv;
+    auto load = [&](int64_t t0) {
+        const int64_t nv = t_end - t0 < 0 ? 0 : imin64(kQ, t_end - t0), row0 = bi * L + t0;
+        const auto rc = make_rsrc(a.Cm + row0 * N, (uint32_t)(nv * N * 4));
+#pragma unroll
+        for (int e = 0; e < kC; ++e) {
+            const int q = e * kThreads + tid, i = q / (N / 4), n = (q % (N / 4)) * 4;
+            cr[e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, (i * N + n) * 4, 0, 0));
+        }
+        const auto rd = make_rsrc(a.dt + row0 * H, (uint32_t)(nv * H * 4));
+        dtv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)(lane * H + h) * 4, 0, 0));
+    };
+    load(t_begin);
+
     float carry = 0.0f;  // log-decay from the segment's start to the current chunk's start
     for (int64_t t0 = t_begin; t0 < t_end; t0 += kQ) {
         const int nv = (int)imin64(kQ, t_end - t0);
         const int64_t row0 = bi * L + t0;
-        const auto rc = make_rsrc(a.Cm + row0 * N, (uint32_t)(nv * N * 4));
-        for (int e = tid; e < kQ * N / 4; e += kThreads) {
-            const int i = e / (N / 4), n = (e % (N / 4)) * 4;
-            const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, (i * N + n) * 4, 0, 0));
-            s.c[i][n] = v.x; s.c[i][n + 1] = v.y; s.c[i][n + 2] = v.z; s.c[i][n + 3] = v.w;
+#pragma unroll
+        for (int e = 0; e < kC; ++e) {
+            const int q = e * kThreads + tid, i = q / (N / 4), n = (q % (N / 4)) * 4;
+            s.c[i][n] = cr[e].x; s.c[i][n + 1] = cr[e].y; s.c[i][n + 2] = cr[e].z; s.c[i][n + 3] = cr[e].w;
         }
         if (wv == 0) {
-            const auto rd = make_rsrc(a.dt + row0 * H, (uint32_t)(nv * H * 4));
-            const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)(lane * H + h) * 4, 0, 0)) + bias;
+            const float v = dtv + bias;
             float c = lane < nv ? (a.softplus ? softplus(v) : v) * Ah : 0.0f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -420,7 +435,17 @@ __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
             s.cum[lane] = carry + c;
         }
         __syncthreads();
+        load(t0 + kQ);  // the next chunk's inputs travel during this chunk (past the end: no access)
 
+        // the outputs this lane adds to, read before the products; rows past the end fall outside the resource
+        const auto ry = make_rsrc(a.y + row0 * H * kP, (uint32_t)(nv * H * kP * 4));
+        const int p = tj * 32 + l32;
+        float old[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = ti * 32 + acc_row(r, hl);
+            old[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ry, (int)((i * H + h) * kP + p) * 4, 0, 0));
+        }
         const int oc = opaque((ti * 32 + l32) * SB + hl);
         const int ost = opaque(hl * SX + tj * 32 + l32);
         const float* cf = &s.c[0][0];
@@ -429,15 +454,11 @@ __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
             av = cf[oc + 2 * k];
             bv = stf[ost + 2 * k * SX];
         });
-        // add into the segment's outputs; rows past the end fall outside the resource
-        const auto ry = make_rsrc(a.y + row0 * H * kP, (uint32_t)(nv * H * kP * 4));
-        const int p = tj * 32 + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = ti * 32 + acc_row(r, hl);
-            const int off = (int)((i * H + h) * kP + p) * 4;
-            const float old = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ry, off, 0, 0));
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(old + y[r] * fexp(s.cum[i])), ry, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(old[r] + y[r] * fexp(s.cum[i])), ry,
+                                                  (int)((i * H + h) * kP + p) * 4, 0, 0);
         }
         carry = s.cum[kQ - 1];
         __syncthreads();
