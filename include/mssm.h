@@ -255,13 +255,15 @@ mssm_status mssm_conv_step(const mssm_problem* p, int32_t d_conv,
  * i.e. mssm_scan_fwd over the H * P channels d = h * P + p with
  * A[d, n] = A[h], delta[b,t,d] = dt[b,t,h], Dskip[d] = Dskip[h].  Computed in
  * chunks of 64 steps as dense products on the matrix cores.
- *   x, y       (B, L, H, P) float32        dt        (B, L, H) float32
- *   Bm, Cm     (B, L, N) float32           A, Dskip, dt_bias  (H) float32
+ *   x, y       (B, L, H, P)                dt        (B, L, H)
+ *   Bm, Cm     (B, L, N)                   A, Dskip, dt_bias  (H) float32
  *   h0, h_final (B, H, P, N) float32
+ * x, dt, Bm, Cm and y in p->dtype (MSSM_F32 or MSSM_BF16); arithmetic float32
+ * throughout, bfloat16 outputs rounded to nearest even.
  * Required: p, x, dt, A, Bm, Cm, y.  Optional (NULL): Dskip, dt_bias (-> 0),
  * h0 (-> zeros), h_final (not written; may be the same buffer as h0).
- * Built for headdim P = 64 and dstate N in {64, 128}, float32 only: other
- * sizes or dtype MSSM_BF16 -> MSSM_ERR_UNSUPPORTED.  Other errors as
+ * Built for headdim P = 64 and dstate N in {64, 128}: other sizes ->
+ * MSSM_ERR_UNSUPPORTED.  Other errors as
  * mssm_scan_fwd; batch * nheads must be below 2^31 and nheads * headdim below
  * 2^23 (else MSSM_ERR_SHAPE).  workspace as mssm_scan_fwd's, sized by
  * mssm_ssd_fwd_workspace_bytes.
@@ -272,7 +274,7 @@ typedef struct {
     int64_t nheads;         /* H */
     int64_t headdim;        /* P */
     int64_t dstate;         /* N */
-    int32_t dtype;          /* mssm_dtype; only MSSM_F32 is built */
+    int32_t dtype;          /* mssm_dtype of x, dt, Bm, Cm, y */
     int32_t delta_softplus; /* nonzero: Delta = softplus(dt + dt_bias) */
 } mssm_ssd_problem;
 
@@ -283,9 +285,9 @@ typedef struct {
  * floats.  0 for an invalid problem. */
 size_t mssm_ssd_fwd_workspace_bytes(const mssm_ssd_problem* p);
 
-mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const float* x, const float* dt, const float* A,
-                         const float* Bm, const float* Cm, const float* Dskip, const float* dt_bias,
-                         const float* h0, float* y, float* h_final,
+mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                         const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                         const float* h0, void* y, float* h_final,
                          void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Static, human-readable name of a status code. */

@@ -383,27 +383,27 @@ def conv_step(x_t, conv_w, conv_state, delta_t, A, Bm_t, Cm_t, state, Dskip=None
 
 def ssd_fwd(x, dt, A, Bm, Cm, Dskip=None, dt_bias=None, h0=None, delta_softplus=True,
             return_final_state=True, y=None, h_final=None, workspace=None):
-    """Mamba-2 (SSD) forward.  x: (B, L, H, P); dt: (B, L, H); Bm, Cm: (B, L, N);
-    A, Dskip, dt_bias: (H); h0: (B, H, P, N); all float32.  Returns (y, h_final)
-    (h_final None unless requested)."""
+    """Mamba-2 (SSD) forward.  x: (B, L, H, P); dt: (B, L, H); Bm, Cm: (B, L, N),
+    all float32 or all bfloat16; A, Dskip, dt_bias: (H); h0: (B, H, P, N):
+    float32.  Returns (y, h_final) (y in x's dtype; h_final None unless requested)."""
     B, L, H, P = x.shape
     N = Bm.shape[2]
-    f = torch.float32
-    _req(x, "x", (B, L, H, P), f)
-    _req(dt, "dt", (B, L, H), f)
+    f, act = torch.float32, x.dtype
+    _req(x, "x", (B, L, H, P), act)
+    _req(dt, "dt", (B, L, H), act)
     _req(A, "A", (H,), f)
-    _req(Bm, "Bm", (B, L, N), f)
-    _req(Cm, "Cm", (B, L, N), f)
+    _req(Bm, "Bm", (B, L, N), act)
+    _req(Cm, "Cm", (B, L, N), act)
     _opt(Dskip, "Dskip", (H,), f)
     _opt(dt_bias, "dt_bias", (H,), f)
     _opt(h0, "h0", (B, H, P, N), f)
     if y is None:
-        y = torch.empty((B, L, H, P), dtype=f, device=x.device)
-    _req(y, "y", (B, L, H, P), f)
+        y = torch.empty((B, L, H, P), dtype=act, device=x.device)
+    _req(y, "y", (B, L, H, P), act)
     if return_final_state and h_final is None:
         h_final = torch.empty((B, H, P, N), dtype=f, device=x.device)
     _opt(h_final, "h_final", (B, H, P, N), f)
-    prob = SsdProblem(B, L, H, P, N, MSSM_F32, 1 if delta_softplus else 0)
+    prob = SsdProblem(B, L, H, P, N, _dtype_code(x), 1 if delta_softplus else 0)
     nbytes = int(lib.mssm_ssd_fwd_workspace_bytes(ctypes.byref(prob)))
     ws = _workspace(nbytes, x.device, workspace)
     _check(lib.mssm_ssd_fwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),

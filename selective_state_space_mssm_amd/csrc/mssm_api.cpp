@@ -214,7 +214,7 @@ mssm_status check_ssd_problem(const mssm_ssd_problem* p) {
     if (p->batch < 1 || p->seqlen < 1 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1) return MSSM_ERR_SHAPE;
     if (p->batch * p->nheads >= (int64_t{1} << 31) || p->seqlen >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
     if (p->nheads * p->headdim >= (int64_t{1} << 23)) return MSSM_ERR_SHAPE;  // a 64-step chunk stays below 2^31 bytes
-    if (p->dtype != MSSM_F32 || !mssm::ssd_supported(p->headdim, p->dstate)) return MSSM_ERR_UNSUPPORTED;
+    if (!mssm::ssd_supported(p->headdim, p->dstate)) return MSSM_ERR_UNSUPPORTED;
     return MSSM_OK;
 }
 }  // namespace
@@ -224,9 +224,9 @@ size_t mssm_ssd_fwd_workspace_bytes(const mssm_ssd_problem* p) {
     return mssm::plan_ssd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate).ws_bytes;
 }
 
-mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const float* x, const float* dt, const float* A,
-                         const float* Bm, const float* Cm, const float* Dskip, const float* dt_bias,
-                         const float* h0, float* y, float* h_final,
+mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                         const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                         const float* h0, void* y, float* h_final,
                          void* workspace, size_t workspace_bytes, void* hip_stream) {
     const mssm_status chk = check_ssd_problem(p);
     if (chk != MSSM_OK) return chk;
@@ -239,6 +239,7 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const float* x, const float*
     mssm::SsdArgs a{};
     a.B = p->batch; a.L = p->seqlen; a.H = p->nheads; a.P = p->headdim; a.N = p->dstate;
     a.softplus = p->delta_softplus ? 1 : 0;
+    a.dtype = p->dtype == MSSM_BF16 ? 1 : 0;
     a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm;
     a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0; a.y = y; a.h_final = h_final;
     a.nseg = plan.nseg; a.seg_len = plan.seg_len; a.ws = static_cast<float*>(workspace);

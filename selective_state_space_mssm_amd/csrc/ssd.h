@@ -7,19 +7,21 @@
 namespace mssm {
 
 // Validated arguments of one SSD forward: x, y (B, L, H, P); dt (B, L, H);
-// Bm, Cm (B, L, N); A, Dskip, dt_bias (H); h0, h_final (B, H, P, N).  Float32.
+// Bm, Cm (B, L, N) in the activation type (float32 or bfloat16 bits, `dtype`);
+// A, Dskip, dt_bias (H); h0, h_final (B, H, P, N) float32.
 struct SsdArgs {
     int64_t B, L, H, P, N;
     int softplus;
-    const float* x;
-    const float* dt;
+    int dtype;             // 0: float32 activations, 1: bfloat16
+    const void* x;
+    const void* dt;
     const float* A;
-    const float* Bm;
-    const float* Cm;
+    const void* Bm;
+    const void* Cm;
     const float* Dskip;    // may be null
     const float* dt_bias;  // may be null
     const float* h0;       // may be null
-    float* y;
+    void* y;
     float* h_final;        // may be null
     // time segments scanned in parallel (1: the whole sequence in one pass)
     int64_t nseg;

@@ -46,6 +46,26 @@ __device__ __forceinline__ int acc_row(int r, int hl) { return (r >> 2) * 8 + hl
 
 __device__ __forceinline__ float fexp(float x) { return fast_exp2(x * kLog2e); }
 
+// Activation access through a buffer resource, by element offset: T = float,
+// or uint16_t holding bfloat16 bits (widened exactly to float32).
+__device__ __forceinline__ float4 load4(const float*, __amdgpu_buffer_rsrc_t r, int e) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, 0));
+}
+__device__ __forceinline__ float4 load4(const uint16_t*, __amdgpu_buffer_rsrc_t r, int e) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, e * 2, 0, 0);
+    return make_float4(bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1]));
+}
+__device__ __forceinline__ float load1(const float*, __amdgpu_buffer_rsrc_t r, int e) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, e * 4, 0, 0));
+}
+__device__ __forceinline__ float load1(const uint16_t*, __amdgpu_buffer_rsrc_t r, int e) {
+    return bf16_lo(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, e * 2, 0, 0)));
+}
+template <class T>
+__device__ __forceinline__ void store1(float v, __amdgpu_buffer_rsrc_t r, int e) {
+    buffer_store_act(v, r, static_cast<uint32_t>(e) * sizeof(T), T{});
+}
+
 // An integer the compiler must treat as unknown at this point (an empty asm
 // statement, no instruction).  Recomputing a lane's LDS base offsets through
 // it once per chunk keeps them out of loop-invariant hoisting: each step's
@@ -142,34 +162,33 @@ struct ChunkRegs {
 // cover only the chunk's valid rows (those before t_end): a row past the sequence end lies outside
 // its resource and reads as zeros, with no branch and no address select (a
 // chunk wholly past the end has an empty resource and touches no memory).
-template <int N>
+template <class T, int N>
 __device__ __forceinline__ void load_chunk(const SsdArgs& a, int64_t bi, int64_t h, int64_t t0, int64_t t_end,
                                            int tid, ChunkRegs<N>& g) {
     const int64_t H = a.H, L = a.L;
     const int64_t nv = t_end - t0 < 0 ? 0 : imin64(kQ, t_end - t0);
     const int64_t row0 = bi * L + t0;
-    const auto rx = make_rsrc(a.x + row0 * H * kP, (uint32_t)(nv * H * kP * 4));
-    const auto rb = make_rsrc(a.Bm + row0 * N, (uint32_t)(nv * N * 4));
-    const auto rc = make_rsrc(a.Cm + row0 * N, (uint32_t)(nv * N * 4));
-    const auto rd = make_rsrc(a.dt + row0 * H, (uint32_t)(nv * H * 4));
+    const T* x = static_cast<const T*>(a.x);
+    const auto rx = make_rsrc(x + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
+    const auto rb = make_rsrc(static_cast<const T*>(a.Bm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
+    const auto rc = make_rsrc(static_cast<const T*>(a.Cm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
+    const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
 #pragma unroll
     for (int e = 0; e < ChunkRegs<N>::kX; ++e) {
         const int q = e * kThreads + tid, i = q / (kP / 4), p = (q % (kP / 4)) * 4;
-        const int off = (int)((i * H + h) * kP + p) * 4;
-        g.x[e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+        g.x[e] = load4(x, rx, (int)((i * H + h) * kP + p));
     }
 #pragma unroll
     for (int e = 0; e < ChunkRegs<N>::kB; ++e) {
         const int q = e * kThreads + tid, i = q / (N / 4), n = (q % (N / 4)) * 4;
-        const int off = (i * N + n) * 4;
-        g.b[e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
-        g.c[e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
+        g.b[e] = load4(x, rb, i * N + n);
+        g.c[e] = load4(x, rc, i * N + n);
     }
     // step sizes, used by wave 0 only
-    g.dt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)((tid & 63) * H + h) * 4, 0, 0));
+    g.dt = load1(x, rd, (int)((tid & 63) * H + h));
 }
 
-template <int N>
+template <class T, int N>
 __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     constexpr int NT = N / 64;  // state tiles per wave: the P x N state is 2 x (N / 32) tiles over 4 waves
     __shared__ SsdSmem<N> s;
@@ -207,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     const int ti = wv >> 1, tj = wv & 1;
 
     ChunkRegs<N> g;
-    load_chunk<N>(a, bi, h, t_begin, t_end, tid, g);
+    load_chunk<T, N>(a, bi, h, t_begin, t_end, tid, g);
     float lam = 0.0f;  // the segment's total log-decay, sum of Delta A_h
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += kQ) {
@@ -251,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
         __syncthreads();
 
         // the next chunk's inputs travel while this chunk computes (past the end: no access)
-        load_chunk<N>(a, bi, h, t0 + kQ, t_end, tid, g);
+        load_chunk<T, N>(a, bi, h, t0 + kQ, t_end, tid, g);
         lam += s.cum[kQ - 1];
 
         // per-lane LDS base offsets (floats) of the MFMA operands; step k adds a constant
@@ -309,13 +328,12 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             else
                 y = mfma_chain<32>(y, ld_mx);
             // rows past the sequence end fall outside the resource and are dropped
-            const auto ry = make_rsrc(a.y + (bi * L + t0) * H * kP, (uint32_t)(nv * H * kP * 4));
+            const auto ry = make_rsrc(static_cast<T*>(a.y) + (bi * L + t0) * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
             const int p = tj * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = ti * 32 + acc_row(r, hl);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y[r] + Dh * s.x[i][p]), ry,
-                                                      (int)((i * H + h) * kP + p) * 4, 0, 0);
+                store1<T>(y[r] + Dh * s.x[i][p], ry, (int)((i * H + h) * kP + p));
             }
         }
 
@@ -378,7 +396,7 @@ struct SsdCorrSmem {
     float cum[kQ];
 };
 
-template <int N>
+template <class T, int N>
 __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
     __shared__ SsdCorrSmem<N> s;
     constexpr int SB = N + kPadCol, SX = kP + kPadRow;
@@ -404,14 +422,15 @@ __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
     float dtv;
     auto load = [&](int64_t t0) {
         const int64_t nv = t_end - t0 < 0 ? 0 : imin64(kQ, t_end - t0), row0 = bi * L + t0;
-        const auto rc = make_rsrc(a.Cm + row0 * N, (uint32_t)(nv * N * 4));
+        const T* cm = static_cast<const T*>(a.Cm);
+        const auto rc = make_rsrc(cm + row0 * N, (uint32_t)(nv * N * sizeof(T)));
 #pragma unroll
         for (int e = 0; e < kC; ++e) {
             const int q = e * kThreads + tid, i = q / (N / 4), n = (q % (N / 4)) * 4;
-            cr[e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, (i * N + n) * 4, 0, 0));
+            cr[e] = load4(cm, rc, i * N + n);
         }
-        const auto rd = make_rsrc(a.dt + row0 * H, (uint32_t)(nv * H * 4));
-        dtv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (int)(lane * H + h) * 4, 0, 0));
+        const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
+        dtv = load1(cm, rd, (int)(lane * H + h));
     };
     load(t_begin);
 
@@ -438,13 +457,14 @@ __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
         load(t0 + kQ);  // the next chunk's inputs travel during this chunk (past the end: no access)
 
         // the outputs this lane adds to, read before the products; rows past the end fall outside the resource
-        const auto ry = make_rsrc(a.y + row0 * H * kP, (uint32_t)(nv * H * kP * 4));
+        T* yp = static_cast<T*>(a.y);
+        const auto ry = make_rsrc(yp + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
         const int p = tj * 32 + l32;
         float old[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = ti * 32 + acc_row(r, hl);
-            old[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ry, (int)((i * H + h) * kP + p) * 4, 0, 0));
+            old[r] = load1(yp, ry, (int)((i * H + h) * kP + p));
         }
         const int oc = opaque((ti * 32 + l32) * SB + hl);
         const int ost = opaque(hl * SX + tj * 32 + l32);
@@ -457,32 +477,30 @@ __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int i = ti * 32 + acc_row(r, hl);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(old[r] + y[r] * fexp(s.cum[i])), ry,
-                                                  (int)((i * H + h) * kP + p) * 4, 0, 0);
+            store1<T>(old[r] + y[r] * fexp(s.cum[i]), ry, (int)((i * H + h) * kP + p));
         }
         carry = s.cum[kQ - 1];
         __syncthreads();
     }
 }
 
-}  // namespace
-
-hipError_t launch_ssd_fwd(const SsdArgs& a, hipStream_t st) {
-    const dim3 grid((unsigned)(a.B * a.H * a.nseg)), block(kThreads);
-    if (a.N == 64)
-        hipLaunchKernelGGL(ssd_fwd_kernel<64>, grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL(ssd_fwd_kernel<128>, grid, block, 0, st, a);
+template <class T, int N>
+hipError_t launch_typed(const SsdArgs& a, hipStream_t st) {
+    const dim3 block(kThreads);
+    hipLaunchKernelGGL((ssd_fwd_kernel<T, N>), dim3((unsigned)(a.B * a.H * a.nseg)), block, 0, st, a);
     if (a.nseg > 1) {
         const int64_t n = a.B * a.H * a.P * a.N;
         hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
-        const dim3 cgrid((unsigned)(a.B * a.H * (a.nseg - 1)));
-        if (a.N == 64)
-            hipLaunchKernelGGL(ssd_correct_kernel<64>, cgrid, block, 0, st, a);
-        else
-            hipLaunchKernelGGL(ssd_correct_kernel<128>, cgrid, block, 0, st, a);
+        hipLaunchKernelGGL((ssd_correct_kernel<T, N>), dim3((unsigned)(a.B * a.H * (a.nseg - 1))), block, 0, st, a);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ssd_fwd(const SsdArgs& a, hipStream_t st) {
+    if (a.dtype == 1) return a.N == 64 ? launch_typed<uint16_t, 64>(a, st) : launch_typed<uint16_t, 128>(a, st);
+    return a.N == 64 ? launch_typed<float, 64>(a, st) : launch_typed<float, 128>(a, st);
 }
 
 }  // namespace mssm

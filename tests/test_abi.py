@@ -209,7 +209,6 @@ def test_ssd_validation():
     assert ssd(good(batch=1, nheads=1 << 17)) == -2         # H * P >= 2^23
     assert ssd(good(headdim=32)) == -4                      # built for P = 64
     assert ssd(good(dstate=16)) == -4                       # built for N in {64, 128}
-    assert ssd(good(dtype=1)) == -4                         # float32 only
     for n in ("x", "dt", "A", "Bm", "Cm", "y"):
         assert ssd(good(), **{n: None}) == -1, n
     for n in ("x", "dt", "A", "Bm", "Cm", "Dskip", "dt_bias", "h0", "y", "h_final"):

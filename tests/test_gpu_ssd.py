@@ -119,3 +119,24 @@ def test_ssd_time_segments(lib, B, L, H, N):
     yr, hr = oracle.ssd_fwd(inp["x"], inp["dt"], inp["A"], inp["Bm"], inp["Cm"], inp["Dskip"], inp["dt_bias"], h0n)
     assert fwd_err(to_np(y), yr) <= TOL
     assert fwd_err(to_np(state), hr) <= TOL
+
+
+@pytest.mark.parametrize("B,L,H,N", [(2, 200, 3, 64), (1, 257, 4, 128), (3, 130, 2, 64), (1, 1000, 5, 128),
+                                     (8, 300, 20, 128)])
+def test_ssd_bf16(lib, B, L, H, N):
+    # bfloat16 x, dt, Bm, Cm and y, float32 arithmetic: the oracle takes the rounded inputs (exact in float32);
+    # the first and fourth shapes take the segmented path, the last one workgroup per (batch, head)
+    print(f"[ssd bf16] B={B} L={L} H={H} N={N}", flush=True)
+    inp = workloads.ssd_inputs(B, L, H, 64, N, seed=5000 + L)
+    t = gpu(inp)
+    for k in ("x", "dt", "Bm", "Cm"):
+        t[k] = t[k].to(torch.bfloat16)
+    h0n = np.random.default_rng(N).standard_normal((B, H, 64, N)).astype(np.float32)
+    y, hf = lib.ssd_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["dt_bias"],
+                        torch.from_numpy(h0n).cuda())
+    torch.cuda.synchronize()
+    assert y.dtype == torch.bfloat16
+    r = {k: t[k].float().cpu().numpy() for k in ("x", "dt", "Bm", "Cm")}
+    yr, hr = oracle.ssd_fwd(r["x"], r["dt"], inp["A"], r["Bm"], r["Cm"], inp["Dskip"], inp["dt_bias"], h0n)
+    assert fwd_err(to_np(y), yr) <= FWD_TOL["bf16"]
+    assert fwd_err(to_np(hf), hr) <= FWD_TOL["bf16"]
