@@ -376,6 +376,7 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     log(f"workload {workloads.DESCRIPTIONS[w.name]}; steps {args.steps}, warmup {args.warmup}")
     wall, launch_ms, cold_ms = time_fwd(mssm, torch, w, args.steps, args.warmup, cold_reps=5)
+    log(f"forward timed: {wall * 1e6:.1f} us per step")
     copy_gbs = copy_bandwidth(torch)
     nbytes = fwd_bytes(w)
     gbs = nbytes / wall / 1e9
@@ -429,6 +430,7 @@ def main():
         out["extra"]["conv_fwd_us"] = round(conv_us, 1)   # median kernel time, fused conv1d + SiLU front end
         out["extra"]["conv_fwd_GBs"] = round(conv_fwd_bytes(w) / conv_us / 1e3, 1)
         out["extra"]["conv_fwd_vs_plain_median"] = round(conv_us / (float(np.median(launch_ms)) * 1e3), 3)
+        log("extra: 130M forward and fused conv forward timed")
         cb_us = time_conv_bwd(mssm, torch, w)
         out["extra"]["conv_bwd_us"] = round(cb_us, 1)   # median, backward of the conv front end
         out["extra"]["conv_bwd_GBs"] = round(conv_bwd_bytes(w) / cb_us / 1e3, 1)
@@ -444,6 +446,7 @@ def main():
         sw = workloads.custom(256, 4, w.D, w.N, w.dtype, seed=w.seed)
         _, sl, _ = time_fwd(mssm, torch, sw, 30, 3)
         out["extra"]["short_fwd_B256_L4_us"] = round(float(np.median(sl)) * 1e3, 1)
+        log("extra: conv backward, decode steps and short-sequence forward timed")
         # Mamba-2 (SSD) layer of the 2.7B shape: 80 heads of 64, d_state 128, B = 8, L = 2048, float32 on MFMA
         ssd_us, ssd_flops = time_ssd(mssm, torch, 8, 2048, 80, 128)
         out["extra"]["ssd_fwd_H80_N128_B8_L2048_us"] = round(ssd_us, 1)
@@ -451,6 +454,7 @@ def main():
         # batch-1 prefill of a 24-head layer (Mamba-2 130M shape): time segments scanned in parallel
         ssd_us, _ = time_ssd(mssm, torch, 1, 2048, 24, 128)
         out["extra"]["ssd_fwd_H24_N128_B1_L2048_us"] = round(ssd_us, 1)
+        log("extra: SSD forwards timed")
         tw = workloads.WORKLOADS["train"]
         tb = time_bwd(mssm, torch, tw, 10, 2)
         out.setdefault("extra", {})["train_bwd_us"] = round(tb * 1e6, 1)
@@ -463,6 +467,7 @@ def main():
             out["extra"]["long_fwd_GBs"] = round(fwd_bytes(lw) / wl / 1e9, 1)
             out["extra"]["long_elem_state_per_s"] = float(f"{lw.elem_states / wl:.4e}")
     if not args.no_cpu_baseline:
+        log("cpu baseline: the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 

@@ -282,7 +282,9 @@ typedef struct {
  * (batch, head) pairs or the sequence is shorter than 4 chunks; otherwise the
  * sequence is cut into time segments scanned in parallel, and the scratch
  * holds each segment's state and log-decay, (B * H * segments * (P * N + 1))
- * floats.  0 for an invalid problem. */
+ * floats, and with bfloat16 activations also float32 outputs (B * L * H * P
+ * floats) that the last pass completes and rounds once.  0 for an invalid
+ * problem. */
 size_t mssm_ssd_fwd_workspace_bytes(const mssm_ssd_problem* p);
 
 mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,

@@ -221,7 +221,7 @@ mssm_status check_ssd_problem(const mssm_ssd_problem* p) {
 
 size_t mssm_ssd_fwd_workspace_bytes(const mssm_ssd_problem* p) {
     if (check_ssd_problem(p) != MSSM_OK) return 0;
-    return mssm::plan_ssd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate).ws_bytes;
+    return mssm::plan_ssd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate, p->dtype == MSSM_BF16).ws_bytes;
 }
 
 mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
@@ -233,7 +233,8 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* d
     if (!x || !dt || !A || !Bm || !Cm || !y) return MSSM_ERR_NULL;
     const mssm_status st = check_align({x, dt, A, Bm, Cm, Dskip, dt_bias, h0, y, h_final, workspace});
     if (st != MSSM_OK) return st;
-    const mssm::SsdPlan plan = mssm::plan_ssd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate);
+    const mssm::SsdPlan plan = mssm::plan_ssd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate,
+                                              p->dtype == MSSM_BF16);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return MSSM_ERR_WORKSPACE;
 
     mssm::SsdArgs a{};
@@ -243,6 +244,8 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* d
     a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm;
     a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0; a.y = y; a.h_final = h_final;
     a.nseg = plan.nseg; a.seg_len = plan.seg_len; a.ws = static_cast<float*>(workspace);
+    a.ws_y = plan.nseg > 1 && p->dtype == MSSM_BF16
+                 ? a.ws + p->batch * p->nheads * plan.nseg * (p->headdim * p->dstate + 1) : nullptr;
     return from_hip(mssm::launch_ssd_fwd(a, static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -27,6 +27,8 @@ struct SsdArgs {
     int64_t nseg;
     int64_t seg_len;       // steps per segment, a multiple of the chunk length (L when nseg == 1)
     float* ws;             // nseg > 1: segment states (B, H, nseg, P, N), then log-decays (B, H, nseg)
+    float* ws_y;           // nseg > 1 with bf16 outputs: float32 outputs (B, L, H, P) of segments 1.. before the
+                           // correction (a bf16 partial would be rounded twice); else null
 };
 
 constexpr int kSsdHeadDim = 64;   // P the kernel is built for
@@ -39,14 +41,16 @@ inline bool ssd_supported(int64_t P, int64_t N) { return P == kSsdHeadDim && (N 
 // CUs, the sequence splits into segments of at least two chunks, enough to
 // give about 256 workgroups; each segment is scanned from a zero state, a
 // carry pass forms the state entering every segment, and a correction pass
-// adds that state's contribution to the segment's outputs.
+// adds that state's contribution to the segment's outputs.  Scratch: the
+// segment states and log-decays, and for bfloat16 outputs a float32 copy of
+// the outputs the correction completes.
 struct SsdPlan {
     int64_t nseg;
     int64_t seg_len;
     size_t ws_bytes;
 };
 
-inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N) {
+inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, bool bf16) {
     SsdPlan pl{1, L, 0};
     const int64_t jobs = B * H, chunks = (L + kSsdChunk - 1) / kSsdChunk;
     if (jobs >= 128 || chunks < 4) return pl;
@@ -59,7 +63,7 @@ inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N) {
         pl.seg_len = L;
         return pl;
     }
-    pl.ws_bytes = static_cast<size_t>(jobs * pl.nseg * (P * N + 1)) * sizeof(float);
+    pl.ws_bytes = static_cast<size_t>(jobs * pl.nseg * (P * N + 1) + (bf16 ? B * L * H * P : 0)) * sizeof(float);
     return pl;
 }
 

@@ -328,12 +328,22 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             else
                 y = mfma_chain<32>(y, ld_mx);
             // rows past the sequence end fall outside the resource and are dropped
-            const auto ry = make_rsrc(static_cast<T*>(a.y) + (bi * L + t0) * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
             const int p = tj * 32 + l32;
+            if (a.ws_y && seg > 0) {  // a bf16 segment output the correction completes: kept in float32 until then
+                const auto rw = make_rsrc(a.ws_y + (bi * L + t0) * H * kP, (uint32_t)(nv * H * kP * 4));
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = ti * 32 + acc_row(r, hl);
-                store1<T>(y[r] + Dh * s.x[i][p], ry, (int)((i * H + h) * kP + p));
+                for (int r = 0; r < 16; ++r) {
+                    const int i = ti * 32 + acc_row(r, hl);
+                    store1<float>(y[r] + Dh * s.x[i][p], rw, (int)((i * H + h) * kP + p));
+                }
+            } else {
+                const auto ry = make_rsrc(static_cast<T*>(a.y) + (bi * L + t0) * H * kP,
+                                          (uint32_t)(nv * H * kP * sizeof(T)));
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = ti * 32 + acc_row(r, hl);
+                    store1<T>(y[r] + Dh * s.x[i][p], ry, (int)((i * H + h) * kP + p));
+                }
             }
         }
 
@@ -461,10 +471,16 @@ __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
         const auto ry = make_rsrc(yp + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
         const int p = tj * 32 + l32;
         float old[16];
+        if (a.ws_y) {  // the segment pass's float32 outputs (bf16 problems)
+            const float* wy = a.ws_y;
+            const auto rw = make_rsrc(wy + row0 * H * kP, (uint32_t)(nv * H * kP * 4));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = ti * 32 + acc_row(r, hl);
-            old[r] = load1(yp, ry, (int)((i * H + h) * kP + p));
+            for (int r = 0; r < 16; ++r)
+                old[r] = load1(wy, rw, (int)(((ti * 32 + acc_row(r, hl)) * H + h) * kP + p));
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                old[r] = load1(yp, ry, (int)(((ti * 32 + acc_row(r, hl)) * H + h) * kP + p));
         }
         const int oc = opaque((ti * 32 + l32) * SB + hl);
         const int ost = opaque(hl * SX + tj * 32 + l32);

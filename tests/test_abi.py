@@ -217,6 +217,7 @@ def test_ssd_validation():
     q = lambda **k: lib.mssm_ssd_fwd_workspace_bytes(ctypes.byref(good(**k)))  # noqa: E731
     need = q(seqlen=1000)  # 6 pairs, 16 chunks: 8 segments of 128 steps
     assert need == 6 * 8 * (64 * 64 + 1) * 4
+    assert q(seqlen=1000, dtype=1) == need + 2 * 1000 * 3 * 64 * 4  # bf16: float32 outputs before the correction
     assert q() == 0 and q(seqlen=1000, batch=64, nheads=2) == 0 and q(seqlen=1000, dstate=16) == 0
     assert ssd(good(seqlen=1000)) == -6
     assert ssd(good(seqlen=1000), ws=FAKE, wsb=need - 1) == -6

@@ -144,3 +144,36 @@ def test_random_conv_decode(mssm_lib, i):
                                      f["dt_bias"], None, bias=f["conv_b"], x_prev=f["x_prev"] if K > 1 else None)
     assert fwd_err(to_np(torch.stack(ys, 1)), yr) <= FWD_TOL[dtype]
     assert fwd_err(to_np(state), hr) <= FWD_TOL[dtype]
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_ssd(mssm_lib, i):
+    # Mamba-2 (SSD) forward: shapes on both sides of the segmented path (fewer than 128 (batch, head) pairs and at
+    # least 4 chunks), both state sizes and activation types, optional inputs, h0 and the softplus flag drawn
+    rng = np.random.default_rng(5000 + i)
+    B, H = int(rng.integers(1, 5)), int(rng.integers(1, 48))
+    L = int(rng.choice([rng.integers(1, 65), rng.integers(65, 700), rng.integers(700, 2600)]))
+    L = min(L, max(1, 400000 // (B * H)))  # keeps the float64 oracle to a few seconds
+    N = int(rng.choice([64, 128]))
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    use_d, use_bias, h0, sp = (bool(rng.random() < 0.6) for _ in range(4))
+    print(f"[random ssd {i}] B={B} L={L} H={H} N={N} {dtype} D={use_d} bias={use_bias} h0={h0} softplus={sp}",
+          flush=True)
+    inp = workloads.ssd_inputs(B, L, H, 64, N, seed=6000 + i)
+    if not sp:  # without softplus the raw step dt + dt_bias must be >= 0: no (negative) bias, |dt| scaled down
+        inp["dt"] = np.abs(inp["dt"]) * np.float32(0.05)
+        use_bias = False
+    t = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    if dtype == "bf16":
+        for k in ("x", "dt", "Bm", "Cm"):
+            t[k] = t[k].to(torch.bfloat16)
+    h0n = rng.standard_normal((B, H, 64, N)).astype(np.float32) if h0 else None
+    y, hf = mssm_lib.ssd_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"] if use_d else None,
+                             t["dt_bias"] if use_bias else None, torch.from_numpy(h0n).cuda() if h0 else None,
+                             delta_softplus=sp)
+    torch.cuda.synchronize()
+    r = {k: t[k].float().cpu().numpy() for k in ("x", "dt", "Bm", "Cm")}
+    yr, hr = oracle.ssd_fwd(r["x"], r["dt"], inp["A"], r["Bm"], r["Cm"], inp["Dskip"] if use_d else None,
+                            inp["dt_bias"] if use_bias else None, h0n, softplus=sp)
+    assert fwd_err(to_np(y), yr) <= FWD_TOL[dtype]
+    assert fwd_err(to_np(hf), hr) <= FWD_TOL[dtype]
