@@ -261,7 +261,8 @@ mssm_status mssm_conv_step(const mssm_problem* p, int32_t d_conv,
  * x, dt, Bm, Cm and y in p->dtype (MSSM_F32 or MSSM_BF16); arithmetic float32
  * throughout, bfloat16 outputs rounded to nearest even.
  * Required: p, x, dt, A, Bm, Cm, y.  Optional (NULL): Dskip, dt_bias (-> 0),
- * h0 (-> zeros), h_final (not written; may be the same buffer as h0).
+ * h0 (-> zeros), h_final (not written; may be the same buffer as h0, which
+ * then advances in place).  y and the workspace may not alias any input.
  * Built for headdim P = 64 and dstate N in {64, 128}: other sizes ->
  * MSSM_ERR_UNSUPPORTED.  Other errors as
  * mssm_scan_fwd; batch * nheads must be below 2^31 and nheads * headdim below
