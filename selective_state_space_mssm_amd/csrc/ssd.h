@@ -38,8 +38,9 @@ constexpr int kSsdChunk = 64;     // chunk length of the dual form
 inline bool ssd_supported(int64_t P, int64_t N) { return P == kSsdHeadDim && (N == 64 || N == 128); }
 
 // How the sequence is cut: with fewer (batch, head) pairs than half the 256
-// CUs, the sequence splits into segments of at least two chunks, enough to
-// give about 256 workgroups; each segment is scanned from a zero state, a
+// CUs, the sequence splits into segments of at least two chunks, as many as
+// fit one workgroup per CU in a single round (a second, partial round would
+// double the time); each segment is scanned from a zero state, a
 // carry pass forms the state entering every segment, and a correction pass
 // adds that state's contribution to the segment's outputs.  Scratch: the
 // segment states and log-decays, and for bfloat16 outputs a float32 copy of
@@ -54,7 +55,7 @@ inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, b
     SsdPlan pl{1, L, 0};
     const int64_t jobs = B * H, chunks = (L + kSsdChunk - 1) / kSsdChunk;
     if (jobs >= 128 || chunks < 4) return pl;
-    const int64_t want = (256 + jobs - 1) / jobs, most = chunks / 2;
+    const int64_t want = 256 / jobs, most = chunks / 2;
     const int64_t segs = want < most ? want : most;
     const int64_t per = (chunks + segs - 1) / segs;  // chunks per segment
     pl.seg_len = per * kSsdChunk;
