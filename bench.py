@@ -15,17 +15,23 @@ float32 arithmetic), inputs resident in HBM.  Prints one JSON line:
   launch, a cold launch (after overwriting the 256 MB last-level cache with a
   512 MB scratch write, untimed) and the bandwidth of a plain 1 GiB device
   copy measured in the same run;
+* configs: the other workloads, each timed the same way -- Tiny (per call,
+  and per call inside a replayed HIP graph, which leaves out the host's launch
+  cost), the 130M-layer and 1M-step forwards (GB/s, fractions of the HBM and
+  VALU bounds) and the training workload's forward + backward;
 * cpu_baseline: the float64 oracle timed on this host on a bounded channel
-  sample of the same workload.
+  sample of the same workload (host CPU model and core count stated).
 
 ``--gpus N`` with N > 1 exits: this benchmark and the library run on one GPU.
-``--extra`` adds the 130M-layer forward, the 2.8B-layer forward behind the fused
-causal conv1d + SiLU front end (x in place of u, d_conv = 4) and that front end's backward, the recurrent step at the 2.8B layer's
-width (B=4, D=5120, N=16: one decode step per call from Python, so the host's
-launch overhead, not the kernel, sets this rate; the kernel's own duration is
-in the kernel trace), the same step at B = 64 and 256 (batched decode, where the
-state's read and write set the rate), the step behind the conv front end at B = 256, a 4-token forward at B = 256 (the short-sequence path) and the training-workload backward
-(``--long`` also the 1M-step forward).
+``--extra`` adds the 2.8B-layer forward behind the fused causal conv1d + SiLU
+front end (x in place of u, d_conv = 4) and that front end's backward, the
+recurrent step at the 2.8B layer's width (B=4, D=5120, N=16: one decode step
+per call from Python, so the host's launch overhead, not the kernel, sets this
+rate; the kernel's own duration is in the kernel trace), the same step at
+B = 64 and 256 (batched decode, where the state's read and write set the
+rate), the step behind the conv front end at B = 256, a 4-token forward at
+B = 256 (the short-sequence path) and the Mamba-2 (SSD) layers.
+``--no-configs`` leaves out the other workloads (the headline alone).
 ``--copy-probe`` runs a plain device copy of 1 GiB first (counter calibration).
 """
 from __future__ import annotations
@@ -190,6 +196,64 @@ def time_fwd(mssm, torch, w, steps, warmup, cold_reps=0, conv=False):
     return wall, launch_ms, cold_ms
 
 
+def time_fwd_graph(mssm, torch, w, calls=200, reps=5):
+    """Forward time per call with `calls` calls captured in one HIP graph and
+    the graph replayed (launch-bound workloads: no host cost between calls).
+    Median over `reps` replays, HIP events around each replay."""
+    inp = workloads.make_inputs(w)
+    t = workloads.to_torch(inp, "cuda")
+    y = torch.empty_like(t["u"])
+    hf = torch.empty((w.B, w.D, w.N), dtype=torch.float32, device="cuda")
+    ws_n = mssm.fwd_workspace_bytes(w.B, w.L, w.D, w.N, t["u"].dtype)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+
+    def run():
+        mssm.scan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"], t["dt_bias"],
+                      None, y=y, h_final=hf, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            run()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    return float(np.median(ms)) * 1e3 / calls
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def fwd_entry(w, kern_s):
+    """GB/s of algorithmic bytes and the fractions of the HBM and VALU bounds
+    at kernel time `kern_s` seconds per forward."""
+    return {"GBs": round(fwd_bytes(w) / kern_s / 1e9, 1),
+            "hbm_frac": round(fwd_bytes(w) / kern_s / 1e9 / HBM_PEAK_GBS, 4),
+            "valu_frac": round(SLOTS_PER_ELEM_STATE * w.elem_states / kern_s / 1e12 / VALU_PEAK_TOPS, 4),
+            "elem_state_per_s": float(f"{w.elem_states / kern_s:.4e}")}
+
+
 def copy_bandwidth(torch, reps=5):
     """Read + write bytes per second of a plain 1 GiB device-to-device copy."""
     n = 1 << 30
@@ -222,11 +286,14 @@ def time_bwd(mssm, torch, w, steps, warmup):
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
         run()
+        b.record(stream)
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    return float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3
 
 
 def time_conv_step(mssm, torch, w, batch, reps=100):
@@ -338,9 +405,45 @@ def cpu_baseline(w: workloads.Workload, target_s: float = 12.0):
     frac = nch / w.D
     gbs = fwd_bytes(w) * frac / dt / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(),
             "sample": f"{nch} of {w.D} channels of the {w.name} workload (B={w.B}, L={w.L}, full sequence), "
                       f"median of {len(times)} runs of {dt:.2f} s ({sum(times):.1f} s in all); "
                       f"elem_state_per_s={w.B * w.L * nch * w.N / dt:.3e}"}
+
+
+def other_configs(mssm, torch):
+    """The other workloads, timed with HIP events on the launch stream (median
+    launch; cold = after a 512 MB scratch write)."""
+    cfg = {}
+    tw = workloads.WORKLOADS["tiny"]
+    _, tl, _ = time_fwd(mssm, torch, tw, 200, 20)
+    cfg["tiny"] = {"fwd_us_per_call": round(float(np.median(tl)) * 1e3, 2)}
+    try:
+        cfg["tiny"]["fwd_us_in_graph"] = round(time_fwd_graph(mssm, torch, tw), 2)
+    except RuntimeError as e:  # graph capture unavailable: the per-call figure stands alone
+        log(f"tiny: graph timing skipped ({e})")
+    log("configs: tiny timed")
+    w = workloads.WORKLOADS["130m"]
+    _, ml, cl = time_fwd(mssm, torch, w, 20, 3, cold_reps=3)
+    k = float(np.median(ml)) / 1e3
+    cfg["130m"] = dict(fwd_us=round(k * 1e6, 1), fwd_us_cold=round(float(np.median(cl)) * 1e3, 1), **fwd_entry(w, k))
+    log("configs: 130m timed")
+    w = workloads.WORKLOADS["long"]
+    _, ml, _ = time_fwd(mssm, torch, w, 3, 1)
+    k = float(np.median(ml)) / 1e3
+    cfg["long"] = dict(fwd_us=round(k * 1e6, 1), **fwd_entry(w, k))
+    log("configs: long timed")
+    w = workloads.WORKLOADS["train"]
+    _, ml, _ = time_fwd(mssm, torch, w, 20, 3)
+    kf = float(np.median(ml)) / 1e3
+    kb = time_bwd(mssm, torch, w, 10, 2)
+    cfg["train"] = {"fwd_us": round(kf * 1e6, 1), "bwd_us": round(kb * 1e6, 1),
+                    "fwd_bwd_us": round((kf + kb) * 1e6, 1),
+                    "bwd_GBs": round(bwd_bytes(w) / kb / 1e9, 1),
+                    "fwd_bwd_GBs": round((fwd_bytes(w) + bwd_bytes(w)) / (kf + kb) / 1e9, 1),
+                    "fwd_bwd_hbm_frac": round((fwd_bytes(w) + bwd_bytes(w)) / (kf + kb) / 1e9 / HBM_PEAK_GBS, 4)}
+    log("configs: train fwd + bwd timed")
+    return cfg
 
 
 def main():
@@ -350,9 +453,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="2.8b", choices=["2.8b", "130m", "long", "tiny", "train"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="only the headline workload")
     ap.add_argument("--extra", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--long", action="store_true", help="with --extra: also the 1M-step forward")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the selective-scan library has no multi-GPU path; "
@@ -381,6 +484,7 @@ def main():
     nbytes = fwd_bytes(w)
     gbs = nbytes / wall / 1e9
     kern_s = float(np.mean(launch_ms)) / 1e3
+    cold_s = float(np.median(cold_ms)) / 1e3
     slots = SLOTS_PER_ELEM_STATE * w.elem_states
     achieved = slots / kern_s / 1e12
     out = {
@@ -395,6 +499,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "act_dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": workloads.DESCRIPTIONS[w.name], "B": w.B, "L": w.L, "D": w.D, "N": w.N,
                    "act_storage": w.dtype, "direction": "fwd"},
@@ -417,20 +522,22 @@ def main():
             "hbm_peak_GBs": HBM_PEAK_GBS,
             "copy_GBs": round(copy_gbs, 1),
             "frac_of_copy": round(nbytes / kern_s / 1e9 / copy_gbs, 4),
+            "hbm_frac": round(nbytes / kern_s / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "frac is against the VALU issue bound (the binding one); hbm_frac against 8 TB/s",
         },
+        # cold: each launch after a 512 MB scratch write has evicted the inputs from the last-level cache
+        "cold": {"kernel_us": round(cold_s * 1e6, 2), "GBs": round(nbytes / cold_s / 1e9, 1),
+                 "hbm_frac": round(nbytes / cold_s / 1e9 / HBM_PEAK_GBS, 4)},
     }
+    if not args.no_configs:
+        out["configs"] = other_configs(mssm, torch)
     if args.extra:
-        for name in ("130m",):
-            ww = workloads.WORKLOADS[name]
-            wl, _, _ = time_fwd(mssm, torch, ww, 20, 3)
-            out.setdefault("extra", {})[f"{name}_fwd_GBs"] = round(fwd_bytes(ww) / wl / 1e9, 1)
-            out["extra"][f"{name}_fwd_us"] = round(wl * 1e6, 1)
         _, cl, _ = time_fwd(mssm, torch, w, 20, 3, conv=True)
         conv_us = float(np.median(cl)) * 1e3
-        out["extra"]["conv_fwd_us"] = round(conv_us, 1)   # median kernel time, fused conv1d + SiLU front end
+        out.setdefault("extra", {})["conv_fwd_us"] = round(conv_us, 1)   # median kernel time, fused front end
         out["extra"]["conv_fwd_GBs"] = round(conv_fwd_bytes(w) / conv_us / 1e3, 1)
         out["extra"]["conv_fwd_vs_plain_median"] = round(conv_us / (float(np.median(launch_ms)) * 1e3), 3)
-        log("extra: 130M forward and fused conv forward timed")
+        log("extra: fused conv forward timed")
         cb_us = time_conv_bwd(mssm, torch, w)
         out["extra"]["conv_bwd_us"] = round(cb_us, 1)   # median, backward of the conv front end
         out["extra"]["conv_bwd_GBs"] = round(conv_bwd_bytes(w) / cb_us / 1e3, 1)
@@ -455,17 +562,6 @@ def main():
         ssd_us, _ = time_ssd(mssm, torch, 1, 2048, 24, 128)
         out["extra"]["ssd_fwd_H24_N128_B1_L2048_us"] = round(ssd_us, 1)
         log("extra: SSD forwards timed")
-        tw = workloads.WORKLOADS["train"]
-        tb = time_bwd(mssm, torch, tw, 10, 2)
-        out.setdefault("extra", {})["train_bwd_us"] = round(tb * 1e6, 1)
-        out["extra"]["train_bwd_GBs"] = round(bwd_bytes(tw) / tb / 1e9, 1)
-        if args.long:
-            lw = workloads.WORKLOADS["long"]
-            log("generating the 1M-step workload")
-            wl, _, _ = time_fwd(mssm, torch, lw, 5, 1)
-            out["extra"]["long_fwd_us"] = round(wl * 1e6, 1)
-            out["extra"]["long_fwd_GBs"] = round(fwd_bytes(lw) / wl / 1e9, 1)
-            out["extra"]["long_elem_state_per_s"] = float(f"{lw.elem_states / wl:.4e}")
     if not args.no_cpu_baseline:
         log("cpu baseline: the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(w)

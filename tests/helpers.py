@@ -4,6 +4,10 @@ binding and the float64 oracle on the same seeded inputs, and compare.
 Tolerances (float32 arithmetic on the GPU against the float64 oracle):
 * forward outputs y, h_final: max_i |g - r| / max(1, |r|) <= 1e-4 for float32
   activations and <= 2e-2 for bfloat16 activations (abs-or-rel criterion);
+* the float32 state (h_final, a decode state) at 1e-4 whatever the activation
+  type: bfloat16 inputs widen to float32 exactly and the state is never
+  rounded to bfloat16, so only float32 arithmetic separates it from the
+  float64 oracle -- the bfloat16 bar would hide a carry defect of 1e-3;
 * gradients: max_i |g - r| / max(|r|, rms(r)) <= 1e-3 per tensor (relative,
   with an rms floor so that entries near zero are judged on the tensor's
   scale), 2e-2 for bfloat16 activations.
@@ -15,6 +19,7 @@ import numpy as np
 import workloads
 
 FWD_TOL = {"f32": 1e-4, "bf16": 2e-2}
+STATE_TOL = 1e-4
 GRAD_TOL = {"f32": 1e-3, "bf16": 2e-2}
 
 
@@ -33,7 +38,9 @@ def grad_err(g, r) -> float:
 
 
 def to_np(t):
-    return t.detach().float().cpu().numpy() if t is not None else None
+    if t is None or isinstance(t, np.ndarray):
+        return t
+    return t.detach().float().cpu().numpy()
 
 
 def gpu_inputs(inp, device="cuda"):

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads
-from helpers import FWD_TOL, fwd_err, gpu_inputs, to_np
+from helpers import FWD_TOL, STATE_TOL, fwd_err, gpu_inputs, to_np
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -45,7 +45,7 @@ def check(out, ref, dtype, with_u=True):
     yr, hr, ur = ref
     tol = FWD_TOL[dtype]
     assert fwd_err(to_np(y), yr) <= tol
-    assert fwd_err(to_np(hf), hr) <= tol
+    assert fwd_err(to_np(hf), hr) <= STATE_TOL
     if with_u:
         assert fwd_err(to_np(u), ur) <= tol
 
@@ -143,20 +143,22 @@ def test_fused_equals_unfused_scan_of_its_u(mssm):
     assert torch.equal(hf, hf2)
 
 
-def test_full_size_2p8b_sampled(mssm):
+def test_full_size_2p8b(mssm):
     """The Mamba-2.8B layer shape (B=4, L=4096, D=5120, bf16) in the launch
-    configuration of the benchmark, checked on a sample of channels (first,
-    last, and spread over the blocks) against the oracle on those channels."""
+    configuration of the benchmark: every element of y, h_final and u against
+    the oracle."""
     w = workloads.WORKLOADS["2.8b"]
     inp, t = make(w, 4)
     print(f"[conv] {w} full size", flush=True)
     y, hf, u = gpu_run(mssm, t)
     torch.cuda.synchronize()
-    ch = np.unique(np.concatenate([[0, 63, 64, 5119], np.random.default_rng(5).choice(w.D, 44, replace=False)]))
-    sub = workloads.select_channels(inp, ch)
-    yr, hr, ur = oracle_run(sub)
-    cht = torch.from_numpy(ch).cuda()
-    check((y[:, :, cht], hf[:, cht], u[:, :, cht]), (yr, hr, ur), "bf16")
+    out = (to_np(y), to_np(hf), to_np(u))
+    del y, hf, u, t
+    torch.cuda.empty_cache()
+    yr, hr, ur = oracle_run(inp)
+    print(f"2.8b conv: y err {fwd_err(out[0], yr):.2e}, h_final err {fwd_err(out[1], hr):.2e}, "
+          f"u err {fwd_err(out[2], ur):.2e}", flush=True)
+    check(out, (yr, hr, ur), "bf16")
 
 
 # ---- backward of the front end (mssm_conv_bwd) --------------------------------------------------
@@ -215,9 +217,9 @@ def test_conv_backward_edge_shapes(mssm, B, L, D):
     check_conv_grads(g, r, "f32", 4)
 
 
-def test_conv_backward_full_size_2p8b_sampled(mssm):
-    """The 2.8B layer shape (B=4, L=4096, D=5120, bf16): dx, dconv_w and dconv_b
-    of sampled channels against the oracle on those channels."""
+def test_conv_backward_full_size_2p8b(mssm):
+    """The 2.8B layer shape (B=4, L=4096, D=5120, bf16): every element of dx,
+    dconv_w, dconv_b and dx_prev against the oracle."""
     w = workloads.WORKLOADS["2.8b"]
     inp, t = make(w, 4)
     print(f"[conv bwd] {w} full size", flush=True)
@@ -225,14 +227,9 @@ def test_conv_backward_full_size_2p8b_sampled(mssm):
     du = workloads.to_torch({"u": du_st, "dtype": "bf16"}, "cuda", keys=("u",))["u"]
     g = mssm.conv_bwd(t["u"], t["conv_w"], du, conv_b=t["conv_b"], x_prev=t["x_prev"], want_dx_prev=True)
     torch.cuda.synchronize()
-    ch = np.unique(np.concatenate([[0, 255, 256, 5119], np.random.default_rng(8).choice(w.D, 40, replace=False)]))
-    sub = workloads.as_float32(workloads.select_channels(inp, ch))
-    r = oracle.causal_conv_silu_bwd(sub["u"], sub["conv_w"], workloads.to_f32(du_st, "bf16")[:, :, ch],
-                                    sub["conv_b"], sub["x_prev"])
-    cht = torch.from_numpy(ch).cuda()
-    sel = {"dx": g["dx"][:, :, cht], "dconv_w": g["dconv_w"][cht], "dconv_b": g["dconv_b"][cht],
-           "dx_prev": g["dx_prev"][:, :, cht]}
-    check_conv_grads(sel, r, "bf16", 4)
+    f = workloads.as_float32(inp)
+    r = oracle.causal_conv_silu_bwd(f["u"], f["conv_w"], workloads.to_f32(du_st, "bf16"), f["conv_b"], f["x_prev"])
+    check_conv_grads(g, r, "bf16", 4)
 
 
 def test_training_chain_through_the_front_end(mssm):
@@ -278,7 +275,7 @@ def test_conv_step_decode(mssm, dtype, N, K):
     yr, hr, _ = oracle_run(inp, h0=h0)
     tol = FWD_TOL[dtype]
     assert fwd_err(to_np(torch.stack(ys, 1)), yr) <= tol
-    assert fwd_err(to_np(state), hr) <= tol
+    assert fwd_err(to_np(state), hr) <= STATE_TOL
     if K > 1:
         assert torch.equal(cst, torch.cat([t["x_prev"], t["u"]], 1)[:, -(K - 1):])
 
@@ -304,4 +301,4 @@ def test_prefill_then_decode(mssm):
     torch.cuda.synchronize()
     yr, hr, _ = oracle_run(inp)
     assert fwd_err(to_np(torch.cat(ys, 1)), yr) <= FWD_TOL["bf16"]
-    assert fwd_err(to_np(state), hr) <= FWD_TOL["bf16"]
+    assert fwd_err(to_np(state), hr) <= STATE_TOL

@@ -5,17 +5,19 @@ Covers: the Tiny workload in full; ragged small shapes (channels not a
 multiple of 64, sequence not a multiple of the 16-step tile) with every
 optional input present and absent, softplus on and off; last tiles that end
 inside a readout group; every supported state size in fp32 and bf16; the chunked (cross-chunk carry) schedule
-with a ragged last chunk; the 130M and 2.8B layer workloads (130M in full,
-2.8B on sampled channels over the whole sequence -- channels are independent,
-so the oracle computes them one by one); the 1M-step workload on sampled
-channels; bitwise determinism; and streaming (a split scan equals one scan).
+with a ragged last chunk; the 130M and 2.8B layer workloads in full; the
+1M-step workload in full, every channel, with the oracle run over batches of
+64 channels (channels are independent, so the oracle can take them in any
+grouping); bitwise determinism; and streaming (a split scan equals one scan).
+y is judged at the activation type's bar, the float32 final state at 1e-4
+(helpers.STATE_TOL) for every workload.
 """
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from helpers import FWD_TOL, fwd_err, gpu_inputs, run_gpu_fwd, run_oracle_fwd, to_np
+from helpers import FWD_TOL, STATE_TOL, fwd_err, gpu_inputs, run_gpu_fwd, run_oracle_fwd, to_np
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -42,8 +44,9 @@ def check(mssm, w, h0=False, use=("Dskip", "z", "dt_bias"), softplus=True, tol=N
     tol = tol or FWD_TOL[w.dtype]
     ey, eh = fwd_err(to_np(y), yr), fwd_err(to_np(hf), hr)
     assert np.all(np.isfinite(to_np(y)))
+    print(f"  y err {ey:.2e}, h_final err {eh:.2e}", flush=True)
     assert ey <= tol, f"y err {ey:.3e} > {tol}"
-    assert eh <= tol, f"h_final err {eh:.3e} > {tol}"
+    assert eh <= STATE_TOL, f"h_final err {eh:.3e} > {STATE_TOL}"
     return ey, eh
 
 
@@ -138,34 +141,49 @@ def test_130m_layer_full(mssm):
     print(f"130M: y err {ey:.2e}, h_final err {eh:.2e}")
 
 
-def sampled_check(mssm, w, channels, tol):
-    print(f"[fwd sampled] {w} channels={len(channels)}", flush=True)
+def test_2p8b_layer_full(mssm):
+    """The Mamba-2.8B layer workload (B=4, L=4096, D=5120, bf16) in the launch
+    configuration of the benchmark (balanced persistent schedule), every
+    element of y and h_final against the oracle."""
+    w = workloads.WORKLOADS["2.8b"]
+    print(f"[fwd full] {w}", flush=True)
     inp = workloads.make_inputs(w)
     t = gpu_inputs(inp)
     y, hf = run_gpu_fwd(mssm, t)
     torch.cuda.synchronize()
-    ys = to_np(y[:, :, channels])
-    hs = to_np(hf[:, channels])
+    yg, hg = to_np(y), to_np(hf)
     del y, hf, t
     torch.cuda.empty_cache()
-    sub = workloads.select_channels(inp, channels)
-    yr, hr = run_oracle_fwd(oracle, sub)
-    ey, eh = fwd_err(ys, yr), fwd_err(hs, hr)
-    print(f"{w.name}: y err {ey:.2e}, h_final err {eh:.2e}", flush=True)
-    assert ey <= tol and eh <= tol
+    yr, hr = run_oracle_fwd(oracle, inp)
+    ey, eh = fwd_err(yg, yr), fwd_err(hg, hr)
+    print(f"2.8b: y err {ey:.2e}, h_final err {eh:.2e}", flush=True)
+    assert ey <= FWD_TOL["bf16"] and eh <= STATE_TOL
 
 
-def test_2p8b_layer_sampled_channels(mssm):
-    w = workloads.WORKLOADS["2.8b"]
-    ch = np.sort(np.random.default_rng(0).choice(w.D, 192, replace=False))
-    ch = np.unique(np.concatenate([ch, [0, 63, 64, w.D - 1]]))
-    sampled_check(mssm, w, ch, FWD_TOL["bf16"])
-
-
-def test_long_sequence_sampled_channels(mssm):
+def test_long_sequence_all_channels(mssm):
+    """The 1M-step workload (B=1, L=1,048,576, D=1536, bf16; time-chunked
+    schedule with the cross-chunk carry): every channel of y and h_final, the
+    oracle taking 64 channels at a time (one channel block of the GPU path
+    each, so all 24 blocks are covered)."""
     w = workloads.WORKLOADS["long"]
-    ch = np.array([0, 1, 63, 64, 500, 777, 1024, 1535])
-    sampled_check(mssm, w, ch, FWD_TOL["bf16"])
+    print(f"[fwd full] {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    t = gpu_inputs(inp)
+    y, hf = run_gpu_fwd(mssm, t)
+    torch.cuda.synchronize()
+    del t
+    hg = to_np(hf)
+    ey = eh = 0.0
+    for c0 in range(0, w.D, 64):
+        ch = np.arange(c0, min(c0 + 64, w.D))
+        yg = y[:, :, c0:c0 + len(ch)].float().cpu().numpy()
+        yr, hr = run_oracle_fwd(oracle, workloads.select_channels(inp, ch))
+        ey = max(ey, fwd_err(yg, yr))
+        eh = max(eh, fwd_err(hg[:, ch], hr))
+        print(f"  channels {c0}..{c0 + len(ch) - 1}: y err {ey:.2e}, h_final err {eh:.2e}", flush=True)
+    del y, hf
+    torch.cuda.empty_cache()
+    assert ey <= FWD_TOL["bf16"] and eh <= STATE_TOL
 
 
 def test_bitwise_deterministic(mssm):

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads
-from helpers import FWD_TOL, fwd_err, to_np
+from helpers import FWD_TOL, STATE_TOL, fwd_err, to_np
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -139,4 +139,4 @@ def test_ssd_bf16(lib, B, L, H, N):
     r = {k: t[k].float().cpu().numpy() for k in ("x", "dt", "Bm", "Cm")}
     yr, hr = oracle.ssd_fwd(r["x"], r["dt"], inp["A"], r["Bm"], r["Cm"], inp["Dskip"], inp["dt_bias"], h0n)
     assert fwd_err(to_np(y), yr) <= FWD_TOL["bf16"]
-    assert fwd_err(to_np(hf), hr) <= FWD_TOL["bf16"]
+    assert fwd_err(to_np(hf), hr) <= STATE_TOL

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads
-from helpers import FWD_TOL, fwd_err, gpu_inputs, run_oracle_fwd, to_np
+from helpers import FWD_TOL, STATE_TOL, fwd_err, gpu_inputs, run_oracle_fwd, to_np
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -38,12 +38,12 @@ def test_steps_equal_scan(mssm, dtype, N):
     yr, hr = run_oracle_fwd(oracle, inp, h0)
     tol = FWD_TOL[dtype]
     assert fwd_err(to_np(y), yr) <= tol
-    assert fwd_err(to_np(state), hr) <= tol
+    assert fwd_err(to_np(state), hr) <= STATE_TOL
     # and the GPU scan from the same state agrees with the GPU steps
     ysc, hsc = mssm.scan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"],
                              t["dt_bias"], torch.from_numpy(h0).cuda())
     assert fwd_err(to_np(ysc), to_np(y)) <= tol
-    assert fwd_err(to_np(hsc), to_np(state)) <= tol
+    assert fwd_err(to_np(hsc), to_np(state)) <= STATE_TOL
 
 
 def test_step_without_optional_inputs(mssm):
@@ -103,7 +103,7 @@ def test_multi_token_steps_in_place(mssm, B, D, segments, dtype):
     yr, hr = run_oracle_fwd(oracle, inp, h0)
     tol = FWD_TOL[dtype]
     assert fwd_err(to_np(torch.cat(ys, 1)), yr) <= tol
-    assert fwd_err(to_np(state), hr) <= tol
+    assert fwd_err(to_np(state), hr) <= STATE_TOL
 
 
 @pytest.mark.parametrize("N", [1, 2, 4, 8, 16, 32, 64])
@@ -124,7 +124,7 @@ def test_short_sequence_path(mssm, N, dtype):
         yr, hr = run_oracle_fwd(oracle, inp, h0)
         tol = FWD_TOL[dtype]
         assert fwd_err(to_np(y), yr) <= tol
-        assert fwd_err(to_np(hf), hr) <= tol
+        assert fwd_err(to_np(hf), hr) <= STATE_TOL
 
 
 @pytest.mark.parametrize("use,softplus", [((), True), (("z",), False), (("Dskip", "dt_bias"), True)])
@@ -156,4 +156,4 @@ def test_short_path_many_rows(mssm):
         torch.cuda.synchronize()
         yr, hr = run_oracle_fwd(oracle, inp)
         assert fwd_err(to_np(y), yr) <= FWD_TOL["bf16"]
-        assert fwd_err(to_np(hf), hr) <= FWD_TOL["bf16"]
+        assert fwd_err(to_np(hf), hr) <= STATE_TOL
