@@ -40,7 +40,9 @@
  *   throughout; bfloat16 outputs are rounded to nearest even.
  * Memory: every pointer is a device pointer owned by the caller, 16-byte
  *   aligned.  The library allocates and frees nothing and keeps no state
- *   between calls; it is re-entrant.  Scratch memory is the caller's
+ *   between calls; it is re-entrant.  (One exception, for callers that cannot
+ *   allocate: mssm_scan_fwd_noalloc uses a fixed scratch array of the
+ *   library's own, shared by its calls on a GPU.)  Scratch memory is the caller's
  *   `workspace`, of at least the size the matching *_workspace_bytes query
  *   returns for the same problem (NULL is accepted when that size is 0).
  * Streams: all work is enqueued on `hip_stream` (a hipStream_t; NULL = the
@@ -122,6 +124,37 @@ mssm_status mssm_scan_fwd(const mssm_problem* p,
                           const float* h0,
                           void* y, float* h_final,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * The forward scan of mssm_scan_fwd for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc -- and so cannot provide a workspace: same arguments,
+ * outputs and errors as mssm_scan_fwd minus workspace / workspace_bytes, same
+ * kernels and results (bit for bit).  The scratch comes from a fixed device
+ * array inside the library, MSSM_NOALLOC_SCRATCH_BYTES on every GPU the
+ * library runs on, reserved when the library's code is loaded onto that GPU
+ * and held until the process ends; its device address is looked up once per
+ * GPU (hipGetSymbolAddress, on the first call with that GPU current).  The
+ * call itself allocates and frees nothing.
+ * A problem whose scratch exceeds MSSM_NOALLOC_SCRATCH_BYTES returns
+ * MSSM_ERR_WORKSPACE before anything is enqueued; the scratch is what
+ * mssm_scan_fwd_workspace_bytes returns, except for the short sequences
+ * (at most 8 steps, or at most 64 steps over at most 32,768 (batch, channel)
+ * rows) that run without any.  32 MiB covers every time-chunked plan up to
+ * dstate 64 and the balanced schedule up to 8,192 channel blocks at dstate 16.  Everything in the array that
+ * must start at zero is cleared by a kernel of the call itself, so the contents
+ * left by an earlier call do not matter -- but all calls on one GPU share the
+ * one array: calls that may run at the same time on one GPU (other streams,
+ * other host threads, a replayed graph next to a live call) race and give wrong
+ * results.  Serialise them, or use mssm_scan_fwd with a workspace each.
+ */
+#define MSSM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+mssm_status mssm_scan_fwd_noalloc(const mssm_problem* p,
+                                  const void* u, const void* delta, const float* A,
+                                  const void* Bm, const void* Cm,
+                                  const float* Dskip, const void* z, const float* dt_bias,
+                                  const float* h0,
+                                  void* y, float* h_final, void* hip_stream);
 
 /*
  * Forward scan behind the Mamba block's causal conv1d + SiLU, fused: the scan

@@ -21,7 +21,7 @@ MSSM_F32, MSSM_BF16 = 0, 1
 STATUS = {0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_SHAPE", -3: "MSSM_ERR_DTYPE",
           -4: "MSSM_ERR_UNSUPPORTED", -5: "MSSM_ERR_ALIGN", -6: "MSSM_ERR_WORKSPACE",
           -7: "MSSM_ERR_HIP"}
-EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd",
+EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd", "mssm_scan_fwd_noalloc",
            "mssm_conv_scan_fwd", "mssm_conv_bwd_workspace_bytes", "mssm_conv_bwd", "mssm_scan_bwd", "mssm_step",
            "mssm_conv_step", "mssm_ssd_fwd_workspace_bytes", "mssm_ssd_fwd", "mssm_status_string", "mssm_build_info"]
 MAX_DCONV = 4
@@ -60,6 +60,8 @@ def _open(path: str):
     lib.mssm_scan_bwd_workspace_bytes.restype = sz
     lib.mssm_scan_fwd.argtypes = [P] + [vp] * 11 + [vp, sz, vp]
     lib.mssm_scan_fwd.restype = st
+    lib.mssm_scan_fwd_noalloc.argtypes = [P] + [vp] * 11 + [vp]
+    lib.mssm_scan_fwd_noalloc.restype = st
     lib.mssm_conv_scan_fwd.argtypes = [P, ctypes.c_int32] + [vp] * 15 + [vp, sz, vp]
     lib.mssm_conv_scan_fwd.restype = st
     lib.mssm_conv_bwd_workspace_bytes.argtypes = [P, ctypes.c_int32]
@@ -177,6 +179,36 @@ def scan_fwd(u, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
     _check(lib.mssm_scan_fwd(ctypes.byref(prob), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
                              _ptr(Dskip), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),
                              _ptr(ws), nbytes, _stream(u.device)))
+    return y, h_final
+
+
+def scan_fwd_noalloc(u, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
+                     delta_softplus=True, return_final_state=True, y=None, h_final=None):
+    """scan_fwd through mssm_scan_fwd_noalloc: no workspace, the library's own
+    fixed scratch array instead (calls on one GPU must not overlap).  Pass y
+    (and h_final) to allocate nothing here either."""
+    act = u.dtype
+    B, L, D = u.shape
+    N = A.shape[1]
+    _req(u, "u", (B, L, D), act)
+    _req(delta, "delta", (B, L, D), act)
+    _req(A, "A", (D, N), torch.float32)
+    _req(Bm, "Bm", (B, L, N), act)
+    _req(Cm, "Cm", (B, L, N), act)
+    _opt(Dskip, "Dskip", (D,), torch.float32)
+    _opt(z, "z", (B, L, D), act)
+    _opt(dt_bias, "dt_bias", (D,), torch.float32)
+    _opt(h0, "h0", (B, D, N), torch.float32)
+    if y is None:
+        y = torch.empty((B, L, D), dtype=act, device=u.device)
+    _req(y, "y", (B, L, D), act)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((B, D, N), dtype=torch.float32, device=u.device)
+    _opt(h_final, "h_final", (B, D, N), torch.float32)
+    prob = problem(B, L, D, N, _dtype_code(u), delta_softplus)
+    _check(lib.mssm_scan_fwd_noalloc(ctypes.byref(prob), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                                     _ptr(Dskip), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),
+                                     _stream(u.device)))
     return y, h_final
 
 

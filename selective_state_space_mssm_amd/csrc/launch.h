@@ -61,6 +61,9 @@ struct FwdPlan {
 };
 FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N);
 hipError_t launch_fwd(const ScanArgs& a, hipStream_t s);
+// launch_fwd with the library's own fixed scratch array (mssm_scan_fwd_noalloc)
+// as the workspace; the caller has checked that the plan fits it.
+hipError_t launch_fwd_noalloc(ScanArgs a, hipStream_t s);
 // The forward behind the fused front end: a.u is x, a.conv_w (a.conv_b,
 // a.x_prev) its causal conv; u = silu(conv(x) + bias) is formed inside the
 // kernels (and written to a.u_out if set).  Same schedule and workspace as

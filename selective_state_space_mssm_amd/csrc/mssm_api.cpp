@@ -97,6 +97,26 @@ mssm_status mssm_scan_fwd(const mssm_problem* p, const void* u, const void* delt
     return from_hip(mssm::launch_fwd(a, static_cast<hipStream_t>(hip_stream)));
 }
 
+mssm_status mssm_scan_fwd_noalloc(const mssm_problem* p, const void* u, const void* delta, const float* A,
+                                  const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                                  const float* dt_bias, const float* h0, void* y, float* h_final,
+                                  void* hip_stream) {
+    mssm_status st = check_problem(p, true);
+    if (st != MSSM_OK) return st;
+    if (!u || !delta || !A || !Bm || !Cm || !y) return MSSM_ERR_NULL;
+    st = check_align({u, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, y, h_final});
+    if (st != MSSM_OK) return st;
+    const size_t need = mssm::use_tokens(p->batch, p->seqlen, p->dim)
+                            ? 0 : mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    if (need > MSSM_NOALLOC_SCRATCH_BYTES) return MSSM_ERR_WORKSPACE;
+
+    mssm::ScanArgs a = base_args(p);
+    a.u = u; a.delta = delta; a.z = z; a.Bm = Bm; a.Cm = Cm;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0;
+    a.y = y; a.h_final = h_final;
+    return from_hip(mssm::launch_fwd_noalloc(a, static_cast<hipStream_t>(hip_stream)));
+}
+
 mssm_status mssm_conv_scan_fwd(const mssm_problem* p, int32_t d_conv, const void* x, const float* conv_w,
                                const float* conv_b, const void* x_prev, const void* delta, const float* A,
                                const void* Bm, const void* Cm, const float* Dskip, const void* z,

@@ -3,7 +3,50 @@
 // whose header describes the mapping onto gfx950.
 #include "scan_fwd_kernels.h"
 
+#include <mutex>
+
+#include "mssm.h"
+
 namespace mssm {
+
+// Scratch of mssm_scan_fwd_noalloc: a fixed array in device memory, one copy
+// per GPU (reserved when the code object is loaded onto that GPU), shared by
+// every such call on it.  In host code `scratch` is only a handle for the
+// symbol lookup below: its device address differs per GPU and is what kernels
+// are given.
+static __device__ __align__(256) unsigned char scratch[MSSM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};  // device address of `scratch` per GPU, looked up on first use
+
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_fwd_noalloc(ScanArgs a, hipStream_t st) {
+    void* p = nullptr;
+    const hipError_t e = scratch_address(&p);
+    if (e != hipSuccess) return e;
+    a.workspace = p;
+    a.workspace_bytes = MSSM_NOALLOC_SCRATCH_BYTES;
+    return launch_fwd(a, st);
+}
 
 FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N) {
     FwdPlan p{1, L, 0};

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), f"libmssm.so does not export {n}"
     assert sorted(mssm.EXPORTS) == names
@@ -240,6 +240,35 @@ def test_workspace_sizes_and_checks():
     # invalid problems report no workspace
     assert lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(good(N=3))) == 0
     assert lib.mssm_scan_bwd_workspace_bytes(None) == 0
+
+
+def fwd_noalloc(p, u=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dskip=None, z=None, dt_bias=None, h0=None,
+                y=FAKE, hf=None):
+    pp = ctypes.byref(p) if p is not None else None
+    v = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    return lib.mssm_scan_fwd_noalloc(pp, v(u), v(delta), v(A), v(Bm), v(Cm), v(Dskip), v(z), v(dt_bias), v(h0),
+                                     v(y), v(hf), None)
+
+
+def test_noalloc_forward_validation():
+    """mssm_scan_fwd_noalloc: the forward's checks, then the fixed scratch's
+    limit -- all on the host, before the scratch array is looked up."""
+    assert fwd_noalloc(None) == -1
+    assert fwd_noalloc(good(dtype=3)) == -3
+    assert fwd_noalloc(good(L=0)) == -2
+    assert fwd_noalloc(good(N=12)) == -4
+    for k in ("u", "delta", "A", "Bm", "Cm", "y"):
+        assert fwd_noalloc(good(), **{k: None}) == -1, k
+    for k in ("u", "Dskip", "h0", "y", "hf"):
+        assert fwd_noalloc(good(), **{k: MIS}) == -5, k
+    limit = 32 << 20
+    # 8,192 channel blocks at dstate 64: the balanced schedule's published states alone take 128 MiB
+    big = P(64, 4096, 8192, 64, 1, 1)
+    assert lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(big)) > limit
+    assert fwd_noalloc(big) == -6
+    # the largest time-chunked plans (1M steps, dstate 64) fit
+    for prob in (P(1, 1 << 20, 1536, 64, 1, 1), P(2, 1 << 20, 1536, 64, 0, 1), P(1, 1 << 20, 3072, 64, 1, 1)):
+        assert 0 < lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(prob)) <= limit
 
 
 def test_binding_rejects_cpu_tensors_and_bad_shapes():
