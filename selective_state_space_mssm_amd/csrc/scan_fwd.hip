@@ -53,8 +53,9 @@ FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N) {
     const int64_t blocks = B * ((D + 63) / 64);
     if (blocks >= kBalancedMinBlocks) {
         // room for the balanced schedule (used when the blocks do not split
-        // evenly over the CUs): a flag and a published 64 x N state per block
-        p.ws_bytes = align256(static_cast<size_t>(blocks) * sizeof(uint32_t)) +
+        // evenly over the CUs): a flag and a published 64 x N state per
+        // block, and the word that records a wait that gave up
+        p.ws_bytes = align256(static_cast<size_t>(blocks + 1) * sizeof(uint32_t)) +
                      align256(static_cast<size_t>(blocks) * 64 * N * sizeof(float));
     }
     // Cut time only when the channel blocks alone cannot occupy the chip:

@@ -52,6 +52,7 @@
 //    by SiLU: each helper wave loads its rows of x and the three rows before
 //    them and computes u in registers, so u never goes through HBM.
 #pragma once
+#include "balanced_plan.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -62,6 +63,8 @@ namespace mssm {
 namespace {
 
 constexpr int kTB = 16;  // time steps per tile (= lanes per DPP row)
+// Spin limit of a worker waiting for a published state (s_sleep 2 between polls).
+constexpr uint32_t kMaxWaitSpins = 1u << 27;
 
 // Helper waves of a workgroup: besides the G state waves, which run only the
 // recurrence of their states, the workgroup has helper waves that run the
@@ -109,7 +112,8 @@ struct FwdKArgs {
     float* h_final;
     float* agg_h;          // (B, K, D, N) chunk end state from zero (chunk 0: from h0)
     float* agg_s;          // (B, K, D) chunk sum of Delta
-    uint32_t* flags;       // (nblk) balanced schedule: 1 once a block's split state is published
+    uint32_t* flags;       // (nblk + 1) balanced schedule: 1 once a block's split state is published;
+                           // word nblk: 1 if a wait gave up (kMaxWaitSpins)
     float* carry;          // (nblk, 64, N) balanced schedule: the published states
     int64_t L, D;
     int64_t chunk_len;
@@ -817,14 +821,9 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
 //    and time chunk (initial state from h_in when K > 1);
 //  * workers > 0 -- balanced persistent schedule, one workgroup per worker:
 //    the (block, tile) sequence is cut into `workers` equal contiguous ranges
-//    of at least one block each.  A block is split between at most two
-//    workers.  Each worker first runs its range's last piece if that piece
-//    ends inside a block (it starts at t = 0, so it depends on nobody) and
-//    publishes the end state; then its whole blocks; then its first piece if
-//    that starts inside a block, from the state the previous worker
-//    published.  Equal work per workgroup, no extra arithmetic.  A worker only
-//    waits on a lower-numbered worker, which never waits before publishing
-//    (workgroups are dispatched in increasing order), so every wait ends.
+//    of at least one block each (balanced_plan.h), a block split between two
+//    workers handing its state over through memory.  Equal work per
+//    workgroup, no extra arithmetic.
 template <typename T, int NG, int G, bool HAS_Z, bool PRE, bool CONV>
 __global__ __launch_bounds__(64 * (G + helper_waves(NG, G, PRE)))
 __attribute__((amdgpu_waves_per_eu(conv_min_waves(NG, G, CONV, sizeof(T) == 2)))) void scan_fwd_kernel(FwdKArgs a) {
@@ -837,26 +836,15 @@ __attribute__((amdgpu_waves_per_eu(conv_min_waves(NG, G, CONV, sizeof(T) == 2)))
     const bool state_wave = wave_id() < G;
     const int n0 = state_wave ? wave_id() * NG : 0;
 
-    // Segments of this workgroup, in processing order.  Each is (block,
-    // steps [t_begin, t_end), where its initial state comes from, what
-    // happens to its final state).
-    enum { kFromH0 = 0, kFromChunkCarry = 1, kFromPublished = 2 };
-    enum { kKeep = 0, kFinal = 1, kPublish = 2 };
-    int nseg = 1, tail_piece = 0, full_first = 0, b0 = 0, b1 = 0;
-    int64_t t0 = 0, t1 = 0, T_ = 0;
+    // Segments of this workgroup, in processing order (balanced_plan.h): each
+    // is (block, steps [t_begin, t_end), where its initial state comes from,
+    // what becomes of its final state).
+    const int64_t T_ = (a.L + kTB - 1) / kTB;  // tiles per sequence
+    BalancedRange rg{};
+    int nseg = 1;
     if (a.workers > 0) {
-        T_ = (a.L + kTB - 1) / kTB;  // tiles per sequence
-        const int64_t U = static_cast<int64_t>(a.nblk) * T_;
-        const int64_t u0 = U * blockIdx.x / a.workers;
-        const int64_t u1 = U * (blockIdx.x + 1) / a.workers;
-        b0 = static_cast<int>(u0 / T_);
-        t0 = u0 - b0 * T_;                               // first tile of the range, in block b0
-        b1 = static_cast<int>((u1 - 1) / T_);
-        t1 = u1 - static_cast<int64_t>(b1) * T_;        // end tile of the range, in block b1 (1..T)
-        tail_piece = (b1 > b0 && t1 < T_) ? 1 : 0;       // ends inside b1: run it first and publish
-        full_first = t0 == 0 ? b0 : b0 + 1;
-        const int full_last = t1 == T_ ? b1 : b1 - 1;
-        nseg = tail_piece + (full_last - full_first + 1) + (t0 > 0 ? 1 : 0);
+        rg = balanced_range(a.nblk, T_, a.workers, blockIdx.x);
+        nseg = rg.nseg;
     }
     for (int sg = 0; sg < nseg; ++sg) {
         int blk, from, to;
@@ -867,12 +855,13 @@ __attribute__((amdgpu_waves_per_eu(conv_min_waves(NG, G, CONV, sizeof(T) == 2)))
             t_end = imin64(a.L, t_begin + a.chunk_len);
             from = a.h_in ? kFromChunkCarry : kFromH0;
             to = static_cast<int>(blockIdx.y) == a.chunks - 1 ? kFinal : kKeep;
-        } else if (sg < tail_piece) {  // last piece of the range, ends inside block b1
-            blk = b1; t_begin = 0; t_end = t1 * kTB; from = kFromH0; to = kPublish;
-        } else if (sg < nseg - (t0 > 0 ? 1 : 0)) {  // a whole block
-            blk = full_first + (sg - tail_piece); t_begin = 0; t_end = a.L; from = kFromH0; to = kFinal;
-        } else {  // first piece of the range, starts inside block b0
-            blk = b0; t_begin = t0 * kTB; t_end = a.L; from = kFromPublished; to = kFinal;
+        } else {
+            const BalancedSegment seg = balanced_segment(rg, T_, sg);
+            blk = seg.blk;
+            t_begin = seg.tile_begin * kTB;
+            t_end = imin64(a.L, seg.tile_end * kTB);
+            from = seg.from;
+            to = seg.to;
         }
         const int64_t b = blk / a.dblocks;
         const int64_t chan0 = static_cast<int64_t>(blk % a.dblocks) * 64;
@@ -893,8 +882,17 @@ __attribute__((amdgpu_waves_per_eu(conv_min_waves(NG, G, CONV, sizeof(T) == 2)))
             }
         } else {
             if (threadIdx.x == 0) {
-                while (__hip_atomic_load(a.flags + blk, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u)
+                // bounded: past the limit (minutes; a legitimate wait lasts one
+                // worker's range) the worker records the failure in the word
+                // after the flags and goes on instead of hanging the GPU
+                uint32_t spins = 0;
+                while (__hip_atomic_load(a.flags + blk, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                    if (++spins == kMaxWaitSpins) {
+                        __hip_atomic_store(a.flags + a.nblk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(2);
+                }
             }
             __syncthreads();
             if (state_wave) {
@@ -1175,12 +1173,12 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, void* scratch, con
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        if (ncu > 0 && a.nblk >= ncu && a.nblk % ncu != 0) {
+        if (balanced_plan_ok(a.nblk, ncu) && a.nblk % ncu != 0) {
             a.workers = ncu;
             a.flags = reinterpret_cast<uint32_t*>(ws);
-            a.carry = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(a.nblk) * sizeof(uint32_t)));
-            hipLaunchKernelGGL(zero_flags_kernel, dim3(static_cast<unsigned>((a.nblk + 255) / 256)), dim3(256), 0,
-                               st, a.flags, a.nblk);
+            a.carry = reinterpret_cast<float*>(ws + align256(static_cast<size_t>(a.nblk + 1) * sizeof(uint32_t)));
+            hipLaunchKernelGGL(zero_flags_kernel, dim3(static_cast<unsigned>((a.nblk + 1 + 255) / 256)), dim3(256),
+                               0, st, a.flags, a.nblk + 1);
             grid = dim3(static_cast<unsigned>(ncu));
         }
     }
