@@ -132,6 +132,15 @@ def test_chunked_reverse_state_sizes(mssm, N):
     assert_grads(g, r, GRAD_TOL["f32"])
 
 
+@pytest.mark.parametrize("shape,dtype", [((1, 600, 100), "f32"), ((2, 1024, 64), "bf16")])
+def test_chunked_prepass_short(mssm, shape, dtype):
+    # few channel blocks and 512 <= L < 2048: the pre-pass runs the time-chunked forward schedule
+    B, L, D = shape
+    assert mssm.fwd_workspace_bytes(B, L, D, 16) > 0
+    g, r = run_both(mssm, workloads.custom(B, L, D, 16, dtype, seed=L + 43))
+    assert_grads(g, r, GRAD_TOL[dtype])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_chunked_prepass(mssm, dtype):
     # one channel block and L >= 2048: the forward pre-pass runs the chunked

@@ -111,6 +111,16 @@ def test_chunked_carry_schedule(mssm, dtype):
     check(mssm, workloads.custom(B, L, D, 16, dtype, seed=21), h0=True)
 
 
+@pytest.mark.parametrize("shape,dtype", [((1, 511, 200), "f32"), ((1, 512, 200), "bf16"), ((1, 700, 1536), "bf16"),
+                                         ((2, 1024, 130), "f32"), ((1, 2047, 64), "f32"), ((3, 600, 1000), "bf16")])
+def test_time_split_short_sequences(mssm, shape, dtype):
+    # few channel blocks and 512 <= L < 2048: time cut into chunks of >= 128 steps (K = 4 at L = 512,
+    # up to 16 at L = 2047), ragged last chunks and channel blocks; L = 511 stays one pass
+    B, L, D = shape
+    assert (mssm.fwd_workspace_bytes(B, L, D, 16) > 0) == (L >= 512)
+    check(mssm, workloads.custom(B, L, D, 16, dtype, seed=L + D + 3), h0=True)
+
+
 @pytest.mark.parametrize("shape,dtype", [((5, 100, 3840), "f32"), ((3, 333, 5760), "bf16"), ((4, 101, 4160), "f32")])
 def test_balanced_schedule(mssm, shape, dtype):
     # more channel blocks than CUs but not a multiple of them: the persistent
