@@ -95,6 +95,10 @@ inline bool use_tokens(int64_t B, int64_t L, int64_t D) {
     return L <= 8 || (L <= kTokensMaxL && B * D <= 32768);
 }
 hipError_t launch_tokens(const ScanArgs& a, hipStream_t s);
+// Below this many (b, d) rows the short-sequence path loads 16 tokens' inputs
+// at a time (a few waves run the whole call and would otherwise wait on every
+// token's loads).
+constexpr int64_t kTokensDeepMaxRows = 4096;
 
 // Backward of the conv1d + SiLU front end (a.u = x, a.conv_w, a.conv_b,
 // a.x_prev, a.d_conv as in launch_conv_fwd): time chunks of T steps, partial

@@ -256,6 +256,74 @@ __global__ __launch_bounds__(256) void scan_tokens_kernel(TokKArgs a) {
     }
 }
 
+// The same for few (b, d) rows, where a handful of waves run the whole call
+// and each token's loads would sit on the critical path: the inputs of P
+// tokens are loaded together, then the P tokens are computed, so the load
+// latency is paid once per P tokens instead of once per token.
+template <typename T, int N, int P>
+__global__ __launch_bounds__(256) void scan_tokens_deep_kernel(TokKArgs a) {
+    constexpr int V = N >= 4 ? 4 : N;
+    constexpr int R = N / V;
+    const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t i = g / R;
+    const int q = static_cast<int>(g % R);
+    if (i >= a.B * a.D) return;
+    const int64_t b = i / a.D, d = i % a.D;
+    const int n0 = q * V;
+    const int64_t D = a.D, L = a.L;
+    float A2[V], h[V];
+#pragma unroll
+    for (int n = 0; n < V; ++n) {
+        A2[n] = a.A[d * N + n0 + n] * kLog2e;
+        h[n] = a.h0 ? a.h0[i * N + n0 + n] : 0.0f;
+    }
+    const float bias = a.dt_bias ? a.dt_bias[d] : 0.0f;
+    const float Dk = a.Dskip ? a.Dskip[d] : 0.0f;
+    const T* __restrict__ u = static_cast<const T*>(a.u) + b * L * D + d;
+    const T* __restrict__ dl = static_cast<const T*>(a.delta) + b * L * D + d;
+    const T* __restrict__ z = a.z ? static_cast<const T*>(a.z) + b * L * D + d : nullptr;
+    T* __restrict__ y = static_cast<T*>(a.y) + b * L * D + d;
+    const T* __restrict__ Bm = static_cast<const T*>(a.Bm) + b * L * N + n0;
+    const T* __restrict__ Cm = static_cast<const T*>(a.Cm) + b * L * N + n0;
+    for (int64_t t0 = 0; t0 < L; t0 += P) {
+        float ru[P], rx[P], rz[P], rb[P][V], rc[P][V];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int64_t t = imin64(t0 + j, L - 1);  // past the end: the last token again, never used
+            ru[j] = load_act(u, t * D);
+            rx[j] = load_act(dl, t * D);
+            rz[j] = z ? load_act(z, t * D) : 0.0f;
+            load_states<V>(Bm + t * N, rb[j]);
+            load_states<V>(Cm + t * N, rc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            if (t0 + j < L) {
+                const float x = rx[j] + bias;
+                const float dt = a.softplus ? softplus(x) : x;
+                const float du = dt * ru[j];
+                float s = 0.0f;
+#pragma unroll
+                for (int n = 0; n < V; ++n) {
+                    h[n] = __builtin_fmaf(fast_exp2(dt * A2[n]), h[n], du * rb[j][n]);
+                    s = __builtin_fmaf(rc[j][n], h[n], s);
+                }
+#pragma unroll
+                for (int m = 1; m < R; m <<= 1) s += __shfl_xor(s, m);
+                if (q == 0) {
+                    s = __builtin_fmaf(Dk, ru[j], s);
+                    if (z) s *= silu(rz[j]);
+                    store_act(y, (t0 + j) * D, s);
+                }
+            }
+        }
+    }
+    if (a.h_final) {
+#pragma unroll
+        for (int n = 0; n < V; ++n) a.h_final[i * N + n0 + n] = h[n];
+    }
+}
+
 template <typename T, bool CONV>
 hipError_t dispatch(const StepKArgs& k, int64_t N, hipStream_t st) {
     const int64_t lanes = k.B * k.D * (N >= 4 ? N / 4 : 1);  // N/4 lanes per (b, d) row
@@ -279,6 +347,20 @@ template <typename T>
 hipError_t dispatch_tokens(const TokKArgs& k, int64_t N, hipStream_t st) {
     const int64_t lanes = k.B * k.D * (N >= 4 ? N / 4 : 1);
     const dim3 grid(static_cast<unsigned>((lanes + 255) / 256));
+    if (k.B * k.D <= kTokensDeepMaxRows && k.L > 8) {  // few rows: loads of 16 tokens at a time
+        constexpr int P = 16;
+        switch (N) {
+            case 1: hipLaunchKernelGGL((scan_tokens_deep_kernel<T, 1, P>), grid, dim3(256), 0, st, k); break;
+            case 2: hipLaunchKernelGGL((scan_tokens_deep_kernel<T, 2, P>), grid, dim3(256), 0, st, k); break;
+            case 4: hipLaunchKernelGGL((scan_tokens_deep_kernel<T, 4, P>), grid, dim3(256), 0, st, k); break;
+            case 8: hipLaunchKernelGGL((scan_tokens_deep_kernel<T, 8, P>), grid, dim3(256), 0, st, k); break;
+            case 16: hipLaunchKernelGGL((scan_tokens_deep_kernel<T, 16, P>), grid, dim3(256), 0, st, k); break;
+            case 32: hipLaunchKernelGGL((scan_tokens_deep_kernel<T, 32, P>), grid, dim3(256), 0, st, k); break;
+            case 64: hipLaunchKernelGGL((scan_tokens_deep_kernel<T, 64, P>), grid, dim3(256), 0, st, k); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (N) {
         case 1: hipLaunchKernelGGL((scan_tokens_kernel<T, 1>), grid, dim3(256), 0, st, k); break;
         case 2: hipLaunchKernelGGL((scan_tokens_kernel<T, 2>), grid, dim3(256), 0, st, k); break;

@@ -157,3 +157,23 @@ def test_short_path_many_rows(mssm):
         yr, hr = run_oracle_fwd(oracle, inp)
         assert fwd_err(to_np(y), yr) <= FWD_TOL["bf16"]
         assert fwd_err(to_np(hf), hr) <= STATE_TOL
+
+
+@pytest.mark.parametrize("shape,dtype", [((2, 20, 2048), "bf16"), ((1, 33, 4097), "f32"), ((1, 64, 32), "f32"),
+                                         ((3, 17, 5), "bf16"), ((1, 9, 64), "f32")])
+def test_short_path_few_rows(mssm, shape, dtype):
+    """Few (b, d) rows (at most 4,096) over 9 to 64 steps: the short path loads
+    16 tokens' inputs at a time (here 1, 2, 3 or 4 groups of 16, the last one
+    partial); 4,097 rows keep the one-token prefetch."""
+    B, L, D = shape
+    w = workloads.custom(B, L, D, 16, dtype, seed=230 + L + D)
+    print(f"[short few rows] {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    t = gpu_inputs(inp)
+    h0 = np.random.default_rng(D).standard_normal((B, D, 16)).astype(np.float32)
+    y, hf = mssm.scan_fwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"], t["dt_bias"],
+                          torch.from_numpy(h0).cuda())
+    torch.cuda.synchronize()
+    yr, hr = run_oracle_fwd(oracle, inp, h0)
+    assert fwd_err(to_np(y), yr) <= FWD_TOL[dtype]
+    assert fwd_err(to_np(hf), hr) <= STATE_TOL
