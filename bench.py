@@ -55,7 +55,7 @@ HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, published
 # kernel sources it was measured on (their SHA-256 is recorded beside it).
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "scan_fwd_2p8b_hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_mssm_amd", "csrc", f)
-                  for f in ("scan_fwd.hip", "scan_fwd_kernels.h", "device_common.h", "launch.h")]
+                  for f in ("scan_fwd.hip", "scan_fwd_kernels.h", "balanced_plan.h", "device_common.h", "launch.h")]
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # lane-instructions/s: CUs x SIMDs x lanes x clock
 SLOTS_PER_ELEM_STATE = 6                  # 4 VALU + 1 v_exp_f32 at half rate (2 issue slots)
 
