@@ -52,7 +52,11 @@
  *   enqueued, and return without touching any buffer.  A launch failure
  *   returns MSSM_ERR_HIP.  NaN and Inf in inputs are not trapped; they
  *   propagate.  No exception crosses the ABI.
- * Limits: 1 <= dstate <= MSSM_MAX_DSTATE and dstate a power of two;
+ * Limits: 1 <= dstate <= MSSM_MAX_DSTATE (a dstate that is not a power of two
+ *   runs the next power of two's kernels with the extra states inert --
+ *   A, Bm, Cm and h0 zero for them, so they stay 0 and add nothing to y -- on
+ *   zero-padded copies of Bm, Cm, A, h0 in the workspace, which the
+ *   *_workspace_bytes queries include);
  *   batch, seqlen, dim >= 1; batch * dim and seqlen below 2^31; dim below
  *   2^24; all indexing of (B, L, D) tensors is 64-bit.
  */
@@ -77,7 +81,7 @@ typedef enum {
     MSSM_ERR_NULL = -1,        /* a required pointer is NULL */
     MSSM_ERR_SHAPE = -2,       /* a dimension is out of range */
     MSSM_ERR_DTYPE = -3,       /* unknown problem.dtype */
-    MSSM_ERR_UNSUPPORTED = -4, /* valid but not built: dstate not a power of two or > MSSM_MAX_DSTATE */
+    MSSM_ERR_UNSUPPORTED = -4, /* valid but not built: dstate > MSSM_MAX_DSTATE (SSD: other sizes) */
     MSSM_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
     MSSM_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the query returns */
     MSSM_ERR_HIP = -7          /* a HIP launch failed */

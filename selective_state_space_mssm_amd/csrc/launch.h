@@ -95,6 +95,16 @@ inline bool use_tokens(int64_t B, int64_t L, int64_t D) {
     return L <= 8 || (L <= kTokensMaxL && B * D <= 32768);
 }
 hipError_t launch_tokens(const ScanArgs& a, hipStream_t s);
+
+// Any state size <= 64 (pad.hip): powers of two run as they are, other sizes
+// at the next power of two with the extra states inert (zero-padded Bm, Cm,
+// A, h0 in the workspace).  The *_ws_bytes give the workspace of either.
+bool needs_padding(int64_t N);
+size_t fwd_ws_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype);
+size_t bwd_ws_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype);
+hipError_t launch_fwd_any(const ScanArgs& a, hipStream_t s);
+hipError_t launch_conv_fwd_any(const ScanArgs& a, hipStream_t s);
+hipError_t launch_bwd_any(const ScanArgs& a, hipStream_t s);
 // Below this many (b, d) rows the short-sequence path loads 16 tokens' inputs
 // at a time (a few waves run the whole call and would otherwise wait on every
 // token's loads).

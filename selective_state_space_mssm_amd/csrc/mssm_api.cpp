@@ -16,7 +16,6 @@
 
 namespace {
 
-bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Problem checks shared by every entry point.  `need_seq`: seqlen matters.
@@ -28,7 +27,7 @@ mssm_status check_problem(const mssm_problem* p, bool need_seq) {
     if (p->batch * p->dim >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
     if (p->dim >= (int64_t{1} << 24)) return MSSM_ERR_SHAPE;  // per-tile byte offsets are 31-bit
     if (need_seq && p->seqlen >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
-    if (!is_pow2(p->dstate) || p->dstate > MSSM_MAX_DSTATE) return MSSM_ERR_UNSUPPORTED;
+    if (p->dstate > MSSM_MAX_DSTATE) return MSSM_ERR_UNSUPPORTED;
     return MSSM_OK;
 }
 
@@ -69,12 +68,12 @@ extern "C" {
 
 size_t mssm_scan_fwd_workspace_bytes(const mssm_problem* p) {
     if (check_problem(p, true) != MSSM_OK) return 0;
-    return mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    return mssm::fwd_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate, p->dtype);
 }
 
 size_t mssm_scan_bwd_workspace_bytes(const mssm_problem* p) {
     if (check_problem(p, true) != MSSM_OK) return 0;
-    return mssm::plan_bwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    return mssm::bwd_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate, p->dtype);
 }
 
 mssm_status mssm_scan_fwd(const mssm_problem* p, const void* u, const void* delta, const float* A,
@@ -86,7 +85,7 @@ mssm_status mssm_scan_fwd(const mssm_problem* p, const void* u, const void* delt
     if (!u || !delta || !A || !Bm || !Cm || !y) return MSSM_ERR_NULL;
     st = check_align({u, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, y, h_final, workspace});
     if (st != MSSM_OK) return st;
-    const size_t need = mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    const size_t need = mssm::fwd_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate, p->dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return MSSM_ERR_WORKSPACE;
 
     mssm::ScanArgs a = base_args(p);
@@ -94,7 +93,7 @@ mssm_status mssm_scan_fwd(const mssm_problem* p, const void* u, const void* delt
     a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0;
     a.y = y; a.h_final = h_final;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    return from_hip(mssm::launch_fwd(a, static_cast<hipStream_t>(hip_stream)));
+    return from_hip(mssm::launch_fwd_any(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 mssm_status mssm_scan_fwd_noalloc(const mssm_problem* p, const void* u, const void* delta, const float* A,
@@ -106,8 +105,8 @@ mssm_status mssm_scan_fwd_noalloc(const mssm_problem* p, const void* u, const vo
     if (!u || !delta || !A || !Bm || !Cm || !y) return MSSM_ERR_NULL;
     st = check_align({u, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, y, h_final});
     if (st != MSSM_OK) return st;
-    const size_t need = mssm::use_tokens(p->batch, p->seqlen, p->dim)
-                            ? 0 : mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    const size_t need = mssm::use_tokens(p->batch, p->seqlen, p->dim) && !mssm::needs_padding(p->dstate)
+                            ? 0 : mssm::fwd_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate, p->dtype);
     if (need > MSSM_NOALLOC_SCRATCH_BYTES) return MSSM_ERR_WORKSPACE;
 
     mssm::ScanArgs a = base_args(p);
@@ -129,7 +128,7 @@ mssm_status mssm_conv_scan_fwd(const mssm_problem* p, int32_t d_conv, const void
     st = check_align({x, conv_w, conv_b, x_prev, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, y, h_final, u_out,
                       workspace});
     if (st != MSSM_OK) return st;
-    const size_t need = mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    const size_t need = mssm::fwd_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate, p->dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return MSSM_ERR_WORKSPACE;
 
     mssm::ScanArgs a = base_args(p);
@@ -139,7 +138,7 @@ mssm_status mssm_conv_scan_fwd(const mssm_problem* p, int32_t d_conv, const void
     a.conv_w = conv_w; a.conv_b = conv_b; a.x_prev = d_conv > 1 ? x_prev : nullptr; a.u_out = u_out;
     a.d_conv = d_conv;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    return from_hip(mssm::launch_conv_fwd(a, static_cast<hipStream_t>(hip_stream)));
+    return from_hip(mssm::launch_conv_fwd_any(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 size_t mssm_conv_bwd_workspace_bytes(const mssm_problem* p, int32_t d_conv) {
@@ -180,7 +179,7 @@ mssm_status mssm_scan_bwd(const mssm_problem* p, const void* u, const void* delt
     st = check_align({u, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, dy, dh_final, du, ddelta, dA, dB,
                       dC, dD, dz, ddt_bias, dh0, workspace});
     if (st != MSSM_OK) return st;
-    const size_t need = mssm::plan_bwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    const size_t need = mssm::bwd_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate, p->dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return MSSM_ERR_WORKSPACE;
 
     mssm::ScanArgs a = base_args(p);
@@ -190,7 +189,7 @@ mssm_status mssm_scan_bwd(const mssm_problem* p, const void* u, const void* delt
     a.du = du; a.ddelta = ddelta; a.dz = z ? dz : nullptr; a.dB = dB; a.dC = dC;
     a.dA = dA; a.dD = dD; a.ddt_bias = ddt_bias; a.dh0 = dh0;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    return from_hip(mssm::launch_bwd(a, static_cast<hipStream_t>(hip_stream)));
+    return from_hip(mssm::launch_bwd_any(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 mssm_status mssm_step(const mssm_problem* p, const void* u_t, const void* delta_t, const float* A,
@@ -275,7 +274,7 @@ const char* mssm_status_string(mssm_status s) {
         case MSSM_ERR_NULL: return "MSSM_ERR_NULL: a required pointer is NULL";
         case MSSM_ERR_SHAPE: return "MSSM_ERR_SHAPE: a dimension is out of range";
         case MSSM_ERR_DTYPE: return "MSSM_ERR_DTYPE: unknown element type";
-        case MSSM_ERR_UNSUPPORTED: return "MSSM_ERR_UNSUPPORTED: dstate must be a power of two <= 64";
+        case MSSM_ERR_UNSUPPORTED: return "MSSM_ERR_UNSUPPORTED: dstate > 64 (or an SSD size not built)";
         case MSSM_ERR_ALIGN: return "MSSM_ERR_ALIGN: a pointer is not 16-byte aligned";
         case MSSM_ERR_WORKSPACE: return "MSSM_ERR_WORKSPACE: workspace missing or too small";
         case MSSM_ERR_HIP: return "MSSM_ERR_HIP: a HIP launch failed";

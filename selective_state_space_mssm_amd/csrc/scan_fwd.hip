@@ -45,7 +45,7 @@ hipError_t launch_fwd_noalloc(ScanArgs a, hipStream_t st) {
     if (e != hipSuccess) return e;
     a.workspace = p;
     a.workspace_bytes = MSSM_NOALLOC_SCRATCH_BYTES;
-    return launch_fwd(a, st);
+    return launch_fwd_any(a, st);
 }
 
 FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N) {

@@ -136,6 +136,47 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
     }
 }
 
+// The step for a state size that is not a power of two (any N <= 64): one
+// lane per (b, d) row, looping over the N states of the row in memory.
+template <typename T, bool CONV>
+__global__ __launch_bounds__(256) void scan_step_any_kernel(StepKArgs a, int N) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= a.B * a.D) return;
+    const int64_t b = i / a.D, d = i % a.D;
+    float uu = load_act(static_cast<const T*>(a.u), i);
+    if constexpr (CONV) {
+        // as the single-lane rows of scan_step_kernel: x_{t-K+1} .. x_{t-1} from the conv state, x_t shifted in
+        const int K = a.K;
+        T* cs = static_cast<T*>(a.conv_state) + b * (K - 1) * a.D + d;  // (b, 0, d)
+        float c = a.conv_b ? a.conv_b[d] : 0.0f;
+        for (int k = 0; k < K - 1; ++k) {  // row k is read before row k is rewritten (as row (k + 1) - 1)
+            const float xk = load_act(cs, k * a.D);
+            c = __builtin_fmaf(a.conv_w[d * K + k], xk, c);
+            if (k > 0) store_act(cs, (k - 1) * a.D, xk);
+        }
+        c = __builtin_fmaf(a.conv_w[d * K + K - 1], uu, c);
+        if (K > 1) store_act(cs, (K - 2) * a.D, uu);
+        uu = silu(c);
+    }
+    const float x = load_act(static_cast<const T*>(a.delta), i) + (a.dt_bias ? a.dt_bias[d] : 0.0f);
+    const float dt = a.softplus ? softplus(x) : x;
+    const float du = dt * uu;
+    const float dtl = dt * kLog2e;
+    const T* __restrict__ Bm = static_cast<const T*>(a.Bm) + b * N;
+    const T* __restrict__ Cm = static_cast<const T*>(a.Cm) + b * N;
+    float* __restrict__ st = a.state + i * N;
+    const float* __restrict__ Ad = a.A + d * N;
+    float s = 0.0f;
+    for (int n = 0; n < N; ++n) {
+        const float h = __builtin_fmaf(fast_exp2(dtl * Ad[n]), st[n], du * load_act(Bm, n));
+        s = __builtin_fmaf(load_act(Cm, n), h, s);
+        st[n] = h;
+    }
+    s = __builtin_fmaf(a.Dskip ? a.Dskip[d] : 0.0f, uu, s);
+    if (a.z) s *= silu(load_act(static_cast<const T*>(a.z), i));
+    store_act(static_cast<T*>(a.y), i, s);
+}
+
 // V consecutive values (V = 4: one 8-byte bf16 / 16-byte fp32 load; the
 // lane's first state index is a multiple of 4, so the address is aligned).
 template <int V>
@@ -326,6 +367,11 @@ __global__ __launch_bounds__(256) void scan_tokens_deep_kernel(TokKArgs a) {
 
 template <typename T, bool CONV>
 hipError_t dispatch(const StepKArgs& k, int64_t N, hipStream_t st) {
+    if ((N & (N - 1)) != 0) {  // not a power of two: one lane per row
+        hipLaunchKernelGGL((scan_step_any_kernel<T, CONV>), dim3(static_cast<unsigned>((k.B * k.D + 255) / 256)),
+                           dim3(256), 0, st, k, static_cast<int>(N));
+        return hipGetLastError();
+    }
     const int64_t lanes = k.B * k.D * (N >= 4 ? N / 4 : 1);  // N/4 lanes per (b, d) row
     const dim3 grid(static_cast<unsigned>((lanes + 255) / 256));
     switch (N) {

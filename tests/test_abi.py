@@ -94,12 +94,16 @@ def test_problem_validation():
         assert fwd(bad) == -2
     assert fwd(good(B=1 << 20, D=1 << 11)) == -2     # B*D >= 2^31
     assert fwd(good(L=1 << 31)) == -2
-    assert fwd(good(N=12)) == -4
+    assert fwd(good(N=65)) == -4
     assert fwd(good(N=128)) == -4
+    # any dstate up to 64 is valid (not a power of two: padded in the workspace), so N = 12 gets as far as the
+    # workspace check
+    assert lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(good(N=12))) > 0
+    assert fwd(good(N=12)) == -6
     # the same checks guard the backward and the step
-    assert bwd(good(N=12)) == -4
+    assert bwd(good(N=65)) == -4
     assert bwd(good(dtype=5)) == -3
-    assert step(good(N=3)) == -4
+    assert step(good(N=96)) == -4
     assert step(good(D=0)) == -2
 
 
@@ -129,7 +133,7 @@ def test_alignment():
 def test_conv_front_end_validation():
     # the problem checks of the forward, then the conv's own: width, required taps, alignment
     assert conv_fwd(None) == -1
-    assert conv_fwd(good(N=12)) == -4
+    assert conv_fwd(good(N=72)) == -4
     assert conv_fwd(good(L=0)) == -2
     for k in (0, 5, -1):
         assert conv_fwd(good(), d_conv=k) == -2, k
@@ -177,7 +181,7 @@ def test_conv_step_validation():
         args = [v(kw.get(n, FAKE if n in req else None)) for n in names]
         return lib.mssm_conv_step(ctypes.byref(p) if p is not None else None, d_conv, *args, None)
     assert cs(None) == -1
-    assert cs(good(N=12)) == -4
+    assert cs(good(N=72)) == -4
     for k in (0, 5):
         assert cs(good(), d_conv=k) == -2
     for k in ("x_t", "conv_w", "conv_state", "delta_t", "A", "Bm_t", "Cm_t", "state", "y_t"):
@@ -238,7 +242,7 @@ def test_workspace_sizes_and_checks():
     assert bwd(good(), ws=None) == -6
     assert bwd(good(), ws=FAKE, wsb=nbw - 1) == -6
     # invalid problems report no workspace
-    assert lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(good(N=3))) == 0
+    assert lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(good(N=65))) == 0
     assert lib.mssm_scan_bwd_workspace_bytes(None) == 0
 
 
@@ -256,7 +260,7 @@ def test_noalloc_forward_validation():
     assert fwd_noalloc(None) == -1
     assert fwd_noalloc(good(dtype=3)) == -3
     assert fwd_noalloc(good(L=0)) == -2
-    assert fwd_noalloc(good(N=12)) == -4
+    assert fwd_noalloc(good(N=80)) == -4
     for k in ("u", "delta", "A", "Bm", "Cm", "y"):
         assert fwd_noalloc(good(), **{k: None}) == -1, k
     for k in ("u", "Dskip", "h0", "y", "hf"):
