@@ -316,13 +316,21 @@ typedef struct {
     int32_t delta_softplus; /* nonzero: Delta = softplus(dt + dt_bias) */
 } mssm_ssd_problem;
 
-/* Bytes of device scratch mssm_ssd_fwd needs: 0 when there are at least 128
- * (batch, head) pairs or the sequence is shorter than 4 chunks; otherwise the
- * sequence is cut into time segments scanned in parallel, and the scratch
- * holds each segment's state and log-decay, (B * H * segments * (P * N + 1))
- * floats, and with bfloat16 activations also float32 outputs (B * L * H * P
- * floats) that the last pass completes and rounds once.  0 for an invalid
- * problem. */
+/* Bytes of device scratch mssm_ssd_fwd needs on the current device, which has
+ * C compute units:
+ *  - B * H >= C and not a multiple of C: one persistent workgroup per CU
+ *    scans an equal share of all 64-step chunks, a (batch, head) pair split
+ *    between two of them handing its state over; scratch: C + 1 flags (padded
+ *    to 256 bytes) and C states of P * N floats;
+ *  - otherwise 0 when there are at least 128 (batch, head) pairs or the
+ *    sequence is shorter than 4 chunks;
+ *  - otherwise the sequence is cut into time segments scanned in parallel, and
+ *    the scratch holds each segment's state and log-decay,
+ *    (B * H * segments * (P * N + 1)) floats, and with bfloat16 activations
+ *    also float32 outputs (B * L * H * P floats) that the last pass completes
+ *    and rounds once.
+ * 0 for an invalid problem.  A workspace sized on one device may be too small
+ * on another with more CUs (MSSM_ERR_WORKSPACE). */
 size_t mssm_ssd_fwd_workspace_bytes(const mssm_ssd_problem* p);
 
 mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,

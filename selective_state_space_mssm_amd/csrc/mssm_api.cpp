@@ -227,6 +227,16 @@ mssm_status mssm_conv_step(const mssm_problem* p, int32_t d_conv, const void* x_
 }
 
 namespace {
+// Compute units of the current device (0 if the query fails: no balanced schedule then).
+int64_t device_cus() {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return ncu;
+}
+
 mssm_status check_ssd_problem(const mssm_ssd_problem* p) {
     if (!p) return MSSM_ERR_NULL;
     if (p->dtype != MSSM_F32 && p->dtype != MSSM_BF16) return MSSM_ERR_DTYPE;
@@ -240,7 +250,9 @@ mssm_status check_ssd_problem(const mssm_ssd_problem* p) {
 
 size_t mssm_ssd_fwd_workspace_bytes(const mssm_ssd_problem* p) {
     if (check_ssd_problem(p) != MSSM_OK) return 0;
-    return mssm::plan_ssd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate, p->dtype == MSSM_BF16).ws_bytes;
+    return mssm::plan_ssd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate, p->dtype == MSSM_BF16,
+                          device_cus())
+        .ws_bytes;
 }
 
 mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
@@ -253,7 +265,7 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* d
     const mssm_status st = check_align({x, dt, A, Bm, Cm, Dskip, dt_bias, h0, y, h_final, workspace});
     if (st != MSSM_OK) return st;
     const mssm::SsdPlan plan = mssm::plan_ssd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate,
-                                              p->dtype == MSSM_BF16);
+                                              p->dtype == MSSM_BF16, device_cus());
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return MSSM_ERR_WORKSPACE;
 
     mssm::SsdArgs a{};
@@ -265,6 +277,13 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* d
     a.nseg = plan.nseg; a.seg_len = plan.seg_len; a.ws = static_cast<float*>(workspace);
     a.ws_y = plan.nseg > 1 && p->dtype == MSSM_BF16
                  ? a.ws + p->batch * p->nheads * plan.nseg * (p->headdim * p->dstate + 1) : nullptr;
+    if (plan.workers > 0) {
+        a.workers = static_cast<int32_t>(plan.workers);
+        a.flags = static_cast<uint32_t*>(workspace);
+        a.carry = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           ((static_cast<size_t>(plan.workers + 1) * sizeof(uint32_t) + 255) &
+                                            ~static_cast<size_t>(255)));
+    }
     return from_hip(mssm::launch_ssd_fwd(a, static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -29,6 +29,10 @@ struct SsdArgs {
     float* ws;             // nseg > 1: segment states (B, H, nseg, P, N), then log-decays (B, H, nseg)
     float* ws_y;           // nseg > 1 with bf16 outputs: float32 outputs (B, L, H, P) of segments 1.. before the
                            // correction (a bf16 partial would be rounded twice); else null
+    // balanced persistent schedule (workers > 0, nseg == 1): one workgroup per worker
+    int32_t workers;
+    uint32_t* flags;       // (workers + 1): 1 once worker w has published; word `workers`: 1 if a wait gave up
+    float* carry;          // (workers, P, N): the state worker w hands to worker w + 1
 };
 
 constexpr int kSsdHeadDim = 64;   // P the kernel is built for
@@ -37,23 +41,34 @@ constexpr int kSsdChunk = 64;     // chunk length of the dual form
 // True when the kernel is built for this head dimension and state size.
 inline bool ssd_supported(int64_t P, int64_t N) { return P == kSsdHeadDim && (N == 64 || N == 128); }
 
-// How the sequence is cut: with fewer (batch, head) pairs than half the 256
-// CUs, the sequence splits into segments of at least two chunks, as many as
-// fit one workgroup per CU in a single round (a second, partial round would
-// double the time); each segment is scanned from a zero state, a
-// carry pass forms the state entering every segment, and a correction pass
-// adds that state's contribution to the segment's outputs.  Scratch: the
-// segment states and log-decays, and for bfloat16 outputs a float32 copy of
-// the outputs the correction completes.
+// How the work is cut, for a device of ncu compute units (one workgroup fits
+// a CU).  With fewer (batch, head) pairs than half the 256 CUs of an MI355X,
+// the sequence splits into segments of at least two chunks, as many as fit
+// one workgroup per CU in a single round (a second, partial round would
+// double the time); each segment is scanned from a zero state, a carry pass
+// forms the state entering every segment, and a correction pass adds that
+// state's contribution to the segment's outputs.  Scratch: the segment states
+// and log-decays, and for bfloat16 outputs a float32 copy of the outputs the
+// correction completes.  With at least ncu pairs that do not divide evenly
+// over the CUs (the last round of a grid would run partly empty), a
+// persistent workgroup per CU scans an equal share of all chunks instead;
+// scratch: a flag per worker and the one state each worker hands over.
 struct SsdPlan {
     int64_t nseg;
     int64_t seg_len;
+    int64_t workers;
     size_t ws_bytes;
 };
 
-inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, bool bf16) {
-    SsdPlan pl{1, L, 0};
+inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, bool bf16, int64_t ncu) {
+    SsdPlan pl{1, L, 0, 0};
     const int64_t jobs = B * H, chunks = (L + kSsdChunk - 1) / kSsdChunk;
+    if (ncu > 0 && jobs >= ncu && jobs % ncu != 0) {
+        pl.workers = ncu;
+        pl.ws_bytes = ((static_cast<size_t>(ncu + 1) * sizeof(uint32_t) + 255) & ~static_cast<size_t>(255)) +
+                      static_cast<size_t>(ncu * P * N) * sizeof(float);
+        return pl;
+    }
     if (jobs >= 128 || chunks < 4) return pl;
     const int64_t want = 256 / jobs, most = chunks / 2;
     const int64_t segs = want < most ? want : most;

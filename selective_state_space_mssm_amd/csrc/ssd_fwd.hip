@@ -25,6 +25,7 @@
 //   accumulator item r: row (r / 4) * 8 + hl * 4 + r % 4, column l % 32.
 #include <hip/hip_runtime.h>
 
+#include "balanced_plan.h"
 #include "device_common.h"
 #include "ssd.h"
 
@@ -34,6 +35,8 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kQ = kSsdChunk;
+// spins of a bounded wait for a handed-over state (each with a short sleep)
+constexpr uint32_t kSsdMaxWaitSpins = 1u << 27;
 constexpr int kP = kSsdHeadDim;
 constexpr int kThreads = 256;
 
@@ -82,9 +85,9 @@ __device__ __forceinline__ int opaque(int v) {
 constexpr int kPadCol = 1;
 constexpr int kPadRow = 1;
 
-// One chunk's operands.
+// One chunk's operands.  16-byte aligned: cum is read four floats at a time.
 template <int N>
-struct SsdSmem {
+struct alignas(16) SsdSmem {
     static constexpr int kSB = N + kPadCol;    // row stride of b, c
     static constexpr int kSX = kP + kPadRow;   // row stride of x, st
     static constexpr int kSM = kQ + kPadCol;   // row stride of m
@@ -103,8 +106,8 @@ struct SsdSmem {
 // latency hides behind the matrix core (one wave per SIMD has no other wave
 // to cover it).  DIST times the reads per step stays within the 15 LDS
 // operations the wave's lgkm counter can track.
-template <int STEPS, int DIST = 6, class F>
-__device__ __forceinline__ f32x16 mfma_chain(f32x16 acc, F&& ld) {
+template <int STEPS, int DIST = 6, class F, class S>
+__device__ __forceinline__ f32x16 mfma_chain(f32x16 acc, F&& ld, S&& side) {
     float av[STEPS], bv[STEPS];
 #pragma unroll
     for (int s = 0; s < DIST && s < STEPS; ++s) ld(s, av[s], bv[s]);
@@ -115,8 +118,16 @@ __device__ __forceinline__ f32x16 mfma_chain(f32x16 acc, F&& ld) {
         // one next to its MFMA and wait out its latency there
         __builtin_amdgcn_sched_barrier(0);
         acc = mfma32(av[s], bv[s], acc);
+        // other work of step s (side(s)) issues behind the product
+        side(s);
+        __builtin_amdgcn_sched_barrier(0);
     }
     return acc;
+}
+
+template <int STEPS, int DIST = 6, class F>
+__device__ __forceinline__ f32x16 mfma_chain(f32x16 acc, F&& ld) {
+    return mfma_chain<STEPS, DIST>(acc, ld, [](int) {});
 }
 
 // As mfma_chain, with the A operand of step s the product of two values
@@ -148,6 +159,18 @@ __device__ __forceinline__ int64_t xcd_order(int64_t i, int64_t n) {
     return x * per + (x < rem ? x : rem) + slot;
 }
 
+// Where float4 number f of a staged row-major array (cpr float4 per row, an
+// odd row stride in LDS) goes: each 32 lanes take 4 rows x 8 float4, lane l at
+// row l % 4 and float4 column l / 4.  A staging write of component j then puts
+// lane l at bank (row + 4 * column + j) % 32 = (l + const) % 32, 32 distinct
+// banks, where 32 lanes along one row would meet 8 banks four times each.  In
+// global memory a 32-lane group still reads 4 runs of 128 contiguous bytes.
+__device__ __forceinline__ void stage_pos(int f, int cpr, int& row, int& c4) {
+    const int u = f >> 5, l = f & 31, upr = cpr / 8;
+    row = (u / upr) * 4 + (l & 3);
+    c4 = (u % upr) * 8 + (l >> 2);
+}
+
 // One chunk's global inputs, held in registers from the previous chunk's
 // compute until they are staged into LDS.
 template <int N>
@@ -159,33 +182,100 @@ struct ChunkRegs {
 };
 
 // Loads chunk [t0, t0 + 64) into registers through buffer resources that
-// cover only the chunk's valid rows (those before t_end): a row past the sequence end lies outside
-// its resource and reads as zeros, with no branch and no address select (a
-// chunk wholly past the end has an empty resource and touches no memory).
+// cover only the chunk's valid rows (those before t_end): a row past the
+// sequence end lies outside its resource and reads as zeros, with no branch and
+// no address select (a chunk wholly past the end has an empty resource and
+// touches no memory).  The loads are numbered (piece k < kPieces: the X float4s,
+// then Bm's, Cm's, then the step sizes) so that a caller can spread their
+// issue over other work; k must be a compile-time constant after unrolling.
 template <class T, int N>
-__device__ __forceinline__ void load_chunk(const SsdArgs& a, int64_t bi, int64_t h, int64_t t0, int64_t t_end,
-                                           int tid, ChunkRegs<N>& g) {
-    const int64_t H = a.H, L = a.L;
-    const int64_t nv = t_end - t0 < 0 ? 0 : imin64(kQ, t_end - t0);
-    const int64_t row0 = bi * L + t0;
-    const T* x = static_cast<const T*>(a.x);
-    const auto rx = make_rsrc(x + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
-    const auto rb = make_rsrc(static_cast<const T*>(a.Bm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
-    const auto rc = make_rsrc(static_cast<const T*>(a.Cm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
-    const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
-#pragma unroll
-    for (int e = 0; e < ChunkRegs<N>::kX; ++e) {
-        const int q = e * kThreads + tid, i = q / (kP / 4), p = (q % (kP / 4)) * 4;
-        g.x[e] = load4(x, rx, (int)((i * H + h) * kP + p));
+struct ChunkLoader {
+    static constexpr int kX = ChunkRegs<N>::kX, kB = ChunkRegs<N>::kB;
+    static constexpr int kPieces = kX + 2 * kB + 1;
+    __amdgpu_buffer_rsrc_t rx, rb, rc, rd;
+    int64_t H, h;
+    int tid;
+
+    __device__ __forceinline__ ChunkLoader(const SsdArgs& a, int64_t bi, int64_t h_, int64_t t0, int64_t t_end,
+                                           int tid_)
+        : H(a.H), h(h_), tid(tid_) {
+        const int64_t nv = t_end - t0 < 0 ? 0 : imin64(kQ, t_end - t0);
+        const int64_t row0 = bi * a.L + t0;
+        rx = make_rsrc(static_cast<const T*>(a.x) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
+        rb = make_rsrc(static_cast<const T*>(a.Bm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
+        rc = make_rsrc(static_cast<const T*>(a.Cm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
+        rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
     }
-#pragma unroll
-    for (int e = 0; e < ChunkRegs<N>::kB; ++e) {
-        const int q = e * kThreads + tid, i = q / (N / 4), n = (q % (N / 4)) * 4;
-        g.b[e] = load4(x, rb, i * N + n);
-        g.c[e] = load4(x, rc, i * N + n);
+
+    __device__ __forceinline__ void piece(int k, ChunkRegs<N>& g) const {
+        const T* tag = nullptr;  // selects the load4 / load1 overload of the activation type
+        if (k < kX) {
+            int i, p;
+            stage_pos(k * kThreads + tid, kP / 4, i, p);
+            g.x[k] = load4(tag, rx, (int)((i * H + h) * kP + 4 * p));
+        } else if (k < kX + 2 * kB) {
+            const int e = (k - kX) % kB;
+            int i, n;
+            stage_pos(e * kThreads + tid, N / 4, i, n);
+            if (k < kX + kB)
+                g.b[e] = load4(tag, rb, i * N + 4 * n);
+            else
+                g.c[e] = load4(tag, rc, i * N + 4 * n);
+        } else {
+            g.dt = load1(tag, rd, (int)((tid & 63) * H + h));  // lane = step; used by wave 1
+        }
     }
-    // step sizes, used by wave 0 only
-    g.dt = load1(x, rd, (int)((tid & 63) * H + h));
+
+    __device__ __forceinline__ void all(ChunkRegs<N>& g) const {
+#pragma unroll
+        for (int k = 0; k < kPieces; ++k) piece(k, g);
+    }
+};
+
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele shifts inside each
+// row of 16 lanes (DPP row_shr, lanes before the shift add 0), then the
+// totals of the earlier rows, read from lanes 15, 31 and 47.
+__device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, true));
+    const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
+    const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+    const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
+    const int row = lane >> 4;
+    return v + (row >= 1 ? t0 : 0.0f) + (row >= 2 ? t1 : 0.0f) + (row >= 3 ? t2 : 0.0f);
+}
+
+// One chunk's step quantities, lane t = step t of the chunk: Delta_t (0 for
+// steps past the segment end, nv valid steps), the chunk-local cumulative
+// log-decay cum_t = sum_{s <= t} Delta_s A_h, and the state weight
+// w_t = exp(cum_last - cum_t) Delta_t.
+struct ChunkScan {
+    float d, cum, w;
+};
+__device__ __forceinline__ ChunkScan chunk_scan(float dtv, int nv, float bias, float Ah, int softplus_on, int lane) {
+    float d = 0.0f;
+    if (lane < nv) {
+        const float v = dtv + bias;
+        d = softplus_on ? softplus(v) : v;
+    }
+    const float c = wave_prefix_sum(d * Ah, lane);
+    const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+    return {d, c, fexp(last - c) * d};
+}
+
+// cum of the 16 accumulator rows a lane of half hl holds in row block ti
+// (rows ti * 32 + g * 8 + hl * 4 + q for item r = 4 g + q): four 16-byte reads.
+__device__ __forceinline__ void acc_row_cum(const float* cum, int ti, int hl, float (&ci)[16]) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const float4 v = *reinterpret_cast<const float4*>(cum + ti * 32 + g * 8 + hl * 4);
+        ci[4 * g] = v.x;
+        ci[4 * g + 1] = v.y;
+        ci[4 * g + 2] = v.z;
+        ci[4 * g + 3] = v.w;
+    }
 }
 
 template <class T, int N>
@@ -197,183 +287,254 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     const int lane = tid & 63;
     const int l32 = lane & 31, hl = lane >> 5;
     const int64_t H = a.H, L = a.L;
-    // job = (batch, head, time segment); the segment's steps are [t_begin, t_end)
-    const int64_t job = xcd_order(blockIdx.x, gridDim.x);
-    const int64_t seg = job % a.nseg, bi = job / a.nseg / H, h = job / a.nseg % H;
-    const int64_t t_begin = seg * a.seg_len, t_end = imin64(L, t_begin + a.seg_len);
-
-    const float Ah = a.A[h];
-    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-    const float Dh = a.Dskip ? a.Dskip[h] : 0.0f;
-
     // this wave's state tiles: rows p in [sp * 32, +32), columns n in [((wv & 1) * NT + k) * 32, +32)
     const int sp = wv >> 1;
-    const int64_t state_base = (bi * H + h) * kP * N;
-    f32x16 S[NT];
-    if (a.h0 && seg == 0) {  // later segments start from zero; the carry pass supplies their state
-#pragma unroll
-        for (int k = 0; k < NT; ++k) {
-            const int n = ((wv & 1) * NT + k) * 32 + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) S[k][r] = a.h0[state_base + (int64_t)(sp * 32 + acc_row(r, hl)) * N + n];
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < NT; ++k) S[k] = f32x16{};
-    }
-
     // this wave's tile (ti, tj) of M (Q x Q) and of Y (Q x P)
     const int ti = wv >> 1, tj = wv & 1;
+    // offset of state item (tile k, accumulator item r) of this lane in a (P, N) state
+    auto state_off = [&](int k, int r) { return (sp * 32 + acc_row(r, hl)) * N + ((wv & 1) * NT + k) * 32 + l32; };
 
-    ChunkRegs<N> g;
-    load_chunk<T, N>(a, bi, h, t_begin, t_end, tid, g);
-    float lam = 0.0f;  // the segment's total log-decay, sum of Delta A_h
-
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += kQ) {
-        const int nv = (int)imin64(kQ, t_end - t0);
-
-        // ---- stage: the chunk's operands and S^T into LDS; cum, Delta, w ----
-#pragma unroll
-        for (int e = 0; e < ChunkRegs<N>::kX; ++e) {
-            const int q = e * kThreads + tid, i = q / (kP / 4), p = (q % (kP / 4)) * 4;
-            s.x[i][p] = g.x[e].x; s.x[i][p + 1] = g.x[e].y; s.x[i][p + 2] = g.x[e].z; s.x[i][p + 3] = g.x[e].w;
+    // What this workgroup scans, as segments: a (batch, head) job and its steps [t_begin, t_end).
+    //  * workers == 0: one segment, (batch, head, time segment) number xcd_order(blockIdx.x);
+    //  * workers > 0: worker xcd_order(blockIdx.x) of the balanced persistent schedule
+    //    (balanced_plan.h) over B * H jobs of nch chunks each: every CU scans the same number of
+    //    chunks, and a job split between two workers hands its state over through the workspace.
+    //    Consecutive workers run on one XCD, so a handed-over state and the Bm, Cm rows of a batch
+    //    mostly stay in one L2.
+    const int64_t nch = (L + kQ - 1) / kQ;
+    const int64_t worker = xcd_order(blockIdx.x, gridDim.x);
+    BalancedRange rg{};
+    int nsegs = 1;
+    if (a.workers > 0) {
+        rg = balanced_range(a.B * H, nch, a.workers, worker);
+        nsegs = rg.nseg;
+    }
+    for (int sg = 0; sg < nsegs; ++sg) {
+        int64_t bh, seg = 0, t_begin, t_end;
+        int from = kFromH0, to = kFinal;
+        if (a.workers == 0) {
+            bh = worker / a.nseg;
+            seg = worker % a.nseg;
+            t_begin = seg * a.seg_len;
+            t_end = imin64(L, t_begin + a.seg_len);
+        } else {
+            const BalancedSegment bs = balanced_segment(rg, nch, sg);
+            bh = bs.blk;
+            t_begin = bs.tile_begin * kQ;
+            t_end = imin64(L, bs.tile_end * kQ);
+            from = bs.from;
+            to = bs.to;
         }
-#pragma unroll
-        for (int e = 0; e < ChunkRegs<N>::kB; ++e) {
-            const int q = e * kThreads + tid, i = q / (N / 4), n = (q % (N / 4)) * 4;
-            s.b[i][n] = g.b[e].x; s.b[i][n + 1] = g.b[e].y; s.b[i][n + 2] = g.b[e].z; s.b[i][n + 3] = g.b[e].w;
-            s.c[i][n] = g.c[e].x; s.c[i][n + 1] = g.c[e].y; s.c[i][n + 2] = g.c[e].z; s.c[i][n + 3] = g.c[e].w;
-        }
-#pragma unroll
-        for (int k = 0; k < NT; ++k) {
-            const int n = ((wv & 1) * NT + k) * 32 + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s.st[n][sp * 32 + acc_row(r, hl)] = S[k][r];
-        }
-        if (wv == 0) {
-            float d = 0.0f;
-            if (lane < nv) {
-                const float v = g.dt + bias;
-                d = a.softplus ? softplus(v) : v;
-            }
-            float c = d * Ah;  // inclusive prefix sum over the wave
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(c, off);
-                if (lane >= off) c += o;
-            }
-            const float last = __shfl(c, 63);
-            s.cum[lane] = c;
-            s.dlt[lane] = d;
-            s.w[lane] = fexp(last - c) * d;
-        }
-        __syncthreads();
+        const int64_t bi = bh / H, h = bh % H;
 
-        // the next chunk's inputs travel while this chunk computes (past the end: no access)
-        load_chunk<T, N>(a, bi, h, t0 + kQ, t_end, tid, g);
-        lam += s.cum[kQ - 1];
+        const float Ah = a.A[h];
+        const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+        const float Dh = a.Dskip ? a.Dskip[h] : 0.0f;
 
-        // per-lane LDS base offsets (floats) of the MFMA operands; step k adds a constant
-        constexpr int SB = SsdSmem<N>::kSB, SX = SsdSmem<N>::kSX, SM = SsdSmem<N>::kSM;
-        const float* cf = &s.c[0][0];
-        const float* bf = &s.b[0][0];
-        const float* xf = &s.x[0][0];
-        const float* mf = &s.m[0][0];
-        const float* stf = &s.st[0][0];
-        const int oc = opaque((ti * 32 + l32) * SB + hl);   // C[i][k + hl]
-        const int ob = opaque((tj * 32 + l32) * SB + hl);   // B^T[k + hl][j]
-        const int ost = opaque(hl * SX + tj * 32 + l32);     // S^T[k + hl][p]
-        const int om = opaque((ti * 32 + l32) * SM + hl);   // M[i][k + hl]
-        const int ox = opaque(hl * SX + tj * 32 + l32);     // X[k + hl][p]
-        const int oxs = opaque(hl * SX + sp * 32 + l32);     // X[j + hl][p] of the state rows
-        const int ob_s = opaque(hl * SB + (wv & 1) * NT * 32 + l32);   // B[j + hl][n]
-
-        // ---- M = (C B^T) o Lmask, tile (ti, tj); the tile above the diagonal is zero ----
-        {
-            f32x16 gm = {};
-            if (ti >= tj)
-                gm = mfma_chain<N / 2>(gm, [&](int k, float& av, float& bv) {
-                    av = cf[oc + 2 * k];
-                    bv = bf[ob + 2 * k];
-                });
-            const int j = tj * 32 + l32;
-            const float cj = s.cum[j], dj = s.dlt[j];
-            // above the diagonal: exponent -inf and a selected 0 (a non-finite future Bm row must not
-            // reach an earlier output), both as selects rather than a branch around the exponential
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = ti * 32 + acc_row(r, hl);
-                const bool keep = j <= i;
-                const float v = gm[r] * fexp(keep ? s.cum[i] - cj : -__builtin_inff()) * dj;
-                s.m[i][j] = keep ? v : 0.0f;
-            }
-        }
-        __syncthreads();
-
-        // ---- Y tile (ti, tj): exp(cum_i) (C S^T) + M X + D X ----
-        {
-            f32x16 y = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
-                av = cf[oc + 2 * k];
-                bv = stf[ost + 2 * k * SX];
-            });
-#pragma unroll
-            for (int r = 0; r < 16; ++r) y[r] *= fexp(s.cum[ti * 32 + acc_row(r, hl)]);
-            auto ld_mx = [&](int k, float& av, float& bv) {
-                av = mf[om + 2 * k];
-                bv = xf[ox + 2 * k * SX];
-            };
-            // M is zero right of the diagonal tile: row block ti contracts over k < (ti + 1) * 32
-            if (ti == 0)
-                y = mfma_chain<16>(y, ld_mx);
-            else
-                y = mfma_chain<32>(y, ld_mx);
-            // rows past the sequence end fall outside the resource and are dropped
-            const int p = tj * 32 + l32;
-            if (a.ws_y && seg > 0) {  // a bf16 segment output the correction completes: kept in float32 until then
-                const auto rw = make_rsrc(a.ws_y + (bi * L + t0) * H * kP, (uint32_t)(nv * H * kP * 4));
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = ti * 32 + acc_row(r, hl);
-                    store1<float>(y[r] + Dh * s.x[i][p], rw, (int)((i * H + h) * kP + p));
-                }
-            } else {
-                const auto ry = make_rsrc(static_cast<T*>(a.y) + (bi * L + t0) * H * kP,
-                                          (uint32_t)(nv * H * kP * sizeof(T)));
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int i = ti * 32 + acc_row(r, hl);
-                    store1<T>(y[r] + Dh * s.x[i][p], ry, (int)((i * H + h) * kP + p));
+        const int64_t state_base = bh * kP * N;
+        f32x16 S[NT];
+    #pragma unroll
+        for (int k = 0; k < NT; ++k) S[k] = f32x16{};
+        if (from == kFromPublished) {
+            // the previous worker scanned this job up to t_begin first of all its segments and published
+            // the state; bounded wait: past the limit (minutes; a legitimate wait lasts at most one
+            // worker's range) the worker records the failure in the word after the flags and goes on
+            // instead of hanging the GPU
+            if (tid == 0) {
+                uint32_t spins = 0;
+                while (__hip_atomic_load(a.flags + worker - 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                    if (++spins == kSsdMaxWaitSpins) {
+                        __hip_atomic_store(a.flags + a.workers, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
                 }
             }
+            __syncthreads();
+            float* src = a.carry + (worker - 1) * kP * N;
+    #pragma unroll
+            for (int k = 0; k < NT; ++k)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    S[k][r] = __hip_atomic_load(src + state_off(k, r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (a.h0 && seg == 0) {  // later time segments start from zero; the carry pass supplies their state
+    #pragma unroll
+            for (int k = 0; k < NT; ++k)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) S[k][r] = a.h0[state_base + state_off(k, r)];
         }
 
-        // ---- S' = exp(cum_last) S + (w o X)^T B ----
-        {
-            const float decay = fexp(s.cum[kQ - 1]);
-#pragma unroll
+        ChunkRegs<N> g;
+        ChunkLoader<T, N>(a, bi, h, t_begin, t_end, tid).all(g);
+        float lam = 0.0f;  // the segment's total log-decay, sum of Delta A_h
+        // wave 1, the one with the least matrix work (its M tile lies above the
+        // diagonal), forms each chunk's step quantities one chunk ahead, off the
+        // path to the first barrier
+        ChunkScan cs{};
+        if (wv == 1) cs = chunk_scan(g.dt, (int)imin64(kQ, t_end - t_begin), bias, Ah, a.softplus, lane);
+
+        for (int64_t t0 = t_begin; t0 < t_end; t0 += kQ) {
+            const int nv = (int)imin64(kQ, t_end - t0);
+
+            // ---- stage: the chunk's operands and S^T into LDS; cum, Delta, w ----
+    #pragma unroll
+            for (int e = 0; e < ChunkRegs<N>::kX; ++e) {
+                int i, p;
+                stage_pos(e * kThreads + tid, kP / 4, i, p);
+                p *= 4;
+                s.x[i][p] = g.x[e].x; s.x[i][p + 1] = g.x[e].y; s.x[i][p + 2] = g.x[e].z; s.x[i][p + 3] = g.x[e].w;
+            }
+    #pragma unroll
+            for (int e = 0; e < ChunkRegs<N>::kB; ++e) {
+                int i, n;
+                stage_pos(e * kThreads + tid, N / 4, i, n);
+                n *= 4;
+                s.b[i][n] = g.b[e].x; s.b[i][n + 1] = g.b[e].y; s.b[i][n + 2] = g.b[e].z; s.b[i][n + 3] = g.b[e].w;
+                s.c[i][n] = g.c[e].x; s.c[i][n + 1] = g.c[e].y; s.c[i][n + 2] = g.c[e].z; s.c[i][n + 3] = g.c[e].w;
+            }
+    #pragma unroll
             for (int k = 0; k < NT; ++k) {
-                const int obs = ob_s + k * 32;
-                S[k] = mfma_chain_scaled<kQ / 2>(S[k] * decay, [&](int j, float& av, float& a2, float& bv) {
-                    av = s.w[2 * j + hl];
-                    a2 = xf[oxs + 2 * j * SX];
-                    bv = bf[obs + 2 * j * SB];
-                });
+                const int n = ((wv & 1) * NT + k) * 32 + l32;
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) s.st[n][sp * 32 + acc_row(r, hl)] = S[k][r];
             }
-        }
-        __syncthreads();
-    }
+            if (wv == 1) {
+                s.cum[lane] = cs.cum;
+                s.dlt[lane] = cs.d;
+                s.w[lane] = cs.w;
+            }
+            __syncthreads();
 
-    // one segment: the final state; several: this segment's state from zero and its log-decay, for the carry pass
-    float* out = a.nseg > 1 ? a.ws + ((bi * H + h) * a.nseg + seg) * kP * N : a.h_final ? a.h_final + state_base : nullptr;
-    if (out) {
-#pragma unroll
-        for (int k = 0; k < NT; ++k) {
-            const int n = ((wv & 1) * NT + k) * 32 + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) out[(int64_t)(sp * 32 + acc_row(r, hl)) * N + n] = S[k][r];
+            // the next chunk's inputs travel while this chunk computes (past the end: no access)
+            const ChunkLoader<T, N> next(a, bi, h, t0 + kQ, t_end, tid);
+            lam += s.cum[kQ - 1];
+
+            // per-lane LDS base offsets (floats) of the MFMA operands; step k adds a constant
+            constexpr int SB = SsdSmem<N>::kSB, SX = SsdSmem<N>::kSX, SM = SsdSmem<N>::kSM;
+            const float* cf = &s.c[0][0];
+            const float* bf = &s.b[0][0];
+            const float* xf = &s.x[0][0];
+            const float* mf = &s.m[0][0];
+            const float* stf = &s.st[0][0];
+            const int oc = opaque((ti * 32 + l32) * SB + hl);   // C[i][k + hl]
+            const int ob = opaque((tj * 32 + l32) * SB + hl);   // B^T[k + hl][j]
+            const int ost = opaque(hl * SX + tj * 32 + l32);     // S^T[k + hl][p]
+            const int om = opaque((ti * 32 + l32) * SM + hl);   // M[i][k + hl]
+            const int ox = opaque(hl * SX + tj * 32 + l32);     // X[k + hl][p]
+            const int oxs = opaque(hl * SX + sp * 32 + l32);     // X[j + hl][p] of the state rows
+            const int ob_s = opaque(hl * SB + (wv & 1) * NT * 32 + l32);   // B[j + hl][n]
+
+            // ---- M = (C B^T) o Lmask, tile (ti, tj); the tile above the diagonal is zero ----
+            {
+                f32x16 gm = {};
+                if (ti >= tj) {
+                    // the next chunk's loads go out one every other product, while the matrix core runs:
+                    // issued back to back they hold the wave for thousands of cycles
+                    gm = mfma_chain<N / 2>(
+                        gm,
+                        [&](int k, float& av, float& bv) {
+                            av = cf[oc + 2 * k];
+                            bv = bf[ob + 2 * k];
+                        },
+                        [&](int k) {
+                            if (k % 2 == 0 && k / 2 < next.kPieces) next.piece(k / 2, g);
+                        });
+                    static_assert(ChunkLoader<T, N>::kPieces <= N / 4, "the G chain has a slot for every load");
+                } else {
+                    next.all(g);
+                }
+                const int j = tj * 32 + l32;
+                const float cj = s.cum[j], dj = s.dlt[j];
+                float ci[16];
+                acc_row_cum(s.cum, ti, hl, ci);
+                // above the diagonal: exponent -inf and a selected 0 (a non-finite future Bm row must not
+                // reach an earlier output), both as selects rather than a branch around the exponential
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = ti * 32 + acc_row(r, hl);
+                    const bool keep = j <= i;
+                    const float v = gm[r] * fexp(keep ? ci[r] - cj : -__builtin_inff()) * dj;
+                    s.m[i][j] = keep ? v : 0.0f;
+                }
+            }
+            __syncthreads();
+
+            // ---- Y tile (ti, tj): exp(cum_i) (C S^T) + M X + D X ----
+            {
+                f32x16 y = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
+                    av = cf[oc + 2 * k];
+                    bv = stf[ost + 2 * k * SX];
+                });
+                float ci[16];
+                acc_row_cum(s.cum, ti, hl, ci);
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) y[r] *= fexp(ci[r]);
+                auto ld_mx = [&](int k, float& av, float& bv) {
+                    av = mf[om + 2 * k];
+                    bv = xf[ox + 2 * k * SX];
+                };
+                // M is zero right of the diagonal tile: row block ti contracts over k < (ti + 1) * 32
+                if (ti == 0)
+                    y = mfma_chain<16>(y, ld_mx);
+                else
+                    y = mfma_chain<32>(y, ld_mx);
+                // rows past the sequence end fall outside the resource and are dropped
+                const int p = tj * 32 + l32;
+                if (a.ws_y && seg > 0) {  // a bf16 segment output the correction completes: kept in float32 until then
+                    const auto rw = make_rsrc(a.ws_y + (bi * L + t0) * H * kP, (uint32_t)(nv * H * kP * 4));
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = ti * 32 + acc_row(r, hl);
+                        store1<float>(y[r] + Dh * s.x[i][p], rw, (int)((i * H + h) * kP + p));
+                    }
+                } else {
+                    const auto ry = make_rsrc(static_cast<T*>(a.y) + (bi * L + t0) * H * kP,
+                                              (uint32_t)(nv * H * kP * sizeof(T)));
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int i = ti * 32 + acc_row(r, hl);
+                        store1<T>(y[r] + Dh * s.x[i][p], ry, (int)((i * H + h) * kP + p));
+                    }
+                }
+            }
+
+            if (wv == 1) cs = chunk_scan(g.dt, (int)imin64(kQ, t_end - t0 - kQ), bias, Ah, a.softplus, lane);
+
+            // ---- S' = exp(cum_last) S + (w o X)^T B ----
+            {
+                const float decay = fexp(s.cum[kQ - 1]);
+    #pragma unroll
+                for (int k = 0; k < NT; ++k) {
+                    const int obs = ob_s + k * 32;
+                    S[k] = mfma_chain_scaled<kQ / 2>(S[k] * decay, [&](int j, float& av, float& a2, float& bv) {
+                        av = s.w[2 * j + hl];
+                        a2 = xf[oxs + 2 * j * SX];
+                        bv = bf[obs + 2 * j * SB];
+                    });
+                }
+            }
+            __syncthreads();
+        }
+
+        // The segment's end state: h_final; with time segments, this segment's state from zero and its
+        // log-decay, for the carry pass; a split job's first part, the state the next worker continues from.
+        float* out = to == kPublish ? a.carry + worker * kP * N
+                     : a.nseg > 1   ? a.ws + (bh * a.nseg + seg) * kP * N
+                     : a.h_final    ? a.h_final + state_base
+                                    : nullptr;
+        if (out) {
+    #pragma unroll
+            for (int k = 0; k < NT; ++k)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) out[state_off(k, r)] = S[k][r];
+        }
+        if (a.nseg > 1 && tid == 0) a.ws[a.B * H * a.nseg * kP * N + bh * a.nseg + seg] = lam;
+        if (to == kPublish) {
+            __threadfence();
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(a.flags + worker, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    if (a.nseg > 1 && tid == 0) a.ws[a.B * H * a.nseg * kP * N + (bi * H + h) * a.nseg + seg] = lam;
 }
 
 // Carry pass over the segments, one thread per (batch, head, p, n): the state
@@ -500,9 +661,20 @@ __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
     }
 }
 
+__global__ __launch_bounds__(256) void ssd_zero_flags_kernel(uint32_t* flags, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) flags[i] = 0u;
+}
+
 template <class T, int N>
 hipError_t launch_typed(const SsdArgs& a, hipStream_t st) {
     const dim3 block(kThreads);
+    if (a.workers > 0) {  // a fill kernel rather than a memset: the launch may be captured in a graph
+        hipLaunchKernelGGL(ssd_zero_flags_kernel, dim3((unsigned)((a.workers + 1 + 255) / 256)), dim3(256), 0, st,
+                           a.flags, a.workers + 1);
+        hipLaunchKernelGGL((ssd_fwd_kernel<T, N>), dim3((unsigned)a.workers), block, 0, st, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((ssd_fwd_kernel<T, N>), dim3((unsigned)(a.B * a.H * a.nseg)), block, 0, st, a);
     if (a.nseg > 1) {
         const int64_t n = a.B * a.H * a.P * a.N;

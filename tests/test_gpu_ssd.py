@@ -140,3 +140,50 @@ def test_ssd_bf16(lib, B, L, H, N):
     yr, hr = oracle.ssd_fwd(r["x"], r["dt"], inp["A"], r["Bm"], r["Cm"], inp["Dskip"], inp["dt_bias"], h0n)
     assert fwd_err(to_np(y), yr) <= FWD_TOL["bf16"]
     assert fwd_err(to_np(hf), hr) <= STATE_TOL
+
+
+@pytest.mark.parametrize("B,L,H,N,dtype", [(3, 300, 90, 64, "f32"), (5, 130, 60, 128, "f32"),
+                                           (3, 200, 86, 64, "bf16")])
+def test_ssd_balanced_schedule(lib, B, L, H, N, dtype):
+    # at least as many (batch, head) pairs as CUs, not a multiple of them (270, 300, 258 on a 256-CU MI355X):
+    # one persistent workgroup per CU scans an equal share of the chunks, pairs split between two workgroups
+    # handing their state over through the workspace; with h0 and the state advanced in place
+    import ctypes
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    prob = lib.binding.SsdProblem(B, L, H, 64, N, 1 if dtype == "bf16" else 0, 1)
+    ws = lib.lib.mssm_ssd_fwd_workspace_bytes(ctypes.byref(prob))
+    assert (ws > 0) == (B * H >= ncu and B * H % ncu != 0)
+    print(f"[ssd balanced] B={B} L={L} H={H} N={N} {dtype} ws={ws}", flush=True)
+    inp = workloads.ssd_inputs(B, L, H, 64, N, seed=B * H + L)
+    t = gpu(inp)
+    if dtype == "bf16":
+        for k in ("x", "dt", "Bm", "Cm"):
+            t[k] = t[k].to(torch.bfloat16)
+    h0n = np.random.default_rng(H).standard_normal((B, H, 64, N)).astype(np.float32)
+    state = torch.from_numpy(h0n).cuda()
+    y, _ = lib.ssd_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["dt_bias"], state, h_final=state)
+    torch.cuda.synchronize()
+    r = {k: t[k].float().cpu().numpy() for k in ("x", "dt", "Bm", "Cm")}
+    yr, hr = oracle.ssd_fwd(r["x"], r["dt"], inp["A"], r["Bm"], r["Cm"], inp["Dskip"], inp["dt_bias"], h0n)
+    assert fwd_err(to_np(y), yr) <= FWD_TOL[dtype]
+    assert fwd_err(to_np(state), hr) <= STATE_TOL
+
+
+def test_ssd_mamba2_layer_batch8_sampled(lib):
+    # the timed 80-head layer (B = 8, L = 2048, d_state 128): 640 (batch, head) pairs on the balanced
+    # schedule (on 256 CUs, 2.5 pairs per workgroup; every pair with head = 2 mod 5 is split between two
+    # workgroups); the oracle recomputes heads {0, 37, 79} of every batch in full
+    B, L, H, N = 8, 2048, 80, 128
+    print(f"[ssd 2.7B layer, batch 8] B={B} L={L} H={H} N={N}", flush=True)
+    inp = workloads.ssd_inputs(B, L, H, 64, N, seed=4096)
+    t = gpu(inp)
+    h0n = np.random.default_rng(9).standard_normal((B, H, 64, N)).astype(np.float32)
+    y, hf = lib.ssd_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["dt_bias"],
+                        torch.from_numpy(h0n).cuda())
+    torch.cuda.synchronize()
+    heads = [0, 37, 79]
+    sub = lambda k: inp[k][:, :, heads]  # noqa: E731
+    yr, hr = oracle.ssd_fwd(sub("x"), sub("dt"), inp["A"][heads], inp["Bm"], inp["Cm"], inp["Dskip"][heads],
+                            inp["dt_bias"][heads], h0n[:, heads])
+    assert fwd_err(to_np(y[:, :, heads]), yr) <= TOL
+    assert fwd_err(to_np(hf[:, heads]), hr) <= STATE_TOL
