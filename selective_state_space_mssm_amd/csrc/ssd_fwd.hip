@@ -133,8 +133,8 @@ __device__ __forceinline__ f32x16 mfma_chain(f32x16 acc, F&& ld) {
 // As mfma_chain, with the A operand of step s the product of two values
 // ld(s, a, a2, b) reads: the product is formed when the step issues, so its
 // reads stay DIST steps ahead too.
-template <int STEPS, int DIST = 4, class F>
-__device__ __forceinline__ f32x16 mfma_chain_scaled(f32x16 acc, F&& ld) {
+template <int STEPS, int DIST = 4, class F, class S>
+__device__ __forceinline__ f32x16 mfma_chain_scaled(f32x16 acc, F&& ld, S&& side) {
     float av[STEPS], a2[STEPS], bv[STEPS];
 #pragma unroll
     for (int s = 0; s < DIST && s < STEPS; ++s) ld(s, av[s], a2[s], bv[s]);
@@ -143,6 +143,8 @@ __device__ __forceinline__ f32x16 mfma_chain_scaled(f32x16 acc, F&& ld) {
         if (s + DIST < STEPS) ld(s + DIST, av[s + DIST], a2[s + DIST], bv[s + DIST]);
         __builtin_amdgcn_sched_barrier(0);
         acc = mfma32(av[s] * a2[s], bv[s], acc);
+        side(s);
+        __builtin_amdgcn_sched_barrier(0);
     }
     return acc;
 }
@@ -460,8 +462,9 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             __syncthreads();
 
             // ---- Y tile (ti, tj): exp(cum_i) (C S^T) + M X + D X ----
+            f32x16 y;
             {
-                f32x16 y = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
+                y = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
                     av = cf[oc + 2 * k];
                     bv = stf[ost + 2 * k * SX];
                 });
@@ -478,25 +481,23 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                     y = mfma_chain<16>(y, ld_mx);
                 else
                     y = mfma_chain<32>(y, ld_mx);
-                // rows past the sequence end fall outside the resource and are dropped
                 const int p = tj * 32 + l32;
-                if (a.ws_y && seg > 0) {  // a bf16 segment output the correction completes: kept in float32 until then
-                    const auto rw = make_rsrc(a.ws_y + (bi * L + t0) * H * kP, (uint32_t)(nv * H * kP * 4));
     #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int i = ti * 32 + acc_row(r, hl);
-                        store1<float>(y[r] + Dh * s.x[i][p], rw, (int)((i * H + h) * kP + p));
-                    }
-                } else {
-                    const auto ry = make_rsrc(static_cast<T*>(a.y) + (bi * L + t0) * H * kP,
-                                              (uint32_t)(nv * H * kP * sizeof(T)));
-    #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int i = ti * 32 + acc_row(r, hl);
-                        store1<T>(y[r] + Dh * s.x[i][p], ry, (int)((i * H + h) * kP + p));
-                    }
-                }
+                for (int r = 0; r < 16; ++r) y[r] += Dh * s.x[ti * 32 + acc_row(r, hl)][p];
             }
+            // rows past the sequence end fall outside the resource and are dropped; a bf16 output of a
+            // time segment the correction completes stays float32 until then
+            const bool to_ws = a.ws_y && seg > 0;
+            const auto ry = to_ws ? make_rsrc(a.ws_y + (bi * L + t0) * H * kP, (uint32_t)(nv * H * kP * 4))
+                                  : make_rsrc(static_cast<T*>(a.y) + (bi * L + t0) * H * kP,
+                                              (uint32_t)(nv * H * kP * sizeof(T)));
+            auto store_y = [&](int r) {
+                const int e = (int)(((ti * 32 + acc_row(r, hl)) * H + h) * kP + tj * 32 + l32);
+                if (to_ws)
+                    store1<float>(y[r], ry, e);
+                else
+                    store1<T>(y[r], ry, e);
+            };
 
             if (wv == 1) cs = chunk_scan(g.dt, (int)imin64(kQ, t_end - t0 - kQ), bias, Ah, a.softplus, lane);
 
@@ -506,11 +507,17 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     #pragma unroll
                 for (int k = 0; k < NT; ++k) {
                     const int obs = ob_s + k * 32;
-                    S[k] = mfma_chain_scaled<kQ / 2>(S[k] * decay, [&](int j, float& av, float& a2, float& bv) {
-                        av = s.w[2 * j + hl];
-                        a2 = xf[oxs + 2 * j * SX];
-                        bv = bf[obs + 2 * j * SB];
-                    });
+                    // the Y tile goes out one item every other product of the first update
+                    S[k] = mfma_chain_scaled<kQ / 2>(
+                        S[k] * decay,
+                        [&](int j, float& av, float& a2, float& bv) {
+                            av = s.w[2 * j + hl];
+                            a2 = xf[oxs + 2 * j * SX];
+                            bv = bf[obs + 2 * j * SB];
+                        },
+                        [&](int j) {
+                            if (k == 0 && j % 2 == 0) store_y(j / 2);
+                        });
                 }
             }
             __syncthreads();
