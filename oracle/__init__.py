@@ -29,9 +29,14 @@ read as the same scan with one scalar decay and one step size per head,
 shared by the head's channels and states, and Bm, Cm shared by all heads; the
 oracle runs it through ``scan_fwd`` on the flattened channels.
 
+Its backward (``ssd_bwd``) is the chain rule through that tying: the scan's
+adjoint on the flattened channels, the gradients of the shared step size,
+decay, skip and bias summed over the channels (and states) that share them.
+
 Pinning (what checks this oracle against something other than itself) is in
 ``tests/test_oracle_fwd_pins.py``, ``tests/test_oracle_bwd_pins.py``,
-``tests/test_oracle_conv_pins.py`` and ``tests/test_ssd_dual_form.py``.
+``tests/test_oracle_conv_pins.py``, ``tests/test_ssd_dual_form.py`` and
+``tests/test_ssd_bwd_oracle.py``.
 """
 from __future__ import annotations
 
@@ -233,3 +238,34 @@ def scan_bwd(u, delta, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, h0=None,
         _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
         _ptr(out["ddt_bias"]), _ptr(out["dh0"]))
     return out
+
+
+def ssd_bwd(x, dt, A, Bm, Cm, dy, Dskip=None, dt_bias=None, h0=None, dh_final=None, softplus=True):
+    """Mamba-2 (SSD) backward in float64: the adjoint of ``ssd_fwd`` (the same
+    reading: the selective scan over channels d = (h, p) with A[d, n] = A[h],
+    delta[b,t,d] = dt[b,t,h], Dskip[d] = Dskip[h], dt_bias[d] = dt_bias[h]).
+    By the chain rule through that tying, ``scan_bwd`` on the flattened
+    channels gives every gradient once the ones of tied parameters are summed
+    over the entries that share them: ddt[b,t,h] = sum_p ddelta[b,t,(h,p)],
+    dA[h] = sum_{p,n} dA[(h,p),n], dDskip[h] and ddt_bias[h] = sum_p.  dy
+    (B, L, H, P); dh_final (B, H, P, N) optional.  Returns a dict with dx
+    (B, L, H, P), ddt (B, L, H), dA, dD, ddt_bias (H), dB, dC (B, L, N) and
+    dh0 (B, H, P, N), float64."""
+    x, dt, A, Bm, Cm, dy = _f64(x), _f64(dt), _f64(A), _f64(Bm), _f64(Cm), _f64(dy)
+    B, L, H, P = x.shape
+    N = Bm.shape[2]
+    rep = lambda v: None if v is None else np.repeat(_f64(v), P, axis=-1)  # noqa: E731
+    flat = lambda v: None if v is None else _f64(v).reshape(B, H * P, N)  # noqa: E731
+    g = scan_bwd(x.reshape(B, L, H * P), rep(dt), np.repeat(A, P)[:, None] * np.ones((1, N)), Bm, Cm,
+                 dy.reshape(B, L, H * P), Dskip=rep(Dskip), z=None, dt_bias=rep(dt_bias), h0=flat(h0),
+                 dh_final=flat(dh_final), softplus=softplus)
+    return {
+        "dx": g["du"].reshape(B, L, H, P),
+        "ddt": g["ddelta"].reshape(B, L, H, P).sum(-1),
+        "dA": g["dA"].reshape(H, P, N).sum((1, 2)),
+        "dB": g["dB"],
+        "dC": g["dC"],
+        "dD": g["dD"].reshape(H, P).sum(-1),
+        "ddt_bias": g["ddt_bias"].reshape(H, P).sum(-1),
+        "dh0": g["dh0"].reshape(B, H, P, N),
+    }
