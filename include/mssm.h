@@ -338,6 +338,34 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* d
                          const float* h0, void* y, float* h_final,
                          void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Mamba-2 (state-space dual) backward: the adjoint of mssm_ssd_fwd (same
+ * reading: one decay A[h] and one step size per head, shared by the head's P
+ * channels and N states, and Bm, Cm shared by all heads).  Given dy (the
+ * gradient of y) and optionally dh_final (of h_final), writes
+ *   dx (B, L, H, P), ddt (B, L, H): gradient w.r.t. the raw step input dt
+ *     (before dt_bias and softplus), dB, dC (B, L, N)  -- in p->dtype;
+ *   dA (H), and optionally dD (H), ddt_bias (H), dh0 (B, H, P, N) -- float32.
+ * Gradients are overwritten, not accumulated.  Computed in 64-step chunks on
+ * the matrix cores: a pass storing the state entering every chunk, a reverse
+ * pass storing the adjoint state leaving every chunk, a chunk-parallel pass
+ * forming every gradient from them, and fixed-order reductions of the tied
+ * parameters' gradients (bitwise reproducible; no atomics).
+ * Required: p, x, dt, A, Bm, Cm, dy, dx, ddt, dA, dB, dC.  Optional (NULL):
+ * Dskip, dt_bias (-> 0), h0 (-> zeros), dh_final (-> zeros), dD, ddt_bias,
+ * dh0 (not written).  No output may alias an input or another output.
+ * Sizes, errors and alignment as mssm_ssd_fwd; the workspace (sized by
+ * mssm_ssd_bwd_workspace_bytes, never 0) holds the chunk states and adjoint
+ * states, (B * H * (2 * ceil(L / 64) + 1) * P * N) floats, plus small
+ * partials. */
+size_t mssm_ssd_bwd_workspace_bytes(const mssm_ssd_problem* p);
+
+mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                         const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                         const float* h0, const void* dy, const float* dh_final,
+                         void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
+                         float* ddt_bias, float* dh0,
+                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char* mssm_status_string(mssm_status s);
 

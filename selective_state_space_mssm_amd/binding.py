@@ -23,7 +23,8 @@ STATUS = {0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_SHAPE", -3: "MSSM_ERR
           -7: "MSSM_ERR_HIP"}
 EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd", "mssm_scan_fwd_noalloc",
            "mssm_conv_scan_fwd", "mssm_conv_bwd_workspace_bytes", "mssm_conv_bwd", "mssm_scan_bwd", "mssm_step",
-           "mssm_conv_step", "mssm_ssd_fwd_workspace_bytes", "mssm_ssd_fwd", "mssm_status_string", "mssm_build_info"]
+           "mssm_conv_step", "mssm_ssd_fwd_workspace_bytes", "mssm_ssd_fwd", "mssm_ssd_bwd_workspace_bytes",
+           "mssm_ssd_bwd", "mssm_status_string", "mssm_build_info"]
 MAX_DCONV = 4
 
 
@@ -78,6 +79,10 @@ def _open(path: str):
     lib.mssm_ssd_fwd_workspace_bytes.restype = sz
     lib.mssm_ssd_fwd.argtypes = [ctypes.POINTER(SsdProblem)] + [vp] * 10 + [vp, sz, vp]
     lib.mssm_ssd_fwd.restype = st
+    lib.mssm_ssd_bwd_workspace_bytes.argtypes = [ctypes.POINTER(SsdProblem)]
+    lib.mssm_ssd_bwd_workspace_bytes.restype = sz
+    lib.mssm_ssd_bwd.argtypes = [ctypes.POINTER(SsdProblem)] + [vp] * 18 + [vp, sz, vp]
+    lib.mssm_ssd_bwd.restype = st
     lib.mssm_status_string.argtypes = [st]
     lib.mssm_status_string.restype = ctypes.c_char_p
     lib.mssm_build_info.argtypes = []
@@ -441,3 +446,42 @@ def ssd_fwd(x, dt, A, Bm, Cm, Dskip=None, dt_bias=None, h0=None, delta_softplus=
     _check(lib.mssm_ssd_fwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
                             _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(ws), nbytes, _stream(x.device)))
     return y, h_final
+
+
+def ssd_bwd(x, dt, A, Bm, Cm, dy, Dskip=None, dt_bias=None, h0=None, dh_final=None, delta_softplus=True,
+            want_dD=True, want_ddt_bias=True, want_dh0=True, workspace=None):
+    """Mamba-2 (SSD) backward.  Inputs as ssd_fwd, with dy (B, L, H, P) in x's dtype and dh_final
+    (B, H, P, N) float32 optional.  Returns a dict with dx, ddt, dB, dC (x's dtype), dA and, unless
+    switched off, dD, ddt_bias, dh0 (float32)."""
+    B, L, H, P = x.shape
+    N = Bm.shape[2]
+    f, act = torch.float32, x.dtype
+    _req(x, "x", (B, L, H, P), act)
+    _req(dt, "dt", (B, L, H), act)
+    _req(A, "A", (H,), f)
+    _req(Bm, "Bm", (B, L, N), act)
+    _req(Cm, "Cm", (B, L, N), act)
+    _req(dy, "dy", (B, L, H, P), act)
+    _opt(Dskip, "Dskip", (H,), f)
+    _opt(dt_bias, "dt_bias", (H,), f)
+    _opt(h0, "h0", (B, H, P, N), f)
+    _opt(dh_final, "dh_final", (B, H, P, N), f)
+    dev = x.device
+    g = {
+        "dx": torch.empty((B, L, H, P), dtype=act, device=dev),
+        "ddt": torch.empty((B, L, H), dtype=act, device=dev),
+        "dA": torch.empty((H,), dtype=f, device=dev),
+        "dB": torch.empty((B, L, N), dtype=act, device=dev),
+        "dC": torch.empty((B, L, N), dtype=act, device=dev),
+        "dD": torch.empty((H,), dtype=f, device=dev) if want_dD else None,
+        "ddt_bias": torch.empty((H,), dtype=f, device=dev) if want_ddt_bias else None,
+        "dh0": torch.empty((B, H, P, N), dtype=f, device=dev) if want_dh0 else None,
+    }
+    prob = SsdProblem(B, L, H, P, N, _dtype_code(x), 1 if delta_softplus else 0)
+    nbytes = int(lib.mssm_ssd_bwd_workspace_bytes(ctypes.byref(prob)))
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.mssm_ssd_bwd(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
+                            _ptr(dt_bias), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(g["dx"]), _ptr(g["ddt"]),
+                            _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["ddt_bias"]),
+                            _ptr(g["dh0"]), _ptr(ws), nbytes, _stream(dev)))
+    return g

@@ -287,6 +287,62 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* d
     return from_hip(mssm::launch_ssd_fwd(a, static_cast<hipStream_t>(hip_stream)));
 }
 
+size_t mssm_ssd_bwd_workspace_bytes(const mssm_ssd_problem* p) {
+    if (check_ssd_problem(p) != MSSM_OK) return 0;
+    return mssm::plan_ssd_bwd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate, p->dtype == MSSM_BF16,
+                              device_cus())
+        .total;
+}
+
+mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                         const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                         const float* h0, const void* dy, const float* dh_final,
+                         void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
+                         float* ddt_bias, float* dh0,
+                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const mssm_status chk = check_ssd_problem(p);
+    if (chk != MSSM_OK) return chk;
+    if (!x || !dt || !A || !Bm || !Cm || !dy || !dx || !ddt || !dA || !dB || !dC) return MSSM_ERR_NULL;
+    const mssm_status al = check_align({x, dt, A, Bm, Cm, Dskip, dt_bias, h0, dy, dh_final, dx, ddt, dA, dB, dC, dD,
+                                        ddt_bias, dh0, workspace});
+    if (al != MSSM_OK) return al;
+    const bool bf16 = p->dtype == MSSM_BF16;
+    const mssm::SsdBwdPlan plan =
+        mssm::plan_ssd_bwd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate, bf16, device_cus());
+    if (!workspace || workspace_bytes < plan.total) return MSSM_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+
+    mssm::SsdBwdArgs a{};
+    a.B = p->batch; a.L = p->seqlen; a.H = p->nheads; a.P = p->headdim; a.N = p->dstate;
+    a.softplus = p->delta_softplus ? 1 : 0;
+    a.dtype = bf16 ? 1 : 0;
+    a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0;
+    a.dy = dy; a.dh_final = dh_final;
+    a.dx = dx; a.ddt = ddt; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.ddt_bias = ddt_bias; a.dh0 = dh0;
+    a.states = reinterpret_cast<float*>(ws + plan.states);
+    a.dstates = reinterpret_cast<float*>(ws + plan.dstates);
+    a.dots = reinterpret_cast<float*>(ws + plan.dots);
+    a.parts = reinterpret_cast<float*>(ws + plan.parts);
+    a.dbc = plan.groups > 1 ? reinterpret_cast<float*>(ws + plan.dbc) : nullptr;
+    a.groups = plan.groups;
+    a.heads_per_group = plan.heads_per_group;
+
+    mssm::SsdArgs& f = a.fwd;  // the states pass: the forward recurrence without outputs
+    f.B = a.B; f.L = a.L; f.H = a.H; f.P = a.P; f.N = a.N;
+    f.softplus = a.softplus; f.dtype = a.dtype;
+    f.x = x; f.dt = dt; f.A = A; f.Bm = Bm; f.Cm = Cm; f.Dskip = Dskip; f.dt_bias = dt_bias; f.h0 = h0;
+    f.nseg = 1; f.seg_len = a.L;
+    f.chunk_states = a.states;
+    if (plan.fwd.workers > 0) {
+        f.workers = static_cast<int32_t>(plan.fwd.workers);
+        f.flags = reinterpret_cast<uint32_t*>(ws + plan.fwd_ws);
+        f.carry = reinterpret_cast<float*>(ws + plan.fwd_ws +
+                                           ((static_cast<size_t>(plan.fwd.workers + 1) * sizeof(uint32_t) + 255) &
+                                            ~static_cast<size_t>(255)));
+    }
+    return from_hip(mssm::launch_ssd_bwd(a, static_cast<hipStream_t>(hip_stream)));
+}
+
 const char* mssm_status_string(mssm_status s) {
     switch (s) {
         case MSSM_OK: return "MSSM_OK: success";

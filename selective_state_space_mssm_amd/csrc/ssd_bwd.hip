@@ -1,0 +1,681 @@
+// ssd_bwd.hip -- backward of the Mamba-2 layer (the state-space dual, SSD) on
+// the gfx950 matrix cores.
+//
+// The reading is the forward's (ssd_fwd.hip): the selective scan with one
+// scalar decay A_h and one step size Delta per head, shared by the head's P
+// channels and N states, and Bm, Cm shared by all heads.  The backward is its
+// adjoint in the chunked dual form, per chunk of Q = 64 steps with chunk-local
+// cum_i = sum_{s <= i} Delta_s A_h, S_in the state entering the chunk, S_out
+// the one leaving it and dS the adjoint of S_out:
+//   G = C B^T,  Lmask_ij = exp(cum_i - cum_j) Delta_j (j <= i),
+//   U_jk = exp(cum_k - cum_j) (k >= j),  e_j = exp(cum_last - cum_j),
+//   dC   = diag(exp(cum)) dY S_in + ((dY X^T) o Lmask) B
+//   V    = (G^T o U) dY + diag(e) B dS^T                 (V_j = lambda_j B_j)
+//   dX   = diag(Delta) V + D dY
+//   dB   = diag(Delta) [((X dY^T) o U) C + diag(e) X dS]
+//   r_i  = x_i . V_i,  dcum_i = C_i . dC_i - Delta_i r_i (+ <dS, S_out> at the chunk's last row)
+//   dDelta_t = A_h sum_{i >= t} dcum_i + r_t,  dA_h += sum_i dcum_i sum_{s <= i} Delta_s
+//   dS_in = dY^T diag(exp(cum)) C + exp(cum_last) dS.
+// dB and dC sum over heads; dA, dDskip and ddt_bias over batch and time.
+//
+// Four passes:
+//   1. states (ssd_fwd.hip, launch_ssd_states): the forward recurrence alone,
+//      storing the state entering every chunk (and the final state);
+//   2. adjoint states (ssd_dstate_kernel): one workgroup per (batch, head)
+//      walks the chunks backwards carrying dS in its accumulators, storing the
+//      dS of every chunk and <dS, S_out>; dh0 is the last dS_in;
+//   3. chunk gradients (ssd_bwd_chunk_kernel): one workgroup per (batch,
+//      chunk, head group), independent of every other: Bm, Cm and G = C B^T
+//      are staged and formed once, then for each head of the group the
+//      products above, dB and dC summed over the group's heads in the
+//      accumulators;
+//   4. reductions (ssd_bwd_reduce_kernel): dA, dDskip, ddt_bias over (batch,
+//      chunk) and, with several head groups, dB and dC over the groups, in a
+//      fixed order (no atomics: bitwise reproducible).
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "ssd.h"
+#include "ssd_common.h"
+
+namespace mssm {
+namespace {
+using namespace ssdk;
+
+// Sum over the 64 lanes (every lane gets it).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// Row sums of an accumulator tile: the 16 items of a lane (rows acc_row(r, hl))
+// summed over the 32 lanes of its half.  Each butterfly step hands half of the
+// remaining rows to the partner lane, so 16 shuffles do all 16 rows; afterwards
+// lanes l and l ^ 1 (l = l32) hold the sum of item r = (l >> 1) & 15.  Returns
+// that sum; the caller writes it from the even lanes.
+__device__ __forceinline__ float tile_row_sums(f32x16 v, int l32) {
+    float a8[8], a4[4], a2[2];
+    const bool b4 = l32 & 16, b3 = l32 & 8, b2 = l32 & 4, b1 = l32 & 2;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float send = b4 ? v[q] : v[q + 8], keep = b4 ? v[q + 8] : v[q];
+        a8[q] = keep + __shfl_xor(send, 16);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float send = b3 ? a8[q] : a8[q + 4], keep = b3 ? a8[q + 4] : a8[q];
+        a4[q] = keep + __shfl_xor(send, 8);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const float send = b2 ? a4[q] : a4[q + 2], keep = b2 ? a4[q + 2] : a4[q];
+        a2[q] = keep + __shfl_xor(send, 4);
+    }
+    const float send = b1 ? a2[0] : a2[1], keep = b1 ? a2[1] : a2[0];
+    float a1 = keep + __shfl_xor(send, 2);
+    return a1 + __shfl_xor(a1, 1);
+}
+
+// Offset of accumulator item r of the (P, N) state tile set a wave of the
+// state passes keeps: rows sp * 32 + acc_row(r, hl), columns ((w & 1) * NT + k) * 32 + l32.
+template <int N>
+__device__ __forceinline__ int state_item(int wv, int k, int r, int hl, int l32) {
+    constexpr int NT = N / 64;
+    return ((wv >> 1) * 32 + acc_row(r, hl)) * N + ((wv & 1) * NT + k) * 32 + l32;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: adjoint states.  dS_in = exp(cum_last) dS + sum_i exp(cum_i) dy_i C_i^T,
+// chunks from the last to the first; the P x N adjoint lives in the
+// accumulators of the four waves as in the forward's state update.
+template <int N>
+struct alignas(16) DStateSmem {
+    float dy[kQ][kP + kPadRow];
+    float c[kQ][N + kPadRow];
+    float ecum[kQ];
+    float red[4];
+};
+
+template <class T, int N>
+struct DStateRegs {
+    static constexpr int kY = kQ * kP / 4 / kThreads;  // float4 of dY per thread
+    static constexpr int kC = kQ * N / 4 / kThreads;   // float4 of Cm per thread
+    float4 y[kY], c[kC];
+    float dt;
+};
+
+// Chunk [t0, t0 + 64)'s dY (this head), Cm and step sizes into registers; rows
+// at or past L lie outside the resources and read as zeros.
+template <class T, int N>
+__device__ __forceinline__ void load_dstate_chunk(const SsdBwdArgs& a, int64_t bi, int64_t h, int64_t t0, int tid,
+                                                  DStateRegs<T, N>& g) {
+    const int64_t H = a.H;
+    const int64_t nv = a.L - t0 < 0 ? 0 : imin64(kQ, a.L - t0);
+    const int64_t row0 = bi * a.L + t0;
+    const T* tag = nullptr;
+    const auto ry = make_rsrc(static_cast<const T*>(a.dy) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
+    const auto rc = make_rsrc(static_cast<const T*>(a.Cm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
+    const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
+#pragma unroll
+    for (int e = 0; e < DStateRegs<T, N>::kY; ++e) {
+        int i, p;
+        stage_pos(e * kThreads + tid, kP / 4, i, p);
+        g.y[e] = load4(tag, ry, (int)((i * H + h) * kP + 4 * p));
+    }
+#pragma unroll
+    for (int e = 0; e < DStateRegs<T, N>::kC; ++e) {
+        int i, n;
+        stage_pos(e * kThreads + tid, N / 4, i, n);
+        g.c[e] = load4(tag, rc, i * N + 4 * n);
+    }
+    g.dt = load1(tag, rd, (int)((tid & 63) * H + h));
+}
+
+template <class T, int N>
+__global__ __launch_bounds__(kThreads) void ssd_dstate_kernel(SsdBwdArgs a) {
+    constexpr int NT = N / 64;
+    __shared__ DStateSmem<N> s;
+    const int tid = threadIdx.x;
+    const int wv = wave_id();
+    const int lane = tid & 63;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int sp = wv >> 1;
+    const int64_t H = a.H, L = a.L, PN = kP * N;
+    const int64_t nch = (L + kQ - 1) / kQ;
+    const int64_t bh = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t bi = bh / H, h = bh % H;
+    const float Ah = a.A[h];
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+
+    f32x16 dS[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dS[k][r] = a.dh_final ? a.dh_final[bh * PN + state_item<N>(wv, k, r, hl, l32)] : 0.0f;
+    }
+
+    DStateRegs<T, N> g;
+    load_dstate_chunk<T, N>(a, bi, h, (nch - 1) * kQ, tid, g);
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int64_t t0 = c * kQ;
+        const int nv = (int)imin64(kQ, L - t0);
+        // ---- stage dY, Cm; exp(cum) ----
+#pragma unroll
+        for (int e = 0; e < DStateRegs<T, N>::kY; ++e) {
+            int i, p;
+            stage_pos(e * kThreads + tid, kP / 4, i, p);
+            p *= 4;
+            s.dy[i][p] = g.y[e].x; s.dy[i][p + 1] = g.y[e].y; s.dy[i][p + 2] = g.y[e].z; s.dy[i][p + 3] = g.y[e].w;
+        }
+#pragma unroll
+        for (int e = 0; e < DStateRegs<T, N>::kC; ++e) {
+            int i, n;
+            stage_pos(e * kThreads + tid, N / 4, i, n);
+            n *= 4;
+            s.c[i][n] = g.c[e].x; s.c[i][n + 1] = g.c[e].y; s.c[i][n + 2] = g.c[e].z; s.c[i][n + 3] = g.c[e].w;
+        }
+        if (wv == 0) {
+            const ChunkScan cs = chunk_scan(g.dt, nv, bias, Ah, a.softplus, lane);
+            s.ecum[lane] = fexp(cs.cum);
+        }
+        // ---- the adjoint of the state leaving this chunk, and <dS, S_out> ----
+        {
+            float* out = a.dstates + (bh * nch + c) * PN;
+            const float* so = a.states + (bh * (nch + 1) + c + 1) * PN;
+            float part = 0.0f;
+#pragma unroll
+            for (int k = 0; k < NT; ++k) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int o = state_item<N>(wv, k, r, hl, l32);
+                    out[o] = dS[k][r];
+                    part += dS[k][r] * so[o];
+                }
+            }
+            part = wave_sum(part);
+            if (lane == 0) s.red[wv] = part;
+        }
+        __syncthreads();
+        if (tid == 0) a.dots[bh * nch + c] = s.red[0] + s.red[1] + s.red[2] + s.red[3];
+        // the previous chunk's inputs travel during this chunk's products (none before the first)
+        if (c > 0) load_dstate_chunk<T, N>(a, bi, h, t0 - kQ, tid, g);
+
+        // ---- dS_in = exp(cum_last) dS + (exp(cum) o dY)^T C ----
+        const float decay = s.ecum[kQ - 1];
+        constexpr int SX = kP + kPadRow, SC = N + kPadRow;
+        const float* yf = &s.dy[0][0];
+        const float* cf = &s.c[0][0];
+        const int oy = opaque(hl * SX + sp * 32 + l32);
+        const int oc = opaque(hl * SC + (wv & 1) * NT * 32 + l32);
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+            dS[k] = mfma_chain_scaled<kQ / 2>(
+                dS[k] * decay,
+                [&](int j, float& av, float& a2, float& bv) {
+                    av = s.ecum[2 * j + hl];
+                    a2 = yf[oy + 2 * j * SX];
+                    bv = cf[oc + k * 32 + 2 * j * SC];
+                },
+                [](int) {});
+        }
+        __syncthreads();
+    }
+    if (a.dh0) {
+#pragma unroll
+        for (int k = 0; k < NT; ++k)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a.dh0[bh * PN + state_item<N>(wv, k, r, hl, l32)] = dS[k][r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3: chunk gradients.
+//
+// mm holds two Q x Q triangular operands in one array: M2 = G^T o U on and
+// above the diagonal (mm[j][k], k >= j) and M3^T = (dY X^T) o U^T strictly
+// below it (mm[k][j] = M3[j][k], k > j), M3's diagonal in d3.  Read as
+//   M2[j][k] = k >= j ? mm[j][k] : 0
+//   M3[j][k] = k > j ? mm[k][j] : k == j ? d3[j] : 0
+//   M1[i][k] = (dY X^T o Lmask)[i][k] = M3[k][i] Delta_k.
+template <int N>
+struct alignas(16) BwdSmem {
+    static constexpr int kSB = N + kPadCol, kSX = kP + kPadRow, kSM = kQ + kPadCol;
+    float b[kQ][kSB];
+    float c[kQ][kSB];
+    float x[kQ][kSX];
+    float dy[kQ][kSX];
+    float dst[N][kSX];   // dS^T: dst[n][p] = dS[p][n]
+    float mm[kQ][kSM];
+    float d3[kQ];
+    float cum[kQ];
+    float dlt[kQ];
+    float ecum[kQ];      // exp(cum_i)
+    float elast[kQ];     // exp(cum_last - cum_j)
+    float red_c[N / 32][kQ];  // per n-block row sums of C o dC
+    float red_r[2][kQ];       // per p-block row sums of X o V
+    float red_d[2][4];        // per wave sums of dY o X (double-buffered by head parity)
+};
+
+// Per-thread registers of one head's inputs, loaded a head ahead.
+template <int N>
+struct HeadRegs {
+    static constexpr int kX = kQ * kP / 4 / kThreads;  // float4 of X, of dY
+    static constexpr int kS = kP * N / kThreads;       // floats of dS
+    float4 x[kX], y[kX];
+    float ds[kS];
+    float dt;
+    float dot;
+};
+
+template <class T, int N>
+__device__ __forceinline__ void load_head(const SsdBwdArgs& a, int64_t bi, int64_t c, int64_t h, int nb, int tid,
+                                          int lane, HeadRegs<N>& g) {
+    const int64_t H = a.H, L = a.L, PN = kP * N;
+    const int64_t nch = (L + kQ - 1) / kQ;
+    const int64_t t0 = c * kQ;
+    const int64_t nv = imin64(kQ, L - t0);
+    const int64_t row0 = bi * L + t0;
+    const int64_t bh = bi * H + h;
+    const T* tag = nullptr;
+    const auto rx = make_rsrc(static_cast<const T*>(a.x) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
+    const auto ry = make_rsrc(static_cast<const T*>(a.dy) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
+#pragma unroll
+    for (int e = 0; e < HeadRegs<N>::kX; ++e) {
+        int i, p;
+        stage_pos(e * kThreads + tid, kP / 4, i, p);
+        const int off = (int)((i * H + h) * kP + 4 * p);
+        g.x[e] = load4(tag, rx, off);
+        g.y[e] = load4(tag, ry, off);
+    }
+    // the states through buffer resources: a lane offset plus per-load constants the compiler keeps in
+    // scalar offsets, not 64-bit addresses per load
+    const float* ftag = nullptr;
+    const auto rds = make_rsrc(a.dstates + (bh * nch + c) * PN, (uint32_t)(PN * sizeof(float)));
+#pragma unroll
+    for (int e = 0; e < HeadRegs<N>::kS; ++e) g.ds[e] = load1(ftag, rds, e * kThreads + tid);
+    const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
+    g.dt = load1(tag, rd, (int)((tid & 63) * H + h));
+    g.dot = a.dots[bh * nch + c];
+}
+
+// S_in[2 k + hl][nb * 32 + l32], k < 32: the B operand of dY S_in for n-block nb (loaded when the head
+// starts, so that it is not held across the previous head's products).
+template <int N>
+__device__ __forceinline__ void load_sin(const SsdBwdArgs& a, int64_t bh, int64_t c, int nb, int lane, float (&sin)[32]) {
+    const int64_t PN = kP * N, nch = (a.L + kQ - 1) / kQ;
+    const float* ftag = nullptr;
+    const auto rsi = make_rsrc(a.states + (bh * (nch + 1) + c) * PN, (uint32_t)(PN * sizeof(float)));
+    const int lo = (lane >> 5) * N + nb * 32 + (lane & 31);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) sin[k] = load1(ftag, rsi, lo + 2 * k * N);
+}
+
+template <class T, int N>
+__global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
+    constexpr int NB = N / 32;           // n-blocks
+    constexpr int NTC = NB / 2;          // dC (and dB) tiles per wave: N = 128: (0, w), (1, w); N = 64: (w / 2, w % 2)
+    constexpr int SB = BwdSmem<N>::kSB, SX = BwdSmem<N>::kSX, SM = BwdSmem<N>::kSM;
+    __shared__ BwdSmem<N> s;
+    const int tid = threadIdx.x;
+    const int wv = wave_id();
+    const int lane = tid & 63;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int64_t H = a.H, L = a.L;
+    const int64_t nch = (L + kQ - 1) / kQ;
+    const int64_t g_idx = blockIdx.x % a.groups, rest = blockIdx.x / a.groups;
+    const int64_t c = rest % nch, bi = rest / nch;
+    const int64_t t0 = c * kQ;
+    const int nv = (int)imin64(kQ, L - t0);
+    const int64_t h_begin = g_idx * a.heads_per_group, h_end = imin64(H, h_begin + a.heads_per_group);
+    const float* bf = &s.b[0][0];
+    const float* cf = &s.c[0][0];
+    const float* xf = &s.x[0][0];
+    const float* yf = &s.dy[0][0];
+    const float* sf = &s.dst[0][0];
+    const float* mf = &s.mm[0][0];
+
+    // this wave's tiles: dC and dB tiles (row block, n-block) for t < NTC; the V tile (jb, pb)
+    auto tile_rb = [&](int t) { return NB == 4 ? t : (wv >> 1); };
+    const int nb = NB == 4 ? wv : (wv & 1);
+    const int vjb = wv >> 1, vpb = wv & 1;
+
+    // ---- Bm, Cm rows of the chunk, once for all heads ----
+    {
+        const int64_t row0 = bi * L + t0;
+        const T* tag = nullptr;
+        const auto rb = make_rsrc(static_cast<const T*>(a.Bm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
+        const auto rc = make_rsrc(static_cast<const T*>(a.Cm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
+#pragma unroll
+        for (int e = 0; e < kQ * N / 4 / kThreads; ++e) {
+            int i, n;
+            stage_pos(e * kThreads + tid, N / 4, i, n);
+            const float4 vb = load4(tag, rb, i * N + 4 * n), vc = load4(tag, rc, i * N + 4 * n);
+            n *= 4;
+            s.b[i][n] = vb.x; s.b[i][n + 1] = vb.y; s.b[i][n + 2] = vb.z; s.b[i][n + 3] = vb.w;
+            s.c[i][n] = vc.x; s.c[i][n + 1] = vc.y; s.c[i][n + 2] = vc.z; s.c[i][n + 3] = vc.w;
+        }
+    }
+    HeadRegs<N> g;
+    if (h_begin < h_end) load_head<T, N>(a, bi, c, h_begin, nb, tid, lane, g);
+    __syncthreads();
+
+    // ---- G = C B^T, tiles (0, 0), (1, 0), (1, 1) on waves 0, 1, 2, kept for all heads ----
+    const int gti = wv == 0 ? 0 : 1, gtj = wv == 2 ? 1 : 0;
+    f32x16 Gt = {};
+    if (wv < 3) {
+        const int oc = opaque((gti * 32 + l32) * SB + hl), ob = opaque((gtj * 32 + l32) * SB + hl);
+        Gt = mfma_chain<N / 2>(Gt, [&](int k, float& av, float& bv) {
+            av = cf[oc + 2 * k];
+            bv = bf[ob + 2 * k];
+        });
+    }
+
+    f32x16 dCacc[NTC], dBacc[NTC];
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+        dCacc[t] = f32x16{};
+        dBacc[t] = f32x16{};
+    }
+
+    float sig = 1.0f, dlt_l = 0.0f, cumd = 0.0f;  // wave 3: this head's sigmoid factor, Delta, sum_{s<=t} Delta_s
+    float dot = 0.0f;
+    int par = 0;
+    for (int64_t h = h_begin; h < h_end; ++h, par ^= 1) {
+        const float Ah = a.A[h];
+        const float Dh = a.Dskip ? a.Dskip[h] : 0.0f;
+        // ---- (a) stage X, dY, dS^T; step quantities (wave 3) ----
+        float pd = 0.0f;
+#pragma unroll
+        for (int e = 0; e < HeadRegs<N>::kX; ++e) {
+            int i, p;
+            stage_pos(e * kThreads + tid, kP / 4, i, p);
+            p *= 4;
+            s.x[i][p] = g.x[e].x; s.x[i][p + 1] = g.x[e].y; s.x[i][p + 2] = g.x[e].z; s.x[i][p + 3] = g.x[e].w;
+            s.dy[i][p] = g.y[e].x; s.dy[i][p + 1] = g.y[e].y; s.dy[i][p + 2] = g.y[e].z; s.dy[i][p + 3] = g.y[e].w;
+            pd += g.x[e].x * g.y[e].x + g.x[e].y * g.y[e].y + g.x[e].z * g.y[e].z + g.x[e].w * g.y[e].w;
+        }
+#pragma unroll
+        for (int e = 0; e < HeadRegs<N>::kS; ++e) {
+            const int f = e * kThreads + tid;  // element (p, n) = (f / N, f % N) of dS
+            s.dst[f % N][f / N] = g.ds[e];
+        }
+        pd = wave_sum(pd);
+        if (lane == 0) s.red_d[par][wv] = pd;
+        if (wv == 3) {
+            const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+            const float v = g.dt + bias;
+            const ChunkScan cs = chunk_scan(g.dt, nv, bias, Ah, a.softplus, lane);
+            sig = a.softplus ? sigmoid(v) : 1.0f;
+            dlt_l = cs.d;
+            cumd = wave_prefix_sum(cs.d, lane);
+            dot = g.dot;
+            s.cum[lane] = cs.cum;
+            s.dlt[lane] = cs.d;
+            s.ecum[lane] = fexp(cs.cum);
+            const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs.cum), 63));
+            s.elast[lane] = fexp(last - cs.cum);
+        }
+        __syncthreads();
+
+        float sin[32];
+        load_sin<N>(a, bi * H + h, c, nb, lane, sin);
+
+        // ---- (b) dY X^T tiles and the masked operands (waves 0, 1, 2) ----
+        if (wv < 3) {
+            const int oy = opaque((gti * 32 + l32) * SX + hl), ox = opaque((gtj * 32 + l32) * SX + hl);
+            const f32x16 dyx = mfma_chain<kP / 2>(f32x16{}, [&](int k, float& av, float& bv) {
+                av = yf[oy + 2 * k];
+                bv = xf[ox + 2 * k];
+            });
+            const int j = gtj * 32 + l32;
+            const float cj = s.cum[j];
+            float ci[16];
+            acc_row_cum(s.cum, gti, hl, ci);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = gti * 32 + acc_row(r, hl);
+                if (i > j) {
+                    const float f = fexp(ci[r] - cj);
+                    s.mm[j][i] = Gt[r] * f;   // M2[j][i]
+                    s.mm[i][j] = dyx[r] * f;  // M3[j][i], stored transposed
+                } else if (i == j) {
+                    s.mm[j][j] = Gt[r];
+                    s.d3[j] = dyx[r];
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- (c) products ----
+        // the next head's inputs travel during this head's products
+        const bool more = h + 1 < h_end;
+        // dC tiles (rb, nb): diag(exp(cum)) dY S_in + M1 B
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) {
+            const int rb = tile_rb(t);
+            const int oy = opaque((rb * 32 + l32) * SX + hl);
+            f32x16 acc = mfma_chain<kP / 2>(f32x16{}, [&](int k, float& av, float& bv) {
+                av = yf[oy + 2 * k];
+                bv = sin[k];
+            });
+            float ci[16];
+            acc_row_cum(s.ecum, rb, hl, ci);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] *= ci[r];
+            // M1[i][k] B[k][n] over k <= i: k-blocks 0 .. rb, the last one the diagonal block
+            const int i = rb * 32 + l32;
+            const int om = opaque(i * SM + hl);
+            const int ob = opaque(hl * SB + nb * 32 + l32);
+            auto ld_m1 = [&](int kb) {
+                return [&, kb](int k, float& av, float& a2, float& bv) {
+                    const int kk = kb * 32 + 2 * k + hl;
+                    const float m = mf[om + kb * 32 + 2 * k];
+                    av = kb < rb ? m : (kk < i ? m : (kk == i ? s.d3[i] : 0.0f));
+                    a2 = s.dlt[kk];
+                    bv = bf[ob + (kb * 32 + 2 * k) * SB];
+                };
+            };
+            if (rb == 1) acc = mfma_chain_scaled<16>(acc, ld_m1(0), [](int) {});
+            acc = mfma_chain_scaled<16>(acc, ld_m1(rb), [](int) {});
+            dCacc[t] += acc;
+            // row sums of C o dC over this n-block
+            f32x16 cdc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) cdc[r] = acc[r] * s.c[rb * 32 + acc_row(r, hl)][nb * 32 + l32];
+            const float rs = tile_row_sums(cdc, l32);
+            if ((l32 & 1) == 0) s.red_c[nb][rb * 32 + acc_row((l32 >> 1) & 15, hl)] = rs;
+        }
+        if (more) load_head<T, N>(a, bi, c, h + 1, nb, tid, lane, g);
+
+        // dB tiles (rb, nb): diag(Delta) [diag(e) X dS + M3 C]
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) {
+            const int rb = tile_rb(t);
+            const int ox = opaque((rb * 32 + l32) * SX + hl);
+            const int os = opaque((nb * 32 + l32) * SX + hl);
+            f32x16 acc = mfma_chain<kP / 2>(f32x16{}, [&](int k, float& av, float& bv) {
+                av = xf[ox + 2 * k];
+                bv = sf[os + 2 * k];
+            });
+            float el[16], dl[16];
+            acc_row_cum(s.elast, rb, hl, el);
+            acc_row_cum(s.dlt, rb, hl, dl);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] *= el[r];
+            // M3[j][k] C[k][n] over k >= j: k-blocks rb .. 1, the first one the diagonal block
+            const int j = rb * 32 + l32;
+            const int om = opaque(hl * SM + j);
+            const int oc = opaque(hl * SB + nb * 32 + l32);
+            auto ld_m3 = [&](int kb) {
+                return [&, kb](int k, float& av, float& bv) {
+                    const int kk = kb * 32 + 2 * k + hl;
+                    const float m = mf[om + (kb * 32 + 2 * k) * SM];
+                    av = kb > rb ? m : (kk > j ? m : (kk == j ? s.d3[j] : 0.0f));
+                    bv = cf[oc + (kb * 32 + 2 * k) * SB];
+                };
+            };
+            acc = mfma_chain<16>(acc, ld_m3(rb));
+            if (rb == 0) acc = mfma_chain<16>(acc, ld_m3(1));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dBacc[t][r] += dl[r] * acc[r];
+        }
+
+        // V tile (vjb, vpb): diag(e) B dS^T + M2 dY; dX = diag(Delta) V + D dY; row sums of X o V
+        {
+            const int ob = opaque((vjb * 32 + l32) * SB + hl);
+            const int os = opaque(hl * SX + vpb * 32 + l32);
+            f32x16 acc = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
+                av = bf[ob + 2 * k];
+                bv = sf[os + 2 * k * SX];
+            });
+            float el[16], dl[16];
+            acc_row_cum(s.elast, vjb, hl, el);
+            acc_row_cum(s.dlt, vjb, hl, dl);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] *= el[r];
+            // M2[j][k] dY[k][p] over k >= j: k-blocks vjb .. 1, the first one the diagonal block
+            const int j = vjb * 32 + l32;
+            const int om = opaque(j * SM + hl);
+            const int oy = opaque(hl * SX + vpb * 32 + l32);
+            auto ld_m2 = [&](int kb) {
+                return [&, kb](int k, float& av, float& bv) {
+                    const int kk = kb * 32 + 2 * k + hl;
+                    const float m = mf[om + kb * 32 + 2 * k];
+                    av = kb > vjb ? m : (kk >= j ? m : 0.0f);
+                    bv = yf[oy + (kb * 32 + 2 * k) * SX];
+                };
+            };
+            acc = mfma_chain<16>(acc, ld_m2(vjb));
+            if (vjb == 0) acc = mfma_chain<16>(acc, ld_m2(1));
+            // dX, rows past the end dropped by the resource
+            const int p = vpb * 32 + l32;
+            const auto rx = make_rsrc(static_cast<T*>(a.dx) + (bi * L + t0) * H * kP,
+                                      (uint32_t)(nv * H * kP * sizeof(T)));
+            f32x16 xv;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int jr = vjb * 32 + acc_row(r, hl);
+                store1<T>(dl[r] * acc[r] + Dh * s.dy[jr][p], rx, (int)((jr * H + h) * kP + p));
+                xv[r] = s.x[jr][p] * acc[r];
+            }
+            const float rs = tile_row_sums(xv, l32);
+            if ((l32 & 1) == 0) s.red_r[vpb][vjb * 32 + acc_row((l32 >> 1) & 15, hl)] = rs;
+        }
+        __syncthreads();
+
+        // ---- (d) per-step scalars (wave 3): dcum, dDelta, ddt; this head's dA, dDskip, ddt_bias parts ----
+        if (wv == 3) {
+            float cdc = 0.0f;
+#pragma unroll
+            for (int q = 0; q < NB; ++q) cdc += s.red_c[q][lane];
+            const float r = s.red_r[0][lane] + s.red_r[1][lane];
+            const float dcum = cdc - dlt_l * r + (lane == kQ - 1 ? dot : 0.0f);
+            const float incl = wave_prefix_sum(dcum, lane);
+            const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+            const float dDelta = Ah * (total - incl + dcum) + r;
+            const float ddt = dDelta * sig;
+            const auto rt = make_rsrc(static_cast<T*>(a.ddt) + (bi * L + t0) * H, (uint32_t)(nv * H * sizeof(T)));
+            store1<T>(ddt, rt, (int)(lane * H + h));
+            const float pa = wave_sum(dcum * cumd);
+            const float pb = wave_sum(lane < nv ? ddt : 0.0f);
+            if (lane == 0) {
+                float* part = a.parts + ((bi * nch + c) * H + h) * 3;
+                part[0] = pa;
+                part[1] = s.red_d[par][0] + s.red_d[par][1] + s.red_d[par][2] + s.red_d[par][3];
+                part[2] = pb;
+            }
+        }
+        // no barrier: the next head's staging writes x, dy, dst (read above only before the last barrier), and
+        // red_d of the other parity; wave 3 rewrites the step quantities after its own reads
+    }
+
+    // ---- dB, dC of the chunk summed over this group's heads ----
+    const int64_t row0 = bi * L + t0;
+    if (a.groups == 1) {
+        const auto rb_ = make_rsrc(static_cast<T*>(a.dB) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
+        const auto rc_ = make_rsrc(static_cast<T*>(a.dC) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) {
+            const int rb = tile_rb(t);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int e = (rb * 32 + acc_row(r, hl)) * N + nb * 32 + l32;
+                store1<T>(dBacc[t][r], rb_, e);
+                store1<T>(dCacc[t][r], rc_, e);
+            }
+        }
+    } else {
+        float* db = a.dbc + (g_idx * a.B * L + row0) * N;
+        float* dc = a.dbc + ((a.groups + g_idx) * a.B * L + row0) * N;
+        const auto rb_ = make_rsrc(db, (uint32_t)(nv * N * sizeof(float)));
+        const auto rc_ = make_rsrc(dc, (uint32_t)(nv * N * sizeof(float)));
+#pragma unroll
+        for (int t = 0; t < NTC; ++t) {
+            const int rb = tile_rb(t);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int e = (rb * 32 + acc_row(r, hl)) * N + nb * 32 + l32;
+                store1<float>(dBacc[t][r], rb_, e);
+                store1<float>(dCacc[t][r], rc_, e);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 4: reductions in a fixed order.  Threads [0, H): dA, dDskip, ddt_bias of
+// head h over (batch, chunk); with head groups, threads [H, H + B L N): dB and
+// dC of one element over the groups.
+template <class T>
+__global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(SsdBwdArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t H = a.H;
+    const int64_t nch = (a.L + kQ - 1) / kQ;
+    if (i < H) {
+        float sa = 0.0f, sd = 0.0f, sb = 0.0f;
+        for (int64_t bc = 0; bc < a.B * nch; ++bc) {
+            const float* p = a.parts + (bc * H + i) * 3;
+            sa += p[0];
+            sd += p[1];
+            sb += p[2];
+        }
+        a.dA[i] = sa;
+        if (a.dD) a.dD[i] = sd;
+        if (a.ddt_bias) a.ddt_bias[i] = sb;
+        return;
+    }
+    const int64_t e = i - H, BLN = a.B * a.L * a.N;
+    if (a.groups > 1 && e < BLN) {
+        float sb = 0.0f, sc = 0.0f;
+        for (int64_t g = 0; g < a.groups; ++g) {
+            sb += a.dbc[g * BLN + e];
+            sc += a.dbc[(a.groups + g) * BLN + e];
+        }
+        store_act(static_cast<T*>(a.dB), e, sb);
+        store_act(static_cast<T*>(a.dC), e, sc);
+    }
+}
+
+template <class T, int N>
+hipError_t launch_bwd_typed(const SsdBwdArgs& a, hipStream_t st) {
+    hipError_t e = launch_ssd_states(a.fwd, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ssd_dstate_kernel<T, N>), dim3((unsigned)(a.B * a.H)), dim3(kThreads), 0, st, a);
+    const int64_t nch = (a.L + kQ - 1) / kQ;
+    hipLaunchKernelGGL((ssd_bwd_chunk_kernel<T, N>), dim3((unsigned)(a.B * nch * a.groups)), dim3(kThreads), 0, st,
+                       a);
+    const int64_t n = a.H + (a.groups > 1 ? a.B * a.L * a.N : 0);
+    hipLaunchKernelGGL((ssd_bwd_reduce_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ssd_bwd(const SsdBwdArgs& a, hipStream_t st) {
+    if (a.dtype == 1) return a.N == 64 ? launch_bwd_typed<uint16_t, 64>(a, st) : launch_bwd_typed<uint16_t, 128>(a, st);
+    return a.N == 64 ? launch_bwd_typed<float, 64>(a, st) : launch_bwd_typed<float, 128>(a, st);
+}
+
+}  // namespace mssm

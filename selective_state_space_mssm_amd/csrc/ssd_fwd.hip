@@ -28,62 +28,11 @@
 #include "balanced_plan.h"
 #include "device_common.h"
 #include "ssd.h"
+#include "ssd_common.h"
 
 namespace mssm {
 namespace {
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int kQ = kSsdChunk;
-// spins of a bounded wait for a handed-over state (each with a short sleep)
-constexpr uint32_t kSsdMaxWaitSpins = 1u << 27;
-constexpr int kP = kSsdHeadDim;
-constexpr int kThreads = 256;
-
-__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
-// Tile row of accumulator item r for a lane in half hl.
-__device__ __forceinline__ int acc_row(int r, int hl) { return (r >> 2) * 8 + hl * 4 + (r & 3); }
-
-__device__ __forceinline__ float fexp(float x) { return fast_exp2(x * kLog2e); }
-
-// Activation access through a buffer resource, by element offset: T = float,
-// or uint16_t holding bfloat16 bits (widened exactly to float32).
-__device__ __forceinline__ float4 load4(const float*, __amdgpu_buffer_rsrc_t r, int e) {
-    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, e * 4, 0, 0));
-}
-__device__ __forceinline__ float4 load4(const uint16_t*, __amdgpu_buffer_rsrc_t r, int e) {
-    const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, e * 2, 0, 0);
-    return make_float4(bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1]));
-}
-__device__ __forceinline__ float load1(const float*, __amdgpu_buffer_rsrc_t r, int e) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, e * 4, 0, 0));
-}
-__device__ __forceinline__ float load1(const uint16_t*, __amdgpu_buffer_rsrc_t r, int e) {
-    return bf16_lo(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, e * 2, 0, 0)));
-}
-template <class T>
-__device__ __forceinline__ void store1(float v, __amdgpu_buffer_rsrc_t r, int e) {
-    buffer_store_act(v, r, static_cast<uint32_t>(e) * sizeof(T), T{});
-}
-
-// An integer the compiler must treat as unknown at this point (an empty asm
-// statement, no instruction).  Recomputing a lane's LDS base offsets through
-// it once per chunk keeps them out of loop-invariant hoisting: each step's
-// address stays base + constant, with the constant folded into the ds_read
-// offset field, instead of one precomputed address register per step.
-__device__ __forceinline__ int opaque(int v) {
-    asm volatile("" : "+v"(v));
-    return v;
-}
-
-// Row padding (floats) of the LDS operands: kPadCol for arrays read down a
-// column (32 rows at one k, the A-operand pattern), kPadRow for arrays read
-// along rows by both lane halves (two rows, 32 consecutive columns each).
-constexpr int kPadCol = 1;
-constexpr int kPadRow = 1;
+using namespace ssdk;
 
 // One chunk's operands.  16-byte aligned: cum is read four floats at a time.
 template <int N>
@@ -100,78 +49,6 @@ struct alignas(16) SsdSmem {
     float dlt[kQ];         // Delta (0 past the sequence end)
     float w[kQ];           // exp(cum_last - cum_j) Delta_j
 };
-
-// acc += sum over STEPS k-steps of A_s B_s, the operands of step s read by
-// ld(s, a, b).  The reads run DIST steps ahead of the MFMAs, so the LDS
-// latency hides behind the matrix core (one wave per SIMD has no other wave
-// to cover it).  DIST times the reads per step stays within the 15 LDS
-// operations the wave's lgkm counter can track.
-template <int STEPS, int DIST = 6, class F, class S>
-__device__ __forceinline__ f32x16 mfma_chain(f32x16 acc, F&& ld, S&& side) {
-    float av[STEPS], bv[STEPS];
-#pragma unroll
-    for (int s = 0; s < DIST && s < STEPS; ++s) ld(s, av[s], bv[s]);
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        if (s + DIST < STEPS) ld(s + DIST, av[s + DIST], bv[s + DIST]);
-        // keep the reads issued ahead: the scheduler would otherwise sink each
-        // one next to its MFMA and wait out its latency there
-        __builtin_amdgcn_sched_barrier(0);
-        acc = mfma32(av[s], bv[s], acc);
-        // other work of step s (side(s)) issues behind the product
-        side(s);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    return acc;
-}
-
-template <int STEPS, int DIST = 6, class F>
-__device__ __forceinline__ f32x16 mfma_chain(f32x16 acc, F&& ld) {
-    return mfma_chain<STEPS, DIST>(acc, ld, [](int) {});
-}
-
-// As mfma_chain, with the A operand of step s the product of two values
-// ld(s, a, a2, b) reads: the product is formed when the step issues, so its
-// reads stay DIST steps ahead too.
-template <int STEPS, int DIST = 4, class F, class S>
-__device__ __forceinline__ f32x16 mfma_chain_scaled(f32x16 acc, F&& ld, S&& side) {
-    float av[STEPS], a2[STEPS], bv[STEPS];
-#pragma unroll
-    for (int s = 0; s < DIST && s < STEPS; ++s) ld(s, av[s], a2[s], bv[s]);
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        if (s + DIST < STEPS) ld(s + DIST, av[s + DIST], a2[s + DIST], bv[s + DIST]);
-        __builtin_amdgcn_sched_barrier(0);
-        acc = mfma32(av[s] * a2[s], bv[s], acc);
-        side(s);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    return acc;
-}
-
-// The (batch, head) a workgroup takes.  Workgroups are dealt to the eight
-// XCDs round robin (workgroup i to XCD i % 8), each XCD with its own L2; this
-// order gives XCD x a contiguous run of (batch, head) pairs, so the heads of a
-// batch, which all read the same Bm and Cm rows, share one L2 instead of each
-// XCD fetching those rows again.  A bijection of [0, n) for any n.
-__device__ __forceinline__ int64_t xcd_order(int64_t i, int64_t n) {
-    constexpr int64_t kXcds = 8;
-    const int64_t per = n / kXcds, rem = n % kXcds;
-    const int64_t x = i % kXcds, slot = i / kXcds;
-    return x * per + (x < rem ? x : rem) + slot;
-}
-
-// Where float4 number f of a staged row-major array (cpr float4 per row, an
-// odd row stride in LDS) goes: each 32 lanes take 4 rows x 8 float4, lane l at
-// row l % 4 and float4 column l / 4.  A staging write of component j then puts
-// lane l at bank (row + 4 * column + j) % 32 = (l + const) % 32, 32 distinct
-// banks, where 32 lanes along one row would meet 8 banks four times each.  In
-// global memory a 32-lane group still reads 4 runs of 128 contiguous bytes.
-__device__ __forceinline__ void stage_pos(int f, int cpr, int& row, int& c4) {
-    const int u = f >> 5, l = f & 31, upr = cpr / 8;
-    row = (u / upr) * 4 + (l & 3);
-    c4 = (u % upr) * 8 + (l >> 2);
-}
 
 // One chunk's global inputs, held in registers from the previous chunk's
 // compute until they are staged into LDS.
@@ -234,53 +111,10 @@ struct ChunkLoader {
     }
 };
 
-// Inclusive prefix sum over the 64 lanes: Hillis-Steele shifts inside each
-// row of 16 lanes (DPP row_shr, lanes before the shift add 0), then the
-// totals of the earlier rows, read from lanes 15, 31 and 47.
-__device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, true));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, true));
-    const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15));
-    const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
-    const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47));
-    const int row = lane >> 4;
-    return v + (row >= 1 ? t0 : 0.0f) + (row >= 2 ? t1 : 0.0f) + (row >= 3 ? t2 : 0.0f);
-}
-
-// One chunk's step quantities, lane t = step t of the chunk: Delta_t (0 for
-// steps past the segment end, nv valid steps), the chunk-local cumulative
-// log-decay cum_t = sum_{s <= t} Delta_s A_h, and the state weight
-// w_t = exp(cum_last - cum_t) Delta_t.
-struct ChunkScan {
-    float d, cum, w;
-};
-__device__ __forceinline__ ChunkScan chunk_scan(float dtv, int nv, float bias, float Ah, int softplus_on, int lane) {
-    float d = 0.0f;
-    if (lane < nv) {
-        const float v = dtv + bias;
-        d = softplus_on ? softplus(v) : v;
-    }
-    const float c = wave_prefix_sum(d * Ah, lane);
-    const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-    return {d, c, fexp(last - c) * d};
-}
-
-// cum of the 16 accumulator rows a lane of half hl holds in row block ti
-// (rows ti * 32 + g * 8 + hl * 4 + q for item r = 4 g + q): four 16-byte reads.
-__device__ __forceinline__ void acc_row_cum(const float* cum, int ti, int hl, float (&ci)[16]) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const float4 v = *reinterpret_cast<const float4*>(cum + ti * 32 + g * 8 + hl * 4);
-        ci[4 * g] = v.x;
-        ci[4 * g + 1] = v.y;
-        ci[4 * g + 2] = v.z;
-        ci[4 * g + 3] = v.w;
-    }
-}
-
-template <class T, int N>
+// STATES: the backward's first pass -- only the state recurrence, no outputs:
+// the state entering every chunk c goes to chunk_states[(b, h)][c] and the
+// final state to chunk_states[(b, h)][nch] (time segments are not used then).
+template <class T, int N, bool STATES>
 __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     constexpr int NT = N / 64;  // state tiles per wave: the P x N state is 2 x (N / 32) tiles over 4 waves
     __shared__ SsdSmem<N> s;
@@ -335,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
 
         const int64_t state_base = bh * kP * N;
         f32x16 S[NT];
-    #pragma unroll
+#pragma unroll
         for (int k = 0; k < NT; ++k) S[k] = f32x16{};
         if (from == kFromPublished) {
             // the previous worker scanned this job up to t_begin first of all its segments and published
@@ -354,15 +188,15 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             }
             __syncthreads();
             float* src = a.carry + (worker - 1) * kP * N;
-    #pragma unroll
+#pragma unroll
             for (int k = 0; k < NT; ++k)
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r)
                     S[k][r] = __hip_atomic_load(src + state_off(k, r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else if (a.h0 && seg == 0) {  // later time segments start from zero; the carry pass supplies their state
-    #pragma unroll
+#pragma unroll
             for (int k = 0; k < NT; ++k)
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) S[k][r] = a.h0[state_base + state_off(k, r)];
         }
 
@@ -379,14 +213,14 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             const int nv = (int)imin64(kQ, t_end - t0);
 
             // ---- stage: the chunk's operands and S^T into LDS; cum, Delta, w ----
-    #pragma unroll
+#pragma unroll
             for (int e = 0; e < ChunkRegs<N>::kX; ++e) {
                 int i, p;
                 stage_pos(e * kThreads + tid, kP / 4, i, p);
                 p *= 4;
                 s.x[i][p] = g.x[e].x; s.x[i][p + 1] = g.x[e].y; s.x[i][p + 2] = g.x[e].z; s.x[i][p + 3] = g.x[e].w;
             }
-    #pragma unroll
+#pragma unroll
             for (int e = 0; e < ChunkRegs<N>::kB; ++e) {
                 int i, n;
                 stage_pos(e * kThreads + tid, N / 4, i, n);
@@ -394,11 +228,18 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                 s.b[i][n] = g.b[e].x; s.b[i][n + 1] = g.b[e].y; s.b[i][n + 2] = g.b[e].z; s.b[i][n + 3] = g.b[e].w;
                 s.c[i][n] = g.c[e].x; s.c[i][n + 1] = g.c[e].y; s.c[i][n + 2] = g.c[e].z; s.c[i][n + 3] = g.c[e].w;
             }
-    #pragma unroll
+#pragma unroll
             for (int k = 0; k < NT; ++k) {
                 const int n = ((wv & 1) * NT + k) * 32 + l32;
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) s.st[n][sp * 32 + acc_row(r, hl)] = S[k][r];
+            }
+            if constexpr (STATES) {
+                float* cst = a.chunk_states + (bh * (nch + 1) + t0 / kQ) * kP * N;
+#pragma unroll
+                for (int k = 0; k < NT; ++k)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) cst[state_off(k, r)] = S[k][r];
             }
             if (wv == 1) {
                 s.cum[lane] = cs.cum;
@@ -427,7 +268,9 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             const int ob_s = opaque(hl * SB + (wv & 1) * NT * 32 + l32);   // B[j + hl][n]
 
             // ---- M = (C B^T) o Lmask, tile (ti, tj); the tile above the diagonal is zero ----
-            {
+            if constexpr (STATES) {
+                next.all(g);
+            } else {
                 f32x16 gm = {};
                 if (ti >= tj) {
                     // the next chunk's loads go out one every other product, while the matrix core runs:
@@ -451,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                 acc_row_cum(s.cum, ti, hl, ci);
                 // above the diagonal: exponent -inf and a selected 0 (a non-finite future Bm row must not
                 // reach an earlier output), both as selects rather than a branch around the exponential
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int i = ti * 32 + acc_row(r, hl);
                     const bool keep = j <= i;
@@ -462,15 +305,15 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             __syncthreads();
 
             // ---- Y tile (ti, tj): exp(cum_i) (C S^T) + M X + D X ----
-            f32x16 y;
-            {
+            f32x16 y = {};
+            if constexpr (!STATES) {
                 y = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
                     av = cf[oc + 2 * k];
                     bv = stf[ost + 2 * k * SX];
                 });
                 float ci[16];
                 acc_row_cum(s.cum, ti, hl, ci);
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) y[r] *= fexp(ci[r]);
                 auto ld_mx = [&](int k, float& av, float& bv) {
                     av = mf[om + 2 * k];
@@ -482,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                 else
                     y = mfma_chain<32>(y, ld_mx);
                 const int p = tj * 32 + l32;
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) y[r] += Dh * s.x[ti * 32 + acc_row(r, hl)][p];
             }
             // rows past the sequence end fall outside the resource and are dropped; a bf16 output of a
@@ -504,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             // ---- S' = exp(cum_last) S + (w o X)^T B ----
             {
                 const float decay = fexp(s.cum[kQ - 1]);
-    #pragma unroll
+#pragma unroll
                 for (int k = 0; k < NT; ++k) {
                     const int obs = ob_s + k * 32;
                     // the Y tile goes out one item every other product of the first update
@@ -516,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                             bv = bf[obs + 2 * j * SB];
                         },
                         [&](int j) {
-                            if (k == 0 && j % 2 == 0) store_y(j / 2);
+                            if (!STATES && k == 0 && j % 2 == 0) store_y(j / 2);
                         });
                 }
             }
@@ -530,10 +373,17 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                      : a.h_final    ? a.h_final + state_base
                                     : nullptr;
         if (out) {
-    #pragma unroll
+#pragma unroll
             for (int k = 0; k < NT; ++k)
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) out[state_off(k, r)] = S[k][r];
+        }
+        if (STATES && to == kFinal) {
+            float* cst = a.chunk_states + (bh * (nch + 1) + nch) * kP * N;
+#pragma unroll
+            for (int k = 0; k < NT; ++k)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) cst[state_off(k, r)] = S[k][r];
         }
         if (a.nseg > 1 && tid == 0) a.ws[a.B * H * a.nseg * kP * N + bh * a.nseg + seg] = lam;
         if (to == kPublish) {
@@ -673,16 +523,17 @@ __global__ __launch_bounds__(256) void ssd_zero_flags_kernel(uint32_t* flags, in
     if (i < n) flags[i] = 0u;
 }
 
-template <class T, int N>
+template <class T, int N, bool STATES = false>
 hipError_t launch_typed(const SsdArgs& a, hipStream_t st) {
     const dim3 block(kThreads);
     if (a.workers > 0) {  // a fill kernel rather than a memset: the launch may be captured in a graph
         hipLaunchKernelGGL(ssd_zero_flags_kernel, dim3((unsigned)((a.workers + 1 + 255) / 256)), dim3(256), 0, st,
                            a.flags, a.workers + 1);
-        hipLaunchKernelGGL((ssd_fwd_kernel<T, N>), dim3((unsigned)a.workers), block, 0, st, a);
+        hipLaunchKernelGGL((ssd_fwd_kernel<T, N, STATES>), dim3((unsigned)a.workers), block, 0, st, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((ssd_fwd_kernel<T, N>), dim3((unsigned)(a.B * a.H * a.nseg)), block, 0, st, a);
+    hipLaunchKernelGGL((ssd_fwd_kernel<T, N, STATES>), dim3((unsigned)(a.B * a.H * a.nseg)), block, 0, st, a);
+    if constexpr (STATES) return hipGetLastError();
     if (a.nseg > 1) {
         const int64_t n = a.B * a.H * a.P * a.N;
         hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
@@ -696,6 +547,12 @@ hipError_t launch_typed(const SsdArgs& a, hipStream_t st) {
 hipError_t launch_ssd_fwd(const SsdArgs& a, hipStream_t st) {
     if (a.dtype == 1) return a.N == 64 ? launch_typed<uint16_t, 64>(a, st) : launch_typed<uint16_t, 128>(a, st);
     return a.N == 64 ? launch_typed<float, 64>(a, st) : launch_typed<float, 128>(a, st);
+}
+
+hipError_t launch_ssd_states(const SsdArgs& a, hipStream_t st) {
+    if (a.dtype == 1)
+        return a.N == 64 ? launch_typed<uint16_t, 64, true>(a, st) : launch_typed<uint16_t, 128, true>(a, st);
+    return a.N == 64 ? launch_typed<float, 64, true>(a, st) : launch_typed<float, 128, true>(a, st);
 }
 
 }  // namespace mssm
