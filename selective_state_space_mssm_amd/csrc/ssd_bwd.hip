@@ -29,7 +29,7 @@
 //      are staged and formed once, then for each head of the group the
 //      products above, dB and dC summed over the group's heads in the
 //      accumulators;
-//   4. reductions (ssd_bwd_reduce_kernel): dA, dDskip, ddt_bias over (batch,
+//   4. reductions (ssd_bwd_reduce_*_kernel): dA, dDskip, ddt_bias over (batch,
 //      chunk) and, with several head groups, dB and dC over the groups, in a
 //      fixed order (no atomics: bitwise reproducible).
 #include <hip/hip_runtime.h>
@@ -42,39 +42,74 @@ namespace mssm {
 namespace {
 using namespace ssdk;
 
+// Cross-lane partners without the LDS crossbar (ds_bpermute would queue behind
+// the matrix operands' LDS reads): DPP within rows of 16 lanes and gfx950's
+// v_permlane16_swap / v_permlane32_swap across them.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]: lane l ^ 1
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]: lane l ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane l ^ 7 (reversal within 8 lanes)
+constexpr int kDppMirror = 0x140;      // lane l ^ 15 (reversal within 16 lanes)
+// value of lane l ^ 16: the swap moves rows 0 <-> 1 and 2 <-> 3 of 16 lanes
+__device__ __forceinline__ float xor16(float v, int lane) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+}
+// value of lane l ^ 32
+__device__ __forceinline__ float xor32(float v, int lane) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+}
+
 // Sum over the 64 lanes (every lane gets it).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+__device__ __forceinline__ float wave_sum(float v, int lane) {
+    v += dpp_mov<kDppXor1>(v);
+    v += dpp_mov<kDppXor2>(v);
+    v += dpp_mov<kDppHalfMirror>(v);
+    v += dpp_mov<kDppMirror>(v);
+    v += xor16(v, lane);
+    return v + xor32(v, lane);
 }
 
 // Row sums of an accumulator tile: the 16 items of a lane (rows acc_row(r, hl))
-// summed over the 32 lanes of its half.  Each butterfly step hands half of the
-// remaining rows to the partner lane, so 16 shuffles do all 16 rows; afterwards
+// summed over the 32 lanes of its half.  Each butterfly step pairs lanes that
+// differ in one bit b (partners l ^ 16, l ^ 15, l ^ 7, l ^ 2, l ^ 1, each
+// flipping b and leaving the bits of earlier steps alone) and hands half of the
+// remaining rows to the partner, so 16 exchanges do all 16 rows; afterwards
 // lanes l and l ^ 1 (l = l32) hold the sum of item r = (l >> 1) & 15.  Returns
 // that sum; the caller writes it from the even lanes.
-__device__ __forceinline__ float tile_row_sums(f32x16 v, int l32) {
+__device__ __forceinline__ float tile_row_sums(f32x16 v, int lane) {
+    // the items as opaque scalars: selecting between two elements of the vector would otherwise be folded
+    // into an element read at a per-lane index, which lowers to a 16-way compare-and-select chain
+    float w[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        w[r] = v[r];
+        asm volatile("" : "+v"(w[r]));
+    }
     float a8[8], a4[4], a2[2];
-    const bool b4 = l32 & 16, b3 = l32 & 8, b2 = l32 & 4, b1 = l32 & 2;
+    const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        const float send = b4 ? v[q] : v[q + 8], keep = b4 ? v[q + 8] : v[q];
-        a8[q] = keep + __shfl_xor(send, 16);
+        const float send = b4 ? w[q] : w[q + 8], keep = b4 ? w[q + 8] : w[q];
+        a8[q] = keep + xor16(send, lane);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const float send = b3 ? a8[q] : a8[q + 4], keep = b3 ? a8[q + 4] : a8[q];
-        a4[q] = keep + __shfl_xor(send, 8);
+        a4[q] = keep + dpp_mov<kDppMirror>(send);
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const float send = b2 ? a4[q] : a4[q + 2], keep = b2 ? a4[q + 2] : a4[q];
-        a2[q] = keep + __shfl_xor(send, 4);
+        a2[q] = keep + dpp_mov<kDppHalfMirror>(send);
     }
     const float send = b1 ? a2[0] : a2[1], keep = b1 ? a2[1] : a2[0];
-    float a1 = keep + __shfl_xor(send, 2);
-    return a1 + __shfl_xor(a1, 1);
+    const float a1 = keep + dpp_mov<kDppXor2>(send);
+    return a1 + dpp_mov<kDppXor1>(a1);
 }
 
 // Offset of accumulator item r of the (P, N) state tile set a wave of the
@@ -180,25 +215,26 @@ __global__ __launch_bounds__(kThreads) void ssd_dstate_kernel(SsdBwdArgs a) {
             const ChunkScan cs = chunk_scan(g.dt, nv, bias, Ah, a.softplus, lane);
             s.ecum[lane] = fexp(cs.cum);
         }
-        // ---- the adjoint of the state leaving this chunk, and <dS, S_out> ----
+        // ---- the adjoint of the state leaving this chunk, stored; S_out loaded for <dS, S_out>, formed
+        // after the update so that neither the loads nor the stores hold the wave here ----
+        float so[NT][16], dso[NT][16];
         {
-            float* out = a.dstates + (bh * nch + c) * PN;
-            const float* so = a.states + (bh * (nch + 1) + c + 1) * PN;
-            float part = 0.0f;
+            const float* ftag = nullptr;
+            const auto rso = make_rsrc(a.states + (bh * (nch + 1) + c + 1) * PN, (uint32_t)(PN * sizeof(float)));
+            const auto rout = make_rsrc(a.dstates + (bh * nch + c) * PN, (uint32_t)(PN * sizeof(float)));
+            const int lo = opaque(state_item<N>(wv, 0, 0, hl, l32));
 #pragma unroll
             for (int k = 0; k < NT; ++k) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int o = state_item<N>(wv, k, r, hl, l32);
-                    out[o] = dS[k][r];
-                    part += dS[k][r] * so[o];
+                    const int o = lo + state_item<N>(wv, k, r, 0, 0) - state_item<N>(wv, 0, 0, 0, 0);
+                    so[k][r] = load1(ftag, rso, o);
+                    dso[k][r] = dS[k][r];
+                    store1<float>(dS[k][r], rout, o);
                 }
             }
-            part = wave_sum(part);
-            if (lane == 0) s.red[wv] = part;
         }
         __syncthreads();
-        if (tid == 0) a.dots[bh * nch + c] = s.red[0] + s.red[1] + s.red[2] + s.red[3];
         // the previous chunk's inputs travel during this chunk's products (none before the first)
         if (c > 0) load_dstate_chunk<T, N>(a, bi, h, t0 - kQ, tid, g);
 
@@ -220,7 +256,15 @@ __global__ __launch_bounds__(kThreads) void ssd_dstate_kernel(SsdBwdArgs a) {
                 },
                 [](int) {});
         }
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NT; ++k)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part += dso[k][r] * so[k][r];
+        part = wave_sum(part, lane);
+        if (lane == 0) s.red[wv] = part;
         __syncthreads();
+        if (tid == 0) a.dots[bh * nch + c] = s.red[0] + s.red[1] + s.red[2] + s.red[3];
     }
     if (a.dh0) {
 #pragma unroll
@@ -256,6 +300,7 @@ struct alignas(16) BwdSmem {
     float red_c[N / 32][kQ];  // per n-block row sums of C o dC
     float red_r[2][kQ];       // per p-block row sums of X o V
     float red_d[2][4];        // per wave sums of dY o X (double-buffered by head parity)
+    float junk[kThreads];     // target of the masked operands' writes that belong to no operand
 };
 
 // Per-thread registers of one head's inputs, loaded a head ahead.
@@ -269,36 +314,58 @@ struct HeadRegs {
     float dot;
 };
 
+// One head's loads, numbered so that a caller can spread their issue over
+// matrix products (piece k < kPieces, a compile-time constant after
+// unrolling): the X and dY float4s, the dS floats, the step sizes, the dot.
 template <class T, int N>
-__device__ __forceinline__ void load_head(const SsdBwdArgs& a, int64_t bi, int64_t c, int64_t h, int nb, int tid,
-                                          int lane, HeadRegs<N>& g) {
-    const int64_t H = a.H, L = a.L, PN = kP * N;
-    const int64_t nch = (L + kQ - 1) / kQ;
-    const int64_t t0 = c * kQ;
-    const int64_t nv = imin64(kQ, L - t0);
-    const int64_t row0 = bi * L + t0;
-    const int64_t bh = bi * H + h;
-    const T* tag = nullptr;
-    const auto rx = make_rsrc(static_cast<const T*>(a.x) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
-    const auto ry = make_rsrc(static_cast<const T*>(a.dy) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
-#pragma unroll
-    for (int e = 0; e < HeadRegs<N>::kX; ++e) {
-        int i, p;
-        stage_pos(e * kThreads + tid, kP / 4, i, p);
-        const int off = (int)((i * H + h) * kP + 4 * p);
-        g.x[e] = load4(tag, rx, off);
-        g.y[e] = load4(tag, ry, off);
+struct HeadLoader {
+    static constexpr int kX = HeadRegs<N>::kX, kS = HeadRegs<N>::kS;
+    static constexpr int kPieces = kX + kS + 2;
+    __amdgpu_buffer_rsrc_t rx, ry, rds, rd;
+    int64_t H, h;
+    const float* dot;
+    int tid;
+
+    __device__ __forceinline__ HeadLoader(const SsdBwdArgs& a, int64_t bi, int64_t c, int64_t h_, int tid_)
+        : H(a.H), h(h_), tid(tid_) {
+        const int64_t L = a.L, PN = kP * N;
+        const int64_t nch = (L + kQ - 1) / kQ;
+        const int64_t t0 = c * kQ;
+        const int64_t nv = imin64(kQ, L - t0);
+        const int64_t row0 = bi * L + t0;
+        const int64_t bh = bi * H + h;
+        rx = make_rsrc(static_cast<const T*>(a.x) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
+        ry = make_rsrc(static_cast<const T*>(a.dy) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
+        // dS through a buffer resource: a lane offset plus per-load constants kept in scalar offsets, not
+        // 64-bit addresses per load
+        rds = make_rsrc(a.dstates + (bh * nch + c) * PN, (uint32_t)(PN * sizeof(float)));
+        rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
+        dot = a.dots + bh * nch + c;
     }
-    // the states through buffer resources: a lane offset plus per-load constants the compiler keeps in
-    // scalar offsets, not 64-bit addresses per load
-    const float* ftag = nullptr;
-    const auto rds = make_rsrc(a.dstates + (bh * nch + c) * PN, (uint32_t)(PN * sizeof(float)));
+
+    __device__ __forceinline__ void piece(int k, HeadRegs<N>& g) const {
+        const T* tag = nullptr;
+        if (k < kX) {
+            int i, p;
+            stage_pos(k * kThreads + tid, kP / 4, i, p);
+            const int off = (int)((i * H + h) * kP + 4 * p);
+            g.x[k] = load4(tag, rx, off);
+            g.y[k] = load4(tag, ry, off);
+        } else if (k < kX + kS) {
+            const float* ftag = nullptr;
+            g.ds[k - kX] = load1(ftag, rds, (k - kX) * kThreads + tid);
+        } else if (k == kX + kS) {
+            g.dt = load1(tag, rd, (int)((tid & 63) * H + h));
+        } else {
+            g.dot = *dot;
+        }
+    }
+
+    __device__ __forceinline__ void all(HeadRegs<N>& g) const {
 #pragma unroll
-    for (int e = 0; e < HeadRegs<N>::kS; ++e) g.ds[e] = load1(ftag, rds, e * kThreads + tid);
-    const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
-    g.dt = load1(tag, rd, (int)((tid & 63) * H + h));
-    g.dot = a.dots[bh * nch + c];
-}
+        for (int k = 0; k < kPieces; ++k) piece(k, g);
+    }
+};
 
 // S_in[2 k + hl][nb * 32 + l32], k < 32: the B operand of dY S_in for n-block nb (loaded when the head
 // starts, so that it is not held across the previous head's products).
@@ -358,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
         }
     }
     HeadRegs<N> g;
-    if (h_begin < h_end) load_head<T, N>(a, bi, c, h_begin, nb, tid, lane, g);
+    if (h_begin < h_end) HeadLoader<T, N>(a, bi, c, h_begin, tid).all(g);
     __syncthreads();
 
     // ---- G = C B^T, tiles (0, 0), (1, 0), (1, 1) on waves 0, 1, 2, kept for all heads ----
@@ -401,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             const int f = e * kThreads + tid;  // element (p, n) = (f / N, f % N) of dS
             s.dst[f % N][f / N] = g.ds[e];
         }
-        pd = wave_sum(pd);
+        pd = wave_sum(pd, lane);
         if (lane == 0) s.red_d[par][wv] = pd;
         if (wv == 3) {
             const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
@@ -433,17 +500,17 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             const float cj = s.cum[j];
             float ci[16];
             acc_row_cum(s.cum, gti, hl, ci);
+            // M2[j][i] = G[i][j] f for i >= j, M3[j][i] = dYX[i][j] f for i > j (stored transposed) and on
+            // the diagonal (d3), f = exp(cum_i - cum_j) (1 on the diagonal); the items with i < j belong to
+            // neither and go to a junk word, so that every lane writes twice per item without a branch
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = gti * 32 + acc_row(r, hl);
-                if (i > j) {
-                    const float f = fexp(ci[r] - cj);
-                    s.mm[j][i] = Gt[r] * f;   // M2[j][i]
-                    s.mm[i][j] = dyx[r] * f;  // M3[j][i], stored transposed
-                } else if (i == j) {
-                    s.mm[j][j] = Gt[r];
-                    s.d3[j] = dyx[r];
-                }
+                const float f = fexp(ci[r] - cj);
+                float* p2 = i >= j ? &s.mm[j][i] : &s.junk[tid];
+                float* p3 = i > j ? &s.mm[i][j] : i == j ? &s.d3[j] : &s.junk[tid];
+                *p2 = Gt[r] * f;
+                *p3 = dyx[r] * f;
             }
         }
         __syncthreads();
@@ -484,10 +551,13 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             f32x16 cdc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) cdc[r] = acc[r] * s.c[rb * 32 + acc_row(r, hl)][nb * 32 + l32];
-            const float rs = tile_row_sums(cdc, l32);
+            const float rs = tile_row_sums(cdc, lane);
             if ((l32 & 1) == 0) s.red_c[nb][rb * 32 + acc_row((l32 >> 1) & 15, hl)] = rs;
         }
-        if (more) load_head<T, N>(a, bi, c, h + 1, nb, tid, lane, g);
+        // the next head's loads go out one per product of the X dS chains (all together, they would hold
+        // the wave); past the group's last head, a loader of the last head again (never used)
+        const HeadLoader<T, N> next(a, bi, c, more ? h + 1 : h, tid);
+        static_assert(HeadLoader<T, N>::kPieces <= NTC * kP / 2, "the X dS chains have a slot for every load");
 
         // dB tiles (rb, nb): diag(Delta) [diag(e) X dS + M3 C]
 #pragma unroll
@@ -495,10 +565,16 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             const int rb = tile_rb(t);
             const int ox = opaque((rb * 32 + l32) * SX + hl);
             const int os = opaque((nb * 32 + l32) * SX + hl);
-            f32x16 acc = mfma_chain<kP / 2>(f32x16{}, [&](int k, float& av, float& bv) {
-                av = xf[ox + 2 * k];
-                bv = sf[os + 2 * k];
-            });
+            f32x16 acc = mfma_chain<kP / 2>(
+                f32x16{},
+                [&](int k, float& av, float& bv) {
+                    av = xf[ox + 2 * k];
+                    bv = sf[os + 2 * k];
+                },
+                [&](int k) {
+                    const int piece = t * (kP / 2) + k;
+                    if (piece < HeadLoader<T, N>::kPieces) next.piece(piece, g);
+                });
             float el[16], dl[16];
             acc_row_cum(s.elast, rb, hl, el);
             acc_row_cum(s.dlt, rb, hl, dl);
@@ -560,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
                 store1<T>(dl[r] * acc[r] + Dh * s.dy[jr][p], rx, (int)((jr * H + h) * kP + p));
                 xv[r] = s.x[jr][p] * acc[r];
             }
-            const float rs = tile_row_sums(xv, l32);
+            const float rs = tile_row_sums(xv, lane);
             if ((l32 & 1) == 0) s.red_r[vpb][vjb * 32 + acc_row((l32 >> 1) & 15, hl)] = rs;
         }
         __syncthreads();
@@ -578,8 +654,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             const float ddt = dDelta * sig;
             const auto rt = make_rsrc(static_cast<T*>(a.ddt) + (bi * L + t0) * H, (uint32_t)(nv * H * sizeof(T)));
             store1<T>(ddt, rt, (int)(lane * H + h));
-            const float pa = wave_sum(dcum * cumd);
-            const float pb = wave_sum(lane < nv ? ddt : 0.0f);
+            const float pa = wave_sum(dcum * cumd, lane);
+            const float pb = wave_sum(lane < nv ? ddt : 0.0f, lane);
             if (lane == 0) {
                 float* part = a.parts + ((bi * nch + c) * H + h) * 3;
                 part[0] = pa;
@@ -625,37 +701,52 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 4: reductions in a fixed order.  Threads [0, H): dA, dDskip, ddt_bias of
-// head h over (batch, chunk); with head groups, threads [H, H + B L N): dB and
-// dC of one element over the groups.
+// Pass 4: reductions in a fixed order (bitwise reproducible).  One workgroup per
+// head h: dA, dDskip, ddt_bias over the (batch, chunk) partials, each thread a
+// strided share, then a tree over the workgroup.
+__global__ __launch_bounds__(256) void ssd_bwd_reduce_heads_kernel(SsdBwdArgs a) {
+    __shared__ float red[3][256];
+    const int64_t h = blockIdx.x, H = a.H;
+    const int64_t nbc = a.B * ((a.L + kQ - 1) / kQ);
+    const int tid = threadIdx.x;
+    float sa = 0.0f, sd = 0.0f, sb = 0.0f;
+    for (int64_t bc = tid; bc < nbc; bc += 256) {
+        const float* p = a.parts + (bc * H + h) * 3;
+        sa += p[0];
+        sd += p[1];
+        sb += p[2];
+    }
+    red[0][tid] = sa;
+    red[1][tid] = sd;
+    red[2][tid] = sb;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) {
+            red[0][tid] += red[0][tid + w];
+            red[1][tid] += red[1][tid + w];
+            red[2][tid] += red[2][tid + w];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        a.dA[h] = red[0][0];
+        if (a.dD) a.dD[h] = red[1][0];
+        if (a.ddt_bias) a.ddt_bias[h] = red[2][0];
+    }
+}
+
+// With several head groups: dB and dC of one element summed over the groups.
 template <class T>
-__global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(SsdBwdArgs a) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t H = a.H;
-    const int64_t nch = (a.L + kQ - 1) / kQ;
-    if (i < H) {
-        float sa = 0.0f, sd = 0.0f, sb = 0.0f;
-        for (int64_t bc = 0; bc < a.B * nch; ++bc) {
-            const float* p = a.parts + (bc * H + i) * 3;
-            sa += p[0];
-            sd += p[1];
-            sb += p[2];
-        }
-        a.dA[i] = sa;
-        if (a.dD) a.dD[i] = sd;
-        if (a.ddt_bias) a.ddt_bias[i] = sb;
-        return;
+__global__ __launch_bounds__(256) void ssd_bwd_reduce_groups_kernel(SsdBwdArgs a) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x, BLN = a.B * a.L * a.N;
+    if (e >= BLN) return;
+    float sb = 0.0f, sc = 0.0f;
+    for (int64_t g = 0; g < a.groups; ++g) {
+        sb += a.dbc[g * BLN + e];
+        sc += a.dbc[(a.groups + g) * BLN + e];
     }
-    const int64_t e = i - H, BLN = a.B * a.L * a.N;
-    if (a.groups > 1 && e < BLN) {
-        float sb = 0.0f, sc = 0.0f;
-        for (int64_t g = 0; g < a.groups; ++g) {
-            sb += a.dbc[g * BLN + e];
-            sc += a.dbc[(a.groups + g) * BLN + e];
-        }
-        store_act(static_cast<T*>(a.dB), e, sb);
-        store_act(static_cast<T*>(a.dC), e, sc);
-    }
+    store_act(static_cast<T*>(a.dB), e, sb);
+    store_act(static_cast<T*>(a.dC), e, sc);
 }
 
 template <class T, int N>
@@ -666,8 +757,11 @@ hipError_t launch_bwd_typed(const SsdBwdArgs& a, hipStream_t st) {
     const int64_t nch = (a.L + kQ - 1) / kQ;
     hipLaunchKernelGGL((ssd_bwd_chunk_kernel<T, N>), dim3((unsigned)(a.B * nch * a.groups)), dim3(kThreads), 0, st,
                        a);
-    const int64_t n = a.H + (a.groups > 1 ? a.B * a.L * a.N : 0);
-    hipLaunchKernelGGL((ssd_bwd_reduce_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(ssd_bwd_reduce_heads_kernel, dim3((unsigned)a.H), dim3(256), 0, st, a);
+    if (a.groups > 1) {
+        const int64_t n = a.B * a.L * a.N;
+        hipLaunchKernelGGL((ssd_bwd_reduce_groups_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 

@@ -67,10 +67,10 @@ struct ChunkRegs {
 // touches no memory).  The loads are numbered (piece k < kPieces: the X float4s,
 // then Bm's, Cm's, then the step sizes) so that a caller can spread their
 // issue over other work; k must be a compile-time constant after unrolling.
-template <class T, int N>
+template <class T, int N, bool LOAD_C = true>
 struct ChunkLoader {
     static constexpr int kX = ChunkRegs<N>::kX, kB = ChunkRegs<N>::kB;
-    static constexpr int kPieces = kX + 2 * kB + 1;
+    static constexpr int kPieces = kX + (LOAD_C ? 2 : 1) * kB + 1;
     __amdgpu_buffer_rsrc_t rx, rb, rc, rd;
     int64_t H, h;
     int tid;
@@ -92,7 +92,7 @@ struct ChunkLoader {
             int i, p;
             stage_pos(k * kThreads + tid, kP / 4, i, p);
             g.x[k] = load4(tag, rx, (int)((i * H + h) * kP + 4 * p));
-        } else if (k < kX + 2 * kB) {
+        } else if (k < kPieces - 1) {
             const int e = (k - kX) % kB;
             int i, n;
             stage_pos(e * kThreads + tid, N / 4, i, n);
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
         }
 
         ChunkRegs<N> g;
-        ChunkLoader<T, N>(a, bi, h, t_begin, t_end, tid).all(g);
+        ChunkLoader<T, N, !STATES>(a, bi, h, t_begin, t_end, tid).all(g);
         float lam = 0.0f;  // the segment's total log-decay, sum of Delta A_h
         // wave 1, the one with the least matrix work (its M tile lies above the
         // diagonal), forms each chunk's step quantities one chunk ahead, off the
@@ -226,15 +226,18 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                 stage_pos(e * kThreads + tid, N / 4, i, n);
                 n *= 4;
                 s.b[i][n] = g.b[e].x; s.b[i][n + 1] = g.b[e].y; s.b[i][n + 2] = g.b[e].z; s.b[i][n + 3] = g.b[e].w;
-                s.c[i][n] = g.c[e].x; s.c[i][n + 1] = g.c[e].y; s.c[i][n + 2] = g.c[e].z; s.c[i][n + 3] = g.c[e].w;
+                if constexpr (!STATES) {
+                    s.c[i][n] = g.c[e].x; s.c[i][n + 1] = g.c[e].y; s.c[i][n + 2] = g.c[e].z; s.c[i][n + 3] = g.c[e].w;
+                }
             }
+            if constexpr (!STATES) {  // S^T is the B operand of C S^T
 #pragma unroll
-            for (int k = 0; k < NT; ++k) {
-                const int n = ((wv & 1) * NT + k) * 32 + l32;
+                for (int k = 0; k < NT; ++k) {
+                    const int n = ((wv & 1) * NT + k) * 32 + l32;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s.st[n][sp * 32 + acc_row(r, hl)] = S[k][r];
-            }
-            if constexpr (STATES) {
+                    for (int r = 0; r < 16; ++r) s.st[n][sp * 32 + acc_row(r, hl)] = S[k][r];
+                }
+            } else {
                 float* cst = a.chunk_states + (bh * (nch + 1) + t0 / kQ) * kP * N;
 #pragma unroll
                 for (int k = 0; k < NT; ++k)
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             __syncthreads();
 
             // the next chunk's inputs travel while this chunk computes (past the end: no access)
-            const ChunkLoader<T, N> next(a, bi, h, t0 + kQ, t_end, tid);
+            const ChunkLoader<T, N, !STATES> next(a, bi, h, t0 + kQ, t_end, tid);
             lam += s.cum[kQ - 1];
 
             // per-lane LDS base offsets (floats) of the MFMA operands; step k adds a constant
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                     s.m[i][j] = keep ? v : 0.0f;
                 }
             }
-            __syncthreads();
+            if constexpr (!STATES) __syncthreads();  // M is read by other waves below
 
             // ---- Y tile (ti, tj): exp(cum_i) (C S^T) + M X + D X ----
             f32x16 y = {};
