@@ -37,6 +37,7 @@ B = 256 (the short-sequence path) and the Mamba-2 (SSD) layers.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -321,18 +322,27 @@ def time_conv_step(mssm, torch, w, batch, reps=100):
     return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
 
 
-def time_ssd(mssm, torch, B, L, H, N, reps=20):
-    """Mamba-2 (SSD) forward, head dim 64, float32: median us per call (HIP
-    events), and the dense flops of its chunked dual form at 64-step chunks
-    (C B^T, C S^T, M X, and the state update, as full 64 x 64 products)."""
+def time_ssd(mssm, torch, B, L, H, N, reps=20, backward=False):
+    """Mamba-2 (SSD) forward (or backward), head dim 64, float32: median us per
+    call (HIP events), and the dense flops of the forward's chunked dual form at
+    64-step chunks (C B^T, C S^T, M X, and the state update, as full 64 x 64
+    products)."""
     inp = workloads.ssd_inputs(B, L, H, 64, N, seed=11)
     t = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
     del inp
     y = torch.empty_like(t["x"])
     hf = torch.empty((B, H, 64, N), dtype=torch.float32, device="cuda")
+    if backward:
+        t["dy"] = torch.randn_like(t["x"])
+        prob = mssm.binding.SsdProblem(B, L, H, 64, N, 0, 1)
+        ws = torch.empty(int(mssm.lib.mssm_ssd_bwd_workspace_bytes(ctypes.byref(prob))), dtype=torch.uint8,
+                         device="cuda")
 
     def run():
-        mssm.ssd_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["dt_bias"], y=y, h_final=hf)
+        if backward:
+            mssm.ssd_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["dy"], t["Dskip"], t["dt_bias"], workspace=ws)
+        else:
+            mssm.ssd_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["dt_bias"], y=y, h_final=hf)
 
     for _ in range(3):
         run()
@@ -561,7 +571,10 @@ def main():
         # batch-1 prefill of a 24-head layer (Mamba-2 130M shape): time segments scanned in parallel
         ssd_us, _ = time_ssd(mssm, torch, 1, 2048, 24, 128)
         out["extra"]["ssd_fwd_H24_N128_B1_L2048_us"] = round(ssd_us, 1)
-        log("extra: SSD forwards timed")
+        # the SSD backward (all eight gradients) at both shapes
+        out["extra"]["ssd_bwd_H80_N128_B8_L2048_us"] = round(time_ssd(mssm, torch, 8, 2048, 80, 128, 5, True)[0], 1)
+        out["extra"]["ssd_bwd_H24_N128_B1_L2048_us"] = round(time_ssd(mssm, torch, 1, 2048, 24, 128, 10, True)[0], 1)
+        log("extra: SSD forwards and backwards timed")
     if not args.no_cpu_baseline:
         log("cpu baseline: the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(w)
