@@ -9,9 +9,12 @@ float32 arithmetic), inputs resident in HBM.  Prints one JSON line:
   expansion is never moved) per wall time of a step;
 * roofline: the forward kernel's average launch duration from HIP events
   recorded around every timed launch on the launch stream, against the VALU
-  issue-rate bound of the chip: the scan does 4 VALU instructions and one
-  half-rate v_exp_f32 per (b, t, d, n) and moves only O(B L D) bytes, so at
-  these shapes the VALU, not HBM, bounds it.  Also the median and minimum
+  bound of the chip (its published fp32 vector rate, 157.3 TFLOP/s: 32 FMA
+  lanes per SIMD per clock, which non-packed code reaches with two or more
+  waves issuing on a SIMD): the scan does 4 VALU instructions and one
+  v_exp_f32 per (b, t, d, n), the transcendental priced at half the FMA rate,
+  and moves only O(B L D) bytes, so at these shapes the VALU, not HBM,
+  bounds it.  Also the median and minimum
   launch, a cold launch (after overwriting the 256 MB last-level cache with a
   512 MB scratch write, untimed) and the bandwidth of a plain 1 GiB device
   copy measured in the same run;
@@ -57,8 +60,9 @@ HBM_PEAK_GBS = 8000.0                     # MI355X HBM3E, published
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "scan_fwd_2p8b_hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_mssm_amd", "csrc", f)
                   for f in ("scan_fwd.hip", "scan_fwd_kernels.h", "balanced_plan.h", "device_common.h", "launch.h")]
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # lane-instructions/s: CUs x SIMDs x lanes x clock
-SLOTS_PER_ELEM_STATE = 6                  # 4 VALU + 1 v_exp_f32 at half rate (2 issue slots)
+# FMA-lane slots per second: CUs x SIMDs x 32 lanes per clock x clock = 78.6 T (157.3 TFLOP/s)
+VALU_PEAK_TOPS = 256 * 4 * 32 * 2.4e9 / 1e12
+SLOTS_PER_ELEM_STATE = 6                  # 4 VALU + 1 v_exp_f32 priced at half the FMA rate (2 slots)
 
 
 def log(*a):
@@ -519,12 +523,12 @@ def main():
             "bound": "alu",
             "achieved": round(achieved, 3),
             "peak": round(VALU_PEAK_TOPS, 3),
-            "unit": "T lane-instr/s",
+            "unit": "T FMA-lane slots/s",
             "frac": round(achieved / VALU_PEAK_TOPS, 4),
             "traffic": measured_traffic() if w.name == "2.8b" else None,
             "kernel": "scan_fwd_kernel",
             "kernel_us": round(kern_s * 1e6, 2),
-            "work_per_launch": f"{SLOTS_PER_ELEM_STATE} VALU issue slots x {w.elem_states} (b,t,d,n)",
+            "work_per_launch": f"{SLOTS_PER_ELEM_STATE} VALU slots x {w.elem_states} (b,t,d,n)",
             "kernel_us_median": round(float(np.median(launch_ms)) * 1e3, 2),
             "kernel_us_min": round(float(np.min(launch_ms)) * 1e3, 2),
             "kernel_us_cold": round(float(np.median(cold_ms)) * 1e3, 2),
@@ -533,7 +537,7 @@ def main():
             "copy_GBs": round(copy_gbs, 1),
             "frac_of_copy": round(nbytes / kern_s / 1e9 / copy_gbs, 4),
             "hbm_frac": round(nbytes / kern_s / 1e9 / HBM_PEAK_GBS, 4),
-            "note": "frac is against the VALU issue bound (the binding one); hbm_frac against 8 TB/s",
+            "note": "frac is against the fp32 VALU bound, 157.3 TFLOP/s (the binding one); hbm_frac against 8 TB/s",
         },
         # cold: each launch after a 512 MB scratch write has evicted the inputs from the last-level cache
         "cold": {"kernel_us": round(cold_s * 1e6, 2), "GBs": round(nbytes / cold_s / 1e9, 1),
