@@ -321,25 +321,10 @@ mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* d
     a.dx = dx; a.ddt = ddt; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.ddt_bias = ddt_bias; a.dh0 = dh0;
     a.states = reinterpret_cast<float*>(ws + plan.states);
     a.dstates = reinterpret_cast<float*>(ws + plan.dstates);
-    a.dots = reinterpret_cast<float*>(ws + plan.dots);
     a.parts = reinterpret_cast<float*>(ws + plan.parts);
     a.dbc = plan.groups > 1 ? reinterpret_cast<float*>(ws + plan.dbc) : nullptr;
     a.groups = plan.groups;
     a.heads_per_group = plan.heads_per_group;
-
-    mssm::SsdArgs& f = a.fwd;  // the states pass: the forward recurrence without outputs
-    f.B = a.B; f.L = a.L; f.H = a.H; f.P = a.P; f.N = a.N;
-    f.softplus = a.softplus; f.dtype = a.dtype;
-    f.x = x; f.dt = dt; f.A = A; f.Bm = Bm; f.Cm = Cm; f.Dskip = Dskip; f.dt_bias = dt_bias; f.h0 = h0;
-    f.nseg = 1; f.seg_len = a.L;
-    f.chunk_states = a.states;
-    if (plan.fwd.workers > 0) {
-        f.workers = static_cast<int32_t>(plan.fwd.workers);
-        f.flags = reinterpret_cast<uint32_t*>(ws + plan.fwd_ws);
-        f.carry = reinterpret_cast<float*>(ws + plan.fwd_ws +
-                                           ((static_cast<size_t>(plan.fwd.workers + 1) * sizeof(uint32_t) + 255) &
-                                            ~static_cast<size_t>(255)));
-    }
     return from_hip(mssm::launch_ssd_bwd(a, static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -33,9 +33,6 @@ struct SsdArgs {
     int32_t workers;
     uint32_t* flags;       // (workers + 1): 1 once worker w has published; word `workers`: 1 if a wait gave up
     float* carry;          // (workers, P, N): the state worker w hands to worker w + 1
-    // backward's first pass (launch_ssd_states): (B, H, nch + 1, P, N) states entering each 64-step chunk, then
-    // the final state
-    float* chunk_states;
 };
 
 constexpr int kSsdHeadDim = 64;   // P the kernel is built for
@@ -114,30 +111,23 @@ struct SsdBwdArgs {
     // workspace
     float* states;          // (B, H, nch + 1, P, N): state entering each 64-step chunk, then the final state
     float* dstates;         // (B, H, nch, P, N): adjoint of the state leaving each chunk
-    float* dots;            // (B, H, nch): <adjoint, state> at each chunk's end
     float* parts;           // (B, nch, H, 3): per chunk and head, the dA, dDskip, ddt_bias contributions
     float* dbc;             // groups > 1: (2, groups, B, L, N) float32 dB, dC per head group; else null
     int64_t groups;         // head groups per (batch, chunk)
     int64_t heads_per_group;
-    SsdArgs fwd;            // the states pass (launch_ssd_states)
 };
 
-// Workspace of the backward: the forward states pass's scheduling scratch
-// (fwd_ws), then states, adjoint states, dots, partials and the head-group
-// partials of dB, dC (each 256-byte aligned).
+// Workspace of the backward: states, adjoint states, partials and the
+// head-group partials of dB, dC (each 256-byte aligned).
 struct SsdBwdPlan {
     int64_t groups, heads_per_group;
-    size_t fwd_ws, states, dstates, dots, parts, dbc, total;  // byte offsets (total: size)
-    SsdPlan fwd;
+    size_t states, dstates, parts, dbc, total;  // byte offsets (total: size)
 };
 
 inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, bool bf16, int64_t ncu) {
     auto al = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
     SsdBwdPlan p{};
     const int64_t nch = (L + kSsdChunk - 1) / kSsdChunk;
-    // the states pass: the forward's schedule without time segments (they would start later segments from zero)
-    p.fwd = plan_ssd(B, L, H, P, N, bf16, ncu);
-    if (p.fwd.nseg > 1) p.fwd = SsdPlan{1, L, 0, 0};
     // one workgroup per (batch, chunk, head group): groups so that there are about 2 workgroups per CU
     const int64_t want = ncu > 0 ? 2 * ncu : 512;
     p.groups = (B * nch >= want) ? 1 : (want + B * nch - 1) / (B * nch);
@@ -145,10 +135,8 @@ inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64
     p.heads_per_group = (H + p.groups - 1) / p.groups;
     p.groups = (H + p.heads_per_group - 1) / p.heads_per_group;
     size_t off = 0;
-    p.fwd_ws = off;  off += al(p.fwd.ws_bytes);
     p.states = off;  off += al(static_cast<size_t>(B * H * (nch + 1) * P * N) * sizeof(float));
     p.dstates = off; off += al(static_cast<size_t>(B * H * nch * P * N) * sizeof(float));
-    p.dots = off;    off += al(static_cast<size_t>(B * H * nch) * sizeof(float));
     p.parts = off;   off += al(static_cast<size_t>(B * nch * H * 3) * sizeof(float));
     p.dbc = off;     off += p.groups > 1 ? al(static_cast<size_t>(2 * p.groups * B * L * N) * sizeof(float)) : 0;
     p.total = off;
@@ -157,7 +145,5 @@ inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64
 
 hipError_t launch_ssd_fwd(const SsdArgs& a, hipStream_t st);
 hipError_t launch_ssd_bwd(const SsdBwdArgs& a, hipStream_t st);
-// The state recurrence alone (nseg must be 1): fills a.chunk_states; writes no outputs.
-hipError_t launch_ssd_states(const SsdArgs& a, hipStream_t st);
 
 }  // namespace mssm

@@ -23,12 +23,12 @@
 //      storing the state entering every chunk (and the final state);
 //   2. adjoint states (ssd_dstate_kernel): one workgroup per (batch, head)
 //      walks the chunks backwards carrying dS in its accumulators, storing the
-//      dS of every chunk and <dS, S_out>; dh0 is the last dS_in;
+//      dS of every chunk; dh0 is the last dS_in;
 //   3. chunk gradients (ssd_bwd_chunk_kernel): one workgroup per (batch,
 //      chunk, head group), independent of every other: Bm, Cm and G = C B^T
 //      are staged and formed once, then for each head of the group the
 //      products above, dB and dC summed over the group's heads in the
-//      accumulators;
+//      accumulators, and <dS, S_out> from S_in and the X dS products;
 //   4. reductions (ssd_bwd_reduce_*_kernel): dA, dDskip, ddt_bias over (batch,
 //      chunk) and, with several head groups, dB and dC over the groups, in a
 //      fixed order (no atomics: bitwise reproducible).
@@ -121,56 +121,66 @@ __device__ __forceinline__ int state_item(int wv, int k, int r, int hl, int l32)
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2: adjoint states.  dS_in = exp(cum_last) dS + sum_i exp(cum_i) dy_i C_i^T,
-// chunks from the last to the first; the P x N adjoint lives in the
-// accumulators of the four waves as in the forward's state update.
+// Passes 1 and 2: the chains over chunks.  Both carry a P x N matrix through
+// the chunks of one (batch, head) as the same update,
+//   M <- exp(cum_last) M + sum_i q_i U_i^T V_i        (U: Q x P, V: Q x N rows),
+// the states forward (M = S, U = X, V = Bm, q_i = exp(cum_last - cum_i) Delta_i:
+// the forward's state update) and the adjoint states backward (M = dS, U = dY,
+// V = Cm, q_i = exp(cum_i): dS_in from dS), and store M as it enters each
+// chunk: the state entering chunk c (and the final state) for pass 3's dY S_in,
+// the adjoint of the state leaving chunk c for its dB and V.  The matrix lives
+// in the accumulators of the four waves as in the forward's state update.
 template <int N>
-struct alignas(16) DStateSmem {
-    float dy[kQ][kP + kPadRow];
-    float c[kQ][N + kPadRow];
-    float ecum[kQ];
-    float red[4];
+struct alignas(16) ChainSmem {
+    float u[kQ][kP + kPadRow];
+    float v[kQ][N + kPadRow];
+    float q[kQ];
+    float decay;
 };
 
 template <class T, int N>
-struct DStateRegs {
-    static constexpr int kY = kQ * kP / 4 / kThreads;  // float4 of dY per thread
-    static constexpr int kC = kQ * N / 4 / kThreads;   // float4 of Cm per thread
-    float4 y[kY], c[kC];
+struct ChainRegs {
+    static constexpr int kU = kQ * kP / 4 / kThreads;  // float4 of U per thread
+    static constexpr int kV = kQ * N / 4 / kThreads;   // float4 of V per thread
+    float4 u[kU], v[kV];
     float dt;
 };
 
-// Chunk [t0, t0 + 64)'s dY (this head), Cm and step sizes into registers; rows
-// at or past L lie outside the resources and read as zeros.
+// Chunk [t0, t0 + 64)'s U rows (this head), V rows and step sizes into
+// registers; rows at or past L lie outside the resources and read as zeros.
 template <class T, int N>
-__device__ __forceinline__ void load_dstate_chunk(const SsdBwdArgs& a, int64_t bi, int64_t h, int64_t t0, int tid,
-                                                  DStateRegs<T, N>& g) {
+__device__ __forceinline__ void load_chain_chunk(const SsdBwdArgs& a, const void* U, const void* V, int64_t bi,
+                                                 int64_t h, int64_t t0, int tid, ChainRegs<T, N>& g) {
     const int64_t H = a.H;
     const int64_t nv = a.L - t0 < 0 ? 0 : imin64(kQ, a.L - t0);
     const int64_t row0 = bi * a.L + t0;
     const T* tag = nullptr;
-    const auto ry = make_rsrc(static_cast<const T*>(a.dy) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
-    const auto rc = make_rsrc(static_cast<const T*>(a.Cm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
+    const auto ru = make_rsrc(static_cast<const T*>(U) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
+    const auto rv = make_rsrc(static_cast<const T*>(V) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
     const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
 #pragma unroll
-    for (int e = 0; e < DStateRegs<T, N>::kY; ++e) {
+    for (int e = 0; e < ChainRegs<T, N>::kU; ++e) {
         int i, p;
         stage_pos(e * kThreads + tid, kP / 4, i, p);
-        g.y[e] = load4(tag, ry, (int)((i * H + h) * kP + 4 * p));
+        g.u[e] = load4(tag, ru, (int)((i * H + h) * kP + 4 * p));
     }
 #pragma unroll
-    for (int e = 0; e < DStateRegs<T, N>::kC; ++e) {
+    for (int e = 0; e < ChainRegs<T, N>::kV; ++e) {
         int i, n;
         stage_pos(e * kThreads + tid, N / 4, i, n);
-        g.c[e] = load4(tag, rc, i * N + 4 * n);
+        g.v[e] = load4(tag, rv, i * N + 4 * n);
     }
     g.dt = load1(tag, rd, (int)((tid & 63) * H + h));
 }
 
-template <class T, int N>
-__global__ __launch_bounds__(kThreads) void ssd_dstate_kernel(SsdBwdArgs a) {
+// One workgroup per (batch, head), kept small (about 50 KB of LDS, under 170
+// registers) so that three run on a CU and all (batch, head) chains of a
+// training batch run at once.  REV: the adjoint states (pass 2), else the
+// states (pass 1).
+template <class T, int N, bool REV>
+__global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
     constexpr int NT = N / 64;
-    __shared__ DStateSmem<N> s;
+    __shared__ ChainSmem<N> s;
     const int tid = threadIdx.x;
     const int wv = wave_id();
     const int lane = tid & 63;
@@ -182,95 +192,87 @@ __global__ __launch_bounds__(kThreads) void ssd_dstate_kernel(SsdBwdArgs a) {
     const int64_t bi = bh / H, h = bh % H;
     const float Ah = a.A[h];
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const void* U = REV ? a.dy : a.x;
+    const void* V = REV ? a.Cm : a.Bm;
+    // where chunk c's entering matrix goes: the states (nch + 1 per job: the final state last), the adjoints
+    float* const store_base = REV ? a.dstates + bh * nch * PN : a.states + bh * (nch + 1) * PN;
 
-    f32x16 dS[NT];
+    const float* init = REV ? a.dh_final : a.h0;
+    f32x16 M[NT];
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            dS[k][r] = a.dh_final ? a.dh_final[bh * PN + state_item<N>(wv, k, r, hl, l32)] : 0.0f;
+        for (int r = 0; r < 16; ++r) M[k][r] = init ? init[bh * PN + state_item<N>(wv, k, r, hl, l32)] : 0.0f;
     }
 
-    DStateRegs<T, N> g;
-    load_dstate_chunk<T, N>(a, bi, h, (nch - 1) * kQ, tid, g);
-    for (int64_t c = nch - 1; c >= 0; --c) {
+    ChainRegs<T, N> g;
+    load_chain_chunk<T, N>(a, U, V, bi, h, (REV ? nch - 1 : 0) * kQ, tid, g);
+    for (int64_t step = 0; step < nch; ++step) {
+        const int64_t c = REV ? nch - 1 - step : step;
         const int64_t t0 = c * kQ;
         const int nv = (int)imin64(kQ, L - t0);
-        // ---- stage dY, Cm; exp(cum) ----
+        // ---- stage U, V; the weights q and the chunk's decay ----
 #pragma unroll
-        for (int e = 0; e < DStateRegs<T, N>::kY; ++e) {
+        for (int e = 0; e < ChainRegs<T, N>::kU; ++e) {
             int i, p;
             stage_pos(e * kThreads + tid, kP / 4, i, p);
             p *= 4;
-            s.dy[i][p] = g.y[e].x; s.dy[i][p + 1] = g.y[e].y; s.dy[i][p + 2] = g.y[e].z; s.dy[i][p + 3] = g.y[e].w;
+            s.u[i][p] = g.u[e].x; s.u[i][p + 1] = g.u[e].y; s.u[i][p + 2] = g.u[e].z; s.u[i][p + 3] = g.u[e].w;
         }
 #pragma unroll
-        for (int e = 0; e < DStateRegs<T, N>::kC; ++e) {
+        for (int e = 0; e < ChainRegs<T, N>::kV; ++e) {
             int i, n;
             stage_pos(e * kThreads + tid, N / 4, i, n);
             n *= 4;
-            s.c[i][n] = g.c[e].x; s.c[i][n + 1] = g.c[e].y; s.c[i][n + 2] = g.c[e].z; s.c[i][n + 3] = g.c[e].w;
+            s.v[i][n] = g.v[e].x; s.v[i][n + 1] = g.v[e].y; s.v[i][n + 2] = g.v[e].z; s.v[i][n + 3] = g.v[e].w;
         }
         if (wv == 0) {
             const ChunkScan cs = chunk_scan(g.dt, nv, bias, Ah, a.softplus, lane);
-            s.ecum[lane] = fexp(cs.cum);
+            s.q[lane] = REV ? fexp(cs.cum) : cs.w;
+            if (lane == kQ - 1) s.decay = fexp(cs.cum);
         }
-        // ---- the adjoint of the state leaving this chunk, stored; S_out loaded for <dS, S_out>, formed
-        // after the update so that neither the loads nor the stores hold the wave here ----
-        float so[NT][16], dso[NT][16];
+        // ---- the matrix entering this chunk, stored ----
         {
-            const float* ftag = nullptr;
-            const auto rso = make_rsrc(a.states + (bh * (nch + 1) + c + 1) * PN, (uint32_t)(PN * sizeof(float)));
-            const auto rout = make_rsrc(a.dstates + (bh * nch + c) * PN, (uint32_t)(PN * sizeof(float)));
+            const auto rout = make_rsrc(store_base + c * PN, (uint32_t)(PN * sizeof(float)));
             const int lo = opaque(state_item<N>(wv, 0, 0, hl, l32));
 #pragma unroll
-            for (int k = 0; k < NT; ++k) {
+            for (int k = 0; k < NT; ++k)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int o = lo + state_item<N>(wv, k, r, 0, 0) - state_item<N>(wv, 0, 0, 0, 0);
-                    so[k][r] = load1(ftag, rso, o);
-                    dso[k][r] = dS[k][r];
-                    store1<float>(dS[k][r], rout, o);
-                }
-            }
+                for (int r = 0; r < 16; ++r)
+                    store1<float>(M[k][r], rout, lo + state_item<N>(wv, k, r, 0, 0) - state_item<N>(wv, 0, 0, 0, 0));
         }
         __syncthreads();
-        // the previous chunk's inputs travel during this chunk's products (none before the first)
-        if (c > 0) load_dstate_chunk<T, N>(a, bi, h, t0 - kQ, tid, g);
+        // the next chunk's inputs travel during this chunk's products (none after the last)
+        if (step + 1 < nch) load_chain_chunk<T, N>(a, U, V, bi, h, (REV ? c - 1 : c + 1) * kQ, tid, g);
 
-        // ---- dS_in = exp(cum_last) dS + (exp(cum) o dY)^T C ----
-        const float decay = s.ecum[kQ - 1];
-        constexpr int SX = kP + kPadRow, SC = N + kPadRow;
-        const float* yf = &s.dy[0][0];
-        const float* cf = &s.c[0][0];
-        const int oy = opaque(hl * SX + sp * 32 + l32);
-        const int oc = opaque(hl * SC + (wv & 1) * NT * 32 + l32);
+        // ---- M = exp(cum_last) M + (q o U)^T V ----
+        const float decay = s.decay;
+        constexpr int SU = kP + kPadRow, SV = N + kPadRow;
+        const float* uf = &s.u[0][0];
+        const float* vf = &s.v[0][0];
+        const int ou = opaque(hl * SU + sp * 32 + l32);
+        const int ov = opaque(hl * SV + (wv & 1) * NT * 32 + l32);
 #pragma unroll
         for (int k = 0; k < NT; ++k) {
-            dS[k] = mfma_chain_scaled<kQ / 2>(
-                dS[k] * decay,
+            M[k] = mfma_chain_scaled<kQ / 2>(
+                M[k] * decay,
                 [&](int j, float& av, float& a2, float& bv) {
-                    av = s.ecum[2 * j + hl];
-                    a2 = yf[oy + 2 * j * SX];
-                    bv = cf[oc + k * 32 + 2 * j * SC];
+                    av = s.q[2 * j + hl];
+                    a2 = uf[ou + 2 * j * SU];
+                    bv = vf[ov + k * 32 + 2 * j * SV];
                 },
                 [](int) {});
         }
-        float part = 0.0f;
-#pragma unroll
-        for (int k = 0; k < NT; ++k)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) part += dso[k][r] * so[k][r];
-        part = wave_sum(part, lane);
-        if (lane == 0) s.red[wv] = part;
-        __syncthreads();
-        if (tid == 0) a.dots[bh * nch + c] = s.red[0] + s.red[1] + s.red[2] + s.red[3];
+        __syncthreads();  // every wave is done with u, v, q before the next chunk stages over them
     }
-    if (a.dh0) {
+    // the final state (pass 1) or dh0 (pass 2)
+    float* const last = REV ? a.dh0 : store_base + nch * PN;
+    if (last) {
+        const int64_t base = REV ? bh * PN : 0;
 #pragma unroll
         for (int k = 0; k < NT; ++k)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) a.dh0[bh * PN + state_item<N>(wv, k, r, hl, l32)] = dS[k][r];
+            for (int r = 0; r < 16; ++r) last[base + state_item<N>(wv, k, r, hl, l32)] = M[k][r];
     }
 }
 
@@ -300,6 +302,7 @@ struct alignas(16) BwdSmem {
     float red_c[N / 32][kQ];  // per n-block row sums of C o dC
     float red_r[2][kQ];       // per p-block row sums of X o V
     float red_d[2][4];        // per wave sums of dY o X (double-buffered by head parity)
+    float red_o[2][4];        // per wave parts of <dS, S_out> (double-buffered by head parity)
     float junk[kThreads];     // target of the masked operands' writes that belong to no operand
 };
 
@@ -311,19 +314,17 @@ struct HeadRegs {
     float4 x[kX], y[kX];
     float ds[kS];
     float dt;
-    float dot;
 };
 
 // One head's loads, numbered so that a caller can spread their issue over
 // matrix products (piece k < kPieces, a compile-time constant after
-// unrolling): the X and dY float4s, the dS floats, the step sizes, the dot.
+// unrolling): the X and dY float4s, the dS floats, the step sizes.
 template <class T, int N>
 struct HeadLoader {
     static constexpr int kX = HeadRegs<N>::kX, kS = HeadRegs<N>::kS;
-    static constexpr int kPieces = kX + kS + 2;
+    static constexpr int kPieces = kX + kS + 1;
     __amdgpu_buffer_rsrc_t rx, ry, rds, rd;
     int64_t H, h;
-    const float* dot;
     int tid;
 
     __device__ __forceinline__ HeadLoader(const SsdBwdArgs& a, int64_t bi, int64_t c, int64_t h_, int tid_)
@@ -340,7 +341,6 @@ struct HeadLoader {
         // 64-bit addresses per load
         rds = make_rsrc(a.dstates + (bh * nch + c) * PN, (uint32_t)(PN * sizeof(float)));
         rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
-        dot = a.dots + bh * nch + c;
     }
 
     __device__ __forceinline__ void piece(int k, HeadRegs<N>& g) const {
@@ -354,10 +354,8 @@ struct HeadLoader {
         } else if (k < kX + kS) {
             const float* ftag = nullptr;
             g.ds[k - kX] = load1(ftag, rds, (k - kX) * kThreads + tid);
-        } else if (k == kX + kS) {
-            g.dt = load1(tag, rd, (int)((tid & 63) * H + h));
         } else {
-            g.dot = *dot;
+            g.dt = load1(tag, rd, (int)((tid & 63) * H + h));
         }
     }
 
@@ -447,7 +445,6 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
     }
 
     float sig = 1.0f, dlt_l = 0.0f, cumd = 0.0f;  // wave 3: this head's sigmoid factor, Delta, sum_{s<=t} Delta_s
-    float dot = 0.0f;
     int par = 0;
     for (int64_t h = h_begin; h < h_end; ++h, par ^= 1) {
         const float Ah = a.A[h];
@@ -477,7 +474,6 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             sig = a.softplus ? sigmoid(v) : 1.0f;
             dlt_l = cs.d;
             cumd = wave_prefix_sum(cs.d, lane);
-            dot = g.dot;
             s.cum[lane] = cs.cum;
             s.dlt[lane] = cs.d;
             s.ecum[lane] = fexp(cs.cum);
@@ -518,6 +514,10 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
         // ---- (c) products ----
         // the next head's inputs travel during this head's products
         const bool more = h + 1 < h_end;
+        // <dS, S_out>, the adjoint's pairing with the state leaving the chunk, from the products at hand:
+        // S_out = exp(cum_last) S_in + sum_j Delta_j e_j X_j^T B_j, so it is exp(cum_last) <dS, S_in> plus
+        // sum_j Delta_j e_j X_j . (B dS^T)_j, whose (B dS^T) tiles the V products below form anyway
+        float odot = 0.0f;
         // dC tiles (rb, nb): diag(exp(cum)) dY S_in + M1 B
 #pragma unroll
         for (int t = 0; t < NTC; ++t) {
@@ -554,6 +554,14 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             const float rs = tile_row_sums(cdc, lane);
             if ((l32 & 1) == 0) s.red_c[nb][rb * 32 + acc_row((l32 >> 1) & 15, hl)] = rs;
         }
+        // <dS, S_in> over this wave's n-block (N = 64: waves 2 and 3 hold the blocks of waves 0 and 1)
+        if (wv < NB) {
+            float sdot = 0.0f;
+            const int os = opaque((nb * 32 + l32) * SX + hl);
+#pragma unroll
+            for (int k = 0; k < 32; ++k) sdot += sin[k] * sf[os + 2 * k];
+            odot = s.ecum[kQ - 1] * sdot;
+        }
         // the next head's loads go out one per product of the X dS chains (all together, they would hold
         // the wave); past the group's last head, a loader of the last head again (never used)
         const HeadLoader<T, N> next(a, bi, c, more ? h + 1 : h, tid);
@@ -579,7 +587,9 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             acc_row_cum(s.elast, rb, hl, el);
             acc_row_cum(s.dlt, rb, hl, dl);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] *= el[r];
+            for (int r = 0; r < 16; ++r) {
+                acc[r] *= el[r];
+            }
             // M3[j][k] C[k][n] over k >= j: k-blocks rb .. 1, the first one the diagonal block
             const int j = rb * 32 + l32;
             const int om = opaque(hl * SM + j);
@@ -609,8 +619,12 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             float el[16], dl[16];
             acc_row_cum(s.elast, vjb, hl, el);
             acc_row_cum(s.dlt, vjb, hl, dl);
+            const int px = vpb * 32 + l32;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] *= el[r];
+            for (int r = 0; r < 16; ++r) {
+                acc[r] *= el[r];
+                odot += dl[r] * acc[r] * s.x[vjb * 32 + acc_row(r, hl)][px];
+            }
             // M2[j][k] dY[k][p] over k >= j: k-blocks vjb .. 1, the first one the diagonal block
             const int j = vjb * 32 + l32;
             const int om = opaque(j * SM + hl);
@@ -639,6 +653,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             const float rs = tile_row_sums(xv, lane);
             if ((l32 & 1) == 0) s.red_r[vpb][vjb * 32 + acc_row((l32 >> 1) & 15, hl)] = rs;
         }
+        odot = wave_sum(odot, lane);
+        if (lane == 0) s.red_o[par][wv] = odot;
         __syncthreads();
 
         // ---- (d) per-step scalars (wave 3): dcum, dDelta, ddt; this head's dA, dDskip, ddt_bias parts ----
@@ -647,6 +663,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
 #pragma unroll
             for (int q = 0; q < NB; ++q) cdc += s.red_c[q][lane];
             const float r = s.red_r[0][lane] + s.red_r[1][lane];
+            const float dot = s.red_o[par][0] + s.red_o[par][1] + s.red_o[par][2] + s.red_o[par][3];
             const float dcum = cdc - dlt_l * r + (lane == kQ - 1 ? dot : 0.0f);
             const float incl = wave_prefix_sum(dcum, lane);
             const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
@@ -751,9 +768,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_groups_kernel(SsdBwdArgs a
 
 template <class T, int N>
 hipError_t launch_bwd_typed(const SsdBwdArgs& a, hipStream_t st) {
-    hipError_t e = launch_ssd_states(a.fwd, st);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ssd_dstate_kernel<T, N>), dim3((unsigned)(a.B * a.H)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((ssd_chain_kernel<T, N, false>), dim3((unsigned)(a.B * a.H)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((ssd_chain_kernel<T, N, true>), dim3((unsigned)(a.B * a.H)), dim3(kThreads), 0, st, a);
     const int64_t nch = (a.L + kQ - 1) / kQ;
     hipLaunchKernelGGL((ssd_bwd_chunk_kernel<T, N>), dim3((unsigned)(a.B * nch * a.groups)), dim3(kThreads), 0, st,
                        a);

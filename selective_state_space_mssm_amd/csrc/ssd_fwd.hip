@@ -67,10 +67,10 @@ struct ChunkRegs {
 // touches no memory).  The loads are numbered (piece k < kPieces: the X float4s,
 // then Bm's, Cm's, then the step sizes) so that a caller can spread their
 // issue over other work; k must be a compile-time constant after unrolling.
-template <class T, int N, bool LOAD_C = true>
+template <class T, int N>
 struct ChunkLoader {
     static constexpr int kX = ChunkRegs<N>::kX, kB = ChunkRegs<N>::kB;
-    static constexpr int kPieces = kX + (LOAD_C ? 2 : 1) * kB + 1;
+    static constexpr int kPieces = kX + 2 * kB + 1;
     __amdgpu_buffer_rsrc_t rx, rb, rc, rd;
     int64_t H, h;
     int tid;
@@ -111,10 +111,7 @@ struct ChunkLoader {
     }
 };
 
-// STATES: the backward's first pass -- only the state recurrence, no outputs:
-// the state entering every chunk c goes to chunk_states[(b, h)][c] and the
-// final state to chunk_states[(b, h)][nch] (time segments are not used then).
-template <class T, int N, bool STATES>
+template <class T, int N>
 __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     constexpr int NT = N / 64;  // state tiles per wave: the P x N state is 2 x (N / 32) tiles over 4 waves
     __shared__ SsdSmem<N> s;
@@ -201,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
         }
 
         ChunkRegs<N> g;
-        ChunkLoader<T, N, !STATES>(a, bi, h, t_begin, t_end, tid).all(g);
+        ChunkLoader<T, N>(a, bi, h, t_begin, t_end, tid).all(g);
         float lam = 0.0f;  // the segment's total log-decay, sum of Delta A_h
         // wave 1, the one with the least matrix work (its M tile lies above the
         // diagonal), forms each chunk's step quantities one chunk ahead, off the
@@ -226,23 +223,14 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                 stage_pos(e * kThreads + tid, N / 4, i, n);
                 n *= 4;
                 s.b[i][n] = g.b[e].x; s.b[i][n + 1] = g.b[e].y; s.b[i][n + 2] = g.b[e].z; s.b[i][n + 3] = g.b[e].w;
-                if constexpr (!STATES) {
-                    s.c[i][n] = g.c[e].x; s.c[i][n + 1] = g.c[e].y; s.c[i][n + 2] = g.c[e].z; s.c[i][n + 3] = g.c[e].w;
-                }
+                s.c[i][n] = g.c[e].x; s.c[i][n + 1] = g.c[e].y; s.c[i][n + 2] = g.c[e].z; s.c[i][n + 3] = g.c[e].w;
             }
-            if constexpr (!STATES) {  // S^T is the B operand of C S^T
+            // S^T is the B operand of C S^T
 #pragma unroll
-                for (int k = 0; k < NT; ++k) {
-                    const int n = ((wv & 1) * NT + k) * 32 + l32;
+            for (int k = 0; k < NT; ++k) {
+                const int n = ((wv & 1) * NT + k) * 32 + l32;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) s.st[n][sp * 32 + acc_row(r, hl)] = S[k][r];
-                }
-            } else {
-                float* cst = a.chunk_states + (bh * (nch + 1) + t0 / kQ) * kP * N;
-#pragma unroll
-                for (int k = 0; k < NT; ++k)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) cst[state_off(k, r)] = S[k][r];
+                for (int r = 0; r < 16; ++r) s.st[n][sp * 32 + acc_row(r, hl)] = S[k][r];
             }
             if (wv == 1) {
                 s.cum[lane] = cs.cum;
@@ -252,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             __syncthreads();
 
             // the next chunk's inputs travel while this chunk computes (past the end: no access)
-            const ChunkLoader<T, N, !STATES> next(a, bi, h, t0 + kQ, t_end, tid);
+            const ChunkLoader<T, N> next(a, bi, h, t0 + kQ, t_end, tid);
             lam += s.cum[kQ - 1];
 
             // per-lane LDS base offsets (floats) of the MFMA operands; step k adds a constant
@@ -271,9 +259,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             const int ob_s = opaque(hl * SB + (wv & 1) * NT * 32 + l32);   // B[j + hl][n]
 
             // ---- M = (C B^T) o Lmask, tile (ti, tj); the tile above the diagonal is zero ----
-            if constexpr (STATES) {
-                next.all(g);
-            } else {
+            {
                 f32x16 gm = {};
                 if (ti >= tj) {
                     // the next chunk's loads go out one every other product, while the matrix core runs:
@@ -305,11 +291,11 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                     s.m[i][j] = keep ? v : 0.0f;
                 }
             }
-            if constexpr (!STATES) __syncthreads();  // M is read by other waves below
+            __syncthreads();  // M is read by other waves below
 
             // ---- Y tile (ti, tj): exp(cum_i) (C S^T) + M X + D X ----
             f32x16 y = {};
-            if constexpr (!STATES) {
+            {
                 y = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
                     av = cf[oc + 2 * k];
                     bv = stf[ost + 2 * k * SX];
@@ -362,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                             bv = bf[obs + 2 * j * SB];
                         },
                         [&](int j) {
-                            if (!STATES && k == 0 && j % 2 == 0) store_y(j / 2);
+                            if (k == 0 && j % 2 == 0) store_y(j / 2);
                         });
                 }
             }
@@ -380,13 +366,6 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             for (int k = 0; k < NT; ++k)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) out[state_off(k, r)] = S[k][r];
-        }
-        if (STATES && to == kFinal) {
-            float* cst = a.chunk_states + (bh * (nch + 1) + nch) * kP * N;
-#pragma unroll
-            for (int k = 0; k < NT; ++k)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) cst[state_off(k, r)] = S[k][r];
         }
         if (a.nseg > 1 && tid == 0) a.ws[a.B * H * a.nseg * kP * N + bh * a.nseg + seg] = lam;
         if (to == kPublish) {
@@ -526,17 +505,16 @@ __global__ __launch_bounds__(256) void ssd_zero_flags_kernel(uint32_t* flags, in
     if (i < n) flags[i] = 0u;
 }
 
-template <class T, int N, bool STATES = false>
+template <class T, int N>
 hipError_t launch_typed(const SsdArgs& a, hipStream_t st) {
     const dim3 block(kThreads);
     if (a.workers > 0) {  // a fill kernel rather than a memset: the launch may be captured in a graph
         hipLaunchKernelGGL(ssd_zero_flags_kernel, dim3((unsigned)((a.workers + 1 + 255) / 256)), dim3(256), 0, st,
                            a.flags, a.workers + 1);
-        hipLaunchKernelGGL((ssd_fwd_kernel<T, N, STATES>), dim3((unsigned)a.workers), block, 0, st, a);
+        hipLaunchKernelGGL((ssd_fwd_kernel<T, N>), dim3((unsigned)a.workers), block, 0, st, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((ssd_fwd_kernel<T, N, STATES>), dim3((unsigned)(a.B * a.H * a.nseg)), block, 0, st, a);
-    if constexpr (STATES) return hipGetLastError();
+    hipLaunchKernelGGL((ssd_fwd_kernel<T, N>), dim3((unsigned)(a.B * a.H * a.nseg)), block, 0, st, a);
     if (a.nseg > 1) {
         const int64_t n = a.B * a.H * a.P * a.N;
         hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
@@ -550,12 +528,6 @@ hipError_t launch_typed(const SsdArgs& a, hipStream_t st) {
 hipError_t launch_ssd_fwd(const SsdArgs& a, hipStream_t st) {
     if (a.dtype == 1) return a.N == 64 ? launch_typed<uint16_t, 64>(a, st) : launch_typed<uint16_t, 128>(a, st);
     return a.N == 64 ? launch_typed<float, 64>(a, st) : launch_typed<float, 128>(a, st);
-}
-
-hipError_t launch_ssd_states(const SsdArgs& a, hipStream_t st) {
-    if (a.dtype == 1)
-        return a.N == 64 ? launch_typed<uint16_t, 64, true>(a, st) : launch_typed<uint16_t, 128, true>(a, st);
-    return a.N == 64 ? launch_typed<float, 64, true>(a, st) : launch_typed<float, 128, true>(a, st);
 }
 
 }  // namespace mssm
