@@ -300,11 +300,12 @@ mssm_status mssm_conv_step(const mssm_problem* p, int32_t d_conv,
  * Required: p, x, dt, A, Bm, Cm, y.  Optional (NULL): Dskip, dt_bias (-> 0),
  * h0 (-> zeros), h_final (not written; may be the same buffer as h0, which
  * then advances in place).  y and the workspace may not alias any input.
- * Built for headdim P = 64 and dstate N in {64, 128}: other sizes ->
- * MSSM_ERR_UNSUPPORTED.  Other errors as
- * mssm_scan_fwd; batch * nheads must be below 2^31 and nheads * headdim below
- * 2^23 (else MSSM_ERR_SHAPE).  workspace as mssm_scan_fwd's, sized by
- * mssm_ssd_fwd_workspace_bytes.
+ * Built for headdim P in {64, 128, 192, 256} and dstate N in {64, 128}: other
+ * sizes -> MSSM_ERR_UNSUPPORTED (a head of P channels runs as P / 64 heads of
+ * 64 channels that share its dt, A, Dskip and dt_bias).  Other errors as
+ * mssm_scan_fwd; batch * nheads * headdim / 64 must be below 2^31 and
+ * nheads * headdim below 2^23 (else MSSM_ERR_SHAPE).  workspace as
+ * mssm_scan_fwd's, sized by mssm_ssd_fwd_workspace_bytes.
  */
 typedef struct {
     int64_t batch;          /* B */
@@ -356,7 +357,8 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* d
  * Sizes, errors and alignment as mssm_ssd_fwd; the workspace (sized by
  * mssm_ssd_bwd_workspace_bytes, never 0) holds the chunk states and adjoint
  * states, (B * H * (2 * ceil(L / 64) + 1) * P * N) floats, plus small
- * partials. */
+ * partials (with headdim above 64 also B * L * H * P / 64 floats of ddt per
+ * 64-channel part of a head). */
 size_t mssm_ssd_bwd_workspace_bytes(const mssm_ssd_problem* p);
 
 mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,

@@ -241,17 +241,23 @@ mssm_status check_ssd_problem(const mssm_ssd_problem* p) {
     if (!p) return MSSM_ERR_NULL;
     if (p->dtype != MSSM_F32 && p->dtype != MSSM_BF16) return MSSM_ERR_DTYPE;
     if (p->batch < 1 || p->seqlen < 1 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1) return MSSM_ERR_SHAPE;
-    if (p->batch * p->nheads >= (int64_t{1} << 31) || p->seqlen >= (int64_t{1} << 31)) return MSSM_ERR_SHAPE;
+    // the kernels' (batch, sub-head) pairs, a sub-head being 64 channels of a head
+    if (p->batch * p->nheads * ((p->headdim + 63) / 64) >= (int64_t{1} << 31) || p->seqlen >= (int64_t{1} << 31))
+        return MSSM_ERR_SHAPE;
     if (p->nheads * p->headdim >= (int64_t{1} << 23)) return MSSM_ERR_SHAPE;  // a 64-step chunk stays below 2^31 bytes
     if (!mssm::ssd_supported(p->headdim, p->dstate)) return MSSM_ERR_UNSUPPORTED;
     return MSSM_OK;
 }
+
+// The kernels' heads: sub-heads of 64 channels (a head of headdim channels is
+// headdim / 64 of them, sharing its step size, decay, skip weight and bias).
+int64_t ssd_subheads(const mssm_ssd_problem* p) { return p->headdim / mssm::kSsdHeadDim; }
 }  // namespace
 
 size_t mssm_ssd_fwd_workspace_bytes(const mssm_ssd_problem* p) {
     if (check_ssd_problem(p) != MSSM_OK) return 0;
-    return mssm::plan_ssd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate, p->dtype == MSSM_BF16,
-                          device_cus())
+    return mssm::plan_ssd(p->batch, p->seqlen, p->nheads * ssd_subheads(p), mssm::kSsdHeadDim, p->dstate,
+                          p->dtype == MSSM_BF16, device_cus())
         .ws_bytes;
 }
 
@@ -264,19 +270,20 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* d
     if (!x || !dt || !A || !Bm || !Cm || !y) return MSSM_ERR_NULL;
     const mssm_status st = check_align({x, dt, A, Bm, Cm, Dskip, dt_bias, h0, y, h_final, workspace});
     if (st != MSSM_OK) return st;
-    const mssm::SsdPlan plan = mssm::plan_ssd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate,
+    const int64_t hsub = ssd_subheads(p), Hs = p->nheads * hsub;
+    const mssm::SsdPlan plan = mssm::plan_ssd(p->batch, p->seqlen, Hs, mssm::kSsdHeadDim, p->dstate,
                                               p->dtype == MSSM_BF16, device_cus());
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return MSSM_ERR_WORKSPACE;
 
     mssm::SsdArgs a{};
-    a.B = p->batch; a.L = p->seqlen; a.H = p->nheads; a.P = p->headdim; a.N = p->dstate;
+    a.B = p->batch; a.L = p->seqlen; a.H = Hs; a.P = mssm::kSsdHeadDim; a.N = p->dstate; a.hsub = hsub;
     a.softplus = p->delta_softplus ? 1 : 0;
     a.dtype = p->dtype == MSSM_BF16 ? 1 : 0;
     a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm;
     a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0; a.y = y; a.h_final = h_final;
     a.nseg = plan.nseg; a.seg_len = plan.seg_len; a.ws = static_cast<float*>(workspace);
     a.ws_y = plan.nseg > 1 && p->dtype == MSSM_BF16
-                 ? a.ws + p->batch * p->nheads * plan.nseg * (p->headdim * p->dstate + 1) : nullptr;
+                 ? a.ws + p->batch * Hs * plan.nseg * (mssm::kSsdHeadDim * p->dstate + 1) : nullptr;
     if (plan.workers > 0) {
         a.workers = static_cast<int32_t>(plan.workers);
         a.flags = static_cast<uint32_t*>(workspace);
@@ -289,8 +296,8 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* d
 
 size_t mssm_ssd_bwd_workspace_bytes(const mssm_ssd_problem* p) {
     if (check_ssd_problem(p) != MSSM_OK) return 0;
-    return mssm::plan_ssd_bwd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate, p->dtype == MSSM_BF16,
-                              device_cus())
+    return mssm::plan_ssd_bwd(p->batch, p->seqlen, p->nheads * ssd_subheads(p), mssm::kSsdHeadDim, p->dstate,
+                              ssd_subheads(p), device_cus())
         .total;
 }
 
@@ -307,13 +314,14 @@ mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* d
                                         ddt_bias, dh0, workspace});
     if (al != MSSM_OK) return al;
     const bool bf16 = p->dtype == MSSM_BF16;
+    const int64_t hsub = ssd_subheads(p), Hs = p->nheads * hsub;
     const mssm::SsdBwdPlan plan =
-        mssm::plan_ssd_bwd(p->batch, p->seqlen, p->nheads, p->headdim, p->dstate, bf16, device_cus());
+        mssm::plan_ssd_bwd(p->batch, p->seqlen, Hs, mssm::kSsdHeadDim, p->dstate, hsub, device_cus());
     if (!workspace || workspace_bytes < plan.total) return MSSM_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
 
     mssm::SsdBwdArgs a{};
-    a.B = p->batch; a.L = p->seqlen; a.H = p->nheads; a.P = p->headdim; a.N = p->dstate;
+    a.B = p->batch; a.L = p->seqlen; a.H = Hs; a.P = mssm::kSsdHeadDim; a.N = p->dstate; a.hsub = hsub;
     a.softplus = p->delta_softplus ? 1 : 0;
     a.dtype = bf16 ? 1 : 0;
     a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0;
@@ -323,6 +331,7 @@ mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* d
     a.dstates = reinterpret_cast<float*>(ws + plan.dstates);
     a.parts = reinterpret_cast<float*>(ws + plan.parts);
     a.dbc = plan.groups > 1 ? reinterpret_cast<float*>(ws + plan.dbc) : nullptr;
+    a.ddt_ws = hsub > 1 ? reinterpret_cast<float*>(ws + plan.ddt) : nullptr;
     a.groups = plan.groups;
     a.heads_per_group = plan.heads_per_group;
     return from_hip(mssm::launch_ssd_bwd(a, static_cast<hipStream_t>(hip_stream)));

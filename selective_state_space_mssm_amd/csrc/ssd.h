@@ -9,8 +9,16 @@ namespace mssm {
 // Validated arguments of one SSD forward: x, y (B, L, H, P); dt (B, L, H);
 // Bm, Cm (B, L, N) in the activation type (float32 or bfloat16 bits, `dtype`);
 // A, Dskip, dt_bias (H); h0, h_final (B, H, P, N) float32.
+//
+// Heads as the kernels see them: sub-heads of P = 64 channels.  A head of
+// hsub * 64 channels is hsub consecutive sub-heads (x, y and the state keep
+// their layout: (B, L, H, hsub * 64) is (B, L, H * hsub, 64)) that share the
+// head's step size, decay, skip weight and bias; here H counts sub-heads and
+// dt, A, Dskip, dt_bias are indexed by sub-head / hsub (dt's row has H / hsub
+// entries).
 struct SsdArgs {
-    int64_t B, L, H, P, N;
+    int64_t B, L, H, P, N;  // H: sub-heads; P = 64
+    int64_t hsub;           // sub-heads per head (the head dim / 64)
     int softplus;
     int dtype;             // 0: float32 activations, 1: bfloat16
     const void* x;
@@ -38,8 +46,12 @@ struct SsdArgs {
 constexpr int kSsdHeadDim = 64;   // P the kernel is built for
 constexpr int kSsdChunk = 64;     // chunk length of the dual form
 
-// True when the kernel is built for this head dimension and state size.
-inline bool ssd_supported(int64_t P, int64_t N) { return P == kSsdHeadDim && (N == 64 || N == 128); }
+constexpr int kSsdMaxSubHeads = 4;  // head dims 64, 128, 192, 256
+
+// True when the kernels are built for this head dimension and state size.
+inline bool ssd_supported(int64_t P, int64_t N) {
+    return P % kSsdHeadDim == 0 && P / kSsdHeadDim <= kSsdMaxSubHeads && (N == 64 || N == 128);
+}
 
 // How the work is cut, for a device of ncu compute units (one workgroup fits
 // a CU).  With fewer (batch, head) pairs than half the 256 CUs of an MI355X,
@@ -87,7 +99,8 @@ inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, b
 // ddt (B, L, H); dB, dC (B, L, N) in the activation type; dA, dD, ddt_bias (H),
 // dh0, dh_final (B, H, P, N) float32).
 struct SsdBwdArgs {
-    int64_t B, L, H, P, N;
+    int64_t B, L, H, P, N;  // H: sub-heads; P = 64 (as SsdArgs)
+    int64_t hsub;
     int softplus;
     int dtype;
     const void* x;
@@ -111,20 +124,22 @@ struct SsdBwdArgs {
     // workspace
     float* states;          // (B, H, nch + 1, P, N): state entering each 64-step chunk, then the final state
     float* dstates;         // (B, H, nch, P, N): adjoint of the state leaving each chunk
-    float* parts;           // (B, nch, H, 3): per chunk and head, the dA, dDskip, ddt_bias contributions
+    float* parts;           // (B, nch, H, 3): per chunk and sub-head, the dA, dDskip, ddt_bias contributions
+    float* ddt_ws;          // hsub > 1: (B, L, H) float32 ddt per sub-head, summed per head at the end; else null
     float* dbc;             // groups > 1: (2, groups, B, L, N) float32 dB, dC per head group; else null
     int64_t groups;         // head groups per (batch, chunk)
     int64_t heads_per_group;
 };
 
-// Workspace of the backward: states, adjoint states, partials and the
-// head-group partials of dB, dC (each 256-byte aligned).
+// Workspace of the backward: states, adjoint states, partials, the
+// head-group partials of dB, dC and, with sub-heads, their ddt (each 256-byte
+// aligned).  H counts sub-heads, P = 64.
 struct SsdBwdPlan {
     int64_t groups, heads_per_group;
-    size_t states, dstates, parts, dbc, total;  // byte offsets (total: size)
+    size_t states, dstates, parts, dbc, ddt, total;  // byte offsets (total: size)
 };
 
-inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, bool bf16, int64_t ncu) {
+inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t hsub, int64_t ncu) {
     auto al = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
     SsdBwdPlan p{};
     const int64_t nch = (L + kSsdChunk - 1) / kSsdChunk;
@@ -139,6 +154,7 @@ inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64
     p.dstates = off; off += al(static_cast<size_t>(B * H * nch * P * N) * sizeof(float));
     p.parts = off;   off += al(static_cast<size_t>(B * nch * H * 3) * sizeof(float));
     p.dbc = off;     off += p.groups > 1 ? al(static_cast<size_t>(2 * p.groups * B * L * N) * sizeof(float)) : 0;
+    p.ddt = off;     off += hsub > 1 ? al(static_cast<size_t>(B * L * H) * sizeof(float)) : 0;
     p.total = off;
     return p;
 }

@@ -157,7 +157,8 @@ __device__ __forceinline__ void load_chain_chunk(const SsdBwdArgs& a, const void
     const T* tag = nullptr;
     const auto ru = make_rsrc(static_cast<const T*>(U) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
     const auto rv = make_rsrc(static_cast<const T*>(V) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
-    const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
+    const int64_t Hd = H / a.hsub;  // dt has a row of heads; sub-head h reads its head's
+    const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * Hd, (uint32_t)(nv * Hd * sizeof(T)));
 #pragma unroll
     for (int e = 0; e < ChainRegs<T, N>::kU; ++e) {
         int i, p;
@@ -170,7 +171,7 @@ __device__ __forceinline__ void load_chain_chunk(const SsdBwdArgs& a, const void
         stage_pos(e * kThreads + tid, N / 4, i, n);
         g.v[e] = load4(tag, rv, i * N + 4 * n);
     }
-    g.dt = load1(tag, rd, (int)((tid & 63) * H + h));
+    g.dt = load1(tag, rd, (int)((tid & 63) * Hd + h / a.hsub));
 }
 
 // One workgroup per (batch, head), kept small (about 50 KB of LDS, under 170
@@ -190,8 +191,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
     const int64_t nch = (L + kQ - 1) / kQ;
     const int64_t bh = xcd_order(blockIdx.x, gridDim.x);
     const int64_t bi = bh / H, h = bh % H;
-    const float Ah = a.A[h];
-    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float Ah = a.A[h / a.hsub];
+    const float bias = a.dt_bias ? a.dt_bias[h / a.hsub] : 0.0f;
     const void* U = REV ? a.dy : a.x;
     const void* V = REV ? a.Cm : a.Bm;
     // where chunk c's entering matrix goes: the states (nch + 1 per job: the final state last), the adjoints
@@ -324,11 +325,11 @@ struct HeadLoader {
     static constexpr int kX = HeadRegs<N>::kX, kS = HeadRegs<N>::kS;
     static constexpr int kPieces = kX + kS + 1;
     __amdgpu_buffer_rsrc_t rx, ry, rds, rd;
-    int64_t H, h;
+    int64_t H, h, Hd, hd;  // sub-heads and this sub-head (x, dy); heads and this sub-head's head (dt)
     int tid;
 
     __device__ __forceinline__ HeadLoader(const SsdBwdArgs& a, int64_t bi, int64_t c, int64_t h_, int tid_)
-        : H(a.H), h(h_), tid(tid_) {
+        : H(a.H), h(h_), Hd(a.H / a.hsub), hd(h_ / a.hsub), tid(tid_) {
         const int64_t L = a.L, PN = kP * N;
         const int64_t nch = (L + kQ - 1) / kQ;
         const int64_t t0 = c * kQ;
@@ -340,7 +341,7 @@ struct HeadLoader {
         // dS through a buffer resource: a lane offset plus per-load constants kept in scalar offsets, not
         // 64-bit addresses per load
         rds = make_rsrc(a.dstates + (bh * nch + c) * PN, (uint32_t)(PN * sizeof(float)));
-        rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
+        rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * Hd, (uint32_t)(nv * Hd * sizeof(T)));
     }
 
     __device__ __forceinline__ void piece(int k, HeadRegs<N>& g) const {
@@ -355,7 +356,7 @@ struct HeadLoader {
             const float* ftag = nullptr;
             g.ds[k - kX] = load1(ftag, rds, (k - kX) * kThreads + tid);
         } else {
-            g.dt = load1(tag, rd, (int)((tid & 63) * H + h));
+            g.dt = load1(tag, rd, (int)((tid & 63) * Hd + hd));
         }
     }
 
@@ -447,8 +448,9 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
     float sig = 1.0f, dlt_l = 0.0f, cumd = 0.0f;  // wave 3: this head's sigmoid factor, Delta, sum_{s<=t} Delta_s
     int par = 0;
     for (int64_t h = h_begin; h < h_end; ++h, par ^= 1) {
-        const float Ah = a.A[h];
-        const float Dh = a.Dskip ? a.Dskip[h] : 0.0f;
+        const int64_t hd = h / a.hsub;  // the head this sub-head belongs to
+        const float Ah = a.A[hd];
+        const float Dh = a.Dskip ? a.Dskip[hd] : 0.0f;
         // ---- (a) stage X, dY, dS^T; step quantities (wave 3) ----
         float pd = 0.0f;
 #pragma unroll
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
         pd = wave_sum(pd, lane);
         if (lane == 0) s.red_d[par][wv] = pd;
         if (wv == 3) {
-            const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+            const float bias = a.dt_bias ? a.dt_bias[hd] : 0.0f;
             const float v = g.dt + bias;
             const ChunkScan cs = chunk_scan(g.dt, nv, bias, Ah, a.softplus, lane);
             sig = a.softplus ? sigmoid(v) : 1.0f;
@@ -669,8 +671,13 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
             const float dDelta = Ah * (total - incl + dcum) + r;
             const float ddt = dDelta * sig;
-            const auto rt = make_rsrc(static_cast<T*>(a.ddt) + (bi * L + t0) * H, (uint32_t)(nv * H * sizeof(T)));
-            store1<T>(ddt, rt, (int)(lane * H + h));
+            if (a.ddt_ws) {  // sub-heads of one head: summed per head in pass 4
+                const auto rt = make_rsrc(a.ddt_ws + (bi * L + t0) * H, (uint32_t)(nv * H * sizeof(float)));
+                store1<float>(ddt, rt, (int)(lane * H + h));
+            } else {
+                const auto rt = make_rsrc(static_cast<T*>(a.ddt) + (bi * L + t0) * H, (uint32_t)(nv * H * sizeof(T)));
+                store1<T>(ddt, rt, (int)(lane * H + h));
+            }
             const float pa = wave_sum(dcum * cumd, lane);
             const float pb = wave_sum(lane < nv ? ddt : 0.0f, lane);
             if (lane == 0) {
@@ -719,19 +726,21 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Pass 4: reductions in a fixed order (bitwise reproducible).  One workgroup per
-// head h: dA, dDskip, ddt_bias over the (batch, chunk) partials, each thread a
-// strided share, then a tree over the workgroup.
+// head h: dA, dDskip, ddt_bias over the (batch, chunk) partials of its
+// sub-heads, each thread a strided share, then a tree over the workgroup.
 __global__ __launch_bounds__(256) void ssd_bwd_reduce_heads_kernel(SsdBwdArgs a) {
     __shared__ float red[3][256];
-    const int64_t h = blockIdx.x, H = a.H;
+    const int64_t h = blockIdx.x, H = a.H, G = a.hsub;
     const int64_t nbc = a.B * ((a.L + kQ - 1) / kQ);
     const int tid = threadIdx.x;
     float sa = 0.0f, sd = 0.0f, sb = 0.0f;
     for (int64_t bc = tid; bc < nbc; bc += 256) {
-        const float* p = a.parts + (bc * H + h) * 3;
-        sa += p[0];
-        sd += p[1];
-        sb += p[2];
+        for (int64_t q = 0; q < G; ++q) {
+            const float* p = a.parts + (bc * H + h * G + q) * 3;
+            sa += p[0];
+            sd += p[1];
+            sb += p[2];
+        }
     }
     red[0][tid] = sa;
     red[1][tid] = sd;
@@ -750,6 +759,17 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_heads_kernel(SsdBwdArgs a)
         if (a.dD) a.dD[h] = red[1][0];
         if (a.ddt_bias) a.ddt_bias[h] = red[2][0];
     }
+}
+
+// With sub-heads: ddt of one (batch, step, head) summed over the head's sub-heads.
+template <class T>
+__global__ __launch_bounds__(256) void ssd_bwd_ddt_kernel(SsdBwdArgs a) {
+    const int64_t G = a.hsub, Hd = a.H / G;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= a.B * a.L * Hd) return;
+    float v = 0.0f;
+    for (int64_t q = 0; q < G; ++q) v += a.ddt_ws[e * G + q];
+    store_act(static_cast<T*>(a.ddt), e, v);
 }
 
 // With several head groups: dB and dC of one element summed over the groups.
@@ -773,7 +793,11 @@ hipError_t launch_bwd_typed(const SsdBwdArgs& a, hipStream_t st) {
     const int64_t nch = (a.L + kQ - 1) / kQ;
     hipLaunchKernelGGL((ssd_bwd_chunk_kernel<T, N>), dim3((unsigned)(a.B * nch * a.groups)), dim3(kThreads), 0, st,
                        a);
-    hipLaunchKernelGGL(ssd_bwd_reduce_heads_kernel, dim3((unsigned)a.H), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(ssd_bwd_reduce_heads_kernel, dim3((unsigned)(a.H / a.hsub)), dim3(256), 0, st, a);
+    if (a.ddt_ws) {
+        const int64_t n = a.B * a.L * (a.H / a.hsub);
+        hipLaunchKernelGGL((ssd_bwd_ddt_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+    }
     if (a.groups > 1) {
         const int64_t n = a.B * a.L * a.N;
         hipLaunchKernelGGL((ssd_bwd_reduce_groups_kernel<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);

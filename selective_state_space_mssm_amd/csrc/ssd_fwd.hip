@@ -72,18 +72,18 @@ struct ChunkLoader {
     static constexpr int kX = ChunkRegs<N>::kX, kB = ChunkRegs<N>::kB;
     static constexpr int kPieces = kX + 2 * kB + 1;
     __amdgpu_buffer_rsrc_t rx, rb, rc, rd;
-    int64_t H, h;
+    int64_t H, h, Hd, hd;  // sub-heads and this sub-head (x); heads and this sub-head's head (dt)
     int tid;
 
     __device__ __forceinline__ ChunkLoader(const SsdArgs& a, int64_t bi, int64_t h_, int64_t t0, int64_t t_end,
                                            int tid_)
-        : H(a.H), h(h_), tid(tid_) {
+        : H(a.H), h(h_), Hd(a.H / a.hsub), hd(h_ / a.hsub), tid(tid_) {
         const int64_t nv = t_end - t0 < 0 ? 0 : imin64(kQ, t_end - t0);
         const int64_t row0 = bi * a.L + t0;
         rx = make_rsrc(static_cast<const T*>(a.x) + row0 * H * kP, (uint32_t)(nv * H * kP * sizeof(T)));
         rb = make_rsrc(static_cast<const T*>(a.Bm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
         rc = make_rsrc(static_cast<const T*>(a.Cm) + row0 * N, (uint32_t)(nv * N * sizeof(T)));
-        rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
+        rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * Hd, (uint32_t)(nv * Hd * sizeof(T)));
     }
 
     __device__ __forceinline__ void piece(int k, ChunkRegs<N>& g) const {
@@ -101,7 +101,7 @@ struct ChunkLoader {
             else
                 g.c[e] = load4(tag, rc, i * N + 4 * n);
         } else {
-            g.dt = load1(tag, rd, (int)((tid & 63) * H + h));  // lane = step; used by wave 1
+            g.dt = load1(tag, rd, (int)((tid & 63) * Hd + hd));  // lane = step; used by wave 1
         }
     }
 
@@ -160,9 +160,10 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
         }
         const int64_t bi = bh / H, h = bh % H;
 
-        const float Ah = a.A[h];
-        const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-        const float Dh = a.Dskip ? a.Dskip[h] : 0.0f;
+        const int64_t hd = h / a.hsub;  // the head this sub-head belongs to
+        const float Ah = a.A[hd];
+        const float bias = a.dt_bias ? a.dt_bias[hd] : 0.0f;
+        const float Dh = a.Dskip ? a.Dskip[hd] : 0.0f;
 
         const int64_t state_base = bh * kP * N;
         f32x16 S[NT];
@@ -418,8 +419,9 @@ __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
     const int64_t job = xcd_order(blockIdx.x, gridDim.x);
     const int64_t seg = job % S1 + 1, bi = job / S1 / H, h = job / S1 % H;
     const int64_t t_begin = seg * a.seg_len, t_end = imin64(L, t_begin + a.seg_len);
-    const float Ah = a.A[h];
-    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const int64_t Hd = H / a.hsub, hd = h / a.hsub;  // heads; the head this sub-head belongs to
+    const float Ah = a.A[hd];
+    const float bias = a.dt_bias ? a.dt_bias[hd] : 0.0f;
     const int ti = wv >> 1, tj = wv & 1;
 
     // S_in^T into LDS, once: the state is the same for the whole segment
@@ -439,8 +441,8 @@ __global__ __launch_bounds__(kThreads) void ssd_correct_kernel(SsdArgs a) {
             const int q = e * kThreads + tid, i = q / (N / 4), n = (q % (N / 4)) * 4;
             cr[e] = load4(cm, rc, i * N + n);
         }
-        const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * H, (uint32_t)(nv * H * sizeof(T)));
-        dtv = load1(cm, rd, (int)(lane * H + h));
+        const auto rd = make_rsrc(static_cast<const T*>(a.dt) + row0 * Hd, (uint32_t)(nv * Hd * sizeof(T)));
+        dtv = load1(cm, rd, (int)(lane * Hd + hd));
     };
     load(t_begin);
 

@@ -211,7 +211,9 @@ def test_ssd_validation():
     assert ssd(good(batch=1 << 20, nheads=1 << 11)) == -2   # B*H >= 2^31
     assert ssd(good(seqlen=1 << 31)) == -2
     assert ssd(good(batch=1, nheads=1 << 17)) == -2         # H * P >= 2^23
-    assert ssd(good(headdim=32)) == -4                      # built for P = 64
+    assert ssd(good(headdim=32)) == -4                      # built for P = 64, 128, 192, 256
+    assert ssd(good(headdim=96)) == -4 and ssd(good(headdim=320)) == -4
+    assert ssd(good(batch=1 << 20, nheads=1 << 10, headdim=128)) == -2  # B * H * P / 64 >= 2^31
     assert ssd(good(dstate=16)) == -4                       # built for N in {64, 128}
     for n in ("x", "dt", "A", "Bm", "Cm", "y"):
         assert ssd(good(), **{n: None}) == -1, n
@@ -222,6 +224,8 @@ def test_ssd_validation():
     need = q(seqlen=1000)  # 6 pairs, 16 chunks: 8 segments of 128 steps
     assert need == 6 * 8 * (64 * 64 + 1) * 4
     assert q(seqlen=1000, dtype=1) == need + 2 * 1000 * 3 * 64 * 4  # bf16: float32 outputs before the correction
+    # a 128-channel head is two 64-channel sub-heads: 12 (batch, sub-head) pairs, 8 segments
+    assert q(seqlen=1000, headdim=128) == 12 * 8 * (64 * 64 + 1) * 4
     assert q() == 0 and q(seqlen=1000, batch=64, nheads=2) == 0 and q(seqlen=1000, dstate=16) == 0
     assert ssd(good(seqlen=1000)) == -6
     assert ssd(good(seqlen=1000), ws=FAKE, wsb=need - 1) == -6
