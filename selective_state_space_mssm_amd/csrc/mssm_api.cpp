@@ -332,6 +332,10 @@ mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* d
     a.parts = reinterpret_cast<float*>(ws + plan.parts);
     a.dbc = plan.groups > 1 ? reinterpret_cast<float*>(ws + plan.dbc) : nullptr;
     a.ddt_ws = hsub > 1 ? reinterpret_cast<float*>(ws + plan.ddt) : nullptr;
+    a.nseg = plan.nseg;
+    a.seg_chunks = plan.seg_chunks;
+    a.seg_state = plan.nseg > 1 ? reinterpret_cast<float*>(ws + plan.seg_state) : nullptr;
+    a.chunk_lam = plan.nseg > 1 ? reinterpret_cast<float*>(ws + plan.chunk_lam) : nullptr;
     a.groups = plan.groups;
     a.heads_per_group = plan.heads_per_group;
     return from_hip(mssm::launch_ssd_bwd(a, static_cast<hipStream_t>(hip_stream)));

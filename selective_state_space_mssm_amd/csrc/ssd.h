@@ -129,14 +129,20 @@ struct SsdBwdArgs {
     float* dbc;             // groups > 1: (2, groups, B, L, N) float32 dB, dC per head group; else null
     int64_t groups;         // head groups per (batch, chunk)
     int64_t heads_per_group;
+    // the chains (passes 1 and 2) in time segments of seg_chunks chunks, scanned in parallel from zero and
+    // then corrected (nseg == 1: one walk per (batch, sub-head))
+    int64_t nseg, seg_chunks;
+    float* seg_state;       // nseg > 1: (B, H, nseg, P, N) each segment's end state (pass 1) / start adjoint (pass 2)
+    float* chunk_lam;       // nseg > 1: (B, H, nch) each chunk's log-decay, sum of Delta A_h
 };
 
 // Workspace of the backward: states, adjoint states, partials, the
-// head-group partials of dB, dC and, with sub-heads, their ddt (each 256-byte
+// head-group partials of dB, dC, with sub-heads their ddt, with time
+// segments the chains' segment states and chunk log-decays (each 256-byte
 // aligned).  H counts sub-heads, P = 64.
 struct SsdBwdPlan {
-    int64_t groups, heads_per_group;
-    size_t states, dstates, parts, dbc, ddt, total;  // byte offsets (total: size)
+    int64_t groups, heads_per_group, nseg, seg_chunks;
+    size_t states, dstates, parts, dbc, ddt, seg_state, chunk_lam, total;  // byte offsets (total: size)
 };
 
 inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t hsub, int64_t ncu) {
@@ -155,6 +161,19 @@ inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64
     p.parts = off;   off += al(static_cast<size_t>(B * nch * H * 3) * sizeof(float));
     p.dbc = off;     off += p.groups > 1 ? al(static_cast<size_t>(2 * p.groups * B * L * N) * sizeof(float)) : 0;
     p.ddt = off;     off += hsub > 1 ? al(static_cast<size_t>(B * L * H) * sizeof(float)) : 0;
+    // The chains walk their chunks one after another, three workgroups to a CU: with fewer (batch, sub-head)
+    // pairs than fill the CUs that way, time segments of at least two chunks, about 768 workgroups in all
+    p.nseg = 1;
+    p.seg_chunks = nch;
+    const int64_t jobs = B * H, slots = 3 * (ncu > 0 ? ncu : 256);
+    if (jobs < slots / 3 && nch >= 4) {
+        const int64_t want = slots / jobs, most = nch / 2;
+        const int64_t segs = want < most ? want : most;
+        p.seg_chunks = (nch + segs - 1) / segs;
+        p.nseg = (nch + p.seg_chunks - 1) / p.seg_chunks;
+    }
+    p.seg_state = off; off += p.nseg > 1 ? al(static_cast<size_t>(jobs * p.nseg * P * N) * sizeof(float)) : 0;
+    p.chunk_lam = off; off += p.nseg > 1 ? al(static_cast<size_t>(jobs * nch) * sizeof(float)) : 0;
     p.total = off;
     return p;
 }

@@ -174,10 +174,13 @@ __device__ __forceinline__ void load_chain_chunk(const SsdBwdArgs& a, const void
     g.dt = load1(tag, rd, (int)((tid & 63) * Hd + h / a.hsub));
 }
 
-// One workgroup per (batch, head), kept small (about 50 KB of LDS, under 170
-// registers) so that three run on a CU and all (batch, head) chains of a
-// training batch run at once.  REV: the adjoint states (pass 2), else the
-// states (pass 1).
+// One workgroup per (batch, sub-head) and time segment, kept small (about
+// 50 KB of LDS, under 170 registers) so that three run on a CU and all
+// chains of a training batch run at once.  REV: the adjoint states (pass 2),
+// else the states (pass 1).  With time segments (a.nseg > 1) each segment
+// starts from zero -- the first from h0, the last adjoint from dh_final --
+// and leaves its end state (start adjoint) in seg_state; ssd_chain_fix_kernel
+// then adds what the true entering matrix contributes to every stored one.
 template <class T, int N, bool REV>
 __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
     constexpr int NT = N / 64;
@@ -189,8 +192,12 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
     const int sp = wv >> 1;
     const int64_t H = a.H, L = a.L, PN = kP * N;
     const int64_t nch = (L + kQ - 1) / kQ;
-    const int64_t bh = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t job = xcd_order(blockIdx.x, gridDim.x);
+    const int64_t bh = job / a.nseg, seg = job % a.nseg;
     const int64_t bi = bh / H, h = bh % H;
+    const int64_t c_begin = seg * a.seg_chunks, c_end = imin64(nch, c_begin + a.seg_chunks);
+    const int64_t steps = c_end - c_begin;
+    const bool first_seg = REV ? c_end == nch : seg == 0;  // the segment whose walk starts at the true boundary
     const float Ah = a.A[h / a.hsub];
     const float bias = a.dt_bias ? a.dt_bias[h / a.hsub] : 0.0f;
     const void* U = REV ? a.dy : a.x;
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
     // where chunk c's entering matrix goes: the states (nch + 1 per job: the final state last), the adjoints
     float* const store_base = REV ? a.dstates + bh * nch * PN : a.states + bh * (nch + 1) * PN;
 
-    const float* init = REV ? a.dh_final : a.h0;
+    const float* init = first_seg ? (REV ? a.dh_final : a.h0) : nullptr;
     f32x16 M[NT];
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
@@ -207,9 +214,9 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
     }
 
     ChainRegs<T, N> g;
-    load_chain_chunk<T, N>(a, U, V, bi, h, (REV ? nch - 1 : 0) * kQ, tid, g);
-    for (int64_t step = 0; step < nch; ++step) {
-        const int64_t c = REV ? nch - 1 - step : step;
+    load_chain_chunk<T, N>(a, U, V, bi, h, (REV ? c_end - 1 : c_begin) * kQ, tid, g);
+    for (int64_t step = 0; step < steps; ++step) {
+        const int64_t c = REV ? c_end - 1 - step : c_begin + step;
         const int64_t t0 = c * kQ;
         const int nv = (int)imin64(kQ, L - t0);
         // ---- stage U, V; the weights q and the chunk's decay ----
@@ -230,7 +237,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
         if (wv == 0) {
             const ChunkScan cs = chunk_scan(g.dt, nv, bias, Ah, a.softplus, lane);
             s.q[lane] = REV ? fexp(cs.cum) : cs.w;
-            if (lane == kQ - 1) s.decay = fexp(cs.cum);
+            if (lane == kQ - 1) {
+                s.decay = fexp(cs.cum);
+                if (!REV && a.nseg > 1) a.chunk_lam[bh * nch + c] = cs.cum;  // for the correction
+            }
         }
         // ---- the matrix entering this chunk, stored ----
         {
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
         }
         __syncthreads();
         // the next chunk's inputs travel during this chunk's products (none after the last)
-        if (step + 1 < nch) load_chain_chunk<T, N>(a, U, V, bi, h, (REV ? c - 1 : c + 1) * kQ, tid, g);
+        if (step + 1 < steps) load_chain_chunk<T, N>(a, U, V, bi, h, (REV ? c - 1 : c + 1) * kQ, tid, g);
 
         // ---- M = exp(cum_last) M + (q o U)^T V ----
         const float decay = s.decay;
@@ -266,14 +276,59 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
         }
         __syncthreads();  // every wave is done with u, v, q before the next chunk stages over them
     }
-    // the final state (pass 1) or dh0 (pass 2)
-    float* const last = REV ? a.dh0 : store_base + nch * PN;
+    // the final state (pass 1) or dh0 (pass 2) from the segment that reaches it, else the segment's own end
+    const bool at_end = REV ? seg == 0 : c_end == nch;
+    float* const last = at_end ? (REV ? (a.dh0 ? a.dh0 + bh * PN : nullptr) : store_base + nch * PN)
+                               : a.seg_state + (bh * a.nseg + seg) * PN;
     if (last) {
-        const int64_t base = REV ? bh * PN : 0;
 #pragma unroll
         for (int k = 0; k < NT; ++k)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) last[base + state_item<N>(wv, k, r, hl, l32)] = M[k][r];
+            for (int r = 0; r < 16; ++r) last[state_item<N>(wv, k, r, hl, l32)] = M[k][r];
+    }
+}
+
+// The chains' time segments joined, one thread per (batch, sub-head, item of
+// the P x N matrix), from the segment whose walk was exact outwards: the true
+// matrix T at a segment's outer boundary (the state entering it, the adjoint
+// leaving it) is the neighbour's own end value plus that neighbour's decay
+// times the neighbour's T, and every matrix stored inside the segment gains
+// T times the decay between the boundary and it (chunk log-decays lambda_c,
+// summed).  Pass 1 also completes the final state, pass 2 dh0.
+template <int N, bool REV>
+__global__ __launch_bounds__(256) void ssd_chain_fix_kernel(SsdBwdArgs a) {
+    const int64_t PN = kP * N, nch = (a.L + kQ - 1) / kQ;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.B * a.H * PN) return;
+    const int64_t bh = i / PN, e = i % PN;
+    const float* lam = a.chunk_lam + bh * nch;
+    const float* own = a.seg_state + bh * a.nseg * PN + e;  // each segment's own end state / start adjoint
+    float* const m = (REV ? a.dstates + bh * nch * PN : a.states + bh * (nch + 1) * PN) + e;
+    float T = 0.0f;  // the first segment walked (exact) needs nothing
+    for (int64_t q = 0; q < a.nseg; ++q) {
+        const int64_t seg = REV ? a.nseg - 1 - q : q;
+        const int64_t c0 = seg * a.seg_chunks, c1 = imin64(nch, c0 + a.seg_chunks);
+        float sum = 0.0f;  // log-decay from the segment's outer boundary to the current chunk
+        if (REV) {
+            for (int64_t c = c1 - 1; c >= c0; --c) {
+                if (q > 0) m[c * PN] += fexp(sum) * T;
+                sum += lam[c];
+            }
+        } else {
+            for (int64_t c = c0; c < c1; ++c) {
+                if (q > 0) m[c * PN] += fexp(sum) * T;
+                sum += lam[c];
+            }
+        }
+        // T of the next segment: this one's own end value plus its whole decay times its T
+        const bool last_walked = q == a.nseg - 1;
+        float* const end = last_walked ? (REV ? (a.dh0 ? a.dh0 + bh * PN + e : nullptr) : m + nch * PN)
+                                       : nullptr;
+        if (end) {
+            *end += fexp(sum) * T;
+        } else if (!last_walked) {
+            T = own[seg * PN] + fexp(sum) * T;
+        }
     }
 }
 
@@ -788,8 +843,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_groups_kernel(SsdBwdArgs a
 
 template <class T, int N>
 hipError_t launch_bwd_typed(const SsdBwdArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((ssd_chain_kernel<T, N, false>), dim3((unsigned)(a.B * a.H)), dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL((ssd_chain_kernel<T, N, true>), dim3((unsigned)(a.B * a.H)), dim3(kThreads), 0, st, a);
+    const dim3 chains((unsigned)(a.B * a.H * a.nseg));
+    const dim3 fix((unsigned)((a.B * a.H * kP * N + 255) / 256));
+    hipLaunchKernelGGL((ssd_chain_kernel<T, N, false>), chains, dim3(kThreads), 0, st, a);
+    if (a.nseg > 1) hipLaunchKernelGGL((ssd_chain_fix_kernel<N, false>), fix, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((ssd_chain_kernel<T, N, true>), chains, dim3(kThreads), 0, st, a);
+    if (a.nseg > 1) hipLaunchKernelGGL((ssd_chain_fix_kernel<N, true>), fix, dim3(256), 0, st, a);
     const int64_t nch = (a.L + kQ - 1) / kQ;
     hipLaunchKernelGGL((ssd_bwd_chunk_kernel<T, N>), dim3((unsigned)(a.B * nch * a.groups)), dim3(kThreads), 0, st,
                        a);

@@ -7,8 +7,9 @@ element by element with helpers.grad_err at 1e-3 (float32) or 2e-2
 Shapes span several 64-step chunks with a ragged last chunk, one step, both
 built state sizes, every optional input or none, softplus off, bfloat16, the
 head-group partials (few (batch, chunk) pairs) and one group per (batch,
-chunk), the balanced schedule of the states pass, and the 80-head d_state-128
-layer at batch 8 on sampled heads; dB, dC there by linearity in dy."""
+chunk), the chains in time segments (few (batch, head) pairs), many pairs, and
+the 80-head d_state-128 layer at batch 8 on sampled heads; dB, dC there by
+linearity in dy."""
 import numpy as np
 import pytest
 
@@ -101,8 +102,17 @@ def test_ssd_bwd_one_group(lib):
     assert_grads(g, r, GRAD_TOL["f32"])
 
 
-def test_ssd_bwd_balanced_states_pass(lib):
-    # 270 (batch, head) pairs: the states pass runs the forward's balanced persistent schedule
+@pytest.mark.parametrize("B,L,H,N", [(1, 1000, 3, 64), (1, 2048, 24, 128), (2, 1100, 5, 128)])
+def test_ssd_bwd_time_segments(lib, B, L, H, N):
+    # few (batch, head) pairs: both chains run in time segments from zero, joined and corrected afterwards
+    # (1000 steps, 3 pairs: 8 segments of 2 chunks, the last ragged; the 24-head batch-1 layer: 16 segments;
+    # 10 pairs over 18 chunks: 9 segments), with h0 and dh_final entering the outer segments
+    g, r = run_both(lib, B, L, H, N, seed=L + H)
+    assert_grads(g, r, GRAD_TOL["f32"])
+
+
+def test_ssd_bwd_many_pairs(lib):
+    # 270 (batch, head) pairs: one walk per pair, more chains than CUs
     g, r = run_both(lib, 3, 130, 90, 64, seed=41)
     assert_grads(g, r, GRAD_TOL["f32"])
 
