@@ -335,7 +335,8 @@ mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* d
     a.nseg = plan.nseg;
     a.seg_chunks = plan.seg_chunks;
     a.seg_state = plan.nseg > 1 ? reinterpret_cast<float*>(ws + plan.seg_state) : nullptr;
-    a.chunk_lam = plan.nseg > 1 ? reinterpret_cast<float*>(ws + plan.chunk_lam) : nullptr;
+    a.seg_lam = plan.nseg > 1 ? reinterpret_cast<float*>(ws + plan.seg_lam) : nullptr;
+    a.chunk_dec = plan.nseg > 1 ? reinterpret_cast<float*>(ws + plan.chunk_dec) : nullptr;
     a.groups = plan.groups;
     a.heads_per_group = plan.heads_per_group;
     return from_hip(mssm::launch_ssd_bwd(a, static_cast<hipStream_t>(hip_stream)));

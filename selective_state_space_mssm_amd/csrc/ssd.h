@@ -133,16 +133,17 @@ struct SsdBwdArgs {
     // then corrected (nseg == 1: one walk per (batch, sub-head))
     int64_t nseg, seg_chunks;
     float* seg_state;       // nseg > 1: (B, H, nseg, P, N) each segment's end state (pass 1) / start adjoint (pass 2)
-    float* chunk_lam;       // nseg > 1: (B, H, nch) each chunk's log-decay, sum of Delta A_h
+    float* seg_lam;         // nseg > 1: (B, H, nseg) each segment's log-decay, sum of Delta A_h over it
+    float* chunk_dec;       // nseg > 1: (B, H, nch) decay from the chunk's segment boundary to its stored matrix
 };
 
 // Workspace of the backward: states, adjoint states, partials, the
 // head-group partials of dB, dC, with sub-heads their ddt, with time
-// segments the chains' segment states and chunk log-decays (each 256-byte
-// aligned).  H counts sub-heads, P = 64.
+// segments the chains' segment states, segment log-decays and per-chunk
+// decays (each 256-byte aligned).  H counts sub-heads, P = 64.
 struct SsdBwdPlan {
     int64_t groups, heads_per_group, nseg, seg_chunks;
-    size_t states, dstates, parts, dbc, ddt, seg_state, chunk_lam, total;  // byte offsets (total: size)
+    size_t states, dstates, parts, dbc, ddt, seg_state, seg_lam, chunk_dec, total;  // byte offsets (total: size)
 };
 
 inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t hsub, int64_t ncu) {
@@ -173,7 +174,8 @@ inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64
         p.nseg = (nch + p.seg_chunks - 1) / p.seg_chunks;
     }
     p.seg_state = off; off += p.nseg > 1 ? al(static_cast<size_t>(jobs * p.nseg * P * N) * sizeof(float)) : 0;
-    p.chunk_lam = off; off += p.nseg > 1 ? al(static_cast<size_t>(jobs * nch) * sizeof(float)) : 0;
+    p.seg_lam = off;   off += p.nseg > 1 ? al(static_cast<size_t>(jobs * p.nseg) * sizeof(float)) : 0;
+    p.chunk_dec = off; off += p.nseg > 1 ? al(static_cast<size_t>(jobs * nch) * sizeof(float)) : 0;
     p.total = off;
     return p;
 }

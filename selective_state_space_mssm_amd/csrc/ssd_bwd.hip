@@ -179,8 +179,9 @@ __device__ __forceinline__ void load_chain_chunk(const SsdBwdArgs& a, const void
 // chains of a training batch run at once.  REV: the adjoint states (pass 2),
 // else the states (pass 1).  With time segments (a.nseg > 1) each segment
 // starts from zero -- the first from h0, the last adjoint from dh_final --
-// and leaves its end state (start adjoint) in seg_state; ssd_chain_fix_kernel
-// then adds what the true entering matrix contributes to every stored one.
+// and leaves its end state (start adjoint) in seg_state; ssd_chain_carry_kernel
+// and ssd_chain_fix_kernel then add what the true boundary matrix contributes
+// to every stored one.
 template <class T, int N, bool REV>
 __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
     constexpr int NT = N / 64;
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
 
     ChainRegs<T, N> g;
     load_chain_chunk<T, N>(a, U, V, bi, h, (REV ? c_end - 1 : c_begin) * kQ, tid, g);
+    float run = 0.0f;  // wave 0, lane 63: log-decay of the chunks walked so far in this segment
     for (int64_t step = 0; step < steps; ++step) {
         const int64_t c = REV ? c_end - 1 - step : c_begin + step;
         const int64_t t0 = c * kQ;
@@ -239,7 +241,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
             s.q[lane] = REV ? fexp(cs.cum) : cs.w;
             if (lane == kQ - 1) {
                 s.decay = fexp(cs.cum);
-                if (!REV && a.nseg > 1) a.chunk_lam[bh * nch + c] = cs.cum;  // for the correction
+                if (a.nseg > 1) {  // for the correction: the decay from the segment's boundary to this chunk
+                    a.chunk_dec[bh * nch + c] = fexp(run);
+                    run += cs.cum;
+                }
             }
         }
         // ---- the matrix entering this chunk, stored ----
@@ -276,6 +281,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
         }
         __syncthreads();  // every wave is done with u, v, q before the next chunk stages over them
     }
+    if (a.nseg > 1 && tid == kQ - 1) a.seg_lam[bh * a.nseg + seg] = run;
     // the final state (pass 1) or dh0 (pass 2) from the segment that reaches it, else the segment's own end
     const bool at_end = REV ? seg == 0 : c_end == nch;
     float* const last = at_end ? (REV ? (a.dh0 ? a.dh0 + bh * PN : nullptr) : store_base + nch * PN)
@@ -288,48 +294,56 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
     }
 }
 
-// The chains' time segments joined, one thread per (batch, sub-head, item of
-// the P x N matrix), from the segment whose walk was exact outwards: the true
-// matrix T at a segment's outer boundary (the state entering it, the adjoint
-// leaving it) is the neighbour's own end value plus that neighbour's decay
-// times the neighbour's T, and every matrix stored inside the segment gains
-// T times the decay between the boundary and it (chunk log-decays lambda_c,
-// summed).  Pass 1 also completes the final state, pass 2 dh0.
+// The chains' time segments joined: walking the segments outwards from the
+// one whose walk was exact, the true matrix T at a segment's outer boundary
+// (the state entering it, the adjoint leaving it) is the neighbour's own end
+// value plus the neighbour's decay (exp of its chunks' log-decays, summed)
+// times the neighbour's T.  One thread per (batch, sub-head, item of the
+// P x N matrix) carries T and leaves each segment's T in place of the
+// segment's own end value (read a segment ahead); pass 1 also completes the
+// final state, pass 2 dh0.
 template <int N, bool REV>
-__global__ __launch_bounds__(256) void ssd_chain_fix_kernel(SsdBwdArgs a) {
+__global__ __launch_bounds__(256) void ssd_chain_carry_kernel(SsdBwdArgs a) {
     const int64_t PN = kP * N, nch = (a.L + kQ - 1) / kQ;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= a.B * a.H * PN) return;
     const int64_t bh = i / PN, e = i % PN;
-    const float* lam = a.chunk_lam + bh * nch;
-    const float* own = a.seg_state + bh * a.nseg * PN + e;  // each segment's own end state / start adjoint
-    float* const m = (REV ? a.dstates + bh * nch * PN : a.states + bh * (nch + 1) * PN) + e;
-    float T = 0.0f;  // the first segment walked (exact) needs nothing
+    const float* __restrict__ lam = a.seg_lam + bh * a.nseg;
+    float* __restrict__ seg_t = a.seg_state + bh * a.nseg * PN + e;
+    float T = 0.0f;  // the first segment walked is exact
+    auto seg_of = [&](int64_t q) { return REV ? a.nseg - 1 - q : q; };
+    float own_next = seg_t[seg_of(0) * PN];
     for (int64_t q = 0; q < a.nseg; ++q) {
-        const int64_t seg = REV ? a.nseg - 1 - q : q;
-        const int64_t c0 = seg * a.seg_chunks, c1 = imin64(nch, c0 + a.seg_chunks);
-        float sum = 0.0f;  // log-decay from the segment's outer boundary to the current chunk
-        if (REV) {
-            for (int64_t c = c1 - 1; c >= c0; --c) {
-                if (q > 0) m[c * PN] += fexp(sum) * T;
-                sum += lam[c];
-            }
-        } else {
-            for (int64_t c = c0; c < c1; ++c) {
-                if (q > 0) m[c * PN] += fexp(sum) * T;
-                sum += lam[c];
-            }
-        }
-        // T of the next segment: this one's own end value plus its whole decay times its T
-        const bool last_walked = q == a.nseg - 1;
-        float* const end = last_walked ? (REV ? (a.dh0 ? a.dh0 + bh * PN + e : nullptr) : m + nch * PN)
-                                       : nullptr;
-        if (end) {
-            *end += fexp(sum) * T;
-        } else if (!last_walked) {
-            T = own[seg * PN] + fexp(sum) * T;
+        const int64_t seg = seg_of(q);
+        const float own = own_next;
+        if (q + 1 < a.nseg) own_next = seg_t[seg_of(q + 1) * PN];
+        const float decay = fexp(lam[seg]);
+        seg_t[seg * PN] = T;
+        if (q < a.nseg - 1) {
+            T = own + decay * T;
+        } else {  // the last segment walked: its end value is the final state (pass 1) or dh0 (pass 2)
+            float* const end = REV ? (a.dh0 ? a.dh0 + bh * PN + e : nullptr)
+                                   : a.states + (bh * (nch + 1) + nch) * PN + e;
+            if (end) *end += decay * T;
         }
     }
+}
+
+// Every matrix stored inside a segment other than the exact one gains its
+// segment's boundary matrix T times the decay between them: one workgroup
+// per (batch, sub-head, chunk), its threads over the P x N items.
+template <int N, bool REV>
+__global__ __launch_bounds__(256) void ssd_chain_fix_kernel(SsdBwdArgs a) {
+    constexpr int64_t PN = kP * N;
+    const int64_t nch = (a.L + kQ - 1) / kQ;
+    const int64_t bh = blockIdx.x / nch, c = blockIdx.x % nch;
+    const int64_t seg = c / a.seg_chunks;
+    if (seg == (REV ? a.nseg - 1 : 0)) return;  // the exact segment
+    const float d = a.chunk_dec[bh * nch + c];
+    const float* __restrict__ t = a.seg_state + (bh * a.nseg + seg) * PN;
+    float* __restrict__ m = (REV ? a.dstates + (bh * nch + c) * PN : a.states + (bh * (nch + 1) + c) * PN);
+#pragma unroll 4
+    for (int64_t e = threadIdx.x; e < PN; e += 256) m[e] += d * t[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -844,11 +858,18 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_groups_kernel(SsdBwdArgs a
 template <class T, int N>
 hipError_t launch_bwd_typed(const SsdBwdArgs& a, hipStream_t st) {
     const dim3 chains((unsigned)(a.B * a.H * a.nseg));
-    const dim3 fix((unsigned)((a.B * a.H * kP * N + 255) / 256));
+    const dim3 carry((unsigned)((a.B * a.H * kP * N + 255) / 256));
+    const dim3 fix((unsigned)(a.B * a.H * ((a.L + kQ - 1) / kQ)));
     hipLaunchKernelGGL((ssd_chain_kernel<T, N, false>), chains, dim3(kThreads), 0, st, a);
-    if (a.nseg > 1) hipLaunchKernelGGL((ssd_chain_fix_kernel<N, false>), fix, dim3(256), 0, st, a);
+    if (a.nseg > 1) {
+        hipLaunchKernelGGL((ssd_chain_carry_kernel<N, false>), carry, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((ssd_chain_fix_kernel<N, false>), fix, dim3(256), 0, st, a);
+    }
     hipLaunchKernelGGL((ssd_chain_kernel<T, N, true>), chains, dim3(kThreads), 0, st, a);
-    if (a.nseg > 1) hipLaunchKernelGGL((ssd_chain_fix_kernel<N, true>), fix, dim3(256), 0, st, a);
+    if (a.nseg > 1) {
+        hipLaunchKernelGGL((ssd_chain_carry_kernel<N, true>), carry, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((ssd_chain_fix_kernel<N, true>), fix, dim3(256), 0, st, a);
+    }
     const int64_t nch = (a.L + kQ - 1) / kQ;
     hipLaunchKernelGGL((ssd_bwd_chunk_kernel<T, N>), dim3((unsigned)(a.B * nch * a.groups)), dim3(kThreads), 0, st,
                        a);
