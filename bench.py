@@ -30,7 +30,8 @@ float32 arithmetic), inputs resident in HBM.  Prints one JSON line:
 front end (x in place of u, d_conv = 4) and that front end's backward, the
 recurrent step at the 2.8B layer's width (B=4, D=5120, N=16: one decode step
 per call from Python, so the host's launch overhead, not the kernel, sets this
-rate; the kernel's own duration is in the kernel trace), the same step at
+rate; the kernel's own duration is in the kernel trace; also over buffers
+bound once, per call and per step inside a replayed graph), the same step at
 B = 64 and 256 (batched decode, where the state's read and write set the
 rate), the step behind the conv front end at B = 256, a 4-token forward at
 B = 256 (the short-sequence path) and the Mamba-2 (SSD) layers.
@@ -392,6 +393,48 @@ def time_step(mssm, torch, w, reps=200, batch=None):
     return us, nbytes / (us * 1e-6) / 1e9
 
 
+def time_step_bound(mssm, torch, w, reps=200, graph_steps=32):
+    """The decode step over buffers bound once (binding.Stepper): us per call
+    from Python, and us per step inside a replayed graph of `graph_steps`
+    steps (no host work per step)."""
+    inp = workloads.make_inputs(workloads.custom(w.B, 1, w.D, w.N, w.dtype, seed=w.seed))
+    t = workloads.to_torch(inp, "cuda")
+    b = {k: t[k][:, 0].contiguous() for k in ("u", "delta", "Bm", "Cm", "z")}
+    state = torch.zeros((w.B, w.D, w.N), dtype=torch.float32, device="cuda")
+
+    def bound():
+        return mssm.Stepper(b["u"], b["delta"], t["A"], b["Bm"], b["Cm"], state, t["Dskip"], b["z"], t["dt_bias"])
+
+    st = bound()
+    for _ in range(10):
+        st()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        st()
+    e1.record()
+    torch.cuda.synchronize()
+    per_call = e0.elapsed_time(e1) / reps * 1e3
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        gs = bound()
+        for _ in range(graph_steps):
+            gs()
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    n = 20
+    e0.record()
+    for _ in range(n):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return per_call, e0.elapsed_time(e1) / (n * graph_steps) * 1e3
+
+
 def cpu_baseline(w: workloads.Workload, target_s: float = 12.0):
     """Oracle (float64 C, OpenMP) on a channel sample of the workload."""
     import oracle
@@ -558,6 +601,9 @@ def main():
         st_us, st_gbs = time_step(mssm, torch, w)
         out.setdefault("extra", {})["step_us_per_call"] = round(st_us, 2)
         out["extra"]["step_GBs_per_call"] = round(st_gbs, 1)
+        bound_us, graph_us = time_step_bound(mssm, torch, w)  # bound buffers; and inside a replayed graph
+        out["extra"]["step_us_per_call_bound"] = round(bound_us, 2)
+        out["extra"]["step_us_in_graph"] = round(graph_us, 2)
         for bb in (64, 256):  # batched decode: the state read and write dominate
             st_us, st_gbs = time_step(mssm, torch, w, reps=100, batch=bb)
             out["extra"][f"step_B{bb}_us_per_call"] = round(st_us, 2)

@@ -377,6 +377,46 @@ def step(u_t, delta_t, A, Bm_t, Cm_t, state, Dskip=None, z_t=None, dt_bias=None,
     return y_t
 
 
+class Stepper:
+    """The recurrent step over fixed buffers, for decode loops: the buffers are
+    checked and their addresses marshalled once, so that a call is one C call
+    (mssm_step) on the stream current at construction.  The caller writes
+    each token's inputs into u_t, delta_t, Bm_t, Cm_t (and z_t) in place; the
+    step updates state and writes y_t.  Arguments as step(); the buffers must
+    outlive the Stepper.  A call enqueues no allocation or memset, so it can
+    be captured in a CUDA/HIP graph."""
+
+    def __init__(self, u_t, delta_t, A, Bm_t, Cm_t, state, Dskip=None, z_t=None, dt_bias=None,
+                 delta_softplus=True, y_t=None):
+        act = u_t.dtype
+        B, D = u_t.shape
+        N = A.shape[1]
+        _req(u_t, "u_t", (B, D), act)
+        _req(delta_t, "delta_t", (B, D), act)
+        _req(A, "A", (D, N), torch.float32)
+        _req(Bm_t, "Bm_t", (B, N), act)
+        _req(Cm_t, "Cm_t", (B, N), act)
+        _req(state, "state", (B, D, N), torch.float32)
+        _opt(Dskip, "Dskip", (D,), torch.float32)
+        _opt(z_t, "z_t", (B, D), act)
+        _opt(dt_bias, "dt_bias", (D,), torch.float32)
+        if y_t is None:
+            y_t = torch.empty((B, D), dtype=act, device=u_t.device)
+        _req(y_t, "y_t", (B, D), act)
+        self.y_t = y_t
+        self._keep = (u_t, delta_t, A, Bm_t, Cm_t, state, Dskip, z_t, dt_bias, y_t)
+        self._prob = problem(B, 1, D, N, _dtype_code(u_t), delta_softplus)
+        self._args = (ctypes.byref(self._prob), _ptr(u_t), _ptr(delta_t), _ptr(A), _ptr(Bm_t), _ptr(Cm_t),
+                      _ptr(Dskip), _ptr(z_t), _ptr(dt_bias), _ptr(state), _ptr(y_t), _stream(u_t.device))
+        self._fn = lib.mssm_step
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != 0:
+            raise MssmError(status, lib)
+        return self.y_t
+
+
 def conv_step(x_t, conv_w, conv_state, delta_t, A, Bm_t, Cm_t, state, Dskip=None, z_t=None, dt_bias=None,
               conv_b=None, delta_softplus=True, y_t=None):
     """One token through the conv1d + SiLU front end and the recurrent step.

@@ -177,3 +177,56 @@ def test_short_path_few_rows(mssm, shape, dtype):
     yr, hr = run_oracle_fwd(oracle, inp, h0)
     assert fwd_err(to_np(y), yr) <= FWD_TOL[dtype]
     assert fwd_err(to_np(hf), hr) <= STATE_TOL
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stepper_over_bound_buffers_and_in_a_graph(mssm, dtype):
+    # Stepper: the step over buffers bound once, each token's inputs copied into them in place.  Eager calls
+    # equal step(); a captured graph of 4 steps over the bound buffers, replayed 3 times (new inputs each time)
+    # with eager work and checks between replays, equals 4 eager steps from the same state, bit for bit
+    w = workloads.custom(4, 16, 96, 16, dtype, seed=91)
+    print(f"[stepper] {w}", flush=True)
+    inp = workloads.make_inputs(w)
+    t = gpu_inputs(inp)
+    tok = lambda k, i: t[k][:, i].contiguous()  # noqa: E731
+    ref_state = torch.zeros((w.B, w.D, w.N), device="cuda")
+    ref = [mssm.step(tok("u", i), tok("delta", i), t["A"], tok("Bm", i), tok("Cm", i), ref_state, t["Dskip"],
+                     tok("z", i), t["dt_bias"]).clone() for i in range(4)]
+    bufs = {k: torch.empty_like(tok(k, 0)) for k in ("u", "delta", "Bm", "Cm", "z")}
+    state = torch.zeros((w.B, w.D, w.N), device="cuda")
+
+    def feed(i):
+        for k, b in bufs.items():
+            b.copy_(tok(k, i))
+
+    def bound():
+        return mssm.Stepper(bufs["u"], bufs["delta"], t["A"], bufs["Bm"], bufs["Cm"], state, t["Dskip"],
+                            bufs["z"], t["dt_bias"])
+
+    st = bound()
+    for i in range(4):
+        feed(i)
+        assert torch.equal(st(), ref[i]), i
+    assert torch.equal(state, ref_state)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    outs = [torch.empty_like(ref[0]) for _ in range(4)]
+    with torch.cuda.graph(g, stream=side):
+        gs = bound()  # binds the capture stream
+        for j in range(4):
+            outs[j].copy_(gs())
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        feed(4 + r)
+        check_state = state.clone()
+        check = [mssm.step(bufs["u"], bufs["delta"], t["A"], bufs["Bm"], bufs["Cm"], check_state, t["Dskip"],
+                           bufs["z"], t["dt_bias"]).clone() for _ in range(4)]
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for j in range(4):
+            assert torch.equal(outs[j], check[j]), (r, j)
+        assert torch.equal(state, check_state), r
