@@ -36,6 +36,8 @@ B = 64 and 256 (batched decode, where the state's read and write set the
 rate), the step behind the conv front end at B = 256, a 4-token forward at
 B = 256 (the short-sequence path) and the Mamba-2 (SSD) layers.
 ``--no-configs`` leaves out the other workloads (the headline alone).
+``--ssd`` times only the Mamba-2 (SSD) layers of ``--extra`` and prints them
+as their own JSON line (no headline).
 ``--copy-probe`` runs a plain device copy of 1 GiB first (counter calibration).
 """
 from __future__ import annotations
@@ -364,6 +366,21 @@ def time_ssd(mssm, torch, B, L, H, N, reps=20, backward=False):
     return us, flops
 
 
+def ssd_layers(mssm, torch):
+    """The Mamba-2 (SSD) layers, float32 on the matrix cores: the 2.7B shape
+    (80 heads of 64, d_state 128, B = 8, L = 2048) and the batch-1 prefill of
+    a 24-head layer (time segments scanned in parallel), forward and backward
+    (all eight gradients): median us per call."""
+    r = {}
+    ssd_us, ssd_flops = time_ssd(mssm, torch, 8, 2048, 80, 128)
+    r["ssd_fwd_H80_N128_B8_L2048_us"] = round(ssd_us, 1)
+    r["ssd_fwd_dense_TFLOPs"] = round(ssd_flops / ssd_us / 1e6, 1)
+    r["ssd_fwd_H24_N128_B1_L2048_us"] = round(time_ssd(mssm, torch, 1, 2048, 24, 128)[0], 1)
+    r["ssd_bwd_H80_N128_B8_L2048_us"] = round(time_ssd(mssm, torch, 8, 2048, 80, 128, 5, True)[0], 1)
+    r["ssd_bwd_H24_N128_B1_L2048_us"] = round(time_ssd(mssm, torch, 1, 2048, 24, 128, 10, True)[0], 1)
+    return r
+
+
 def time_step(mssm, torch, w, reps=200, batch=None):
     """One recurrent step (decode) at the workload's width: (B, D) inputs, the
     (B, D, N) float32 state updated in place; `batch` overrides B (batched
@@ -513,6 +530,7 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="only the headline workload")
     ap.add_argument("--extra", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--ssd", action="store_true", help="only the Mamba-2 (SSD) layers (their own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the selective-scan library has no multi-GPU path; "
@@ -524,6 +542,9 @@ def main():
 
     import selective_state_space_mssm_amd as mssm
 
+    if args.ssd:
+        print(json.dumps({"ssd": ssd_layers(mssm, torch)}), flush=True)
+        return
     if args.copy_probe:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -614,16 +635,7 @@ def main():
         _, sl, _ = time_fwd(mssm, torch, sw, 30, 3)
         out["extra"]["short_fwd_B256_L4_us"] = round(float(np.median(sl)) * 1e3, 1)
         log("extra: conv backward, decode steps and short-sequence forward timed")
-        # Mamba-2 (SSD) layer of the 2.7B shape: 80 heads of 64, d_state 128, B = 8, L = 2048, float32 on MFMA
-        ssd_us, ssd_flops = time_ssd(mssm, torch, 8, 2048, 80, 128)
-        out["extra"]["ssd_fwd_H80_N128_B8_L2048_us"] = round(ssd_us, 1)
-        out["extra"]["ssd_fwd_dense_TFLOPs"] = round(ssd_flops / ssd_us / 1e6, 1)
-        # batch-1 prefill of a 24-head layer (Mamba-2 130M shape): time segments scanned in parallel
-        ssd_us, _ = time_ssd(mssm, torch, 1, 2048, 24, 128)
-        out["extra"]["ssd_fwd_H24_N128_B1_L2048_us"] = round(ssd_us, 1)
-        # the SSD backward (all eight gradients) at both shapes
-        out["extra"]["ssd_bwd_H80_N128_B8_L2048_us"] = round(time_ssd(mssm, torch, 8, 2048, 80, 128, 5, True)[0], 1)
-        out["extra"]["ssd_bwd_H24_N128_B1_L2048_us"] = round(time_ssd(mssm, torch, 1, 2048, 24, 128, 10, True)[0], 1)
+        out["extra"].update(ssd_layers(mssm, torch))
         log("extra: SSD forwards and backwards timed")
     if not args.no_cpu_baseline:
         log("cpu baseline: the oracle on the host")
