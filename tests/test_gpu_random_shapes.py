@@ -157,9 +157,11 @@ def test_random_ssd(mssm_lib, i):
     N = int(rng.choice([64, 128]))
     dtype = "bf16" if rng.random() < 0.5 else "f32"
     use_d, use_bias, h0, sp = (bool(rng.random() < 0.6) for _ in range(4))
-    print(f"[random ssd {i}] B={B} L={L} H={H} N={N} {dtype} D={use_d} bias={use_bias} h0={h0} softplus={sp}",
+    P = int(rng.choice([64, 64, 64, 128, 256]))  # head dim (drawn last: the draws above are those of P = 64 only)
+    L = min(L, max(1, 400000 * 64 // (B * H * P)))
+    print(f"[random ssd {i}] B={B} L={L} H={H} P={P} N={N} {dtype} D={use_d} bias={use_bias} h0={h0} softplus={sp}",
           flush=True)
-    inp = workloads.ssd_inputs(B, L, H, 64, N, seed=6000 + i)
+    inp = workloads.ssd_inputs(B, L, H, P, N, seed=6000 + i)
     if not sp:  # without softplus the raw step dt + dt_bias must be >= 0: no (negative) bias, |dt| scaled down
         inp["dt"] = np.abs(inp["dt"]) * np.float32(0.05)
         use_bias = False
@@ -167,7 +169,7 @@ def test_random_ssd(mssm_lib, i):
     if dtype == "bf16":
         for k in ("x", "dt", "Bm", "Cm"):
             t[k] = t[k].to(torch.bfloat16)
-    h0n = rng.standard_normal((B, H, 64, N)).astype(np.float32) if h0 else None
+    h0n = rng.standard_normal((B, H, P, N)).astype(np.float32) if h0 else None
     y, hf = mssm_lib.ssd_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"] if use_d else None,
                              t["dt_bias"] if use_bias else None, torch.from_numpy(h0n).cuda() if h0 else None,
                              delta_softplus=sp)
@@ -177,3 +179,46 @@ def test_random_ssd(mssm_lib, i):
                             inp["dt_bias"] if use_bias else None, h0n, softplus=sp)
     assert fwd_err(to_np(y), yr) <= FWD_TOL[dtype]
     assert fwd_err(to_np(hf), hr) <= STATE_TOL
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_ssd_backward(mssm_lib, i):
+    # Mamba-2 (SSD) backward: head dims 64..256, both state sizes and activation types, optional inputs, h0,
+    # dh_final and the softplus flag drawn; sequences long enough for the chains' time segments (few pairs)
+    # and the head groups of the chunk pass (few (batch, chunk) pairs) to come up
+    rng = np.random.default_rng(7000 + i)
+    B, H = int(rng.integers(1, 4)), int(rng.integers(1, 20))
+    P = int(rng.choice([64, 64, 128, 192, 256]))
+    L = int(rng.choice([rng.integers(1, 65), rng.integers(65, 400), rng.integers(400, 1500)]))
+    L = min(L, max(1, 60000 * 64 // (B * H * P)))  # the float64 adjoint keeps the whole state history
+    N = int(rng.choice([64, 128]))
+    dtype = "bf16" if rng.random() < 0.5 else "f32"
+    use_d, use_bias, h0, dhf, sp = (bool(rng.random() < 0.6) for _ in range(5))
+    print(f"[random ssd bwd {i}] B={B} L={L} H={H} P={P} N={N} {dtype} D={use_d} bias={use_bias} h0={h0} "
+          f"dh_final={dhf} softplus={sp}", flush=True)
+    inp = workloads.ssd_inputs(B, L, H, P, N, seed=7100 + i)
+    inp["Dskip"] = rng.uniform(-2.0, 2.0, size=H).astype(np.float32)
+    if not sp:
+        inp["dt"] = np.abs(inp["dt"]) * np.float32(0.05)
+        use_bias = False
+    inp["dy"] = rng.standard_normal((B, L, H, P)).astype(np.float32)
+    t = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    if dtype == "bf16":
+        for k in ("x", "dt", "Bm", "Cm", "dy"):
+            t[k] = t[k].to(torch.bfloat16)
+    h0n = rng.standard_normal((B, H, P, N)).astype(np.float32) if h0 else None
+    dhn = rng.standard_normal((B, H, P, N)).astype(np.float32) if dhf else None
+    cu = lambda a: None if a is None else torch.from_numpy(a).cuda()  # noqa: E731
+    g = mssm_lib.ssd_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["dy"], t["Dskip"] if use_d else None,
+                         t["dt_bias"] if use_bias else None, cu(h0n), cu(dhn), delta_softplus=sp)
+    torch.cuda.synchronize()
+    r = {k: t[k].float().cpu().numpy() for k in ("x", "dt", "Bm", "Cm", "dy")}
+    ref = oracle.ssd_bwd(r["x"], r["dt"], inp["A"], r["Bm"], r["Cm"], r["dy"], Dskip=inp["Dskip"] if use_d else None,
+                         dt_bias=inp["dt_bias"] if use_bias else None, h0=h0n, dh_final=dhn, softplus=sp)
+    tol = GRAD_TOL[dtype]
+    keys = ["dx", "ddt", "dA", "dB", "dC", "dD", "ddt_bias", "dh0"]
+    if L == 1 and not h0:
+        keys.remove("dA")  # exactly 0 in the oracle, a difference of equal sums on the GPU (judged in test_gpu_ssd_bwd)
+    errs = {k: grad_err(to_np(g[k]), ref[k]) for k in keys}
+    print("grad errs: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    assert all(v <= tol for v in errs.values()), errs
