@@ -238,12 +238,12 @@ __global__ __launch_bounds__(kThreads) void ssd_chain_kernel(SsdBwdArgs a) {
         }
         if (wv == 0) {
             const ChunkScan cs = chunk_scan(g.dt, nv, bias, Ah, a.softplus, lane);
-            s.q[lane] = REV ? fexp(cs.cum) : cs.w;
+            s.q[lane] = REV ? fexp(cs.cum + cs.lo) : cs.w;
             if (lane == kQ - 1) {
-                s.decay = fexp(cs.cum);
+                s.decay = fexp(cs.cum + cs.lo);
                 if (a.nseg > 1) {  // for the correction: the decay from the segment's boundary to this chunk
                     a.chunk_dec[bh * nch + c] = fexp(run);
-                    run += cs.cum;
+                    run += cs.cum + cs.lo;
                 }
             }
         }
@@ -365,7 +365,8 @@ struct alignas(16) BwdSmem {
     float dst[N][kSX];   // dS^T: dst[n][p] = dS[p][n]
     float mm[kQ][kSM];
     float d3[kQ];
-    float cum[kQ];
+    float cum[kQ];       // chunk-local cumulative Delta * A_h, as cum + cum_lo (ssdk::chunk_scan)
+    float cum_lo[kQ];
     float dlt[kQ];
     float ecum[kQ];      // exp(cum_i)
     float elast[kQ];     // exp(cum_last - cum_j)
@@ -373,6 +374,7 @@ struct alignas(16) BwdSmem {
     float red_r[2][kQ];       // per p-block row sums of X o V
     float red_d[2][4];        // per wave sums of dY o X (double-buffered by head parity)
     float red_o[2][4];        // per wave parts of <dS, S_out> (double-buffered by head parity)
+    float dcd[kQ];            // sum over the group's heads of Delta_i (dY_i . x_i): dC's same-step terms / Bm_i
     float junk[kThreads];     // target of the masked operands' writes that belong to no operand
 };
 
@@ -515,6 +517,7 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
     }
 
     float sig = 1.0f, dlt_l = 0.0f, cumd = 0.0f;  // wave 3: this head's sigmoid factor, Delta, sum_{s<=t} Delta_s
+    float dcd = 0.0f;  // wave 3: sum over the heads so far of Delta_t (dY_t . x_t)
     int par = 0;
     for (int64_t h = h_begin; h < h_end; ++h, par ^= 1) {
         const int64_t hd = h / a.hsub;  // the head this sub-head belongs to
@@ -546,10 +549,12 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             dlt_l = cs.d;
             cumd = wave_prefix_sum(cs.d, lane);
             s.cum[lane] = cs.cum;
+            s.cum_lo[lane] = cs.lo;
             s.dlt[lane] = cs.d;
-            s.ecum[lane] = fexp(cs.cum);
+            s.ecum[lane] = fexp(cs.cum + cs.lo);
             const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs.cum), 63));
-            s.elast[lane] = fexp(last - cs.cum);
+            const float last_lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs.lo), 63));
+            s.elast[lane] = fexp((last - cs.cum) + (last_lo - cs.lo));
         }
         __syncthreads();
 
@@ -563,17 +568,19 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
                 av = yf[oy + 2 * k];
                 bv = xf[ox + 2 * k];
             });
-            const int j = gtj * 32 + l32;
-            const float cj = s.cum[j];
-            float ci[16];
+            // (opaque: the item addresses below are formed per head, not kept in registers across the loop)
+            const int j = opaque(gtj * 32 + l32);
+            const float cj = s.cum[j], cjl = s.cum_lo[j];
+            float ci[16], cil[16];
             acc_row_cum(s.cum, gti, hl, ci);
+            acc_row_cum(s.cum_lo, gti, hl, cil);
             // M2[j][i] = G[i][j] f for i >= j, M3[j][i] = dYX[i][j] f for i > j (stored transposed) and on
             // the diagonal (d3), f = exp(cum_i - cum_j) (1 on the diagonal); the items with i < j belong to
             // neither and go to a junk word, so that every lane writes twice per item without a branch
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int i = gti * 32 + acc_row(r, hl);
-                const float f = fexp(ci[r] - cj);
+                const float f = fexp((ci[r] - cj) + (cil[r] - cjl));
                 float* p2 = i >= j ? &s.mm[j][i] : &s.junk[tid];
                 float* p3 = i > j ? &s.mm[i][j] : i == j ? &s.d3[j] : &s.junk[tid];
                 *p2 = Gt[r] * f;
@@ -606,24 +613,28 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             const int i = rb * 32 + l32;
             const int om = opaque(i * SM + hl);
             const int ob = opaque(hl * SB + nb * 32 + l32);
+            // (the diagonal k = i is left out here and added below: see the row sums)
             auto ld_m1 = [&](int kb) {
                 return [&, kb](int k, float& av, float& a2, float& bv) {
                     const int kk = kb * 32 + 2 * k + hl;
                     const float m = mf[om + kb * 32 + 2 * k];
-                    av = kb < rb ? m : (kk < i ? m : (kk == i ? s.d3[i] : 0.0f));
+                    av = kb < rb ? m : (kk < i ? m : 0.0f);
                     a2 = s.dlt[kk];
                     bv = bf[ob + (kb * 32 + 2 * k) * SB];
                 };
             };
             if (rb == 1) acc = mfma_chain_scaled<16>(acc, ld_m1(0), [](int) {});
             acc = mfma_chain_scaled<16>(acc, ld_m1(rb), [](int) {});
-            dCacc[t] += acc;
-            // row sums of C o dC over this n-block
+            // row sums of C o dC over this n-block, without dC's same-step term Delta_i (dY_i . x_i) B_i: in
+            // dcum_i = C_i . dC_i - Delta_i x_i . V_i that term cancels exactly against Delta_i (x_i . dY_i)
+            // G_ii of the second sum, and with a large step and a fast decay it would dominate both, leaving
+            // dcum to the rounding of their difference
             f32x16 cdc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) cdc[r] = acc[r] * s.c[rb * 32 + acc_row(r, hl)][nb * 32 + l32];
             const float rs = tile_row_sums(cdc, lane);
             if ((l32 & 1) == 0) s.red_c[nb][rb * 32 + acc_row((l32 >> 1) & 15, hl)] = rs;
+            dCacc[t] += acc;  // the same-step terms, summed over the group's heads, are added at the end
         }
         // <dS, S_in> over this wave's n-block (N = 64: waves 2 and 3 hold the blocks of waves 0 and 1)
         if (wv < NB) {
@@ -696,7 +707,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
                 acc[r] *= el[r];
                 odot += dl[r] * acc[r] * s.x[vjb * 32 + acc_row(r, hl)][px];
             }
-            // M2[j][k] dY[k][p] over k >= j: k-blocks vjb .. 1, the first one the diagonal block
+            // M2[j][k] dY[k][p] over k > j: k-blocks vjb .. 1, the first one the diagonal block (whose own
+            // diagonal, G_jj dY_j, is added after the row sums: see dC's)
             const int j = vjb * 32 + l32;
             const int om = opaque(j * SM + hl);
             const int oy = opaque(hl * SX + vpb * 32 + l32);
@@ -704,13 +716,14 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
                 return [&, kb](int k, float& av, float& bv) {
                     const int kk = kb * 32 + 2 * k + hl;
                     const float m = mf[om + kb * 32 + 2 * k];
-                    av = kb > vjb ? m : (kk >= j ? m : 0.0f);
+                    av = kb > vjb ? m : (kk > j ? m : 0.0f);
                     bv = yf[oy + (kb * 32 + 2 * k) * SX];
                 };
             };
             acc = mfma_chain<16>(acc, ld_m2(vjb));
             if (vjb == 0) acc = mfma_chain<16>(acc, ld_m2(1));
-            // dX, rows past the end dropped by the resource
+            // dX = Delta_j (V without its same-step term) + (Delta_j G_jj + Dskip) dY_j (rows past the end
+            // dropped by the resource); row sums of X o V without the same-step term
             const int p = vpb * 32 + l32;
             const auto rx = make_rsrc(static_cast<T*>(a.dx) + (bi * L + t0) * H * kP,
                                       (uint32_t)(nv * H * kP * sizeof(T)));
@@ -718,7 +731,8 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int jr = vjb * 32 + acc_row(r, hl);
-                store1<T>(dl[r] * acc[r] + Dh * s.dy[jr][p], rx, (int)((jr * H + h) * kP + p));
+                const float dyj = s.dy[jr][p];
+                store1<T>(dl[r] * (acc[r] + s.mm[jr][jr] * dyj) + Dh * dyj, rx, (int)((jr * H + h) * kP + p));
                 xv[r] = s.x[jr][p] * acc[r];
             }
             const float rs = tile_row_sums(xv, lane);
@@ -733,12 +747,17 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
             float cdc = 0.0f;
 #pragma unroll
             for (int q = 0; q < NB; ++q) cdc += s.red_c[q][lane];
+            // both row sums leave out the same-step terms (equal, they cancel in dcum); r_t, the direct
+            // derivative by Delta_t, has it: G_tt (x_t . dY_t), M2's and d3's diagonals
             const float r = s.red_r[0][lane] + s.red_r[1][lane];
+            const float d3t = s.d3[lane];
+            const float r_full = r + s.mm[lane][lane] * d3t;
+            dcd += dlt_l * d3t;
             const float dot = s.red_o[par][0] + s.red_o[par][1] + s.red_o[par][2] + s.red_o[par][3];
             const float dcum = cdc - dlt_l * r + (lane == kQ - 1 ? dot : 0.0f);
             const float incl = wave_prefix_sum(dcum, lane);
             const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
-            const float dDelta = Ah * (total - incl + dcum) + r;
+            const float dDelta = Ah * (total - incl + dcum) + r_full;
             const float ddt = dDelta * sig;
             if (a.ddt_ws) {  // sub-heads of one head: summed per head in pass 4
                 const auto rt = make_rsrc(a.ddt_ws + (bi * L + t0) * H, (uint32_t)(nv * H * sizeof(float)));
@@ -760,7 +779,19 @@ __global__ __launch_bounds__(kThreads) void ssd_bwd_chunk_kernel(SsdBwdArgs a) {
         // red_d of the other parity; wave 3 rewrites the step quantities after its own reads
     }
 
-    // ---- dB, dC of the chunk summed over this group's heads ----
+    // ---- dB, dC of the chunk summed over this group's heads; dC's same-step terms Bm_i dcd_i first ----
+    __syncthreads();  // every wave is past its last reads of the head's operands (wave 3 past its dcd)
+    if (wv == 3) s.dcd[lane] = dcd;
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NTC; ++t) {
+        const int rb = tile_rb(t);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = rb * 32 + acc_row(r, hl);
+            dCacc[t][r] += s.dcd[i] * s.b[i][nb * 32 + l32];
+        }
+    }
     const int64_t row0 = bi * L + t0;
     if (a.groups == 1) {
         const auto rb_ = make_rsrc(static_cast<T*>(a.dB) + row0 * N, (uint32_t)(nv * N * sizeof(T)));

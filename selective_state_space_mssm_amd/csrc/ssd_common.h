@@ -156,22 +156,70 @@ __device__ __forceinline__ float wave_prefix_sum(float v, int lane) {
     return v + (row >= 1 ? t0 : 0.0f) + (row >= 2 ? t1 : 0.0f) + (row >= 3 ? t2 : 0.0f);
 }
 
+// Inclusive prefix sum over the 64 lanes of a value held as an unevaluated
+// sum hi + lo, each addition exact: Knuth's TwoSum gives the rounding error
+// of hi + hi' exactly, and it joins the lo parts.  cum_i - cum_j for two
+// steps of a chunk is then (hi_i - hi_j) + (lo_i - lo_j): when the chunk's
+// log-decay is large (|cum| in the thousands) and the steps between i and j
+// are tiny, hi_i - hi_j is exact (Sterbenz) and the difference keeps its
+// digits, where a plain float32 prefix sum would leave an error of
+// ulp(cum) -- a relative error of ulp(cum) in exp(cum_i - cum_j).
+// (No contraction anywhere here: an addend fused with the multiply that made
+// it into one fma would no longer be the value the error terms refer to.)
+__device__ __forceinline__ void two_sum(float a, float b, float& s, float& e) {
+#pragma clang fp contract(off)
+    s = a + b;
+    const float bb = s - a;
+    e = (a - (s - bb)) + (b - bb);
+}
+__device__ __forceinline__ void add_df(float& hi, float& lo, float h2, float l2) {
+#pragma clang fp contract(off)
+    float s, e;
+    two_sum(hi, h2, s, e);
+    hi = s;
+    lo = lo + l2 + e;
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_shr(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ void wave_prefix_sum_df(float& hi, float& lo, int lane) {
+    add_df(hi, lo, dpp_shr<0x111>(hi), dpp_shr<0x111>(lo));
+    add_df(hi, lo, dpp_shr<0x112>(hi), dpp_shr<0x112>(lo));
+    add_df(hi, lo, dpp_shr<0x114>(hi), dpp_shr<0x114>(lo));
+    add_df(hi, lo, dpp_shr<0x118>(hi), dpp_shr<0x118>(lo));
+    const int row = lane >> 4;
+    float th = 0.0f, tl = 0.0f;  // the totals of the earlier rows, added in row order
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const float h2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hi), 16 * q + 15));
+        const float l2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lo), 16 * q + 15));
+        if (row > q) add_df(th, tl, h2, l2);
+    }
+    add_df(hi, lo, th, tl);
+}
+
 // One chunk's step quantities, lane t = step t of the chunk: Delta_t (0 for
 // steps past the segment end, nv valid steps), the chunk-local cumulative
-// log-decay cum_t = sum_{s <= t} Delta_s A_h, and the state weight
+// log-decay cum_t = sum_{s <= t} Delta_s A_h as hi + lo (wave_prefix_sum_df;
+// each product Delta_s A_h split exactly by an fma), and the state weight
 // w_t = exp(cum_last - cum_t) Delta_t.
 struct ChunkScan {
-    float d, cum, w;
+    float d, cum, lo, w;
 };
 __device__ __forceinline__ ChunkScan chunk_scan(float dtv, int nv, float bias, float Ah, int softplus_on, int lane) {
+#pragma clang fp contract(off)
     float d = 0.0f;
     if (lane < nv) {
         const float v = dtv + bias;
         d = softplus_on ? softplus(v) : v;
     }
-    const float c = wave_prefix_sum(d * Ah, lane);
-    const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-    return {d, c, fexp(last - c) * d};
+    float hi = d * Ah;
+    float lo = __builtin_fmaf(d, Ah, -hi);
+    wave_prefix_sum_df(hi, lo, lane);
+    const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hi), 63));
+    const float last_lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lo), 63));
+    return {d, hi, lo, fexp((last - hi) + (last_lo - lo)) * d};
 }
 
 // cum of the 16 accumulator rows a lane of half hl holds in row block ti

@@ -45,7 +45,8 @@ struct alignas(16) SsdSmem {
     float c[kQ][kSB];      // Cm rows
     float m[kQ][kSM];      // M = G o Lmask
     float st[N][kSX];      // S^T, the state entering the chunk
-    float cum[kQ];         // chunk-local cumulative Delta * A_h
+    float cum[kQ];         // chunk-local cumulative Delta * A_h, as cum + cum_lo (ssdk::chunk_scan)
+    float cum_lo[kQ];
     float dlt[kQ];         // Delta (0 past the sequence end)
     float w[kQ];           // exp(cum_last - cum_j) Delta_j
 };
@@ -235,6 +236,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
             }
             if (wv == 1) {
                 s.cum[lane] = cs.cum;
+                s.cum_lo[lane] = cs.lo;
                 s.dlt[lane] = cs.d;
                 s.w[lane] = cs.w;
             }
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
 
             // the next chunk's inputs travel while this chunk computes (past the end: no access)
             const ChunkLoader<T, N> next(a, bi, h, t0 + kQ, t_end, tid);
-            lam += s.cum[kQ - 1];
+            lam += s.cum[kQ - 1] + s.cum_lo[kQ - 1];
 
             // per-lane LDS base offsets (floats) of the MFMA operands; step k adds a constant
             constexpr int SB = SsdSmem<N>::kSB, SX = SsdSmem<N>::kSX, SM = SsdSmem<N>::kSM;
@@ -279,16 +281,17 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                     next.all(g);
                 }
                 const int j = tj * 32 + l32;
-                const float cj = s.cum[j], dj = s.dlt[j];
-                float ci[16];
+                const float cj = s.cum[j], cjl = s.cum_lo[j], dj = s.dlt[j];
+                float ci[16], cil[16];
                 acc_row_cum(s.cum, ti, hl, ci);
+                acc_row_cum(s.cum_lo, ti, hl, cil);
                 // above the diagonal: exponent -inf and a selected 0 (a non-finite future Bm row must not
                 // reach an earlier output), both as selects rather than a branch around the exponential
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int i = ti * 32 + acc_row(r, hl);
                     const bool keep = j <= i;
-                    const float v = gm[r] * fexp(keep ? ci[r] - cj : -__builtin_inff()) * dj;
+                    const float v = gm[r] * fexp(keep ? (ci[r] - cj) + (cil[r] - cjl) : -__builtin_inff()) * dj;
                     s.m[i][j] = keep ? v : 0.0f;
                 }
             }
@@ -301,10 +304,11 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                     av = cf[oc + 2 * k];
                     bv = stf[ost + 2 * k * SX];
                 });
-                float ci[16];
+                float ci[16], cil[16];
                 acc_row_cum(s.cum, ti, hl, ci);
+                acc_row_cum(s.cum_lo, ti, hl, cil);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) y[r] *= fexp(ci[r]);
+                for (int r = 0; r < 16; ++r) y[r] *= fexp(ci[r] + cil[r]);
                 auto ld_mx = [&](int k, float& av, float& bv) {
                     av = mf[om + 2 * k];
                     bv = xf[ox + 2 * k * SX];
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
 
             // ---- S' = exp(cum_last) S + (w o X)^T B ----
             {
-                const float decay = fexp(s.cum[kQ - 1]);
+                const float decay = fexp(s.cum[kQ - 1] + s.cum_lo[kQ - 1]);
 #pragma unroll
                 for (int k = 0; k < NT; ++k) {
                     const int obs = ob_s + k * 32;
