@@ -79,6 +79,8 @@ struct BwdPlan {
     int64_t tiles;       // ceil(L / tile)
     int64_t chunks;      // K >= 1: the reverse walk cut into K time chunks (carry of the adjoint between them)
     int64_t chunk_tiles; // tiles per chunk (the last may have fewer)
+    int64_t head_chunks; // walk 0 covers chunks [0, head_chunks), each later walk one chunk
+    int64_t units;       // reverse walks per channel block: chunks - head_chunks + 1
     size_t ws_bytes;
 };
 BwdPlan plan_bwd(int64_t B, int64_t L, int64_t D, int64_t N);

@@ -38,6 +38,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 namespace mssm {
@@ -70,9 +71,9 @@ struct BwdKArgs {
     float* ddt_bias;
     float* dh0;
     float* pBC;    // (B, L, dblocks, 2, N): per channel block, dB partial then dC partial
-    float* pA;     // (B, K, D, N): per time chunk
-    float* pD;     // (B, K, D)
-    float* pbias;  // (B, K, D)
+    float* pA;     // (B, units, D, N): per walk
+    float* pD;     // (B, units, D)
+    float* pbias;  // (B, units, D)
     float* qlam;   // (B, K - 1, D, N): chunks 1 .. K-1, a_{t0} lam_{t0} from a zero adjoint at the chunk's end
     float* slam;   // (B, K - 1, D): chunks 1 .. K-1, sum of Delta over the chunk
     float* pin;    // (B, K, D, N): a_{t1} lam_{t1} entering each chunk at its end (t1 = its end step)
@@ -82,6 +83,8 @@ struct BwdKArgs {
     int32_t softplus;
     int32_t chunks;       // K
     int32_t chunk_tiles;  // tiles per chunk
+    int32_t head_chunks;  // walk 0 covers chunks [0, head_chunks), walk u >= 1 chunk head_chunks + u - 1
+    int32_t units;        // walks per channel block: K - head_chunks + 1
 };
 
 // ---- cross-lane sums -------------------------------------------------------------
@@ -547,9 +550,10 @@ __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)
     }
 }
 
-// Reverse kernel.  Grid: (B * dblocks, K) workgroups of G state waves + the
-// helper waves; workgroup (blk, c) walks time chunk c of channel block blk,
-// starting from the adjoint that enters the chunk at its end.
+// Reverse kernel.  Grid: (B * dblocks, units) workgroups of G state waves +
+// the helper waves; workgroup (blk, u) walks the time chunks of walk u of
+// channel block blk backwards, starting from the adjoint that enters its last
+// chunk at that chunk's end.
 template <typename T, int NG, int G>
 __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel(BwdKArgs a) {
     constexpr int N = NG * G;
@@ -579,9 +583,11 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
     const bool state_wave = bk.w < G;
     bk.n0 = state_wave ? bk.w * NG : 0;
     bk.hw = state_wave ? 0 : bk.w - G;
-    const int64_t chunk = blockIdx.y;
-    bk.tile_begin = static_cast<int>(chunk) * a.chunk_tiles;
-    bk.tile_end = min(bk.tile_begin + a.chunk_tiles, static_cast<int>(a.tiles));
+    const int64_t unit = blockIdx.y;
+    const int c_first = unit == 0 ? 0 : a.head_chunks + static_cast<int>(unit) - 1;
+    const int c_last = unit == 0 ? a.head_chunks - 1 : c_first;
+    bk.tile_begin = c_first * a.chunk_tiles;
+    bk.tile_end = min((c_last + 1) * a.chunk_tiles, static_cast<int>(a.tiles));
     bk.softplus_on = a.softplus;
     bk.bias = a.dt_bias ? a.dt_bias[dc] : 0.0f;
     bk.Dk = a.Dskip ? a.Dskip[dc] : 0.0f;
@@ -605,10 +611,17 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
     for (int k = 0; k < NG; ++k) {
         Aval[k] = state_wave ? a.A[dc * N + n0 + k] : 0.0f;
         A2[k] = Aval[k] * kLog2e;
-        if (a.chunks > 1)
-            r.pc[k] = (state_wave && bk.dvalid) ? a.pin[((b * a.chunks + chunk) * D + dc) * N + n0 + k] : 0.0f;
-        else
-            r.pc[k] = (state_wave && a.dh_final && bk.dvalid) ? a.dh_final[(b * D + dc) * N + n0 + k] : 0.0f;
+        const float dhf = (state_wave && a.dh_final && bk.dvalid) ? a.dh_final[(b * D + dc) * N + n0 + k] : 0.0f;
+        if (a.head_chunks > 1 && unit == 0) {
+            // one long walk and the last chunk's: the carry over that one chunk, Q + exp(A sum Delta) dh_final
+            const int64_t q = (b * (a.chunks - 1) + (a.chunks - 2)) * D + dc;
+            r.pc[k] = (state_wave && bk.dvalid) ? __builtin_fmaf(expf(Aval[k] * a.slam[q]), dhf, a.qlam[q * N + n0 + k])
+                                                : 0.0f;
+        } else if (a.chunks > 1 && c_last < a.chunks - 1) {
+            r.pc[k] = (state_wave && bk.dvalid) ? a.pin[((b * a.chunks + c_last) * D + dc) * N + n0 + k] : 0.0f;
+        } else {
+            r.pc[k] = dhf;  // the walk over the last chunk starts from dh_final
+        }
         r.dA[k] = 0.0f;
     }
     r.accD = r.accBias = 0.0f;
@@ -621,10 +634,10 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
         rev_run<true>(bk, A2, Aval, r, sX, sLQ);
     // ---- per-(b, d) results
     if (state_wave && bk.dvalid) {
-        float* pa = a.pA + ((b * a.chunks + chunk) * D + dc) * N + n0;
+        float* pa = a.pA + ((b * a.units + unit) * D + dc) * N + n0;
 #pragma unroll
         for (int k = 0; k < NG; ++k) pa[k] = r.dA[k];
-        if (a.dh0 && chunk == 0) {
+        if (a.dh0 && unit == 0) {
             float* g0 = a.dh0 + (b * D + dc) * N + n0;
 #pragma unroll
             for (int k = 0; k < NG; ++k) g0[k] = r.pc[k];  // a_0 lam_0
@@ -642,8 +655,8 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
             sd += sRed[0][g][lane];
             sb += sRed[1][g][lane];
         }
-        a.pD[(b * a.chunks + chunk) * D + dc] = sd;
-        a.pbias[(b * a.chunks + chunk) * D + dc] = sb;
+        a.pD[(b * a.units + unit) * D + dc] = sd;
+        a.pbias[(b * a.units + unit) * D + dc] = sb;
     }
 }
 
@@ -653,9 +666,10 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
 // a_{t0} lam_{t0} leaving it, p_out = Q_c + R_c p, where R_c = prod_{t in c}
 // a_t = exp(A sum_{t in c} Delta_t) (the forward's chunk decay) and Q_c is
 // p_out for p = 0.  bwd_chunk_lambda_kernel computes Q_c and the chunk's sum
-// of Delta for every chunk but the first; bwd_lambda_carry_kernel chains
-// them from the last chunk (p = dh_final) back to the first; then every
-// chunk's reverse walk runs from its own entering p, all chunks at once.
+// of Delta for the chunks after the first walk's (every chunk but the first
+// when each walk is one chunk); bwd_lambda_carry_kernel chains them from the
+// last chunk (p = dh_final) back to the first walk's last chunk; then every
+// walk runs from its own entering p, all at once.
 
 // Reverse step J of the zero-started adjoint: lam = p + sbar Cm, p = a lam.
 template <int NG, bool FULL, int J>
@@ -676,11 +690,19 @@ __device__ __forceinline__ void lam_steps(std::integer_sequence<int, I...>, int 
     (lam_step<NG, FULL, kTB - 1 - I>(nval, A2, Ct, xs, p), ...);  // J = 15 .. 0
 }
 
-// Grid: (B * dblocks, K - 1), G waves; workgroup (blk, c - 1) walks chunk c
-// backwards.  Per tile each wave prepares (Delta, sbar) of its rows of the
+// Grid: (B * dblocks, K - head_chunks), G waves; workgroup (blk, c -
+// head_chunks) walks chunk c backwards.  Per tile each wave prepares (Delta, sbar) of its rows of the
 // tile before into the other LDS buffer while every wave runs the adjoint of
 // its states over this tile: one barrier per tile.
-template <typename T, int NG, int G>
+template <int K>
+using Slot = std::integral_constant<int, K>;
+// f(Slot<0>), f(Slot<1>), ... in order
+template <typename F, int... S>
+__device__ __forceinline__ void for_slots(F&& f, std::integer_sequence<int, S...>) {
+    (f(Slot<S>{}), ...);
+}
+
+template <typename T, int NG, int G, int PF>
 __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
     constexpr int N = NG * G;
     constexpr int SPW = kTB / G;
@@ -693,7 +715,7 @@ __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
     const int w = wave_id();
     const int64_t b = blockIdx.x / a.dblocks;
     const int64_t chan0 = static_cast<int64_t>(blockIdx.x % a.dblocks) * 64;
-    const int64_t c = static_cast<int64_t>(blockIdx.y) + 1;
+    const int64_t c = static_cast<int64_t>(blockIdx.y) + a.head_chunks;
     const int64_t D = a.D, L = a.L;
     const int L32 = static_cast<int>(L);
     const bool dvalid = chan0 + lane < D;
@@ -717,49 +739,51 @@ __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
     const T* d_b = static_cast<const T*>(a.delta) + row_b * D + chan0;
     const float* s_b = a.sbar + row_b * D + chan0;
     const T* Cm = static_cast<const T*>(a.Cm);
-    float rd[SPW], rs[SPW];
-    uint32_t qc[W], qn[W];
+    // loads of PF tiles in flight, in a ring of register slots: tile t's raw rows and Cm sit in slot
+    // (te - 1 - t) % PF, issued PF tiles before its steps (one tile of steps does not cover a load's latency)
+    float rd[PF][SPW], rs[PF][SPW];
+    uint32_t qc[PF][W];
 
     // raw delta and sbar of this wave's rows of `tile` (clamped to the last row), and the tile's Cm
-    auto fetch = [&](int tile, uint32_t (&q)[W]) {
+    auto fetch = [&](int tile, float (&d)[SPW], float (&sb)[SPW], uint32_t (&q)[W]) {
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int t = min(tile * kTB + w * SPW + i, L32 - 1);
             const int64_t off = static_cast<int64_t>(t) * D + lo;
-            rd[i] = load_act(d_b, off);
-            rs[i] = s_b[off];
+            d[i] = load_act(d_b, off);
+            sb[i] = s_b[off];
         }
         fetch_tile_rows<T, NG>(Cm, row_b + static_cast<int64_t>(tile) * kTB, last_row, N, n0, lane, q);
     };
-    // (Delta, sbar) of this wave's rows of `tile` into buffer `buf`
-    auto prep = [&](int tile, int buf) {
+    // (Delta, sbar) of this wave's rows of `tile` into buffer `buf`; a tile before the chunk (the one after
+    // its first, in the unconditional main loop) is written to the unused buffer and left out of the sum
+    auto prep = [&](int tile, int buf, const float (&d)[SPW], const float (&sb)[SPW]) {
         const int nval = min(kTB, L32 - tile * kTB);
+        const bool in = tile >= tb;
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int j = w * SPW + i;
             if (j < nval) {
-                const float x = rd[i] + bias;
+                const float x = d[i] + bias;
                 const float dt = a.softplus ? softplus(x) : x;
-                sDS[buf][j][lane] = make_float2(dt, rs[i]);
-                psum += dt;
+                sDS[buf][j][lane] = make_float2(dt, sb[i]);
+                psum += in ? dt : 0.0f;
             }
         }
     };
-
-    fetch(te - 1, qc);
-    prep(te - 1, (te - 1) & 1);
-    if (te - 2 >= tb) fetch(te - 2, qn);
-    __syncthreads();
-    for (int tile = te - 1; tile >= tb; --tile) {
+    // the steps of `tile` (slot S), after preparing the tile before it and issuing the loads of tile - PF.
+    // MAIN: a tile of the loop over whole groups of PF tiles, whose loads and preparation are unconditional
+    // (a load past the chunk's first tile reads that tile again): a branch around them would make the
+    // compiler wait for every load in flight where the paths join
+    auto walk = [&](auto slot, auto main, int tile) {
+        constexpr int S = decltype(slot)::value;
+        constexpr bool MAIN = decltype(main)::value;
+        if (!MAIN && tile < tb) return;  // uniform over the workgroup
         const int cur = tile & 1;
         float Ct[NG];
-        unpack_lane_row<T, NG>(qc, Ct);
-        if (tile - 1 >= tb) {
-            prep(tile - 1, cur ^ 1);
-#pragma unroll
-            for (int i = 0; i < W; ++i) qc[i] = qn[i];
-            if (tile - 2 >= tb) fetch(tile - 2, qn);
-        }
+        unpack_lane_row<T, NG>(qc[S], Ct);
+        if (MAIN || tile - 1 >= tb) prep(tile - 1, cur ^ 1, rd[(S + 1) % PF], rs[(S + 1) % PF]);
+        if (MAIN) fetch(max(tile - PF, tb), rd[S], rs[S], qc[S]);
         const int nval = min(kTB, L32 - tile * kTB);
         float2 xs[kTB];
 #pragma unroll
@@ -769,7 +793,21 @@ __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
         else
             lam_steps<NG, false>(std::make_integer_sequence<int, kTB>{}, nval, A2, Ct, xs, p);
         __syncthreads();
-    }
+    };
+    using Main = std::true_type;
+    using Rest = std::false_type;
+
+#pragma unroll
+    for (int i = 0; i < PF; ++i) fetch(max(te - 1 - i, tb), rd[i], rs[i], qc[i]);
+    prep(te - 1, (te - 1) & 1, rd[0], rs[0]);
+    __syncthreads();
+    int base = te - 1;
+    // groups of PF tiles, every slot index a constant; then the fewer than PF tiles left, their loads issued
+    for (int g = (te - tb) / PF; g > 0; --g, base -= PF)
+        for_slots([&](auto slot) { walk(slot, Main{}, base - decltype(slot)::value); },
+                  std::make_integer_sequence<int, PF>{});
+    for_slots([&](auto slot) { walk(slot, Rest{}, base - decltype(slot)::value); },
+              std::make_integer_sequence<int, PF - 1>{});
     sSum[w][lane] = psum;
     __syncthreads();
     if (dvalid) {
@@ -786,8 +824,9 @@ __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
     }
 }
 
-// pin of every chunk, from the last (dh_final, or 0) back to the first:
-// p_in(c - 1) = Q_c + exp(A sum Delta_c) p_in(c).  One thread per (b, d, n).
+// pin of the chunks from the last (dh_final, or 0) back to the first walk's
+// last chunk: p_in(c - 1) = Q_c + exp(A sum Delta_c) p_in(c).  One thread per
+// (b, d, n).
 __global__ __launch_bounds__(256) void bwd_lambda_carry_kernel(BwdKArgs a) {
     const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (i >= a.B * a.D * a.N) return;
@@ -797,7 +836,7 @@ __global__ __launch_bounds__(256) void bwd_lambda_carry_kernel(BwdKArgs a) {
     const float A = a.A[d * a.N + n];
     float p = a.dh_final ? a.dh_final[i] : 0.0f;
     a.pin[((b * K + (K - 1)) * a.D + d) * a.N + n] = p;
-    for (int64_t c = K - 1; c >= 1; --c) {
+    for (int64_t c = K - 1; c >= a.head_chunks; --c) {
         const int64_t q = (b * (K - 1) + (c - 1)) * a.D + d;
         p = __builtin_fmaf(expf(A * a.slam[q]), p, a.qlam[q * a.N + n]);
         a.pin[((b * K + (c - 1)) * a.D + d) * a.N + n] = p;
@@ -815,7 +854,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdKArgs a) {
     const int64_t nBC = a.B * a.L * a.N;
     const int64_t nA = a.D * a.N;
     const int64_t total = nBC + nA + a.D;
-    const int64_t parts = a.B * a.chunks;  // (b, c) in order
+    const int64_t parts = a.B * a.units;  // (b, walk) in order
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
          i += static_cast<int64_t>(gridDim.x) * 256) {
         if (i < nBC) {
@@ -902,18 +941,30 @@ hipError_t launch_bwd_t(const ScanArgs& s, hipStream_t st) {
     a.softplus = s.softplus;
     a.chunks = static_cast<int32_t>(pl.chunks);
     a.chunk_tiles = static_cast<int32_t>(pl.chunk_tiles);
+    a.head_chunks = static_cast<int32_t>(pl.head_chunks);
+    a.units = static_cast<int32_t>(pl.units);
     const unsigned nblk = static_cast<unsigned>(s.B * a.dblocks);
-    if (pl.chunks > 1) {
+    if (pl.head_chunks > 1) {
+        // one long walk per block and the last chunk's: Q of that chunk alone, one workgroup per block on a
+        // GPU that is otherwise idle, so up to 16 waves of one state or more (four waves per SIMD); the
+        // reverse kernel forms the long walk's entering adjoint itself (no carry pass)
+        constexpr int Gq = NG * G < 16 ? NG * G : 16;
+        constexpr int NGq = NG * G / Gq;
+        hipLaunchKernelGGL((bwd_chunk_lambda_kernel<T, NGq, Gq, 4>), dim3(nblk, 1u), dim3(64 * Gq), 0, st, a);
+    } else if (pl.chunks > 1) {
         // its own layout: four states per wave where N allows (no LDS partial sums to keep small)
         constexpr int NGc = NG * G >= 16 ? (NG > 4 ? NG : 4) : NG;
         constexpr int Gc = NG * G / NGc;
-        hipLaunchKernelGGL((bwd_chunk_lambda_kernel<T, NGc, Gc>), dim3(nblk, static_cast<unsigned>(pl.chunks - 1)),
+        hipLaunchKernelGGL((bwd_chunk_lambda_kernel<T, NGc, Gc, 4>),
+                           dim3(nblk, static_cast<unsigned>(pl.chunks - pl.head_chunks)),
                            dim3(64 * Gc), 0, st, a);
         const int64_t threads = s.B * s.D * s.N;
         hipLaunchKernelGGL(bwd_lambda_carry_kernel, dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
                            st, a);
     }
-    hipLaunchKernelGGL((bwd_reverse_kernel<T, NG, G>), dim3(nblk, static_cast<unsigned>(pl.chunks)),
+    // walk 0 of every block first: with one long walk per block and the short ones after it, the hardware's
+    // in-order dispatch gives each long walk a CU of its own and runs the short ones on the rest as they free up
+    hipLaunchKernelGGL((bwd_reverse_kernel<T, NG, G>), dim3(nblk, static_cast<unsigned>(pl.units)),
                        dim3(64 * (G + helper_waves(G))), 0, st, a);
     const int64_t items = s.B * s.L * s.N + s.D * s.N + s.D;
     const int64_t blocks = std::min<int64_t>((items + 255) / 256, 16384);
@@ -937,22 +988,45 @@ hipError_t dispatch_n(const ScanArgs& s, hipStream_t st) {
 
 }  // namespace
 
-// Time chunks of the reverse walk: when the channel blocks fill at most half
-// of a 256-CU MI355X, enough chunks for about three workgroups per CU, each
-// at least 4 tiles long.  (The chunk carry's extra pass costs about a quarter
-// of the reverse walk over the chunks it covers; with more blocks it costs
-// what it gains: 192 blocks, 4 chunks: reverse 408 -> 306 us, carry 115 us.)
-// Depends only on the problem (the workspace size query has no device).
+// Time chunks of the reverse walk, for a 256-CU MI355X (the workspace size
+// query has no device, so the plan depends only on the problem).
+// * Channel blocks fill at most half of the CUs: enough chunks for about three
+//   workgroups per CU, each at least 4 tiles long, one walk per chunk.  (The
+//   chunk carry's extra pass costs about a quarter of the reverse walk over
+//   the chunks it covers.)
+// * More blocks than half the CUs but fewer than all (the training shape: 192
+//   blocks): with m = ceil(blocks / idle CUs), K = m + 1 chunks; each block's
+//   first walk covers chunks 0 .. K - 2 on a CU of its own and its last chunk
+//   is a walk of its own, m of them in turn on each otherwise idle CU.  The
+//   carry then needs the last chunk's Q alone (one pass over 1/K of the
+//   sequence), and every CU walks (K - 1)/K of it.  Only where a reverse
+//   workgroup takes a CU by itself (N >= 4: 96 KB of LDS or more), so that no
+//   short walk shares a long one's CU, with chunks of at least 4 tiles and at
+//   most 8 short walks per idle CU.  Training shape, fp32: reverse 408 ->
+//   303-337 us (all 256 CUs busy run at a lower clock than 192), plus 44 us for
+//   the last chunk's Q.
 BwdPlan plan_bwd(int64_t B, int64_t L, int64_t D, int64_t N) {
+    constexpr int64_t kCUs = 256;
     BwdPlan p{};
     p.tile = kTB;
     p.tiles = (L + kTB - 1) / kTB;
     const int64_t nblk = B * ((D + 63) / 64);
     int64_t K = 1;
-    if (nblk <= 128) K = std::min<int64_t>((768 + nblk - 1) / nblk, p.tiles / 4);
+    bool tail = false;
+    if (nblk <= kCUs / 2) {
+        K = std::min<int64_t>((3 * kCUs + nblk - 1) / nblk, p.tiles / 4);
+    } else if (nblk < kCUs && N >= 4) {
+        const int64_t m = (nblk + (kCUs - nblk) - 1) / (kCUs - nblk);
+        if (m <= 8 && p.tiles / (m + 1) >= 4) {
+            K = m + 1;
+            tail = true;
+        }
+    }
     K = std::max<int64_t>(K, 1);
     p.chunk_tiles = (p.tiles + K - 1) / K;
     p.chunks = (p.tiles + p.chunk_tiles - 1) / p.chunk_tiles;  // no empty chunk
+    p.head_chunks = (tail && p.chunks > 1) ? p.chunks - 1 : 1;
+    p.units = p.chunks - p.head_chunks + 1;
     p.ws_bytes = ws_layout(B, L, D, N, p.tiles, p.chunks).total;
     return p;
 }

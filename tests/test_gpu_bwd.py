@@ -5,7 +5,8 @@ element with the relative criterion of helpers.grad_err.
 Covers the training workload (B=8, L=2048, D=1536, N=16, fp32) in full, ragged
 small shapes with every optional input (h0, dh_final, z, Dskip, dt_bias), the
 ungated path, every supported state size, bfloat16 activations, the reverse
-walk cut into time chunks joined by the adjoint carry, the forward pre-pass
+walk cut into time chunks joined by the adjoint carry (one walk per chunk, or
+one long walk per block and its last chunk walked apart), the forward pre-pass
 under its chunked and its balanced schedules, and bitwise reproducibility
 (the reductions have a fixed order, no atomics)."""
 import numpy as np
@@ -129,6 +130,27 @@ def test_chunked_reverse_many_chunks(mssm):
 @pytest.mark.parametrize("N", [1, 4, 64])
 def test_chunked_reverse_state_sizes(mssm, N):
     g, r = run_both(mssm, workloads.custom(1, 200, 50, N, "f32", seed=N + 300))
+    assert_grads(g, r, GRAD_TOL["f32"])
+
+
+@pytest.mark.parametrize("shape,N,dtype", [
+    ((3, 300, 3200), 16, "f32"),    # 150 blocks: 3 chunks of 7, 7, 5 tiles; walks [0, 2) and 2, last tile ragged
+    ((2, 260, 6144), 16, "bf16"),   # 192 blocks: 4 chunks of 5, 5, 5, 2 tiles; walks [0, 3) and 3
+    ((1, 400, 12800), 4, "f32"),    # 200 blocks: 5 chunks of 5 tiles; walks [0, 4) and 4
+    ((1, 200, 8960), 64, "f32"),    # 140 blocks: 3 chunks of 5, 5, 3 tiles
+])
+def test_tail_walk_reverse(mssm, shape, N, dtype):
+    # more channel blocks than half the CUs of a 256-CU MI355X but fewer than all: each block's reverse walk
+    # covers all chunks but the last, whose own walk runs on an otherwise idle CU from dh_final; the walk
+    # before it starts from the adjoint the carry forms from the last chunk's Q
+    B, L, D = shape
+    g, r = run_both(mssm, workloads.custom(B, L, D, N, dtype, seed=L + D + N))
+    assert_grads(g, r, GRAD_TOL[dtype])
+
+
+def test_tail_walk_reverse_plain(mssm):
+    # the same plan with no dh_final (the last chunk's walk starts from zero), no gate, no h0
+    g, r = run_both(mssm, workloads.custom(3, 300, 3200, 16, "f32", seed=91), h0=False, dhf=False, gate=False)
     assert_grads(g, r, GRAD_TOL["f32"])
 
 
