@@ -154,6 +154,38 @@ def test_tail_walk_reverse_plain(mssm):
     assert_grads(g, r, GRAD_TOL["f32"])
 
 
+def test_tail_walk_backward_in_a_graph(mssm):
+    # the tail-walk plan (pre-pass, the last chunk's Q pass, the long and short reverse walks, the
+    # reductions) captured in a graph, replayed 3 times with a new dy each time (eager calls between the
+    # replays): every replay equals the eager call on the same inputs bit for bit
+    w = workloads.custom(3, 300, 3200, 16, "f32", seed=5)
+    print(f"[bwd graph] {w}", flush=True)
+    inp = workloads.make_inputs(w, with_dy=True)
+    t = gpu_inputs(inp)
+    dy = t["dy"].clone()
+
+    def call():
+        return mssm.scan_bwd(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], dy, t["Dskip"], t["z"], t["dt_bias"])
+
+    call()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        out = call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    for r in range(3):
+        dy.copy_(torch.from_numpy(rng.standard_normal(tuple(dy.shape)).astype(np.float32)).cuda())
+        ref = {k: v.clone() for k, v in call().items() if v is not None}
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert torch.equal(out[k], v), (r, k)
+
+
 @pytest.mark.parametrize("shape,dtype", [((1, 600, 100), "f32"), ((2, 1024, 64), "bf16")])
 def test_chunked_prepass_short(mssm, shape, dtype):
     # few channel blocks and 512 <= L < 2048: the pre-pass runs the time-chunked forward schedule
