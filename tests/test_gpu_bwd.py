@@ -138,6 +138,8 @@ def test_chunked_reverse_state_sizes(mssm, N):
     ((2, 260, 6144), 16, "bf16"),   # 192 blocks: 4 chunks of 5, 5, 5, 2 tiles; walks [0, 3) and 3
     ((1, 400, 12800), 4, "f32"),    # 200 blocks: 5 chunks of 5 tiles; walks [0, 4) and 4
     ((1, 200, 8960), 64, "f32"),    # 140 blocks: 3 chunks of 5, 5, 3 tiles
+    ((1, 300, 9600), 8, "f32"),     # 150 blocks, two states per wave
+    ((2, 300, 5120), 32, "bf16"),   # 160 blocks, four states per wave
 ])
 def test_tail_walk_reverse(mssm, shape, N, dtype):
     # more channel blocks than half the CUs of a 256-CU MI355X but fewer than all: each block's reverse walk
