@@ -13,7 +13,7 @@
 // state S (P x N) entering the chunk:
 //     G   = C B^T                                        (Q x Q, over N)
 //     M   = G o Lmask,  Lmask_ij = exp(cum_i - cum_j) Delta_j  for j <= i, else 0
-//     Y   = diag(exp(cum)) C S^T + M X + D_h X           (Q x P)
+//     Y   = diag(exp(cum)) C S^T + (M + D_h I) X         (Q x P)
 //     S'  = exp(cum_last) S + (w o X)^T B,   w_j = exp(cum_last - cum_j) Delta_j
 // All four products are dense fp32 contractions: they run as
 // v_mfma_f32_32x32x2f32, one 32 x 32 output tile per wave per product, with
@@ -286,18 +286,20 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                 acc_row_cum(s.cum, ti, hl, ci);
                 acc_row_cum(s.cum_lo, ti, hl, cil);
                 // above the diagonal: exponent -inf and a selected 0 (a non-finite future Bm row must not
-                // reach an earlier output), both as selects rather than a branch around the exponential
+                // reach an earlier output), both as selects rather than a branch around the exponential; on the
+                // diagonal the skip weight D_h joins M (Y = (M + D_h I) X: the skip term rides the M X product)
+                const float dsk = ti == tj ? Dh : 0.0f;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int i = ti * 32 + acc_row(r, hl);
                     const bool keep = j <= i;
                     const float v = gm[r] * fexp(keep ? (ci[r] - cj) + (cil[r] - cjl) : -__builtin_inff()) * dj;
-                    s.m[i][j] = keep ? v : 0.0f;
+                    s.m[i][j] = keep ? (i == j ? v + dsk : v) : 0.0f;
                 }
             }
             __syncthreads();  // M is read by other waves below
 
-            // ---- Y tile (ti, tj): exp(cum_i) (C S^T) + M X + D X ----
+            // ---- Y tile (ti, tj): exp(cum_i) (C S^T) + (M + D_h I) X ----
             f32x16 y = {};
             {
                 y = mfma_chain<N / 2>(f32x16{}, [&](int k, float& av, float& bv) {
@@ -318,9 +320,6 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
                     y = mfma_chain<16>(y, ld_mx);
                 else
                     y = mfma_chain<32>(y, ld_mx);
-                const int p = tj * 32 + l32;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) y[r] += Dh * s.x[ti * 32 + acc_row(r, hl)][p];
             }
             // rows past the sequence end fall outside the resource and are dropped; a bf16 output of a
             // time segment the correction completes stays float32 until then
