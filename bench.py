@@ -304,6 +304,48 @@ def time_bwd(mssm, torch, w, steps, warmup):
     return float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3
 
 
+def time_train_pair(mssm, torch, w, steps, warmup):
+    """The training pair: mssm_scan_fwd_train (the forward saving its context)
+    and mssm_scan_bwd_saved (the backward from it).  Median seconds of each,
+    HIP events on the launch stream, buffers allocated once."""
+    inp = workloads.make_inputs(w, with_dy=True)
+    t = workloads.to_torch(inp, "cuda")
+    del inp
+    act = t["u"].dtype
+    y = torch.empty_like(t["u"])
+    hf = torch.empty((w.B, w.D, w.N), dtype=torch.float32, device="cuda")
+    ctx = torch.empty(mssm.ctx_bytes(w.B, w.L, w.D, w.N, act), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(max(1, mssm.fwd_workspace_bytes(w.B, w.L, w.D, w.N, act)), dtype=torch.uint8, device="cuda")
+    prob = mssm.problem(w.B, w.L, w.D, w.N, act)
+    bws = torch.empty(int(mssm.lib.mssm_scan_bwd_saved_workspace_bytes(ctypes.byref(prob))),
+                      dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        mssm.scan_fwd_train(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"], t["dt_bias"],
+                            y=y, h_final=hf, ctx=ctx, workspace=fws)
+
+    def bwd():
+        mssm.scan_bwd_saved(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["dy"], ctx, t["Dskip"], t["z"],
+                            t["dt_bias"], want_dh0=False, workspace=bws)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for a, b, c in ev:
+        a.record(stream)
+        fwd()
+        b.record(stream)
+        bwd()
+        c.record(stream)
+    torch.cuda.synchronize()
+    kf = float(np.median([a.elapsed_time(b) for a, b, _ in ev])) / 1e3
+    kb = float(np.median([b.elapsed_time(c) for _, b, c in ev])) / 1e3
+    return kf, kb
+
+
 def time_conv_step(mssm, torch, w, batch, reps=100):
     """mssm_conv_step (conv front end + recurrent step, d_conv = 4) at batch
     `batch`, the workload's width: median us per call (HIP events)."""
@@ -516,6 +558,13 @@ def other_configs(mssm, torch):
                     "bwd_GBs": round(bwd_bytes(w) / kb / 1e9, 1),
                     "fwd_bwd_GBs": round((fwd_bytes(w) + bwd_bytes(w)) / (kf + kb) / 1e9, 1),
                     "fwd_bwd_hbm_frac": round((fwd_bytes(w) + bwd_bytes(w)) / (kf + kb) / 1e9 / HBM_PEAK_GBS, 4)}
+    # the training pair: the forward saves the tile states and the pre-gate readout, the backward starts from them
+    tf, tb = time_train_pair(mssm, torch, w, 10, 2)
+    cfg["train"].update({"fwd_train_us": round(tf * 1e6, 1), "bwd_saved_us": round(tb * 1e6, 1),
+                         "fwd_bwd_saved_us": round((tf + tb) * 1e6, 1),
+                         "fwd_bwd_saved_GBs": round((fwd_bytes(w) + bwd_bytes(w)) / (tf + tb) / 1e9, 1),
+                         "fwd_bwd_saved_hbm_frac": round((fwd_bytes(w) + bwd_bytes(w)) / (tf + tb) / 1e9
+                                                         / HBM_PEAK_GBS, 4)})
     log("configs: train fwd + bwd timed")
     return cfg
 

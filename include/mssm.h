@@ -244,6 +244,60 @@ mssm_status mssm_scan_bwd(const mssm_problem* p,
                           void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Training pair: a forward that saves what its backward needs, and that
+ * backward.  mssm_scan_bwd recomputes the forward's states with a pre-pass
+ * over the whole recurrence; mssm_scan_fwd_train instead writes them, once
+ * per 16-step tile, into a caller-owned context buffer, and
+ * mssm_scan_bwd_saved starts its reverse walk from them (the forward-state
+ * recomputation of the page "mamba.py: 一个简单高效的Mamba实现", performance
+ * section, then covers one tile at a time).  The gradients are those of
+ * mssm_scan_bwd (same definitions, same fixed reduction order).
+ *
+ * Context (ctx): device memory of at least mssm_scan_ctx_bytes(p), 16-byte
+ * aligned, owned by the caller; its contents are the library's (the state
+ * before every 16-step tile, (B, ceil(L/16), N, D) float32, and the readout
+ * before the gate, sum_n Cm h_t + Dskip u_t, (B, L, D) float32, written only
+ * when z is given).  Valid for the inputs of the forward that wrote it.
+ * Both calls need dstate a power of two (1 .. 64); other sizes return
+ * MSSM_ERR_UNSUPPORTED (and the size queries 0).  ctx_bytes below the query
+ * returns MSSM_ERR_WORKSPACE.
+ */
+size_t mssm_scan_ctx_bytes(const mssm_problem* p);
+
+/* Forward of mssm_scan_fwd that also writes the context: same arguments (the
+ * workspace is mssm_scan_fwd_workspace_bytes), outputs and aliasing rules,
+ * plus ctx (required).  Always runs the tiled kernels, so its results are bit
+ * for bit those of mssm_scan_fwd except for the short sequences (at most 64
+ * steps) that mssm_scan_fwd runs on its short-sequence path. */
+mssm_status mssm_scan_fwd_train(const mssm_problem* p,
+                                const void* u, const void* delta, const float* A,
+                                const void* Bm, const void* Cm,
+                                const float* Dskip, const void* z, const float* dt_bias,
+                                const float* h0,
+                                void* y, float* h_final,
+                                void* ctx, size_t ctx_bytes,
+                                void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of device scratch mssm_scan_bwd_saved needs (the partial sums of
+ * dB, dC, dA, dD, ddt_bias and, with time chunks, the adjoint carries). */
+size_t mssm_scan_bwd_saved_workspace_bytes(const mssm_problem* p);
+
+/* Backward of mssm_scan_bwd from the context mssm_scan_fwd_train wrote for
+ * the same u, delta, A, Bm, Cm, Dskip, z, dt_bias and h0 (h0 itself is not
+ * needed: the context holds it as the state before the first tile).
+ * Arguments, outputs and errors otherwise those of mssm_scan_bwd; workspace
+ * from mssm_scan_bwd_saved_workspace_bytes (required). */
+mssm_status mssm_scan_bwd_saved(const mssm_problem* p,
+                                const void* u, const void* delta, const float* A,
+                                const void* Bm, const void* Cm,
+                                const float* Dskip, const void* z, const float* dt_bias,
+                                const void* ctx, size_t ctx_bytes,
+                                const void* dy, const float* dh_final,
+                                void* du, void* ddelta, float* dA, void* dB, void* dC,
+                                float* dD, void* dz, float* ddt_bias, float* dh0,
+                                void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * One token of the recurrent (RNN) form, for streaming decode: the step
  * function that the page "mamba.py: 一个简单高效的Mamba实现" lists in its
  * updates section.  p->seqlen is ignored.  Shapes: u_t, delta_t, z_t, y_t

@@ -24,7 +24,8 @@ STATUS = {0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_SHAPE", -3: "MSSM_ERR
 EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd", "mssm_scan_fwd_noalloc",
            "mssm_conv_scan_fwd", "mssm_conv_bwd_workspace_bytes", "mssm_conv_bwd", "mssm_scan_bwd", "mssm_step",
            "mssm_conv_step", "mssm_ssd_fwd_workspace_bytes", "mssm_ssd_fwd", "mssm_ssd_bwd_workspace_bytes",
-           "mssm_ssd_bwd", "mssm_status_string", "mssm_build_info"]
+           "mssm_ssd_bwd", "mssm_scan_ctx_bytes", "mssm_scan_fwd_train", "mssm_scan_bwd_saved_workspace_bytes",
+           "mssm_scan_bwd_saved", "mssm_status_string", "mssm_build_info"]
 MAX_DCONV = 4
 
 
@@ -83,6 +84,14 @@ def _open(path: str):
     lib.mssm_ssd_bwd_workspace_bytes.restype = sz
     lib.mssm_ssd_bwd.argtypes = [ctypes.POINTER(SsdProblem)] + [vp] * 18 + [vp, sz, vp]
     lib.mssm_ssd_bwd.restype = st
+    lib.mssm_scan_ctx_bytes.argtypes = [P]
+    lib.mssm_scan_ctx_bytes.restype = sz
+    lib.mssm_scan_fwd_train.argtypes = [P] + [vp] * 11 + [vp, sz, vp, sz, vp]
+    lib.mssm_scan_fwd_train.restype = st
+    lib.mssm_scan_bwd_saved_workspace_bytes.argtypes = [P]
+    lib.mssm_scan_bwd_saved_workspace_bytes.restype = sz
+    lib.mssm_scan_bwd_saved.argtypes = [P] + [vp] * 8 + [vp, sz] + [vp] * 11 + [vp, sz, vp]
+    lib.mssm_scan_bwd_saved.restype = st
     lib.mssm_status_string.argtypes = [st]
     lib.mssm_status_string.restype = ctypes.c_char_p
     lib.mssm_build_info.argtypes = []
@@ -349,6 +358,90 @@ def scan_bwd(u, delta, A, Bm, Cm, dy, Dskip=None, z=None, dt_bias=None, h0=None,
                              _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
                              _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddt_bias"]),
                              _ptr(g["dh0"]), _ptr(ws), nbytes, _stream(dev)))
+    return g
+
+
+def ctx_bytes(B, L, D, N, dtype=torch.float32) -> int:
+    return int(lib.mssm_scan_ctx_bytes(ctypes.byref(problem(B, L, D, N, dtype))))
+
+
+def scan_fwd_train(u, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None,
+                   delta_softplus=True, return_final_state=True, y=None, h_final=None, ctx=None, workspace=None):
+    """The forward of scan_fwd that also saves the training context for
+    scan_bwd_saved.  Returns (y, h_final, ctx); ctx is a uint8 device tensor
+    of ctx_bytes(...) bytes (pass one to reuse it)."""
+    act = u.dtype
+    B, L, D = u.shape
+    N = A.shape[1]
+    _req(u, "u", (B, L, D), act)
+    _req(delta, "delta", (B, L, D), act)
+    _req(A, "A", (D, N), torch.float32)
+    _req(Bm, "Bm", (B, L, N), act)
+    _req(Cm, "Cm", (B, L, N), act)
+    _opt(Dskip, "Dskip", (D,), torch.float32)
+    _opt(z, "z", (B, L, D), act)
+    _opt(dt_bias, "dt_bias", (D,), torch.float32)
+    _opt(h0, "h0", (B, D, N), torch.float32)
+    if y is None:
+        y = torch.empty((B, L, D), dtype=act, device=u.device)
+    _req(y, "y", (B, L, D), act)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((B, D, N), dtype=torch.float32, device=u.device)
+    _opt(h_final, "h_final", (B, D, N), torch.float32)
+    prob = problem(B, L, D, N, _dtype_code(u), delta_softplus)
+    cbytes = int(lib.mssm_scan_ctx_bytes(ctypes.byref(prob)))
+    if cbytes == 0:
+        raise MssmError(-4, lib)
+    if ctx is None:
+        ctx = torch.empty(cbytes, dtype=torch.uint8, device=u.device)
+    nbytes = int(lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(prob)))
+    ws = _workspace(nbytes, u.device, workspace)
+    _check(lib.mssm_scan_fwd_train(ctypes.byref(prob), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                                   _ptr(Dskip), _ptr(z), _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final),
+                                   _ptr(ctx), ctx.numel() * ctx.element_size(), _ptr(ws), nbytes, _stream(u.device)))
+    return y, h_final, ctx
+
+
+def scan_bwd_saved(u, delta, A, Bm, Cm, dy, ctx, Dskip=None, z=None, dt_bias=None, dh_final=None,
+                   delta_softplus=True, want_dh0=True, workspace=None):
+    """scan_bwd from the context scan_fwd_train saved for the same inputs (no
+    h0 argument: the context holds it).  Returns the dict of scan_bwd."""
+    act = u.dtype
+    B, L, D = u.shape
+    N = A.shape[1]
+    dev = u.device
+    _req(u, "u", (B, L, D), act)
+    _req(delta, "delta", (B, L, D), act)
+    _req(A, "A", (D, N), torch.float32)
+    _req(Bm, "Bm", (B, L, N), act)
+    _req(Cm, "Cm", (B, L, N), act)
+    _req(dy, "dy", (B, L, D), act)
+    _opt(Dskip, "Dskip", (D,), torch.float32)
+    _opt(z, "z", (B, L, D), act)
+    _opt(dt_bias, "dt_bias", (D,), torch.float32)
+    _opt(dh_final, "dh_final", (B, D, N), torch.float32)
+    if not ctx.is_cuda or not ctx.is_contiguous():
+        raise ValueError("ctx must be a contiguous GPU tensor")
+    g = {
+        "du": torch.empty((B, L, D), dtype=act, device=dev),
+        "ddelta": torch.empty((B, L, D), dtype=act, device=dev),
+        "dA": torch.empty((D, N), dtype=torch.float32, device=dev),
+        "dB": torch.empty((B, L, N), dtype=act, device=dev),
+        "dC": torch.empty((B, L, N), dtype=act, device=dev),
+        "dD": torch.empty((D,), dtype=torch.float32, device=dev),
+        "dz": torch.empty((B, L, D), dtype=act, device=dev) if z is not None else None,
+        "ddt_bias": torch.empty((D,), dtype=torch.float32, device=dev),
+        "dh0": torch.empty((B, D, N), dtype=torch.float32, device=dev) if want_dh0 else None,
+    }
+    prob = problem(B, L, D, N, _dtype_code(u), delta_softplus)
+    nbytes = int(lib.mssm_scan_bwd_saved_workspace_bytes(ctypes.byref(prob)))
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.mssm_scan_bwd_saved(ctypes.byref(prob), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm),
+                                   _ptr(Dskip), _ptr(z), _ptr(dt_bias), _ptr(ctx),
+                                   ctx.numel() * ctx.element_size(), _ptr(dy), _ptr(dh_final),
+                                   _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                                   _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddt_bias"]),
+                                   _ptr(g["dh0"]), _ptr(ws), nbytes, _stream(dev)))
     return g
 
 

@@ -45,6 +45,9 @@ struct ScanArgs {
     float* dD;             // nullable
     float* ddt_bias;       // nullable
     float* dh0;            // nullable
+    // training context (mssm_scan_fwd_train writes it, mssm_scan_bwd_saved reads it)
+    float* ctx_ckpt;       // (B, tiles, N, D) state before every 16-step tile; null: no context
+    float* ctx_s;          // (B, L, D) readout before the gate, sum_n Cm h + Dskip u (only with z)
     // scratch
     void* workspace;
     size_t workspace_bytes;
@@ -85,6 +88,20 @@ struct BwdPlan {
 };
 BwdPlan plan_bwd(int64_t B, int64_t L, int64_t D, int64_t N);
 hipError_t launch_bwd(const ScanArgs& a, hipStream_t s);
+
+// Training context saved by the forward for the backward (power-of-two N):
+// the state before every 16-step tile and the readout before the gate.
+struct CtxLayout {
+    size_t ckpt, s, total;
+};
+CtxLayout ctx_layout(int64_t B, int64_t L, int64_t D, int64_t N);
+// The forward that also writes the context at a.ctx_ckpt / a.ctx_s (always the
+// tiled kernels: the short-sequence path keeps no checkpoints).
+hipError_t launch_fwd_train(const ScanArgs& a, hipStream_t s);
+// The backward from a saved context: no pre-pass; the reverse walk forms
+// sbar = dy silu(z) and dz = dy s silu'(z) from dy, z and the saved s.
+size_t bwd_saved_ws_bytes(int64_t B, int64_t L, int64_t D, int64_t N);
+hipError_t launch_bwd_saved(const ScanArgs& a, hipStream_t s);
 
 hipError_t launch_step(const ScanArgs& a, float* state, hipStream_t s);
 // The forward for short sequences: the state in registers across the L steps,

@@ -192,6 +192,73 @@ mssm_status mssm_scan_bwd(const mssm_problem* p, const void* u, const void* delt
     return from_hip(mssm::launch_bwd_any(a, static_cast<hipStream_t>(hip_stream)));
 }
 
+size_t mssm_scan_ctx_bytes(const mssm_problem* p) {
+    if (check_problem(p, true) != MSSM_OK || mssm::needs_padding(p->dstate)) return 0;
+    return mssm::ctx_layout(p->batch, p->seqlen, p->dim, p->dstate).total;
+}
+
+size_t mssm_scan_bwd_saved_workspace_bytes(const mssm_problem* p) {
+    if (check_problem(p, true) != MSSM_OK || mssm::needs_padding(p->dstate)) return 0;
+    return mssm::bwd_saved_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate);
+}
+
+mssm_status mssm_scan_fwd_train(const mssm_problem* p, const void* u, const void* delta, const float* A,
+                                const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                                const float* dt_bias, const float* h0, void* y, float* h_final, void* ctx,
+                                size_t ctx_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
+    mssm_status st = check_problem(p, true);
+    if (st != MSSM_OK) return st;
+    if (mssm::needs_padding(p->dstate)) return MSSM_ERR_UNSUPPORTED;
+    if (!u || !delta || !A || !Bm || !Cm || !y || !ctx) return MSSM_ERR_NULL;
+    st = check_align({u, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, y, h_final, ctx, workspace});
+    if (st != MSSM_OK) return st;
+    const mssm::CtxLayout cl = mssm::ctx_layout(p->batch, p->seqlen, p->dim, p->dstate);
+    if (ctx_bytes < cl.total) return MSSM_ERR_WORKSPACE;
+    const size_t need = mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return MSSM_ERR_WORKSPACE;
+
+    mssm::ScanArgs a = base_args(p);
+    a.u = u; a.delta = delta; a.z = z; a.Bm = Bm; a.Cm = Cm;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0;
+    a.y = y; a.h_final = h_final;
+    a.ctx_ckpt = reinterpret_cast<float*>(static_cast<char*>(ctx) + cl.ckpt);
+    a.ctx_s = reinterpret_cast<float*>(static_cast<char*>(ctx) + cl.s);
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return from_hip(mssm::launch_fwd_train(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+mssm_status mssm_scan_bwd_saved(const mssm_problem* p, const void* u, const void* delta, const float* A,
+                                const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                                const float* dt_bias, const void* ctx, size_t ctx_bytes, const void* dy,
+                                const float* dh_final, void* du, void* ddelta, float* dA, void* dB, void* dC,
+                                float* dD, void* dz, float* ddt_bias, float* dh0, void* workspace,
+                                size_t workspace_bytes, void* hip_stream) {
+    mssm_status st = check_problem(p, true);
+    if (st != MSSM_OK) return st;
+    if (mssm::needs_padding(p->dstate)) return MSSM_ERR_UNSUPPORTED;
+    if (!u || !delta || !A || !Bm || !Cm || !dy || !ctx) return MSSM_ERR_NULL;
+    if (!du || !ddelta || !dA || !dB || !dC) return MSSM_ERR_NULL;
+    if (z && !dz) return MSSM_ERR_NULL;
+    st = check_align({u, delta, A, Bm, Cm, Dskip, z, dt_bias, ctx, dy, dh_final, du, ddelta, dA, dB, dC, dD, dz,
+                      ddt_bias, dh0, workspace});
+    if (st != MSSM_OK) return st;
+    const mssm::CtxLayout cl = mssm::ctx_layout(p->batch, p->seqlen, p->dim, p->dstate);
+    if (ctx_bytes < cl.total) return MSSM_ERR_WORKSPACE;
+    const size_t need = mssm::bwd_saved_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate);
+    if (!workspace || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
+
+    mssm::ScanArgs a = base_args(p);
+    a.u = u; a.delta = delta; a.z = z; a.Bm = Bm; a.Cm = Cm;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias;
+    a.dy = dy; a.dh_final = dh_final;
+    a.du = du; a.ddelta = ddelta; a.dz = z ? dz : nullptr; a.dB = dB; a.dC = dC;
+    a.dA = dA; a.dD = dD; a.ddt_bias = ddt_bias; a.dh0 = dh0;
+    a.ctx_ckpt = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ctx)) + cl.ckpt);
+    a.ctx_s = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ctx)) + cl.s);
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return from_hip(mssm::launch_bwd_saved(a, static_cast<hipStream_t>(hip_stream)));
+}
+
 mssm_status mssm_step(const mssm_problem* p, const void* u_t, const void* delta_t, const float* A,
                       const void* Bm_t, const void* Cm_t, const float* Dskip, const void* z_t,
                       const float* dt_bias, float* state, void* y_t, void* hip_stream) {

@@ -60,8 +60,13 @@ struct BwdKArgs {
     const float* Dskip;
     const float* dt_bias;
     const float* dh_final;
-    const float* ckpt;   // (B, tiles, N, D) state before every tile (pre-pass)
-    const float* sbar;   // (B, L, D) (pre-pass)
+    const float* ckpt;   // (B, tiles, N, D) state before every tile (pre-pass, or the saved context)
+    const float* sbar;   // (B, L, D) (pre-pass); null with a saved context
+    // saved context: sbar and dz are formed from dy, z and the forward's readout s
+    const void* dy;
+    const void* z;        // nullable: no gate
+    const float* s_saved; // (B, L, D) sum_n Cm h + Dskip u (with z)
+    void* dz;             // (B, L, D) (with z)
     void* du;
     void* ddelta;
     void* dB;
@@ -181,6 +186,31 @@ __device__ __forceinline__ void fetch_rows(const T* __restrict__ u_b, const T* _
     }
 }
 
+// Saved context: raw u, delta, dy, z and the forward's readout s of this
+// wave's rows of tile `tile` (clamped as fetch_rows).
+template <typename T, int SPW>
+__device__ __forceinline__ void fetch_rows_saved(const T* __restrict__ u_b, const T* __restrict__ d_b,
+                                                 const T* __restrict__ dy_b, const T* __restrict__ z_b,
+                                                 const float* __restrict__ s_b, int tile, int L32, int D32,
+                                                 int first_row, int lo, float (&ru)[SPW], float (&rd)[SPW],
+                                                 float (&rdy)[SPW], float (&rz)[SPW], float (&rs)[SPW]) {
+    const int t0 = max(tile, 0) * kTB;
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int t = min(t0 + first_row + i, L32 - 1);
+        const int64_t off = static_cast<int64_t>(t) * D32 + lo;
+        ru[i] = load_act(u_b, off);
+        rd[i] = load_act(d_b, off);
+        rdy[i] = load_act(dy_b, off);
+        if (z_b) {
+            rz[i] = load_act(z_b, off);
+            rs[i] = s_b[off];
+        } else {
+            rz[i] = rs[i] = 0.0f;
+        }
+    }
+}
+
 // What a wave keeps of one of its rows from preparing it until finishing it.
 struct RowKeep {
     float u, sig, dt, sb;  // u, dDelta/dx (sigmoid(x) with softplus, else 1), Delta, sbar
@@ -202,6 +232,33 @@ __device__ __forceinline__ void prep_rows(const float (&ru)[SPW], const float (&
         const float sb = dvalid ? rs[i] : 0.0f;
         dst[w * SPW + i][lane] = make_float4(dt, dt * uu, sb, 0.0f);
         keep[i] = RowKeep{uu, sg, dt, sb};
+    }
+}
+
+// Saved context: the gate's two factors of each row from dy, z and the
+// forward's readout s: rs[i] <- sbar = dy silu(z) (dy without a gate), and dz
+// = dy s silu'(z) stored for rows [0, nstore) of the tile at dz_tile (none
+// for a tile outside this walk: another walk stores it).
+template <typename T, int SPW>
+__device__ __forceinline__ void gate_rows(const float (&rdy)[SPW], const float (&rz)[SPW], float (&rs)[SPW],
+                                          bool has_z, int w, int lane, bool dvalid, int nstore, T* dz_tile,
+                                          int D32) {
+    const __amdgpu_buffer_rsrc_t rdz =
+        make_rsrc(has_z ? dz_tile : nullptr, static_cast<uint32_t>(kTB) * static_cast<uint32_t>(D32) * sizeof(T));
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        if (has_z) {
+            const float zz = rz[i], sg = sigmoid(zz);
+            const float dzf = rdy[i] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
+            const int j = w * SPW + i;
+            const uint32_t off = (dvalid && j < nstore) ? (static_cast<uint32_t>(j) * static_cast<uint32_t>(D32) +
+                                                           static_cast<uint32_t>(lane)) * sizeof(T)
+                                                        : kNoStore;
+            buffer_store_act(rs[i] * dzf, rdz, off, T{});
+            rs[i] = rdy[i] * zz * sg;
+        } else {
+            rs[i] = rdy[i];
+        }
     }
 }
 
@@ -402,7 +459,8 @@ __device__ __forceinline__ void rev_steps(std::integer_sequence<int, I...>, cons
 template <typename T, int NG, int G>
 struct RevRegs {
     static constexpr int SPW = kTB / helper_waves(G);
-    float ru[SPW], rd[SPW], rs[SPW];  // raw u, delta, sbar of the next tile to prepare
+    float ru[SPW], rd[SPW], rs[SPW];  // raw u, delta, sbar (saved context: s) of the next tile to prepare
+    float rdy[SPW], rz[SPW];          // saved context: its raw dy, z
     uint32_t qb[LaneRow<T, NG>::kWords], qc[LaneRow<T, NG>::kWords];  // Bm/Cm of the next tile
     float hin_next[NG];               // checkpoint of the next tile
     RowKeep keep_c[SPW], keep_p[SPW];  // rows of the tile in flight / of the tile to finish
@@ -421,7 +479,10 @@ struct RevBlock {
     int64_t row_b, last_row, ck_stride;
     const T* u_b;
     const T* d_b;
-    const float* s_b;
+    const float* s_b;   // sbar, or with a saved context the forward's readout s
+    const T* dy_b;      // saved context: dy, z, dz of the block's first row (z, dz null without a gate)
+    const T* z_b;
+    T* dz_b;
     const T* Bm;
     const T* Cm;
     T* du_b;
@@ -440,7 +501,7 @@ struct RevBlock {
 //      the two partial-sum buffers (tile k + 1's are still being read).
 // FULL: all 16 steps of the tile exist (every tile but a ragged last one).
 // HELPER: a helper wave (rows' front end and finishing), else a state wave.
-template <bool FULL, bool HELPER, typename T, int NG, int G>
+template <bool FULL, bool HELPER, bool SAVED, typename T, int NG, int G>
 __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int nval, const float (&A2)[NG],
                                              const float (&Aval)[NG], RevRegs<T, NG, G>& r,
                                              float4 (&sX)[2][kTB][64], float2 (&sLQ)[2][G][kTB][64]) {
@@ -455,9 +516,19 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
                                    bk.Dk, bk.du_b + off, bk.dd_b + off, bk.D32, r.accD, r.accBias);
         }
         RowKeep keep_n[SPW];
+        if constexpr (SAVED) {  // tile k - 1's dz, unless that tile belongs to the walk before
+            const int tp = max(k - 1, 0);
+            gate_rows<T, SPW>(r.rdy, r.rz, r.rs, bk.z_b != nullptr, bk.hw, lane, bk.dvalid,
+                              k - 1 >= bk.tile_begin ? min(kTB, bk.L32 - tp * kTB) : 0,
+                              bk.dz_b + static_cast<int64_t>(tp) * kTB * bk.D32, bk.D32);
+        }
         prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, bk.hw, lane, sX[prv],
                        keep_n);  // k == 0: unused
-        fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, k - 2, bk.L32, bk.D32, bk.hw * SPW, bk.lo, r.ru, r.rd, r.rs);
+        if constexpr (SAVED)
+            fetch_rows_saved<T, SPW>(bk.u_b, bk.d_b, bk.dy_b, bk.z_b, bk.s_b, k - 2, bk.L32, bk.D32, bk.hw * SPW,
+                                     bk.lo, r.ru, r.rd, r.rdy, r.rz, r.rs);
+        else
+            fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, k - 2, bk.L32, bk.D32, bk.hw * SPW, bk.lo, r.ru, r.rd, r.rs);
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             r.keep_p[i] = r.keep_c[i];
@@ -507,7 +578,7 @@ __device__ __forceinline__ void rev_interval(const RevBlock<T>& bk, int k, int n
 }
 
 // The reverse walk over the chunk's tiles.  Both roles execute the same barriers.
-template <bool HELPER, typename T, int NG, int G>
+template <bool HELPER, bool SAVED, typename T, int NG, int G>
 __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)[NG], const float (&Aval)[NG],
                                         RevRegs<T, NG, G>& r, float4 (&sX)[2][kTB][64],
                                         float2 (&sLQ)[2][G][kTB][64]) {
@@ -519,11 +590,23 @@ __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)
         const int tl = bk.tile_end - 1;
         const int64_t rowl = bk.row_b + static_cast<int64_t>(tl) * kTB;
         if constexpr (HELPER) {
-            fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl, bk.L32, bk.D32, bk.hw * SPW, bk.lo, r.ru, r.rd, r.rs);
+            if constexpr (SAVED) {
+                fetch_rows_saved<T, SPW>(bk.u_b, bk.d_b, bk.dy_b, bk.z_b, bk.s_b, tl, bk.L32, bk.D32, bk.hw * SPW,
+                                         bk.lo, r.ru, r.rd, r.rdy, r.rz, r.rs);
+                gate_rows<T, SPW>(r.rdy, r.rz, r.rs, bk.z_b != nullptr, bk.hw, lane, bk.dvalid,
+                                  min(kTB, bk.L32 - tl * kTB), bk.dz_b + static_cast<int64_t>(tl) * kTB * bk.D32,
+                                  bk.D32);
+            } else {
+                fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl, bk.L32, bk.D32, bk.hw * SPW, bk.lo, r.ru, r.rd, r.rs);
+            }
             prep_rows<SPW>(r.ru, r.rd, r.rs, bk.bias, bk.softplus_on, bk.dvalid, bk.hw, lane, sX[tl & 1],
                            r.keep_c);
-            fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl - 1, bk.L32, bk.D32, bk.hw * SPW, bk.lo, r.ru, r.rd,
-                               r.rs);
+            if constexpr (SAVED)
+                fetch_rows_saved<T, SPW>(bk.u_b, bk.d_b, bk.dy_b, bk.z_b, bk.s_b, tl - 1, bk.L32, bk.D32,
+                                         bk.hw * SPW, bk.lo, r.ru, r.rd, r.rdy, r.rz, r.rs);
+            else
+                fetch_rows<T, SPW>(bk.u_b, bk.d_b, bk.s_b, tl - 1, bk.L32, bk.D32, bk.hw * SPW, bk.lo, r.ru, r.rd,
+                                   r.rs);
         } else {
             fetch_tile_rows<T, NG>(bk.Bm, rowl, bk.last_row, N, n0, lane, r.qb);
             fetch_tile_rows<T, NG>(bk.Cm, rowl, bk.last_row, N, n0, lane, r.qc);
@@ -536,9 +619,9 @@ __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)
     for (int k = bk.tile_end - 1; k >= bk.tile_begin; --k) {
         const int nval = min(kTB, bk.L32 - k * kTB);
         if (nval == kTB)
-            rev_interval<true, HELPER>(bk, k, kTB, A2, Aval, r, sX, sLQ);
+            rev_interval<true, HELPER, SAVED>(bk, k, kTB, A2, Aval, r, sX, sLQ);
         else
-            rev_interval<false, HELPER>(bk, k, nval, A2, Aval, r, sX, sLQ);
+            rev_interval<false, HELPER, SAVED>(bk, k, nval, A2, Aval, r, sX, sLQ);
         __syncthreads();
     }
     // ---- epilogue: finish the chunk's first tile
@@ -554,7 +637,7 @@ __device__ __forceinline__ void rev_run(const RevBlock<T>& bk, const float (&A2)
 // the helper waves; workgroup (blk, u) walks the time chunks of walk u of
 // channel block blk backwards, starting from the adjoint that enters its last
 // chunk at that chunk's end.
-template <typename T, int NG, int G>
+template <typename T, int NG, int G, bool SAVED>
 __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel(BwdKArgs a) {
     constexpr int N = NG * G;
     constexpr int H = helper_waves(G);
@@ -596,7 +679,10 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
     bk.ck_stride = D * N;
     bk.u_b = static_cast<const T*>(a.u) + bk.row_b * D + chan0;
     bk.d_b = static_cast<const T*>(a.delta) + bk.row_b * D + chan0;
-    bk.s_b = a.sbar + bk.row_b * D + chan0;
+    bk.s_b = SAVED ? (a.z ? a.s_saved + bk.row_b * D + chan0 : nullptr) : a.sbar + bk.row_b * D + chan0;
+    bk.dy_b = SAVED ? static_cast<const T*>(a.dy) + bk.row_b * D + chan0 : nullptr;
+    bk.z_b = (SAVED && a.z) ? static_cast<const T*>(a.z) + bk.row_b * D + chan0 : nullptr;
+    bk.dz_b = (SAVED && a.z) ? static_cast<T*>(a.dz) + bk.row_b * D + chan0 : nullptr;
     bk.Bm = static_cast<const T*>(a.Bm);
     bk.Cm = static_cast<const T*>(a.Cm);
     bk.du_b = static_cast<T*>(a.du) + bk.row_b * D + chan0;
@@ -629,9 +715,9 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
     for (int i = 0; i < SPW; ++i) r.keep_p[i] = RowKeep{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (state_wave)
-        rev_run<false>(bk, A2, Aval, r, sX, sLQ);
+        rev_run<false, SAVED>(bk, A2, Aval, r, sX, sLQ);
     else
-        rev_run<true>(bk, A2, Aval, r, sX, sLQ);
+        rev_run<true, SAVED>(bk, A2, Aval, r, sX, sLQ);
     // ---- per-(b, d) results
     if (state_wave && bk.dvalid) {
         float* pa = a.pA + ((b * a.units + unit) * D + dc) * N + n0;
@@ -702,7 +788,7 @@ __device__ __forceinline__ void for_slots(F&& f, std::integer_sequence<int, S...
     (f(Slot<S>{}), ...);
 }
 
-template <typename T, int NG, int G, int PF>
+template <typename T, int NG, int G, int PF, bool SAVED>
 __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
     constexpr int N = NG * G;
     constexpr int SPW = kTB / G;
@@ -737,27 +823,36 @@ __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
     const int64_t row_b = b * L;
     const int64_t last_row = row_b + L - 1;
     const T* d_b = static_cast<const T*>(a.delta) + row_b * D + chan0;
-    const float* s_b = a.sbar + row_b * D + chan0;
+    const float* s_b = SAVED ? nullptr : a.sbar + row_b * D + chan0;
+    // saved context: sbar = dy silu(z) formed here from dy and z
+    const T* dy_b = SAVED ? static_cast<const T*>(a.dy) + row_b * D + chan0 : nullptr;
+    const T* z_b = (SAVED && a.z) ? static_cast<const T*>(a.z) + row_b * D + chan0 : nullptr;
     const T* Cm = static_cast<const T*>(a.Cm);
     // loads of PF tiles in flight, in a ring of register slots: tile t's raw rows and Cm sit in slot
     // (te - 1 - t) % PF, issued PF tiles before its steps (one tile of steps does not cover a load's latency)
-    float rd[PF][SPW], rs[PF][SPW];
+    float rd[PF][SPW], rs[PF][SPW], rz[PF][SPW];
     uint32_t qc[PF][W];
 
-    // raw delta and sbar of this wave's rows of `tile` (clamped to the last row), and the tile's Cm
-    auto fetch = [&](int tile, float (&d)[SPW], float (&sb)[SPW], uint32_t (&q)[W]) {
+    // raw delta and sbar (saved context: dy, and z in zz) of this wave's rows of `tile` (clamped to the
+    // last row), and the tile's Cm
+    auto fetch = [&](int tile, float (&d)[SPW], float (&sb)[SPW], float (&zz)[SPW], uint32_t (&q)[W]) {
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int t = min(tile * kTB + w * SPW + i, L32 - 1);
             const int64_t off = static_cast<int64_t>(t) * D + lo;
             d[i] = load_act(d_b, off);
-            sb[i] = s_b[off];
+            if constexpr (SAVED) {
+                sb[i] = load_act(dy_b, off);
+                zz[i] = z_b ? load_act(z_b, off) : 0.0f;
+            } else {
+                sb[i] = s_b[off];
+            }
         }
         fetch_tile_rows<T, NG>(Cm, row_b + static_cast<int64_t>(tile) * kTB, last_row, N, n0, lane, q);
     };
     // (Delta, sbar) of this wave's rows of `tile` into buffer `buf`; a tile before the chunk (the one after
     // its first, in the unconditional main loop) is written to the unused buffer and left out of the sum
-    auto prep = [&](int tile, int buf, const float (&d)[SPW], const float (&sb)[SPW]) {
+    auto prep = [&](int tile, int buf, const float (&d)[SPW], const float (&sb)[SPW], const float (&zz)[SPW]) {
         const int nval = min(kTB, L32 - tile * kTB);
         const bool in = tile >= tb;
 #pragma unroll
@@ -766,7 +861,8 @@ __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
             if (j < nval) {
                 const float x = d[i] + bias;
                 const float dt = a.softplus ? softplus(x) : x;
-                sDS[buf][j][lane] = make_float2(dt, sb[i]);
+                const float sbar = (SAVED && z_b) ? sb[i] * zz[i] * sigmoid(zz[i]) : sb[i];  // as the pre-pass
+                sDS[buf][j][lane] = make_float2(dt, sbar);
                 psum += in ? dt : 0.0f;
             }
         }
@@ -782,8 +878,8 @@ __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
         const int cur = tile & 1;
         float Ct[NG];
         unpack_lane_row<T, NG>(qc[S], Ct);
-        if (MAIN || tile - 1 >= tb) prep(tile - 1, cur ^ 1, rd[(S + 1) % PF], rs[(S + 1) % PF]);
-        if (MAIN) fetch(max(tile - PF, tb), rd[S], rs[S], qc[S]);
+        if (MAIN || tile - 1 >= tb) prep(tile - 1, cur ^ 1, rd[(S + 1) % PF], rs[(S + 1) % PF], rz[(S + 1) % PF]);
+        if (MAIN) fetch(max(tile - PF, tb), rd[S], rs[S], rz[S], qc[S]);
         const int nval = min(kTB, L32 - tile * kTB);
         float2 xs[kTB];
 #pragma unroll
@@ -798,8 +894,8 @@ __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
     using Rest = std::false_type;
 
 #pragma unroll
-    for (int i = 0; i < PF; ++i) fetch(max(te - 1 - i, tb), rd[i], rs[i], qc[i]);
-    prep(te - 1, (te - 1) & 1, rd[0], rs[0]);
+    for (int i = 0; i < PF; ++i) fetch(max(te - 1 - i, tb), rd[i], rs[i], rz[i], qc[i]);
+    prep(te - 1, (te - 1) & 1, rd[0], rs[0], rz[0]);
     __syncthreads();
     int base = te - 1;
     // groups of PF tiles, every slot index a constant; then the fewer than PF tiles left, their loads issued
@@ -895,13 +991,15 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct WsLayout {
     size_t fwd, ckpt, sbar, pBC, pA, pD, pbias, qlam, slam, pin, total;
 };
-WsLayout ws_layout(int64_t B, int64_t L, int64_t D, int64_t N, int64_t tiles, int64_t K) {
+// `saved`: the backward from a saved context, with no pre-pass (no forward
+// scratch, checkpoints or sbar).
+WsLayout ws_layout(int64_t B, int64_t L, int64_t D, int64_t N, int64_t tiles, int64_t K, bool saved = false) {
     const int64_t dblocks = (D + 63) / 64;
     WsLayout w{};
     size_t off = 0;
-    w.fwd = off;   off += align256(plan_fwd(B, L, D, N).ws_bytes);
-    w.ckpt = off;  off += align256(static_cast<size_t>(B) * tiles * D * N * 4);
-    w.sbar = off;  off += align256(static_cast<size_t>(B) * L * D * 4);
+    w.fwd = off;   off += saved ? 0 : align256(plan_fwd(B, L, D, N).ws_bytes);
+    w.ckpt = off;  off += saved ? 0 : align256(static_cast<size_t>(B) * tiles * D * N * 4);
+    w.sbar = off;  off += saved ? 0 : align256(static_cast<size_t>(B) * L * D * 4);
     w.pBC = off;   off += align256(static_cast<size_t>(B) * L * dblocks * 2 * N * 4);
     w.pA = off;    off += align256(static_cast<size_t>(B) * K * D * N * 4);
     w.pD = off;    off += align256(static_cast<size_t>(B) * K * D * 4);
@@ -913,16 +1011,26 @@ WsLayout ws_layout(int64_t B, int64_t L, int64_t D, int64_t N, int64_t tiles, in
     return w;
 }
 
-template <typename T, int NG, int G>
+// SAVED: from the context a training forward saved (checkpoints and readout),
+// with no pre-pass; else the pre-pass recomputes the checkpoints.
+template <typename T, int NG, int G, bool SAVED>
 hipError_t launch_bwd_t(const ScanArgs& s, hipStream_t st) {
     const BwdPlan pl = plan_bwd(s.B, s.L, s.D, s.N);
-    const WsLayout wl = ws_layout(s.B, s.L, s.D, s.N, pl.tiles, pl.chunks);
+    const WsLayout wl = ws_layout(s.B, s.L, s.D, s.N, pl.tiles, pl.chunks, SAVED);
     char* ws = static_cast<char*>(s.workspace);
-    float* ckpt = reinterpret_cast<float*>(ws + wl.ckpt);
-    float* sbar = reinterpret_cast<float*>(ws + wl.sbar);
-    hipError_t e = launch_fwd_prepass(s, ws + wl.fwd, ckpt, sbar, st);
-    if (e != hipSuccess) return e;
+    float* ckpt = SAVED ? s.ctx_ckpt : reinterpret_cast<float*>(ws + wl.ckpt);
+    float* sbar = SAVED ? nullptr : reinterpret_cast<float*>(ws + wl.sbar);
+    if constexpr (!SAVED) {
+        hipError_t e = launch_fwd_prepass(s, ws + wl.fwd, ckpt, sbar, st);
+        if (e != hipSuccess) return e;
+    }
     BwdKArgs a{};
+    if constexpr (SAVED) {
+        a.dy = s.dy;
+        a.z = s.z;
+        a.s_saved = s.ctx_s;
+        a.dz = s.dz;
+    }
     a.u = s.u; a.delta = s.delta; a.Bm = s.Bm; a.Cm = s.Cm;
     a.A = s.A; a.Dskip = s.Dskip; a.dt_bias = s.dt_bias; a.dh_final = s.dh_final;
     a.ckpt = ckpt; a.sbar = sbar;
@@ -950,12 +1058,12 @@ hipError_t launch_bwd_t(const ScanArgs& s, hipStream_t st) {
         // reverse kernel forms the long walk's entering adjoint itself (no carry pass)
         constexpr int Gq = NG * G < 16 ? NG * G : 16;
         constexpr int NGq = NG * G / Gq;
-        hipLaunchKernelGGL((bwd_chunk_lambda_kernel<T, NGq, Gq, 4>), dim3(nblk, 1u), dim3(64 * Gq), 0, st, a);
+        hipLaunchKernelGGL((bwd_chunk_lambda_kernel<T, NGq, Gq, 4, SAVED>), dim3(nblk, 1u), dim3(64 * Gq), 0, st, a);
     } else if (pl.chunks > 1) {
         // its own layout: four states per wave where N allows (no LDS partial sums to keep small)
         constexpr int NGc = NG * G >= 16 ? (NG > 4 ? NG : 4) : NG;
         constexpr int Gc = NG * G / NGc;
-        hipLaunchKernelGGL((bwd_chunk_lambda_kernel<T, NGc, Gc, 4>),
+        hipLaunchKernelGGL((bwd_chunk_lambda_kernel<T, NGc, Gc, 4, SAVED>),
                            dim3(nblk, static_cast<unsigned>(pl.chunks - pl.head_chunks)),
                            dim3(64 * Gc), 0, st, a);
         const int64_t threads = s.B * s.D * s.N;
@@ -964,7 +1072,7 @@ hipError_t launch_bwd_t(const ScanArgs& s, hipStream_t st) {
     }
     // walk 0 of every block first: with one long walk per block and the short ones after it, the hardware's
     // in-order dispatch gives each long walk a CU of its own and runs the short ones on the rest as they free up
-    hipLaunchKernelGGL((bwd_reverse_kernel<T, NG, G>), dim3(nblk, static_cast<unsigned>(pl.units)),
+    hipLaunchKernelGGL((bwd_reverse_kernel<T, NG, G, SAVED>), dim3(nblk, static_cast<unsigned>(pl.units)),
                        dim3(64 * (G + helper_waves(G))), 0, st, a);
     const int64_t items = s.B * s.L * s.N + s.D * s.N + s.D;
     const int64_t blocks = std::min<int64_t>((items + 255) / 256, 16384);
@@ -972,16 +1080,16 @@ hipError_t launch_bwd_t(const ScanArgs& s, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool SAVED>
 hipError_t dispatch_n(const ScanArgs& s, hipStream_t st) {
     switch (s.N) {  // NG states per wave x G waves; NG divides 8 (16-value batches)
-        case 1: return launch_bwd_t<T, 1, 1>(s, st);
-        case 2: return launch_bwd_t<T, 1, 2>(s, st);
-        case 4: return launch_bwd_t<T, 1, 4>(s, st);
-        case 8: return launch_bwd_t<T, 2, 4>(s, st);
-        case 16: return launch_bwd_t<T, 2, 8>(s, st);
-        case 32: return launch_bwd_t<T, 4, 8>(s, st);
-        case 64: return launch_bwd_t<T, 8, 8>(s, st);
+        case 1: return launch_bwd_t<T, 1, 1, SAVED>(s, st);
+        case 2: return launch_bwd_t<T, 1, 2, SAVED>(s, st);
+        case 4: return launch_bwd_t<T, 1, 4, SAVED>(s, st);
+        case 8: return launch_bwd_t<T, 2, 4, SAVED>(s, st);
+        case 16: return launch_bwd_t<T, 2, 8, SAVED>(s, st);
+        case 32: return launch_bwd_t<T, 4, 8, SAVED>(s, st);
+        case 64: return launch_bwd_t<T, 8, 8, SAVED>(s, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1032,7 +1140,26 @@ BwdPlan plan_bwd(int64_t B, int64_t L, int64_t D, int64_t N) {
 }
 
 hipError_t launch_bwd(const ScanArgs& s, hipStream_t st) {
-    return s.dtype == 1 ? dispatch_n<uint16_t>(s, st) : dispatch_n<float>(s, st);
+    return s.dtype == 1 ? dispatch_n<uint16_t, false>(s, st) : dispatch_n<float, false>(s, st);
+}
+
+CtxLayout ctx_layout(int64_t B, int64_t L, int64_t D, int64_t N) {
+    CtxLayout c{};
+    const int64_t tiles = (L + kTB - 1) / kTB;
+    c.ckpt = 0;
+    c.s = align256(static_cast<size_t>(B) * tiles * N * D * 4);
+    c.total = c.s + align256(static_cast<size_t>(B) * L * D * 4);
+    return c;
+}
+
+size_t bwd_saved_ws_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
+    const BwdPlan p = plan_bwd(B, L, D, N);
+    return ws_layout(B, L, D, N, p.tiles, p.chunks, true).total;
+}
+
+hipError_t launch_bwd_saved(const ScanArgs& s, hipStream_t st) {
+    if (!s.ctx_ckpt || (s.z && !s.ctx_s)) return hipErrorInvalidValue;
+    return s.dtype == 1 ? dispatch_n<uint16_t, true>(s, st) : dispatch_n<float, true>(s, st);
 }
 
 }  // namespace mssm

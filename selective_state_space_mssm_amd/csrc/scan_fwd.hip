@@ -82,12 +82,15 @@ FwdPlan plan_fwd(int64_t B, int64_t L, int64_t D, int64_t N) {
 }
 
 hipError_t launch_fwd(const ScanArgs& s, hipStream_t st) {
-    if (use_tokens(s.B, s.L, s.D)) return launch_tokens(s, st);  // a few tokens: the state moves once (scan_step.hip)
+    // a few tokens: the state moves once (scan_step.hip); a training forward keeps the tiled path's checkpoints
+    if (!s.ctx_ckpt && use_tokens(s.B, s.L, s.D)) return launch_tokens(s, st);
     const FwdPlan pl = plan_fwd(s.B, s.L, s.D, s.N);
     const PreOut none{};
     return s.dtype == 1 ? dispatch_n<uint16_t, false, false>(s, pl, s.workspace, none, st)
                         : dispatch_n<float, false, false>(s, pl, s.workspace, none, st);
 }
+
+hipError_t launch_fwd_train(const ScanArgs& s, hipStream_t st) { return s.ctx_ckpt ? launch_fwd(s, st) : hipErrorInvalidValue; }
 
 hipError_t launch_fwd_prepass(const ScanArgs& s, void* fwd_scratch, float* ckpt, float* sbar, hipStream_t st) {
     const FwdPlan pl = plan_fwd(s.B, s.L, s.D, s.N);

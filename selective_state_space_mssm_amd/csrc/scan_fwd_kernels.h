@@ -126,8 +126,10 @@ struct FwdKArgs {
     const void* dy;
     void* dz;              // nullable (no gate)
     float* sbar;           // (B, L, D) dy * silu(z), or dy without a gate
-    float* ckpt;           // (B, tiles, N, D) state before every kTB-step tile
+    float* ckpt;           // (B, tiles, N, D) state before every kTB-step tile (forward: nullable)
     int64_t tiles;         // ceil(L / kTB)
+    // forward saving a training context: ckpt above and the readout before the gate
+    float* s_out;          // (B, L, D) sum_n Cm h + Dskip u, float32; nullable
     // fused causal conv1d + SiLU front end only: u holds the conv input x
     const float* conv_w;   // (D, d_conv)
     const float* conv_b;   // (D) nullable
@@ -399,7 +401,8 @@ struct FwdSeg {
     const T* Bm_seg;  // row (b, t_begin) of Bm / Cm
     const T* Cm_seg;
     float* sbar_seg;  // pre-pass: element (b, t_begin, chan0) of sbar
-    float* ckpt_seg;  // pre-pass: element (b, t_begin / kTB, 0, chan0) of the (B, tiles, N, D) states
+    float* ckpt_seg;  // element (b, t_begin / kTB, 0, chan0) of the (B, tiles, N, D) states (forward: nullable)
+    float* s_seg;     // forward saving a context: element (b, t_begin, chan0) of s_out, or null
     uint32_t row_off[SPW];  // byte offset of this wave's row i of a tile, this lane's channel
     uint32_t bc_off;        // byte offset of this lane's Bm/Cm values in a tile (step lane % 16)
     // fused conv front end (u_seg then points at x)
@@ -606,7 +609,7 @@ __device__ __forceinline__ void store_sbar(const FwdSeg<T, NG, G, HAS_Z, PRE, CO
 
 // Sum of the G partial readouts plus the skip term, times the gate, of this
 // wave's rows of segment tile `tile` -> y (pre-pass: dz).
-template <typename T, int NG, int G, bool HAS_Z, bool PRE, bool CONV>
+template <bool SAVE, typename T, int NG, int G, bool HAS_Z, bool PRE, bool CONV>
 __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE, CONV>& sg, int tile,
                                             const float (&part)[kTB / helper_waves(NG, G, PRE)][G], const float (&skip)[kTB / helper_waves(NG, G, PRE)],
                                             const float (&gate)[kTB / helper_waves(NG, G, PRE)]) {
@@ -616,6 +619,11 @@ __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE, C
     const __amdgpu_buffer_rsrc_t ry =
         make_rsrc(sg.y_seg + (rows > 0 ? static_cast<int64_t>(tile) * kTB * sg.D : 0),
                   static_cast<uint32_t>(kTB) * static_cast<uint32_t>(D32) * sizeof(T));
+    // training forward: the readout before the gate, float32, at the same element offsets
+    constexpr bool SAVE_S = SAVE && HAS_Z && !PRE;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(SAVE_S ? sg.s_seg + (rows > 0 ? static_cast<int64_t>(tile) * kTB * sg.D : 0) : nullptr,
+                  static_cast<uint32_t>(kTB) * static_cast<uint32_t>(D32) * 4u);
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
         float s = 0.0f;
@@ -627,6 +635,12 @@ __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE, C
                                       static_cast<uint32_t>(sg.lane)) * static_cast<uint32_t>(sizeof(T))
                                    : kNoStore;
         buffer_store_act((s + skip[i]) * gate[i], ry, off, T{});
+        if constexpr (SAVE_S) {
+            const uint32_t so = store ? (static_cast<uint32_t>(j) * static_cast<uint32_t>(D32) +
+                                         static_cast<uint32_t>(sg.lane)) * 4u
+                                      : kNoStore;
+            buffer_store_act(s + skip[i], rs, so, 0.0f);
+        }
     }
 }
 
@@ -643,7 +657,7 @@ __device__ __forceinline__ void finish_rows(const FwdSeg<T, NG, G, HAS_Z, PRE, C
 // register sets used alternately by consecutive intervals, so nothing is copied).
 // HELPER: a helper wave (front end and finishing of rows); else a state wave
 // (recurrence of its states).
-template <bool FULL, bool HELPER, typename T, int NG, int G, bool HAS_Z, bool PRE, bool CONV>
+template <bool FULL, bool HELPER, bool SAVE, typename T, int NG, int G, bool HAS_Z, bool PRE, bool CONV>
 __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE, CONV>& sg, int k, int nval,
                                              const float (&A2)[NG], float (&h)[NG], FwdRegs<T, NG, G, PRE, CONV>& r,
                                              const float2 (&ddt)[kTB], float2 (&ddt_next)[kTB],
@@ -661,7 +675,7 @@ __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE, 
         prep_rows(sg, k + 2, r.ru, r.rd, r.rz, r.rdy, sDD[cur], skip_nn, gate_nn, sbv);  // buffer (k + 2) & 1 == k & 1
         fetch_rows<false>(sg, k + 3, r.ru, r.rd, r.rz, r.rdy);
         store_sbar(sg, k + 2, sbv);
-        finish_rows(sg, k - 1, part, r.skip_p, r.gate_p);  // k == 0: nothing stored
+        finish_rows<SAVE>(sg, k - 1, part, r.skip_p, r.gate_p);  // k == 0: nothing stored
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             r.skip_p[i] = r.skip_c[i];
@@ -678,7 +692,7 @@ __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE, 
         unpack_lane_row<T, NG>(r.qb, Bt);
         unpack_lane_row<T, NG>(r.qc, Ct);
         fetch_bc(sg, k + 1, r.qb, r.qc);
-        if constexpr (PRE) {  // the state before tile k: per state one 64-channel row, coalesced
+        if constexpr (PRE || SAVE) {  // the state before tile k: per state one 64-channel row, coalesced
 #pragma unroll
             for (int q = 0; q < NG; ++q) {
                 const __amdgpu_buffer_rsrc_t rc =
@@ -697,7 +711,7 @@ __device__ __forceinline__ void fwd_interval(const FwdSeg<T, NG, G, HAS_Z, PRE, 
 // Runs steps [t_begin, t_end) of channel block `blk` (batch row b = blk /
 // dblocks, channels chan0 .. chan0 + 63) from the state in h, leaving the
 // final state in h.
-template <bool HELPER, typename T, int NG, int G, bool HAS_Z, bool PRE, bool CONV>
+template <bool HELPER, bool SAVE, typename T, int NG, int G, bool HAS_Z, bool PRE, bool CONV>
 __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t t_begin, int64_t t_end,
                                             float (&h)[NG], float2 (&sDD)[2][kTB][64],
                                             float (&sP)[2][G][kTB][64]) {
@@ -738,7 +752,8 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     sg.Bm_seg = static_cast<const T*>(a.Bm) + row_begin * N;
     sg.Cm_seg = static_cast<const T*>(a.Cm) + row_begin * N;
     sg.sbar_seg = PRE ? a.sbar + seg_off : nullptr;
-    sg.ckpt_seg = PRE ? a.ckpt + (b * a.tiles + t_begin / kTB) * N * D + chan0 : nullptr;
+    sg.ckpt_seg = (PRE || SAVE) ? a.ckpt + (b * a.tiles + t_begin / kTB) * N * D + chan0 : nullptr;
+    sg.s_seg = (SAVE && HAS_Z && !PRE) ? a.s_out + seg_off : nullptr;
     const int D32 = static_cast<int>(D);
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
@@ -788,19 +803,19 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
     const int nfull = sg.t_len / kTB;
     int k = 0;
     for (; k + 2 <= nfull; k += 2) {
-        fwd_interval<true, HELPER>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+        fwd_interval<true, HELPER, SAVE>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
         __syncthreads();
-        fwd_interval<true, HELPER>(sg, k + 1, kTB, A2, h, r, ddtB, ddtA, sDD, sP);
+        fwd_interval<true, HELPER, SAVE>(sg, k + 1, kTB, A2, h, r, ddtB, ddtA, sDD, sP);
         __syncthreads();
     }
     if (k < sg.ntiles) {
         if (k < nfull)
-            fwd_interval<true, HELPER>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+            fwd_interval<true, HELPER, SAVE>(sg, k, kTB, A2, h, r, ddtA, ddtB, sDD, sP);
         else
-            fwd_interval<false, HELPER>(sg, k, sg.t_len - k * kTB, A2, h, r, ddtA, ddtB, sDD, sP);
+            fwd_interval<false, HELPER, SAVE>(sg, k, sg.t_len - k * kTB, A2, h, r, ddtA, ddtB, sDD, sP);
         __syncthreads();
         if (k + 1 < sg.ntiles) {  // ragged last tile after a full one
-            fwd_interval<false, HELPER>(sg, k + 1, sg.t_len - (k + 1) * kTB, A2, h, r, ddtB, ddtA, sDD, sP);
+            fwd_interval<false, HELPER, SAVE>(sg, k + 1, sg.t_len - (k + 1) * kTB, A2, h, r, ddtB, ddtA, sDD, sP);
             __syncthreads();
         }
     }
@@ -812,7 +827,7 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
         for (int i = 0; i < SPW; ++i)
 #pragma unroll
             for (int g = 0; g < G; ++g) part[i][g] = sP[klast & 1][g][sg.hw * SPW + i][lane];
-        finish_rows(sg, klast, part, r.skip_p, r.gate_p);
+        finish_rows<SAVE>(sg, klast, part, r.skip_p, r.gate_p);
     }
 }
 
@@ -824,7 +839,9 @@ __device__ __forceinline__ void fwd_segment(const FwdKArgs& a, int blk, int64_t 
 //    of at least one block each (balanced_plan.h), a block split between two
 //    workers handing its state over through memory.  Equal work per
 //    workgroup, no extra arithmetic.
-template <typename T, int NG, int G, bool HAS_Z, bool PRE, bool CONV>
+// SAVE: the training forward, which also writes the state before every tile
+// (a.ckpt) and the readout before the gate (a.s_out).
+template <typename T, int NG, int G, bool HAS_Z, bool PRE, bool CONV, bool SAVE>
 __global__ __launch_bounds__(64 * (G + helper_waves(NG, G, PRE)))
 __attribute__((amdgpu_waves_per_eu(conv_min_waves(NG, G, CONV, sizeof(T) == 2)))) void scan_fwd_kernel(FwdKArgs a) {
     constexpr int N = NG * G;
@@ -903,9 +920,9 @@ __attribute__((amdgpu_waves_per_eu(conv_min_waves(NG, G, CONV, sizeof(T) == 2)))
         }
         // the same barriers on both paths: the roles differ only in work between them
         if (state_wave)
-            fwd_segment<false, T, NG, G, HAS_Z, PRE, CONV>(a, blk, t_begin, t_end, h, sDD, sP);
+            fwd_segment<false, SAVE, T, NG, G, HAS_Z, PRE, CONV>(a, blk, t_begin, t_end, h, sDD, sP);
         else
-            fwd_segment<true, T, NG, G, HAS_Z, PRE, CONV>(a, blk, t_begin, t_end, h, sDD, sP);
+            fwd_segment<true, SAVE, T, NG, G, HAS_Z, PRE, CONV>(a, blk, t_begin, t_end, h, sDD, sP);
         if (!state_wave) {
             if (to == kPublish) {  // the barriers of the state waves' hand-over
                 __threadfence();
@@ -1138,6 +1155,10 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, void* scratch, con
     a.dblocks = static_cast<int32_t>((s.D + 63) / 64);
     a.softplus = s.softplus;
     a.tiles = (s.L + kTB - 1) / kTB;
+    if constexpr (!PRE) {  // a training forward saves its context (null otherwise)
+        a.ckpt = s.ctx_ckpt;
+        a.s_out = s.z ? s.ctx_s : nullptr;
+    }
     if constexpr (PRE) {
         a.dy = pre.dy;
         a.dz = pre.dz;
@@ -1183,10 +1204,15 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, void* scratch, con
         }
     }
     const dim3 main_block(64 * (G + helper_waves(NG, G, PRE)));  // state waves + helper waves
-    if (s.z)
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE, CONV>), grid, main_block, 0, st, a);
+    const bool save = !PRE && !CONV && a.ckpt;  // the training forward
+    if (save && s.z)
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE, CONV, !PRE && !CONV>), grid, main_block, 0, st, a);
+    else if (save)
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false, PRE, CONV, !PRE && !CONV>), grid, main_block, 0, st, a);
+    else if (s.z)
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE, CONV, false>), grid, main_block, 0, st, a);
     else
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false, PRE, CONV>), grid, main_block, 0, st, a);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false, PRE, CONV, false>), grid, main_block, 0, st, a);
     return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), f"libmssm.so does not export {n}"
     assert sorted(mssm.EXPORTS) == names
@@ -248,6 +248,63 @@ def test_workspace_sizes_and_checks():
     # invalid problems report no workspace
     assert lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(good(N=65))) == 0
     assert lib.mssm_scan_bwd_workspace_bytes(None) == 0
+
+
+def fwd_train(p, ctx=FAKE, ctxb=1 << 40, ws=FAKE, wsb=1 << 40, **kw):
+    pp = ctypes.byref(p) if p is not None else None
+    v = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dskip=None, z=None, dt_bias=None, h0=None, y=FAKE,
+             hf=None)
+    a.update(kw)
+    return lib.mssm_scan_fwd_train(pp, *(v(a[k]) for k in ("u", "delta", "A", "Bm", "Cm", "Dskip", "z", "dt_bias",
+                                                            "h0", "y", "hf")), v(ctx), ctxb, v(ws), wsb, None)
+
+
+def bwd_saved(p, ctx=FAKE, ctxb=1 << 40, ws=FAKE, wsb=1 << 40, **kw):
+    pp = ctypes.byref(p) if p is not None else None
+    v = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dskip=None, z=None, dt_bias=None, dy=FAKE, dhf=None,
+             du=FAKE, ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, ddt_bias=None, dh0=None)
+    a.update(kw)
+    head = [v(a[k]) for k in ("u", "delta", "A", "Bm", "Cm", "Dskip", "z", "dt_bias")]
+    tail = [v(a[k]) for k in ("dy", "dhf", "du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddt_bias", "dh0")]
+    return lib.mssm_scan_bwd_saved(pp, *head, v(ctx), ctxb, *tail, v(ws), wsb, None)
+
+
+def test_training_pair_validation():
+    """mssm_scan_fwd_train / mssm_scan_bwd_saved: the forward's and backward's
+    checks, plus the context: required, at least mssm_scan_ctx_bytes, aligned,
+    and a power-of-two state size (the size queries return 0 otherwise)."""
+    p = good(2, 100, 70, 16)
+    nctx = lib.mssm_scan_ctx_bytes(ctypes.byref(p))
+    tiles = (100 + 15) // 16
+    assert nctx >= 2 * tiles * 16 * 70 * 4 + 2 * 100 * 70 * 4
+    assert lib.mssm_scan_ctx_bytes(ctypes.byref(good(N=12))) == 0
+    assert lib.mssm_scan_ctx_bytes(ctypes.byref(good(N=65))) == 0
+    assert lib.mssm_scan_ctx_bytes(None) == 0
+    nws = lib.mssm_scan_bwd_saved_workspace_bytes(ctypes.byref(p))
+    assert 0 < nws < lib.mssm_scan_bwd_workspace_bytes(ctypes.byref(p))  # no pre-pass scratch
+    assert lib.mssm_scan_bwd_saved_workspace_bytes(ctypes.byref(good(N=12))) == 0
+    for call in (fwd_train, bwd_saved):
+        assert call(None) == -1
+        assert call(good(N=12)) == -4
+        assert call(good(N=65)) == -4
+        assert call(p, ctx=None) == -1
+        assert call(p, ctx=MIS) == -5
+        assert call(p, ctxb=nctx - 1) == -6
+        assert call(p, u=None) == -1
+        assert call(p, A=MIS) == -5
+        bad = good(2, 100, 70, 16)
+        bad.dtype = 7
+        assert call(bad) == -3
+    long_ = P(1, 1 << 20, 1536, 16, 1, 1)
+    nf = lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(long_))
+    assert fwd_train(long_, ws=FAKE, wsb=nf - 1) == -6
+    assert bwd_saved(p, ws=None) == -6
+    assert bwd_saved(p, wsb=nws - 1) == -6
+    assert bwd_saved(p, dy=None) == -1
+    assert bwd_saved(p, z=FAKE, dz=None) == -1
+    assert bwd_saved(p, dC=None) == -1
 
 
 def fwd_noalloc(p, u=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, Dskip=None, z=None, dt_bias=None, h0=None,
