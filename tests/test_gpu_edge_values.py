@@ -151,6 +151,35 @@ def test_backward_edge_values(mssm, shape, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 150, 100), (1, 600, 70)])
+def test_training_pair_edge_values(mssm, shape, dtype):
+    # the training pair: the backward from the saved context forms sbar and dz from dy, z and the saved
+    # readout itself (silu' at |z| up to 100); (1, 600, 70): chunked forward and chunked reverse
+    B, L, D = shape
+    print(f"[edge train pair] shape={shape} dtype={dtype}", flush=True)
+    inp = edge_inputs(B, L, D, 16, dtype, seed=B * L + D + 5, with_dy=True)
+    rng = np.random.default_rng(5)
+    h0 = rng.standard_normal((B, D, 16)).astype(np.float32)
+    dhf = rng.standard_normal((B, D, 16)).astype(np.float32)
+    t = gpu_inputs(inp)
+    _, _, ctx = mssm.scan_fwd_train(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"],
+                                    t["dt_bias"], torch.from_numpy(h0).cuda())
+    g = mssm.scan_bwd_saved(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["dy"], ctx, t["Dskip"], t["z"],
+                            t["dt_bias"], torch.from_numpy(dhf).cuda())
+    torch.cuda.synchronize()
+    f = workloads.as_float32(inp)
+    r = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["Bm"], f["Cm"], f["dy"], Dskip=f["Dskip"], z=f["z"],
+                        dt_bias=f["dt_bias"], h0=h0, dh_final=dhf)
+    errs = {k: grad_err(to_np(g[k]), r[k]) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddt_bias",
+                                                     "dh0")}
+    print("  grad errs: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k in errs:
+        assert np.all(np.isfinite(to_np(g[k]))), k
+    bad = {k: v for k, v in errs.items() if not v <= GRAD_TOL[dtype]}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_step_edge_values(mssm, dtype):
     B, L, D, N = 3, 12, 100, 16
     print(f"[edge step] dtype={dtype}", flush=True)
