@@ -224,6 +224,26 @@ __device__ __forceinline__ void fmac_row_bcast_x4(float (&acc)[4], float c, cons
         : "v"(c), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "i"(J0), "i"(J0 + 1), "i"(J0 + 2), "i"(J0 + 3));
 }
 
+// Sum over aligned groups of R consecutive lanes (R = 1, 2, 4, 8 or 16),
+// every lane of a group receiving the group's sum.  Within-row DPP moves (no
+// LDS round trip, unlike a lane shuffle): swap neighbours, swap pairs of a
+// quad, then mirror the half-rows and the row; each step adds a lane's value
+// to the one at lane ^ m of the same partial sums, so the pairing, and the
+// result, are those of the butterfly s += shfl_xor(s, m), m = 1, 2, 4, 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int R>
+__device__ __forceinline__ float group_sum(float s) {
+    static_assert(R == 1 || R == 2 || R == 4 || R == 8 || R == 16, "groups of 1, 2, 4, 8 or 16 lanes");
+    if constexpr (R >= 2) s += dpp_move<0xB1>(s);   // quad_perm [1, 0, 3, 2]
+    if constexpr (R >= 4) s += dpp_move<0x4E>(s);   // quad_perm [2, 3, 0, 1]
+    if constexpr (R >= 8) s += dpp_move<0x141>(s);  // row_half_mirror: lane 7 - l of the half-row
+    if constexpr (R >= 16) s += dpp_move<0x140>(s); // row_mirror: lane 15 - l of the row
+    return s;
+}
+
 // ---- transcendental building blocks (hardware v_exp/v_log/v_rcp) --------
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

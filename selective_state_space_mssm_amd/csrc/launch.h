@@ -124,9 +124,9 @@ size_t bwd_ws_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype);
 hipError_t launch_fwd_any(const ScanArgs& a, hipStream_t s);
 hipError_t launch_conv_fwd_any(const ScanArgs& a, hipStream_t s);
 hipError_t launch_bwd_any(const ScanArgs& a, hipStream_t s);
-// Below this many (b, d) rows the short-sequence path loads 16 tokens' inputs
-// at a time (a few waves run the whole call and would otherwise wait on every
-// token's loads).
+// Below this many (b, d) rows the short-sequence path loads 8 tokens' inputs
+// at a time, the next 8 in flight while the current ones are computed (a few
+// waves run the whole call and would otherwise wait on every token's loads).
 constexpr int64_t kTokensDeepMaxRows = 4096;
 
 // Backward of the conv1d + SiLU front end (a.u = x, a.conv_w, a.conv_b,

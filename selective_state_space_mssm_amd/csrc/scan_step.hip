@@ -23,6 +23,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace mssm {
 namespace {
 
@@ -76,8 +78,7 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
             float prod = q < K ? a.conv_w[d * K + q] * in : 0.0f;
             const float next = __shfl(in, static_cast<int>(threadIdx.x & 63) + 1);
             if (q < K - 1) store_act(cs, q * a.D, next);
-#pragma unroll
-            for (int m = 1; m < R; m <<= 1) prod += __shfl_xor(prod, m);
+            prod = group_sum<R>(prod);
             c = (a.conv_b ? a.conv_b[d] : 0.0f) + prod;
         } else if (q == 0) {
             const int K = a.K;
@@ -127,8 +128,7 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
             st[n] = h;
         }
     }
-#pragma unroll
-    for (int m = 1; m < R; m <<= 1) s += __shfl_xor(s, m);
+    s = group_sum<R>(s);
     if (q == 0) {
         s = __builtin_fmaf(a.Dskip ? a.Dskip[d] : 0.0f, uu, s);
         if (a.z) s *= silu(load_act(static_cast<const T*>(a.z), i));
@@ -283,8 +283,7 @@ __global__ __launch_bounds__(256) void scan_tokens_kernel(TokKArgs a) {
             h[n] = __builtin_fmaf(fast_exp2(dt * A2[n]), h[n], du * bv[n]);  // A2 = A log2(e)
             s = __builtin_fmaf(cv[n], h[n], s);
         }
-#pragma unroll
-        for (int m = 1; m < R; m <<= 1) s += __shfl_xor(s, m);
+        s = group_sum<R>(s);
         if (q == 0) {
             s = __builtin_fmaf(Dk, uu, s);
             if (z) s *= silu(zz);
@@ -299,69 +298,89 @@ __global__ __launch_bounds__(256) void scan_tokens_kernel(TokKArgs a) {
 
 // The same for few (b, d) rows, where a handful of waves run the whole call
 // and each token's loads would sit on the critical path: the inputs of P
-// tokens are loaded together, then the P tokens are computed, so the load
-// latency is paid once per P tokens instead of once per token.
+// tokens are loaded together, and the next P tokens' loads are issued before
+// the current P are computed (two register sets used in turn), so only the
+// first group's load latency is exposed.
 template <typename T, int N, int P>
 __global__ __launch_bounds__(256) void scan_tokens_deep_kernel(TokKArgs a) {
-    constexpr int V = N >= 4 ? 4 : N;
+    // one state per lane up to 16 states (more waves share the work than with
+    // four, and the readout sum stays within a 16-lane DPP row): V states per
+    // lane, R = N / V <= 16 lanes per (b, d) row
+    constexpr int V = N > 16 ? N / 16 : 1;
     constexpr int R = N / V;
-    const int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t i = g / R;
-    const int q = static_cast<int>(g % R);
+    const int g = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+    const int i = g / R;
+    const int q = g % R;
     if (i >= a.B * a.D) return;
-    const int64_t b = i / a.D, d = i % a.D;
+    // few rows of few tokens: every offset below fits 32 bits
+    const int D = static_cast<int>(a.D), L = static_cast<int>(a.L);
+    const int b = i / D, d = i % D;
     const int n0 = q * V;
-    const int64_t D = a.D, L = a.L;
     float A2[V], h[V];
 #pragma unroll
     for (int n = 0; n < V; ++n) {
         A2[n] = a.A[d * N + n0 + n] * kLog2e;
-        h[n] = a.h0 ? a.h0[i * N + n0 + n] : 0.0f;
+        h[n] = a.h0 ? a.h0[static_cast<int64_t>(i) * N + n0 + n] : 0.0f;
     }
     const float bias = a.dt_bias ? a.dt_bias[d] : 0.0f;
     const float Dk = a.Dskip ? a.Dskip[d] : 0.0f;
-    const T* __restrict__ u = static_cast<const T*>(a.u) + b * L * D + d;
-    const T* __restrict__ dl = static_cast<const T*>(a.delta) + b * L * D + d;
-    const T* __restrict__ z = a.z ? static_cast<const T*>(a.z) + b * L * D + d : nullptr;
-    T* __restrict__ y = static_cast<T*>(a.y) + b * L * D + d;
+    const int row = b * L * D + d;  // element (b, 0, d)
+    const T* __restrict__ u = static_cast<const T*>(a.u) + row;
+    const T* __restrict__ dl = static_cast<const T*>(a.delta) + row;
+    const T* __restrict__ z = a.z ? static_cast<const T*>(a.z) + row : nullptr;
+    T* __restrict__ y = static_cast<T*>(a.y) + row;
     const T* __restrict__ Bm = static_cast<const T*>(a.Bm) + b * L * N + n0;
     const T* __restrict__ Cm = static_cast<const T*>(a.Cm) + b * L * N + n0;
-    for (int64_t t0 = 0; t0 < L; t0 += P) {
-        float ru[P], rx[P], rz[P], rb[P][V], rc[P][V];
+    float ru[2][P], rx[2][P], rz[2][P], rb[2][P][V], rc[2][P][V];
+    // inputs of tokens t0 .. t0 + P - 1 into set S (past the end: the last token again, never used)
+    auto load = [&](auto set, int t0) {
+        constexpr int S = decltype(set)::value;
 #pragma unroll
         for (int j = 0; j < P; ++j) {
-            const int64_t t = imin64(t0 + j, L - 1);  // past the end: the last token again, never used
-            ru[j] = load_act(u, t * D);
-            rx[j] = load_act(dl, t * D);
-            rz[j] = z ? load_act(z, t * D) : 0.0f;
-            load_states<V>(Bm + t * N, rb[j]);
-            load_states<V>(Cm + t * N, rc[j]);
+            const int t = min(t0 + j, L - 1);
+            ru[S][j] = load_act(u, t * D);
+            rx[S][j] = load_act(dl, t * D);
+            rz[S][j] = z ? load_act(z, t * D) : 0.0f;
+            load_states<V>(Bm + t * N, rb[S][j]);
+            load_states<V>(Cm + t * N, rc[S][j]);
         }
+    };
+    auto compute = [&](auto set, int t0) {
+        constexpr int S = decltype(set)::value;
 #pragma unroll
         for (int j = 0; j < P; ++j) {
             if (t0 + j < L) {
-                const float x = rx[j] + bias;
+                const float x = rx[S][j] + bias;
                 const float dt = a.softplus ? softplus(x) : x;
-                const float du = dt * ru[j];
+                const float du = dt * ru[S][j];
                 float s = 0.0f;
 #pragma unroll
                 for (int n = 0; n < V; ++n) {
-                    h[n] = __builtin_fmaf(fast_exp2(dt * A2[n]), h[n], du * rb[j][n]);
-                    s = __builtin_fmaf(rc[j][n], h[n], s);
+                    h[n] = __builtin_fmaf(fast_exp2(dt * A2[n]), h[n], du * rb[S][j][n]);
+                    s = __builtin_fmaf(rc[S][j][n], h[n], s);
                 }
-#pragma unroll
-                for (int m = 1; m < R; m <<= 1) s += __shfl_xor(s, m);
+                s = group_sum<R>(s);
                 if (q == 0) {
-                    s = __builtin_fmaf(Dk, ru[j], s);
-                    if (z) s *= silu(rz[j]);
+                    s = __builtin_fmaf(Dk, ru[S][j], s);
+                    if (z) s *= silu(rz[S][j]);
                     store_act(y, (t0 + j) * D, s);
                 }
             }
         }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    load(S0{}, 0);
+    for (int t0 = 0; t0 < L; t0 += 2 * P) {
+        load(S1{}, t0 + P);
+        compute(S0{}, t0);
+        if (t0 + P >= L) break;
+        load(S0{}, t0 + 2 * P);
+        compute(S1{}, t0 + P);
     }
     if (a.h_final) {
 #pragma unroll
-        for (int n = 0; n < V; ++n) a.h_final[i * N + n0 + n] = h[n];
+        for (int n = 0; n < V; ++n) a.h_final[static_cast<int64_t>(i) * N + n0 + n] = h[n];
     }
 }
 
@@ -393,8 +412,10 @@ template <typename T>
 hipError_t dispatch_tokens(const TokKArgs& k, int64_t N, hipStream_t st) {
     const int64_t lanes = k.B * k.D * (N >= 4 ? N / 4 : 1);
     const dim3 grid(static_cast<unsigned>((lanes + 255) / 256));
-    if (k.B * k.D <= kTokensDeepMaxRows && k.L > 8) {  // few rows: loads of 16 tokens at a time
-        constexpr int P = 16;
+    if (k.B * k.D <= kTokensDeepMaxRows && k.L > 8) {  // few rows: loads of 8 tokens at a time, 8 ahead
+        constexpr int P = 8;
+        const int64_t deep_lanes = k.B * k.D * (N > 16 ? 16 : N);  // one state per lane up to N = 16
+        const dim3 grid(static_cast<unsigned>((deep_lanes + 255) / 256));
         switch (N) {
             case 1: hipLaunchKernelGGL((scan_tokens_deep_kernel<T, 1, P>), grid, dim3(256), 0, st, k); break;
             case 2: hipLaunchKernelGGL((scan_tokens_deep_kernel<T, 2, P>), grid, dim3(256), 0, st, k); break;
