@@ -1,7 +1,8 @@
 """GPU parity on seeded random problems: shapes, state sizes, activation types
 and optional inputs drawn at random, so that combinations the targeted tests
 do not name (ragged channel blocks, short and long sequences, every layout and
-schedule) are compared with the float64 oracle too.  Every case prints its
+schedule; the training pair of a forward saving its context and the backward
+from it) are compared with the float64 oracle too.  Every case prints its
 draw before it runs."""
 import numpy as np
 import pytest
@@ -88,6 +89,34 @@ def test_random_backward(mssm_lib, i):
     tol = GRAD_TOL[dtype]
     for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddt_bias") + (("dz",) if "z" in use else ()) + \
             (("dh0",) if h0 else ()):
+        assert grad_err(to_np(gg[k]), r[k]) <= tol, k
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_training_pair(mssm_lib, i):
+    # the forward saving its context and the backward from it, with the draws of the backward sweep
+    B, L, D, N, dtype, use, h0, K = draw(250 + i)
+    L = min(L, 300)
+    print(f"[random train pair {i}] B={B} L={L} D={D} N={N} {dtype} use={use} h0={h0}", flush=True)
+    w = workloads.custom(B, L, D, N, dtype, seed=3250 + i, backward=True)
+    inp = workloads.make_inputs(w)
+    t = gpu_inputs(inp)
+    h0n = np.random.default_rng(i + 50).standard_normal((B, D, N)).astype(np.float32) if h0 else None
+    g = lambda k: t[k] if k in use else None  # noqa: E731
+    h0t = torch.from_numpy(h0n).cuda() if h0 else None
+    y, hf, ctx = mssm_lib.scan_fwd_train(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], g("Dskip"), g("z"),
+                                         g("dt_bias"), h0t)
+    gg = mssm_lib.scan_bwd_saved(t["u"], t["delta"], t["A"], t["Bm"], t["Cm"], t["dy"], ctx, g("Dskip"), g("z"),
+                                 g("dt_bias"))
+    torch.cuda.synchronize()
+    yr, hr = run_oracle_fwd(oracle, inp, h0n, use=use)
+    assert fwd_err(to_np(y), yr) <= FWD_TOL[dtype]
+    assert fwd_err(to_np(hf), hr) <= STATE_TOL
+    f = workloads.as_float32(inp)
+    h = lambda k: f[k] if k in use else None  # noqa: E731
+    r = oracle.scan_bwd(f["u"], f["delta"], f["A"], f["Bm"], f["Cm"], f["dy"], h("Dskip"), h("z"), h("dt_bias"), h0n)
+    tol = GRAD_TOL[dtype]
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "ddt_bias", "dh0") + (("dz",) if "z" in use else ()):
         assert grad_err(to_np(gg[k]), r[k]) <= tol, k
 
 

@@ -162,3 +162,38 @@ def test_bitwise_reproducible_and_ctx_reuse(mssm):
     for k in GRADS:
         if g1[k] is not None:
             assert torch.equal(g1[k], g2[k]), k
+
+
+def test_training_pair_in_a_graph(mssm):
+    # the forward saving its context and the backward from it (tail-walk plan: the last chunk's Q pass, the long
+    # and short walks, the reductions) captured in one graph, replayed 3 times with new u and dy (eager calls
+    # between the replays): every replay equals the eager calls on the same inputs bit for bit
+    w = workloads.custom(3, 300, 3200, 16, "f32", seed=6)
+    print(f"[train pair graph] {w}", flush=True)
+    inp = workloads.make_inputs(w, with_dy=True)
+    t = gpu_inputs(inp)
+    u, dy = t["u"].clone(), t["dy"].clone()
+
+    def call():
+        y, hf, ctx = mssm.scan_fwd_train(u, t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"], t["dt_bias"])
+        g = mssm.scan_bwd_saved(u, t["delta"], t["A"], t["Bm"], t["Cm"], dy, ctx, t["Dskip"], t["z"], t["dt_bias"])
+        return dict(g, y=y, h_final=hf)
+
+    call()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        out = call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    for r in range(3):
+        u.copy_(torch.from_numpy(rng.standard_normal(tuple(u.shape)).astype(np.float32)).cuda())
+        dy.copy_(torch.from_numpy(rng.standard_normal(tuple(dy.shape)).astype(np.float32)).cuda())
+        ref = {k: v.clone() for k, v in call().items() if v is not None}
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert torch.equal(out[k], v), (r, k)
