@@ -278,6 +278,23 @@ mssm_status mssm_scan_fwd_train(const mssm_problem* p,
                                 void* ctx, size_t ctx_bytes,
                                 void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* The forward behind the fused conv1d + SiLU front end (mssm_conv_scan_fwd)
+ * that also writes the context for mssm_scan_bwd_saved: same arguments,
+ * outputs and errors as mssm_conv_scan_fwd, plus ctx (required, as for
+ * mssm_scan_fwd_train).  The backward of a Mamba block's scan then runs as
+ * mssm_scan_bwd_saved with u = the front end's output (u_out of this call),
+ * followed by mssm_conv_bwd for dx, dconv_w, dconv_b. */
+mssm_status mssm_conv_scan_fwd_train(const mssm_problem* p, int32_t d_conv,
+                                     const void* x, const float* conv_w, const float* conv_b,
+                                     const void* x_prev,
+                                     const void* delta, const float* A,
+                                     const void* Bm, const void* Cm,
+                                     const float* Dskip, const void* z, const float* dt_bias,
+                                     const float* h0,
+                                     void* y, float* h_final, void* u_out,
+                                     void* ctx, size_t ctx_bytes,
+                                     void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Bytes of device scratch mssm_scan_bwd_saved needs (the partial sums of
  * dB, dC, dA, dD, ddt_bias and, with time chunks, the adjoint carries). */
 size_t mssm_scan_bwd_saved_workspace_bytes(const mssm_problem* p);

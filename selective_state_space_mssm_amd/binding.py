@@ -24,7 +24,7 @@ STATUS = {0: "MSSM_OK", -1: "MSSM_ERR_NULL", -2: "MSSM_ERR_SHAPE", -3: "MSSM_ERR
 EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "mssm_scan_fwd", "mssm_scan_fwd_noalloc",
            "mssm_conv_scan_fwd", "mssm_conv_bwd_workspace_bytes", "mssm_conv_bwd", "mssm_scan_bwd", "mssm_step",
            "mssm_conv_step", "mssm_ssd_fwd_workspace_bytes", "mssm_ssd_fwd", "mssm_ssd_bwd_workspace_bytes",
-           "mssm_ssd_bwd", "mssm_scan_ctx_bytes", "mssm_scan_fwd_train", "mssm_scan_bwd_saved_workspace_bytes",
+           "mssm_ssd_bwd", "mssm_scan_ctx_bytes", "mssm_scan_fwd_train", "mssm_conv_scan_fwd_train", "mssm_scan_bwd_saved_workspace_bytes",
            "mssm_scan_bwd_saved", "mssm_status_string", "mssm_build_info"]
 MAX_DCONV = 4
 
@@ -88,6 +88,8 @@ def _open(path: str):
     lib.mssm_scan_ctx_bytes.restype = sz
     lib.mssm_scan_fwd_train.argtypes = [P] + [vp] * 11 + [vp, sz, vp, sz, vp]
     lib.mssm_scan_fwd_train.restype = st
+    lib.mssm_conv_scan_fwd_train.argtypes = [P, ctypes.c_int32] + [vp] * 15 + [vp, sz, vp, sz, vp]
+    lib.mssm_conv_scan_fwd_train.restype = st
     lib.mssm_scan_bwd_saved_workspace_bytes.argtypes = [P]
     lib.mssm_scan_bwd_saved_workspace_bytes.restype = sz
     lib.mssm_scan_bwd_saved.argtypes = [P] + [vp] * 8 + [vp, sz] + [vp] * 11 + [vp, sz, vp]
@@ -236,6 +238,21 @@ def conv_scan_fwd(x, conv_w, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None,
     x_prev (B, d_conv - 1, D): the inputs before t = 0 (zeros when None).
     Returns (y, h_final, u): h_final None unless requested, u (B, L, D) only
     with return_u (or u_out)."""
+    return _conv_fwd(x, conv_w, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, conv_b, x_prev, delta_softplus,
+                     return_final_state, return_u, y, h_final, u_out, workspace, None, False)[:3]
+
+
+def conv_scan_fwd_train(x, conv_w, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None, h0=None, conv_b=None,
+                        x_prev=None, delta_softplus=True, return_final_state=True, y=None, h_final=None,
+                        u_out=None, ctx=None, workspace=None):
+    """conv_scan_fwd that also saves the training context for scan_bwd_saved
+    (which takes the returned u).  Returns (y, h_final, u, ctx)."""
+    return _conv_fwd(x, conv_w, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, conv_b, x_prev, delta_softplus,
+                     return_final_state, True, y, h_final, u_out, workspace, ctx, True)
+
+
+def _conv_fwd(x, conv_w, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, conv_b, x_prev, delta_softplus,
+              return_final_state, return_u, y, h_final, u_out, workspace, ctx, train):
     act = x.dtype
     B, L, D = x.shape
     N = A.shape[1]
@@ -276,11 +293,23 @@ def conv_scan_fwd(x, conv_w, delta, A, Bm, Cm, Dskip=None, z=None, dt_bias=None,
     prob = problem(B, L, D, N, _dtype_code(x), delta_softplus)
     nbytes = int(lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(prob)))
     ws = _workspace(nbytes, x.device, workspace)
-    _check(lib.mssm_conv_scan_fwd(ctypes.byref(prob), K, _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(x_prev),
-                                  _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
-                                  _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(u_out),
-                                  _ptr(ws), nbytes, _stream(x.device)))
-    return y, h_final, u_out
+    if not train:
+        _check(lib.mssm_conv_scan_fwd(ctypes.byref(prob), K, _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(x_prev),
+                                      _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+                                      _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(u_out),
+                                      _ptr(ws), nbytes, _stream(x.device)))
+        return y, h_final, u_out, None
+    cbytes = int(lib.mssm_scan_ctx_bytes(ctypes.byref(prob)))
+    if cbytes == 0:
+        raise MssmError(-4, lib)
+    if ctx is None:
+        ctx = torch.empty(cbytes, dtype=torch.uint8, device=x.device)
+    _check(lib.mssm_conv_scan_fwd_train(ctypes.byref(prob), K, _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(x_prev),
+                                        _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(z),
+                                        _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(u_out),
+                                        _ptr(ctx), ctx.numel() * ctx.element_size(), _ptr(ws), nbytes,
+                                        _stream(x.device)))
+    return y, h_final, u_out, ctx
 
 
 def conv_bwd(x, conv_w, du, conv_b=None, x_prev=None, want_dconv_b=True, want_dx_prev=False, workspace=None):

@@ -71,7 +71,7 @@ hipError_t launch_fwd_noalloc(ScanArgs a, hipStream_t s);
 // a.x_prev) its causal conv; u = silu(conv(x) + bias) is formed inside the
 // kernels (and written to a.u_out if set).  Same schedule and workspace as
 // launch_fwd.
-hipError_t launch_conv_fwd(const ScanArgs& a, hipStream_t s);
+hipError_t launch_conv_fwd(const ScanArgs& a, hipStream_t s);  // with a.ctx_ckpt set: the training forward
 // Backward pre-pass: the forward recurrence with, instead of y, the state
 // before every 16-step tile (ckpt, (B, tiles, N, D)), sbar = dy * silu(z)
 // ((B, L, D) float32) and dz; fwd_scratch is plan_fwd(...).ws_bytes of scratch.

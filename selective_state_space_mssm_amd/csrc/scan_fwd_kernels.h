@@ -1204,11 +1204,11 @@ hipError_t launch_fwd_t(const ScanArgs& s, const FwdPlan& pl, void* scratch, con
         }
     }
     const dim3 main_block(64 * (G + helper_waves(NG, G, PRE)));  // state waves + helper waves
-    const bool save = !PRE && !CONV && a.ckpt;  // the training forward
+    const bool save = !PRE && a.ckpt;  // the training forward
     if (save && s.z)
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE, CONV, !PRE && !CONV>), grid, main_block, 0, st, a);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE, CONV, !PRE>), grid, main_block, 0, st, a);
     else if (save)
-        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false, PRE, CONV, !PRE && !CONV>), grid, main_block, 0, st, a);
+        hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, false, PRE, CONV, !PRE>), grid, main_block, 0, st, a);
     else if (s.z)
         hipLaunchKernelGGL((scan_fwd_kernel<T, NG, G, true, PRE, CONV, false>), grid, main_block, 0, st, a);
     else

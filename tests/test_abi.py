@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), f"libmssm.so does not export {n}"
     assert sorted(mssm.EXPORTS) == names
@@ -300,6 +300,21 @@ def test_training_pair_validation():
     long_ = P(1, 1 << 20, 1536, 16, 1, 1)
     nf = lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(long_))
     assert fwd_train(long_, ws=FAKE, wsb=nf - 1) == -6
+    # the conv front end's training forward: mssm_conv_scan_fwd's checks plus the context's
+    v = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+
+    def conv_train(pp, K=4, x=FAKE, w=FAKE, ctx=FAKE, ctxb=1 << 40, ws=FAKE, wsb=1 << 40):
+        return lib.mssm_conv_scan_fwd_train(ctypes.byref(pp) if pp is not None else None, K, v(x), v(w), None, None,
+                                            v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, None, None, None, v(FAKE),
+                                            None, None, v(ctx), ctxb, v(ws), wsb, None)
+    assert conv_train(None) == -1
+    assert conv_train(p, K=5) == -2
+    assert conv_train(good(N=12)) == -4
+    assert conv_train(p, w=None) == -1
+    assert conv_train(p, ctx=None) == -1
+    assert conv_train(p, ctx=MIS) == -5
+    assert conv_train(p, ctxb=nctx - 1) == -6
+    assert conv_train(long_, wsb=nf - 1) == -6
     assert bwd_saved(p, ws=None) == -6
     assert bwd_saved(p, wsb=nws - 1) == -6
     assert bwd_saved(p, dy=None) == -1

@@ -252,6 +252,40 @@ def test_training_chain_through_the_front_end(mssm):
     check_conv_grads(gc, rc, "f32", 4)
 
 
+@pytest.mark.parametrize("shape,dtype,K", [((2, 150, 130), "f32", 4), ((2, 150, 130), "bf16", 3),
+                                           ((1, 600, 100), "f32", 4), ((3, 48, 5760), "f32", 2)])
+def test_training_pair_through_the_front_end(mssm, shape, dtype, K):
+    """The training pair behind the front end: mssm_conv_scan_fwd_train (y,
+    h_final and u bit for bit those of mssm_conv_scan_fwd; it also saves the
+    context), mssm_scan_bwd_saved on its u, mssm_conv_bwd on that du: every
+    gradient against the oracle's chain.  (1, 600, 100): the time-chunked
+    forward; (3, 48, 5760): 270 channel blocks, the balanced schedule."""
+    B, L, D = shape
+    w = workloads.custom(B, L, D, 16, dtype, seed=L + D + K, backward=True)
+    inp, t = make(w, K)
+    print(f"[conv train pair] {w} d_conv={K}", flush=True)
+    xp = t["x_prev"] if K > 1 else None
+    y, hf, u, ctx = mssm.conv_scan_fwd_train(t["u"], t["conv_w"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"],
+                                             t["z"], t["dt_bias"], conv_b=t["conv_b"], x_prev=xp)
+    y0, hf0, u0 = mssm.conv_scan_fwd(t["u"], t["conv_w"], t["delta"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["z"],
+                                     t["dt_bias"], conv_b=t["conv_b"], x_prev=xp, return_u=True)
+    assert torch.equal(y, y0) and torch.equal(hf, hf0) and torch.equal(u, u0)
+    gs = mssm.scan_bwd_saved(u, t["delta"], t["A"], t["Bm"], t["Cm"], t["dy"], ctx, t["Dskip"], t["z"], t["dt_bias"])
+    gc = mssm.conv_bwd(t["u"], t["conv_w"], gs["du"], conv_b=t["conv_b"], x_prev=xp, want_dx_prev=K > 1)
+    torch.cuda.synchronize()
+    f = workloads.as_float32(inp)
+    fxp = f["x_prev"] if K > 1 else None
+    ur = oracle.causal_conv_silu(f["u"], f["conv_w"], f["conv_b"], fxp)
+    rs = oracle.scan_bwd(ur, f["delta"], f["A"], f["Bm"], f["Cm"], f["dy"], f["Dskip"], f["z"], f["dt_bias"])
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddt_bias", "dh0"):
+        assert grad_err(to_np(gs[k]), rs[k]) <= GRAD_TOL[dtype], k
+    # the front end's backward against the oracle's on the du it was given: with bfloat16 activations du is
+    # rounded to bfloat16 before it, and the rounding of du and then of dx compounds beyond one rounding's bar
+    du_in = rs["du"] if dtype == "f32" else to_np(gs["du"]).astype(np.float64)
+    rc = oracle.causal_conv_silu_bwd(f["u"], f["conv_w"], du_in, f["conv_b"], fxp)
+    check_conv_grads(gc, rc, dtype, K)
+
+
 # ---- decode through the front end (mssm_conv_step) ----------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
