@@ -257,10 +257,11 @@ mssm_status mssm_scan_bwd(const mssm_problem* p,
  * aligned, owned by the caller; its contents are the library's (the state
  * before every 16-step tile, (B, ceil(L/16), N, D) float32, and the readout
  * before the gate, sum_n Cm h_t + Dskip u_t, (B, L, D) float32, written only
- * when z is given).  Valid for the inputs of the forward that wrote it.
- * Both calls need dstate a power of two (1 .. 64); other sizes return
- * MSSM_ERR_UNSUPPORTED (and the size queries 0).  ctx_bytes below the query
- * returns MSSM_ERR_WORKSPACE.
+ * when z is given).  Valid for the inputs of the forward that wrote it.  A
+ * dstate that is not a power of two runs as elsewhere at the next power of
+ * two with inert extra states, and the context is that problem's (the size
+ * query accounts for it).  ctx_bytes below the query returns
+ * MSSM_ERR_WORKSPACE.
  */
 size_t mssm_scan_ctx_bytes(const mssm_problem* p);
 

@@ -124,6 +124,13 @@ size_t bwd_ws_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype);
 hipError_t launch_fwd_any(const ScanArgs& a, hipStream_t s);
 hipError_t launch_conv_fwd_any(const ScanArgs& a, hipStream_t s);
 hipError_t launch_bwd_any(const ScanArgs& a, hipStream_t s);
+// The training pair at any N <= 64: the context is that of the N'-state
+// problem (N' = padded_dstate(N), the next power of two), the backward's
+// workspace holds its padded copies.
+int64_t padded_dstate(int64_t N);
+size_t bwd_saved_ws_bytes_any(int64_t B, int64_t L, int64_t D, int64_t N, int dtype);
+hipError_t launch_fwd_train_any(const ScanArgs& a, hipStream_t s);
+hipError_t launch_bwd_saved_any(const ScanArgs& a, hipStream_t s);
 // Below this many (b, d) rows the short-sequence path loads 8 tokens' inputs
 // at a time, the next 8 in flight while the current ones are computed (a few
 // waves run the whole call and would otherwise wait on every token's loads).

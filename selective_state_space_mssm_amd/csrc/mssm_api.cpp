@@ -192,14 +192,21 @@ mssm_status mssm_scan_bwd(const mssm_problem* p, const void* u, const void* delt
     return from_hip(mssm::launch_bwd_any(a, static_cast<hipStream_t>(hip_stream)));
 }
 
+namespace {
+// The context of a problem: that of its N'-state form (N' the next power of two).
+mssm::CtxLayout ctx_of(const mssm_problem* p) {
+    return mssm::ctx_layout(p->batch, p->seqlen, p->dim, mssm::padded_dstate(p->dstate));
+}
+}  // namespace
+
 size_t mssm_scan_ctx_bytes(const mssm_problem* p) {
-    if (check_problem(p, true) != MSSM_OK || mssm::needs_padding(p->dstate)) return 0;
-    return mssm::ctx_layout(p->batch, p->seqlen, p->dim, p->dstate).total;
+    if (check_problem(p, true) != MSSM_OK) return 0;
+    return ctx_of(p).total;
 }
 
 size_t mssm_scan_bwd_saved_workspace_bytes(const mssm_problem* p) {
-    if (check_problem(p, true) != MSSM_OK || mssm::needs_padding(p->dstate)) return 0;
-    return mssm::bwd_saved_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate);
+    if (check_problem(p, true) != MSSM_OK) return 0;
+    return mssm::bwd_saved_ws_bytes_any(p->batch, p->seqlen, p->dim, p->dstate, p->dtype);
 }
 
 mssm_status mssm_scan_fwd_train(const mssm_problem* p, const void* u, const void* delta, const float* A,
@@ -208,13 +215,12 @@ mssm_status mssm_scan_fwd_train(const mssm_problem* p, const void* u, const void
                                 size_t ctx_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
     mssm_status st = check_problem(p, true);
     if (st != MSSM_OK) return st;
-    if (mssm::needs_padding(p->dstate)) return MSSM_ERR_UNSUPPORTED;
     if (!u || !delta || !A || !Bm || !Cm || !y || !ctx) return MSSM_ERR_NULL;
     st = check_align({u, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, y, h_final, ctx, workspace});
     if (st != MSSM_OK) return st;
-    const mssm::CtxLayout cl = mssm::ctx_layout(p->batch, p->seqlen, p->dim, p->dstate);
+    const mssm::CtxLayout cl = ctx_of(p);
     if (ctx_bytes < cl.total) return MSSM_ERR_WORKSPACE;
-    const size_t need = mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    const size_t need = mssm::fwd_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate, p->dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return MSSM_ERR_WORKSPACE;
 
     mssm::ScanArgs a = base_args(p);
@@ -224,7 +230,7 @@ mssm_status mssm_scan_fwd_train(const mssm_problem* p, const void* u, const void
     a.ctx_ckpt = reinterpret_cast<float*>(static_cast<char*>(ctx) + cl.ckpt);
     a.ctx_s = reinterpret_cast<float*>(static_cast<char*>(ctx) + cl.s);
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    return from_hip(mssm::launch_fwd_train(a, static_cast<hipStream_t>(hip_stream)));
+    return from_hip(mssm::launch_fwd_train_any(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 mssm_status mssm_conv_scan_fwd_train(const mssm_problem* p, int32_t d_conv, const void* x, const float* conv_w,
@@ -236,14 +242,13 @@ mssm_status mssm_conv_scan_fwd_train(const mssm_problem* p, int32_t d_conv, cons
     mssm_status st = check_problem(p, true);
     if (st != MSSM_OK) return st;
     if (d_conv < 1 || d_conv > MSSM_MAX_DCONV) return MSSM_ERR_SHAPE;
-    if (mssm::needs_padding(p->dstate)) return MSSM_ERR_UNSUPPORTED;
     if (!x || !conv_w || !delta || !A || !Bm || !Cm || !y || !ctx) return MSSM_ERR_NULL;
     st = check_align({x, conv_w, conv_b, x_prev, delta, A, Bm, Cm, Dskip, z, dt_bias, h0, y, h_final, u_out, ctx,
                       workspace});
     if (st != MSSM_OK) return st;
-    const mssm::CtxLayout cl = mssm::ctx_layout(p->batch, p->seqlen, p->dim, p->dstate);
+    const mssm::CtxLayout cl = ctx_of(p);
     if (ctx_bytes < cl.total) return MSSM_ERR_WORKSPACE;
-    const size_t need = mssm::plan_fwd(p->batch, p->seqlen, p->dim, p->dstate).ws_bytes;
+    const size_t need = mssm::fwd_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate, p->dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return MSSM_ERR_WORKSPACE;
 
     mssm::ScanArgs a = base_args(p);
@@ -255,7 +260,7 @@ mssm_status mssm_conv_scan_fwd_train(const mssm_problem* p, int32_t d_conv, cons
     a.ctx_ckpt = reinterpret_cast<float*>(static_cast<char*>(ctx) + cl.ckpt);
     a.ctx_s = reinterpret_cast<float*>(static_cast<char*>(ctx) + cl.s);
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    return from_hip(mssm::launch_conv_fwd(a, static_cast<hipStream_t>(hip_stream)));
+    return from_hip(mssm::launch_conv_fwd_any(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 mssm_status mssm_scan_bwd_saved(const mssm_problem* p, const void* u, const void* delta, const float* A,
@@ -266,16 +271,15 @@ mssm_status mssm_scan_bwd_saved(const mssm_problem* p, const void* u, const void
                                 size_t workspace_bytes, void* hip_stream) {
     mssm_status st = check_problem(p, true);
     if (st != MSSM_OK) return st;
-    if (mssm::needs_padding(p->dstate)) return MSSM_ERR_UNSUPPORTED;
     if (!u || !delta || !A || !Bm || !Cm || !dy || !ctx) return MSSM_ERR_NULL;
     if (!du || !ddelta || !dA || !dB || !dC) return MSSM_ERR_NULL;
     if (z && !dz) return MSSM_ERR_NULL;
     st = check_align({u, delta, A, Bm, Cm, Dskip, z, dt_bias, ctx, dy, dh_final, du, ddelta, dA, dB, dC, dD, dz,
                       ddt_bias, dh0, workspace});
     if (st != MSSM_OK) return st;
-    const mssm::CtxLayout cl = mssm::ctx_layout(p->batch, p->seqlen, p->dim, p->dstate);
+    const mssm::CtxLayout cl = ctx_of(p);
     if (ctx_bytes < cl.total) return MSSM_ERR_WORKSPACE;
-    const size_t need = mssm::bwd_saved_ws_bytes(p->batch, p->seqlen, p->dim, p->dstate);
+    const size_t need = mssm::bwd_saved_ws_bytes_any(p->batch, p->seqlen, p->dim, p->dstate, p->dtype);
     if (!workspace || workspace_bytes < need) return MSSM_ERR_WORKSPACE;
 
     mssm::ScanArgs a = base_args(p);
@@ -287,7 +291,7 @@ mssm_status mssm_scan_bwd_saved(const mssm_problem* p, const void* u, const void
     a.ctx_ckpt = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ctx)) + cl.ckpt);
     a.ctx_s = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(ctx)) + cl.s);
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
-    return from_hip(mssm::launch_bwd_saved(a, static_cast<hipStream_t>(hip_stream)));
+    return from_hip(mssm::launch_bwd_saved_any(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 mssm_status mssm_step(const mssm_problem* p, const void* u_t, const void* delta_t, const float* A,

@@ -74,15 +74,17 @@ hipError_t unpad_act(int dtype, const void* src, void* dst, int64_t rows, int64_
 }
 
 // Workspace of a padded call: the N'-state call's own, then the padded
-// copies (each 256-byte aligned).
+// copies (each 256-byte aligned).  `saved`: the backward from a saved context.
 struct PadLayout {
     size_t inner, bm, cm, A, h0, hf, dhf, dB, dC, dA, dh0, total;
 };
-PadLayout pad_layout(int64_t B, int64_t L, int64_t D, int64_t Np, int dtype, bool bwd) {
+PadLayout pad_layout(int64_t B, int64_t L, int64_t D, int64_t Np, int dtype, bool bwd, bool saved = false) {
     const size_t act = dtype == 1 ? 2 : 4;
     PadLayout p{};
     size_t off = 0;
-    p.inner = off; off += al256(bwd ? plan_bwd(B, L, D, Np).ws_bytes : plan_fwd(B, L, D, Np).ws_bytes);
+    p.inner = off;
+    off += al256(bwd ? (saved ? bwd_saved_ws_bytes(B, L, D, Np) : plan_bwd(B, L, D, Np).ws_bytes)
+                     : plan_fwd(B, L, D, Np).ws_bytes);
     p.bm = off;    off += al256(static_cast<size_t>(B * L * Np) * act);
     p.cm = off;    off += al256(static_cast<size_t>(B * L * Np) * act);
     p.A = off;     off += al256(static_cast<size_t>(D * Np) * 4);
@@ -152,10 +154,21 @@ hipError_t launch_conv_fwd_any(const ScanArgs& a, hipStream_t st) {
     return needs_padding(a.N) ? fwd_padded<launch_conv_fwd>(a, st) : launch_conv_fwd(a, st);
 }
 
-hipError_t launch_bwd_any(const ScanArgs& a, hipStream_t st) {
-    if (!needs_padding(a.N)) return launch_bwd(a, st);
+int64_t padded_dstate(int64_t N) { return needs_padding(N) ? next_pow2(N) : N; }
+
+size_t bwd_saved_ws_bytes_any(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
+    if (!needs_padding(N)) return bwd_saved_ws_bytes(B, L, D, N);
+    return pad_layout(B, L, D, next_pow2(N), dtype, true, true).total;
+}
+
+hipError_t launch_fwd_train_any(const ScanArgs& a, hipStream_t st) {
+    return needs_padding(a.N) ? fwd_padded<launch_fwd_train>(a, st) : launch_fwd_train(a, st);
+}
+
+template <hipError_t (*LAUNCH)(const ScanArgs&, hipStream_t), bool SAVED>
+hipError_t bwd_padded(const ScanArgs& a, hipStream_t st) {
     const int64_t Np = next_pow2(a.N), N = a.N;
-    const PadLayout pl = pad_layout(a.B, a.L, a.D, Np, a.dtype, true);
+    const PadLayout pl = pad_layout(a.B, a.L, a.D, Np, a.dtype, true, SAVED);
     char* ws = static_cast<char*>(a.workspace);
     ScanArgs p = a;
     p.N = Np;
@@ -166,12 +179,21 @@ hipError_t launch_bwd_any(const ScanArgs& a, hipStream_t st) {
     p.dC = ws + pl.dC;
     p.dA = reinterpret_cast<float*>(ws + pl.dA);
     p.dh0 = a.dh0 ? reinterpret_cast<float*>(ws + pl.dh0) : nullptr;
-    if (e == hipSuccess) e = launch_bwd(p, st);
+    if (e == hipSuccess) e = LAUNCH(p, st);
     if (e == hipSuccess) e = unpad_act(a.dtype, ws + pl.dB, a.dB, a.B * a.L, N, Np, st);
     if (e == hipSuccess) e = unpad_act(a.dtype, ws + pl.dC, a.dC, a.B * a.L, N, Np, st);
     if (e == hipSuccess) e = unpad<float>(ws + pl.dA, a.dA, a.D, N, Np, st);
     if (e == hipSuccess && a.dh0) e = unpad<float>(ws + pl.dh0, a.dh0, a.B * a.D, N, Np, st);
     return e;
+}
+
+hipError_t launch_bwd_any(const ScanArgs& a, hipStream_t st) {
+    return needs_padding(a.N) ? bwd_padded<launch_bwd, false>(a, st) : launch_bwd(a, st);
+}
+
+// The saved context holds N' states (its layout is that of the N'-state problem).
+hipError_t launch_bwd_saved_any(const ScanArgs& a, hipStream_t st) {
+    return needs_padding(a.N) ? bwd_padded<launch_bwd_saved, true>(a, st) : launch_bwd_saved(a, st);
 }
 
 }  // namespace mssm

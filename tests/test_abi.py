@@ -273,21 +273,21 @@ def bwd_saved(p, ctx=FAKE, ctxb=1 << 40, ws=FAKE, wsb=1 << 40, **kw):
 
 def test_training_pair_validation():
     """mssm_scan_fwd_train / mssm_scan_bwd_saved: the forward's and backward's
-    checks, plus the context: required, at least mssm_scan_ctx_bytes, aligned,
-    and a power-of-two state size (the size queries return 0 otherwise)."""
+    checks, plus the context: required, at least mssm_scan_ctx_bytes, aligned
+    (a state size that is not a power of two has its next power's context)."""
     p = good(2, 100, 70, 16)
     nctx = lib.mssm_scan_ctx_bytes(ctypes.byref(p))
     tiles = (100 + 15) // 16
     assert nctx >= 2 * tiles * 16 * 70 * 4 + 2 * 100 * 70 * 4
-    assert lib.mssm_scan_ctx_bytes(ctypes.byref(good(N=12))) == 0
+    # any state size up to 64: one that is not a power of two has the context of the next power of two
+    assert lib.mssm_scan_ctx_bytes(ctypes.byref(good(2, 100, 70, 12))) == nctx
     assert lib.mssm_scan_ctx_bytes(ctypes.byref(good(N=65))) == 0
     assert lib.mssm_scan_ctx_bytes(None) == 0
     nws = lib.mssm_scan_bwd_saved_workspace_bytes(ctypes.byref(p))
     assert 0 < nws < lib.mssm_scan_bwd_workspace_bytes(ctypes.byref(p))  # no pre-pass scratch
-    assert lib.mssm_scan_bwd_saved_workspace_bytes(ctypes.byref(good(N=12))) == 0
+    assert lib.mssm_scan_bwd_saved_workspace_bytes(ctypes.byref(good(2, 100, 70, 12))) > nws  # + padded copies
     for call in (fwd_train, bwd_saved):
         assert call(None) == -1
-        assert call(good(N=12)) == -4
         assert call(good(N=65)) == -4
         assert call(p, ctx=None) == -1
         assert call(p, ctx=MIS) == -5
@@ -309,7 +309,7 @@ def test_training_pair_validation():
                                             None, None, v(ctx), ctxb, v(ws), wsb, None)
     assert conv_train(None) == -1
     assert conv_train(p, K=5) == -2
-    assert conv_train(good(N=12)) == -4
+    assert conv_train(good(N=65)) == -4
     assert conv_train(p, w=None) == -1
     assert conv_train(p, ctx=None) == -1
     assert conv_train(p, ctx=MIS) == -5

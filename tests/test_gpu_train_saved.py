@@ -90,8 +90,9 @@ def test_no_gate_no_state_inputs(mssm):
     assert_grads(g, r, GRAD_TOL["f32"])
 
 
-@pytest.mark.parametrize("N", [1, 2, 4, 8, 32, 64])
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 32, 64, 3, 12, 24, 48])
 def test_state_sizes(mssm, N):
+    # 3, 12, 24, 48: the next power of two's kernels with inert extra states, its context
     g, r = run_pair(mssm, workloads.custom(2, 90, 70, N, "f32", seed=N + 150))
     assert_grads(g, r, GRAD_TOL["f32"])
 
