@@ -76,7 +76,9 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
             T* cs = static_cast<T*>(a.conv_state) + b * (K - 1) * a.D + d;  // (b, 0, d)
             const float in = q < K - 1 ? load_act(cs, q * a.D) : uu;
             float prod = q < K ? a.conv_w[d * K + q] * in : 0.0f;
-            const float next = __shfl(in, static_cast<int>(threadIdx.x & 63) + 1);
+            // lane q + 1's input (row_shl:1 within the 16-lane row; a row's last lane gets 0, and only lanes
+            // q < K - 1 <= 2 use it, which never end a row)
+            const float next = dpp_move<0x101>(in);
             if (q < K - 1) store_act(cs, q * a.D, next);
             prod = group_sum<R>(prod);
             c = (a.conv_b ? a.conv_b[d] : 0.0f) + prod;
@@ -98,7 +100,8 @@ __global__ __launch_bounds__(256) void scan_step_kernel(StepKArgs a) {
                 if (k - 1 >= kTaps - K) store_act(cs, (k - 1 - (kTaps - K)) * a.D, xs[k]);
             if (K > 1) store_act(cs, (K - 2) * a.D, uu);
         }
-        if constexpr (R > 1 && R < kTaps) c = __shfl(c, static_cast<int>(threadIdx.x & 63) - q);
+        if constexpr (R == 2) c = dpp_move<0xA0>(c);  // the pair's first lane's c: quad_perm [0, 0, 2, 2]
+        static_assert(R == 1 || R == 2 || R >= kTaps, "rows of 1, 2 or at least kTaps lanes");
         uu = silu(c);
     }
     const float x = load_act(static_cast<const T*>(a.delta), i) + (a.dt_bias ? a.dt_bias[d] : 0.0f);
