@@ -408,6 +408,46 @@ def time_ssd(mssm, torch, B, L, H, N, reps=20, backward=False):
     return us, flops
 
 
+def time_ssd_train_pair(mssm, torch, B, L, H, N, reps=5):
+    """The SSD training pair (mssm_ssd_fwd_train, then mssm_ssd_bwd_saved), head
+    dim 64, float32: median us of the forward and of the backward."""
+    inp = workloads.ssd_inputs(B, L, H, 64, N, seed=11)
+    t = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    del inp
+    t["dy"] = torch.randn_like(t["x"])
+    y = torch.empty_like(t["x"])
+    hf = torch.empty((B, H, 64, N), dtype=torch.float32, device="cuda")
+    prob = mssm.binding.SsdProblem(B, L, H, 64, N, 0, 1)
+    ctx = torch.empty(int(mssm.lib.mssm_ssd_ctx_bytes(ctypes.byref(prob))), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(max(1, int(mssm.lib.mssm_ssd_fwd_train_workspace_bytes(ctypes.byref(prob)))),
+                      dtype=torch.uint8, device="cuda")
+    bws = torch.empty(int(mssm.lib.mssm_ssd_bwd_saved_workspace_bytes(ctypes.byref(prob))), dtype=torch.uint8,
+                      device="cuda")
+
+    def fwd():
+        mssm.ssd_fwd_train(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["Dskip"], t["dt_bias"], y=y, h_final=hf,
+                           ctx=ctx, workspace=fws)
+
+    def bwd():
+        mssm.ssd_bwd_saved(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["dy"], ctx, t["Dskip"], t["dt_bias"],
+                           workspace=bws)
+
+    for _ in range(2):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for a, b, c in ev:
+        a.record()
+        fwd()
+        b.record()
+        bwd()
+        c.record()
+    torch.cuda.synchronize()
+    return (float(np.median([a.elapsed_time(b) for a, b, _ in ev])) * 1e3,
+            float(np.median([b.elapsed_time(c) for _, b, c in ev])) * 1e3)
+
+
 def ssd_layers(mssm, torch):
     """The Mamba-2 (SSD) layers, float32 on the matrix cores: the 2.7B shape
     (80 heads of 64, d_state 128, B = 8, L = 2048) and the batch-1 prefill of
@@ -420,6 +460,10 @@ def ssd_layers(mssm, torch):
     r["ssd_fwd_H24_N128_B1_L2048_us"] = round(time_ssd(mssm, torch, 1, 2048, 24, 128)[0], 1)
     r["ssd_bwd_H80_N128_B8_L2048_us"] = round(time_ssd(mssm, torch, 8, 2048, 80, 128, 5, True)[0], 1)
     r["ssd_bwd_H24_N128_B1_L2048_us"] = round(time_ssd(mssm, torch, 1, 2048, 24, 128, 10, True)[0], 1)
+    # the training pair: the forward keeps the chunk states, the backward skips its first pass over the chunks
+    tf, tb = time_ssd_train_pair(mssm, torch, 8, 2048, 80, 128)
+    r["ssd_fwd_train_H80_N128_B8_L2048_us"] = round(tf, 1)
+    r["ssd_bwd_saved_H80_N128_B8_L2048_us"] = round(tb, 1)
     return r
 
 

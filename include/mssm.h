@@ -440,6 +440,36 @@ mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* d
                          float* ddt_bias, float* dh0,
                          void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * Training pair of the SSD layer, as mssm_scan_fwd_train / mssm_scan_bwd_saved
+ * for the selective scan: the forward keeps the state entering every 64-step
+ * chunk and the final state, (B, H, ceil(L / 64) + 1, P, N) float32 in the
+ * caller-owned ctx (at least mssm_ssd_ctx_bytes), and the backward starts from
+ * them instead of recomputing them with its first pass over the chunks.
+ * mssm_ssd_fwd_train: arguments, outputs and errors of mssm_ssd_fwd plus ctx
+ * (required); its workspace is mssm_ssd_fwd_train_workspace_bytes (the
+ * training forward never cuts the sequence into time segments, whose stored
+ * states would not be the true ones; with few (batch, head) pairs it is
+ * therefore slower than mssm_ssd_fwd).  y and h_final are those of
+ * mssm_ssd_fwd bit for bit wherever mssm_ssd_fwd runs without segments.
+ * mssm_ssd_bwd_saved: arguments, outputs and errors of mssm_ssd_bwd with ctx
+ * in place of h0 (the ctx holds it); workspace
+ * mssm_ssd_bwd_saved_workspace_bytes (the states are not in it).
+ */
+size_t mssm_ssd_ctx_bytes(const mssm_ssd_problem* p);
+size_t mssm_ssd_fwd_train_workspace_bytes(const mssm_ssd_problem* p);
+mssm_status mssm_ssd_fwd_train(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                               const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                               const float* h0, void* y, float* h_final, void* ctx, size_t ctx_bytes,
+                               void* workspace, size_t workspace_bytes, void* hip_stream);
+size_t mssm_ssd_bwd_saved_workspace_bytes(const mssm_ssd_problem* p);
+mssm_status mssm_ssd_bwd_saved(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                               const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                               const void* ctx, size_t ctx_bytes, const void* dy, const float* dh_final,
+                               void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
+                               float* ddt_bias, float* dh0,
+                               void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char* mssm_status_string(mssm_status s);
 

@@ -25,7 +25,8 @@ EXPORTS = ["mssm_scan_fwd_workspace_bytes", "mssm_scan_bwd_workspace_bytes", "ms
            "mssm_conv_scan_fwd", "mssm_conv_bwd_workspace_bytes", "mssm_conv_bwd", "mssm_scan_bwd", "mssm_step",
            "mssm_conv_step", "mssm_ssd_fwd_workspace_bytes", "mssm_ssd_fwd", "mssm_ssd_bwd_workspace_bytes",
            "mssm_ssd_bwd", "mssm_scan_ctx_bytes", "mssm_scan_fwd_train", "mssm_conv_scan_fwd_train", "mssm_scan_bwd_saved_workspace_bytes",
-           "mssm_scan_bwd_saved", "mssm_status_string", "mssm_build_info"]
+           "mssm_scan_bwd_saved", "mssm_ssd_ctx_bytes", "mssm_ssd_fwd_train_workspace_bytes", "mssm_ssd_fwd_train",
+           "mssm_ssd_bwd_saved_workspace_bytes", "mssm_ssd_bwd_saved", "mssm_status_string", "mssm_build_info"]
 MAX_DCONV = 4
 
 
@@ -94,6 +95,14 @@ def _open(path: str):
     lib.mssm_scan_bwd_saved_workspace_bytes.restype = sz
     lib.mssm_scan_bwd_saved.argtypes = [P] + [vp] * 8 + [vp, sz] + [vp] * 11 + [vp, sz, vp]
     lib.mssm_scan_bwd_saved.restype = st
+    SP = ctypes.POINTER(SsdProblem)
+    for q in ("mssm_ssd_ctx_bytes", "mssm_ssd_fwd_train_workspace_bytes", "mssm_ssd_bwd_saved_workspace_bytes"):
+        getattr(lib, q).argtypes = [SP]
+        getattr(lib, q).restype = sz
+    lib.mssm_ssd_fwd_train.argtypes = [SP] + [vp] * 10 + [vp, sz, vp, sz, vp]
+    lib.mssm_ssd_fwd_train.restype = st
+    lib.mssm_ssd_bwd_saved.argtypes = [SP] + [vp] * 7 + [vp, sz] + [vp] * 10 + [vp, sz, vp]
+    lib.mssm_ssd_bwd_saved.restype = st
     lib.mssm_status_string.argtypes = [st]
     lib.mssm_status_string.restype = ctypes.c_char_p
     lib.mssm_build_info.argtypes = []
@@ -646,4 +655,79 @@ def ssd_bwd(x, dt, A, Bm, Cm, dy, Dskip=None, dt_bias=None, h0=None, dh_final=No
                             _ptr(dt_bias), _ptr(h0), _ptr(dy), _ptr(dh_final), _ptr(g["dx"]), _ptr(g["ddt"]),
                             _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["ddt_bias"]),
                             _ptr(g["dh0"]), _ptr(ws), nbytes, _stream(dev)))
+    return g
+
+
+def ssd_fwd_train(x, dt, A, Bm, Cm, Dskip=None, dt_bias=None, h0=None, delta_softplus=True,
+                  return_final_state=True, y=None, h_final=None, ctx=None, workspace=None):
+    """ssd_fwd that also keeps the chunk states for ssd_bwd_saved (no time segments).
+    Returns (y, h_final, ctx); ctx a uint8 device tensor of mssm_ssd_ctx_bytes."""
+    B, L, H, P = x.shape
+    N = Bm.shape[2]
+    f, act = torch.float32, x.dtype
+    _req(x, "x", (B, L, H, P), act)
+    _req(dt, "dt", (B, L, H), act)
+    _req(A, "A", (H,), f)
+    _req(Bm, "Bm", (B, L, N), act)
+    _req(Cm, "Cm", (B, L, N), act)
+    _opt(Dskip, "Dskip", (H,), f)
+    _opt(dt_bias, "dt_bias", (H,), f)
+    _opt(h0, "h0", (B, H, P, N), f)
+    if y is None:
+        y = torch.empty((B, L, H, P), dtype=act, device=x.device)
+    _req(y, "y", (B, L, H, P), act)
+    if return_final_state and h_final is None:
+        h_final = torch.empty((B, H, P, N), dtype=f, device=x.device)
+    _opt(h_final, "h_final", (B, H, P, N), f)
+    prob = SsdProblem(B, L, H, P, N, _dtype_code(x), 1 if delta_softplus else 0)
+    cbytes = int(lib.mssm_ssd_ctx_bytes(ctypes.byref(prob)))
+    if cbytes == 0:
+        raise MssmError(-4, lib)
+    if ctx is None:
+        ctx = torch.empty(cbytes, dtype=torch.uint8, device=x.device)
+    nbytes = int(lib.mssm_ssd_fwd_train_workspace_bytes(ctypes.byref(prob)))
+    ws = _workspace(nbytes, x.device, workspace)
+    _check(lib.mssm_ssd_fwd_train(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
+                                  _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(h_final), _ptr(ctx),
+                                  ctx.numel() * ctx.element_size(), _ptr(ws), nbytes, _stream(x.device)))
+    return y, h_final, ctx
+
+
+def ssd_bwd_saved(x, dt, A, Bm, Cm, dy, ctx, Dskip=None, dt_bias=None, dh_final=None, delta_softplus=True,
+                  want_dD=True, want_ddt_bias=True, want_dh0=True, workspace=None):
+    """ssd_bwd from the context ssd_fwd_train kept for the same inputs (no h0 argument: the context
+    holds it).  Returns the dict of ssd_bwd."""
+    B, L, H, P = x.shape
+    N = Bm.shape[2]
+    f, act = torch.float32, x.dtype
+    _req(x, "x", (B, L, H, P), act)
+    _req(dt, "dt", (B, L, H), act)
+    _req(A, "A", (H,), f)
+    _req(Bm, "Bm", (B, L, N), act)
+    _req(Cm, "Cm", (B, L, N), act)
+    _req(dy, "dy", (B, L, H, P), act)
+    _opt(Dskip, "Dskip", (H,), f)
+    _opt(dt_bias, "dt_bias", (H,), f)
+    _opt(dh_final, "dh_final", (B, H, P, N), f)
+    if not ctx.is_cuda or not ctx.is_contiguous():
+        raise ValueError("ctx must be a contiguous GPU tensor")
+    dev = x.device
+    g = {
+        "dx": torch.empty((B, L, H, P), dtype=act, device=dev),
+        "ddt": torch.empty((B, L, H), dtype=act, device=dev),
+        "dA": torch.empty((H,), dtype=f, device=dev),
+        "dB": torch.empty((B, L, N), dtype=act, device=dev),
+        "dC": torch.empty((B, L, N), dtype=act, device=dev),
+        "dD": torch.empty((H,), dtype=f, device=dev) if want_dD else None,
+        "ddt_bias": torch.empty((H,), dtype=f, device=dev) if want_ddt_bias else None,
+        "dh0": torch.empty((B, H, P, N), dtype=f, device=dev) if want_dh0 else None,
+    }
+    prob = SsdProblem(B, L, H, P, N, _dtype_code(x), 1 if delta_softplus else 0)
+    nbytes = int(lib.mssm_ssd_bwd_saved_workspace_bytes(ctypes.byref(prob)))
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.mssm_ssd_bwd_saved(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(Dskip),
+                                  _ptr(dt_bias), _ptr(ctx), ctx.numel() * ctx.element_size(), _ptr(dy),
+                                  _ptr(dh_final), _ptr(g["dx"]), _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]),
+                                  _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["ddt_bias"]), _ptr(g["dh0"]), _ptr(ws),
+                                  nbytes, _stream(dev)))
     return g

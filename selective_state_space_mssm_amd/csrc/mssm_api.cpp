@@ -363,18 +363,22 @@ size_t mssm_ssd_fwd_workspace_bytes(const mssm_ssd_problem* p) {
         .ws_bytes;
 }
 
-mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
-                         const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
-                         const float* h0, void* y, float* h_final,
-                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+namespace {
+// The SSD forward; with ctx, the training forward (no time segments; the chunk states into ctx).
+mssm_status ssd_fwd_common(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                           const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                           const float* h0, void* y, float* h_final, void* ctx, size_t ctx_bytes,
+                           void* workspace, size_t workspace_bytes, void* hip_stream, bool train) {
     const mssm_status chk = check_ssd_problem(p);
     if (chk != MSSM_OK) return chk;
-    if (!x || !dt || !A || !Bm || !Cm || !y) return MSSM_ERR_NULL;
-    const mssm_status st = check_align({x, dt, A, Bm, Cm, Dskip, dt_bias, h0, y, h_final, workspace});
+    if (!x || !dt || !A || !Bm || !Cm || !y || (train && !ctx)) return MSSM_ERR_NULL;
+    const mssm_status st = check_align({x, dt, A, Bm, Cm, Dskip, dt_bias, h0, y, h_final, ctx, workspace});
     if (st != MSSM_OK) return st;
     const int64_t hsub = ssd_subheads(p), Hs = p->nheads * hsub;
     const mssm::SsdPlan plan = mssm::plan_ssd(p->batch, p->seqlen, Hs, mssm::kSsdHeadDim, p->dstate,
-                                              p->dtype == MSSM_BF16, device_cus());
+                                              p->dtype == MSSM_BF16, device_cus(), !train);
+    if (train && ctx_bytes < mssm::ssd_ctx_bytes(p->batch, p->seqlen, Hs, mssm::kSsdHeadDim, p->dstate))
+        return MSSM_ERR_WORKSPACE;
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return MSSM_ERR_WORKSPACE;
 
     mssm::SsdArgs a{};
@@ -393,7 +397,37 @@ mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* d
                                            ((static_cast<size_t>(plan.workers + 1) * sizeof(uint32_t) + 255) &
                                             ~static_cast<size_t>(255)));
     }
+    a.states = train ? static_cast<float*>(ctx) : nullptr;
     return from_hip(mssm::launch_ssd_fwd(a, static_cast<hipStream_t>(hip_stream)));
+}
+}  // namespace
+
+mssm_status mssm_ssd_fwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                         const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                         const float* h0, void* y, float* h_final,
+                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return ssd_fwd_common(p, x, dt, A, Bm, Cm, Dskip, dt_bias, h0, y, h_final, nullptr, 0, workspace,
+                          workspace_bytes, hip_stream, false);
+}
+
+size_t mssm_ssd_ctx_bytes(const mssm_ssd_problem* p) {
+    if (check_ssd_problem(p) != MSSM_OK) return 0;
+    return mssm::ssd_ctx_bytes(p->batch, p->seqlen, p->nheads * ssd_subheads(p), mssm::kSsdHeadDim, p->dstate);
+}
+
+size_t mssm_ssd_fwd_train_workspace_bytes(const mssm_ssd_problem* p) {
+    if (check_ssd_problem(p) != MSSM_OK) return 0;
+    return mssm::plan_ssd(p->batch, p->seqlen, p->nheads * ssd_subheads(p), mssm::kSsdHeadDim, p->dstate,
+                          p->dtype == MSSM_BF16, device_cus(), false)
+        .ws_bytes;
+}
+
+mssm_status mssm_ssd_fwd_train(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                               const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                               const float* h0, void* y, float* h_final, void* ctx, size_t ctx_bytes,
+                               void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return ssd_fwd_common(p, x, dt, A, Bm, Cm, Dskip, dt_bias, h0, y, h_final, ctx, ctx_bytes, workspace,
+                          workspace_bytes, hip_stream, true);
 }
 
 size_t mssm_ssd_bwd_workspace_bytes(const mssm_ssd_problem* p) {
@@ -403,22 +437,27 @@ size_t mssm_ssd_bwd_workspace_bytes(const mssm_ssd_problem* p) {
         .total;
 }
 
-mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
-                         const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
-                         const float* h0, const void* dy, const float* dh_final,
-                         void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
-                         float* ddt_bias, float* dh0,
-                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+namespace {
+// The SSD backward; with ctx, from the chunk states a training forward saved (no first chain).
+mssm_status ssd_bwd_common(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                           const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                           const float* h0, const void* ctx, size_t ctx_bytes, const void* dy,
+                           const float* dh_final, void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
+                           float* ddt_bias, float* dh0, void* workspace, size_t workspace_bytes, void* hip_stream,
+                           bool saved) {
     const mssm_status chk = check_ssd_problem(p);
     if (chk != MSSM_OK) return chk;
     if (!x || !dt || !A || !Bm || !Cm || !dy || !dx || !ddt || !dA || !dB || !dC) return MSSM_ERR_NULL;
-    const mssm_status al = check_align({x, dt, A, Bm, Cm, Dskip, dt_bias, h0, dy, dh_final, dx, ddt, dA, dB, dC, dD,
-                                        ddt_bias, dh0, workspace});
+    if (saved && !ctx) return MSSM_ERR_NULL;
+    const mssm_status al = check_align({x, dt, A, Bm, Cm, Dskip, dt_bias, h0, ctx, dy, dh_final, dx, ddt, dA, dB,
+                                        dC, dD, ddt_bias, dh0, workspace});
     if (al != MSSM_OK) return al;
     const bool bf16 = p->dtype == MSSM_BF16;
     const int64_t hsub = ssd_subheads(p), Hs = p->nheads * hsub;
+    if (saved && ctx_bytes < mssm::ssd_ctx_bytes(p->batch, p->seqlen, Hs, mssm::kSsdHeadDim, p->dstate))
+        return MSSM_ERR_WORKSPACE;
     const mssm::SsdBwdPlan plan =
-        mssm::plan_ssd_bwd(p->batch, p->seqlen, Hs, mssm::kSsdHeadDim, p->dstate, hsub, device_cus());
+        mssm::plan_ssd_bwd(p->batch, p->seqlen, Hs, mssm::kSsdHeadDim, p->dstate, hsub, device_cus(), saved);
     if (!workspace || workspace_bytes < plan.total) return MSSM_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
 
@@ -429,7 +468,7 @@ mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* d
     a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.dt_bias = dt_bias; a.h0 = h0;
     a.dy = dy; a.dh_final = dh_final;
     a.dx = dx; a.ddt = ddt; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD; a.ddt_bias = ddt_bias; a.dh0 = dh0;
-    a.states = reinterpret_cast<float*>(ws + plan.states);
+    a.states = saved ? static_cast<float*>(const_cast<void*>(ctx)) : reinterpret_cast<float*>(ws + plan.states);
     a.dstates = reinterpret_cast<float*>(ws + plan.dstates);
     a.parts = reinterpret_cast<float*>(ws + plan.parts);
     a.dbc = plan.groups > 1 ? reinterpret_cast<float*>(ws + plan.dbc) : nullptr;
@@ -441,7 +480,36 @@ mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* d
     a.chunk_dec = plan.nseg > 1 ? reinterpret_cast<float*>(ws + plan.chunk_dec) : nullptr;
     a.groups = plan.groups;
     a.heads_per_group = plan.heads_per_group;
-    return from_hip(mssm::launch_ssd_bwd(a, static_cast<hipStream_t>(hip_stream)));
+    return from_hip(saved ? mssm::launch_ssd_bwd_saved(a, static_cast<hipStream_t>(hip_stream))
+                          : mssm::launch_ssd_bwd(a, static_cast<hipStream_t>(hip_stream)));
+}
+}  // namespace
+
+mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                         const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                         const float* h0, const void* dy, const float* dh_final,
+                         void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
+                         float* ddt_bias, float* dh0,
+                         void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return ssd_bwd_common(p, x, dt, A, Bm, Cm, Dskip, dt_bias, h0, nullptr, 0, dy, dh_final, dx, ddt, dA, dB, dC,
+                          dD, ddt_bias, dh0, workspace, workspace_bytes, hip_stream, false);
+}
+
+size_t mssm_ssd_bwd_saved_workspace_bytes(const mssm_ssd_problem* p) {
+    if (check_ssd_problem(p) != MSSM_OK) return 0;
+    return mssm::plan_ssd_bwd(p->batch, p->seqlen, p->nheads * ssd_subheads(p), mssm::kSsdHeadDim, p->dstate,
+                              ssd_subheads(p), device_cus(), true)
+        .total;
+}
+
+mssm_status mssm_ssd_bwd_saved(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,
+                               const void* Bm, const void* Cm, const float* Dskip, const float* dt_bias,
+                               const void* ctx, size_t ctx_bytes, const void* dy, const float* dh_final,
+                               void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
+                               float* ddt_bias, float* dh0,
+                               void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return ssd_bwd_common(p, x, dt, A, Bm, Cm, Dskip, dt_bias, nullptr, ctx, ctx_bytes, dy, dh_final, dx, ddt, dA,
+                          dB, dC, dD, ddt_bias, dh0, workspace, workspace_bytes, hip_stream, true);
 }
 
 const char* mssm_status_string(mssm_status s) {

@@ -41,6 +41,9 @@ struct SsdArgs {
     int32_t workers;
     uint32_t* flags;       // (workers + 1): 1 once worker w has published; word `workers`: 1 if a wait gave up
     float* carry;          // (workers, P, N): the state worker w hands to worker w + 1
+    // training forward (nseg == 1): (B, H, nch + 1, P, N) float32, the state entering every 64-step chunk, then
+    // the final state -- what the backward's first chain would recompute; null otherwise
+    float* states;
 };
 
 constexpr int kSsdHeadDim = 64;   // P the kernel is built for
@@ -72,7 +75,10 @@ struct SsdPlan {
     size_t ws_bytes;
 };
 
-inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, bool bf16, int64_t ncu) {
+// `segments` false (the training forward, whose stored chunk states must be
+// the true ones): no time segments.
+inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, bool bf16, int64_t ncu,
+                        bool segments = true) {
     SsdPlan pl{1, L, 0, 0};
     const int64_t jobs = B * H, chunks = (L + kSsdChunk - 1) / kSsdChunk;
     if (ncu > 0 && jobs >= ncu && jobs % ncu != 0) {
@@ -81,7 +87,7 @@ inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, b
                       static_cast<size_t>(ncu * P * N) * sizeof(float);
         return pl;
     }
-    if (jobs >= 128 || chunks < 4) return pl;
+    if (!segments || jobs >= 128 || chunks < 4) return pl;
     const int64_t want = 256 / jobs, most = chunks / 2;
     const int64_t segs = want < most ? want : most;
     const int64_t per = (chunks + segs - 1) / segs;  // chunks per segment
@@ -146,7 +152,10 @@ struct SsdBwdPlan {
     size_t states, dstates, parts, dbc, ddt, seg_state, seg_lam, chunk_dec, total;  // byte offsets (total: size)
 };
 
-inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t hsub, int64_t ncu) {
+// `saved`: the backward from a training forward's context, whose chunk states
+// are not in the workspace.
+inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t hsub, int64_t ncu,
+                               bool saved = false) {
     auto al = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
     SsdBwdPlan p{};
     const int64_t nch = (L + kSsdChunk - 1) / kSsdChunk;
@@ -157,7 +166,7 @@ inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64
     p.heads_per_group = (H + p.groups - 1) / p.groups;
     p.groups = (H + p.heads_per_group - 1) / p.heads_per_group;
     size_t off = 0;
-    p.states = off;  off += al(static_cast<size_t>(B * H * (nch + 1) * P * N) * sizeof(float));
+    p.states = off;  off += saved ? 0 : al(static_cast<size_t>(B * H * (nch + 1) * P * N) * sizeof(float));
     p.dstates = off; off += al(static_cast<size_t>(B * H * nch * P * N) * sizeof(float));
     p.parts = off;   off += al(static_cast<size_t>(B * nch * H * 3) * sizeof(float));
     p.dbc = off;     off += p.groups > 1 ? al(static_cast<size_t>(2 * p.groups * B * L * N) * sizeof(float)) : 0;
@@ -182,5 +191,11 @@ inline SsdBwdPlan plan_ssd_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64
 
 hipError_t launch_ssd_fwd(const SsdArgs& a, hipStream_t st);
 hipError_t launch_ssd_bwd(const SsdBwdArgs& a, hipStream_t st);
+// Bytes of an SSD training forward's context: the chunk states (B, H, nch + 1, P, N) float32.
+inline size_t ssd_ctx_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N) {
+    return static_cast<size_t>(B * H * ((L + kSsdChunk - 1) / kSsdChunk + 1) * P * N) * sizeof(float);
+}
+// The backward with a.states the context a training forward wrote: no first chain.
+hipError_t launch_ssd_bwd_saved(const SsdBwdArgs& a, hipStream_t st);
 
 }  // namespace mssm

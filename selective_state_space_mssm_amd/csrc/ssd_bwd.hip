@@ -886,15 +886,19 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_groups_kernel(SsdBwdArgs a
     store_act(static_cast<T*>(a.dC), e, sc);
 }
 
-template <class T, int N>
+// SAVED: a.states holds what the first chain computes (a training forward
+// stored it), so only the adjoint chain runs.
+template <class T, int N, bool SAVED>
 hipError_t launch_bwd_typed(const SsdBwdArgs& a, hipStream_t st) {
     const dim3 chains((unsigned)(a.B * a.H * a.nseg));
     const dim3 carry((unsigned)((a.B * a.H * kP * N + 255) / 256));
     const dim3 fix((unsigned)(a.B * a.H * ((a.L + kQ - 1) / kQ)));
-    hipLaunchKernelGGL((ssd_chain_kernel<T, N, false>), chains, dim3(kThreads), 0, st, a);
-    if (a.nseg > 1) {
-        hipLaunchKernelGGL((ssd_chain_carry_kernel<N, false>), carry, dim3(256), 0, st, a);
-        hipLaunchKernelGGL((ssd_chain_fix_kernel<N, false>), fix, dim3(256), 0, st, a);
+    if constexpr (!SAVED) {
+        hipLaunchKernelGGL((ssd_chain_kernel<T, N, false>), chains, dim3(kThreads), 0, st, a);
+        if (a.nseg > 1) {
+            hipLaunchKernelGGL((ssd_chain_carry_kernel<N, false>), carry, dim3(256), 0, st, a);
+            hipLaunchKernelGGL((ssd_chain_fix_kernel<N, false>), fix, dim3(256), 0, st, a);
+        }
     }
     hipLaunchKernelGGL((ssd_chain_kernel<T, N, true>), chains, dim3(kThreads), 0, st, a);
     if (a.nseg > 1) {
@@ -919,8 +923,15 @@ hipError_t launch_bwd_typed(const SsdBwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_ssd_bwd(const SsdBwdArgs& a, hipStream_t st) {
-    if (a.dtype == 1) return a.N == 64 ? launch_bwd_typed<uint16_t, 64>(a, st) : launch_bwd_typed<uint16_t, 128>(a, st);
-    return a.N == 64 ? launch_bwd_typed<float, 64>(a, st) : launch_bwd_typed<float, 128>(a, st);
+    if (a.dtype == 1)
+        return a.N == 64 ? launch_bwd_typed<uint16_t, 64, false>(a, st) : launch_bwd_typed<uint16_t, 128, false>(a, st);
+    return a.N == 64 ? launch_bwd_typed<float, 64, false>(a, st) : launch_bwd_typed<float, 128, false>(a, st);
+}
+
+hipError_t launch_ssd_bwd_saved(const SsdBwdArgs& a, hipStream_t st) {
+    if (a.dtype == 1)
+        return a.N == 64 ? launch_bwd_typed<uint16_t, 64, true>(a, st) : launch_bwd_typed<uint16_t, 128, true>(a, st);
+    return a.N == 64 ? launch_bwd_typed<float, 64, true>(a, st) : launch_bwd_typed<float, 128, true>(a, st);
 }
 
 }  // namespace mssm

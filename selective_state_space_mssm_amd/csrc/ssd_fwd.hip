@@ -112,7 +112,10 @@ struct ChunkLoader {
     }
 };
 
-template <class T, int N>
+// SAVE: the training forward, which also stores the state entering every
+// chunk and the final state (a.states), one workgroup per (batch, head) or the
+// balanced schedule (no time segments).
+template <class T, int N, bool SAVE>
 __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     constexpr int NT = N / 64;  // state tiles per wave: the P x N state is 2 x (N / 32) tiles over 4 waves
     __shared__ SsdSmem<N> s;
@@ -210,6 +213,13 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
 
         for (int64_t t0 = t_begin; t0 < t_end; t0 += kQ) {
             const int nv = (int)imin64(kQ, t_end - t0);
+            if constexpr (SAVE) {  // the state entering this chunk, in the (P, N) layout of the backward's chains
+                float* st_out = a.states + (bh * (nch + 1) + t0 / kQ) * kP * N;
+#pragma unroll
+                for (int k = 0; k < NT; ++k)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) st_out[state_off(k, r)] = S[k][r];
+            }
 
             // ---- stage: the chunk's operands and S^T into LDS; cum, Delta, w ----
 #pragma unroll
@@ -371,6 +381,13 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) out[state_off(k, r)] = S[k][r];
         }
+        if (SAVE && to == kFinal) {  // the final state, after the states entering the chunks
+            float* st_out = a.states + (bh * (nch + 1) + nch) * kP * N;
+#pragma unroll
+            for (int k = 0; k < NT; ++k)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st_out[state_off(k, r)] = S[k][r];
+        }
         if (a.nseg > 1 && tid == 0) a.ws[a.B * H * a.nseg * kP * N + bh * a.nseg + seg] = lam;
         if (to == kPublish) {
             __threadfence();
@@ -516,10 +533,17 @@ hipError_t launch_typed(const SsdArgs& a, hipStream_t st) {
     if (a.workers > 0) {  // a fill kernel rather than a memset: the launch may be captured in a graph
         hipLaunchKernelGGL(ssd_zero_flags_kernel, dim3((unsigned)((a.workers + 1 + 255) / 256)), dim3(256), 0, st,
                            a.flags, a.workers + 1);
-        hipLaunchKernelGGL((ssd_fwd_kernel<T, N>), dim3((unsigned)a.workers), block, 0, st, a);
+        if (a.states)
+            hipLaunchKernelGGL((ssd_fwd_kernel<T, N, true>), dim3((unsigned)a.workers), block, 0, st, a);
+        else
+            hipLaunchKernelGGL((ssd_fwd_kernel<T, N, false>), dim3((unsigned)a.workers), block, 0, st, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((ssd_fwd_kernel<T, N>), dim3((unsigned)(a.B * a.H * a.nseg)), block, 0, st, a);
+    if (a.states && a.nseg != 1) return hipErrorInvalidValue;  // the stored states must be the true ones
+    if (a.states)
+        hipLaunchKernelGGL((ssd_fwd_kernel<T, N, true>), dim3((unsigned)(a.B * a.H)), block, 0, st, a);
+    else
+        hipLaunchKernelGGL((ssd_fwd_kernel<T, N, false>), dim3((unsigned)(a.B * a.H * a.nseg)), block, 0, st, a);
     if (a.nseg > 1) {
         const int64_t n = a.B * a.H * a.P * a.N;
         hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
