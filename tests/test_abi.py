@@ -232,6 +232,43 @@ def test_ssd_validation():
     assert ssd(good(seqlen=1000), ws=MIS, wsb=need) == -5
 
 
+def test_ssd_training_pair_validation():
+    """mssm_ssd_fwd_train / mssm_ssd_bwd_saved: the SSD calls' checks plus the
+    context (required, aligned, at least mssm_ssd_ctx_bytes: the state
+    entering every 64-step chunk and the final one); the training forward
+    never takes time segments, so it needs no segment scratch."""
+    S = mssm.binding.SsdProblem
+    good = lambda **k: S(**{**dict(batch=2, seqlen=100, nheads=3, headdim=64, dstate=64, dtype=0,  # noqa: E731
+                                   delta_softplus=1), **k})
+    v = lambda x: None if x is None else ctypes.c_void_p(x)  # noqa: E731
+    nctx = lib.mssm_ssd_ctx_bytes(ctypes.byref(good()))
+    assert nctx == 2 * 3 * (2 + 1) * 64 * 64 * 4
+    assert lib.mssm_ssd_ctx_bytes(ctypes.byref(good(headdim=128))) == 2 * nctx
+    assert lib.mssm_ssd_ctx_bytes(ctypes.byref(good(dstate=16))) == 0
+    assert lib.mssm_ssd_fwd_workspace_bytes(ctypes.byref(good(seqlen=1000))) > 0     # segments
+    assert lib.mssm_ssd_fwd_train_workspace_bytes(ctypes.byref(good(seqlen=1000))) == 0  # none
+    nb = lib.mssm_ssd_bwd_workspace_bytes(ctypes.byref(good()))
+    assert lib.mssm_ssd_bwd_saved_workspace_bytes(ctypes.byref(good())) == nb - 2 * 3 * 3 * 64 * 64 * 4
+
+    def fwd_tr(p, ctx=FAKE, ctxb=1 << 40, x=FAKE):
+        return lib.mssm_ssd_fwd_train(ctypes.byref(p) if p is not None else None, v(x), v(FAKE), v(FAKE), v(FAKE),
+                                      v(FAKE), None, None, None, v(FAKE), None, v(ctx), ctxb, None, 0, None)
+
+    def bwd_sv(p, ctx=FAKE, ctxb=1 << 40, ws=FAKE, wsb=1 << 40, dy=FAKE):
+        return lib.mssm_ssd_bwd_saved(ctypes.byref(p) if p is not None else None, v(FAKE), v(FAKE), v(FAKE),
+                                      v(FAKE), v(FAKE), None, None, v(ctx), ctxb, v(dy), None, v(FAKE), v(FAKE),
+                                      v(FAKE), v(FAKE), v(FAKE), None, None, None, v(ws), wsb, None)
+    for call in (fwd_tr, bwd_sv):
+        assert call(None) == -1
+        assert call(good(dstate=16)) == -4
+        assert call(good(), ctx=None) == -1
+        assert call(good(), ctx=MIS) == -5
+        assert call(good(), ctxb=nctx - 1) == -6
+    assert fwd_tr(good(), x=None) == -1
+    assert bwd_sv(good(), dy=None) == -1
+    assert bwd_sv(good(), ws=None) == -6
+
+
 def test_workspace_sizes_and_checks():
     tiny = good(1, 64, 32, 16)
     assert lib.mssm_scan_fwd_workspace_bytes(ctypes.byref(tiny)) == 0
