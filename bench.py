@@ -464,6 +464,9 @@ def ssd_layers(mssm, torch):
     tf, tb = time_ssd_train_pair(mssm, torch, 8, 2048, 80, 128)
     r["ssd_fwd_train_H80_N128_B8_L2048_us"] = round(tf, 1)
     r["ssd_bwd_saved_H80_N128_B8_L2048_us"] = round(tb, 1)
+    tf, tb = time_ssd_train_pair(mssm, torch, 1, 2048, 24, 128, 10)  # time segments in both
+    r["ssd_fwd_train_H24_N128_B1_L2048_us"] = round(tf, 1)
+    r["ssd_bwd_saved_H24_N128_B1_L2048_us"] = round(tb, 1)
     return r
 
 

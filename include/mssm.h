@@ -447,11 +447,13 @@ mssm_status mssm_ssd_bwd(const mssm_ssd_problem* p, const void* x, const void* d
  * caller-owned ctx (at least mssm_ssd_ctx_bytes), and the backward starts from
  * them instead of recomputing them with its first pass over the chunks.
  * mssm_ssd_fwd_train: arguments, outputs and errors of mssm_ssd_fwd plus ctx
- * (required); its workspace is mssm_ssd_fwd_train_workspace_bytes (the
- * training forward never cuts the sequence into time segments, whose stored
- * states would not be the true ones; with few (batch, head) pairs it is
- * therefore slower than mssm_ssd_fwd).  y and h_final are those of
- * mssm_ssd_fwd bit for bit wherever mssm_ssd_fwd runs without segments.
+ * (required); its workspace is mssm_ssd_fwd_train_workspace_bytes: that of
+ * mssm_ssd_fwd, and where mssm_ssd_fwd cuts the sequence into time segments
+ * (few (batch, head) pairs) also, from the next 256-byte boundary, one float
+ * per (batch, sub-head, chunk): each chunk's decay from its segment's start,
+ * with which a last pass turns the states a segment stored from its zero
+ * start into the true ones.  y and h_final are those of mssm_ssd_fwd bit for
+ * bit (the same kernels, which also store the states).
  * mssm_ssd_bwd_saved: arguments, outputs and errors of mssm_ssd_bwd with ctx
  * in place of h0 (the ctx holds it); workspace
  * mssm_ssd_bwd_saved_workspace_bytes (the states are not in it).

@@ -660,7 +660,7 @@ def ssd_bwd(x, dt, A, Bm, Cm, dy, Dskip=None, dt_bias=None, h0=None, dh_final=No
 
 def ssd_fwd_train(x, dt, A, Bm, Cm, Dskip=None, dt_bias=None, h0=None, delta_softplus=True,
                   return_final_state=True, y=None, h_final=None, ctx=None, workspace=None):
-    """ssd_fwd that also keeps the chunk states for ssd_bwd_saved (no time segments).
+    """ssd_fwd that also keeps the chunk states for ssd_bwd_saved.
     Returns (y, h_final, ctx); ctx a uint8 device tensor of mssm_ssd_ctx_bytes."""
     B, L, H, P = x.shape
     N = Bm.shape[2]

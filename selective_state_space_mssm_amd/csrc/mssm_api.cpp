@@ -376,10 +376,12 @@ mssm_status ssd_fwd_common(const mssm_ssd_problem* p, const void* x, const void*
     if (st != MSSM_OK) return st;
     const int64_t hsub = ssd_subheads(p), Hs = p->nheads * hsub;
     const mssm::SsdPlan plan = mssm::plan_ssd(p->batch, p->seqlen, Hs, mssm::kSsdHeadDim, p->dstate,
-                                              p->dtype == MSSM_BF16, device_cus(), !train);
+                                              p->dtype == MSSM_BF16, device_cus());
     if (train && ctx_bytes < mssm::ssd_ctx_bytes(p->batch, p->seqlen, Hs, mssm::kSsdHeadDim, p->dstate))
         return MSSM_ERR_WORKSPACE;
-    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return MSSM_ERR_WORKSPACE;
+    const size_t need = train ? mssm::ssd_train_ws_bytes(plan.ws_bytes, plan.nseg, p->batch, p->seqlen, Hs)
+                              : plan.ws_bytes;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return MSSM_ERR_WORKSPACE;
 
     mssm::SsdArgs a{};
     a.B = p->batch; a.L = p->seqlen; a.H = Hs; a.P = mssm::kSsdHeadDim; a.N = p->dstate; a.hsub = hsub;
@@ -398,6 +400,10 @@ mssm_status ssd_fwd_common(const mssm_ssd_problem* p, const void* x, const void*
                                             ~static_cast<size_t>(255)));
     }
     a.states = train ? static_cast<float*>(ctx) : nullptr;
+    a.chunk_dec = train && plan.nseg > 1
+                      ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                 ((plan.ws_bytes + 255) & ~static_cast<size_t>(255)))
+                      : nullptr;
     return from_hip(mssm::launch_ssd_fwd(a, static_cast<hipStream_t>(hip_stream)));
 }
 }  // namespace
@@ -417,9 +423,10 @@ size_t mssm_ssd_ctx_bytes(const mssm_ssd_problem* p) {
 
 size_t mssm_ssd_fwd_train_workspace_bytes(const mssm_ssd_problem* p) {
     if (check_ssd_problem(p) != MSSM_OK) return 0;
-    return mssm::plan_ssd(p->batch, p->seqlen, p->nheads * ssd_subheads(p), mssm::kSsdHeadDim, p->dstate,
-                          p->dtype == MSSM_BF16, device_cus(), false)
-        .ws_bytes;
+    const int64_t Hs = p->nheads * ssd_subheads(p);
+    const mssm::SsdPlan plan = mssm::plan_ssd(p->batch, p->seqlen, Hs, mssm::kSsdHeadDim, p->dstate,
+                                              p->dtype == MSSM_BF16, device_cus());
+    return mssm::ssd_train_ws_bytes(plan.ws_bytes, plan.nseg, p->batch, p->seqlen, Hs);
 }
 
 mssm_status mssm_ssd_fwd_train(const mssm_ssd_problem* p, const void* x, const void* dt, const float* A,

@@ -41,13 +41,26 @@ struct SsdArgs {
     int32_t workers;
     uint32_t* flags;       // (workers + 1): 1 once worker w has published; word `workers`: 1 if a wait gave up
     float* carry;          // (workers, P, N): the state worker w hands to worker w + 1
-    // training forward (nseg == 1): (B, H, nch + 1, P, N) float32, the state entering every 64-step chunk, then
-    // the final state -- what the backward's first chain would recompute; null otherwise
+    // training forward: (B, H, nch + 1, P, N) float32, the state entering every 64-step chunk, then the final
+    // state -- what the backward's first chain would recompute; null otherwise.  With time segments the main
+    // kernel stores the states of a segment's zero start and, per chunk, the decay from the segment's start
+    // (chunk_dec, (B, H, nch)); a fix pass adds the segment's true entering state times that decay
     float* states;
+    float* chunk_dec;
 };
+
+
 
 constexpr int kSsdHeadDim = 64;   // P the kernel is built for
 constexpr int kSsdChunk = 64;     // chunk length of the dual form
+
+// Workspace of the training forward: the forward's, and with time segments
+// the per-chunk decays of the stored states' fix pass.
+inline size_t ssd_train_ws_bytes(size_t fwd_ws, int64_t nseg, int64_t B, int64_t L, int64_t H) {
+    return nseg > 1 ? ((fwd_ws + 255) & ~static_cast<size_t>(255)) +
+                          static_cast<size_t>(B * H * ((L + kSsdChunk - 1) / kSsdChunk)) * sizeof(float)
+                    : fwd_ws;
+}
 
 constexpr int kSsdMaxSubHeads = 4;  // head dims 64, 128, 192, 256
 
@@ -75,10 +88,7 @@ struct SsdPlan {
     size_t ws_bytes;
 };
 
-// `segments` false (the training forward, whose stored chunk states must be
-// the true ones): no time segments.
-inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, bool bf16, int64_t ncu,
-                        bool segments = true) {
+inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, bool bf16, int64_t ncu) {
     SsdPlan pl{1, L, 0, 0};
     const int64_t jobs = B * H, chunks = (L + kSsdChunk - 1) / kSsdChunk;
     if (ncu > 0 && jobs >= ncu && jobs % ncu != 0) {
@@ -87,7 +97,7 @@ inline SsdPlan plan_ssd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, b
                       static_cast<size_t>(ncu * P * N) * sizeof(float);
         return pl;
     }
-    if (!segments || jobs >= 128 || chunks < 4) return pl;
+    if (jobs >= 128 || chunks < 4) return pl;
     const int64_t want = 256 / jobs, most = chunks / 2;
     const int64_t segs = want < most ? want : most;
     const int64_t per = (chunks + segs - 1) / segs;  // chunks per segment

@@ -113,8 +113,9 @@ struct ChunkLoader {
 };
 
 // SAVE: the training forward, which also stores the state entering every
-// chunk and the final state (a.states), one workgroup per (batch, head) or the
-// balanced schedule (no time segments).
+// chunk and the final state (a.states); with time segments, those of the
+// segment's zero start and each chunk's decay from the segment's start, for
+// ssd_states_fix_kernel.
 template <class T, int N, bool SAVE>
 __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
     constexpr int NT = N / 64;  // state tiles per wave: the P x N state is 2 x (N / 32) tiles over 4 waves
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
         for (int64_t t0 = t_begin; t0 < t_end; t0 += kQ) {
             const int nv = (int)imin64(kQ, t_end - t0);
             if constexpr (SAVE) {  // the state entering this chunk, in the (P, N) layout of the backward's chains
+                if (a.nseg > 1 && tid == 0) a.chunk_dec[bh * nch + t0 / kQ] = fexp(lam);
                 float* st_out = a.states + (bh * (nch + 1) + t0 / kQ) * kP * N;
 #pragma unroll
                 for (int k = 0; k < NT; ++k)
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) out[state_off(k, r)] = S[k][r];
         }
-        if (SAVE && to == kFinal) {  // the final state, after the states entering the chunks
+        if (SAVE && to == kFinal && t_end == L) {  // the final state, after the states entering the chunks
             float* st_out = a.states + (bh * (nch + 1) + nch) * kP * N;
 #pragma unroll
             for (int k = 0; k < NT; ++k)
@@ -415,6 +417,30 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(SsdArgs a) {
         cur = fexp(lam[k]) * cur + loc;
     }
     if (a.h_final) a.h_final[e] = cur;
+}
+
+// The training forward's stored states of time segments k >= 1, which started
+// from zero: adds the segment's true entering state (the carry pass's) times
+// the decay from the segment's start to each chunk, and to the final state the
+// last segment's total decay times its entering state.  One workgroup per
+// (batch, head, chunk or the final slot).
+__global__ __launch_bounds__(256) void ssd_states_fix_kernel(SsdArgs a) {
+    const int64_t PN = a.P * a.N, nch = (a.L + kQ - 1) / kQ;
+    const int64_t bh = blockIdx.x / (nch + 1), c = blockIdx.x % (nch + 1);
+    const float* lam = a.ws + a.B * a.H * a.nseg * PN + bh * a.nseg;
+    int64_t seg;
+    float d;
+    if (c == nch) {
+        seg = a.nseg - 1;
+        d = fexp(lam[seg]);
+    } else {
+        seg = c / (a.seg_len / kQ);
+        if (seg == 0) return;  // segment 0 started from h0: its states are exact
+        d = a.chunk_dec[bh * nch + c];
+    }
+    const float* sin = a.ws + (bh * a.nseg + seg) * PN;
+    float* out = a.states + (bh * (nch + 1) + c) * PN;
+    for (int64_t e = threadIdx.x; e < PN; e += 256) out[e] = __builtin_fmaf(d, sin[e], out[e]);
 }
 
 // Correction pass, one workgroup per (batch, head, segment k >= 1): adds the
@@ -539,15 +565,19 @@ hipError_t launch_typed(const SsdArgs& a, hipStream_t st) {
             hipLaunchKernelGGL((ssd_fwd_kernel<T, N, false>), dim3((unsigned)a.workers), block, 0, st, a);
         return hipGetLastError();
     }
-    if (a.states && a.nseg != 1) return hipErrorInvalidValue;  // the stored states must be the true ones
+    if (a.states && a.nseg > 1 && !a.chunk_dec) return hipErrorInvalidValue;
     if (a.states)
-        hipLaunchKernelGGL((ssd_fwd_kernel<T, N, true>), dim3((unsigned)(a.B * a.H)), block, 0, st, a);
+        hipLaunchKernelGGL((ssd_fwd_kernel<T, N, true>), dim3((unsigned)(a.B * a.H * a.nseg)), block, 0, st, a);
     else
         hipLaunchKernelGGL((ssd_fwd_kernel<T, N, false>), dim3((unsigned)(a.B * a.H * a.nseg)), block, 0, st, a);
     if (a.nseg > 1) {
         const int64_t n = a.B * a.H * a.P * a.N;
         hipLaunchKernelGGL(ssd_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
         hipLaunchKernelGGL((ssd_correct_kernel<T, N>), dim3((unsigned)(a.B * a.H * (a.nseg - 1))), block, 0, st, a);
+        if (a.states) {
+            const int64_t slots = a.B * a.H * ((a.L + kQ - 1) / kQ + 1);
+            hipLaunchKernelGGL(ssd_states_fix_kernel, dim3((unsigned)slots), dim3(256), 0, st, a);
+        }
     }
     return hipGetLastError();
 }

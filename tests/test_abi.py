@@ -235,8 +235,9 @@ def test_ssd_validation():
 def test_ssd_training_pair_validation():
     """mssm_ssd_fwd_train / mssm_ssd_bwd_saved: the SSD calls' checks plus the
     context (required, aligned, at least mssm_ssd_ctx_bytes: the state
-    entering every 64-step chunk and the final one); the training forward
-    never takes time segments, so it needs no segment scratch."""
+    entering every 64-step chunk and the final one); with time segments the
+    training forward's scratch is the forward's plus each chunk's decay from
+    its segment's start."""
     S = mssm.binding.SsdProblem
     good = lambda **k: S(**{**dict(batch=2, seqlen=100, nheads=3, headdim=64, dstate=64, dtype=0,  # noqa: E731
                                    delta_softplus=1), **k})
@@ -246,7 +247,10 @@ def test_ssd_training_pair_validation():
     assert lib.mssm_ssd_ctx_bytes(ctypes.byref(good(headdim=128))) == 2 * nctx
     assert lib.mssm_ssd_ctx_bytes(ctypes.byref(good(dstate=16))) == 0
     assert lib.mssm_ssd_fwd_workspace_bytes(ctypes.byref(good(seqlen=1000))) > 0     # segments
-    assert lib.mssm_ssd_fwd_train_workspace_bytes(ctypes.byref(good(seqlen=1000))) == 0  # none
+    seg = lib.mssm_ssd_fwd_workspace_bytes(ctypes.byref(good(seqlen=1000)))
+    assert lib.mssm_ssd_fwd_train_workspace_bytes(ctypes.byref(good(seqlen=1000))) == \
+        (seg + 255) // 256 * 256 + 2 * 3 * 16 * 4  # 6 pairs, 16 chunks
+    assert lib.mssm_ssd_fwd_train_workspace_bytes(ctypes.byref(good())) == 0  # no segments, no scratch
     nb = lib.mssm_ssd_bwd_workspace_bytes(ctypes.byref(good()))
     assert lib.mssm_ssd_bwd_saved_workspace_bytes(ctypes.byref(good())) == nb - 2 * 3 * 3 * 64 * 64 * 4
 

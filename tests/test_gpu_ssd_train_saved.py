@@ -3,21 +3,23 @@ forward that keeps the state entering every 64-step chunk and the final
 state) and mssm_ssd_bwd_saved (the backward that starts from them, with no
 first pass over the chunks).
 
-* y and h_final equal mssm_ssd_fwd's bit for bit where mssm_ssd_fwd runs
-  without time segments (many (batch, head) pairs), and to the forward
-  tolerance where it cuts few pairs into segments (the training forward
-  never does);
+* y and h_final equal mssm_ssd_fwd's bit for bit (the same kernels, which
+  also store the states), with and without time segments (few (batch, head)
+  pairs) and on the balanced schedule;
+* the stored states equal the oracle's state entering every chunk (with time
+  segments: after the pass that adds each segment's entering state);
 * the gradients dx, ddt, dA, dB, dC, dD, ddt_bias, dh0 match the float64
   oracle's adjoint element by element (helpers.grad_err: 1e-3, 2e-2 for
   bfloat16) and mssm_ssd_bwd's to 1e-5;
 * shapes: ragged last chunks, both state sizes, every optional input or none,
-  bfloat16, a 128-channel head, few pairs (the adjoint chain in time segments)
-  and the balanced forward schedule (more pairs than CUs, not a multiple)."""
+  bfloat16, a 128-channel head, few pairs (the forward and the adjoint chain
+  in time segments, up to 8 of them) and the balanced forward schedule (more
+  pairs than CUs, not a multiple)."""
 import numpy as np
 import pytest
 
 import oracle
-from helpers import FWD_TOL, GRAD_TOL, fwd_err, grad_err, to_np
+from helpers import GRAD_TOL, STATE_TOL, fwd_err, grad_err, to_np
 from test_gpu_ssd_bwd import GRADS, case
 
 torch = pytest.importorskip("torch")
@@ -30,7 +32,24 @@ def lib():
     return m
 
 
-def run_pair(lib, B, L, H, N, seed, dtype="f32", opts="all", segmented=False):
+def check_states(ctx, inp, h0, use, B, L, H, N):
+    """The stored state entering chunk c is the oracle's final state after the first 64 c steps (checked at
+    the first chunks, one in the middle and the last, and the final slot, which is h_final)."""
+    nch = (L + 63) // 64
+    st = to_np(ctx[:B * H * (nch + 1) * 64 * N * 4].view(torch.float32)).reshape(B, H, nch + 1, 64, N)
+    for c in sorted({0, 1, nch // 2, nch - 1, nch} & set(range(nch + 1))):
+        t = min(64 * c, L)
+        if t == 0:
+            ref = h0 if h0 is not None else np.zeros((B, H, 64, N))
+        else:
+            ref = oracle.ssd_fwd(inp["x"][:, :t], inp["dt"][:, :t], inp["A"], inp["Bm"][:, :t], inp["Cm"][:, :t],
+                                 Dskip=inp["Dskip"] if use else None, dt_bias=inp["dt_bias"] if use else None,
+                                 h0=h0)[1]
+        e = fwd_err(st[:, :, c], ref)
+        assert e <= STATE_TOL, f"state entering chunk {c}: {e:.2e}"
+
+
+def run_pair(lib, B, L, H, N, seed, dtype="f32", opts="all"):
     print(f"[ssd train pair] B={B} L={L} H={H} N={N} {dtype} {opts}", flush=True)
     inp, t = case(B, L, H, N, seed, dtype)
     use = opts == "all"
@@ -41,10 +60,8 @@ def run_pair(lib, B, L, H, N, seed, dtype="f32", opts="all", segmented=False):
     D, bias = (t["Dskip"], t["dt_bias"]) if use else (None, None)
     y, hf, ctx = lib.ssd_fwd_train(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], D, bias, cu(h0))
     y0, hf0 = lib.ssd_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], D, bias, cu(h0))
-    if segmented:
-        assert fwd_err(to_np(y), to_np(y0)) <= FWD_TOL[dtype] and fwd_err(to_np(hf), to_np(hf0)) <= 1e-4
-    else:
-        assert torch.equal(y, y0) and torch.equal(hf, hf0), "training forward differs from mssm_ssd_fwd"
+    assert torch.equal(y, y0) and torch.equal(hf, hf0), "training forward differs from mssm_ssd_fwd"
+    check_states(ctx, inp, h0, use, B, L, H, N)
     g = lib.ssd_bwd_saved(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["dy"], ctx, D, bias, cu(dhf))
     ref = lib.ssd_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], t["dy"], D, bias, cu(h0), cu(dhf))
     torch.cuda.synchronize()
@@ -62,8 +79,15 @@ def run_pair(lib, B, L, H, N, seed, dtype="f32", opts="all", segmented=False):
 
 @pytest.mark.parametrize("L,N", [(1, 64), (130, 64), (257, 128), (200, 128)])
 def test_shapes(lib, L, N):
-    # 8 pairs: mssm_ssd_fwd cuts four chunks or more into time segments (the training forward does not)
-    run_pair(lib, 2, L, 4, N, seed=L + N, segmented=L > 192)
+    # 8 pairs: four chunks or more are cut into time segments
+    run_pair(lib, 2, L, 4, N, seed=L + N)
+
+
+@pytest.mark.parametrize("B,L,H,N,dtype", [(1, 900, 2, 64, "f32"), (1, 1000, 2, 128, "bf16"), (2, 700, 1, 64, "f32")])
+def test_many_segments(lib, B, L, H, N, dtype):
+    # few pairs, long sequences: up to 8 time segments, the last one short and ragged; bfloat16 completes the
+    # outputs in a float32 copy
+    run_pair(lib, B, L, H, N, seed=L + H, dtype=dtype)
 
 
 def test_no_optional_inputs(lib):
