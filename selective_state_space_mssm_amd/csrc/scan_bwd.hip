@@ -195,6 +195,9 @@ __device__ __forceinline__ void fetch_rows_saved(const T* __restrict__ u_b, cons
                                                  int first_row, int lo, float (&ru)[SPW], float (&rd)[SPW],
                                                  float (&rdy)[SPW], float (&rz)[SPW], float (&rs)[SPW]) {
     const int t0 = max(tile, 0) * kTB;
+    // without a gate, z is read from dy and s from the context's (unused) readout: the loads stay
+    // unconditional, with no branch for the wait counters to merge over; gate_rows ignores both
+    const T* zl = z_b ? z_b : dy_b;
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
         const int t = min(t0 + first_row + i, L32 - 1);
@@ -202,12 +205,8 @@ __device__ __forceinline__ void fetch_rows_saved(const T* __restrict__ u_b, cons
         ru[i] = load_act(u_b, off);
         rd[i] = load_act(d_b, off);
         rdy[i] = load_act(dy_b, off);
-        if (z_b) {
-            rz[i] = load_act(z_b, off);
-            rs[i] = s_b[off];
-        } else {
-            rz[i] = rs[i] = 0.0f;
-        }
+        rz[i] = load_act(zl, off);
+        rs[i] = s_b[off];
     }
 }
 
@@ -679,7 +678,7 @@ __global__ __launch_bounds__(64 * (G + helper_waves(G))) void bwd_reverse_kernel
     bk.ck_stride = D * N;
     bk.u_b = static_cast<const T*>(a.u) + bk.row_b * D + chan0;
     bk.d_b = static_cast<const T*>(a.delta) + bk.row_b * D + chan0;
-    bk.s_b = SAVED ? (a.z ? a.s_saved + bk.row_b * D + chan0 : nullptr) : a.sbar + bk.row_b * D + chan0;
+    bk.s_b = (SAVED ? a.s_saved : a.sbar) + bk.row_b * D + chan0;  // the context always holds the readout
     bk.dy_b = SAVED ? static_cast<const T*>(a.dy) + bk.row_b * D + chan0 : nullptr;
     bk.z_b = (SAVED && a.z) ? static_cast<const T*>(a.z) + bk.row_b * D + chan0 : nullptr;
     bk.dz_b = (SAVED && a.z) ? static_cast<T*>(a.dz) + bk.row_b * D + chan0 : nullptr;
@@ -827,6 +826,7 @@ __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
     // saved context: sbar = dy silu(z) formed here from dy and z
     const T* dy_b = SAVED ? static_cast<const T*>(a.dy) + row_b * D + chan0 : nullptr;
     const T* z_b = (SAVED && a.z) ? static_cast<const T*>(a.z) + row_b * D + chan0 : nullptr;
+    const T* zl = z_b ? z_b : dy_b;  // without a gate: an unconditional load from dy, its value unused
     const T* Cm = static_cast<const T*>(a.Cm);
     // loads of PF tiles in flight, in a ring of register slots: tile t's raw rows and Cm sit in slot
     // (te - 1 - t) % PF, issued PF tiles before its steps (one tile of steps does not cover a load's latency)
@@ -843,7 +843,7 @@ __global__ __launch_bounds__(64 * G) void bwd_chunk_lambda_kernel(BwdKArgs a) {
             d[i] = load_act(d_b, off);
             if constexpr (SAVED) {
                 sb[i] = load_act(dy_b, off);
-                zz[i] = z_b ? load_act(z_b, off) : 0.0f;
+                zz[i] = load_act(zl, off);
             } else {
                 sb[i] = s_b[off];
             }
